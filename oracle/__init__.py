@@ -1,0 +1,169 @@
+"""CPU oracle of the packed-AdamW step (ctypes wrapper around pa_oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()``
+and the benchmark's ``cpu_baseline`` leg may import this package.  The
+product path (the ``adamw_step_amd`` package and its HIP library) never
+imports, links or runs it, and it imports nothing from the product path.
+
+Every function here is a thin marshalling layer; the arithmetic lives in
+pa_oracle.c, whose header lists the passages each part follows and the
+readings taken where the pages are silent.
+
+Lanes (argument ``lane`` of encode/decode):
+    0  E4M11 signed first moment (low half of the packed word)
+    1  E4M12 unsigned uncorrected RMS (high half of the packed word)
+    2  IEEE binary16 (both halves of the FP16-first/FP16-RMS word)
+    3  bfloat16 (encode only: parameter output of the blockwise mode)
+
+Parity of the E4 exponent bias (15) is unpinned: the pages never print it.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpa_oracle.so")
+
+LANE_M_E4, LANE_R_E4, LANE_F16, LANE_BF16 = 0, 1, 2, 3
+PACKED_E4, PACKED_F16 = 1, 2
+BLOCK = 2048
+
+_lib = None
+
+_f32p = ctypes.POINTER(ctypes.c_float)
+_u32p = ctypes.POINTER(ctypes.c_uint32)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        from . import build as _b
+        _b.build()
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.oracle_scalars.argtypes = [ctypes.c_double] * 5 + [ctypes.c_longlong, _f32p]
+    lib.oracle_scalars.restype = None
+    lib.oracle_encode_batch.argtypes = [ctypes.c_int, _f32p, _u16p, ctypes.c_size_t]
+    lib.oracle_encode_batch.restype = None
+    lib.oracle_decode_batch.argtypes = [ctypes.c_int, _u16p, _f32p, ctypes.c_size_t]
+    lib.oracle_decode_batch.restype = None
+    lib.oracle_step_fp32.argtypes = [_f32p, _f32p, _f32p, _f32p, ctypes.c_size_t, _f32p]
+    lib.oracle_step_fp32.restype = ctypes.c_ulonglong
+    lib.oracle_step_packed.argtypes = [ctypes.c_int, _f32p, _f32p, _u32p, ctypes.c_size_t, _f32p]
+    lib.oracle_step_packed.restype = ctypes.c_ulonglong
+    lib.oracle_step_blockwise.argtypes = [_f32p, _f32p, _u8p, _f32p, _u8p, _f32p, _f32p, _f32p,
+                                          _u16p, ctypes.c_size_t, _f32p]
+    lib.oracle_step_blockwise.restype = ctypes.c_ulonglong
+    lib.oracle_search_codes.argtypes = [_f32p, _f32p, _u8p, ctypes.c_size_t]
+    lib.oracle_search_codes.restype = None
+    lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_block_len.restype = ctypes.c_int
+    lib.oracle_e4_bias.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a, typ):
+    return a.ctypes.data_as(typ)
+
+
+def _need(a, dtype, name):
+    if not isinstance(a, np.ndarray) or a.dtype != dtype or not a.flags.c_contiguous:
+        raise TypeError(f"{name} must be a C-contiguous numpy array of {np.dtype(dtype).name}")
+
+
+def scalars(lr, beta1, beta2, eps, weight_decay, step):
+    """The eight binary32 scalars of one call, formed in double and rounded once:
+    [beta1, 1-beta1, beta2, 1-beta2, bc2, lr/bc1, 1-lr*wd, eps]."""
+    out = np.zeros(8, np.float32)
+    _load().oracle_scalars(float(lr), float(beta1), float(beta2), float(eps),
+                           float(weight_decay), int(step), _ptr(out, _f32p))
+    return out
+
+
+def encode(lane, x):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.uint16)
+    _load().oracle_encode_batch(int(lane), _ptr(x, _f32p), _ptr(out, _u16p), x.size)
+    return out
+
+
+def decode(lane, codes):
+    if lane == LANE_BF16:
+        raise ValueError("bfloat16 decode is not part of the oracle")
+    c = np.ascontiguousarray(codes, dtype=np.uint16)
+    out = np.empty(c.shape, np.float32)
+    _load().oracle_decode_batch(int(lane), _ptr(c, _u16p), _ptr(out, _f32p), c.size)
+    return out
+
+
+def step_fp32(p, g, m, v, sc):
+    """In place on p, m, v.  Returns the non-finite element count."""
+    for a, nm in ((p, "p"), (g, "g"), (m, "m"), (v, "v"), (sc, "scalars")):
+        _need(a, np.float32, nm)
+    n = p.size
+    assert g.size == n and m.size == n and v.size == n and sc.size == 8
+    return int(_load().oracle_step_fp32(_ptr(p, _f32p), _ptr(g, _f32p), _ptr(m, _f32p),
+                                        _ptr(v, _f32p), n, _ptr(sc, _f32p)))
+
+
+def step_packed(kind, p, g, w, sc):
+    """kind PACKED_E4 or PACKED_F16; in place on p and w.  Returns the non-finite count."""
+    _need(p, np.float32, "p")
+    _need(g, np.float32, "g")
+    _need(w, np.uint32, "w")
+    _need(sc, np.float32, "scalars")
+    n = p.size
+    assert g.size == n and w.size == n and sc.size == 8
+    if kind not in (PACKED_E4, PACKED_F16):
+        raise ValueError("kind must be PACKED_E4 or PACKED_F16")
+    return int(_load().oracle_step_packed(int(kind), _ptr(p, _f32p), _ptr(g, _f32p),
+                                          _ptr(w, _u32p), n, _ptr(sc, _f32p)))
+
+
+def step_blockwise(p, g, m_code, m_absmax, v_code, v_absmax, qmap_m, qmap_v, p_out, sc):
+    """Codes, absmax arrays and p_out (uint16 holding bfloat16 bits) are written
+    in place; p is read only.  Returns the non-finite count."""
+    _need(p, np.float32, "p")
+    _need(g, np.float32, "g")
+    _need(m_code, np.uint8, "m_code")
+    _need(v_code, np.uint8, "v_code")
+    _need(m_absmax, np.float32, "m_absmax")
+    _need(v_absmax, np.float32, "v_absmax")
+    _need(qmap_m, np.float32, "qmap_m")
+    _need(qmap_v, np.float32, "qmap_v")
+    _need(p_out, np.uint16, "p_out")
+    _need(sc, np.float32, "scalars")
+    n = p.size
+    if n % BLOCK:
+        raise ValueError("blockwise length must be a multiple of 2048")
+    nb = n // BLOCK
+    assert g.size == n and m_code.size == n and v_code.size == n and p_out.size == n
+    assert m_absmax.size == nb and v_absmax.size == nb
+    assert qmap_m.size == 256 and qmap_v.size == 256
+    r = _load().oracle_step_blockwise(
+        _ptr(p, _f32p), _ptr(g, _f32p), _ptr(m_code, _u8p), _ptr(m_absmax, _f32p),
+        _ptr(v_code, _u8p), _ptr(v_absmax, _f32p), _ptr(qmap_m, _f32p), _ptr(qmap_v, _f32p),
+        _ptr(p_out, _u16p), n, _ptr(sc, _f32p))
+    return int(r)
+
+
+def search_codes(qmap, c):
+    """Map entry chosen for each normalised value c (midpoint search alone)."""
+    _need(qmap, np.float32, "qmap")
+    c = np.ascontiguousarray(c, dtype=np.float32)
+    out = np.empty(c.shape, np.uint8)
+    _load().oracle_search_codes(_ptr(qmap, _f32p), _ptr(c, _f32p), _ptr(out, _u8p), c.size)
+    return out
+
+
+def num_threads():
+    return int(_load().oracle_num_threads())
+
+
+def e4_bias():
+    return int(_load().oracle_e4_bias())

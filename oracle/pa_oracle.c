@@ -1,0 +1,413 @@
+/*
+ * pa_oracle.c -- plain, slow, CPU oracle for the packed-AdamW step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file; only the test suite, the smoke check and the benchmark's
+ * cpu_baseline leg use it.  It shares no code, header, table or constant
+ * generator with the HIP kernels.
+ *
+ * What it computes, and where each piece comes from:
+ *
+ *  - The state word (one uint32 per FP32 parameter; low half a signed finite
+ *    E4M11 first moment, high half an unsigned finite E4M12 uncorrected RMS;
+ *    no shadow moments, block scales or stochastic rounding):
+ *    "Packed AdamW Reference" README, introduction (canonical format);
+ *    "Packed AdamW / Reference / v1.0.0" project page, Release scope.
+ *  - The update order (decode, square the RMS, new moments, FP32 AdamW step
+ *    with the new unquantised moments, pack afterwards): same two passages.
+ *  - The AdamW recurrence and the decoupled-decay update: TurboAdam package
+ *    page, "The AdamW update remains AdamW" equation block.
+ *  - The left-to-right FP32 operation sequence, the host-side scalars held
+ *    in double precision, and the whole blockwise 8-bit mode (2048-element
+ *    blocks, absmax per block, nearest entry of an ascending 256-point map
+ *    through midpoints, BF16 parameter output): KBench task
+ *    "quantized-optimizer-state", environment reference, routines
+ *    `quantized_adamw_step` and `_requantise`.
+ *
+ * Readings where the pages are silent (kept here as named constants):
+ *  - ORACLE_E4_BIAS = 15 for both E4 lanes, IEEE-style gradual underflow at
+ *    exponent field 0, every exponent field finite (no Inf/NaN codes),
+ *    sign|exponent|mantissa from the most significant bit down.
+ *    The bias itself is a reading: parity unpinned.
+ *  - Rounding is to nearest, ties to the even code; |x| at or above the
+ *    largest finite value saturates to it (+-Inf too).
+ *  - NaN encodes as code 0 in an E4 lane.  The RMS lane maps every negative
+ *    input, -0 included, to code 0.  The first-moment lane keeps the sign of
+ *    zero.
+ *  - Binary16 lanes and the BF16 parameter output follow IEEE
+ *    round-to-nearest-even with overflow to Inf.
+ *  - A block whose new moment holds a NaN has a NaN absmax; every code in it
+ *    is then 255, because the midpoint search orders NaN above every number,
+ *    as the page's bucketize does.
+ *
+ * Arithmetic: every float operation is one IEEE binary32 operation rounded to
+ * nearest even (the build uses SSE arithmetic, -ffp-contract=off, no fast
+ * math), sqrtf and division are correctly rounded, denormals are kept.
+ * Codec tables are built in double precision, in which every value of every
+ * lane is exact.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_E4_BIAS 15
+#define ORACLE_BLOCK 2048
+
+/* ---------------------------------------------------------------------- */
+/* Codec tables.                                                           */
+/* ---------------------------------------------------------------------- */
+
+/* Non-negative magnitudes in ascending code order.  Each table ends with the
+ * largest finite value; the binary16 and bfloat16 tables carry one more entry
+ * standing for Inf, placed at the next power of two so that the usual
+ * IEEE overflow threshold (largest finite plus half an ulp, ties to even)
+ * falls out of the same nearest-entry rule. */
+static double tab_m_e4[0x8000];     /* E4M11 magnitudes, codes 0x0000..0x7FFF */
+static double tab_r_e4[0x10000];    /* E4M12 values,     codes 0x0000..0xFFFF */
+static double tab_h[0x7C01];        /* binary16 magnitudes 0x0000..0x7BFF, 0x7C00 = Inf */
+static double tab_bf[0x7F81];       /* bfloat16 magnitudes 0x0000..0x7F7F, 0x7F80 = Inf */
+static int tables_ready = 0;
+
+/* Value of a sign-less mini float with `ebits` exponent bits, `mbits`
+ * mantissa bits and exponent bias `bias`: exponent field 0 is the subnormal
+ * binade f * 2^(1-bias-mbits); otherwise (2^mbits + f) * 2^(e-bias-mbits). */
+static double minifloat_value(unsigned code, int mbits, int bias) {
+    unsigned e = code >> mbits;
+    unsigned f = code & ((1u << mbits) - 1u);
+    if (e == 0) return ldexp((double)f, 1 - bias - mbits);
+    return ldexp((double)((1u << mbits) + f), (int)e - bias - mbits);
+}
+
+static void build_tables(void) {
+    if (tables_ready) return;
+    for (unsigned c = 0; c < 0x8000; ++c) tab_m_e4[c] = minifloat_value(c, 11, ORACLE_E4_BIAS);
+    for (unsigned c = 0; c < 0x10000; ++c) tab_r_e4[c] = minifloat_value(c, 12, ORACLE_E4_BIAS);
+    for (unsigned c = 0; c < 0x7C00; ++c) tab_h[c] = minifloat_value(c, 10, 15);
+    tab_h[0x7C00] = 65536.0;                       /* 2^16: Inf as a rounding target */
+    for (unsigned c = 0; c < 0x7F80; ++c) tab_bf[c] = minifloat_value(c, 7, 127);
+    tab_bf[0x7F80] = ldexp(1.0, 128);              /* 2^128: Inf as a rounding target */
+    tables_ready = 1;
+}
+
+/* Nearest entry of an ascending table to a >= 0: the bracketing pair
+ * tab[k] <= a < tab[k+1] is found by bisection, then a is compared with the
+ * pair's exact midpoint (exact in double: both ends have at most 24
+ * significant bits).  Below the midpoint gives k, above gives k+1, on it
+ * gives whichever of the two codes is even.  a at or past the last entry
+ * gives the last code. */
+static unsigned nearest_code(const double* tab, unsigned ncodes, double a) {
+    if (a >= tab[ncodes - 1]) return ncodes - 1;
+    unsigned lo = 0, hi = ncodes - 1;             /* tab[lo] <= a < tab[hi] */
+    while (hi - lo > 1) {
+        unsigned mid = lo + (hi - lo) / 2;
+        if (tab[mid] <= a) lo = mid; else hi = mid;
+    }
+    double midpoint = 0.5 * (tab[lo] + tab[lo + 1]);
+    if (a < midpoint) return lo;
+    if (a > midpoint) return lo + 1;
+    return (lo % 2 == 0) ? lo : lo + 1;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Lane codecs.                                                            */
+/* ---------------------------------------------------------------------- */
+
+/* E4M11 first-moment lane: bit 15 sign, bits 14..11 exponent, 10..0 mantissa. */
+float oracle_decode_m_e4(uint16_t code) {
+    build_tables();
+    double mag = tab_m_e4[code & 0x7FFF];
+    return (float)((code & 0x8000) ? -mag : mag);
+}
+
+uint16_t oracle_encode_m_e4(float x) {
+    build_tables();
+    if (isnan(x)) return 0;
+    unsigned sign = signbit(x) ? 0x8000u : 0u;
+    double a = fabs((double)x);                   /* +-Inf lands on the last entry */
+    return (uint16_t)(sign | nearest_code(tab_m_e4, 0x8000, a));
+}
+
+/* E4M12 RMS lane: no sign, bits 15..12 exponent, 11..0 mantissa. */
+float oracle_decode_r_e4(uint16_t code) {
+    build_tables();
+    return (float)tab_r_e4[code];
+}
+
+uint16_t oracle_encode_r_e4(float x) {
+    build_tables();
+    if (isnan(x) || signbit(x)) return 0;         /* negative, -0 and NaN -> 0 */
+    return (uint16_t)nearest_code(tab_r_e4, 0x10000, (double)x);
+}
+
+/* IEEE binary16: bit 15 sign, 5 exponent bits (bias 15), 10 mantissa bits. */
+float oracle_decode_f16(uint16_t code) {
+    build_tables();
+    unsigned mag = code & 0x7FFF;
+    double v;
+    if (mag < 0x7C00) v = tab_h[mag];
+    else if (mag == 0x7C00) v = INFINITY;
+    else v = NAN;
+    return (float)((code & 0x8000) ? -v : v);
+}
+
+uint16_t oracle_encode_f16(float x) {
+    build_tables();
+    unsigned sign = signbit(x) ? 0x8000u : 0u;
+    if (isnan(x)) return (uint16_t)(sign | 0x7E00u);
+    return (uint16_t)(sign | nearest_code(tab_h, 0x7C01, fabs((double)x)));
+}
+
+/* bfloat16 (the parameter output of the blockwise mode). */
+uint16_t oracle_encode_bf16(float x) {
+    build_tables();
+    unsigned sign = signbit(x) ? 0x8000u : 0u;
+    if (isnan(x)) return (uint16_t)(sign | 0x7FC0u);
+    return (uint16_t)(sign | nearest_code(tab_bf, 0x7F81, fabs((double)x)));
+}
+
+/* Batch forms, for tests. */
+void oracle_encode_batch(int lane, const float* x, uint16_t* out, size_t n) {
+    build_tables();
+    ptrdiff_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < (ptrdiff_t)n; ++i) {
+        switch (lane) {
+            case 0: out[i] = oracle_encode_m_e4(x[i]); break;
+            case 1: out[i] = oracle_encode_r_e4(x[i]); break;
+            case 2: out[i] = oracle_encode_f16(x[i]); break;
+            default: out[i] = oracle_encode_bf16(x[i]); break;
+        }
+    }
+}
+
+void oracle_decode_batch(int lane, const uint16_t* c, float* out, size_t n) {
+    build_tables();
+    for (size_t i = 0; i < n; ++i) {
+        switch (lane) {
+            case 0: out[i] = oracle_decode_m_e4(c[i]); break;
+            case 1: out[i] = oracle_decode_r_e4(c[i]); break;
+            default: out[i] = oracle_decode_f16(c[i]); break;
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------- */
+/* Scalars.                                                                */
+/* ---------------------------------------------------------------------- */
+
+/* The per-call scalars.  The KBench reference holds lr, the betas, eps, wd,
+ * the bias corrections and their quotients as double-precision host numbers
+ * and meets FP32 tensors with them, so each is formed in double and rounded
+ * to binary32 once, at the point where it meets a tensor.
+ * Layout: [0] beta1, [1] 1-beta1, [2] beta2, [3] 1-beta2,
+ *         [4] bc2 = 1-beta2^t, [5] lr/bc1 with bc1 = 1-beta1^t,
+ *         [6] 1-lr*wd, [7] eps. */
+void oracle_scalars(double lr, double beta1, double beta2, double eps, double wd,
+                    long long step, float out[8]) {
+    double bc1 = 1.0 - pow(beta1, (double)step);
+    double bc2 = 1.0 - pow(beta2, (double)step);
+    out[0] = (float)beta1;
+    out[1] = (float)(1.0 - beta1);
+    out[2] = (float)beta2;
+    out[3] = (float)(1.0 - beta2);
+    out[4] = (float)bc2;
+    out[5] = (float)(lr / bc1);
+    out[6] = (float)(1.0 - lr * wd);
+    out[7] = (float)eps;
+}
+
+/* ---------------------------------------------------------------------- */
+/* The FP32 AdamW element update (shared by every mode of the oracle).     */
+/* ---------------------------------------------------------------------- */
+
+typedef struct {
+    float m1, v1, p1;
+} oracle_elem;
+
+/* New moments from the prior ones, then the bias-corrected step with
+ * decoupled decay, in the order the KBench reference writes it:
+ *   m' = beta1*m + (1-beta1)*g
+ *   v' = beta2*v + ((1-beta2)*g)*g
+ *   denom = sqrt(v'/bc2) + eps
+ *   upd = ((lr/bc1)*m') / denom
+ *   p' = p*(1-lr*wd) - upd
+ * which equals the TurboAdam equation block in exact arithmetic. */
+static oracle_elem adamw_element(float p, float g, float m, float v, const float* s) {
+    oracle_elem r;
+    float beta1 = s[0], one_m_beta1 = s[1], beta2 = s[2], one_m_beta2 = s[3];
+    float bc2 = s[4], lr_over_bc1 = s[5], decay = s[6], eps = s[7];
+    float a = beta1 * m;
+    float b = one_m_beta1 * g;
+    r.m1 = a + b;
+    float c = beta2 * v;
+    float d = one_m_beta2 * g;
+    float e = d * g;
+    r.v1 = c + e;
+    float q = r.v1 / bc2;
+    float denom = sqrtf(q) + eps;
+    float num = lr_over_bc1 * r.m1;
+    float upd = num / denom;
+    float kept = p * decay;
+    r.p1 = kept - upd;
+    return r;
+}
+
+static int elem_nonfinite(const oracle_elem* e) {
+    return !isfinite(e->p1) || !isfinite(e->m1) || !isfinite(e->v1);
+}
+
+/* ---------------------------------------------------------------------- */
+/* Elementwise modes.                                                      */
+/* ---------------------------------------------------------------------- */
+
+/* Plain FP32 AdamW (the comparison mode with two FP32 moment tensors). */
+unsigned long long oracle_step_fp32(float* p, const float* g, float* m, float* v,
+                                    size_t n, const float s[8]) {
+    unsigned long long bad = 0;
+    ptrdiff_t i;
+#pragma omp parallel for schedule(static) reduction(+ : bad)
+    for (i = 0; i < (ptrdiff_t)n; ++i) {
+        oracle_elem e = adamw_element(p[i], g[i], m[i], v[i], s);
+        p[i] = e.p1;
+        m[i] = e.m1;
+        v[i] = e.v1;
+        bad += (unsigned long long)elem_nonfinite(&e);
+    }
+    return bad;
+}
+
+/* Packed modes: one uint32 word per parameter, first moment in the low half,
+ * RMS in the high half.  lane_kind 1 = E4M11/E4M12, 2 = binary16/binary16.
+ * Decode the prior state, square the RMS, update in FP32 with the new
+ * moments, and only then encode m' and sqrt(v') for the next step. */
+unsigned long long oracle_step_packed(int lane_kind, float* p, const float* g, uint32_t* w,
+                                      size_t n, const float s[8]) {
+    build_tables();
+    unsigned long long bad = 0;
+    ptrdiff_t i;
+#pragma omp parallel for schedule(static) reduction(+ : bad)
+    for (i = 0; i < (ptrdiff_t)n; ++i) {
+        uint16_t lo = (uint16_t)(w[i] & 0xFFFFu);
+        uint16_t hi = (uint16_t)(w[i] >> 16);
+        float m, r;
+        if (lane_kind == 1) {
+            m = oracle_decode_m_e4(lo);
+            r = oracle_decode_r_e4(hi);
+        } else {
+            m = oracle_decode_f16(lo);
+            r = oracle_decode_f16(hi);
+        }
+        float v = r * r;
+        oracle_elem e = adamw_element(p[i], g[i], m, v, s);
+        float r1 = sqrtf(e.v1);
+        uint16_t mc, rc;
+        if (lane_kind == 1) {
+            mc = oracle_encode_m_e4(e.m1);
+            rc = oracle_encode_r_e4(r1);
+        } else {
+            mc = oracle_encode_f16(e.m1);
+            rc = oracle_encode_f16(r1);
+        }
+        p[i] = e.p1;
+        w[i] = ((uint32_t)rc << 16) | (uint32_t)mc;
+        bad += (unsigned long long)elem_nonfinite(&e);
+    }
+    return bad;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Blockwise 8-bit mode (KBench quantized-optimizer-state reference).      */
+/* ---------------------------------------------------------------------- */
+
+/* Index of the first midpoint that is not below c, i.e. the number of
+ * midpoints strictly below c (an exact tie goes to the lower map entry).
+ * NaN is ordered above every number, as a sorted search orders it. */
+static unsigned search_code(const float* mid, unsigned nmid, float c) {
+    if (isnan(c)) return nmid;
+    unsigned k = 0;
+    while (k < nmid && mid[k] < c) ++k;
+    return k;
+}
+
+/* Requantise one block of new moments: absmax of the block (NaN if any
+ * element is NaN), normalise by the absmax clamped below at the binary32
+ * value of 1e-30, and pick each element's map entry through the 255 FP32
+ * midpoints.  The stored absmax is the unclamped one. */
+static float requantise_block(const float* x, const float* qmap, uint8_t* code, size_t len) {
+    float mid[255];
+    for (unsigned j = 0; j < 255; ++j) mid[j] = (qmap[j] + qmap[j + 1]) * 0.5f;
+    float amax = 0.0f;
+    int saw_nan = 0;
+    for (size_t i = 0; i < len; ++i) {
+        if (isnan(x[i])) saw_nan = 1;
+        float a = fabsf(x[i]);
+        if (a > amax) amax = a;
+    }
+    if (saw_nan) amax = NAN;
+    float floor_val = (float)1e-30;
+    float d = isnan(amax) ? amax : (amax < floor_val ? floor_val : amax);
+    for (size_t i = 0; i < len; ++i) {
+        float c = x[i] / d;
+        code[i] = (uint8_t)search_code(mid, 255, c);
+    }
+    return amax;
+}
+
+/* One blockwise step over n parameters (n a multiple of 2048).  Parameters
+ * are read as FP32 and left untouched; the updated parameters go to p_out as
+ * BF16.  m_code/v_code and the per-block absmax arrays are replaced by the
+ * requantised new moments.  qmap_m and qmap_v are ascending 256-entry maps.
+ * Returns the number of elements whose p', m' or v' is non-finite, or
+ * (unsigned long long)-1 if n is not a multiple of the block length. */
+unsigned long long oracle_step_blockwise(const float* p, const float* g,
+                                         uint8_t* m_code, float* m_absmax,
+                                         uint8_t* v_code, float* v_absmax,
+                                         const float* qmap_m, const float* qmap_v,
+                                         uint16_t* p_out, size_t n, const float s[8]) {
+    build_tables();
+    if (n % ORACLE_BLOCK != 0) return (unsigned long long)-1;
+    size_t nb = n / ORACLE_BLOCK;
+    unsigned long long bad = 0;
+    ptrdiff_t b;
+#pragma omp parallel for schedule(static) reduction(+ : bad)
+    for (b = 0; b < (ptrdiff_t)nb; ++b) {
+        float m1[ORACLE_BLOCK], v1[ORACLE_BLOCK];
+        size_t base = (size_t)b * ORACLE_BLOCK;
+        float am = m_absmax[b], av = v_absmax[b];
+        for (size_t i = 0; i < ORACLE_BLOCK; ++i) {
+            float m = qmap_m[m_code[base + i]] * am;
+            float v = qmap_v[v_code[base + i]] * av;
+            oracle_elem e = adamw_element(p[base + i], g[base + i], m, v, s);
+            m1[i] = e.m1;
+            v1[i] = e.v1;
+            p_out[base + i] = oracle_encode_bf16(e.p1);
+            bad += (unsigned long long)elem_nonfinite(&e);
+        }
+        m_absmax[b] = requantise_block(m1, qmap_m, m_code + base, ORACLE_BLOCK);
+        v_absmax[b] = requantise_block(v1, qmap_v, v_code + base, ORACLE_BLOCK);
+    }
+    return bad;
+}
+
+/* Midpoint search alone, for tests against a library search. */
+void oracle_search_codes(const float* qmap, const float* c, uint8_t* code, size_t n) {
+    float mid[255];
+    for (unsigned j = 0; j < 255; ++j) mid[j] = (qmap[j] + qmap[j + 1]) * 0.5f;
+    for (size_t i = 0; i < n; ++i) code[i] = (uint8_t)search_code(mid, 255, c[i]);
+}
+
+/* Threads the parallel loops use. */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+int oracle_block_len(void) { return ORACLE_BLOCK; }
+int oracle_e4_bias(void) { return ORACLE_E4_BIAS; }
