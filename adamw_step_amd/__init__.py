@@ -1,0 +1,249 @@
+"""Python binding of libpa.so, the gfx950 packed-AdamW step library.
+
+Argument marshalling only: every step of the update runs in the library's
+HIP kernels.  PyTorch supplies device memory and the current stream.  If the
+library is not built, importing works but every call raises; there is no
+other path.
+
+Functions keep the C names (see include/pa.h):
+
+    pa_step(mode, params, grads, state, hyper, step, stream=None)
+    pa_step_list(mode, params, grads, states, hyper, step, stream=None)
+    pa_state_bytes(mode, n), pa_format_info(mode), pa_status_string(rc)
+    pa_debug_codec(lane, dir, inp, out, stream=None), pa_release_plans()
+
+``state`` is, per mode: PA_PACKED_E4 / PA_PACKED_FP16 -> an int32 (or
+uint32) tensor of words; PA_FP32 -> (m, v); PA_BLOCKWISE8 ->
+(m_code, m_absmax, v_code, v_absmax, qmap_m, qmap_v, p_out_bf16).
+``hyper`` is a mapping with lr, beta1, beta2, eps, weight_decay and an
+optional ``nonfinite`` int64 device tensor of one element.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpa.so")
+
+PA_FP32, PA_PACKED_E4, PA_PACKED_FP16, PA_BLOCKWISE8 = 0, 1, 2, 3
+MODES = {"fp32": PA_FP32, "e4": PA_PACKED_E4, "fp16": PA_PACKED_FP16, "blockwise8": PA_BLOCKWISE8}
+BLOCK = 2048
+
+PA_OK, PA_ERR_ARG, PA_ERR_ALIGN, PA_ERR_SHAPE, PA_ERR_ALIAS, PA_ERR_DEVICE, PA_ERR_NOMEM = 0, -1, -2, -3, -4, -5, -6
+
+
+class PAError(RuntimeError):
+    def __init__(self, rc, msg):
+        super().__init__(f"{msg} (status {rc})")
+        self.rc = rc
+
+
+class Hyper(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double),
+                ("nonfinite", ctypes.c_void_p)]
+
+
+class Fp32State(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_void_p), ("v", ctypes.c_void_p)]
+
+
+class BlockwiseState(ctypes.Structure):
+    _fields_ = [("m_code", ctypes.c_void_p), ("m_absmax", ctypes.c_void_p),
+                ("v_code", ctypes.c_void_p), ("v_absmax", ctypes.c_void_p),
+                ("qmap_m", ctypes.c_void_p), ("qmap_v", ctypes.c_void_p),
+                ("p_out_bf16", ctypes.c_void_p)]
+
+
+class Format(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int), ("lanes", ctypes.c_int),
+                ("m_sign_bits", ctypes.c_int), ("m_exp_bits", ctypes.c_int),
+                ("m_mant_bits", ctypes.c_int), ("m_exp_bias", ctypes.c_int),
+                ("r_sign_bits", ctypes.c_int), ("r_exp_bits", ctypes.c_int),
+                ("r_mant_bits", ctypes.c_int), ("r_exp_bias", ctypes.c_int),
+                ("m_max", ctypes.c_double), ("m_min_normal", ctypes.c_double),
+                ("m_min_subnormal", ctypes.c_double), ("r_max", ctypes.c_double),
+                ("r_min_normal", ctypes.c_double), ("r_min_subnormal", ctypes.c_double),
+                ("block", ctypes.c_int)]
+
+
+EXPORTS = ("pa_step", "pa_step_list", "pa_state_bytes", "pa_format_info", "pa_status_string",
+           "pa_last_hip_error", "pa_release_plans", "pa_debug_codec")
+
+_lib = None
+
+
+def lib():
+    """Load libpa.so (after torch, so both share one HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m adamw_step_amd.build` "
+                           "(there is no fallback path)")
+    import torch  # noqa: F401  -- loads the HIP runtime that the library binds to
+    L = ctypes.CDLL(LIB_PATH)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    L.pa_step.argtypes = [ctypes.c_int, vp, vp, vp, sz, ctypes.POINTER(Hyper), ctypes.c_longlong, vp]
+    L.pa_step.restype = ctypes.c_int
+    L.pa_step_list.argtypes = [ctypes.c_int, sz, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                               ctypes.POINTER(sz), ctypes.POINTER(Hyper), ctypes.c_longlong, vp]
+    L.pa_step_list.restype = ctypes.c_int
+    L.pa_state_bytes.argtypes = [ctypes.c_int, sz]
+    L.pa_state_bytes.restype = sz
+    L.pa_format_info.argtypes = [ctypes.c_int, ctypes.POINTER(Format)]
+    L.pa_format_info.restype = ctypes.c_int
+    L.pa_status_string.argtypes = [ctypes.c_int]
+    L.pa_status_string.restype = ctypes.c_char_p
+    L.pa_last_hip_error.restype = ctypes.c_int
+    L.pa_release_plans.restype = None
+    L.pa_debug_codec.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, sz, vp]
+    L.pa_debug_codec.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(rc):
+    if rc != PA_OK:
+        L = lib()
+        msg = L.pa_status_string(rc).decode()
+        if rc == PA_ERR_DEVICE:
+            msg += f"; hipError {L.pa_last_hip_error()}"
+        raise PAError(rc, msg)
+
+
+def _mode(mode):
+    return MODES[mode] if isinstance(mode, str) else int(mode)
+
+
+def _ptr(t):
+    return None if t is None else int(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return int(torch.cuda.current_stream().cuda_stream)
+    return int(getattr(stream, "cuda_stream", stream))
+
+
+def _hyper(h):
+    nf = h.get("nonfinite")
+    return Hyper(float(h["lr"]), float(h["beta1"]), float(h["beta2"]), float(h["eps"]),
+                 float(h["weight_decay"]), _ptr(nf) if nf is not None else None)
+
+
+def _tensor_ok(t, what):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+        raise TypeError(f"{what} must be a contiguous device tensor")
+    if t.is_sparse:
+        raise TypeError(f"{what} must be dense")
+
+
+def _check_pg(p, g):
+    import torch
+    _tensor_ok(p, "params")
+    _tensor_ok(g, "grads")
+    if p.dtype != torch.float32 or g.dtype != torch.float32:
+        raise TypeError("params and grads must be float32")
+    if g.numel() != p.numel() or g.device != p.device:
+        raise ValueError("grads must match params in size and device")
+
+
+def _state_arg(mode, p, state, keep):
+    """Host-side argument for one tensor's state; `keep` holds ctypes objects alive."""
+    import torch
+    n = p.numel()
+    if mode in (PA_PACKED_E4, PA_PACKED_FP16):
+        _tensor_ok(state, "state")
+        if state.dtype not in (torch.int32, torch.uint32) or state.numel() != n or state.device != p.device:
+            raise TypeError("packed state must be a 32-bit tensor with one word per parameter")
+        return _ptr(state)
+    if mode == PA_FP32:
+        m, v = state
+        for t, nm in ((m, "m"), (v, "v")):
+            _tensor_ok(t, nm)
+            if t.dtype != torch.float32 or t.numel() != n or t.device != p.device:
+                raise TypeError(f"FP32 state {nm} must be float32 with one value per parameter")
+        st = Fp32State(_ptr(m), _ptr(v))
+        keep.append(st)
+        return ctypes.addressof(st)
+    if mode == PA_BLOCKWISE8:
+        mc, ma, vc, va, qm, qv, pout = state
+        for t, nm in ((mc, "m_code"), (ma, "m_absmax"), (vc, "v_code"), (va, "v_absmax"),
+                      (qm, "qmap_m"), (qv, "qmap_v"), (pout, "p_out")):
+            _tensor_ok(t, nm)
+            if t.device != p.device:
+                raise ValueError(f"{nm} is on another device")
+        st = BlockwiseState(_ptr(mc), _ptr(ma), _ptr(vc), _ptr(va), _ptr(qm), _ptr(qv), _ptr(pout))
+        keep.append(st)
+        return ctypes.addressof(st)
+    raise ValueError(f"unknown mode {mode}")
+
+
+def pa_step(mode, params, grads, state, hyper, step, stream=None):
+    """One tensor, updated in place (see include/pa.h)."""
+    mode = _mode(mode)
+    _check_pg(params, grads)
+    keep = []
+    st = _state_arg(mode, params, state, keep)
+    h = _hyper(hyper)
+    _check(lib().pa_step(mode, _ptr(params), _ptr(grads), st, params.numel(), ctypes.byref(h),
+                         int(step), _stream(stream)))
+
+
+def pa_step_list(mode, params, grads, states, hyper, step, stream=None):
+    """A list of tensors sharing one hyperparameter set and step, one launch."""
+    mode = _mode(mode)
+    k = len(params)
+    if len(grads) != k or len(states) != k:
+        raise ValueError("params, grads and states must have the same length")
+    keep = []
+    P = (ctypes.c_void_p * k)()
+    G = (ctypes.c_void_p * k)()
+    S = (ctypes.c_void_p * k)()
+    N = (ctypes.c_size_t * k)()
+    for i in range(k):
+        _check_pg(params[i], grads[i])
+        if params[i].device != params[0].device:
+            raise ValueError("all tensors of one call must be on one device")
+        P[i], G[i] = _ptr(params[i]), _ptr(grads[i])
+        S[i] = _state_arg(mode, params[i], states[i], keep)
+        N[i] = params[i].numel()
+    h = _hyper(hyper)
+    _check(lib().pa_step_list(mode, k, P, G, S, N, ctypes.byref(h), int(step), _stream(stream)))
+
+
+def pa_state_bytes(mode, n):
+    return int(lib().pa_state_bytes(_mode(mode), int(n)))
+
+
+def pa_format_info(mode):
+    f = Format()
+    _check(lib().pa_format_info(_mode(mode), ctypes.byref(f)))
+    return {name: getattr(f, name) for name, _ in Format._fields_}
+
+
+def pa_status_string(rc):
+    return lib().pa_status_string(int(rc)).decode()
+
+
+def pa_last_hip_error():
+    return int(lib().pa_last_hip_error())
+
+
+def pa_release_plans():
+    lib().pa_release_plans()
+
+
+def pa_debug_codec(lane, direction, inp, out, stream=None):
+    """lane 0 E4M11, 1 E4M12, 2 binary16; direction 0 encode (float32 -> uint16
+    held in an int16 tensor), 1 decode."""
+    _tensor_ok(inp, "input")
+    _tensor_ok(out, "output")
+    if inp.numel() != out.numel():
+        raise ValueError("input and output sizes differ")
+    _check(lib().pa_debug_codec(int(lane), int(direction), _ptr(inp), _ptr(out), inp.numel(),
+                                _stream(stream)))

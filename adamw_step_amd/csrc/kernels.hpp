@@ -1,0 +1,368 @@
+// kernels.hpp -- gfx950 kernels of the packed-AdamW step.
+//
+// Elementwise modes (packed E4, packed FP16, FP32): one persistent launch
+// walks a table of tensors cut into 4096-element tiles.  Each thread moves
+// 16-byte vectors of parameter, gradient and state (one read and one write
+// per word), keeps the whole update in registers, and never touches LDS.
+// The table is read with scalar loads; a workgroup's tensor cursor only moves
+// forward, so finding the tensor of a tile costs nothing per element.
+//
+// Blockwise 8-bit mode: a persistent grid over 2048-element blocks, one
+// 256-thread workgroup per block at a time; the code maps and their
+// midpoints sit in LDS, the block absmax is a wavefront shuffle reduction
+// followed by a four-entry LDS reduction.
+//
+// The FP32 update follows the KBench quantized-optimizer-state reference
+// (`quantized_adamw_step`) left to right, one IEEE binary32 operation at a
+// time: no contraction into FMA (this file is compiled with contraction
+// off), correctly rounded division and square root, denormals kept.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "codec.hpp"
+
+#pragma clang fp contract(off)
+
+namespace pa {
+
+// The eight binary32 scalars of one call (formed on the host in double,
+// each rounded once).
+struct Scalars {
+  float beta1, one_m_beta1, beta2, one_m_beta2;
+  float bc2, lr_over_bc1, decay, eps;
+};
+
+// One tensor of an elementwise launch.  Every buffer of a tensor shares one
+// 16-byte phase; `phase` is that phase in elements, so element i sits at
+// virtual index i + phase and virtual indices 4k..4k+3 form one aligned
+// 16-byte vector.
+struct Entry {
+  float* p;
+  const float* g;
+  void* s0;          // packed words, or the FP32 first moment
+  float* s1;         // FP32 second moment (FP32 mode only)
+  long long n;       // elements
+  long long tile0;   // first global tile of this tensor
+  int phase;
+  int pad_;
+};
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+constexpr int kTile = kThreads * 4 * kUnroll;   // elements per tile
+constexpr int kBlock = 2048;                    // blockwise quantisation block
+
+enum { kModeFp32 = 0, kModeE4 = 1, kModeF16 = 2 };
+
+// New moments and the FP32 step with decoupled decay.
+__device__ __forceinline__ void adamw(float p, float g, float m, float v, const Scalars& s,
+                                      float& p1, float& m1, float& v1) {
+  m1 = s.beta1 * m + s.one_m_beta1 * g;
+  v1 = s.beta2 * v + (s.one_m_beta2 * g) * g;
+  const float denom = __fsqrt_rn(__fdiv_rn(v1, s.bc2)) + s.eps;
+  const float upd = __fdiv_rn(s.lr_over_bc1 * m1, denom);
+  p1 = p * s.decay - upd;
+}
+
+__device__ __forceinline__ uint32_t nonfinite3(float a, float b, float c) {
+  return (__builtin_isfinite(a) && __builtin_isfinite(b) && __builtin_isfinite(c)) ? 0u : 1u;
+}
+
+// Packed modes: decode the prior word, update, encode m' and sqrt(v').
+template <int MODE>
+__device__ __forceinline__ uint32_t packed_elem(float& p, float g, uint32_t w, const Scalars& s,
+                                                uint32_t& bad) {
+  float m, r;
+  if constexpr (MODE == kModeE4) {
+    m = e4_decode_m(w);
+    r = e4_decode_r(w);
+  } else {
+    m = f16_decode(w);
+    r = f16_decode(w >> 16);
+  }
+  float p1, m1, v1;
+  adamw(p, g, m, r * r, s, p1, m1, v1);
+  bad += nonfinite3(p1, m1, v1);
+  p = p1;
+  const float r1 = __fsqrt_rn(v1);
+  if constexpr (MODE == kModeE4) {
+    return (e4_encode_r(r1) << 16) | e4_encode_m(m1);
+  } else {
+    return (f16_encode(r1) << 16) | f16_encode(m1);
+  }
+}
+
+__device__ __forceinline__ void fp32_elem(float& p, float g, float& m, float& v, const Scalars& s,
+                                          uint32_t& bad) {
+  float p1, m1, v1;
+  adamw(p, g, m, v, s, p1, m1, v1);
+  bad += nonfinite3(p1, m1, v1);
+  p = p1;
+  m = m1;
+  v = v1;
+}
+
+__device__ __forceinline__ float& lane(float4& v, int k) { return reinterpret_cast<float*>(&v)[k]; }
+__device__ __forceinline__ uint32_t& lane(uint4& v, int k) { return reinterpret_cast<uint32_t*>(&v)[k]; }
+
+// One element at index i of tensor e (ragged edges only).
+template <int MODE>
+__device__ __forceinline__ void scalar_elem(const Entry& e, long long i, const Scalars& s, uint32_t& bad) {
+  float p = e.p[i];
+  const float g = e.g[i];
+  if constexpr (MODE == kModeFp32) {
+    float* m = static_cast<float*>(e.s0);
+    float mm = m[i], vv = e.s1[i];
+    fp32_elem(p, g, mm, vv, s, bad);
+    m[i] = mm;
+    e.s1[i] = vv;
+  } else {
+    uint32_t* w = static_cast<uint32_t*>(e.s0);
+    w[i] = packed_elem<MODE>(p, g, w[i], s, bad);
+  }
+  e.p[i] = p;
+}
+
+// Tile `tile` (local to tensor e).
+template <int MODE>
+__device__ __forceinline__ void run_tile(const Entry& e, long long tile, const Scalars& s, uint32_t& bad) {
+  const long long v0 = tile * kTile;
+  const long long vend = e.n + e.phase;
+  const int tid = threadIdx.x;
+  if (v0 >= e.phase && v0 + kTile <= vend) {
+    // Whole tile inside the tensor: unguarded 16-byte vectors.
+    const long long q0 = v0 / 4 + tid;
+    float4* P = reinterpret_cast<float4*>(e.p - e.phase);
+    const float4* G = reinterpret_cast<const float4*>(e.g - e.phase);
+    if constexpr (MODE == kModeFp32) {
+      float4* M = reinterpret_cast<float4*>(static_cast<float*>(e.s0) - e.phase);
+      float4* V = reinterpret_cast<float4*>(e.s1 - e.phase);
+      float4 p[kUnroll], g[kUnroll], m[kUnroll], v[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const long long q = q0 + (long long)u * kThreads;
+        p[u] = P[q];
+        g[u] = G[q];
+        m[u] = M[q];
+        v[u] = V[q];
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) fp32_elem(lane(p[u], k), lane(g[u], k), lane(m[u], k), lane(v[u], k), s, bad);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const long long q = q0 + (long long)u * kThreads;
+        P[q] = p[u];
+        M[q] = m[u];
+        V[q] = v[u];
+      }
+    } else {
+      uint4* W = reinterpret_cast<uint4*>(static_cast<uint32_t*>(e.s0) - e.phase);
+      float4 p[kUnroll], g[kUnroll];
+      uint4 w[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const long long q = q0 + (long long)u * kThreads;
+        p[u] = P[q];
+        g[u] = G[q];
+        w[u] = W[q];
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) lane(w[u], k) = packed_elem<MODE>(lane(p[u], k), lane(g[u], k), lane(w[u], k), s, bad);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const long long q = q0 + (long long)u * kThreads;
+        P[q] = p[u];
+        W[q] = w[u];
+      }
+    }
+  } else {
+    // Ragged tile (first tile of a misaligned tensor, or the last one).
+    for (int u = 0; u < kUnroll; ++u) {
+      const long long vb = v0 + ((long long)u * kThreads + tid) * 4;
+      for (int k = 0; k < 4; ++k) {
+        const long long vi = vb + k;
+        if (vi >= e.phase && vi < vend) scalar_elem<MODE>(e, vi - e.phase, s, bad);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void flush_count(uint32_t bad, unsigned long long* counter) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) bad += __shfl_xor(bad, off, 64);
+  if ((threadIdx.x & 63) == 0 && bad != 0u) atomicAdd(counter, (unsigned long long)bad);
+}
+
+// Persistent multi-tensor launch.  table[count].tile0 holds the total tile
+// count (a sentinel), so the cursor never runs past the table.
+template <int MODE, bool COUNT>
+__global__ void __launch_bounds__(kThreads)
+elementwise_list(const Entry* __restrict__ table, long long total_tiles, Scalars s,
+                 unsigned long long* nonfinite) {
+  uint32_t bad = 0;
+  int t = 0;
+  for (long long tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
+    while (tile >= table[t + 1].tile0) ++t;
+    const Entry e = table[t];
+    run_tile<MODE>(e, tile - e.tile0, s, bad);
+  }
+  if constexpr (COUNT) flush_count(bad, nonfinite);
+}
+
+// Single tensor, its entry passed by value (no table in device memory).
+template <int MODE, bool COUNT>
+__global__ void __launch_bounds__(kThreads)
+elementwise_one(Entry e, long long total_tiles, Scalars s, unsigned long long* nonfinite) {
+  uint32_t bad = 0;
+  for (long long tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) run_tile<MODE>(e, tile, s, bad);
+  if constexpr (COUNT) flush_count(bad, nonfinite);
+}
+
+// ---------------------------------------------------------------------------
+// Blockwise 8-bit mode.
+
+struct BlockwiseArgs {
+  const float* p;
+  const float* g;
+  uint8_t* m_code;
+  float* m_absmax;
+  uint8_t* v_code;
+  float* v_absmax;
+  const float* qmap_m;
+  const float* qmap_v;
+  uint16_t* p_out;
+  long long nblocks;
+};
+
+// Number of midpoints strictly below c (ties go to the lower map entry);
+// NaN is ordered above every number.  mid[0..254] ascending.
+__device__ __forceinline__ uint32_t search_mid(const float* mid, float c) {
+  uint32_t k = 0;
+#pragma unroll
+  for (uint32_t step = 128; step >= 1; step >>= 1)
+    if (mid[k + step - 1] < c) k += step;
+  return (c != c) ? 255u : k;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, off, 64));
+  return x;
+}
+
+template <bool COUNT>
+__global__ void __launch_bounds__(kThreads)
+blockwise_kernel(BlockwiseArgs a, Scalars s, unsigned long long* nonfinite) {
+  __shared__ float lut_m[256], lut_v[256], mid_m[256], mid_v[256];
+  __shared__ uint32_t wave_max[2][kThreads / 64];
+  const int tid = threadIdx.x;
+  lut_m[tid] = a.qmap_m[tid];
+  lut_v[tid] = a.qmap_v[tid];
+  __syncthreads();
+  mid_m[tid] = tid < 255 ? (lut_m[tid] + lut_m[tid + 1]) * 0.5f : __builtin_inff();
+  mid_v[tid] = tid < 255 ? (lut_v[tid] + lut_v[tid + 1]) * 0.5f : __builtin_inff();
+  __syncthreads();
+
+  // The 1e-30 lower clamp of the normaliser, as a binary32 bit pattern.
+  const uint32_t floor_bits = __float_as_uint((float)1e-30);
+  uint32_t bad = 0;
+  for (long long b = blockIdx.x; b < a.nblocks; b += gridDim.x) {
+    const long long base = b * kBlock;
+    const float am = a.m_absmax[b];
+    const float av = a.v_absmax[b];
+    float m1[8], v1[8];
+    uint32_t mc[2], vc[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const long long e0 = base + h * 1024 + tid * 4;
+      const float4 P = *reinterpret_cast<const float4*>(a.p + e0);
+      const float4 G = *reinterpret_cast<const float4*>(a.g + e0);
+      mc[h] = *reinterpret_cast<const uint32_t*>(a.m_code + e0);
+      vc[h] = *reinterpret_cast<const uint32_t*>(a.v_code + e0);
+      uint32_t bf[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float m = lut_m[(mc[h] >> (8 * k)) & 0xFFu] * am;
+        const float v = lut_v[(vc[h] >> (8 * k)) & 0xFFu] * av;
+        float p1;
+        adamw(reinterpret_cast<const float*>(&P)[k], reinterpret_cast<const float*>(&G)[k], m, v, s, p1,
+              m1[h * 4 + k], v1[h * 4 + k]);
+        bad += nonfinite3(p1, m1[h * 4 + k], v1[h * 4 + k]);
+        bf[k] = bf16_encode(p1);
+      }
+      uint2 out;
+      out.x = bf[0] | (bf[1] << 16);
+      out.y = bf[2] | (bf[3] << 16);
+      *reinterpret_cast<uint2*>(a.p_out + e0) = out;
+    }
+    // Block absmax: on non-negative floats (and NaN with the sign cleared)
+    // the unsigned order of the bit patterns is the numeric order, with NaN
+    // above everything, so an integer max propagates NaN as the reference's
+    // amax does.
+    uint32_t xm = 0, xv = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      xm = max(xm, __float_as_uint(m1[k]) & 0x7FFFFFFFu);
+      xv = max(xv, __float_as_uint(v1[k]) & 0x7FFFFFFFu);
+    }
+    xm = wave_max_u32(xm);
+    xv = wave_max_u32(xv);
+    if ((tid & 63) == 0) {
+      wave_max[0][tid >> 6] = xm;
+      wave_max[1][tid >> 6] = xv;
+    }
+    __syncthreads();
+    uint32_t Am = wave_max[0][0], Av = wave_max[1][0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) {
+      Am = max(Am, wave_max[0][w]);
+      Av = max(Av, wave_max[1][w]);
+    }
+    __syncthreads();   // wave_max is rewritten by the next block
+    const float dm = __uint_as_float(max(Am, floor_bits));
+    const float dv = __uint_as_float(max(Av, floor_bits));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t cm = 0, cv = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        cm |= search_mid(mid_m, __fdiv_rn(m1[h * 4 + k], dm)) << (8 * k);
+        cv |= search_mid(mid_v, __fdiv_rn(v1[h * 4 + k], dv)) << (8 * k);
+      }
+      const long long e0 = base + h * 1024 + tid * 4;
+      *reinterpret_cast<uint32_t*>(a.m_code + e0) = cm;
+      *reinterpret_cast<uint32_t*>(a.v_code + e0) = cv;
+    }
+    if (tid == 0) {
+      a.m_absmax[b] = __uint_as_float(Am);
+      a.v_absmax[b] = __uint_as_float(Av);
+    }
+  }
+  if constexpr (COUNT) flush_count(bad, nonfinite);
+}
+
+// ---------------------------------------------------------------------------
+// Codec export for tests: every code of every lane, on the device.
+
+__global__ void __launch_bounds__(kThreads)
+codec_kernel(int lane_kind, int dir, const void* in, void* out, long long n) {
+  for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < n; i += (long long)gridDim.x * kThreads) {
+    if (dir == 0) {
+      const float x = static_cast<const float*>(in)[i];
+      uint32_t c = lane_kind == 0 ? e4_encode_m(x) : lane_kind == 1 ? e4_encode_r(x) : f16_encode(x);
+      static_cast<uint16_t*>(out)[i] = (uint16_t)c;
+    } else {
+      const uint32_t c = static_cast<const uint16_t*>(in)[i];
+      float x = lane_kind == 0 ? e4_decode_m(c) : lane_kind == 1 ? e4_decode_r(c << 16) : f16_decode(c);
+      static_cast<float*>(out)[i] = x;
+    }
+  }
+}
+
+}  // namespace pa

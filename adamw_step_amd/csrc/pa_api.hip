@@ -1,0 +1,537 @@
+// pa_api.hip -- host side of the C ABI declared in include/pa.h.
+//
+// Validation, the per-call scalars, the launch plan of a tensor list (a
+// device table cached per distinct pointer/size list) and the launches.
+// Nothing here computes the update; every element is handled by the kernels
+// in kernels.hpp.  There is no CPU path.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <list>
+#include <mutex>
+#include <vector>
+
+#include "../../include/pa.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_failed(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return PA_ERR_DEVICE;
+}
+
+// ---------------------------------------------------------------- scalars
+
+// lr, betas, eps and weight decay are host doubles; the bias corrections and
+// the quotients that meet FP32 tensors are formed in double and each is
+// rounded to binary32 once (the KBench reference computes them as Python
+// floats and applies them to FP32 tensors).
+int make_scalars(const pa_hyper* h, long long step, pa::Scalars* s) {
+  if (h == nullptr || step < 1) return PA_ERR_ARG;
+  const double lr = h->lr, b1 = h->beta1, b2 = h->beta2, eps = h->eps, wd = h->weight_decay;
+  if (!std::isfinite(lr) || !std::isfinite(eps) || !std::isfinite(wd) || !std::isfinite(b1) ||
+      !std::isfinite(b2))
+    return PA_ERR_ARG;
+  if (lr < 0.0 || eps < 0.0 || wd < 0.0) return PA_ERR_ARG;
+  if (!(b1 >= 0.0 && b1 < 1.0) || !(b2 >= 0.0 && b2 < 1.0)) return PA_ERR_ARG;
+  const double bc1 = 1.0 - std::pow(b1, (double)step);
+  const double bc2 = 1.0 - std::pow(b2, (double)step);
+  s->beta1 = (float)b1;
+  s->one_m_beta1 = (float)(1.0 - b1);
+  s->beta2 = (float)b2;
+  s->one_m_beta2 = (float)(1.0 - b2);
+  s->bc2 = (float)bc2;
+  s->lr_over_bc1 = (float)(lr / bc1);
+  s->decay = (float)(1.0 - lr * wd);
+  s->eps = (float)eps;
+  return PA_OK;
+}
+
+// ---------------------------------------------------------------- devices
+
+struct DeviceInfo {
+  int cus = 0;
+  int blocks_per_cu = 0;
+};
+
+std::mutex g_dev_mu;
+DeviceInfo g_dev[64];
+
+int device_info(int* dev_out, DeviceInfo* info) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_failed(e);
+  if (dev < 0 || dev >= 64) return PA_ERR_DEVICE;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DeviceInfo& d = g_dev[dev];
+  if (d.cus == 0) {
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_failed(e);
+    int per = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per, reinterpret_cast<const void*>(pa::elementwise_list<pa::kModeE4, false>), pa::kThreads, 0);
+    if (e != hipSuccess || per < 1) per = 4;
+    d.cus = cus;
+    d.blocks_per_cu = per;
+  }
+  *dev_out = dev;
+  *info = d;
+  return PA_OK;
+}
+
+long long grid_for(long long work_items, const DeviceInfo& d) {
+  const long long cap = (long long)d.cus * d.blocks_per_cu;
+  return std::max(1LL, std::min(work_items, cap));
+}
+
+// ---------------------------------------------------------------- checks
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;
+};
+
+Range range_of(const void* p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + bytes};
+}
+
+// True if any two of the ranges overlap (empty ranges never do).
+bool any_overlap(std::vector<Range>& r) {
+  r.erase(std::remove_if(r.begin(), r.end(), [](const Range& x) { return x.hi == x.lo; }), r.end());
+  std::sort(r.begin(), r.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+  for (size_t i = 1; i < r.size(); ++i)
+    if (r[i].lo < r[i - 1].hi) return true;
+  return false;
+}
+
+// One tensor of an elementwise mode: pointers of the tensor, checked.
+struct ElemTensor {
+  float* p;
+  const float* g;
+  void* s0;
+  float* s1;
+  size_t n;
+};
+
+int check_elem_tensor(int mode, float* p, const float* g, void* state, size_t n, ElemTensor* out,
+                      std::vector<Range>* ranges) {
+  out->p = p;
+  out->g = g;
+  out->n = n;
+  out->s0 = nullptr;
+  out->s1 = nullptr;
+  if (n == 0) return PA_OK;
+  if (p == nullptr || g == nullptr || state == nullptr) return PA_ERR_ARG;
+  if (mode == PA_FP32) {
+    const pa_fp32_state* st = static_cast<const pa_fp32_state*>(state);
+    if (st->m == nullptr || st->v == nullptr) return PA_ERR_ARG;
+    out->s0 = st->m;
+    out->s1 = st->v;
+  } else {
+    out->s0 = state;
+  }
+  const uintptr_t ph = reinterpret_cast<uintptr_t>(p) & 15u;
+  const void* bufs[4] = {p, g, out->s0, out->s1};
+  const int nb = mode == PA_FP32 ? 4 : 3;
+  for (int i = 0; i < nb; ++i) {
+    if (!aligned(bufs[i], 4)) return PA_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(bufs[i]) & 15u) != ph) return PA_ERR_ALIGN;
+  }
+  for (int i = 0; i < nb; ++i) ranges->push_back(range_of(bufs[i], n * 4));
+  return PA_OK;
+}
+
+pa::Entry make_entry(const ElemTensor& t, long long tile0) {
+  pa::Entry e;
+  e.p = t.p;
+  e.g = t.g;
+  e.s0 = t.s0;
+  e.s1 = t.s1;
+  e.n = (long long)t.n;
+  e.tile0 = tile0;
+  e.phase = (int)((reinterpret_cast<uintptr_t>(t.p) & 15u) >> 2);
+  e.pad_ = 0;
+  return e;
+}
+
+long long tiles_of(const pa::Entry& e) { return (e.n + e.phase + pa::kTile - 1) / pa::kTile; }
+
+// ---------------------------------------------------------------- launches
+
+template <int MODE>
+hipError_t launch_one(const pa::Entry& e, long long tiles, const pa::Scalars& s, unsigned long long* nf,
+                      hipStream_t st, const DeviceInfo& d) {
+  const dim3 grid((unsigned)grid_for(tiles, d)), block(pa::kThreads);
+  if (nf)
+    hipLaunchKernelGGL((pa::elementwise_one<MODE, true>), grid, block, 0, st, e, tiles, s, nf);
+  else
+    hipLaunchKernelGGL((pa::elementwise_one<MODE, false>), grid, block, 0, st, e, tiles, s, nf);
+  return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_list(const pa::Entry* table, long long tiles, const pa::Scalars& s, unsigned long long* nf,
+                       hipStream_t st, const DeviceInfo& d) {
+  const dim3 grid((unsigned)grid_for(tiles, d)), block(pa::kThreads);
+  if (nf)
+    hipLaunchKernelGGL((pa::elementwise_list<MODE, true>), grid, block, 0, st, table, tiles, s, nf);
+  else
+    hipLaunchKernelGGL((pa::elementwise_list<MODE, false>), grid, block, 0, st, table, tiles, s, nf);
+  return hipGetLastError();
+}
+
+hipError_t dispatch_one(int mode, const pa::Entry& e, long long tiles, const pa::Scalars& s,
+                        unsigned long long* nf, hipStream_t st, const DeviceInfo& d) {
+  switch (mode) {
+    case PA_FP32: return launch_one<pa::kModeFp32>(e, tiles, s, nf, st, d);
+    case PA_PACKED_E4: return launch_one<pa::kModeE4>(e, tiles, s, nf, st, d);
+    default: return launch_one<pa::kModeF16>(e, tiles, s, nf, st, d);
+  }
+}
+
+hipError_t dispatch_list(int mode, const pa::Entry* table, long long tiles, const pa::Scalars& s,
+                         unsigned long long* nf, hipStream_t st, const DeviceInfo& d) {
+  switch (mode) {
+    case PA_FP32: return launch_list<pa::kModeFp32>(table, tiles, s, nf, st, d);
+    case PA_PACKED_E4: return launch_list<pa::kModeE4>(table, tiles, s, nf, st, d);
+    default: return launch_list<pa::kModeF16>(table, tiles, s, nf, st, d);
+  }
+}
+
+// Blockwise: check one tensor's buffers.
+int check_blockwise(const float* p, const float* g, const void* state, size_t n, pa::BlockwiseArgs* a,
+                    std::vector<Range>* ranges) {
+  if (n == 0) return PA_OK;
+  if (p == nullptr || g == nullptr || state == nullptr) return PA_ERR_ARG;
+  const pa_blockwise_state* st = static_cast<const pa_blockwise_state*>(state);
+  if (!st->m_code || !st->m_absmax || !st->v_code || !st->v_absmax || !st->qmap_m || !st->qmap_v ||
+      !st->p_out_bf16)
+    return PA_ERR_ARG;
+  if (n % pa::kBlock != 0) return PA_ERR_SHAPE;
+  if (!aligned(p, 16) || !aligned(g, 16) || !aligned(st->m_code, 4) || !aligned(st->v_code, 4) ||
+      !aligned(st->m_absmax, 4) || !aligned(st->v_absmax, 4) || !aligned(st->qmap_m, 4) ||
+      !aligned(st->qmap_v, 4) || !aligned(st->p_out_bf16, 8))
+    return PA_ERR_ALIGN;
+  const size_t nb = n / pa::kBlock;
+  a->p = p;
+  a->g = g;
+  a->m_code = st->m_code;
+  a->m_absmax = st->m_absmax;
+  a->v_code = st->v_code;
+  a->v_absmax = st->v_absmax;
+  a->qmap_m = st->qmap_m;
+  a->qmap_v = st->qmap_v;
+  a->p_out = st->p_out_bf16;
+  a->nblocks = (long long)nb;
+  // Written buffers must not overlap anything; the read-only inputs (p, g,
+  // the maps) may overlap one another.
+  ranges->push_back(range_of(st->m_code, n));
+  ranges->push_back(range_of(st->v_code, n));
+  ranges->push_back(range_of(st->m_absmax, nb * 4));
+  ranges->push_back(range_of(st->v_absmax, nb * 4));
+  ranges->push_back(range_of(st->p_out_bf16, n * 2));
+  return PA_OK;
+}
+
+int blockwise_inputs_clear(const pa::BlockwiseArgs& a, size_t n, std::vector<Range> written) {
+  const Range ro[4] = {range_of(a.p, n * 4), range_of(a.g, n * 4), range_of(a.qmap_m, 1024),
+                       range_of(a.qmap_v, 1024)};
+  for (const Range& w : written)
+    for (const Range& r : ro)
+      if (w.hi > w.lo && r.lo < w.hi && w.lo < r.hi) return PA_ERR_ALIAS;
+  return PA_OK;
+}
+
+hipError_t launch_blockwise(const pa::BlockwiseArgs& a, const pa::Scalars& s, unsigned long long* nf,
+                            hipStream_t st, const DeviceInfo& d) {
+  const dim3 grid((unsigned)grid_for(a.nblocks, d)), block(pa::kThreads);
+  if (nf)
+    hipLaunchKernelGGL((pa::blockwise_kernel<true>), grid, block, 0, st, a, s, nf);
+  else
+    hipLaunchKernelGGL((pa::blockwise_kernel<false>), grid, block, 0, st, a, s, nf);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- plans
+
+struct Plan {
+  int device = -1;
+  int mode = -1;
+  std::vector<uintptr_t> key;   // per tensor: p, g, s0, s1, n
+  pa::Entry* table = nullptr;   // device memory, count+1 entries
+  long long tiles = 0;
+};
+
+std::mutex g_plan_mu;
+std::list<Plan> g_plans;       // most recently used first
+constexpr size_t kMaxPlans = 16;
+
+void free_plan(Plan& pl) {
+  if (pl.table) {
+    int cur = 0;
+    if (hipGetDevice(&cur) == hipSuccess) {
+      if (hipSetDevice(pl.device) == hipSuccess) (void)hipFree(pl.table);
+      (void)hipSetDevice(cur);
+    }
+    pl.table = nullptr;
+  }
+}
+
+bool valid_mode(int mode) { return mode >= PA_FP32 && mode <= PA_BLOCKWISE8; }
+
+}  // namespace
+
+// =================================================================== C ABI
+
+extern "C" {
+
+int pa_step(int mode, float* params, const float* grads, void* state, size_t n, const pa_hyper* hyper,
+            long long step, void* stream) {
+  if (!valid_mode(mode)) return PA_ERR_ARG;
+  pa::Scalars s;
+  int rc = make_scalars(hyper, step, &s);
+  if (rc) return rc;
+  if (n == 0) return PA_OK;
+  int dev;
+  DeviceInfo d;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (mode == PA_BLOCKWISE8) {
+    pa::BlockwiseArgs a;
+    std::vector<Range> w;
+    rc = check_blockwise(params, grads, state, n, &a, &w);
+    if (rc) return rc;
+    if (any_overlap(w)) return PA_ERR_ALIAS;
+    rc = blockwise_inputs_clear(a, n, w);
+    if (rc) return rc;
+    rc = device_info(&dev, &d);
+    if (rc) return rc;
+    hipError_t e = launch_blockwise(a, s, hyper->nonfinite, st, d);
+    return e == hipSuccess ? PA_OK : hip_failed(e);
+  }
+  ElemTensor t;
+  std::vector<Range> ranges;
+  rc = check_elem_tensor(mode, params, grads, state, n, &t, &ranges);
+  if (rc) return rc;
+  if (any_overlap(ranges)) return PA_ERR_ALIAS;
+  rc = device_info(&dev, &d);
+  if (rc) return rc;
+  const pa::Entry e = make_entry(t, 0);
+  hipError_t err = dispatch_one(mode, e, tiles_of(e), s, hyper->nonfinite, st, d);
+  return err == hipSuccess ? PA_OK : hip_failed(err);
+}
+
+int pa_step_list(int mode, size_t count, float* const* params, const float* const* grads, void* const* states,
+                 const size_t* n, const pa_hyper* hyper, long long step, void* stream) {
+  if (!valid_mode(mode)) return PA_ERR_ARG;
+  pa::Scalars s;
+  int rc = make_scalars(hyper, step, &s);
+  if (rc) return rc;
+  if (count == 0) return PA_OK;
+  if (params == nullptr || grads == nullptr || states == nullptr || n == nullptr) return PA_ERR_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int dev;
+  DeviceInfo d;
+
+  if (mode == PA_BLOCKWISE8) {
+    std::vector<pa::BlockwiseArgs> args;
+    std::vector<Range> written;
+    for (size_t i = 0; i < count; ++i) {
+      if (n[i] == 0) continue;
+      pa::BlockwiseArgs a;
+      std::vector<Range> w;
+      rc = check_blockwise(params[i], grads[i], states[i], n[i], &a, &w);
+      if (rc) return rc;
+      written.insert(written.end(), w.begin(), w.end());
+      args.push_back(a);
+    }
+    std::vector<Range> all = written;
+    if (any_overlap(all)) return PA_ERR_ALIAS;
+    for (size_t i = 0; i < args.size(); ++i) {
+      rc = blockwise_inputs_clear(args[i], (size_t)args[i].nblocks * pa::kBlock, written);
+      if (rc) return rc;
+    }
+    rc = device_info(&dev, &d);
+    if (rc) return rc;
+    for (const pa::BlockwiseArgs& a : args) {
+      hipError_t e = launch_blockwise(a, s, hyper->nonfinite, st, d);
+      if (e != hipSuccess) return hip_failed(e);
+    }
+    return PA_OK;
+  }
+
+  rc = device_info(&dev, &d);
+  if (rc) return rc;
+
+  // Key of this list: every pointer and length, in order.
+  std::vector<uintptr_t> key;
+  key.reserve(count * 5);
+  for (size_t i = 0; i < count; ++i) {
+    uintptr_t s0 = reinterpret_cast<uintptr_t>(states[i]), s1 = 0;
+    if (mode == PA_FP32 && states[i] != nullptr) {
+      const pa_fp32_state* fs = static_cast<const pa_fp32_state*>(states[i]);
+      s0 = reinterpret_cast<uintptr_t>(fs->m);
+      s1 = reinterpret_cast<uintptr_t>(fs->v);
+    }
+    key.push_back(reinterpret_cast<uintptr_t>(params[i]));
+    key.push_back(reinterpret_cast<uintptr_t>(grads[i]));
+    key.push_back(s0);
+    key.push_back(s1);
+    key.push_back((uintptr_t)n[i]);
+  }
+
+  std::lock_guard<std::mutex> lk(g_plan_mu);
+  auto it = std::find_if(g_plans.begin(), g_plans.end(),
+                         [&](const Plan& p) { return p.device == dev && p.mode == mode && p.key == key; });
+  if (it == g_plans.end()) {
+    // Validate and build the table once for this list.
+    std::vector<pa::Entry> host;
+    std::vector<Range> ranges;
+    long long tiles = 0;
+    for (size_t i = 0; i < count; ++i) {
+      ElemTensor t;
+      rc = check_elem_tensor(mode, params[i], grads[i], states[i], n[i], &t, &ranges);
+      if (rc) return rc;
+      if (t.n == 0) continue;
+      pa::Entry e = make_entry(t, tiles);
+      tiles += tiles_of(e);
+      host.push_back(e);
+    }
+    if (any_overlap(ranges)) return PA_ERR_ALIAS;
+    if (host.empty()) return PA_OK;
+    pa::Entry sentinel;
+    std::memset(&sentinel, 0, sizeof(sentinel));
+    sentinel.tile0 = tiles;
+    host.push_back(sentinel);
+    Plan pl;
+    pl.device = dev;
+    pl.mode = mode;
+    pl.key = key;
+    pl.tiles = tiles;
+    hipError_t e = hipMalloc(reinterpret_cast<void**>(&pl.table), host.size() * sizeof(pa::Entry));
+    if (e != hipSuccess) {
+      g_last_hip_error = (int)e;
+      return PA_ERR_NOMEM;
+    }
+    e = hipMemcpyAsync(pl.table, host.data(), host.size() * sizeof(pa::Entry), hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) {
+      (void)hipFree(pl.table);
+      return hip_failed(e);
+    }
+    g_plans.push_front(std::move(pl));
+    while (g_plans.size() > kMaxPlans) {
+      free_plan(g_plans.back());
+      g_plans.pop_back();
+    }
+    it = g_plans.begin();
+  } else if (it != g_plans.begin()) {
+    g_plans.splice(g_plans.begin(), g_plans, it);
+    it = g_plans.begin();
+  }
+  hipError_t e = dispatch_list(mode, it->table, it->tiles, s, hyper->nonfinite, st, d);
+  return e == hipSuccess ? PA_OK : hip_failed(e);
+}
+
+size_t pa_state_bytes(int mode, size_t n) {
+  switch (mode) {
+    case PA_FP32: return 8 * n;
+    case PA_PACKED_E4:
+    case PA_PACKED_FP16: return 4 * n;
+    case PA_BLOCKWISE8: return 2 * n + 8 * (n / pa::kBlock);
+    default: return 0;
+  }
+}
+
+int pa_format_info(int mode, pa_format* out) {
+  if (out == nullptr || !valid_mode(mode)) return PA_ERR_ARG;
+  std::memset(out, 0, sizeof(*out));
+  out->mode = mode;
+  switch (mode) {
+    case PA_PACKED_E4:
+      out->lanes = 2;
+      out->m_sign_bits = 1; out->m_exp_bits = 4; out->m_mant_bits = 11; out->m_exp_bias = 15;
+      out->r_sign_bits = 0; out->r_exp_bits = 4; out->r_mant_bits = 12; out->r_exp_bias = 15;
+      out->m_max = std::ldexp(4095.0, -11);       // (2^12 - 1) * 2^-11
+      out->m_min_normal = std::ldexp(1.0, -14);
+      out->m_min_subnormal = std::ldexp(1.0, -25);
+      out->r_max = std::ldexp(8191.0, -12);
+      out->r_min_normal = std::ldexp(1.0, -14);
+      out->r_min_subnormal = std::ldexp(1.0, -26);
+      break;
+    case PA_PACKED_FP16:
+      out->lanes = 2;
+      out->m_sign_bits = 1; out->m_exp_bits = 5; out->m_mant_bits = 10; out->m_exp_bias = 15;
+      out->r_sign_bits = 1; out->r_exp_bits = 5; out->r_mant_bits = 10; out->r_exp_bias = 15;
+      out->m_max = out->r_max = 65504.0;
+      out->m_min_normal = out->r_min_normal = std::ldexp(1.0, -14);
+      out->m_min_subnormal = out->r_min_subnormal = std::ldexp(1.0, -24);
+      break;
+    case PA_FP32:
+      out->lanes = 2;
+      out->m_sign_bits = out->r_sign_bits = 1;
+      out->m_exp_bits = out->r_exp_bits = 8;
+      out->m_mant_bits = out->r_mant_bits = 23;
+      out->m_exp_bias = out->r_exp_bias = 127;
+      out->m_max = out->r_max = 3.4028234663852886e38;
+      out->m_min_normal = out->r_min_normal = std::ldexp(1.0, -126);
+      out->m_min_subnormal = out->r_min_subnormal = std::ldexp(1.0, -149);
+      break;
+    case PA_BLOCKWISE8:
+      out->lanes = 2;
+      out->m_mant_bits = 8;   // 8-bit code into a 256-entry map
+      out->r_mant_bits = 8;
+      out->block = pa::kBlock;
+      break;
+  }
+  return PA_OK;
+}
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_ARG: return "invalid argument";
+    case PA_ERR_ALIGN: return "misaligned buffer";
+    case PA_ERR_SHAPE: return "length is not a multiple of the 2048-element block";
+    case PA_ERR_ALIAS: return "buffers overlap";
+    case PA_ERR_DEVICE: return "HIP runtime error";
+    case PA_ERR_NOMEM: return "device allocation of the launch plan failed";
+    default: return "unknown status";
+  }
+}
+
+int pa_last_hip_error(void) { return g_last_hip_error; }
+
+void pa_release_plans(void) {
+  std::lock_guard<std::mutex> lk(g_plan_mu);
+  for (Plan& p : g_plans) free_plan(p);
+  g_plans.clear();
+}
+
+int pa_debug_codec(int lane, int dir, const void* in, void* out, size_t n, void* stream) {
+  if (lane < 0 || lane > 2 || dir < 0 || dir > 1) return PA_ERR_ARG;
+  if (n == 0) return PA_OK;
+  if (in == nullptr || out == nullptr) return PA_ERR_ARG;
+  if (!aligned(in, dir == 0 ? 4 : 2) || !aligned(out, dir == 0 ? 2 : 4)) return PA_ERR_ALIGN;
+  int dev;
+  DeviceInfo d;
+  int rc = device_info(&dev, &d);
+  if (rc) return rc;
+  const long long blocks = ((long long)n + pa::kThreads - 1) / pa::kThreads;
+  const dim3 grid((unsigned)grid_for(blocks, d)), block(pa::kThreads);
+  hipLaunchKernelGGL(pa::codec_kernel, grid, block, 0, static_cast<hipStream_t>(stream), lane, dir, in, out,
+                     (long long)n);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PA_OK : hip_failed(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,272 @@
+"""Benchmark of the packed-AdamW step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload llama-7b] [--mode e4]
+
+A step is one pa_step_list call (one persistent launch) over the whole
+parameter list of the workload, with parameters, gradients and state already
+resident in HBM.  Default workload: the 291-tensor Llama-7B list
+(6,738,415,616 FP32 parameters, packed E4 state), gradients drawn once on the
+device and reused, 3 warm-up and 20 timed steps.
+
+Prints one JSON line: params/s over the timed steps (whole job), the
+roofline of the step kernel (algorithmic bytes per launch over the mean
+launch time from HIP events on the launch stream, against 8 TB/s), and the
+CPU oracle's throughput on a bounded sample of the same workload.
+
+Other flags:
+  --no-cpu-baseline       skip the oracle timing
+  --probe                 also time a plain copy and a 3-in/2-out stream probe
+  --calibrate-copy BYTES  only run the plain copy probe (for counter calibration)
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "packed-AdamW step: params/s and achieved HBM GB/s (% of 8 TB/s) at 7B"
+PEAK_GBPS = 8000.0
+BYTES_PER_PARAM = {"e4": 20, "fp16": 20, "fp32": 28}
+WORKLOADS = {"single-262k": 1, "gpt-11m": 2, "gpt2-small-124m": 3, "llama-7b": 4}
+KERNEL_SOURCES = ("adamw_step_amd/csrc/kernels.hpp", "adamw_step_amd/csrc/codec.hpp",
+                  "adamw_step_amd/csrc/pa_api.hip")
+
+
+def kernel_sha():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def probe_lib():
+    import ctypes
+    import adamw_step_amd as pa
+    pa.lib()
+    path = os.path.join(ROOT, "adamw_step_amd", "libpa_probe.so")
+    L = ctypes.CDLL(path)
+    L.pa_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    L.pa_probe_stream5.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                   ctypes.c_int, ctypes.c_void_p]
+    return L
+
+
+def time_probe(fn, reps):
+    import torch
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        s.record()
+        fn()
+        e.record()
+        e.synchronize()
+        ts.append(s.elapsed_time(e))
+    return sorted(ts)[len(ts) // 2]
+
+
+def run_probes(grid):
+    import torch
+    L = probe_lib()
+    st = torch.cuda.current_stream().cuda_stream
+    nbytes = 8 << 30
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    ms = time_probe(lambda: L.pa_probe_copy(a.data_ptr(), b.data_ptr(), nbytes, grid, st), 10)
+    copy_gbps = 2 * nbytes / ms / 1e6
+    c = torch.empty_like(a)
+    c.fill_(2.0)
+    n16 = nbytes // 16
+    ms5 = time_probe(lambda: L.pa_probe_stream5(a.data_ptr(), b.data_ptr(), c.data_ptr(), n16, grid, st), 10)
+    stream_gbps = 5 * nbytes / ms5 / 1e6
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"copy_gbps": round(copy_gbps, 1), "stream_3in_2out_gbps": round(stream_gbps, 1),
+            "bytes": nbytes, "grid": grid}
+
+
+def calibrate_copy(nbytes):
+    import torch
+    L = probe_lib()
+    st = torch.cuda.current_stream().cuda_stream
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        assert L.pa_probe_copy(a.data_ptr(), b.data_ptr(), nbytes, 2048, st) == 0
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": nbytes, "launches": 3}), flush=True)
+
+
+def build_workload(cfg, mode):
+    import torch
+    import workloads
+    sizes = workloads.sizes(cfg)
+    log(f"allocating {workloads.NAMES[cfg]}: {len(sizes)} tensors, {sum(sizes)} params")
+    ps = [torch.empty(n, dtype=torch.float32, device="cuda:0") for n in sizes]
+    gs = [torch.empty(n, dtype=torch.float32, device="cuda:0") for n in sizes]
+    if mode == "fp32":
+        states = [(torch.zeros(n, dtype=torch.float32, device="cuda:0"),
+                   torch.zeros(n, dtype=torch.float32, device="cuda:0")) for n in sizes]
+    else:
+        states = [torch.zeros(n, dtype=torch.int32, device="cuda:0") for n in sizes]
+    workloads.device_fill_params(cfg, ps)
+    workloads.device_fill_grads(cfg, 1, gs)
+    torch.cuda.synchronize()
+    return sizes, ps, gs, states
+
+
+def cpu_baseline(cfg, mode, ps, gs, states, budget_params):
+    """Time the oracle (as it stands) on a bounded sample of the same workload:
+    the leading tensors of the list, up to `budget_params` parameters, one step."""
+    import numpy as np
+    import oracle
+    import workloads
+    h = workloads.HYPER
+    sc = oracle.scalars(h["lr"], h["beta1"], h["beta2"], h["eps"], h["weight_decay"], 1)
+    picked, total = [], 0
+    for k in range(len(ps)):
+        n = ps[k].numel()
+        if total + n > budget_params and picked:
+            break
+        picked.append(k)
+        total += n
+    hp = [ps[k].cpu().numpy() for k in picked]
+    hg = [gs[k].cpu().numpy() for k in picked]
+    if mode == "fp32":
+        hs = [(np.zeros(ps[k].numel(), np.float32), np.zeros(ps[k].numel(), np.float32)) for k in picked]
+    else:
+        hs = [np.zeros(ps[k].numel(), np.uint32) for k in picked]
+    names = [workloads.shapes(cfg)[k][0] for k in picked]
+    t0 = time.perf_counter()
+    for i in range(len(picked)):
+        if mode == "fp32":
+            oracle.step_fp32(hp[i], hg[i], hs[i][0], hs[i][1], sc)
+        else:
+            oracle.step_packed(oracle.PACKED_E4 if mode == "e4" else oracle.PACKED_F16, hp[i], hg[i], hs[i], sc)
+    dt = time.perf_counter() - t0
+    return {"value": round(total / dt, 1), "unit": "params/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"one step over the first {len(picked)} tensors of the list "
+                      f"({names[0]}..{names[-1]}, {total} params), {dt:.1f} s wall"}
+
+
+def load_traffic(workload, mode):
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{mode}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_sha") != kernel_sha():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama-7b", choices=sorted(WORKLOADS))
+    ap.add_argument("--mode", default="e4", choices=sorted(BYTES_PER_PARAM))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-params", type=int, default=400_000_000)
+    ap.add_argument("--probe", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only; every GPU box here has a single GPU, "
+              "so --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import adamw_step_amd as pa
+    import workloads
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
+
+    cfg = WORKLOADS[args.workload]
+    mode = args.mode
+    sizes, ps, gs, states = build_workload(cfg, mode)
+    n_params = sum(sizes)
+    h = dict(workloads.HYPER)
+    t = 0
+
+    def step():
+        nonlocal t
+        t += 1
+        pa.pa_step_list(mode, ps, gs, states, h, t)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        evs[k][0].record(stream)
+        step()
+        evs[k][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in evs]
+    mean_launch_ms = sum(launch_ms) / len(launch_ms)
+    log(f"timed {args.steps} steps: {elapsed * 1e3 / args.steps:.3f} ms/step wall, "
+        f"{mean_launch_ms:.3f} ms/launch (events), min {min(launch_ms):.3f}")
+
+    algo_bytes = BYTES_PER_PARAM[mode] * n_params
+    achieved = algo_bytes / (mean_launch_ms / 1e3) / 1e9
+    traffic = load_traffic(args.workload, mode)
+    out = {
+        "metric": METRIC,
+        "value": round(n_params * args.steps / elapsed, 1),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "params": n_params, "tensors": len(sizes),
+                   "mode": {"e4": "packed-e4m11-e4m12", "fp16": "packed-fp16", "fp32": "fp32-adamw"}[mode],
+                   "state_bytes_per_param": pa.pa_state_bytes(mode, 1),
+                   "grads": "drawn once on the device, reused every step"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": f"elementwise_list<{mode}>", "algorithmic_bytes_per_launch": algo_bytes,
+                     "mean_launch_ms": round(mean_launch_ms, 4), "kernel_sha": kernel_sha()},
+    }
+    if args.probe:
+        import adamw_step_amd as _p  # noqa: F401
+        del ps, gs, states
+        torch.cuda.empty_cache()
+        out["probes"] = run_probes(grid=2048)
+        log(f"probes: {out['probes']}")
+    if not args.no_cpu_baseline and not args.probe:
+        log("timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(cfg, mode, ps, gs, states, args.cpu_sample_params)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

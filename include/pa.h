@@ -1,0 +1,184 @@
+/*
+ * pa.h -- C ABI of the packed-AdamW step library (libpa.so, gfx950).
+ *
+ * One optimizer update of AdamW whose two moments persist, between updates,
+ * in a compact form, with the current update itself done in FP32:
+ *
+ *   m' = beta1*m + (1-beta1)*g
+ *   v' = beta2*v + (1-beta2)*g*g
+ *   p' = p*(1-lr*wd) - (lr/(1-beta1^t)) * m' / (sqrt(v'/(1-beta2^t)) + eps)
+ *
+ * (TurboAdam package page, "The AdamW update remains AdamW": the recurrence
+ * and the decoupled-decay update; KBench quantized-optimizer-state
+ * reference, `quantized_adamw_step`: the FP32 operation order used here,
+ * left to right, with the host scalars formed in double precision and each
+ * rounded once to binary32.)
+ *
+ * Modes (Packed AdamW Reference README, introduction; its project page,
+ * Release scope):
+ *   PA_PACKED_E4   one uint32 per parameter: low 16 bits a signed finite
+ *                  E4M11 first moment, high 16 bits an unsigned finite E4M12
+ *                  uncorrected RMS (sqrt of the second moment).  The prior
+ *                  word is decoded, v = r*r, the update runs in FP32 on the
+ *                  new unquantised moments, and only then m' and sqrt(v')
+ *                  are rounded to nearest (ties to even) with saturation at
+ *                  the largest finite value and packed.  Exponent bias 15 in
+ *                  both lanes, gradual underflow, no Inf/NaN codes; NaN packs
+ *                  as code 0.
+ *   PA_PACKED_FP16 the same word with IEEE binary16 in both halves
+ *                  (round to nearest even, overflow to Inf).
+ *   PA_FP32        plain FP32 AdamW with two FP32 moment tensors.
+ *   PA_BLOCKWISE8  8-bit codes for both moments, one FP32 absmax per
+ *                  2048-element block per moment, ascending 256-entry code
+ *                  maps, nearest-entry requantisation through the 255 FP32
+ *                  midpoints (ties to the lower entry), BF16 parameter output
+ *                  (KBench quantized-optimizer-state reference,
+ *                  `quantized_adamw_step` and `_requantise`).
+ *
+ * Execution contract (project page, Execution contract table): contiguous
+ * FP32 parameters and dense FP32 gradients on one device, one group of
+ * hyperparameters and one global step per call.
+ *
+ * Memory: every pointer handed to pa_step / pa_step_list that names tensor
+ * data is a DEVICE pointer owned by the caller; the library never frees or
+ * keeps it beyond the call.  Descriptor structs (pa_hyper, pa_fp32_state,
+ * pa_blockwise_state) and the pointer/size arrays of pa_step_list are HOST
+ * memory, read during the call only.  State must be zero-filled by the
+ * caller before step 1 (the all-zero word and a zero absmax both decode to
+ * zero moments).
+ *
+ * Streams: work is enqueued on `stream` (a hipStream_t; NULL = the null
+ * stream) and the call returns without waiting.  Faults inside a kernel
+ * surface at the next synchronisation of that stream.
+ *
+ * Errors: every entry point returns PA_OK (0) or a negative PA_ERR_* code
+ * and never aborts or throws.  A call that returns an error has enqueued
+ * nothing.  There is no fallback path of any kind.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_FP32 = 0,
+  PA_PACKED_E4 = 1,
+  PA_PACKED_FP16 = 2,
+  PA_BLOCKWISE8 = 3
+} pa_mode;
+
+enum {
+  PA_OK = 0,
+  PA_ERR_ARG = -1,    /* null pointer with n > 0, unknown mode, step < 1,
+                         beta outside [0,1), non-finite or negative lr/eps/wd,
+                         non-finite beta */
+  PA_ERR_ALIGN = -2,  /* a data pointer not 4-byte aligned (1-byte for codes),
+                         or params/grads/state words not sharing one 16-byte
+                         phase */
+  PA_ERR_SHAPE = -3,  /* blockwise length not a multiple of 2048 */
+  PA_ERR_ALIAS = -4,  /* two buffers of one call overlap */
+  PA_ERR_DEVICE = -5, /* the HIP runtime refused a launch or a copy */
+  PA_ERR_NOMEM = -6   /* the launch plan table could not be allocated */
+};
+
+/* Hyperparameters, host doubles (TurboAdam package page, API section: lr,
+ * betas, eps, weight_decay).  `nonfinite`, if not NULL, is a device counter
+ * that the call increments by the number of elements whose new parameter,
+ * first moment or second moment is not finite (the optimizer non-finite
+ * count of the reference's one-update smoke check). */
+typedef struct {
+  double lr;
+  double beta1;
+  double beta2;
+  double eps;
+  double weight_decay;
+  unsigned long long* nonfinite;
+} pa_hyper;
+
+/* PA_FP32 state: two device arrays of n floats. */
+typedef struct {
+  float* m;
+  float* v;
+} pa_fp32_state;
+
+/* PA_BLOCKWISE8 state.  m_code/v_code: n device bytes; m_absmax/v_absmax:
+ * n/2048 device floats; qmap_m/qmap_v: 256 ascending device floats each
+ * (read only); p_out_bf16: n device uint16 receiving the updated parameters
+ * as bfloat16 bits.  In this mode `params` is read only. */
+typedef struct {
+  uint8_t* m_code;
+  float* m_absmax;
+  uint8_t* v_code;
+  float* v_absmax;
+  const float* qmap_m;
+  const float* qmap_v;
+  uint16_t* p_out_bf16;
+} pa_blockwise_state;
+
+/* One tensor of n parameters, updated in place, step t = `step` (>= 1,
+ * counting this update).
+ *   PA_PACKED_E4 / PA_PACKED_FP16: `state` is a device uint32_t* of n words.
+ *   PA_FP32:       `state` is a host pa_fp32_state*.
+ *   PA_BLOCKWISE8: `state` is a host pa_blockwise_state*.
+ * n == 0 enqueues nothing and returns PA_OK.  `stream` is a hipStream_t. */
+int pa_step(int mode, float* params, const float* grads, void* state, size_t n,
+            const pa_hyper* hyper, long long step, void* stream);
+
+/* `count` tensors sharing one hyperparameter set and one step, updated by
+ * one persistent launch (elementwise modes) that walks a table of all of
+ * them.  params[i], grads[i], states[i] and n[i] describe tensor i exactly
+ * as for pa_step.  The table is uploaded once per distinct pointer/size
+ * list and cached (see pa_release_plans).  Tensors of length 0 are
+ * skipped. */
+int pa_step_list(int mode, size_t count, float* const* params, const float* const* grads,
+                 void* const* states, const size_t* n, const pa_hyper* hyper, long long step,
+                 void* stream);
+
+/* Persistent optimizer-state bytes for n parameters in `mode` (the state
+ * ledger; Packed AdamW Reference README, "The narrow result": 8 bytes per
+ * parameter for FP32 AdamW, 4 for the packed word).  Blockwise: two code
+ * bytes per parameter plus two FP32 absmax values per 2048-block (n must be
+ * a multiple of 2048).  Returns 0 for an unknown mode. */
+size_t pa_state_bytes(int mode, size_t n);
+
+/* Description of one mode's lanes (for inspection and tests). */
+typedef struct {
+  int mode;
+  int lanes;              /* values per parameter in the persistent state */
+  int m_sign_bits, m_exp_bits, m_mant_bits, m_exp_bias;
+  int r_sign_bits, r_exp_bits, r_mant_bits, r_exp_bias;
+  double m_max, m_min_normal, m_min_subnormal;
+  double r_max, r_min_normal, r_min_subnormal;
+  int block;              /* 2048 for PA_BLOCKWISE8, else 0 */
+} pa_format;
+
+int pa_format_info(int mode, pa_format* out);
+
+/* Text for a status code (static storage). */
+const char* pa_status_string(int status);
+
+/* The hipError_t of the last failed HIP call made by the library in this
+ * thread (0 if none). */
+int pa_last_hip_error(void);
+
+/* Free every cached launch-plan table (device memory).  Waits for the
+ * device first.  Safe to call at any time outside a running call. */
+void pa_release_plans(void);
+
+/* Codec self-test export: apply one lane codec of the GPU path to n device
+ * values.  lane 0 = E4M11 first moment, 1 = E4M12 RMS, 2 = binary16.
+ * dir 0 encodes float -> uint16 (in: float*, out: uint16_t*), dir 1 decodes
+ * uint16 -> float.  Device pointers, asynchronous on `stream`.  Used by the
+ * tests to check every code of every lane on the device. */
+int pa_debug_codec(int lane, int dir, const void* in, void* out, size_t n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

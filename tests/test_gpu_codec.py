@@ -1,0 +1,83 @@
+"""GPU lane codecs against the oracle's, through the C ABI (pa_debug_codec):
+every code of every lane decoded, and every rounding boundary (with its
+FP32 neighbours), whole FP32 binades and random bit patterns encoded."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import banner, to_dev, to_host
+from pins import boundary_set, random_patterns, specials
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pa():
+    import adamw_step_amd as pa_mod
+    pa_mod.lib()
+    return pa_mod
+
+
+def _decode_gpu(pa, lane, codes):
+    import torch
+    inp = to_dev(codes.astype(np.uint16))
+    out = torch.empty(codes.size, dtype=torch.float32, device=inp.device)
+    pa.pa_debug_codec(lane, 1, inp, out)
+    torch.cuda.synchronize()
+    return to_host(out)
+
+
+def _encode_gpu(pa, lane, x):
+    import torch
+    inp = to_dev(x.astype(np.float32))
+    out = torch.empty(x.size, dtype=torch.int16, device=inp.device)
+    pa.pa_debug_codec(lane, 0, inp, out)
+    torch.cuda.synchronize()
+    return to_host(out, np.uint16)
+
+
+def _binade(e):
+    return ((np.uint32((e + 127) << 23)) + np.arange(1 << 23, dtype=np.uint32)).view(np.float32)
+
+
+@pytest.mark.parametrize("lane", [0, 1, 2])
+def test_decode_every_code(pa, lane):
+    banner(f"decode all codes lane {lane}")
+    codes = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = _decode_gpu(pa, lane, codes)
+    want = oracle.decode(lane, codes)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    np.testing.assert_array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
+
+
+@pytest.mark.parametrize("lane", [0, 1, 2])
+def test_encode_boundaries_and_random(pa, lane):
+    banner(f"encode boundary sets lane {lane}")
+    if lane == 0:
+        table = oracle.decode(0, np.arange(0x8000, dtype=np.uint16)).astype(np.float64)
+        extra = [2.0]
+    elif lane == 1:
+        table = oracle.decode(1, np.arange(0x10000, dtype=np.uint16)).astype(np.float64)
+        extra = [2.0]
+    else:
+        table = np.arange(0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
+        extra = [65536.0]
+    x = np.concatenate([boundary_set(np.append(table, extra)), random_patterns(1 << 24, 100 + lane),
+                        specials(), _binade(-15), _binade(-27), _binade(0), -_binade(-20)])
+    got = _encode_gpu(pa, lane, x)
+    want = oracle.encode(lane, x)
+    if lane == 2:
+        nan = np.isnan(x)
+        np.testing.assert_array_equal(got[~nan], want[~nan])
+        assert np.all(((got[nan] & 0x7C00) == 0x7C00) & ((got[nan] & 0x3FF) != 0))
+    else:
+        np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("lane", [0, 1])
+def test_decode_encode_identity_on_device(pa, lane):
+    banner(f"identity lane {lane}")
+    codes = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    back = _encode_gpu(pa, lane, _decode_gpu(pa, lane, codes))
+    np.testing.assert_array_equal(back, codes)

@@ -1,0 +1,125 @@
+"""Full-size workloads, in the launch configuration the benchmark times,
+checked against the oracle on sampled outputs.
+
+  * llama-7b: 291 tensors, 6,738,415,616 parameters, packed E4, two steps of
+    one persistent launch each; sampled: every tensor's first and last 64 Ki
+    elements plus a seeded 1/1024 of its 64 Ki-element tiles.  The step is
+    elementwise, so the sampled inputs, gathered from the device before the
+    step, determine the sampled outputs exactly.
+  * blockwise-268m: one flat tensor of 2^28 parameters (131,072 blocks),
+    three steps; sampled: the first, last and 254 seeded blocks (blocks are
+    independent).  Between steps the BF16 output, widened on the device,
+    becomes the next step's FP32 parameters.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import assert_params, assert_words, banner, hyper, scalars, to_host
+
+pytestmark = pytest.mark.gpu
+
+CHUNK = 1 << 16
+
+
+@pytest.fixture(scope="module")
+def pa():
+    import adamw_step_amd as pa_mod
+    pa_mod.lib()
+    return pa_mod
+
+
+def _sample_index(n, rng):
+    tiles = (n + CHUNK - 1) // CHUNK
+    pick = {0, tiles - 1}
+    k = max(1, tiles // 1024)
+    pick.update(rng.choice(tiles, size=min(k, tiles), replace=False).tolist())
+    idx = np.concatenate([np.arange(t * CHUNK, min(n, (t + 1) * CHUNK)) for t in sorted(pick)])
+    if n > CHUNK:
+        idx = np.union1d(idx, np.arange(n - CHUNK, n))
+    return idx
+
+
+@pytest.mark.timeout(900)
+def test_llama_7b_e4_sampled(pa):
+    import torch
+    cfg = 4
+    sizes = workloads.sizes(cfg)
+    banner(f"llama-7b: allocating {sum(sizes) * 12 / 1e9:.1f} GB")
+    ps = [torch.empty(n, dtype=torch.float32, device="cuda:0") for n in sizes]
+    gs = [torch.empty(n, dtype=torch.float32, device="cuda:0") for n in sizes]
+    ws = [torch.zeros(n, dtype=torch.int32, device="cuda:0") for n in sizes]
+    workloads.device_fill_params(cfg, ps)
+    rng = np.random.Generator(np.random.PCG64(4242))
+    idx = [_sample_index(n, rng) for n in sizes]
+    didx = [torch.from_numpy(i).to("cuda:0") for i in idx]
+    total = sum(i.size for i in idx)
+    try:
+        for t in (1, 2):
+            workloads.device_fill_grads(cfg, t, gs)
+            torch.cuda.synchronize()
+            hp = [to_host(p[i]) for p, i in zip(ps, didx)]
+            hg = [to_host(g[i]) for g, i in zip(gs, didx)]
+            hw = [to_host(w[i], np.uint32) for w, i in zip(ws, didx)]
+            banner(f"llama-7b step {t}: one persistent launch over 291 tensors")
+            pa.pa_step_list(1, ps, gs, ws, hyper(), t)
+            torch.cuda.synchronize()
+            sc = scalars(t)
+            same = 0
+            for k in range(len(sizes)):
+                oracle.step_packed(1, hp[k], hg[k], hw[k], sc)
+                assert_words(to_host(ws[k][didx[k]], np.uint32), hw[k], what=f"tensor {k} words")
+                same += assert_params(to_host(ps[k][didx[k]]), hp[k], what=f"tensor {k} params")[0]
+            banner(f"llama-7b step {t}: {total} sampled elements, bit-identical params {same}")
+    finally:
+        del ps, gs, ws
+        torch.cuda.empty_cache()
+        pa.pa_release_plans()
+
+
+@pytest.mark.timeout(600)
+def test_blockwise_268m_sampled(pa):
+    import torch
+    cfg = 5
+    n = workloads.total(cfg)
+    nb = n // 2048
+    qm, qv = workloads.code_maps()
+    zero_m = int(np.nonzero(qm == 0.0)[0][0])
+    p = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    g = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    workloads.device_fill_params(cfg, [p])
+    mc = torch.full((n,), zero_m, dtype=torch.uint8, device="cuda:0")
+    vc = torch.zeros(n, dtype=torch.uint8, device="cuda:0")
+    ma = torch.zeros(nb, dtype=torch.float32, device="cuda:0")
+    va = torch.zeros(nb, dtype=torch.float32, device="cuda:0")
+    dqm = torch.from_numpy(qm).to("cuda:0")
+    dqv = torch.from_numpy(qv).to("cuda:0")
+    pout = torch.empty(n, dtype=torch.int16, device="cuda:0")
+    rng = np.random.Generator(np.random.PCG64(5151))
+    blocks = np.union1d([0, nb - 1], rng.choice(nb, 254, replace=False))
+    eidx = torch.from_numpy((blocks[:, None] * 2048 + np.arange(2048)[None, :]).reshape(-1)).to("cuda:0")
+    bidx = torch.from_numpy(blocks).to("cuda:0")
+    try:
+        for t in (1, 2, 3):
+            workloads.device_fill_grads(cfg, t, [g])
+            torch.cuda.synchronize()
+            hp, hg = to_host(p[eidx]), to_host(g[eidx])
+            hmc, hvc = to_host(mc[eidx]).copy(), to_host(vc[eidx]).copy()
+            hma, hva = to_host(ma[bidx]).copy(), to_host(va[bidx]).copy()
+            banner(f"blockwise-268m step {t}")
+            pa.pa_step(3, p, g, (mc, ma, vc, va, dqm, dqv, pout), hyper(), t)
+            torch.cuda.synchronize()
+            hout = np.zeros(hp.size, np.uint16)
+            oracle.step_blockwise(hp, hg, hmc, hma, hvc, hva, qm, qv, hout, scalars(t))
+            np.testing.assert_array_equal(to_host(pout[eidx], np.uint16), hout)
+            np.testing.assert_array_equal(to_host(mc[eidx]), hmc)
+            np.testing.assert_array_equal(to_host(vc[eidx]), hvc)
+            assert_words(to_host(ma[bidx]).view(np.uint32), hma.view(np.uint32), what="m absmax")
+            assert_words(to_host(va[bidx]).view(np.uint32), hva.view(np.uint32), what="v absmax")
+            assert_params(to_host(pout[eidx].view(torch.bfloat16).float()),
+                          (hout.astype(np.uint32) << 16).view(np.float32))
+            p = pout.view(torch.bfloat16).float()
+    finally:
+        del p, g, mc, vc
+        torch.cuda.empty_cache()
