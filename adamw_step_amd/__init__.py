@@ -69,7 +69,7 @@ class Format(ctypes.Structure):
 
 
 EXPORTS = ("pa_step", "pa_step_list", "pa_state_bytes", "pa_format_info", "pa_status_string",
-           "pa_last_hip_error", "pa_release_plans", "pa_debug_codec")
+           "pa_last_hip_error", "pa_release_plans", "pa_debug_codec", "pa_debug_sqrt")
 
 _lib = None
 
@@ -100,6 +100,8 @@ def lib():
     L.pa_release_plans.restype = None
     L.pa_debug_codec.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, sz, vp]
     L.pa_debug_codec.restype = ctypes.c_int
+    L.pa_debug_sqrt.argtypes = [vp, vp, sz, vp]
+    L.pa_debug_sqrt.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -247,3 +249,12 @@ def pa_debug_codec(lane, direction, inp, out, stream=None):
         raise ValueError("input and output sizes differ")
     _check(lib().pa_debug_codec(int(lane), int(direction), _ptr(inp), _ptr(out), inp.numel(),
                                 _stream(stream)))
+
+
+def pa_debug_sqrt(inp, out, stream=None):
+    """out = the GPU path's correctly rounded square root of inp (float32)."""
+    _tensor_ok(inp, "input")
+    _tensor_ok(out, "output")
+    if inp.numel() != out.numel():
+        raise ValueError("input and output sizes differ")
+    _check(lib().pa_debug_sqrt(_ptr(inp), _ptr(out), inp.numel(), _stream(stream)))

@@ -56,12 +56,39 @@ constexpr int kBlock = 2048;                    // blockwise quantisation block
 
 enum { kModeFp32 = 0, kModeE4 = 1, kModeF16 = 2 };
 
+// Correctly rounded FP32 square root.
+//
+// The hardware estimate s (v_sqrt_f32) is within one ulp of sqrt(x), so
+// RN(sqrt(x)) is one of s-1ulp, s, s+1ulp (integer steps of the bit
+// pattern).  With u the ulp of s, sqrt(x) lies below the midpoint between
+// s-1ulp and s exactly when x <= (s-1ulp)*s: the two sides differ by u^2/4
+// while x and (s-1ulp)*s are both multiples of u^2 (x of a much coarser
+// power of two), so nothing lies strictly between them.  The FMA forms
+// x - (s-1ulp)*s with a single rounding, which keeps the sign, and the test
+// above the midpoint between s and s+1ulp is the mirror image.  Inputs below
+// 2^-96 (denormals included) are first scaled by 2^64, and the root by 2^-32,
+// so that the residuals stay far from underflow.  Zero, Inf and NaN fall
+// through unchanged: the neighbour residuals are then NaN or zero and
+// neither test fires.
+__device__ __forceinline__ float sqrt_rn(float x) {
+  const bool tiny = x < 0x1p-96f;
+  const float xs = tiny ? x * 0x1p64f : x;
+  float s = __builtin_amdgcn_sqrtf(xs);
+  const float s_dn = __uint_as_float(__float_as_uint(s) - 1u);
+  const float s_up = __uint_as_float(__float_as_uint(s) + 1u);
+  const float r_dn = __builtin_fmaf(-s_dn, s, xs);
+  const float r_up = __builtin_fmaf(-s_up, s, xs);
+  s = r_dn <= 0.0f ? s_dn : s;
+  s = r_up > 0.0f ? s_up : s;
+  return tiny ? s * 0x1p-32f : s;
+}
+
 // New moments and the FP32 step with decoupled decay.
 __device__ __forceinline__ void adamw(float p, float g, float m, float v, const Scalars& s,
                                       float& p1, float& m1, float& v1) {
   m1 = s.beta1 * m + s.one_m_beta1 * g;
   v1 = s.beta2 * v + (s.one_m_beta2 * g) * g;
-  const float denom = __fsqrt_rn(__fdiv_rn(v1, s.bc2)) + s.eps;
+  const float denom = sqrt_rn(__fdiv_rn(v1, s.bc2)) + s.eps;
   const float upd = __fdiv_rn(s.lr_over_bc1 * m1, denom);
   p1 = p * s.decay - upd;
 }
@@ -86,7 +113,7 @@ __device__ __forceinline__ uint32_t packed_elem(float& p, float g, uint32_t w, c
   adamw(p, g, m, r * r, s, p1, m1, v1);
   bad += nonfinite3(p1, m1, v1);
   p = p1;
-  const float r1 = __fsqrt_rn(v1);
+  const float r1 = sqrt_rn(v1);
   if constexpr (MODE == kModeE4) {
     return (e4_encode_r(r1) << 16) | e4_encode_m(m1);
   } else {
@@ -348,7 +375,13 @@ blockwise_kernel(BlockwiseArgs a, Scalars s, unsigned long long* nonfinite) {
 }
 
 // ---------------------------------------------------------------------------
-// Codec export for tests: every code of every lane, on the device.
+// Exports for tests: every code of every lane, and the square root, on the
+// device.
+
+__global__ void __launch_bounds__(kThreads) sqrt_kernel(const float* in, float* out, long long n) {
+  for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < n; i += (long long)gridDim.x * kThreads)
+    out[i] = sqrt_rn(in[i]);
+}
 
 __global__ void __launch_bounds__(kThreads)
 codec_kernel(int lane_kind, int dir, const void* in, void* out, long long n) {

@@ -177,6 +177,12 @@ void pa_release_plans(void);
  * tests to check every code of every lane on the device. */
 int pa_debug_codec(int lane, int dir, const void* in, void* out, size_t n, void* stream);
 
+/* Square-root self-test export: out[i] = the GPU path's correctly rounded
+ * binary32 square root of in[i], for n device floats, asynchronous on
+ * `stream`.  The update takes sqrt(v'/bc2) and sqrt(v') with this routine;
+ * the tests compare it with the host's IEEE square root on every float. */
+int pa_debug_sqrt(const float* in, float* out, size_t n, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

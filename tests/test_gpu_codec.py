@@ -81,3 +81,27 @@ def test_decode_encode_identity_on_device(pa, lane):
     codes = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
     back = _encode_gpu(pa, lane, _decode_gpu(pa, lane, codes))
     np.testing.assert_array_equal(back, codes)
+
+
+def test_sqrt_every_float(pa):
+    """The GPU path's square root equals the host's IEEE square root
+    (numpy, correctly rounded) on all 2^32 bit patterns; NaN by class."""
+    import torch
+    chunk = 1 << 28
+    bad = 0
+    for c in range(1 << 4):
+        banner(f"sqrt chunk {c}/16")
+        bits = torch.arange(c * chunk, (c + 1) * chunk, dtype=torch.int64, device="cuda:0")
+        x = bits.to(torch.int32).view(torch.float32)        # wraps to the bit pattern
+        out = torch.empty_like(x)
+        pa.pa_debug_sqrt(x, out)
+        torch.cuda.synchronize()
+        hx = to_host(x)
+        got = to_host(out)
+        with np.errstate(invalid="ignore"):
+            want = np.sqrt(hx)
+        nan = np.isnan(want)
+        assert np.array_equal(np.isnan(got), nan)
+        bad += int((got[~nan].view(np.uint32) != want[~nan].view(np.uint32)).sum())
+        del bits, x, out
+    assert bad == 0, f"{bad} square roots differ from IEEE"
