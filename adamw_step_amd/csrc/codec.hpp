@@ -44,27 +44,36 @@ __device__ __forceinline__ float e4_decode_m(uint32_t word) {
   return __uint_as_float(__float_as_uint(mag) | ((word & 0x8000u) << 16));
 }
 
+// The first moment's fields in place but without the 2^112 scale: the value
+// times 2^-112, an FP32 denormal or small normal.  A product c * m with a
+// binary32 c equals (c * 2^112) * e4_decode_m_unscaled(word) exactly, since
+// c * 2^112 is exact and the product is rounded once either way.
+__device__ __forceinline__ float e4_decode_m_unscaled(uint32_t word) {
+  return __uint_as_float(((word & 0x7FFFu) << 12) | ((word & 0x8000u) << 16));
+}
+
 __device__ __forceinline__ float e4_decode_r(uint32_t word) {
   return __uint_as_float((word >> 16) << 11) * 0x1p112f;
 }
 
 __device__ __forceinline__ uint32_t e4_encode_m(float x) {
   const uint32_t b = __float_as_uint(x);
-  const uint32_t a = b & 0x7FFFFFFFu;
+  const uint32_t mag_bits = b & 0x7FFFFFFFu;
+  // |x| at or above the largest finite value (Inf too) encodes as that value.
+  const uint32_t a = min(mag_bits, kMMaxBits);
   const uint32_t nrm = (a - kRebias + 0x7FFu + ((a >> 12) & 1u)) >> 12;
   const uint32_t sub = __float_as_uint(__uint_as_float(a) + 0.25f) - 0x3E800000u;
-  uint32_t mag = a < kMinNormalBits ? sub : nrm;
-  mag = a >= kMMaxBits ? 0x7FFFu : mag;
+  const uint32_t mag = a < kMinNormalBits ? sub : nrm;
   const uint32_t code = mag | ((b >> 16) & 0x8000u);
-  return a > kInfBits ? 0u : code;
+  return mag_bits > kInfBits ? 0u : code;
 }
 
 __device__ __forceinline__ uint32_t e4_encode_r(float x) {
   const uint32_t b = __float_as_uint(x);
-  const uint32_t nrm = (b - kRebias + 0x3FFu + ((b >> 11) & 1u)) >> 11;
-  const uint32_t sub = __float_as_uint(__uint_as_float(b) + 0.125f) - 0x3E000000u;
-  uint32_t code = b < kMinNormalBits ? sub : nrm;
-  code = b >= kRMaxBits ? 0xFFFFu : code;
+  const uint32_t a = min(b, kRMaxBits);
+  const uint32_t nrm = (a - kRebias + 0x3FFu + ((a >> 11) & 1u)) >> 11;
+  const uint32_t sub = __float_as_uint(__uint_as_float(a) + 0.125f) - 0x3E000000u;
+  const uint32_t code = a < kMinNormalBits ? sub : nrm;
   return b > kInfBits ? 0u : code;   // NaN, and every input with its sign bit set
 }
 

@@ -32,6 +32,9 @@ namespace pa {
 struct Scalars {
   float beta1, one_m_beta1, beta2, one_m_beta2;
   float bc2, lr_over_bc1, decay, eps;
+  float beta1_x2p112;   // beta1 * 2^112, exact (pairs with e4_decode_m_unscaled)
+  float pad_;
+  double inv_bc2;       // 1/bc2 rounded to double, for the exact quotient v'/bc2
 };
 
 // One tensor of an elementwise launch.  Every buffer of a tensor shares one
@@ -49,8 +52,36 @@ struct Entry {
   int pad_;
 };
 
+// Streaming access policy: every byte is read once and written once, so the
+// 16-byte vector loads and stores carry the nontemporal hint (measured on
+// MI355X: the 3-in/2-out stream runs about 4% faster with it).
+#ifndef PA_STREAM_NT_LOADS
+#define PA_STREAM_NT_LOADS 1
+#endif
+#ifndef PA_STREAM_NT_STORES
+#define PA_STREAM_NT_STORES 1
+#endif
+#ifndef PA_TILE_UNROLL
+#define PA_TILE_UNROLL 4
+#endif
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+__device__ __forceinline__ T stream_load(const T* p) {
+  if constexpr (PA_STREAM_NT_LOADS) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <typename T>
+__device__ __forceinline__ void stream_store(T* p, T v) {
+  if constexpr (PA_STREAM_NT_STORES) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = PA_TILE_UNROLL;
 constexpr int kTile = kThreads * 4 * kUnroll;   // elements per tile
 constexpr int kBlock = 2048;                    // blockwise quantisation block
 
@@ -70,25 +101,38 @@ enum { kModeFp32 = 0, kModeE4 = 1, kModeF16 = 2 };
 // so that the residuals stay far from underflow.  Zero, Inf and NaN fall
 // through unchanged: the neighbour residuals are then NaN or zero and
 // neither test fires.
-__device__ __forceinline__ float sqrt_rn(float x) {
-  const bool tiny = x < 0x1p-96f;
-  const float xs = tiny ? x * 0x1p64f : x;
+__device__ __forceinline__ float sqrt_pick(float xs) {
   float s = __builtin_amdgcn_sqrtf(xs);
   const float s_dn = __uint_as_float(__float_as_uint(s) - 1u);
   const float s_up = __uint_as_float(__float_as_uint(s) + 1u);
   const float r_dn = __builtin_fmaf(-s_dn, s, xs);
   const float r_up = __builtin_fmaf(-s_up, s, xs);
   s = r_dn <= 0.0f ? s_dn : s;
-  s = r_up > 0.0f ? s_up : s;
-  return tiny ? s * 0x1p-32f : s;
+  return r_up > 0.0f ? s_up : s;
 }
 
-// New moments and the FP32 step with decoupled decay.
-__device__ __forceinline__ void adamw(float p, float g, float m, float v, const Scalars& s,
+__device__ __forceinline__ float sqrt_rn(float x) {
+  float s = sqrt_pick(x);
+  if (__builtin_expect(x < 0x1p-96f, 0)) s = sqrt_pick(x * 0x1p64f) * 0x1p-32f;
+  return s;
+}
+
+// v'/bc2, correctly rounded: the product of v' and the double nearest 1/bc2
+// is within 2^-52 (relative) of the exact quotient, while a quotient of two
+// binary32 numbers that is not itself a binary32 number lies at least 2^-49
+// (relative) away from every binary32 rounding midpoint, so rounding the
+// double product to binary32 gives the correctly rounded quotient.
+__device__ __forceinline__ float div_bc2(float v1, const Scalars& s) {
+  return (float)((double)v1 * s.inv_bc2);
+}
+
+// New moments and the FP32 step with decoupled decay.  `beta1_m` is the
+// product beta1 * m, formed by the caller (see e4_decode_m_unscaled).
+__device__ __forceinline__ void adamw(float p, float g, float beta1_m, float v, const Scalars& s,
                                       float& p1, float& m1, float& v1) {
-  m1 = s.beta1 * m + s.one_m_beta1 * g;
+  m1 = beta1_m + s.one_m_beta1 * g;
   v1 = s.beta2 * v + (s.one_m_beta2 * g) * g;
-  const float denom = sqrt_rn(__fdiv_rn(v1, s.bc2)) + s.eps;
+  const float denom = sqrt_rn(div_bc2(v1, s)) + s.eps;
   const float upd = __fdiv_rn(s.lr_over_bc1 * m1, denom);
   p1 = p * s.decay - upd;
 }
@@ -101,16 +145,16 @@ __device__ __forceinline__ uint32_t nonfinite3(float a, float b, float c) {
 template <int MODE>
 __device__ __forceinline__ uint32_t packed_elem(float& p, float g, uint32_t w, const Scalars& s,
                                                 uint32_t& bad) {
-  float m, r;
+  float beta1_m, r;
   if constexpr (MODE == kModeE4) {
-    m = e4_decode_m(w);
+    beta1_m = s.beta1_x2p112 * e4_decode_m_unscaled(w);
     r = e4_decode_r(w);
   } else {
-    m = f16_decode(w);
+    beta1_m = s.beta1 * f16_decode(w);
     r = f16_decode(w >> 16);
   }
   float p1, m1, v1;
-  adamw(p, g, m, r * r, s, p1, m1, v1);
+  adamw(p, g, beta1_m, r * r, s, p1, m1, v1);
   bad += nonfinite3(p1, m1, v1);
   p = p1;
   const float r1 = sqrt_rn(v1);
@@ -124,15 +168,13 @@ __device__ __forceinline__ uint32_t packed_elem(float& p, float g, uint32_t w, c
 __device__ __forceinline__ void fp32_elem(float& p, float g, float& m, float& v, const Scalars& s,
                                           uint32_t& bad) {
   float p1, m1, v1;
-  adamw(p, g, m, v, s, p1, m1, v1);
+  adamw(p, g, s.beta1 * m, v, s, p1, m1, v1);
   bad += nonfinite3(p1, m1, v1);
   p = p1;
   m = m1;
   v = v1;
 }
 
-__device__ __forceinline__ float& lane(float4& v, int k) { return reinterpret_cast<float*>(&v)[k]; }
-__device__ __forceinline__ uint32_t& lane(uint4& v, int k) { return reinterpret_cast<uint32_t*>(&v)[k]; }
 
 // One element at index i of tensor e (ragged edges only).
 template <int MODE>
@@ -161,51 +203,61 @@ __device__ __forceinline__ void run_tile(const Entry& e, long long tile, const S
   if (v0 >= e.phase && v0 + kTile <= vend) {
     // Whole tile inside the tensor: unguarded 16-byte vectors.
     const long long q0 = v0 / 4 + tid;
-    float4* P = reinterpret_cast<float4*>(e.p - e.phase);
-    const float4* G = reinterpret_cast<const float4*>(e.g - e.phase);
+    f32x4* P = reinterpret_cast<f32x4*>(e.p - e.phase);
+    const f32x4* G = reinterpret_cast<const f32x4*>(e.g - e.phase);
     if constexpr (MODE == kModeFp32) {
-      float4* M = reinterpret_cast<float4*>(static_cast<float*>(e.s0) - e.phase);
-      float4* V = reinterpret_cast<float4*>(e.s1 - e.phase);
-      float4 p[kUnroll], g[kUnroll], m[kUnroll], v[kUnroll];
+      f32x4* M = reinterpret_cast<f32x4*>(static_cast<float*>(e.s0) - e.phase);
+      f32x4* V = reinterpret_cast<f32x4*>(e.s1 - e.phase);
+      f32x4 p[kUnroll], g[kUnroll], m[kUnroll], v[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const long long q = q0 + (long long)u * kThreads;
-        p[u] = P[q];
-        g[u] = G[q];
-        m[u] = M[q];
-        v[u] = V[q];
+        p[u] = stream_load(P + q);
+        g[u] = stream_load(G + q);
+        m[u] = stream_load(M + q);
+        v[u] = stream_load(V + q);
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) fp32_elem(lane(p[u], k), lane(g[u], k), lane(m[u], k), lane(v[u], k), s, bad);
+        for (int k = 0; k < 4; ++k) {
+          float pk = p[u][k], mk = m[u][k], vk = v[u][k];
+          fp32_elem(pk, g[u][k], mk, vk, s, bad);
+          p[u][k] = pk;
+          m[u][k] = mk;
+          v[u][k] = vk;
+        }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const long long q = q0 + (long long)u * kThreads;
-        P[q] = p[u];
-        M[q] = m[u];
-        V[q] = v[u];
+        stream_store(P + q, p[u]);
+        stream_store(M + q, m[u]);
+        stream_store(V + q, v[u]);
       }
     } else {
-      uint4* W = reinterpret_cast<uint4*>(static_cast<uint32_t*>(e.s0) - e.phase);
-      float4 p[kUnroll], g[kUnroll];
-      uint4 w[kUnroll];
+      u32x4* W = reinterpret_cast<u32x4*>(static_cast<uint32_t*>(e.s0) - e.phase);
+      f32x4 p[kUnroll], g[kUnroll];
+      u32x4 w[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const long long q = q0 + (long long)u * kThreads;
-        p[u] = P[q];
-        g[u] = G[q];
-        w[u] = W[q];
+        p[u] = stream_load(P + q);
+        g[u] = stream_load(G + q);
+        w[u] = stream_load(W + q);
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) lane(w[u], k) = packed_elem<MODE>(lane(p[u], k), lane(g[u], k), lane(w[u], k), s, bad);
+        for (int k = 0; k < 4; ++k) {
+          float pk = p[u][k];
+          w[u][k] = packed_elem<MODE>(pk, g[u][k], w[u][k], s, bad);
+          p[u][k] = pk;
+        }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const long long q = q0 + (long long)u * kThreads;
-        P[q] = p[u];
-        W[q] = w[u];
+        stream_store(P + q, p[u]);
+        stream_store(W + q, w[u]);
       }
     }
   } else {
@@ -318,8 +370,8 @@ blockwise_kernel(BlockwiseArgs a, Scalars s, unsigned long long* nonfinite) {
         const float m = lut_m[(mc[h] >> (8 * k)) & 0xFFu] * am;
         const float v = lut_v[(vc[h] >> (8 * k)) & 0xFFu] * av;
         float p1;
-        adamw(reinterpret_cast<const float*>(&P)[k], reinterpret_cast<const float*>(&G)[k], m, v, s, p1,
-              m1[h * 4 + k], v1[h * 4 + k]);
+        adamw(reinterpret_cast<const float*>(&P)[k], reinterpret_cast<const float*>(&G)[k], s.beta1 * m, v, s,
+              p1, m1[h * 4 + k], v1[h * 4 + k]);
         bad += nonfinite3(p1, m1[h * 4 + k], v1[h * 4 + k]);
         bf[k] = bf16_encode(p1);
       }

@@ -51,6 +51,9 @@ int make_scalars(const pa_hyper* h, long long step, pa::Scalars* s) {
   s->lr_over_bc1 = (float)(lr / bc1);
   s->decay = (float)(1.0 - lr * wd);
   s->eps = (float)eps;
+  s->beta1_x2p112 = std::ldexp(s->beta1, 112);
+  s->pad_ = 0.0f;
+  s->inv_bc2 = 1.0 / (double)s->bc2;
   return PA_OK;
 }
 

@@ -30,8 +30,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "packed-AdamW step: params/s and achieved HBM GB/s (% of 8 TB/s) at 7B"
 PEAK_GBPS = 8000.0
-BYTES_PER_PARAM = {"e4": 20, "fp16": 20, "fp32": 28}
-WORKLOADS = {"single-262k": 1, "gpt-11m": 2, "gpt2-small-124m": 3, "llama-7b": 4}
+BYTES_PER_PARAM = {"e4": 20, "fp16": 20, "fp32": 28, "blockwise8": 14}
+WORKLOADS = {"single-262k": 1, "gpt-11m": 2, "gpt2-small-124m": 3, "llama-7b": 4, "blockwise-268m": 5}
 KERNEL_SOURCES = ("adamw_step_amd/csrc/kernels.hpp", "adamw_step_amd/csrc/codec.hpp",
                   "adamw_step_amd/csrc/pa_api.hip")
 
@@ -109,9 +109,32 @@ def calibrate_copy(nbytes):
     print(json.dumps({"calibrate_copy_bytes": nbytes, "launches": 3}), flush=True)
 
 
+def build_blockwise(cfg):
+    import torch
+    import workloads
+    n = workloads.total(cfg)
+    nb = n // 2048
+    qm, qv = workloads.code_maps()
+    zero_m = int((torch.from_numpy(qm) == 0).nonzero()[0])
+    p = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    g = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    workloads.device_fill_params(cfg, [p])
+    workloads.device_fill_grads(cfg, 1, [g])
+    state = (torch.full((n,), zero_m, dtype=torch.uint8, device="cuda:0"),
+             torch.zeros(nb, dtype=torch.float32, device="cuda:0"),
+             torch.zeros(n, dtype=torch.uint8, device="cuda:0"),
+             torch.zeros(nb, dtype=torch.float32, device="cuda:0"),
+             torch.from_numpy(qm).to("cuda:0"), torch.from_numpy(qv).to("cuda:0"),
+             torch.empty(n, dtype=torch.int16, device="cuda:0"))
+    torch.cuda.synchronize()
+    return [n], [p], [g], [state]
+
+
 def build_workload(cfg, mode):
     import torch
     import workloads
+    if mode == "blockwise8":
+        return build_blockwise(cfg)
     sizes = workloads.sizes(cfg)
     log(f"allocating {workloads.NAMES[cfg]}: {len(sizes)} tensors, {sum(sizes)} params")
     ps = [torch.empty(n, dtype=torch.float32, device="cuda:0") for n in sizes]
@@ -181,7 +204,7 @@ def main():
     ap.add_argument("--workload", default="llama-7b", choices=sorted(WORKLOADS))
     ap.add_argument("--mode", default="e4", choices=sorted(BYTES_PER_PARAM))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-params", type=int, default=400_000_000)
+    ap.add_argument("--cpu-sample-params", type=int, default=1_300_000_000)
     ap.add_argument("--probe", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0)
     args = ap.parse_args()
@@ -201,6 +224,9 @@ def main():
 
     cfg = WORKLOADS[args.workload]
     mode = args.mode
+    if (mode == "blockwise8") != (cfg == 5):
+        print("bench.py: the blockwise8 mode runs on the blockwise-268m workload and only there", file=sys.stderr)
+        sys.exit(2)
     sizes, ps, gs, states = build_workload(cfg, mode)
     n_params = sum(sizes)
     h = dict(workloads.HYPER)
@@ -209,7 +235,10 @@ def main():
     def step():
         nonlocal t
         t += 1
-        pa.pa_step_list(mode, ps, gs, states, h, t)
+        if mode == "blockwise8":
+            pa.pa_step(mode, ps[0], gs[0], states[0], h, t)
+        else:
+            pa.pa_step_list(mode, ps, gs, states, h, t)
 
     for _ in range(args.warmup):
         step()
@@ -232,6 +261,8 @@ def main():
         f"{mean_launch_ms:.3f} ms/launch (events), min {min(launch_ms):.3f}")
 
     algo_bytes = BYTES_PER_PARAM[mode] * n_params
+    if mode == "blockwise8":
+        algo_bytes += 16 * (n_params // 2048)     # absmax read and write, both moments
     achieved = algo_bytes / (mean_launch_ms / 1e3) / 1e9
     traffic = load_traffic(args.workload, mode)
     out = {
@@ -248,12 +279,14 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": args.workload, "params": n_params, "tensors": len(sizes),
-                   "mode": {"e4": "packed-e4m11-e4m12", "fp16": "packed-fp16", "fp32": "fp32-adamw"}[mode],
+                   "mode": {"e4": "packed-e4m11-e4m12", "fp16": "packed-fp16", "fp32": "fp32-adamw",
+                            "blockwise8": "blockwise-8bit-2048"}[mode],
                    "state_bytes_per_param": pa.pa_state_bytes(mode, 1),
                    "grads": "drawn once on the device, reused every step"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": f"elementwise_list<{mode}>", "algorithmic_bytes_per_launch": algo_bytes,
+                     "kernel": "blockwise_kernel" if mode == "blockwise8" else f"elementwise_list<{mode}>",
+                     "algorithmic_bytes_per_launch": algo_bytes,
                      "mean_launch_ms": round(mean_launch_ms, 4), "kernel_sha": kernel_sha()},
     }
     if args.probe:
@@ -262,7 +295,7 @@ def main():
         torch.cuda.empty_cache()
         out["probes"] = run_probes(grid=2048)
         log(f"probes: {out['probes']}")
-    if not args.no_cpu_baseline and not args.probe:
+    if not args.no_cpu_baseline and not args.probe and mode != "blockwise8":
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(cfg, mode, ps, gs, states, args.cpu_sample_params)
     print(json.dumps(out), flush=True)
