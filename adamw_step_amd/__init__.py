@@ -218,6 +218,42 @@ def pa_step_list(mode, params, grads, states, hyper, step, stream=None):
     _check(lib().pa_step_list(mode, k, P, G, S, N, ctypes.byref(h), int(step), _stream(stream)))
 
 
+class StepList:
+    """A fixed tensor list, validated and marshalled once.
+
+    ``step(hyper, t)`` is then a single call of pa_step_list with the cached
+    pointer arrays.  The tensors must stay alive and in place (same storage)
+    for as long as the object is used; build a new StepList if any of them
+    is reallocated.
+    """
+
+    def __init__(self, mode, params, grads, states):
+        self.mode = _mode(mode)
+        k = len(params)
+        if len(grads) != k or len(states) != k:
+            raise ValueError("params, grads and states must have the same length")
+        self._keep = [list(params), list(grads), list(states)]
+        self._structs = []
+        self._P = (ctypes.c_void_p * k)()
+        self._G = (ctypes.c_void_p * k)()
+        self._S = (ctypes.c_void_p * k)()
+        self._N = (ctypes.c_size_t * k)()
+        for i in range(k):
+            _check_pg(params[i], grads[i])
+            if params[i].device != params[0].device:
+                raise ValueError("all tensors of one call must be on one device")
+            self._P[i], self._G[i] = _ptr(params[i]), _ptr(grads[i])
+            self._S[i] = _state_arg(self.mode, params[i], states[i], self._structs)
+            self._N[i] = params[i].numel()
+        self.count = k
+        self._fn = lib().pa_step_list
+
+    def step(self, hyper, step, stream=None):
+        h = _hyper(hyper)
+        _check(self._fn(self.mode, self.count, self._P, self._G, self._S, self._N, ctypes.byref(h),
+                        int(step), _stream(stream)))
+
+
 def pa_state_bytes(mode, n):
     return int(lib().pa_state_bytes(_mode(mode), int(n)))
 

@@ -319,14 +319,44 @@ struct BlockwiseArgs {
   long long nblocks;
 };
 
-// Number of midpoints strictly below c (ties go to the lower map entry);
-// NaN is ordered above every number.  mid[0..254] ascending.
-__device__ __forceinline__ uint32_t search_mid(const float* mid, float c) {
-  uint32_t k = 0;
+// The 255 midpoints are kept in LDS in breadth-first (Eytzinger) order:
+// node t has children 2t+1 and 2t+2, and an in-order walk of the 255 nodes
+// gives the midpoints ascending.  Level l of the tree is the 2^l consecutive
+// entries starting at 2^l - 1, so every step of a search reads from one
+// short contiguous run of LDS words (few bank conflicts), unlike a bisection
+// of the sorted array whose late steps all land in a handful of banks.
+// Node t at level l, position p within the level, holds sorted midpoint
+// (2p + 1) * 2^(7 - l) - 1.
+__device__ __forceinline__ int eytzinger_sorted_index(int t) {
+  const int l = 31 - __builtin_clz(t + 1);   // level of node t
+  const int p = t + 1 - (1 << l);            // position within the level
+  return (2 * p + 1) * (1 << (7 - l)) - 1;
+}
+
+// Number of midpoints strictly below c (ties go to the lower map entry):
+// descend right exactly when the node's midpoint is below c; the leaf
+// reached, counted from the left, is that number.  NaN is ordered above
+// every number.
+__device__ __forceinline__ uint32_t search_mid(const float* tree, float c) {
+  uint32_t t = 0;
 #pragma unroll
-  for (uint32_t step = 128; step >= 1; step >>= 1)
-    if (mid[k + step - 1] < c) k += step;
-  return (c != c) ? 255u : k;
+  for (int level = 0; level < 8; ++level) t = 2 * t + 1 + (tree[t] < c ? 1u : 0u);
+  return (c != c) ? 255u : t - 255u;
+}
+
+// c / d for the block normaliser d (a positive normal binary32): the double
+// product with rd = 1/d rounded to double, rounded once to binary32, is the
+// correctly rounded quotient (the quotient of two binary32 numbers is either
+// one itself or at least 2^-49 relative away from every binary32 midpoint,
+// while the product is within 2^-52).  The one case that argument leaves
+// open is a quotient exactly on a midpoint of the subnormal range, so
+// nonzero products below the normal range take the hardware division
+// instead (a zero product is exact: x is zero or d is Inf).
+__device__ __forceinline__ float div_block(float x, float d, double rd) {
+  const double q = (double)x * rd;
+  float c = (float)q;
+  if (__builtin_expect(q != 0.0 && __builtin_fabs(q) < 0x1p-126, 0)) c = __fdiv_rn(x, d);
+  return c;
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
@@ -338,14 +368,20 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
 template <bool COUNT>
 __global__ void __launch_bounds__(kThreads)
 blockwise_kernel(BlockwiseArgs a, Scalars s, unsigned long long* nonfinite) {
-  __shared__ float lut_m[256], lut_v[256], mid_m[256], mid_v[256];
+  __shared__ float lut_m[256], lut_v[256], tree_m[256], tree_v[256];
   __shared__ uint32_t wave_max[2][kThreads / 64];
   const int tid = threadIdx.x;
   lut_m[tid] = a.qmap_m[tid];
   lut_v[tid] = a.qmap_v[tid];
   __syncthreads();
-  mid_m[tid] = tid < 255 ? (lut_m[tid] + lut_m[tid + 1]) * 0.5f : __builtin_inff();
-  mid_v[tid] = tid < 255 ? (lut_v[tid] + lut_v[tid + 1]) * 0.5f : __builtin_inff();
+  if (tid < 255) {
+    // midpoint j = (q_j + q_{j+1}) * 0.5 in binary32, stored at its tree node
+    const int j = eytzinger_sorted_index(tid);
+    tree_m[tid] = (lut_m[j] + lut_m[j + 1]) * 0.5f;
+    tree_v[tid] = (lut_v[j] + lut_v[j + 1]) * 0.5f;
+  } else {
+    tree_m[tid] = tree_v[tid] = __builtin_inff();
+  }
   __syncthreads();
 
   // The 1e-30 lower clamp of the normaliser, as a binary32 bit pattern.
@@ -406,13 +442,15 @@ blockwise_kernel(BlockwiseArgs a, Scalars s, unsigned long long* nonfinite) {
     __syncthreads();   // wave_max is rewritten by the next block
     const float dm = __uint_as_float(max(Am, floor_bits));
     const float dv = __uint_as_float(max(Av, floor_bits));
+    const double rdm = 1.0 / (double)dm;   // correctly rounded double division
+    const double rdv = 1.0 / (double)dv;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint32_t cm = 0, cv = 0;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        cm |= search_mid(mid_m, __fdiv_rn(m1[h * 4 + k], dm)) << (8 * k);
-        cv |= search_mid(mid_v, __fdiv_rn(v1[h * 4 + k], dv)) << (8 * k);
+        cm |= search_mid(tree_m, div_block(m1[h * 4 + k], dm, rdm)) << (8 * k);
+        cv |= search_mid(tree_v, div_block(v1[h * 4 + k], dv, rdv)) << (8 * k);
       }
       const long long e0 = base + h * 1024 + tid * 4;
       *reinterpret_cast<uint32_t*>(a.m_code + e0) = cm;

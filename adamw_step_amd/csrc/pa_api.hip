@@ -90,8 +90,15 @@ int device_info(int* dev_out, DeviceInfo* info) {
   return PA_OK;
 }
 
+// Workgroups per CU of a persistent launch: the occupancy calculator's figure
+// unless fixed at build time.
+#ifndef PA_BLOCKS_PER_CU
+#define PA_BLOCKS_PER_CU 0
+#endif
+
 long long grid_for(long long work_items, const DeviceInfo& d) {
-  const long long cap = (long long)d.cus * d.blocks_per_cu;
+  const long long per_cu = PA_BLOCKS_PER_CU > 0 ? PA_BLOCKS_PER_CU : d.blocks_per_cu;
+  const long long cap = (long long)d.cus * per_cu;
   return std::max(1LL, std::min(work_items, cap));
 }
 

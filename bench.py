@@ -3,7 +3,8 @@
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload llama-7b] [--mode e4]
 
 A step is one pa_step_list call (one persistent launch) over the whole
-parameter list of the workload, with parameters, gradients and state already
+parameter list of the workload, made through a StepList (the list is
+validated and marshalled once, as an optimizer object would hold it), with parameters, gradients and state already
 resident in HBM.  Default workload: the 291-tensor Llama-7B list
 (6,738,415,616 FP32 parameters, packed E4 state), gradients drawn once on the
 device and reused, 3 warm-up and 20 timed steps.
@@ -231,6 +232,7 @@ def main():
     n_params = sum(sizes)
     h = dict(workloads.HYPER)
     t = 0
+    prepared = None if mode == "blockwise8" else pa.StepList(mode, ps, gs, states)
 
     def step():
         nonlocal t
@@ -238,7 +240,7 @@ def main():
         if mode == "blockwise8":
             pa.pa_step(mode, ps[0], gs[0], states[0], h, t)
         else:
-            pa.pa_step_list(mode, ps, gs, states, h, t)
+            prepared.step(h, t)
 
     for _ in range(args.warmup):
         step()

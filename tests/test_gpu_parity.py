@@ -288,3 +288,36 @@ def test_blockwise_small_multi_step(pa):
         p = np.where(np.isnan(p), np.float32(0), p).astype(np.float32)
         dp = to_dev(p)
     assert int(counter.item()) == want_bad
+
+
+@pytest.mark.parametrize("mode", [E4, F32])
+def test_prepared_step_list(pa, mode):
+    """StepList (validated once, one C call per step) against the oracle."""
+    torch = _torch()
+    sizes = [4096 * 3 + 1, 7, 20000, 256]
+    r = np.random.Generator(np.random.PCG64(91))
+    hp = [r.normal(0, 0.02, n).astype(np.float32) for n in sizes]
+    dp = [to_dev(p) for p in hp]
+    dg = [torch.empty(n, dtype=torch.float32, device="cuda:0") for n in sizes]
+    if mode == F32:
+        hs = [(np.zeros(n, np.float32), np.zeros(n, np.float32)) for n in sizes]
+        ds = [(to_dev(m), to_dev(v)) for m, v in hs]
+    else:
+        hs = [np.zeros(n, np.uint32) for n in sizes]
+        ds = [to_dev(w) for w in hs]
+    sl = pa.StepList(mode, dp, dg, ds)
+    for t in range(1, 5):
+        hg = [r.normal(0, 1e-3, n).astype(np.float32) for n in sizes]
+        for d, g in zip(dg, hg):
+            d.copy_(torch.from_numpy(g))      # same storage, new values
+        banner(f"StepList mode {mode} step {t}")
+        sl.step(hyper(), t)
+        torch.cuda.synchronize()
+        for i in range(len(sizes)):
+            if mode == F32:
+                oracle.step_fp32(hp[i], hg[i], hs[i][0], hs[i][1], scalars(t))
+                assert_words(to_host(ds[i][0]).view(np.uint32), hs[i][0].view(np.uint32))
+            else:
+                oracle.step_packed(mode, hp[i], hg[i], hs[i], scalars(t))
+                assert_words(to_host(ds[i], np.uint32), hs[i])
+            assert_params(to_host(dp[i]), hp[i])
