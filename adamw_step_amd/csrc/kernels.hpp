@@ -319,29 +319,64 @@ struct BlockwiseArgs {
   long long nblocks;
 };
 
-// The 255 midpoints are kept in LDS in breadth-first (Eytzinger) order:
-// node t has children 2t+1 and 2t+2, and an in-order walk of the 255 nodes
-// gives the midpoints ascending.  Level l of the tree is the 2^l consecutive
-// entries starting at 2^l - 1, so every step of a search reads from one
-// short contiguous run of LDS words (few bank conflicts), unlike a bisection
-// of the sorted array whose late steps all land in a handful of banks.
-// Node t at level l, position p within the level, holds sorted midpoint
-// (2p + 1) * 2^(7 - l) - 1.
-__device__ __forceinline__ int eytzinger_sorted_index(int t) {
-  const int l = 31 - __builtin_clz(t + 1);   // level of node t
-  const int p = t + 1 - (1 << l);            // position within the level
-  return (2 * p + 1) * (1 << (7 - l)) - 1;
+// Midpoint search through a bucket table.
+//
+// A float's bit pattern, with the sign bit set for non-negative values and
+// every bit flipped for negative ones, is an unsigned key in the numeric
+// order of the floats.  Its top 13 bits pick one of 8192 buckets (a
+// sixteenth of a binade each); base[b] is the number of midpoints below the
+// bucket's smallest float.  A value's code, the number of midpoints strictly
+// below it, is base[b] plus the number of the bucket's own midpoints below
+// it.  When no bucket holds more than NCMP midpoints that is a plain count
+// over mid[base .. base+NCMP) (midpoints past the bucket are above the value,
+// and mid[255..258] = +Inf pads the end); fuller maps take a bisection over
+// the bucket, whose size is base[b+1] - base[b].  Ties go to the lower map
+// entry; NaN is ordered above every number.
+constexpr int kBucketShift = 19;
+constexpr int kBuckets = 1 << (32 - kBucketShift);
+constexpr int kMidPad = 260;
+
+__device__ __forceinline__ uint32_t order_key(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Number of midpoints strictly below c (ties go to the lower map entry):
-// descend right exactly when the node's midpoint is below c; the leaf
-// reached, counted from the left, is that number.  NaN is ordered above
-// every number.
-__device__ __forceinline__ uint32_t search_mid(const float* tree, float c) {
-  uint32_t t = 0;
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Number of sorted midpoints (mid[0..254]) below x, or at most x.
+__device__ __forceinline__ uint32_t count_below(const float* mid, float x, bool or_equal) {
+  uint32_t lo = 0, n = 255;
+  while (n > 0) {
+    const uint32_t half = n >> 1;
+    const float m = mid[lo + half];
+    const bool take = or_equal ? (m <= x) : (m < x);
+    if (take) { lo += half + 1; n -= half + 1; } else { n = half; }
+  }
+  return lo;
+}
+
+template <int NCMP>
+__device__ __forceinline__ uint32_t search_mid(const float* mid, const uint8_t* base, float c) {
+  const uint32_t b = order_key(c) >> kBucketShift;
+  uint32_t lo = base[b];
+  if constexpr (NCMP > 0) {
+    uint32_t code = lo;
 #pragma unroll
-  for (int level = 0; level < 8; ++level) t = 2 * t + 1 + (tree[t] < c ? 1u : 0u);
-  return (c != c) ? 255u : t - 255u;
+    for (int k = 0; k < NCMP; ++k) code += mid[lo + k] < c ? 1u : 0u;
+    lo = code;
+  } else {
+    uint32_t n = base[b + 1] > lo ? base[b + 1] - lo : 0u;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const uint32_t half = n >> 1;
+      const bool lt = mid[lo + half] < c;
+      lo = lt ? lo + half + 1 : lo;
+      n = lt ? n - half - 1 : half;
+    }
+  }
+  return (c != c) ? 255u : lo;
 }
 
 // c / d for the block normaliser d (a positive normal binary32): the double
@@ -349,13 +384,17 @@ __device__ __forceinline__ uint32_t search_mid(const float* tree, float c) {
 // correctly rounded quotient (the quotient of two binary32 numbers is either
 // one itself or at least 2^-49 relative away from every binary32 midpoint,
 // while the product is within 2^-52).  The one case that argument leaves
-// open is a quotient exactly on a midpoint of the subnormal range, so
-// nonzero products below the normal range take the hardware division
-// instead (a zero product is exact: x is zero or d is Inf).
+// open is a quotient exactly on a midpoint of the subnormal range.  With
+// GUARD, nonzero products below the normal range take the hardware division
+// instead; without it (used when no map midpoint lies within 2^-125 of
+// zero) every quotient in that range gets the same code anyway.
+template <bool GUARD>
 __device__ __forceinline__ float div_block(float x, float d, double rd) {
   const double q = (double)x * rd;
   float c = (float)q;
-  if (__builtin_expect(q != 0.0 && __builtin_fabs(q) < 0x1p-126, 0)) c = __fdiv_rn(x, d);
+  if constexpr (GUARD) {
+    if (__builtin_expect(q != 0.0 && __builtin_fabs(q) < 0x1p-126, 0)) c = __fdiv_rn(x, d);
+  }
   return c;
 }
 
@@ -365,49 +404,115 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
   return x;
 }
 
+// Codes of four values normalised by d, packed little-endian in 32 bits.
+template <int NCMP, bool GUARD>
+__device__ __forceinline__ uint32_t codes4(const float* x, float d, double rd, const float* mid,
+                                           const uint8_t* base) {
+  uint32_t out = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) out |= search_mid<NCMP>(mid, base, div_block<GUARD>(x[k], d, rd)) << (8 * k);
+  return out;
+}
+
+template <bool GUARD>
+__device__ __forceinline__ uint32_t codes4_dispatch(int ncmp, const float* x, float d, double rd,
+                                                    const float* mid, const uint8_t* base) {
+  switch (ncmp) {   // uniform across the workgroup
+    case 1: return codes4<1, GUARD>(x, d, rd, mid, base);
+    case 2: return codes4<2, GUARD>(x, d, rd, mid, base);
+    case 3: return codes4<3, GUARD>(x, d, rd, mid, base);
+    case 4: return codes4<4, GUARD>(x, d, rd, mid, base);
+    default: return codes4<0, GUARD>(x, d, rd, mid, base);
+  }
+}
+
+// Per-map search set-up in LDS: the padded midpoints, the bucket table, the
+// compare count of the fullest bucket (0 = bisection) and whether any
+// midpoint lies within 2^-125 of zero (then the normaliser keeps its guard).
+struct MapTables {
+  float mid[kMidPad];
+  uint8_t base[kBuckets + 4];
+};
+
+__device__ __forceinline__ void build_map(const float* lut, MapTables& t, uint32_t* red, int& ncmp, bool& guard) {
+  const int tid = threadIdx.x;
+  for (int j = tid; j < kMidPad; j += kThreads)
+    t.mid[j] = j < 255 ? (lut[j] + lut[j + 1]) * 0.5f : __builtin_inff();
+  __syncthreads();
+  uint32_t fullest = 0, near_zero = 0;
+  for (int b = tid; b < kBuckets; b += kThreads) {
+    const float lo = key_float((uint32_t)b << kBucketShift);
+    const float hi = key_float((((uint32_t)b + 1) << kBucketShift) - 1u);
+    const uint32_t below = count_below(t.mid, lo, false), upto = count_below(t.mid, hi, true);
+    t.base[b] = (uint8_t)below;
+    fullest = max(fullest, upto > below ? upto - below : 0u);
+  }
+  if (tid < 4) t.base[kBuckets + tid] = 255;
+  for (int j = tid; j < 255; j += kThreads) near_zero |= __builtin_fabsf(t.mid[j]) < 0x1p-125f ? 1u : 0u;
+  fullest = wave_max_u32(fullest);
+  near_zero = wave_max_u32(near_zero);
+  if ((tid & 63) == 0) red[tid >> 6] = fullest | (near_zero << 31);
+  __syncthreads();
+  uint32_t f = 0, nz = 0;
+  for (int w = 0; w < kThreads / 64; ++w) {
+    f = max(f, red[w] & 0x7FFFFFFFu);
+    nz |= red[w] >> 31;
+  }
+  guard = nz != 0;
+  ncmp = f == 0 ? 1 : (f <= 4 ? (int)f : 0);
+  __syncthreads();
+}
+
 template <bool COUNT>
 __global__ void __launch_bounds__(kThreads)
 blockwise_kernel(BlockwiseArgs a, Scalars s, unsigned long long* nonfinite) {
-  __shared__ float lut_m[256], lut_v[256], tree_m[256], tree_v[256];
+  __shared__ float lut_m[256], lut_v[256];
+  __shared__ MapTables tab_m, tab_v;
   __shared__ uint32_t wave_max[2][kThreads / 64];
   const int tid = threadIdx.x;
   lut_m[tid] = a.qmap_m[tid];
   lut_v[tid] = a.qmap_v[tid];
   __syncthreads();
-  if (tid < 255) {
-    // midpoint j = (q_j + q_{j+1}) * 0.5 in binary32, stored at its tree node
-    const int j = eytzinger_sorted_index(tid);
-    tree_m[tid] = (lut_m[j] + lut_m[j + 1]) * 0.5f;
-    tree_v[tid] = (lut_v[j] + lut_v[j + 1]) * 0.5f;
-  } else {
-    tree_m[tid] = tree_v[tid] = __builtin_inff();
-  }
-  __syncthreads();
+  int ncmp_m, ncmp_v;
+  bool guard_m, guard_v;
+  build_map(lut_m, tab_m, wave_max[0], ncmp_m, guard_m);
+  build_map(lut_v, tab_v, wave_max[1], ncmp_v, guard_v);
 
   // The 1e-30 lower clamp of the normaliser, as a binary32 bit pattern.
   const uint32_t floor_bits = __float_as_uint((float)1e-30);
   uint32_t bad = 0;
+  // Inputs of one block for this thread: elements base + h*1024 + 4*tid + k.
+  struct BlockIn {
+    f32x4 p[2], g[2];
+    uint32_t mc[2], vc[2];
+  };
+  auto load_block = [&](long long blk, BlockIn& in) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const long long e0 = blk * kBlock + h * 1024 + tid * 4;
+      in.p[h] = stream_load(reinterpret_cast<const f32x4*>(a.p + e0));
+      in.g[h] = stream_load(reinterpret_cast<const f32x4*>(a.g + e0));
+      in.mc[h] = *reinterpret_cast<const uint32_t*>(a.m_code + e0);
+      in.vc[h] = *reinterpret_cast<const uint32_t*>(a.v_code + e0);
+    }
+  };
+  BlockIn cur;
   for (long long b = blockIdx.x; b < a.nblocks; b += gridDim.x) {
     const long long base = b * kBlock;
     const float am = a.m_absmax[b];
     const float av = a.v_absmax[b];
+    load_block(b, cur);
     float m1[8], v1[8];
-    uint32_t mc[2], vc[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const long long e0 = base + h * 1024 + tid * 4;
-      const float4 P = *reinterpret_cast<const float4*>(a.p + e0);
-      const float4 G = *reinterpret_cast<const float4*>(a.g + e0);
-      mc[h] = *reinterpret_cast<const uint32_t*>(a.m_code + e0);
-      vc[h] = *reinterpret_cast<const uint32_t*>(a.v_code + e0);
       uint32_t bf[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float m = lut_m[(mc[h] >> (8 * k)) & 0xFFu] * am;
-        const float v = lut_v[(vc[h] >> (8 * k)) & 0xFFu] * av;
+        const float m = lut_m[(cur.mc[h] >> (8 * k)) & 0xFFu] * am;
+        const float v = lut_v[(cur.vc[h] >> (8 * k)) & 0xFFu] * av;
         float p1;
-        adamw(reinterpret_cast<const float*>(&P)[k], reinterpret_cast<const float*>(&G)[k], s.beta1 * m, v, s,
-              p1, m1[h * 4 + k], v1[h * 4 + k]);
+        adamw(cur.p[h][k], cur.g[h][k], s.beta1 * m, v, s, p1, m1[h * 4 + k], v1[h * 4 + k]);
         bad += nonfinite3(p1, m1[h * 4 + k], v1[h * 4 + k]);
         bf[k] = bf16_encode(p1);
       }
@@ -446,12 +551,10 @@ blockwise_kernel(BlockwiseArgs a, Scalars s, unsigned long long* nonfinite) {
     const double rdv = 1.0 / (double)dv;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      uint32_t cm = 0, cv = 0;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        cm |= search_mid(tree_m, div_block(m1[h * 4 + k], dm, rdm)) << (8 * k);
-        cv |= search_mid(tree_v, div_block(v1[h * 4 + k], dv, rdv)) << (8 * k);
-      }
+      const uint32_t cm = guard_m ? codes4_dispatch<true>(ncmp_m, m1 + 4 * h, dm, rdm, tab_m.mid, tab_m.base)
+                                  : codes4_dispatch<false>(ncmp_m, m1 + 4 * h, dm, rdm, tab_m.mid, tab_m.base);
+      const uint32_t cv = guard_v ? codes4_dispatch<true>(ncmp_v, v1 + 4 * h, dv, rdv, tab_v.mid, tab_v.base)
+                                  : codes4_dispatch<false>(ncmp_v, v1 + 4 * h, dv, rdv, tab_v.mid, tab_v.base);
       const long long e0 = base + h * 1024 + tid * 4;
       *reinterpret_cast<uint32_t*>(a.m_code + e0) = cm;
       *reinterpret_cast<uint32_t*>(a.v_code + e0) = cv;

@@ -61,7 +61,8 @@ int make_scalars(const pa_hyper* h, long long step, pa::Scalars* s) {
 
 struct DeviceInfo {
   int cus = 0;
-  int blocks_per_cu = 0;
+  int blocks_per_cu = 0;      // elementwise kernels
+  int bw_blocks_per_cu = 0;   // blockwise kernel
 };
 
 std::mutex g_dev_mu;
@@ -82,8 +83,13 @@ int device_info(int* dev_out, DeviceInfo* info) {
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
         &per, reinterpret_cast<const void*>(pa::elementwise_list<pa::kModeE4, false>), pa::kThreads, 0);
     if (e != hipSuccess || per < 1) per = 4;
+    int bw = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &bw, reinterpret_cast<const void*>(pa::blockwise_kernel<false>), pa::kThreads, 0);
+    if (e != hipSuccess || bw < 1) bw = 2;
     d.cus = cus;
     d.blocks_per_cu = per;
+    d.bw_blocks_per_cu = bw;
   }
   *dev_out = dev;
   *info = d;
@@ -96,8 +102,8 @@ int device_info(int* dev_out, DeviceInfo* info) {
 #define PA_BLOCKS_PER_CU 0
 #endif
 
-long long grid_for(long long work_items, const DeviceInfo& d) {
-  const long long per_cu = PA_BLOCKS_PER_CU > 0 ? PA_BLOCKS_PER_CU : d.blocks_per_cu;
+long long grid_for(long long work_items, const DeviceInfo& d, int occupancy) {
+  const long long per_cu = PA_BLOCKS_PER_CU > 0 ? PA_BLOCKS_PER_CU : occupancy;
   const long long cap = (long long)d.cus * per_cu;
   return std::max(1LL, std::min(work_items, cap));
 }
@@ -181,7 +187,7 @@ long long tiles_of(const pa::Entry& e) { return (e.n + e.phase + pa::kTile - 1) 
 template <int MODE>
 hipError_t launch_one(const pa::Entry& e, long long tiles, const pa::Scalars& s, unsigned long long* nf,
                       hipStream_t st, const DeviceInfo& d) {
-  const dim3 grid((unsigned)grid_for(tiles, d)), block(pa::kThreads);
+  const dim3 grid((unsigned)grid_for(tiles, d, d.blocks_per_cu)), block(pa::kThreads);
   if (nf)
     hipLaunchKernelGGL((pa::elementwise_one<MODE, true>), grid, block, 0, st, e, tiles, s, nf);
   else
@@ -192,7 +198,7 @@ hipError_t launch_one(const pa::Entry& e, long long tiles, const pa::Scalars& s,
 template <int MODE>
 hipError_t launch_list(const pa::Entry* table, long long tiles, const pa::Scalars& s, unsigned long long* nf,
                        hipStream_t st, const DeviceInfo& d) {
-  const dim3 grid((unsigned)grid_for(tiles, d)), block(pa::kThreads);
+  const dim3 grid((unsigned)grid_for(tiles, d, d.blocks_per_cu)), block(pa::kThreads);
   if (nf)
     hipLaunchKernelGGL((pa::elementwise_list<MODE, true>), grid, block, 0, st, table, tiles, s, nf);
   else
@@ -264,7 +270,7 @@ int blockwise_inputs_clear(const pa::BlockwiseArgs& a, size_t n, std::vector<Ran
 
 hipError_t launch_blockwise(const pa::BlockwiseArgs& a, const pa::Scalars& s, unsigned long long* nf,
                             hipStream_t st, const DeviceInfo& d) {
-  const dim3 grid((unsigned)grid_for(a.nblocks, d)), block(pa::kThreads);
+  const dim3 grid((unsigned)grid_for(a.nblocks, d, d.bw_blocks_per_cu)), block(pa::kThreads);
   if (nf)
     hipLaunchKernelGGL((pa::blockwise_kernel<true>), grid, block, 0, st, a, s, nf);
   else
@@ -537,7 +543,7 @@ int pa_debug_codec(int lane, int dir, const void* in, void* out, size_t n, void*
   int rc = device_info(&dev, &d);
   if (rc) return rc;
   const long long blocks = ((long long)n + pa::kThreads - 1) / pa::kThreads;
-  const dim3 grid((unsigned)grid_for(blocks, d)), block(pa::kThreads);
+  const dim3 grid((unsigned)grid_for(blocks, d, d.blocks_per_cu)), block(pa::kThreads);
   hipLaunchKernelGGL(pa::codec_kernel, grid, block, 0, static_cast<hipStream_t>(stream), lane, dir, in, out,
                      (long long)n);
   hipError_t e = hipGetLastError();
@@ -553,7 +559,7 @@ int pa_debug_sqrt(const float* in, float* out, size_t n, void* stream) {
   int rc = device_info(&dev, &d);
   if (rc) return rc;
   const long long blocks = ((long long)n + pa::kThreads - 1) / pa::kThreads;
-  const dim3 grid((unsigned)grid_for(blocks, d)), block(pa::kThreads);
+  const dim3 grid((unsigned)grid_for(blocks, d, d.blocks_per_cu)), block(pa::kThreads);
   hipLaunchKernelGGL(pa::sqrt_kernel, grid, block, 0, static_cast<hipStream_t>(stream), in, out, (long long)n);
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? PA_OK : hip_failed(e);

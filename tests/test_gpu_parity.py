@@ -321,3 +321,45 @@ def test_prepared_step_list(pa, mode):
                 oracle.step_packed(mode, hp[i], hg[i], hs[i], scalars(t))
                 assert_words(to_host(ds[i], np.uint32), hs[i])
             assert_params(to_host(dp[i]), hp[i])
+
+
+@pytest.mark.parametrize("kind", ["linear", "clustered"])
+def test_blockwise_other_maps(pa, kind):
+    """Blockwise mode with maps whose midpoints crowd into few buckets of the
+    search table (a linear map, and one with 200 entries packed into
+    [0.5, 0.5 + 2^-10]), against the oracle."""
+    torch = _torch()
+    nb = 16
+    n = nb * 2048
+    if kind == "linear":
+        qm = np.linspace(-1, 1, 256).astype(np.float32)
+        qv = np.linspace(0, 1, 256).astype(np.float32)
+    else:
+        inner = 0.5 + np.arange(200, dtype=np.float64) * 2.0 ** -18
+        rest = np.linspace(0.51, 1.0, 27)
+        pos = np.concatenate([[0.25], inner, rest])
+        qm = np.concatenate([-pos[::-1][:27], [0.0], pos])[:256].astype(np.float32)
+        qm = np.unique(qm)
+        qm = np.concatenate([qm, np.linspace(1.5, 2.0, 256 - qm.size)]).astype(np.float32)
+        qv = np.concatenate([[0.0], pos, np.linspace(1.1, 2.0, 255 - pos.size)]).astype(np.float32)
+    assert qm.size == 256 and qv.size == 256 and np.all(np.diff(qm) > 0) and np.all(np.diff(qv) > 0)
+    r = np.random.Generator(np.random.PCG64(66))
+    p = r.normal(0, 0.02, n).astype(np.float32)
+    mc = r.integers(0, 256, n, dtype=np.uint8)
+    vc = r.integers(0, 256, n, dtype=np.uint8)
+    ma = (10.0 ** r.uniform(-4, -1, nb)).astype(np.float32)
+    va = (10.0 ** r.uniform(-8, -4, nb)).astype(np.float32)
+    dst = [torch.from_numpy(mc.copy()).cuda(), to_dev(ma), torch.from_numpy(vc.copy()).cuda(), to_dev(va),
+           to_dev(qm), to_dev(qv), torch.zeros(n, dtype=torch.int16, device="cuda:0")]
+    hout = np.zeros(n, np.uint16)
+    for t in (1, 2):
+        g = (r.normal(0, 1e-2, n) * np.repeat(10.0 ** r.uniform(-2, 1, nb), 2048)).astype(np.float32)
+        banner(f"blockwise {kind} map step {t}")
+        pa.pa_step(BW, to_dev(p), to_dev(g), tuple(dst), hyper(), t)
+        torch.cuda.synchronize()
+        oracle.step_blockwise(p, g, mc, ma, vc, va, qm, qv, hout, scalars(t))
+        np.testing.assert_array_equal(to_host(dst[0]), mc)
+        np.testing.assert_array_equal(to_host(dst[2]), vc)
+        np.testing.assert_array_equal(to_host(dst[1]).view(np.uint32), ma.view(np.uint32))
+        np.testing.assert_array_equal(to_host(dst[3]).view(np.uint32), va.view(np.uint32))
+        np.testing.assert_array_equal(to_host(dst[6], np.uint16), hout)
