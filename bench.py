@@ -18,6 +18,9 @@ Other flags:
   --no-cpu-baseline       skip the oracle timing
   --probe                 also time a plain copy and a 3-in/2-out stream probe
   --calibrate-copy BYTES  only run the plain copy probe (for counter calibration)
+  --train-gpt             instead: time a synthetic-token training step of the
+                          gpt-11m model (trainer/) with each optimizer and
+                          report the optimizer's share of the step
 """
 import argparse
 import hashlib
@@ -208,6 +211,7 @@ def main():
     ap.add_argument("--cpu-sample-params", type=int, default=1_300_000_000)
     ap.add_argument("--probe", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0)
+    ap.add_argument("--train-gpt", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -221,6 +225,15 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.train_gpt:
+        from trainer.loop import measure
+        rows = [measure(kind, steps=args.steps, warmup=args.warmup) for kind in ("e4", "fp32", "torch-fused")]
+        for r in rows:
+            r["opt_share"] = round(r["opt_ms"] / r["step_ms"], 4)
+            log(f"train {r['optimizer']}: {r['step_ms']:.3f} ms/step, optimizer {r['opt_ms']:.3f} ms")
+        print(json.dumps({"metric": "gpt-11m synthetic training step: optimizer share", "unit": "ms",
+                          "n_gpus": 1, "data": "synthetic", "rows": rows}), flush=True)
         return
 
     cfg = WORKLOADS[args.workload]
