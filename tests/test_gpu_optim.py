@@ -105,4 +105,5 @@ def test_short_training_run():
     banner("trainer: 30 synthetic updates")
     losses = train(model, opt, tape, 30, 3e-3, 5, "cuda:0")
     assert all(np.isfinite(losses)) and opt.nonfinite_count() == 0
-    assert losses[-1] < losses[0]      # memorises token statistics even on random tapes
+    # uniformly random tokens carry nothing to learn: the loss stays near ln(vocab)
+    assert abs(np.mean(losses[-10:]) - np.log(12096)) < 0.5
