@@ -161,3 +161,14 @@ def test_product_path_never_imports_oracle():
         text = f.read()
     assert "codec.hpp" not in text and "kernels.hpp" not in text and "pa.h" not in text
     assert not math.isnan(0.0)
+
+
+def test_inspect_formats_runs_without_torch(pa):
+    """The inspection command imports no torch and agrees with the ledger."""
+    import subprocess
+    import sys as _sys
+    code = ("import sys; from adamw_step_amd import inspect_formats as f; "
+            "t = f.render(markdown=True); assert 'torch' not in sys.modules, 'torch imported'; print(t)")
+    r = subprocess.run([_sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert "bias 15" in r.stdout and "| 4 |" in r.stdout and "| 8 |" in r.stdout

@@ -105,3 +105,15 @@ def test_sqrt_every_float(pa):
         bad += int((got[~nan].view(np.uint32) != want[~nan].view(np.uint32)).sum())
         del bits, x, out
     assert bad == 0, f"{bad} square roots differ from IEEE"
+
+
+def test_inspect_formats_examples(pa):
+    """The inspection command's GPU examples: 1.5 is E4M11 0x7c00 (exponent 15,
+    mantissa 1024) and E4M12 0xf800; 2.0 saturates to 0x7fff / 0xffff."""
+    from adamw_step_amd.inspect_formats import examples
+    banner("inspect_formats --examples")
+    text = examples()
+    line15 = [l for l in text.splitlines() if l.strip().startswith("1.5 ")][0]
+    assert "0x7c00" in line15 and "0xf800" in line15
+    line2 = [l for l in text.splitlines() if l.strip().startswith("2 ")][0]
+    assert "0x7fff" in line2 and "0xffff" in line2
