@@ -68,8 +68,11 @@ class Format(ctypes.Structure):
                 ("block", ctypes.c_int)]
 
 
-EXPORTS = ("pa_step", "pa_step_list", "pa_state_bytes", "pa_format_info", "pa_status_string",
-           "pa_last_hip_error", "pa_release_plans", "pa_debug_codec", "pa_debug_sqrt")
+EXPORTS = ("pa_step", "pa_step_list", "pa_step_typed", "pa_step_list_typed", "pa_state_bytes",
+           "pa_format_info", "pa_status_string", "pa_last_hip_error", "pa_release_plans", "pa_debug_codec",
+           "pa_debug_sqrt")
+
+PA_DT_F32, PA_DT_BF16, PA_DT_F16 = 0, 1, 2
 
 _lib = None
 
@@ -90,6 +93,13 @@ def lib():
     L.pa_step_list.argtypes = [ctypes.c_int, sz, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
                                ctypes.POINTER(sz), ctypes.POINTER(Hyper), ctypes.c_longlong, vp]
     L.pa_step_list.restype = ctypes.c_int
+    L.pa_step_typed.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, sz, ctypes.POINTER(Hyper),
+                                ctypes.c_longlong, vp]
+    L.pa_step_typed.restype = ctypes.c_int
+    L.pa_step_list_typed.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, sz, ctypes.POINTER(vp),
+                                     ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(sz),
+                                     ctypes.POINTER(Hyper), ctypes.c_longlong, vp]
+    L.pa_step_list_typed.restype = ctypes.c_int
     L.pa_state_bytes.argtypes = [ctypes.c_int, sz]
     L.pa_state_bytes.restype = sz
     L.pa_format_info.argtypes = [ctypes.c_int, ctypes.POINTER(Format)]
@@ -144,14 +154,24 @@ def _tensor_ok(t, what):
         raise TypeError(f"{what} must be dense")
 
 
-def _check_pg(p, g):
+def _dtype_code(t):
     import torch
+    code = {torch.float32: PA_DT_F32, torch.bfloat16: PA_DT_BF16, torch.float16: PA_DT_F16}.get(t.dtype)
+    if code is None:
+        raise TypeError(f"unsupported tensor dtype {t.dtype} (float32, bfloat16, float16)")
+    return code
+
+
+def _check_pg(p, g):
+    """Validate one parameter/gradient pair; returns their dtype codes."""
     _tensor_ok(p, "params")
     _tensor_ok(g, "grads")
-    if p.dtype != torch.float32 or g.dtype != torch.float32:
-        raise TypeError("params and grads must be float32")
+    pdt, gdt = _dtype_code(p), _dtype_code(g)
+    if not (pdt == gdt or gdt == PA_DT_F32):
+        raise TypeError("grads must have the params' dtype, or be float32")
     if g.numel() != p.numel() or g.device != p.device:
         raise ValueError("grads must match params in size and device")
+    return pdt, gdt
 
 
 def _state_arg(mode, p, state, keep):
@@ -186,14 +206,15 @@ def _state_arg(mode, p, state, keep):
 
 
 def pa_step(mode, params, grads, state, hyper, step, stream=None):
-    """One tensor, updated in place (see include/pa.h)."""
+    """One tensor, updated in place (see include/pa.h).  float32, bfloat16
+    or float16 params; grads of the same dtype or float32."""
     mode = _mode(mode)
-    _check_pg(params, grads)
+    pdt, gdt = _check_pg(params, grads)
     keep = []
     st = _state_arg(mode, params, state, keep)
     h = _hyper(hyper)
-    _check(lib().pa_step(mode, _ptr(params), _ptr(grads), st, params.numel(), ctypes.byref(h),
-                         int(step), _stream(stream)))
+    _check(lib().pa_step_typed(mode, pdt, gdt, _ptr(params), _ptr(grads), st, params.numel(), ctypes.byref(h),
+                               int(step), _stream(stream)))
 
 
 def pa_step_list(mode, params, grads, states, hyper, step, stream=None):
@@ -207,15 +228,20 @@ def pa_step_list(mode, params, grads, states, hyper, step, stream=None):
     G = (ctypes.c_void_p * k)()
     S = (ctypes.c_void_p * k)()
     N = (ctypes.c_size_t * k)()
+    types = set()
     for i in range(k):
-        _check_pg(params[i], grads[i])
+        types.add(_check_pg(params[i], grads[i]))
         if params[i].device != params[0].device:
             raise ValueError("all tensors of one call must be on one device")
         P[i], G[i] = _ptr(params[i]), _ptr(grads[i])
         S[i] = _state_arg(mode, params[i], states[i], keep)
         N[i] = params[i].numel()
+    if len(types) > 1:
+        raise TypeError("all tensors of one call must share the params' and the grads' dtypes")
+    pdt, gdt = types.pop() if types else (PA_DT_F32, PA_DT_F32)
     h = _hyper(hyper)
-    _check(lib().pa_step_list(mode, k, P, G, S, N, ctypes.byref(h), int(step), _stream(stream)))
+    _check(lib().pa_step_list_typed(mode, pdt, gdt, k, P, G, S, N, ctypes.byref(h), int(step),
+                                    _stream(stream)))
 
 
 class StepList:
@@ -238,20 +264,24 @@ class StepList:
         self._G = (ctypes.c_void_p * k)()
         self._S = (ctypes.c_void_p * k)()
         self._N = (ctypes.c_size_t * k)()
+        types = set()
         for i in range(k):
-            _check_pg(params[i], grads[i])
+            types.add(_check_pg(params[i], grads[i]))
             if params[i].device != params[0].device:
                 raise ValueError("all tensors of one call must be on one device")
             self._P[i], self._G[i] = _ptr(params[i]), _ptr(grads[i])
             self._S[i] = _state_arg(self.mode, params[i], states[i], self._structs)
             self._N[i] = params[i].numel()
+        if len(types) > 1:
+            raise TypeError("all tensors of one call must share the params' and the grads' dtypes")
+        self.pdt, self.gdt = types.pop() if types else (PA_DT_F32, PA_DT_F32)
         self.count = k
-        self._fn = lib().pa_step_list
+        self._fn = lib().pa_step_list_typed
 
     def step(self, hyper, step, stream=None):
         h = _hyper(hyper)
-        _check(self._fn(self.mode, self.count, self._P, self._G, self._S, self._N, ctypes.byref(h),
-                        int(step), _stream(stream)))
+        _check(self._fn(self.mode, self.pdt, self.gdt, self.count, self._P, self._G, self._S, self._N,
+                        ctypes.byref(h), int(step), _stream(stream)))
 
 
 def pa_state_bytes(mode, n):

@@ -42,8 +42,8 @@ struct Scalars {
 // virtual index i + phase and virtual indices 4k..4k+3 form one aligned
 // 16-byte vector.
 struct Entry {
-  float* p;
-  const float* g;
+  void* p;           // parameters, element type PT of the launch
+  const void* g;     // gradients, element type GT
   void* s0;          // packed words, or the FP32 first moment
   float* s1;         // FP32 second moment (FP32 mode only)
   long long n;       // elements
@@ -67,6 +67,7 @@ struct Entry {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
 template <typename T>
 __device__ __forceinline__ T stream_load(const T* p) {
@@ -86,6 +87,32 @@ constexpr int kTile = kThreads * 4 * kUnroll;   // elements per tile
 constexpr int kBlock = 2048;                    // blockwise quantisation block
 
 enum { kModeFp32 = 0, kModeE4 = 1, kModeF16 = 2 };
+
+// Element types of parameters and gradients.  The update always runs in
+// FP32: 16-bit inputs widen exactly, and the new parameter is rounded back
+// to its own type, to nearest even (the KBench reference widens its inputs
+// with .float() and narrows its output with .to(bfloat16)).
+enum { kF32 = 0, kBF16 = 1, kF16 = 2 };
+
+template <int T> struct Elem;
+template <> struct Elem<kF32> {
+  using scalar = float;
+  using vec4 = f32x4;
+  static __device__ __forceinline__ float widen(float x) { return x; }
+  static __device__ __forceinline__ float narrow(float x) { return x; }
+};
+template <> struct Elem<kBF16> {
+  using scalar = uint16_t;
+  using vec4 = u16x4;
+  static __device__ __forceinline__ float widen(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+  static __device__ __forceinline__ uint16_t narrow(float x) { return (uint16_t)bf16_encode(x); }
+};
+template <> struct Elem<kF16> {
+  using scalar = uint16_t;
+  using vec4 = u16x4;
+  static __device__ __forceinline__ float widen(uint16_t x) { return f16_decode(x); }
+  static __device__ __forceinline__ uint16_t narrow(float x) { return (uint16_t)f16_encode(x); }
+};
 
 // Correctly rounded FP32 square root.
 //
@@ -177,10 +204,13 @@ __device__ __forceinline__ void fp32_elem(float& p, float g, float& m, float& v,
 
 
 // One element at index i of tensor e (ragged edges only).
-template <int MODE>
+template <int MODE, int PT, int GT>
 __device__ __forceinline__ void scalar_elem(const Entry& e, long long i, const Scalars& s, uint32_t& bad) {
-  float p = e.p[i];
-  const float g = e.g[i];
+  using PE = Elem<PT>;
+  using GE = Elem<GT>;
+  typename PE::scalar* P = static_cast<typename PE::scalar*>(e.p);
+  float p = PE::widen(P[i]);
+  const float g = GE::widen(static_cast<const typename GE::scalar*>(e.g)[i]);
   if constexpr (MODE == kModeFp32) {
     float* m = static_cast<float*>(e.s0);
     float mm = m[i], vv = e.s1[i];
@@ -191,24 +221,31 @@ __device__ __forceinline__ void scalar_elem(const Entry& e, long long i, const S
     uint32_t* w = static_cast<uint32_t*>(e.s0);
     w[i] = packed_elem<MODE>(p, g, w[i], s, bad);
   }
-  e.p[i] = p;
+  P[i] = PE::narrow(p);
 }
 
-// Tile `tile` (local to tensor e).
-template <int MODE>
+// Tile `tile` (local to tensor e).  Each thread moves four elements per
+// vector access of each stream: 16 bytes for FP32 data, 8 for 16-bit data.
+template <int MODE, int PT, int GT>
 __device__ __forceinline__ void run_tile(const Entry& e, long long tile, const Scalars& s, uint32_t& bad) {
+  using PE = Elem<PT>;
+  using GE = Elem<GT>;
+  using PV = typename PE::vec4;
+  using GV = typename GE::vec4;
   const long long v0 = tile * kTile;
   const long long vend = e.n + e.phase;
   const int tid = threadIdx.x;
   if (v0 >= e.phase && v0 + kTile <= vend) {
-    // Whole tile inside the tensor: unguarded 16-byte vectors.
+    // Whole tile inside the tensor: unguarded vector accesses.
     const long long q0 = v0 / 4 + tid;
-    f32x4* P = reinterpret_cast<f32x4*>(e.p - e.phase);
-    const f32x4* G = reinterpret_cast<const f32x4*>(e.g - e.phase);
+    PV* P = reinterpret_cast<PV*>(static_cast<typename PE::scalar*>(e.p) - e.phase);
+    const GV* G = reinterpret_cast<const GV*>(static_cast<const typename GE::scalar*>(e.g) - e.phase);
     if constexpr (MODE == kModeFp32) {
       f32x4* M = reinterpret_cast<f32x4*>(static_cast<float*>(e.s0) - e.phase);
       f32x4* V = reinterpret_cast<f32x4*>(e.s1 - e.phase);
-      f32x4 p[kUnroll], g[kUnroll], m[kUnroll], v[kUnroll];
+      PV p[kUnroll];
+      GV g[kUnroll];
+      f32x4 m[kUnroll], v[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const long long q = q0 + (long long)u * kThreads;
@@ -221,9 +258,9 @@ __device__ __forceinline__ void run_tile(const Entry& e, long long tile, const S
       for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          float pk = p[u][k], mk = m[u][k], vk = v[u][k];
-          fp32_elem(pk, g[u][k], mk, vk, s, bad);
-          p[u][k] = pk;
+          float pk = PE::widen(p[u][k]), mk = m[u][k], vk = v[u][k];
+          fp32_elem(pk, GE::widen(g[u][k]), mk, vk, s, bad);
+          p[u][k] = PE::narrow(pk);
           m[u][k] = mk;
           v[u][k] = vk;
         }
@@ -236,7 +273,8 @@ __device__ __forceinline__ void run_tile(const Entry& e, long long tile, const S
       }
     } else {
       u32x4* W = reinterpret_cast<u32x4*>(static_cast<uint32_t*>(e.s0) - e.phase);
-      f32x4 p[kUnroll], g[kUnroll];
+      PV p[kUnroll];
+      GV g[kUnroll];
       u32x4 w[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
@@ -249,9 +287,9 @@ __device__ __forceinline__ void run_tile(const Entry& e, long long tile, const S
       for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          float pk = p[u][k];
-          w[u][k] = packed_elem<MODE>(pk, g[u][k], w[u][k], s, bad);
-          p[u][k] = pk;
+          float pk = PE::widen(p[u][k]);
+          w[u][k] = packed_elem<MODE>(pk, GE::widen(g[u][k]), w[u][k], s, bad);
+          p[u][k] = PE::narrow(pk);
         }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
@@ -266,7 +304,7 @@ __device__ __forceinline__ void run_tile(const Entry& e, long long tile, const S
       const long long vb = v0 + ((long long)u * kThreads + tid) * 4;
       for (int k = 0; k < 4; ++k) {
         const long long vi = vb + k;
-        if (vi >= e.phase && vi < vend) scalar_elem<MODE>(e, vi - e.phase, s, bad);
+        if (vi >= e.phase && vi < vend) scalar_elem<MODE, PT, GT>(e, vi - e.phase, s, bad);
       }
     }
   }
@@ -280,7 +318,7 @@ __device__ __forceinline__ void flush_count(uint32_t bad, unsigned long long* co
 
 // Persistent multi-tensor launch.  table[count].tile0 holds the total tile
 // count (a sentinel), so the cursor never runs past the table.
-template <int MODE, bool COUNT>
+template <int MODE, int PT, int GT, bool COUNT>
 __global__ void __launch_bounds__(kThreads)
 elementwise_list(const Entry* __restrict__ table, long long total_tiles, Scalars s,
                  unsigned long long* nonfinite) {
@@ -289,17 +327,17 @@ elementwise_list(const Entry* __restrict__ table, long long total_tiles, Scalars
   for (long long tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
     while (tile >= table[t + 1].tile0) ++t;
     const Entry e = table[t];
-    run_tile<MODE>(e, tile - e.tile0, s, bad);
+    run_tile<MODE, PT, GT>(e, tile - e.tile0, s, bad);
   }
   if constexpr (COUNT) flush_count(bad, nonfinite);
 }
 
 // Single tensor, its entry passed by value (no table in device memory).
-template <int MODE, bool COUNT>
+template <int MODE, int PT, int GT, bool COUNT>
 __global__ void __launch_bounds__(kThreads)
 elementwise_one(Entry e, long long total_tiles, Scalars s, unsigned long long* nonfinite) {
   uint32_t bad = 0;
-  for (long long tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) run_tile<MODE>(e, tile, s, bad);
+  for (long long tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) run_tile<MODE, PT, GT>(e, tile, s, bad);
   if constexpr (COUNT) flush_count(bad, nonfinite);
 }
 

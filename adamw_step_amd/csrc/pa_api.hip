@@ -13,6 +13,7 @@
 #include <cstring>
 #include <list>
 #include <mutex>
+#include <type_traits>
 #include <vector>
 
 #include "../../include/pa.h"
@@ -81,7 +82,8 @@ int device_info(int* dev_out, DeviceInfo* info) {
     if (e != hipSuccess) return hip_failed(e);
     int per = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per, reinterpret_cast<const void*>(pa::elementwise_list<pa::kModeE4, false>), pa::kThreads, 0);
+        &per, reinterpret_cast<const void*>(pa::elementwise_list<pa::kModeE4, pa::kF32, pa::kF32, false>),
+        pa::kThreads, 0);
     if (e != hipSuccess || per < 1) per = 4;
     int bw = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
@@ -132,20 +134,31 @@ bool any_overlap(std::vector<Range>& r) {
 
 // One tensor of an elementwise mode: pointers of the tensor, checked.
 struct ElemTensor {
-  float* p;
-  const float* g;
+  void* p;
+  const void* g;
   void* s0;
   float* s1;
   size_t n;
+  int phase;
 };
 
-int check_elem_tensor(int mode, float* p, const float* g, void* state, size_t n, ElemTensor* out,
-                      std::vector<Range>* ranges) {
+size_t dtype_size(int dt) { return dt == PA_DT_F32 ? 4 : 2; }
+bool valid_dtype(int dt) { return dt == PA_DT_F32 || dt == PA_DT_BF16 || dt == PA_DT_F16; }
+
+// Parameter/gradient element-type pairs with a kernel: equal types, or
+// 16-bit parameters with FP32 gradients.
+bool valid_dtype_pair(int pdt, int gdt) {
+  return valid_dtype(pdt) && valid_dtype(gdt) && (pdt == gdt || gdt == PA_DT_F32);
+}
+
+int check_elem_tensor(int mode, int pdt, int gdt, void* p, const void* g, void* state, size_t n,
+                      ElemTensor* out, std::vector<Range>* ranges) {
   out->p = p;
   out->g = g;
   out->n = n;
   out->s0 = nullptr;
   out->s1 = nullptr;
+  out->phase = 0;
   if (n == 0) return PA_OK;
   if (p == nullptr || g == nullptr || state == nullptr) return PA_ERR_ARG;
   if (mode == PA_FP32) {
@@ -156,14 +169,23 @@ int check_elem_tensor(int mode, float* p, const float* g, void* state, size_t n,
   } else {
     out->s0 = state;
   }
-  const uintptr_t ph = reinterpret_cast<uintptr_t>(p) & 15u;
-  const void* bufs[4] = {p, g, out->s0, out->s1};
-  const int nb = mode == PA_FP32 ? 4 : 3;
-  for (int i = 0; i < nb; ++i) {
-    if (!aligned(bufs[i], 4)) return PA_ERR_ALIGN;
-    if ((reinterpret_cast<uintptr_t>(bufs[i]) & 15u) != ph) return PA_ERR_ALIGN;
+  // Every buffer aligned to its element, and all at one phase in elements
+  // modulo 4, so that elements 4k..4k+3 of every stream form one vector.
+  const size_t ps = dtype_size(pdt), gs = dtype_size(gdt);
+  const uintptr_t pa_ = reinterpret_cast<uintptr_t>(p), ga = reinterpret_cast<uintptr_t>(g);
+  if (pa_ % ps || ga % gs) return PA_ERR_ALIGN;
+  const uintptr_t ph = (pa_ / ps) & 3u;
+  if (((ga / gs) & 3u) != ph) return PA_ERR_ALIGN;
+  const void* st_bufs[2] = {out->s0, out->s1};
+  const int ns = mode == PA_FP32 ? 2 : 1;
+  for (int i = 0; i < ns; ++i) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(st_bufs[i]);
+    if (a % 4 || ((a / 4) & 3u) != ph) return PA_ERR_ALIGN;
   }
-  for (int i = 0; i < nb; ++i) ranges->push_back(range_of(bufs[i], n * 4));
+  out->phase = (int)ph;
+  ranges->push_back(range_of(p, n * ps));
+  ranges->push_back(range_of(g, n * gs));
+  for (int i = 0; i < ns; ++i) ranges->push_back(range_of(st_bufs[i], n * 4));
   return PA_OK;
 }
 
@@ -175,7 +197,7 @@ pa::Entry make_entry(const ElemTensor& t, long long tile0) {
   e.s1 = t.s1;
   e.n = (long long)t.n;
   e.tile0 = tile0;
-  e.phase = (int)((reinterpret_cast<uintptr_t>(t.p) & 15u) >> 2);
+  e.phase = t.phase;
   e.pad_ = 0;
   return e;
 }
@@ -184,44 +206,68 @@ long long tiles_of(const pa::Entry& e) { return (e.n + e.phase + pa::kTile - 1) 
 
 // ---------------------------------------------------------------- launches
 
-template <int MODE>
+template <int MODE, int PT, int GT>
 hipError_t launch_one(const pa::Entry& e, long long tiles, const pa::Scalars& s, unsigned long long* nf,
                       hipStream_t st, const DeviceInfo& d) {
   const dim3 grid((unsigned)grid_for(tiles, d, d.blocks_per_cu)), block(pa::kThreads);
   if (nf)
-    hipLaunchKernelGGL((pa::elementwise_one<MODE, true>), grid, block, 0, st, e, tiles, s, nf);
+    hipLaunchKernelGGL((pa::elementwise_one<MODE, PT, GT, true>), grid, block, 0, st, e, tiles, s, nf);
   else
-    hipLaunchKernelGGL((pa::elementwise_one<MODE, false>), grid, block, 0, st, e, tiles, s, nf);
+    hipLaunchKernelGGL((pa::elementwise_one<MODE, PT, GT, false>), grid, block, 0, st, e, tiles, s, nf);
   return hipGetLastError();
 }
 
-template <int MODE>
+template <int MODE, int PT, int GT>
 hipError_t launch_list(const pa::Entry* table, long long tiles, const pa::Scalars& s, unsigned long long* nf,
                        hipStream_t st, const DeviceInfo& d) {
   const dim3 grid((unsigned)grid_for(tiles, d, d.blocks_per_cu)), block(pa::kThreads);
   if (nf)
-    hipLaunchKernelGGL((pa::elementwise_list<MODE, true>), grid, block, 0, st, table, tiles, s, nf);
+    hipLaunchKernelGGL((pa::elementwise_list<MODE, PT, GT, true>), grid, block, 0, st, table, tiles, s, nf);
   else
-    hipLaunchKernelGGL((pa::elementwise_list<MODE, false>), grid, block, 0, st, table, tiles, s, nf);
+    hipLaunchKernelGGL((pa::elementwise_list<MODE, PT, GT, false>), grid, block, 0, st, table, tiles, s, nf);
   return hipGetLastError();
 }
 
-hipError_t dispatch_one(int mode, const pa::Entry& e, long long tiles, const pa::Scalars& s,
-                        unsigned long long* nf, hipStream_t st, const DeviceInfo& d) {
+// One launch for a (mode, parameter type, gradient type) triple; `L` is
+// launch_one or launch_list through the two lambdas below.
+template <int MODE, typename F>
+hipError_t by_types(int pdt, int gdt, F&& f) {
+  if (pdt == PA_DT_F32) return f(std::integral_constant<int, MODE>(), std::integral_constant<int, pa::kF32>(),
+                                 std::integral_constant<int, pa::kF32>());
+  if (pdt == PA_DT_BF16 && gdt == PA_DT_BF16)
+    return f(std::integral_constant<int, MODE>(), std::integral_constant<int, pa::kBF16>(),
+             std::integral_constant<int, pa::kBF16>());
+  if (pdt == PA_DT_BF16)
+    return f(std::integral_constant<int, MODE>(), std::integral_constant<int, pa::kBF16>(),
+             std::integral_constant<int, pa::kF32>());
+  if (gdt == PA_DT_F16)
+    return f(std::integral_constant<int, MODE>(), std::integral_constant<int, pa::kF16>(),
+             std::integral_constant<int, pa::kF16>());
+  return f(std::integral_constant<int, MODE>(), std::integral_constant<int, pa::kF16>(),
+           std::integral_constant<int, pa::kF32>());
+}
+
+template <typename F>
+hipError_t by_mode(int mode, int pdt, int gdt, F&& f) {
   switch (mode) {
-    case PA_FP32: return launch_one<pa::kModeFp32>(e, tiles, s, nf, st, d);
-    case PA_PACKED_E4: return launch_one<pa::kModeE4>(e, tiles, s, nf, st, d);
-    default: return launch_one<pa::kModeF16>(e, tiles, s, nf, st, d);
+    case PA_FP32: return by_types<pa::kModeFp32>(pdt, gdt, f);
+    case PA_PACKED_E4: return by_types<pa::kModeE4>(pdt, gdt, f);
+    default: return by_types<pa::kModeF16>(pdt, gdt, f);
   }
 }
 
-hipError_t dispatch_list(int mode, const pa::Entry* table, long long tiles, const pa::Scalars& s,
+hipError_t dispatch_one(int mode, int pdt, int gdt, const pa::Entry& e, long long tiles, const pa::Scalars& s,
+                        unsigned long long* nf, hipStream_t st, const DeviceInfo& d) {
+  return by_mode(mode, pdt, gdt, [&](auto m, auto pt, auto gt) {
+    return launch_one<decltype(m)::value, decltype(pt)::value, decltype(gt)::value>(e, tiles, s, nf, st, d);
+  });
+}
+
+hipError_t dispatch_list(int mode, int pdt, int gdt, const pa::Entry* table, long long tiles, const pa::Scalars& s,
                          unsigned long long* nf, hipStream_t st, const DeviceInfo& d) {
-  switch (mode) {
-    case PA_FP32: return launch_list<pa::kModeFp32>(table, tiles, s, nf, st, d);
-    case PA_PACKED_E4: return launch_list<pa::kModeE4>(table, tiles, s, nf, st, d);
-    default: return launch_list<pa::kModeF16>(table, tiles, s, nf, st, d);
-  }
+  return by_mode(mode, pdt, gdt, [&](auto m, auto pt, auto gt) {
+    return launch_list<decltype(m)::value, decltype(pt)::value, decltype(gt)::value>(table, tiles, s, nf, st, d);
+  });
 }
 
 // Blockwise: check one tensor's buffers.
@@ -283,6 +329,7 @@ hipError_t launch_blockwise(const pa::BlockwiseArgs& a, const pa::Scalars& s, un
 struct Plan {
   int device = -1;
   int mode = -1;
+  int pdt = 0, gdt = 0;
   std::vector<uintptr_t> key;   // per tensor: p, g, s0, s1, n
   pa::Entry* table = nullptr;   // device memory, count+1 entries
   long long tiles = 0;
@@ -311,9 +358,10 @@ bool valid_mode(int mode) { return mode >= PA_FP32 && mode <= PA_BLOCKWISE8; }
 
 extern "C" {
 
-int pa_step(int mode, float* params, const float* grads, void* state, size_t n, const pa_hyper* hyper,
-            long long step, void* stream) {
-  if (!valid_mode(mode)) return PA_ERR_ARG;
+int pa_step_typed(int mode, int param_dtype, int grad_dtype, void* params, const void* grads, void* state,
+                  size_t n, const pa_hyper* hyper, long long step, void* stream) {
+  if (!valid_mode(mode) || !valid_dtype_pair(param_dtype, grad_dtype)) return PA_ERR_ARG;
+  if (mode == PA_BLOCKWISE8 && (param_dtype != PA_DT_F32 || grad_dtype != PA_DT_F32)) return PA_ERR_ARG;
   pa::Scalars s;
   int rc = make_scalars(hyper, step, &s);
   if (rc) return rc;
@@ -324,7 +372,7 @@ int pa_step(int mode, float* params, const float* grads, void* state, size_t n, 
   if (mode == PA_BLOCKWISE8) {
     pa::BlockwiseArgs a;
     std::vector<Range> w;
-    rc = check_blockwise(params, grads, state, n, &a, &w);
+    rc = check_blockwise(static_cast<const float*>(params), static_cast<const float*>(grads), state, n, &a, &w);
     if (rc) return rc;
     if (any_overlap(w)) return PA_ERR_ALIAS;
     rc = blockwise_inputs_clear(a, n, w);
@@ -336,19 +384,26 @@ int pa_step(int mode, float* params, const float* grads, void* state, size_t n, 
   }
   ElemTensor t;
   std::vector<Range> ranges;
-  rc = check_elem_tensor(mode, params, grads, state, n, &t, &ranges);
+  rc = check_elem_tensor(mode, param_dtype, grad_dtype, params, grads, state, n, &t, &ranges);
   if (rc) return rc;
   if (any_overlap(ranges)) return PA_ERR_ALIAS;
   rc = device_info(&dev, &d);
   if (rc) return rc;
   const pa::Entry e = make_entry(t, 0);
-  hipError_t err = dispatch_one(mode, e, tiles_of(e), s, hyper->nonfinite, st, d);
+  hipError_t err = dispatch_one(mode, param_dtype, grad_dtype, e, tiles_of(e), s, hyper->nonfinite, st, d);
   return err == hipSuccess ? PA_OK : hip_failed(err);
 }
 
-int pa_step_list(int mode, size_t count, float* const* params, const float* const* grads, void* const* states,
-                 const size_t* n, const pa_hyper* hyper, long long step, void* stream) {
-  if (!valid_mode(mode)) return PA_ERR_ARG;
+int pa_step(int mode, float* params, const float* grads, void* state, size_t n, const pa_hyper* hyper,
+            long long step, void* stream) {
+  return pa_step_typed(mode, PA_DT_F32, PA_DT_F32, params, grads, state, n, hyper, step, stream);
+}
+
+int pa_step_list_typed(int mode, int param_dtype, int grad_dtype, size_t count, void* const* params,
+                       const void* const* grads, void* const* states, const size_t* n, const pa_hyper* hyper,
+                       long long step, void* stream) {
+  if (!valid_mode(mode) || !valid_dtype_pair(param_dtype, grad_dtype)) return PA_ERR_ARG;
+  if (mode == PA_BLOCKWISE8 && (param_dtype != PA_DT_F32 || grad_dtype != PA_DT_F32)) return PA_ERR_ARG;
   pa::Scalars s;
   int rc = make_scalars(hyper, step, &s);
   if (rc) return rc;
@@ -365,7 +420,8 @@ int pa_step_list(int mode, size_t count, float* const* params, const float* cons
       if (n[i] == 0) continue;
       pa::BlockwiseArgs a;
       std::vector<Range> w;
-      rc = check_blockwise(params[i], grads[i], states[i], n[i], &a, &w);
+      rc = check_blockwise(static_cast<const float*>(params[i]), static_cast<const float*>(grads[i]), states[i],
+                           n[i], &a, &w);
       if (rc) return rc;
       written.insert(written.end(), w.begin(), w.end());
       args.push_back(a);
@@ -406,8 +462,9 @@ int pa_step_list(int mode, size_t count, float* const* params, const float* cons
   }
 
   std::lock_guard<std::mutex> lk(g_plan_mu);
-  auto it = std::find_if(g_plans.begin(), g_plans.end(),
-                         [&](const Plan& p) { return p.device == dev && p.mode == mode && p.key == key; });
+  auto it = std::find_if(g_plans.begin(), g_plans.end(), [&](const Plan& p) {
+    return p.device == dev && p.mode == mode && p.pdt == param_dtype && p.gdt == grad_dtype && p.key == key;
+  });
   if (it == g_plans.end()) {
     // Validate and build the table once for this list.
     std::vector<pa::Entry> host;
@@ -415,7 +472,7 @@ int pa_step_list(int mode, size_t count, float* const* params, const float* cons
     long long tiles = 0;
     for (size_t i = 0; i < count; ++i) {
       ElemTensor t;
-      rc = check_elem_tensor(mode, params[i], grads[i], states[i], n[i], &t, &ranges);
+      rc = check_elem_tensor(mode, param_dtype, grad_dtype, params[i], grads[i], states[i], n[i], &t, &ranges);
       if (rc) return rc;
       if (t.n == 0) continue;
       pa::Entry e = make_entry(t, tiles);
@@ -431,6 +488,8 @@ int pa_step_list(int mode, size_t count, float* const* params, const float* cons
     Plan pl;
     pl.device = dev;
     pl.mode = mode;
+    pl.pdt = param_dtype;
+    pl.gdt = grad_dtype;
     pl.key = key;
     pl.tiles = tiles;
     hipError_t e = hipMalloc(reinterpret_cast<void**>(&pl.table), host.size() * sizeof(pa::Entry));
@@ -454,8 +513,14 @@ int pa_step_list(int mode, size_t count, float* const* params, const float* cons
     g_plans.splice(g_plans.begin(), g_plans, it);
     it = g_plans.begin();
   }
-  hipError_t e = dispatch_list(mode, it->table, it->tiles, s, hyper->nonfinite, st, d);
+  hipError_t e = dispatch_list(mode, param_dtype, grad_dtype, it->table, it->tiles, s, hyper->nonfinite, st, d);
   return e == hipSuccess ? PA_OK : hip_failed(e);
+}
+
+int pa_step_list(int mode, size_t count, float* const* params, const float* const* grads, void* const* states,
+                 const size_t* n, const pa_hyper* hyper, long long step, void* stream) {
+  return pa_step_list_typed(mode, PA_DT_F32, PA_DT_F32, count, reinterpret_cast<void* const*>(params),
+                            reinterpret_cast<const void* const*>(grads), states, n, hyper, step, stream);
 }
 
 size_t pa_state_bytes(int mode, size_t n) {

@@ -1,7 +1,8 @@
 """torch.optim front end of the packed-AdamW step.
 
 Follows the reference's execution contract (project page, Execution contract
-table): contiguous FP32 parameters and dense FP32 gradients on one device,
+table): contiguous parameters and dense gradients on one device (FP32, or
+bfloat16/float16 with the update still in FP32),
 one parameter group, one global step, ordinary PyTorch forward and backward
 around it.  Every update is one pa_step_list launch over all parameters
 (see include/pa.h); this module only holds the state tensors and marshals
@@ -47,18 +48,20 @@ class PackedAdamW(torch.optim.Optimizer):
         plist = self.param_groups[0]["params"]
         if not plist:
             raise ValueError("no parameters")
-        dev = plist[0].device
+        dev, dt = plist[0].device, plist[0].dtype
+        if dt not in (torch.float32, torch.bfloat16, torch.float16):
+            raise TypeError("parameters must be float32, bfloat16 or float16")
         for p in plist:
-            if p.dtype != torch.float32 or not p.is_cuda or not p.is_contiguous() or p.device != dev:
-                raise TypeError("parameters must be contiguous float32 tensors on one GPU")
+            if p.dtype != dt or not p.is_cuda or not p.is_contiguous() or p.device != dev:
+                raise TypeError("parameters must be contiguous tensors of one dtype on one GPU")
             self._init_state(p)
         self._nonfinite = torch.zeros(1, dtype=torch.int64, device=dev) if count_nonfinite else None
 
     def _init_state(self, p):
         st = self.state[p]
         if self._mode == PA_FP32:
-            st["exp_avg"] = torch.zeros_like(p)
-            st["exp_avg_sq"] = torch.zeros_like(p)
+            st["exp_avg"] = torch.zeros(p.numel(), dtype=torch.float32, device=p.device)
+            st["exp_avg_sq"] = torch.zeros(p.numel(), dtype=torch.float32, device=p.device)
         else:
             st["words"] = torch.zeros(p.numel(), dtype=torch.int32, device=p.device)
 

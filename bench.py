@@ -134,15 +134,16 @@ def build_blockwise(cfg):
     return [n], [p], [g], [state]
 
 
-def build_workload(cfg, mode):
+def build_workload(cfg, mode, param_dtype="fp32"):
     import torch
     import workloads
     if mode == "blockwise8":
         return build_blockwise(cfg)
     sizes = workloads.sizes(cfg)
     log(f"allocating {workloads.NAMES[cfg]}: {len(sizes)} tensors, {sum(sizes)} params")
-    ps = [torch.empty(n, dtype=torch.float32, device="cuda:0") for n in sizes]
-    gs = [torch.empty(n, dtype=torch.float32, device="cuda:0") for n in sizes]
+    dt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[param_dtype]
+    ps = [torch.empty(n, dtype=dt, device="cuda:0") for n in sizes]
+    gs = [torch.empty(n, dtype=dt, device="cuda:0") for n in sizes]
     if mode == "fp32":
         states = [(torch.zeros(n, dtype=torch.float32, device="cuda:0"),
                    torch.zeros(n, dtype=torch.float32, device="cuda:0")) for n in sizes]
@@ -212,6 +213,8 @@ def main():
     ap.add_argument("--probe", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0)
     ap.add_argument("--train-gpt", action="store_true")
+    ap.add_argument("--param-dtype", default="fp32", choices=["fp32", "bf16", "fp16"],
+                    help="element type of parameters and gradients (state unchanged)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -241,7 +244,10 @@ def main():
     if (mode == "blockwise8") != (cfg == 5):
         print("bench.py: the blockwise8 mode runs on the blockwise-268m workload and only there", file=sys.stderr)
         sys.exit(2)
-    sizes, ps, gs, states = build_workload(cfg, mode)
+    if mode == "blockwise8" and args.param_dtype != "fp32":
+        print("bench.py: the blockwise8 mode takes FP32 parameters", file=sys.stderr)
+        sys.exit(2)
+    sizes, ps, gs, states = build_workload(cfg, mode, args.param_dtype)
     n_params = sum(sizes)
     h = dict(workloads.HYPER)
     t = 0
@@ -276,6 +282,8 @@ def main():
         f"{mean_launch_ms:.3f} ms/launch (events), min {min(launch_ms):.3f}")
 
     algo_bytes = BYTES_PER_PARAM[mode] * n_params
+    if args.param_dtype != "fp32":
+        algo_bytes -= 6 * n_params      # 16-bit params (read + write) and grads: 2 bytes each instead of 4
     if mode == "blockwise8":
         algo_bytes += 16 * (n_params // 2048)     # absmax read and write, both moments
     achieved = algo_bytes / (mean_launch_ms / 1e3) / 1e9
@@ -291,12 +299,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32" if args.param_dtype == "fp32" else f"f32 math, {args.param_dtype} params and grads",
         "data": "synthetic",
         "config": {"workload": args.workload, "params": n_params, "tensors": len(sizes),
                    "mode": {"e4": "packed-e4m11-e4m12", "fp16": "packed-fp16", "fp32": "fp32-adamw",
                             "blockwise8": "blockwise-8bit-2048"}[mode],
                    "state_bytes_per_param": pa.pa_state_bytes(mode, 1),
+                   "param_dtype": args.param_dtype,
                    "grads": "drawn once on the device, reused every step"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
@@ -310,7 +319,7 @@ def main():
         torch.cuda.empty_cache()
         out["probes"] = run_probes(grid=2048)
         log(f"probes: {out['probes']}")
-    if not args.no_cpu_baseline and not args.probe and mode != "blockwise8":
+    if not args.no_cpu_baseline and not args.probe and mode != "blockwise8" and args.param_dtype == "fp32":
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(cfg, mode, ps, gs, states, args.cpu_sample_params)
     print(json.dumps(out), flush=True)

@@ -72,14 +72,28 @@ typedef enum {
   PA_BLOCKWISE8 = 3
 } pa_mode;
 
+/* Element types of parameters and gradients for the typed entry points.
+ * The update always runs in FP32: 16-bit values widen exactly and the new
+ * parameter is rounded back to its own type, to nearest even (Inf past the
+ * largest finite value).  The KBench quantized-optimizer-state reference
+ * widens its inputs with .float() and narrows its output to bfloat16; the
+ * TurboAdam package page, Verification, runs fp16, bf16 and fp32
+ * parameters. */
+typedef enum {
+  PA_DT_F32 = 0,
+  PA_DT_BF16 = 1,
+  PA_DT_F16 = 2
+} pa_dtype;
+
 enum {
   PA_OK = 0,
   PA_ERR_ARG = -1,    /* null pointer with n > 0, unknown mode, step < 1,
                          beta outside [0,1), non-finite or negative lr/eps/wd,
                          non-finite beta */
-  PA_ERR_ALIGN = -2,  /* a data pointer not 4-byte aligned (1-byte for codes),
-                         or params/grads/state words not sharing one 16-byte
-                         phase */
+  PA_ERR_ALIGN = -2,  /* a data pointer not aligned to its element, or the
+                         buffers of one tensor not at one position modulo
+                         four elements (one 16-byte phase for FP32 data);
+                         blockwise: params/grads not 16-byte aligned */
   PA_ERR_SHAPE = -3,  /* blockwise length not a multiple of 2048 */
   PA_ERR_ALIAS = -4,  /* two buffers of one call overlap */
   PA_ERR_DEVICE = -5, /* the HIP runtime refused a launch or a copy */
@@ -138,6 +152,22 @@ int pa_step(int mode, float* params, const float* grads, void* state, size_t n,
 int pa_step_list(int mode, size_t count, float* const* params, const float* const* grads,
                  void* const* states, const size_t* n, const pa_hyper* hyper, long long step,
                  void* stream);
+
+/* pa_step / pa_step_list with 16-bit parameters and/or gradients.
+ * Supported (param_dtype, grad_dtype) pairs: (F32, F32), (BF16, BF16),
+ * (F16, F16), (BF16, F32), (F16, F32); any other pair is PA_ERR_ARG, and
+ * so is a 16-bit type with PA_BLOCKWISE8.  `params` and `grads` point to n
+ * device elements of their type (bfloat16 / binary16 as uint16 bit
+ * patterns); state is as for pa_step.  Alignment: every buffer aligned to
+ * its element size, and all buffers of a tensor at the same position modulo
+ * four elements (PA_ERR_ALIGN otherwise).  pa_step and pa_step_list are the
+ * (F32, F32) case. */
+int pa_step_typed(int mode, int param_dtype, int grad_dtype, void* params, const void* grads, void* state,
+                  size_t n, const pa_hyper* hyper, long long step, void* stream);
+
+int pa_step_list_typed(int mode, int param_dtype, int grad_dtype, size_t count, void* const* params,
+                       const void* const* grads, void* const* states, const size_t* n,
+                       const pa_hyper* hyper, long long step, void* stream);
 
 /* Persistent optimizer-state bytes for n parameters in `mode` (the state
  * ledger; Packed AdamW Reference README, "The narrow result": 8 bytes per

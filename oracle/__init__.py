@@ -13,7 +13,7 @@ Lanes (argument ``lane`` of encode/decode):
     0  E4M11 signed first moment (low half of the packed word)
     1  E4M12 unsigned uncorrected RMS (high half of the packed word)
     2  IEEE binary16 (both halves of the FP16-first/FP16-RMS word)
-    3  bfloat16 (encode only: parameter output of the blockwise mode)
+    3  bfloat16 (parameter output of the blockwise mode; 16-bit parameters)
 
 Parity of the E4 exponent bias (15) is unpinned: the pages never print it.
 """
@@ -58,6 +58,9 @@ def _load():
     lib.oracle_step_blockwise.argtypes = [_f32p, _f32p, _u8p, _f32p, _u8p, _f32p, _f32p, _f32p,
                                           _u16p, ctypes.c_size_t, _f32p]
     lib.oracle_step_blockwise.restype = ctypes.c_ulonglong
+    lib.oracle_step_typed.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, _f32p]
+    lib.oracle_step_typed.restype = ctypes.c_ulonglong
     lib.oracle_search_codes.argtypes = [_f32p, _f32p, _u8p, ctypes.c_size_t]
     lib.oracle_search_codes.restype = None
     lib.oracle_num_threads.restype = ctypes.c_int
@@ -93,8 +96,6 @@ def encode(lane, x):
 
 
 def decode(lane, codes):
-    if lane == LANE_BF16:
-        raise ValueError("bfloat16 decode is not part of the oracle")
     c = np.ascontiguousarray(codes, dtype=np.uint16)
     out = np.empty(c.shape, np.float32)
     _load().oracle_decode_batch(int(lane), _ptr(c, _u16p), _ptr(out, _f32p), c.size)
@@ -150,6 +151,34 @@ def step_blockwise(p, g, m_code, m_absmax, v_code, v_absmax, qmap_m, qmap_v, p_o
         _ptr(v_code, _u8p), _ptr(v_absmax, _f32p), _ptr(qmap_m, _f32p), _ptr(qmap_v, _f32p),
         _ptr(p_out, _u16p), n, _ptr(sc, _f32p))
     return int(r)
+
+
+DT_F32, DT_BF16, DT_F16 = 0, 1, 2
+_DT_NP = {DT_F32: np.float32, DT_BF16: np.uint16, DT_F16: np.uint16}
+
+
+def step_typed(state_kind, pdt, gdt, p, g, state, sc):
+    """Typed step: p, g are float32 arrays (dtype 0) or uint16 bit patterns of
+    bfloat16 (1) / binary16 (2).  state_kind 0: state = (m, v) float32;
+    1: packed E4 words (uint32); 2: packed binary16 words.  In place on p
+    and the state.  Returns the non-finite count."""
+    _need(p, _DT_NP[pdt], "p")
+    _need(g, _DT_NP[gdt], "g")
+    _need(sc, np.float32, "scalars")
+    n = p.size
+    assert g.size == n
+    if state_kind == 0:
+        m, v = state
+        _need(m, np.float32, "m")
+        _need(v, np.float32, "v")
+        assert m.size == n and v.size == n
+        s0, s1 = m.ctypes.data, v.ctypes.data
+    else:
+        _need(state, np.uint32, "words")
+        assert state.size == n
+        s0, s1 = state.ctypes.data, None
+    return int(_load().oracle_step_typed(int(state_kind), int(pdt), int(gdt), p.ctypes.data, g.ctypes.data,
+                                         s0, s1, n, _ptr(sc, _f32p)))
 
 
 def search_codes(qmap, c):

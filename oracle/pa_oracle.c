@@ -161,7 +161,18 @@ uint16_t oracle_encode_f16(float x) {
     return (uint16_t)(sign | nearest_code(tab_h, 0x7C01, fabs((double)x)));
 }
 
-/* bfloat16 (the parameter output of the blockwise mode). */
+/* bfloat16 (the parameter output of the blockwise mode, and 16-bit
+ * parameters/gradients of the typed step). */
+float oracle_decode_bf16(uint16_t code) {
+    build_tables();
+    unsigned mag = code & 0x7FFF;
+    double v;
+    if (mag < 0x7F80) v = tab_bf[mag];
+    else if (mag == 0x7F80) v = INFINITY;
+    else v = NAN;
+    return (float)((code & 0x8000) ? -v : v);
+}
+
 uint16_t oracle_encode_bf16(float x) {
     build_tables();
     unsigned sign = signbit(x) ? 0x8000u : 0u;
@@ -190,7 +201,8 @@ void oracle_decode_batch(int lane, const uint16_t* c, float* out, size_t n) {
         switch (lane) {
             case 0: out[i] = oracle_decode_m_e4(c[i]); break;
             case 1: out[i] = oracle_decode_r_e4(c[i]); break;
-            default: out[i] = oracle_decode_f16(c[i]); break;
+            case 2: out[i] = oracle_decode_f16(c[i]); break;
+            default: out[i] = oracle_decode_bf16(c[i]); break;
         }
     }
 }
@@ -314,6 +326,63 @@ unsigned long long oracle_step_packed(int lane_kind, float* p, const float* g, u
         }
         p[i] = e.p1;
         w[i] = ((uint32_t)rc << 16) | (uint32_t)mc;
+        bad += (unsigned long long)elem_nonfinite(&e);
+    }
+    return bad;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Typed parameters and gradients.                                         */
+/* ---------------------------------------------------------------------- */
+
+/* Element types: 0 binary32, 1 bfloat16, 2 binary16 (16-bit ones as their
+ * bit patterns).  The KBench reference widens parameters and gradients to
+ * FP32 before the update and narrows the new parameters afterwards; here a
+ * 16-bit value widens exactly and the new parameter is rounded to nearest
+ * even in its own type. */
+static float widen_at(int dt, const void* base, size_t i) {
+    if (dt == 0) return ((const float*)base)[i];
+    uint16_t c = ((const uint16_t*)base)[i];
+    return dt == 1 ? oracle_decode_bf16(c) : oracle_decode_f16(c);
+}
+
+static void narrow_at(int dt, void* base, size_t i, float x) {
+    if (dt == 0) ((float*)base)[i] = x;
+    else ((uint16_t*)base)[i] = dt == 1 ? oracle_encode_bf16(x) : oracle_encode_f16(x);
+}
+
+/* One step over n elements with typed parameters (pdt) and gradients (gdt).
+ * state_kind 0: FP32 moments in s0 (m) and s1 (v); 1: packed E4 words in s0;
+ * 2: packed binary16 words in s0.  Returns the non-finite count. */
+unsigned long long oracle_step_typed(int state_kind, int pdt, int gdt, void* p, const void* g,
+                                     void* s0, void* s1, size_t n, const float s[8]) {
+    build_tables();
+    unsigned long long bad = 0;
+    ptrdiff_t i;
+#pragma omp parallel for schedule(static) reduction(+ : bad)
+    for (i = 0; i < (ptrdiff_t)n; ++i) {
+        float pw = widen_at(pdt, p, (size_t)i);
+        float gw = widen_at(gdt, g, (size_t)i);
+        oracle_elem e;
+        if (state_kind == 0) {
+            float* m = (float*)s0;
+            float* v = (float*)s1;
+            e = adamw_element(pw, gw, m[i], v[i], s);
+            m[i] = e.m1;
+            v[i] = e.v1;
+        } else {
+            uint32_t* w = (uint32_t*)s0;
+            uint16_t lo = (uint16_t)(w[i] & 0xFFFFu), hi = (uint16_t)(w[i] >> 16);
+            float m = state_kind == 1 ? oracle_decode_m_e4(lo) : oracle_decode_f16(lo);
+            float r = state_kind == 1 ? oracle_decode_r_e4(hi) : oracle_decode_f16(hi);
+            float v = r * r;
+            e = adamw_element(pw, gw, m, v, s);
+            float r1 = sqrtf(e.v1);
+            uint16_t mc = state_kind == 1 ? oracle_encode_m_e4(e.m1) : oracle_encode_f16(e.m1);
+            uint16_t rc = state_kind == 1 ? oracle_encode_r_e4(r1) : oracle_encode_f16(r1);
+            w[i] = ((uint32_t)rc << 16) | (uint32_t)mc;
+        }
+        narrow_at(pdt, p, (size_t)i, e.p1);
         bad += (unsigned long long)elem_nonfinite(&e);
     }
     return bad;

@@ -172,3 +172,25 @@ def test_inspect_formats_runs_without_torch(pa):
     r = subprocess.run([_sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
     assert "bias 15" in r.stdout and "| 4 |" in r.stdout and "| 8 |" in r.stdout
+
+
+def test_typed_argument_rules(pa):
+    h = _hyper(pa)
+    L = pa.lib()
+    L.pa_step_typed.argtypes = None
+    f = lambda mode, pdt, gdt, p, g, s, n: L.pa_step_typed(mode, pdt, gdt, ctypes.c_void_p(p), ctypes.c_void_p(g),
+                                                             ctypes.c_void_p(s), ctypes.c_size_t(n), ctypes.byref(h),
+                                                             ctypes.c_longlong(1), None)
+    assert f(1, 1, 2, FAKE, FAKE + 8192, FAKE + 16384, 64) == pa.PA_ERR_ARG      # bf16 params, f16 grads
+    assert f(1, 0, 1, FAKE, FAKE + 8192, FAKE + 16384, 64) == pa.PA_ERR_ARG      # f32 params, bf16 grads
+    assert f(1, 3, 3, FAKE, FAKE + 8192, FAKE + 16384, 64) == pa.PA_ERR_ARG      # unknown dtype
+    bw = pa.BlockwiseState(FAKE + 2 ** 20, FAKE + 2 ** 21, FAKE + 2 ** 22, FAKE + 2 ** 23,
+                           FAKE + 2 ** 24, FAKE + 2 ** 25, FAKE + 2 ** 26)
+    assert f(3, 1, 1, FAKE, FAKE + 2 ** 18, ctypes.addressof(bw), 2048) == pa.PA_ERR_ARG   # blockwise 16-bit
+    assert f(1, 1, 1, FAKE + 1, FAKE + 8193, FAKE + 16384, 64) == pa.PA_ERR_ALIGN           # odd address
+    # bf16 params and grads at element phase 1, words at element phase 2
+    assert f(1, 1, 1, FAKE + 2, FAKE + 8194, FAKE + 16392, 64) == pa.PA_ERR_ALIGN
+    # bf16 params at phase 1, f32 grads at phase 0
+    assert f(1, 1, 0, FAKE + 2, FAKE + 8192, FAKE + 16388, 64) == pa.PA_ERR_ALIGN
+    # overlapping bf16 params and words
+    assert f(1, 1, 1, FAKE, FAKE + 65536, FAKE + 64, 64) == pa.PA_ERR_ALIAS

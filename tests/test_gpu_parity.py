@@ -363,3 +363,87 @@ def test_blockwise_other_maps(pa, kind):
         np.testing.assert_array_equal(to_host(dst[1]).view(np.uint32), ma.view(np.uint32))
         np.testing.assert_array_equal(to_host(dst[3]).view(np.uint32), va.view(np.uint32))
         np.testing.assert_array_equal(to_host(dst[6], np.uint16), hout)
+
+
+TYPE_PAIRS = [(1, 1), (2, 2), (1, 0), (2, 0)]       # (param dtype, grad dtype): bf16/f16, 16-bit params + f32 grads
+
+
+def _typed_case(pa, mode, pdt, gdt, n, phase, steps, seed):
+    torch = _torch()
+    tdt = {0: torch.float32, 1: torch.bfloat16, 2: torch.float16}
+    lane = {1: 3, 2: 2}
+    r = np.random.Generator(np.random.PCG64(seed))
+
+    def host16(x, dt):
+        return oracle.encode(lane[dt], x) if dt else x.astype(np.float32)
+
+    def dev_at(host, dt):
+        big = torch.zeros(n + 8, dtype=tdt[dt] if host.dtype != np.uint32 else torch.int32, device="cuda:0")
+        view = big[phase:phase + n]
+        src = torch.from_numpy(host.view(np.int16) if host.dtype == np.uint16 else
+                               (host.view(np.int32) if host.dtype == np.uint32 else host))
+        view.view(src.dtype).copy_(src.to("cuda:0"))
+        return big, view
+
+    hp = host16(r.normal(0, 0.02, n).astype(np.float32), pdt)
+    _, dp = dev_at(hp, pdt)
+    if mode == F32:
+        hs = (np.zeros(n, np.float32), np.zeros(n, np.float32))
+        keep = [dev_at(hs[0], 0), dev_at(hs[1], 0)]
+        ds = (keep[0][1], keep[1][1])
+    else:
+        hs = _random_state(mode, n, seed + 1)
+        keep = dev_at(hs, 0)
+        ds = keep[1].view(torch.int32)
+    for t in range(1, steps + 1):
+        hg = host16((r.normal(0, 1, n) * 1e-3).astype(np.float32), gdt)
+        _, dg = dev_at(hg, gdt)
+        pa.pa_step(mode, dp, dg, ds, hyper(), t)
+        torch.cuda.synchronize()
+        oracle.step_typed({F32: 0, E4: 1, F16: 2}[mode], pdt, gdt, hp, hg, hs, scalars(t))
+        got_p = dp.cpu().view(torch.int16).numpy().view(np.uint16) if pdt else dp.cpu().numpy()
+        if pdt:
+            nan = ((hp & 0x7F80) == 0x7F80) & ((hp & 0x7F) != 0) if pdt == 1 else ((hp & 0x7C00) == 0x7C00) & ((hp & 0x3FF) != 0)
+            np.testing.assert_array_equal(got_p[~nan], hp[~nan])
+        else:
+            assert_params(got_p, hp)
+        if mode == F32:
+            assert_words(ds[0].cpu().numpy().view(np.uint32), hs[0].view(np.uint32), what="m")
+            assert_words(ds[1].cpu().numpy().view(np.uint32), hs[1].view(np.uint32), what="v")
+        else:
+            assert_words(ds.cpu().numpy().view(np.uint32), hs, fp16=(mode == F16))
+
+
+@pytest.mark.parametrize("mode", [E4, F16, F32])
+@pytest.mark.parametrize("pdt,gdt", TYPE_PAIRS)
+def test_typed_params_and_grads(pa, mode, pdt, gdt):
+    """16-bit parameters (and gradients): the new parameter, rounded to its
+    own type, and the state equal the oracle's bit for bit."""
+    for n in (5, 4097, 100003):
+        for phase in (0, 1, 3):
+            banner(f"typed mode {mode} pdt {pdt} gdt {gdt} n {n} phase {phase}")
+            _typed_case(pa, mode, pdt, gdt, n, phase, steps=2, seed=n + phase)
+
+
+def test_typed_list_bf16(pa):
+    """A bfloat16 parameter list through StepList (one launch)."""
+    torch = _torch()
+    sizes = [4096 * 5 + 1, 33, 70000]
+    r = np.random.Generator(np.random.PCG64(123))
+    hp = [oracle.encode(3, r.normal(0, 0.02, n).astype(np.float32)) for n in sizes]
+    dp = [torch.from_numpy(h.view(np.int16).copy()).cuda().view(torch.bfloat16) for h in hp]
+    dg = [torch.empty(n, dtype=torch.bfloat16, device="cuda:0") for n in sizes]
+    hw = [np.zeros(n, np.uint32) for n in sizes]
+    dw = [torch.zeros(n, dtype=torch.int32, device="cuda:0") for n in sizes]
+    sl = pa.StepList(E4, dp, dg, dw)
+    for t in range(1, 4):
+        hg = [oracle.encode(3, r.normal(0, 1e-3, n).astype(np.float32)) for n in sizes]
+        for d, g in zip(dg, hg):
+            d.view(torch.int16).copy_(torch.from_numpy(g.view(np.int16)))
+        banner(f"bf16 StepList step {t}")
+        sl.step(hyper(), t)
+        torch.cuda.synchronize()
+        for i in range(len(sizes)):
+            oracle.step_typed(1, 1, 1, hp[i], hg[i], hw[i], scalars(t))
+            np.testing.assert_array_equal(dp[i].view(torch.int16).cpu().numpy().view(np.uint16), hp[i])
+            assert_words(dw[i].cpu().numpy().view(np.uint32), hw[i])

@@ -268,3 +268,61 @@ def test_e4_tracks_fp32_over_steps(oracle_mod):
         bound = 0.9 * bound + np.abs(mq.astype(np.float64)) * 2.0 ** -12 + 2.0 ** -26
     # the FP32 and packed runs see slightly different moments, hence the 2x margin
     assert np.all(np.abs(mq.astype(np.float64) - m) <= 2 * bound)
+
+
+def test_bf16_decode_against_torch(oracle_mod):
+    torch = pytest.importorskip("torch")
+    c = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = oracle_mod.decode(3, c)
+    want = torch.from_numpy(c.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    np.testing.assert_array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
+
+
+@pytest.mark.parametrize("kind", [0, 1, 2])
+def test_typed_f32_equals_untyped(oracle_mod, kind):
+    n = 5000
+    r = np.random.Generator(np.random.PCG64(31))
+    p = r.normal(0, 0.02, n).astype(np.float32)
+    g = r.normal(0, 1e-3, n).astype(np.float32)
+    s = sc(3)
+    if kind == 0:
+        st_a = (r.normal(0, 1e-3, n).astype(np.float32), (r.normal(0, 1e-3, n) ** 2).astype(np.float32))
+        st_b = (st_a[0].copy(), st_a[1].copy())
+        pa_, pb = p.copy(), p.copy()
+        oracle_mod.step_fp32(pa_, g, st_a[0], st_a[1], s)
+        oracle_mod.step_typed(0, 0, 0, pb, g, st_b, s)
+        np.testing.assert_array_equal(st_a[1].view(np.uint32), st_b[1].view(np.uint32))
+    else:
+        wa = r.integers(0, 1 << 32, n, dtype=np.uint64).astype(np.uint32)
+        if kind == 2:
+            wa &= np.uint32(0x3BFF3BFF)
+        wb = wa.copy()
+        pa_, pb = p.copy(), p.copy()
+        oracle_mod.step_packed(kind, pa_, g, wa, s)
+        oracle_mod.step_typed(kind, 0, 0, pb, g, wb, s)
+        np.testing.assert_array_equal(wa, wb)
+    np.testing.assert_array_equal(pa_.view(np.uint32), pb.view(np.uint32))
+
+
+@pytest.mark.parametrize("pdt,gdt", [(1, 1), (2, 2), (1, 0), (2, 0)])
+def test_typed_16bit_is_widen_update_narrow(oracle_mod, pdt, gdt):
+    """16-bit parameters/gradients: widen (pinned decodes), the FP32 step
+    (pinned against torch's AdamW), round back (pinned encodes)."""
+    n = 8192
+    r = np.random.Generator(np.random.PCG64(40 + pdt))
+    lane = {1: 3, 2: 2}
+    p16 = oracle_mod.encode(lane[pdt], r.normal(0, 0.02, n).astype(np.float32))
+    gf = r.normal(0, 1e-3, n).astype(np.float32)
+    g_in = oracle_mod.encode(lane[gdt], gf) if gdt else gf
+    w = np.zeros(n, np.uint32)
+    s = sc(1)
+    p_typed = p16.copy()
+    w_typed = w.copy()
+    oracle_mod.step_typed(1, pdt, gdt, p_typed, g_in, w_typed, s)
+    p32 = oracle_mod.decode(lane[pdt], p16)
+    g32 = oracle_mod.decode(lane[gdt], g_in) if gdt else gf
+    oracle_mod.step_packed(1, p32, g32, w, s)
+    np.testing.assert_array_equal(w_typed, w)
+    np.testing.assert_array_equal(p_typed, oracle_mod.encode(lane[pdt], p32))
