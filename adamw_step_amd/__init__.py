@@ -9,14 +9,18 @@ Functions keep the C names (see include/pa.h):
 
     pa_step(mode, params, grads, state, hyper, step, stream=None)
     pa_step_list(mode, params, grads, states, hyper, step, stream=None)
+    pa_grad_stats_list(grads, sumsq, nonfinite=None, clip_scale=None, max_norm=0.0, stream=None)
     pa_state_bytes(mode, n), pa_format_info(mode), pa_status_string(rc)
     pa_debug_codec(lane, dir, inp, out, stream=None), pa_release_plans()
 
 ``state`` is, per mode: PA_PACKED_E4 / PA_PACKED_FP16 -> an int32 (or
 uint32) tensor of words; PA_FP32 -> (m, v); PA_BLOCKWISE8 ->
 (m_code, m_absmax, v_code, v_absmax, qmap_m, qmap_v, p_out_bf16).
-``hyper`` is a mapping with lr, beta1, beta2, eps, weight_decay and an
-optional ``nonfinite`` int64 device tensor of one element.
+``hyper`` is a mapping with lr, beta1, beta2, eps, weight_decay and the
+optional device tensors ``nonfinite`` (int64, one element, incremented),
+``grad_scale`` (float32, one element: every gradient is multiplied by it)
+and ``skip_if_nonzero`` (int64, one element: a nonzero value skips the
+update).
 """
 from __future__ import annotations
 
@@ -42,7 +46,8 @@ class PAError(RuntimeError):
 class Hyper(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
                 ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double),
-                ("nonfinite", ctypes.c_void_p)]
+                ("nonfinite", ctypes.c_void_p), ("grad_scale", ctypes.c_void_p),
+                ("skip_if_nonzero", ctypes.c_void_p)]
 
 
 class Fp32State(ctypes.Structure):
@@ -70,7 +75,7 @@ class Format(ctypes.Structure):
 
 EXPORTS = ("pa_step", "pa_step_list", "pa_step_typed", "pa_step_list_typed", "pa_state_bytes",
            "pa_format_info", "pa_status_string", "pa_last_hip_error", "pa_release_plans", "pa_debug_codec",
-           "pa_debug_sqrt")
+           "pa_debug_sqrt", "pa_grad_stats_list")
 
 PA_DT_F32, PA_DT_BF16, PA_DT_F16 = 0, 1, 2
 
@@ -112,6 +117,9 @@ def lib():
     L.pa_debug_codec.restype = ctypes.c_int
     L.pa_debug_sqrt.argtypes = [vp, vp, sz, vp]
     L.pa_debug_sqrt.restype = ctypes.c_int
+    L.pa_grad_stats_list.argtypes = [ctypes.c_int, sz, ctypes.POINTER(vp), ctypes.POINTER(sz), ctypes.c_double,
+                                     vp, vp, vp, vp]
+    L.pa_grad_stats_list.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -140,10 +148,22 @@ def _stream(stream):
     return int(getattr(stream, "cuda_stream", stream))
 
 
+def _device_word(t, dtype, what):
+    import torch
+    if t is None:
+        return None
+    _tensor_ok(t, what)
+    if t.dtype != dtype or t.numel() != 1:
+        raise TypeError(f"{what} must be a one-element {dtype} device tensor")
+    return _ptr(t)
+
+
 def _hyper(h):
-    nf = h.get("nonfinite")
+    import torch
     return Hyper(float(h["lr"]), float(h["beta1"]), float(h["beta2"]), float(h["eps"]),
-                 float(h["weight_decay"]), _ptr(nf) if nf is not None else None)
+                 float(h["weight_decay"]), _device_word(h.get("nonfinite"), torch.int64, "nonfinite"),
+                 _device_word(h.get("grad_scale"), torch.float32, "grad_scale"),
+                 _device_word(h.get("skip_if_nonzero"), torch.int64, "skip_if_nonzero"))
 
 
 def _tensor_ok(t, what):
@@ -282,6 +302,50 @@ class StepList:
         h = _hyper(hyper)
         _check(self._fn(self.mode, self.pdt, self.gdt, self.count, self._P, self._G, self._S, self._N,
                         ctypes.byref(h), int(step), _stream(stream)))
+
+
+def _stats_outputs(sumsq, nonfinite, clip_scale):
+    import torch
+    return (_device_word(sumsq, torch.float64, "sumsq"), _device_word(nonfinite, torch.int64, "nonfinite"),
+            _device_word(clip_scale, torch.float32, "clip_scale"))
+
+
+class GradStats:
+    """Gradient pre-pass over a fixed gradient list (validated and
+    marshalled once): ``run(sumsq, nonfinite=None, clip_scale=None,
+    max_norm=0.0)`` writes the sum of squares (float64), the non-finite count
+    (int64) and the clip coefficient (float32) into one-element device
+    tensors.  Feed ``clip_scale`` and ``nonfinite`` to the step as
+    ``grad_scale`` and ``skip_if_nonzero``."""
+
+    def __init__(self, grads):
+        import torch
+        k = len(grads)
+        self._keep = list(grads)
+        self._G = (ctypes.c_void_p * k)()
+        self._N = (ctypes.c_size_t * k)()
+        dts = set()
+        for i, g in enumerate(grads):
+            _tensor_ok(g, "grads")
+            dts.add(_dtype_code(g))
+            if g.device != grads[0].device:
+                raise ValueError("all gradients of one call must be on one device")
+            self._G[i] = _ptr(g)
+            self._N[i] = g.numel()
+        if len(dts) > 1:
+            raise TypeError("all gradients of one call must share one dtype")
+        self.gdt = dts.pop() if dts else PA_DT_F32
+        self.count = k
+        self._fn = lib().pa_grad_stats_list
+
+    def run(self, sumsq, nonfinite=None, clip_scale=None, max_norm=0.0, stream=None):
+        s, nf, cl = _stats_outputs(sumsq, nonfinite, clip_scale)
+        _check(self._fn(self.gdt, self.count, self._G, self._N, float(max_norm), s, nf, cl, _stream(stream)))
+
+
+def pa_grad_stats_list(grads, sumsq, nonfinite=None, clip_scale=None, max_norm=0.0, stream=None):
+    """One-shot gradient pre-pass (see GradStats and include/pa.h)."""
+    GradStats(grads).run(sumsq, nonfinite, clip_scale, max_norm, stream)
 
 
 def pa_state_bytes(mode, n):

@@ -28,14 +28,34 @@
 namespace pa {
 
 // The eight binary32 scalars of one call (formed on the host in double,
-// each rounded once).
+// each rounded once), and the call's optional device inputs.
 struct Scalars {
   float beta1, one_m_beta1, beta2, one_m_beta2;
   float bc2, lr_over_bc1, decay, eps;
   float beta1_x2p112;   // beta1 * 2^112, exact (pairs with e4_decode_m_unscaled)
-  float pad_;
+  float gmul;           // gradient multiplier: 1, or *gscale once read on the device
   double inv_bc2;       // 1/bc2 rounded to double, for the exact quotient v'/bc2
+  const float* gscale;                // nullable device gradient scale
+  const unsigned long long* skip;     // nullable device flag: nonzero skips the call
 };
+
+// Reads the optional device inputs at the start of a launch (uniform across
+// the grid).  Returns false when the update is to be skipped; otherwise
+// sets the gradient multiplier.  A product with 1 is exact, so gradients
+// without a scale would pass through unchanged; the elementwise kernels
+// still leave the product out when no scale is given (template flag
+// SCALE), since it costs registers in their unrolled tiles.
+__device__ __forceinline__ bool resolve_inputs(Scalars& s) {
+  if (s.skip != nullptr && *s.skip != 0ull) return false;
+  if (s.gscale != nullptr) s.gmul = *s.gscale;
+  return true;
+}
+
+template <bool SCALE>
+__device__ __forceinline__ float scaled(float g, const Scalars& s) {
+  if constexpr (SCALE) return g * s.gmul;
+  else return g;
+}
 
 // One tensor of an elementwise launch.  Every buffer of a tensor shares one
 // 16-byte phase; `phase` is that phase in elements, so element i sits at
@@ -155,6 +175,7 @@ __device__ __forceinline__ float div_bc2(float v1, const Scalars& s) {
 
 // New moments and the FP32 step with decoupled decay.  `beta1_m` is the
 // product beta1 * m, formed by the caller (see e4_decode_m_unscaled).
+// `g` is the gradient already multiplied by the call's gradient scale.
 __device__ __forceinline__ void adamw(float p, float g, float beta1_m, float v, const Scalars& s,
                                       float& p1, float& m1, float& v1) {
   m1 = beta1_m + s.one_m_beta1 * g;
@@ -204,13 +225,13 @@ __device__ __forceinline__ void fp32_elem(float& p, float g, float& m, float& v,
 
 
 // One element at index i of tensor e (ragged edges only).
-template <int MODE, int PT, int GT>
+template <int MODE, int PT, int GT, bool SCALE>
 __device__ __forceinline__ void scalar_elem(const Entry& e, long long i, const Scalars& s, uint32_t& bad) {
   using PE = Elem<PT>;
   using GE = Elem<GT>;
   typename PE::scalar* P = static_cast<typename PE::scalar*>(e.p);
   float p = PE::widen(P[i]);
-  const float g = GE::widen(static_cast<const typename GE::scalar*>(e.g)[i]);
+  const float g = scaled<SCALE>(GE::widen(static_cast<const typename GE::scalar*>(e.g)[i]), s);
   if constexpr (MODE == kModeFp32) {
     float* m = static_cast<float*>(e.s0);
     float mm = m[i], vv = e.s1[i];
@@ -226,7 +247,7 @@ __device__ __forceinline__ void scalar_elem(const Entry& e, long long i, const S
 
 // Tile `tile` (local to tensor e).  Each thread moves four elements per
 // vector access of each stream: 16 bytes for FP32 data, 8 for 16-bit data.
-template <int MODE, int PT, int GT>
+template <int MODE, int PT, int GT, bool SCALE>
 __device__ __forceinline__ void run_tile(const Entry& e, long long tile, const Scalars& s, uint32_t& bad) {
   using PE = Elem<PT>;
   using GE = Elem<GT>;
@@ -259,7 +280,7 @@ __device__ __forceinline__ void run_tile(const Entry& e, long long tile, const S
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           float pk = PE::widen(p[u][k]), mk = m[u][k], vk = v[u][k];
-          fp32_elem(pk, GE::widen(g[u][k]), mk, vk, s, bad);
+          fp32_elem(pk, scaled<SCALE>(GE::widen(g[u][k]), s), mk, vk, s, bad);
           p[u][k] = PE::narrow(pk);
           m[u][k] = mk;
           v[u][k] = vk;
@@ -288,7 +309,7 @@ __device__ __forceinline__ void run_tile(const Entry& e, long long tile, const S
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           float pk = PE::widen(p[u][k]);
-          w[u][k] = packed_elem<MODE>(pk, GE::widen(g[u][k]), w[u][k], s, bad);
+          w[u][k] = packed_elem<MODE>(pk, scaled<SCALE>(GE::widen(g[u][k]), s), w[u][k], s, bad);
           p[u][k] = PE::narrow(pk);
         }
 #pragma unroll
@@ -304,7 +325,7 @@ __device__ __forceinline__ void run_tile(const Entry& e, long long tile, const S
       const long long vb = v0 + ((long long)u * kThreads + tid) * 4;
       for (int k = 0; k < 4; ++k) {
         const long long vi = vb + k;
-        if (vi >= e.phase && vi < vend) scalar_elem<MODE, PT, GT>(e, vi - e.phase, s, bad);
+        if (vi >= e.phase && vi < vend) scalar_elem<MODE, PT, GT, SCALE>(e, vi - e.phase, s, bad);
       }
     }
   }
@@ -318,26 +339,29 @@ __device__ __forceinline__ void flush_count(uint32_t bad, unsigned long long* co
 
 // Persistent multi-tensor launch.  table[count].tile0 holds the total tile
 // count (a sentinel), so the cursor never runs past the table.
-template <int MODE, int PT, int GT, bool COUNT>
+template <int MODE, int PT, int GT, bool COUNT, bool SCALE>
 __global__ void __launch_bounds__(kThreads)
 elementwise_list(const Entry* __restrict__ table, long long total_tiles, Scalars s,
                  unsigned long long* nonfinite) {
+  if (!resolve_inputs(s)) return;
   uint32_t bad = 0;
   int t = 0;
   for (long long tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
     while (tile >= table[t + 1].tile0) ++t;
     const Entry e = table[t];
-    run_tile<MODE, PT, GT>(e, tile - e.tile0, s, bad);
+    run_tile<MODE, PT, GT, SCALE>(e, tile - e.tile0, s, bad);
   }
   if constexpr (COUNT) flush_count(bad, nonfinite);
 }
 
 // Single tensor, its entry passed by value (no table in device memory).
-template <int MODE, int PT, int GT, bool COUNT>
+template <int MODE, int PT, int GT, bool COUNT, bool SCALE>
 __global__ void __launch_bounds__(kThreads)
 elementwise_one(Entry e, long long total_tiles, Scalars s, unsigned long long* nonfinite) {
+  if (!resolve_inputs(s)) return;
   uint32_t bad = 0;
-  for (long long tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) run_tile<MODE, PT, GT>(e, tile, s, bad);
+  for (long long tile = blockIdx.x; tile < total_tiles; tile += gridDim.x)
+    run_tile<MODE, PT, GT, SCALE>(e, tile, s, bad);
   if constexpr (COUNT) flush_count(bad, nonfinite);
 }
 
@@ -507,6 +531,7 @@ blockwise_kernel(BlockwiseArgs a, Scalars s, unsigned long long* nonfinite) {
   __shared__ float lut_m[256], lut_v[256];
   __shared__ MapTables tab_m, tab_v;
   __shared__ uint32_t wave_max[2][kThreads / 64];
+  if (!resolve_inputs(s)) return;   // uniform: before any barrier
   const int tid = threadIdx.x;
   lut_m[tid] = a.qmap_m[tid];
   lut_v[tid] = a.qmap_v[tid];
@@ -550,7 +575,7 @@ blockwise_kernel(BlockwiseArgs a, Scalars s, unsigned long long* nonfinite) {
         const float m = lut_m[(cur.mc[h] >> (8 * k)) & 0xFFu] * am;
         const float v = lut_v[(cur.vc[h] >> (8 * k)) & 0xFFu] * av;
         float p1;
-        adamw(cur.p[h][k], cur.g[h][k], s.beta1 * m, v, s, p1, m1[h * 4 + k], v1[h * 4 + k]);
+        adamw(cur.p[h][k], cur.g[h][k] * s.gmul, s.beta1 * m, v, s, p1, m1[h * 4 + k], v1[h * 4 + k]);
         bad += nonfinite3(p1, m1[h * 4 + k], v1[h * 4 + k]);
         bf[k] = bf16_encode(p1);
       }
@@ -603,6 +628,136 @@ blockwise_kernel(BlockwiseArgs a, Scalars s, unsigned long long* nonfinite) {
     }
   }
   if constexpr (COUNT) flush_count(bad, nonfinite);
+}
+
+// ---------------------------------------------------------------------------
+// Gradient pre-pass: the sum of the squares of all gradients in double and
+// the number of non-finite gradients.  A persistent grid walks the same tile
+// table as the update (only g, n, phase and tile0 are used); each workgroup
+// writes one partial, and one workgroup adds the partials in index order, so
+// the result depends only on the list and the grid size.
+
+__device__ __forceinline__ void stats_add(float x, double& acc, uint32_t& bad) {
+  const double d = (double)x;
+  acc = __builtin_fma(d, d, acc);   // d*d is exact in double: one rounding per term
+  bad += __builtin_isfinite(x) ? 0u : 1u;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+template <int GT>
+__device__ __forceinline__ void stats_tile(const Entry& e, long long tile, double& acc, uint32_t& bad) {
+  using GE = Elem<GT>;
+  using GV = typename GE::vec4;
+  const long long v0 = tile * kTile;
+  const long long vend = e.n + e.phase;
+  const int tid = threadIdx.x;
+  const typename GE::scalar* g = static_cast<const typename GE::scalar*>(e.g);
+  if (v0 >= e.phase && v0 + kTile <= vend) {
+    // The step reads these gradients right after: plain loads, so that a
+    // list that fits the last-level cache stays there.
+    const GV* G = reinterpret_cast<const GV*>(g - e.phase);
+    const long long q0 = v0 / 4 + tid;
+    GV x[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) x[u] = G[q0 + (long long)u * kThreads];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) stats_add(GE::widen(x[u][k]), acc, bad);
+  } else {
+    for (int u = 0; u < kUnroll; ++u) {
+      const long long vb = v0 + ((long long)u * kThreads + tid) * 4;
+      for (int k = 0; k < 4; ++k) {
+        const long long vi = vb + k;
+        if (vi >= e.phase && vi < vend) stats_add(GE::widen(g[vi - e.phase]), acc, bad);
+      }
+    }
+  }
+}
+
+template <int GT>
+__global__ void __launch_bounds__(kThreads)
+grad_stats_list(const Entry* __restrict__ table, long long total_tiles, double* part_sum,
+                unsigned long long* part_bad) {
+  __shared__ double wsum[kThreads / 64];
+  __shared__ unsigned long long wbad[kThreads / 64];
+  double acc = 0.0;
+  uint32_t bad = 0;
+  int t = 0;
+  for (long long tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
+    while (tile >= table[t + 1].tile0) ++t;
+    const Entry e = table[t];
+    stats_tile<GT>(e, tile - e.tile0, acc, bad);
+  }
+  const int tid = threadIdx.x;
+  acc = wave_sum_f64(acc);
+  const unsigned long long b = wave_sum_u64(bad);
+  if ((tid & 63) == 0) {
+    wsum[tid >> 6] = acc;
+    wbad[tid >> 6] = b;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double sacc = wsum[0];
+    unsigned long long bacc = wbad[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) {
+      sacc += wsum[w];
+      bacc += wbad[w];
+    }
+    part_sum[blockIdx.x] = sacc;
+    part_bad[blockIdx.x] = bacc;
+  }
+}
+
+// One workgroup: the partials in index order, then the outputs.  The clip
+// coefficient is min(1, max_norm / (sqrt(sumsq) + 1e-6)) in double (a NaN
+// stays NaN), rounded once to binary32.
+__global__ void __launch_bounds__(kThreads)
+grad_stats_finalize(const double* __restrict__ part_sum, const unsigned long long* __restrict__ part_bad,
+                    int nparts, double max_norm, double* sumsq, unsigned long long* nonfinite, float* clip) {
+  __shared__ double wsum[kThreads / 64];
+  __shared__ unsigned long long wbad[kThreads / 64];
+  const int tid = threadIdx.x;
+  double sacc = 0.0;
+  unsigned long long bacc = 0;
+  for (int i = tid; i < nparts; i += kThreads) {
+    sacc += part_sum[i];
+    bacc += part_bad[i];
+  }
+  sacc = wave_sum_f64(sacc);
+  bacc = wave_sum_u64(bacc);
+  if ((tid & 63) == 0) {
+    wsum[tid >> 6] = sacc;
+    wbad[tid >> 6] = bacc;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double total = wsum[0];
+    unsigned long long nb = wbad[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) {
+      total += wsum[w];
+      nb += wbad[w];
+    }
+    *sumsq = total;
+    if (nonfinite != nullptr) *nonfinite = nb;
+    if (clip != nullptr) {
+      const double coef = max_norm / (__builtin_sqrt(total) + 1e-6);
+      *clip = coef != coef ? (float)coef : (float)(coef < 1.0 ? coef : 1.0);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -53,10 +53,16 @@ int make_scalars(const pa_hyper* h, long long step, pa::Scalars* s) {
   s->decay = (float)(1.0 - lr * wd);
   s->eps = (float)eps;
   s->beta1_x2p112 = std::ldexp(s->beta1, 112);
-  s->pad_ = 0.0f;
+  s->gmul = 1.0f;
   s->inv_bc2 = 1.0 / (double)s->bc2;
+  s->gscale = h->grad_scale;
+  s->skip = h->skip_if_nonzero;
+  const uintptr_t gs = reinterpret_cast<uintptr_t>(h->grad_scale), sk = reinterpret_cast<uintptr_t>(h->skip_if_nonzero),
+                  nf = reinterpret_cast<uintptr_t>(h->nonfinite);
+  if (gs % 4 || sk % 8 || nf % 8) return PA_ERR_ALIGN;
   return PA_OK;
 }
+
 
 // ---------------------------------------------------------------- devices
 
@@ -64,6 +70,7 @@ struct DeviceInfo {
   int cus = 0;
   int blocks_per_cu = 0;      // elementwise kernels
   int bw_blocks_per_cu = 0;   // blockwise kernel
+  int stats_blocks_per_cu = 0;   // gradient pre-pass
 };
 
 std::mutex g_dev_mu;
@@ -82,7 +89,7 @@ int device_info(int* dev_out, DeviceInfo* info) {
     if (e != hipSuccess) return hip_failed(e);
     int per = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per, reinterpret_cast<const void*>(pa::elementwise_list<pa::kModeE4, pa::kF32, pa::kF32, false>),
+        &per, reinterpret_cast<const void*>(pa::elementwise_list<pa::kModeE4, pa::kF32, pa::kF32, false, false>),
         pa::kThreads, 0);
     if (e != hipSuccess || per < 1) per = 4;
     int bw = 0;
@@ -92,6 +99,11 @@ int device_info(int* dev_out, DeviceInfo* info) {
     d.cus = cus;
     d.blocks_per_cu = per;
     d.bw_blocks_per_cu = bw;
+    int st = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &st, reinterpret_cast<const void*>(pa::grad_stats_list<pa::kF32>), pa::kThreads, 0);
+    if (e != hipSuccess || st < 1) st = 4;
+    d.stats_blocks_per_cu = st;
   }
   *dev_out = dev;
   *info = d;
@@ -121,6 +133,22 @@ struct Range {
 Range range_of(const void* p, size_t bytes) {
   const uintptr_t a = reinterpret_cast<uintptr_t>(p);
   return Range{a, a + bytes};
+}
+
+// The device words named by a pa_hyper (counter, gradient scale, skip flag):
+// none may overlap another or any tensor of the call, or a workgroup that
+// starts late could read a value the call itself has changed.
+void hyper_ranges(const pa_hyper* h, std::vector<Range>* out) {
+  if (h->nonfinite) out->push_back(range_of(h->nonfinite, 8));
+  if (h->grad_scale) out->push_back(range_of(h->grad_scale, 4));
+  if (h->skip_if_nonzero) out->push_back(range_of(h->skip_if_nonzero, 8));
+}
+
+// True if r overlaps any range of `sorted` (sorted by start, disjoint).
+bool hits_sorted(const std::vector<Range>& sorted, const Range& r) {
+  auto it = std::upper_bound(sorted.begin(), sorted.end(), r.lo,
+                             [](uintptr_t a, const Range& x) { return a < x.hi; });
+  return it != sorted.end() && it->lo < r.hi;
 }
 
 // True if any two of the ranges overlap (empty ranges never do).
@@ -206,14 +234,21 @@ long long tiles_of(const pa::Entry& e) { return (e.n + e.phase + pa::kTile - 1) 
 
 // ---------------------------------------------------------------- launches
 
+// Kernel variant: with or without the non-finite counter, and with or
+// without a device gradient scale.
 template <int MODE, int PT, int GT>
 hipError_t launch_one(const pa::Entry& e, long long tiles, const pa::Scalars& s, unsigned long long* nf,
                       hipStream_t st, const DeviceInfo& d) {
   const dim3 grid((unsigned)grid_for(tiles, d, d.blocks_per_cu)), block(pa::kThreads);
-  if (nf)
-    hipLaunchKernelGGL((pa::elementwise_one<MODE, PT, GT, true>), grid, block, 0, st, e, tiles, s, nf);
+  const bool sc = s.gscale != nullptr;
+  if (nf && sc)
+    hipLaunchKernelGGL((pa::elementwise_one<MODE, PT, GT, true, true>), grid, block, 0, st, e, tiles, s, nf);
+  else if (nf)
+    hipLaunchKernelGGL((pa::elementwise_one<MODE, PT, GT, true, false>), grid, block, 0, st, e, tiles, s, nf);
+  else if (sc)
+    hipLaunchKernelGGL((pa::elementwise_one<MODE, PT, GT, false, true>), grid, block, 0, st, e, tiles, s, nf);
   else
-    hipLaunchKernelGGL((pa::elementwise_one<MODE, PT, GT, false>), grid, block, 0, st, e, tiles, s, nf);
+    hipLaunchKernelGGL((pa::elementwise_one<MODE, PT, GT, false, false>), grid, block, 0, st, e, tiles, s, nf);
   return hipGetLastError();
 }
 
@@ -221,10 +256,16 @@ template <int MODE, int PT, int GT>
 hipError_t launch_list(const pa::Entry* table, long long tiles, const pa::Scalars& s, unsigned long long* nf,
                        hipStream_t st, const DeviceInfo& d) {
   const dim3 grid((unsigned)grid_for(tiles, d, d.blocks_per_cu)), block(pa::kThreads);
-  if (nf)
-    hipLaunchKernelGGL((pa::elementwise_list<MODE, PT, GT, true>), grid, block, 0, st, table, tiles, s, nf);
+  const bool sc = s.gscale != nullptr;
+  if (nf && sc)
+    hipLaunchKernelGGL((pa::elementwise_list<MODE, PT, GT, true, true>), grid, block, 0, st, table, tiles, s, nf);
+  else if (nf)
+    hipLaunchKernelGGL((pa::elementwise_list<MODE, PT, GT, true, false>), grid, block, 0, st, table, tiles, s, nf);
+  else if (sc)
+    hipLaunchKernelGGL((pa::elementwise_list<MODE, PT, GT, false, true>), grid, block, 0, st, table, tiles, s, nf);
   else
-    hipLaunchKernelGGL((pa::elementwise_list<MODE, PT, GT, false>), grid, block, 0, st, table, tiles, s, nf);
+    hipLaunchKernelGGL((pa::elementwise_list<MODE, PT, GT, false, false>), grid, block, 0, st, table, tiles, s,
+                       nf);
   return hipGetLastError();
 }
 
@@ -331,8 +372,12 @@ struct Plan {
   int mode = -1;
   int pdt = 0, gdt = 0;
   std::vector<uintptr_t> key;   // per tensor: p, g, s0, s1, n
-  pa::Entry* table = nullptr;   // device memory, count+1 entries
+  pa::Entry* table = nullptr;   // device memory, count+1 entries (+ partials of a pre-pass plan)
   long long tiles = 0;
+  std::vector<Range> ranges;    // the tensors' buffers, sorted and disjoint
+  double* part_sum = nullptr;   // pre-pass plans: per-workgroup partials, inside `table`'s block
+  unsigned long long* part_bad = nullptr;
+  int nparts = 0;
 };
 
 std::mutex g_plan_mu;
@@ -351,6 +396,34 @@ void free_plan(Plan& pl) {
 }
 
 bool valid_mode(int mode) { return mode >= PA_FP32 && mode <= PA_BLOCKWISE8; }
+
+constexpr int kStatsPlanMode = 100;   // plan-cache tag of gradient pre-pass plans
+
+// Sorted, disjoint union of the ranges (empty ones dropped).
+std::vector<Range> merged(std::vector<Range> r) {
+  r.erase(std::remove_if(r.begin(), r.end(), [](const Range& x) { return x.hi == x.lo; }), r.end());
+  std::sort(r.begin(), r.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+  std::vector<Range> out;
+  for (const Range& x : r) {
+    if (!out.empty() && x.lo <= out.back().hi) out.back().hi = std::max(out.back().hi, x.hi);
+    else out.push_back(x);
+  }
+  return out;
+}
+
+template <int GT>
+hipError_t launch_stats(const Plan& pl, double max_norm, double* sumsq, unsigned long long* nonfinite,
+                        float* clip, hipStream_t st) {
+  if (pl.nparts > 0) {
+    hipLaunchKernelGGL((pa::grad_stats_list<GT>), dim3((unsigned)pl.nparts), dim3(pa::kThreads), 0, st, pl.table,
+                       pl.tiles, pl.part_sum, pl.part_bad);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(pa::grad_stats_finalize, dim3(1), dim3(pa::kThreads), 0, st, pl.part_sum, pl.part_bad,
+                     pl.nparts, max_norm, sumsq, nonfinite, clip);
+  return hipGetLastError();
+}
 
 }  // namespace
 
@@ -374,6 +447,7 @@ int pa_step_typed(int mode, int param_dtype, int grad_dtype, void* params, const
     std::vector<Range> w;
     rc = check_blockwise(static_cast<const float*>(params), static_cast<const float*>(grads), state, n, &a, &w);
     if (rc) return rc;
+    hyper_ranges(hyper, &w);
     if (any_overlap(w)) return PA_ERR_ALIAS;
     rc = blockwise_inputs_clear(a, n, w);
     if (rc) return rc;
@@ -386,6 +460,7 @@ int pa_step_typed(int mode, int param_dtype, int grad_dtype, void* params, const
   std::vector<Range> ranges;
   rc = check_elem_tensor(mode, param_dtype, grad_dtype, params, grads, state, n, &t, &ranges);
   if (rc) return rc;
+  hyper_ranges(hyper, &ranges);
   if (any_overlap(ranges)) return PA_ERR_ALIAS;
   rc = device_info(&dev, &d);
   if (rc) return rc;
@@ -426,6 +501,7 @@ int pa_step_list_typed(int mode, int param_dtype, int grad_dtype, size_t count, 
       written.insert(written.end(), w.begin(), w.end());
       args.push_back(a);
     }
+    hyper_ranges(hyper, &written);
     std::vector<Range> all = written;
     if (any_overlap(all)) return PA_ERR_ALIAS;
     for (size_t i = 0; i < args.size(); ++i) {
@@ -492,6 +568,7 @@ int pa_step_list_typed(int mode, int param_dtype, int grad_dtype, size_t count, 
     pl.gdt = grad_dtype;
     pl.key = key;
     pl.tiles = tiles;
+    pl.ranges = ranges;
     hipError_t e = hipMalloc(reinterpret_cast<void**>(&pl.table), host.size() * sizeof(pa::Entry));
     if (e != hipSuccess) {
       g_last_hip_error = (int)e;
@@ -513,6 +590,13 @@ int pa_step_list_typed(int mode, int param_dtype, int grad_dtype, size_t count, 
     g_plans.splice(g_plans.begin(), g_plans, it);
     it = g_plans.begin();
   }
+  {
+    std::vector<Range> hr;
+    hyper_ranges(hyper, &hr);
+    for (const Range& r : hr)
+      if (hits_sorted(it->ranges, r)) return PA_ERR_ALIAS;
+    if (any_overlap(hr)) return PA_ERR_ALIAS;
+  }
   hipError_t e = dispatch_list(mode, param_dtype, grad_dtype, it->table, it->tiles, s, hyper->nonfinite, st, d);
   return e == hipSuccess ? PA_OK : hip_failed(e);
 }
@@ -521,6 +605,106 @@ int pa_step_list(int mode, size_t count, float* const* params, const float* cons
                  const size_t* n, const pa_hyper* hyper, long long step, void* stream) {
   return pa_step_list_typed(mode, PA_DT_F32, PA_DT_F32, count, reinterpret_cast<void* const*>(params),
                             reinterpret_cast<const void* const*>(grads), states, n, hyper, step, stream);
+}
+
+int pa_grad_stats_list(int grad_dtype, size_t count, const void* const* grads, const size_t* n, double max_norm,
+                       double* sumsq, unsigned long long* nonfinite, float* clip_scale, void* stream) {
+  if (!valid_dtype(grad_dtype) || sumsq == nullptr) return PA_ERR_ARG;
+  if (clip_scale != nullptr && !(std::isfinite(max_norm) && max_norm > 0.0)) return PA_ERR_ARG;
+  if (count > 0 && (grads == nullptr || n == nullptr)) return PA_ERR_ARG;
+  if (!aligned(sumsq, 8) || !aligned(nonfinite, 8) || !aligned(clip_scale, 4)) return PA_ERR_ALIGN;
+  std::vector<Range> outs{range_of(sumsq, 8)};
+  if (nonfinite) outs.push_back(range_of(nonfinite, 8));
+  if (clip_scale) outs.push_back(range_of(clip_scale, 4));
+  {
+    std::vector<Range> tmp = outs;
+    if (any_overlap(tmp)) return PA_ERR_ALIAS;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int dev;
+  DeviceInfo d;
+  int rc = device_info(&dev, &d);
+  if (rc) return rc;
+
+  std::vector<uintptr_t> key;
+  key.reserve(count * 2);
+  for (size_t i = 0; i < count; ++i) {
+    key.push_back(reinterpret_cast<uintptr_t>(grads[i]));
+    key.push_back((uintptr_t)n[i]);
+  }
+  std::lock_guard<std::mutex> lk(g_plan_mu);
+  auto it = std::find_if(g_plans.begin(), g_plans.end(), [&](const Plan& p) {
+    return p.device == dev && p.mode == kStatsPlanMode && p.gdt == grad_dtype && p.key == key;
+  });
+  if (it == g_plans.end()) {
+    const size_t es = dtype_size(grad_dtype);
+    std::vector<pa::Entry> host;
+    std::vector<Range> ranges;
+    long long tiles = 0;
+    for (size_t i = 0; i < count; ++i) {
+      if (n[i] == 0) continue;
+      if (grads[i] == nullptr) return PA_ERR_ARG;
+      const uintptr_t a = reinterpret_cast<uintptr_t>(grads[i]);
+      if (a % es) return PA_ERR_ALIGN;
+      pa::Entry e;
+      std::memset(&e, 0, sizeof(e));
+      e.g = grads[i];
+      e.n = (long long)n[i];
+      e.phase = (int)((a / es) & 3u);
+      e.tile0 = tiles;
+      tiles += tiles_of(e);
+      host.push_back(e);
+      ranges.push_back(range_of(grads[i], n[i] * es));
+    }
+    pa::Entry sentinel;
+    std::memset(&sentinel, 0, sizeof(sentinel));
+    sentinel.tile0 = tiles;
+    host.push_back(sentinel);
+    Plan pl;
+    pl.device = dev;
+    pl.mode = kStatsPlanMode;
+    pl.pdt = -1;
+    pl.gdt = grad_dtype;
+    pl.key = key;
+    pl.tiles = tiles;
+    pl.ranges = merged(ranges);
+    pl.nparts = tiles > 0 ? (int)grid_for(tiles, d, d.stats_blocks_per_cu) : 0;
+    // One block: the table, then the partial sums and counts (at least one
+    // slot each, so the finalizer always gets valid pointers).
+    const size_t table_bytes = host.size() * sizeof(pa::Entry);
+    const size_t slots = (size_t)std::max(pl.nparts, 1);
+    hipError_t e = hipMalloc(reinterpret_cast<void**>(&pl.table), table_bytes + slots * 16);
+    if (e != hipSuccess) {
+      g_last_hip_error = (int)e;
+      return PA_ERR_NOMEM;
+    }
+    pl.part_sum = reinterpret_cast<double*>(reinterpret_cast<char*>(pl.table) + table_bytes);
+    pl.part_bad = reinterpret_cast<unsigned long long*>(pl.part_sum + slots);
+    e = hipMemcpyAsync(pl.table, host.data(), table_bytes, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) {
+      (void)hipFree(pl.table);
+      return hip_failed(e);
+    }
+    g_plans.push_front(std::move(pl));
+    while (g_plans.size() > kMaxPlans) {
+      free_plan(g_plans.back());
+      g_plans.pop_back();
+    }
+    it = g_plans.begin();
+  } else if (it != g_plans.begin()) {
+    g_plans.splice(g_plans.begin(), g_plans, it);
+    it = g_plans.begin();
+  }
+  for (const Range& r : outs)
+    if (hits_sorted(it->ranges, r)) return PA_ERR_ALIAS;
+  hipError_t e;
+  switch (grad_dtype) {
+    case PA_DT_F32: e = launch_stats<pa::kF32>(*it, max_norm, sumsq, nonfinite, clip_scale, st); break;
+    case PA_DT_BF16: e = launch_stats<pa::kBF16>(*it, max_norm, sumsq, nonfinite, clip_scale, st); break;
+    default: e = launch_stats<pa::kF16>(*it, max_norm, sumsq, nonfinite, clip_scale, st); break;
+  }
+  return e == hipSuccess ? PA_OK : hip_failed(e);
 }
 
 size_t pa_state_bytes(int mode, size_t n) {

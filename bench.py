@@ -21,6 +21,10 @@ Other flags:
   --train-gpt             instead: time a synthetic-token training step of the
                           gpt-11m model (trainer/) with each optimizer and
                           report the optimizer's share of the step
+  --mode gradstats        instead of the step: time the gradient pre-pass
+                          (pa_grad_stats_list: sum of squares, non-finite
+                          count and clip coefficient) over the workload's
+                          gradients
 """
 import argparse
 import hashlib
@@ -34,7 +38,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "packed-AdamW step: params/s and achieved HBM GB/s (% of 8 TB/s) at 7B"
 PEAK_GBPS = 8000.0
-BYTES_PER_PARAM = {"e4": 20, "fp16": 20, "fp32": 28, "blockwise8": 14}
+BYTES_PER_PARAM = {"e4": 20, "fp16": 20, "fp32": 28, "blockwise8": 14, "gradstats": 4}
 WORKLOADS = {"single-262k": 1, "gpt-11m": 2, "gpt2-small-124m": 3, "llama-7b": 4, "blockwise-268m": 5}
 KERNEL_SOURCES = ("adamw_step_amd/csrc/kernels.hpp", "adamw_step_amd/csrc/codec.hpp",
                   "adamw_step_amd/csrc/pa_api.hip")
@@ -190,6 +194,68 @@ def cpu_baseline(cfg, mode, ps, gs, states, budget_params):
                       f"({names[0]}..{names[-1]}, {total} params), {dt:.1f} s wall"}
 
 
+def run_gradstats(args, cfg):
+    """Time the gradient pre-pass over the workload's gradient list."""
+    import torch
+    import adamw_step_amd as pa
+    import workloads
+    sizes = workloads.sizes(cfg)
+    dt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[args.param_dtype]
+    log(f"allocating {workloads.NAMES[cfg]} gradients: {len(sizes)} tensors, {sum(sizes)} values")
+    gs = [torch.empty(n, dtype=dt, device="cuda:0") for n in sizes]
+    workloads.device_fill_grads(cfg, 1, gs)
+    s = torch.zeros(1, dtype=torch.float64, device="cuda:0")
+    nf = torch.zeros(1, dtype=torch.int64, device="cuda:0")
+    clip = torch.zeros(1, dtype=torch.float32, device="cuda:0")
+    stats = pa.GradStats(gs)
+    for _ in range(args.warmup):
+        stats.run(s, nf, clip, max_norm=1.0)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        evs[k][0].record(stream)
+        stats.run(s, nf, clip, max_norm=1.0)
+        evs[k][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in evs]
+    mean_ms = sum(launch_ms) / len(launch_ms)
+    n = sum(sizes)
+    algo = n * (4 if args.param_dtype == "fp32" else 2)
+    achieved = algo / (mean_ms / 1e3) / 1e9
+    log(f"timed {args.steps} pre-passes: {mean_ms:.3f} ms/call (events), sumsq {s.item():.6g}, "
+        f"nonfinite {int(nf.item())}, clip {clip.item():.6g}")
+    out = {"metric": "gradient pre-pass (sum of squares, non-finite count, clip coefficient): params/s",
+           "value": round(n * args.steps / elapsed, 1), "unit": "params/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(elapsed * 1e3 / args.steps, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f64 accumulation of " + args.param_dtype + " grads",
+           "data": "synthetic",
+           "config": {"workload": args.workload, "params": n, "tensors": len(sizes), "mode": "gradstats",
+                      "grad_dtype": args.param_dtype},
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                        "frac": round(achieved / PEAK_GBPS, 4), "traffic": None,
+                        "kernel": "grad_stats_list + grad_stats_finalize", "algorithmic_bytes_per_launch": algo,
+                        "mean_launch_ms": round(mean_ms, 4), "kernel_sha": kernel_sha()}}
+    if not args.no_cpu_baseline and args.param_dtype == "fp32":
+        import oracle
+        picked, total = [], 0
+        for g in gs:
+            if total + g.numel() > args.cpu_sample_params and picked:
+                break
+            picked.append(g)
+            total += g.numel()
+        host = [g.cpu().numpy() for g in picked]
+        t1 = time.perf_counter()
+        oracle.grad_stats(0, host)
+        dt_cpu = time.perf_counter() - t1
+        out["cpu_baseline"] = {"value": round(total / dt_cpu, 1), "unit": "params/s", "cores": oracle.num_threads(),
+                               "kind": "oracle", "sample": f"the first {len(picked)} gradient tensors "
+                               f"({total} values), exact accumulation, {dt_cpu:.1f} s wall"}
+    print(json.dumps(out), flush=True)
+
+
 def load_traffic(workload, mode):
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{mode}.json")
     if not os.path.exists(path):
@@ -241,6 +307,12 @@ def main():
 
     cfg = WORKLOADS[args.workload]
     mode = args.mode
+    if mode == "gradstats":
+        if cfg == 5:
+            print("bench.py: the gradstats mode runs on the list workloads", file=sys.stderr)
+            sys.exit(2)
+        run_gradstats(args, cfg)
+        return
     if (mode == "blockwise8") != (cfg == 5):
         print("bench.py: the blockwise8 mode runs on the blockwise-268m workload and only there", file=sys.stderr)
         sys.exit(2)

@@ -104,7 +104,20 @@ enum {
  * betas, eps, weight_decay).  `nonfinite`, if not NULL, is a device counter
  * that the call increments by the number of elements whose new parameter,
  * first moment or second moment is not finite (the optimizer non-finite
- * count of the reference's one-update smoke check). */
+ * count of the reference's one-update smoke check).
+ *
+ * Two optional device inputs let a caller feed the gradient pre-pass
+ * (pa_grad_stats_list) into the update without a host round trip:
+ *   grad_scale       if not NULL, a device float read by the kernels: every
+ *                    gradient, after widening to FP32, is multiplied by it
+ *                    (one binary32 multiplication) before the update.  Used
+ *                    for global-norm clipping; NULL leaves gradients as
+ *                    they are (exactly as a scale of 1 would).
+ *   skip_if_nonzero  if not NULL, a device counter read by the kernels:
+ *                    when it is nonzero the call changes nothing (no
+ *                    parameter, state or counter is written).  Used to skip
+ *                    an update whose gradients hold NaN or Inf.
+ * Both are read on `stream`, after the work enqueued before the call. */
 typedef struct {
   double lr;
   double beta1;
@@ -112,6 +125,8 @@ typedef struct {
   double eps;
   double weight_decay;
   unsigned long long* nonfinite;
+  const float* grad_scale;
+  const unsigned long long* skip_if_nonzero;
 } pa_hyper;
 
 /* PA_FP32 state: two device arrays of n floats. */
@@ -168,6 +183,34 @@ int pa_step_typed(int mode, int param_dtype, int grad_dtype, void* params, const
 int pa_step_list_typed(int mode, int param_dtype, int grad_dtype, size_t count, void* const* params,
                        const void* const* grads, void* const* states, const size_t* n,
                        const pa_hyper* hyper, long long step, void* stream);
+
+/* Gradient pre-pass over `count` gradient tensors of one element type
+ * (PA_DT_F32, PA_DT_BF16 or PA_DT_F16; grads[i] points to n[i] device
+ * elements), in one persistent launch and one read of every gradient,
+ * followed by a one-workgroup finalizer.  Device outputs, overwritten:
+ *   sumsq       (required) the sum of the squares of all gradients, in
+ *               double: each square is exact in double and the partial sums
+ *               follow a fixed order for a given device and list, so the
+ *               result is reproducible; it differs from the exact sum by at
+ *               most the rounding of a double summation (NaN if any
+ *               gradient is NaN, else +Inf if any is infinite).
+ *   nonfinite   (nullable) the number of NaN or infinite gradients.
+ *   clip_scale  (nullable) min(1, max_norm / (sqrt(sumsq) + 1e-6)), formed
+ *               in double and rounded once to binary32 (NaN stays NaN);
+ *               requires a finite max_norm > 0.
+ * Pass clip_scale as pa_hyper.grad_scale and nonfinite as
+ * pa_hyper.skip_if_nonzero of the following update for clipping and an
+ * overflow skip with no host synchronisation.  The pages train AdamW on
+ * dense FP32, FP16 and BF16 gradients (TurboAdam package page,
+ * Verification; KBench reference, `grads.float()`) and gate on a non-finite
+ * optimizer count (Packed AdamW Reference README, One-update smoke test).
+ * Gradients must be aligned to their element size and must not overlap the
+ * outputs.  The tensor table and per-workgroup partials are cached per
+ * distinct list like the step's plans (see pa_release_plans).  count == 0,
+ * or only empty tensors, writes 0, 0 and the coefficient of a zero norm. */
+int pa_grad_stats_list(int grad_dtype, size_t count, const void* const* grads, const size_t* n,
+                       double max_norm, double* sumsq, unsigned long long* nonfinite, float* clip_scale,
+                       void* stream);
 
 /* Persistent optimizer-state bytes for n parameters in `mode` (the state
  * ledger; Packed AdamW Reference README, "The narrow result": 8 bytes per

@@ -31,6 +31,13 @@ BLOCK = 2048
 
 _lib = None
 
+
+class SumsqAcc(ctypes.Structure):
+    """Exact sum-of-squares accumulator (a 640-bit integer in units of 2^-298)."""
+    _fields_ = [("limb", ctypes.c_uint64 * 10), ("nonfinite", ctypes.c_ulonglong),
+                ("has_nan", ctypes.c_int), ("has_inf", ctypes.c_int)]
+
+
 _f32p = ctypes.POINTER(ctypes.c_float)
 _u32p = ctypes.POINTER(ctypes.c_uint32)
 _u16p = ctypes.POINTER(ctypes.c_uint16)
@@ -66,6 +73,14 @@ def _load():
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_block_len.restype = ctypes.c_int
     lib.oracle_e4_bias.restype = ctypes.c_int
+    lib.oracle_sumsq_add.argtypes = [ctypes.POINTER(SumsqAcc), ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t]
+    lib.oracle_sumsq_add.restype = None
+    lib.oracle_sumsq_value.argtypes = [ctypes.POINTER(SumsqAcc)]
+    lib.oracle_sumsq_value.restype = ctypes.c_double
+    lib.oracle_clip_scale.argtypes = [ctypes.c_double, ctypes.c_double]
+    lib.oracle_clip_scale.restype = ctypes.c_float
+    lib.oracle_scale_grads.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_float, _f32p, ctypes.c_size_t]
+    lib.oracle_scale_grads.restype = None
     _lib = lib
     return lib
 
@@ -196,3 +211,39 @@ def num_threads():
 
 def e4_bias():
     return int(_load().oracle_e4_bias())
+
+
+def sumsq_add(acc, gdt, g):
+    """Add the squares of array g (element type gdt) to an exact SumsqAcc."""
+    _need(g, _DT_NP[gdt], "g")
+    _load().oracle_sumsq_add(ctypes.byref(acc), int(gdt), g.ctypes.data, g.size)
+
+
+def sumsq_value(acc):
+    """The accumulated sum of squares, rounded once to double."""
+    return float(_load().oracle_sumsq_value(ctypes.byref(acc)))
+
+
+def grad_stats(gdt, grads, max_norm=None):
+    """Gradient pre-pass over a list of arrays of one element type gdt:
+    (sum of squares, exact then rounded once to double; non-finite count;
+    clip coefficient for max_norm, or None)."""
+    acc = SumsqAcc()
+    for g in grads:
+        sumsq_add(acc, gdt, g)
+    sumsq = sumsq_value(acc)
+    clip = None if max_norm is None else float(clip_scale(sumsq, max_norm))
+    return sumsq, int(acc.nonfinite), clip
+
+
+def clip_scale(sumsq, max_norm):
+    """min(1, max_norm / (sqrt(sumsq) + 1e-6)) in double, rounded to binary32."""
+    return np.float32(_load().oracle_clip_scale(float(sumsq), float(max_norm)))
+
+
+def scale_grads(gdt, g, scale):
+    """float32 array widen(g) * scale, one binary32 multiplication per element."""
+    _need(g, _DT_NP[gdt], "g")
+    out = np.empty(g.size, np.float32)
+    _load().oracle_scale_grads(int(gdt), g.ctypes.data, float(np.float32(scale)), _ptr(out, _f32p), g.size)
+    return out

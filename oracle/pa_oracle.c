@@ -480,3 +480,136 @@ int oracle_num_threads(void) {
 
 int oracle_block_len(void) { return ORACLE_BLOCK; }
 int oracle_e4_bias(void) { return ORACLE_E4_BIAS; }
+
+/* ---------------------------------------------------------------------- */
+/* Gradient pre-pass: sum of squares, non-finite count, clip coefficient.  */
+/* ---------------------------------------------------------------------- */
+
+/* The pages run AdamW on ordinary dense gradients of FP32, FP16 or BF16
+ * parameters (TurboAdam package page, Verification; KBench reference,
+ * `grads.float()`), and the smoke check of the Packed AdamW Reference README
+ * counts non-finite optimizer values.  The pre-pass gathers, in one read of
+ * the gradients, what a training loop needs before the update: the squared
+ * L2 norm of all gradients, the number of non-finite gradient values, and
+ * the usual clipping coefficient min(1, max_norm / (norm + 1e-6)).
+ *
+ * The sum is exact: every binary32 value is m * 2^e with an integer m below
+ * 2^24 and e >= -149, so its square m^2 * 2^(2e) is an integer multiple of
+ * 2^-298 below 2^554.  The accumulator holds the sum as a 640-bit integer
+ * in units of 2^-298 (room for 2^86 maximal terms), and the value is that
+ * integer rounded once to double, to nearest even.  Any NaN makes the sum
+ * NaN; otherwise any infinity makes it +Inf, as IEEE addition of
+ * non-negative terms does. */
+#define ORACLE_ACC_LIMBS 10
+
+typedef struct {
+    uint64_t limb[ORACLE_ACC_LIMBS];   /* least significant first */
+    unsigned long long nonfinite;
+    int has_nan;
+    int has_inf;
+} oracle_sumsq_acc;
+
+static void acc_add_square(oracle_sumsq_acc* a, float x) {
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    uint32_t ex = (u >> 23) & 0xFFu, mant = u & 0x7FFFFFu;
+    if (ex == 0xFFu) {
+        a->nonfinite++;
+        if (mant) a->has_nan = 1;
+        else a->has_inf = 1;
+        return;
+    }
+    uint64_t m = ex ? (mant | 0x800000u) : mant;   /* x = m * 2^e */
+    int e = ex ? (int)ex - 150 : -149;
+    if (m == 0) return;
+    uint64_t m2 = m * m;                            /* < 2^48 */
+    int shift = 2 * e + 298;                        /* 0 .. 506 */
+    int k = shift >> 6, off = shift & 63;
+    unsigned __int128 t = (unsigned __int128)m2 << off;
+    uint64_t parts[2] = {(uint64_t)t, (uint64_t)(t >> 64)};
+    unsigned carry = 0;
+    for (int i = k; i < ORACLE_ACC_LIMBS; ++i) {
+        uint64_t add = (i - k < 2) ? parts[i - k] : 0;
+        uint64_t s1 = a->limb[i] + add;
+        unsigned c1 = s1 < add;
+        uint64_t s2 = s1 + carry;
+        unsigned c2 = s2 < carry;
+        a->limb[i] = s2;
+        carry = c1 | c2;
+        if (i - k >= 1 && carry == 0) break;
+    }
+}
+
+static void acc_merge(oracle_sumsq_acc* dst, const oracle_sumsq_acc* src) {
+    unsigned carry = 0;
+    for (int i = 0; i < ORACLE_ACC_LIMBS; ++i) {
+        uint64_t s1 = dst->limb[i] + src->limb[i];
+        unsigned c1 = s1 < src->limb[i];
+        uint64_t s2 = s1 + carry;
+        unsigned c2 = s2 < carry;
+        dst->limb[i] = s2;
+        carry = c1 | c2;
+    }
+    dst->nonfinite += src->nonfinite;
+    dst->has_nan |= src->has_nan;
+    dst->has_inf |= src->has_inf;
+}
+
+/* Add the squares of n gradients of element type gdt (0 binary32,
+ * 1 bfloat16, 2 binary16; 16-bit ones as bit patterns) to the accumulator
+ * (zero-filled by the caller before the first call). */
+void oracle_sumsq_add(oracle_sumsq_acc* acc, int gdt, const void* g, size_t n) {
+    build_tables();
+#pragma omp parallel
+    {
+        oracle_sumsq_acc local;
+        memset(&local, 0, sizeof(local));
+        ptrdiff_t i;
+#pragma omp for schedule(static)
+        for (i = 0; i < (ptrdiff_t)n; ++i) acc_add_square(&local, widen_at(gdt, g, (size_t)i));
+#pragma omp critical
+        acc_merge(acc, &local);
+    }
+}
+
+static int acc_bit(const oracle_sumsq_acc* a, int i) {
+    return (int)((a->limb[i >> 6] >> (i & 63)) & 1u);
+}
+
+/* The accumulated sum of squares, rounded once to double (nearest even). */
+double oracle_sumsq_value(const oracle_sumsq_acc* a) {
+    if (a->has_nan) return NAN;
+    if (a->has_inf) return INFINITY;
+    int top = -1;
+    for (int i = ORACLE_ACC_LIMBS * 64 - 1; i >= 0; --i)
+        if (acc_bit(a, i)) { top = i; break; }
+    if (top < 0) return 0.0;
+    int lo = top - 52 > 0 ? top - 52 : 0;
+    uint64_t mant = 0;
+    for (int i = top; i >= lo; --i) mant = (mant << 1) | (uint64_t)acc_bit(a, i);
+    if (lo > 0) {
+        int round = acc_bit(a, lo - 1), sticky = 0;
+        for (int i = lo - 2; i >= 0 && !sticky; --i) sticky = acc_bit(a, i);
+        if (round && (sticky || (mant & 1u))) {
+            mant += 1;
+            if (mant >> 53) { mant >>= 1; lo += 1; }
+        }
+    }
+    return ldexp((double)mant, lo - 298);
+}
+
+/* Clipping coefficient of the global norm sqrt(sumsq) for max_norm, in
+ * double: max_norm / (norm + 1e-6), capped at 1 (a NaN stays NaN), then
+ * rounded to binary32 once. */
+float oracle_clip_scale(double sumsq, double max_norm) {
+    double coef = max_norm / (sqrt(sumsq) + 1e-6);
+    if (isnan(coef)) return NAN;
+    return (float)(coef < 1.0 ? coef : 1.0);
+}
+
+/* Gradients scaled before the update: out[i] = widen(g[i]) * scale, one
+ * binary32 multiplication per element. */
+void oracle_scale_grads(int gdt, const void* g, float scale, float* out, size_t n) {
+    build_tables();
+    for (size_t i = 0; i < n; ++i) out[i] = widen_at(gdt, g, i) * scale;
+}

@@ -194,3 +194,44 @@ def test_typed_argument_rules(pa):
     assert f(1, 1, 0, FAKE + 2, FAKE + 8192, FAKE + 16388, 64) == pa.PA_ERR_ALIGN
     # overlapping bf16 params and words
     assert f(1, 1, 1, FAKE, FAKE + 65536, FAKE + 64, 64) == pa.PA_ERR_ALIAS
+
+
+def test_grad_stats_argument_rules(pa):
+    L = pa.lib()
+    G = (ctypes.c_void_p * 1)(FAKE)
+    N = (ctypes.c_size_t * 1)(64)
+    f = lambda gdt, cnt, g, n, mx, s, nf, cl: L.pa_grad_stats_list(gdt, cnt, g, n, mx, s, nf, cl, None)
+    assert f(3, 1, G, N, 0.0, FAKE + 4096, None, None) == pa.PA_ERR_ARG            # unknown dtype
+    assert f(0, 1, G, N, 0.0, None, None, None) == pa.PA_ERR_ARG                    # no sumsq output
+    assert f(0, 1, None, N, 0.0, FAKE + 4096, None, None) == pa.PA_ERR_ARG          # no gradient list
+    assert f(0, 1, G, N, 0.0, FAKE + 4096, None, FAKE + 4104) == pa.PA_ERR_ARG      # clip without max_norm
+    assert f(0, 1, G, N, float("nan"), FAKE + 4096, None, FAKE + 4104) == pa.PA_ERR_ARG
+    assert f(0, 1, G, N, 1.0, FAKE + 4100, None, None) == pa.PA_ERR_ALIGN           # sumsq not 8-aligned
+    assert f(0, 1, G, N, 1.0, FAKE + 4096, FAKE + 4108, None) == pa.PA_ERR_ALIGN    # counter not 8-aligned
+    assert f(0, 1, G, N, 1.0, FAKE + 4096, FAKE + 4096, None) == pa.PA_ERR_ALIAS    # outputs overlap
+    assert f(0, 1, G, N, 1.0, FAKE + 4096, FAKE + 4104, FAKE + 4100) == pa.PA_ERR_ALIAS
+
+
+def test_hyper_device_inputs_rules(pa):
+    n = 1024
+    h = _hyper(pa)
+    h.grad_scale = FAKE + 2 ** 20 + 2                       # not 4-aligned
+    assert _raw_step(pa, 1, FAKE, FAKE + 8192, FAKE + 16384, n, h) == pa.PA_ERR_ALIGN
+    h = _hyper(pa)
+    h.skip_if_nonzero = FAKE + 2 ** 20 + 4                  # not 8-aligned
+    assert _raw_step(pa, 1, FAKE, FAKE + 8192, FAKE + 16384, n, h) == pa.PA_ERR_ALIGN
+    h = _hyper(pa)
+    h.skip_if_nonzero = FAKE + 64                           # inside the params
+    assert _raw_step(pa, 1, FAKE, FAKE + 8192, FAKE + 16384, n, h) == pa.PA_ERR_ALIAS
+    h = _hyper(pa)
+    h.grad_scale = FAKE + 16384 + 128                       # inside the state words
+    assert _raw_step(pa, 1, FAKE, FAKE + 8192, FAKE + 16384, n, h) == pa.PA_ERR_ALIAS
+    h = _hyper(pa)
+    h.nonfinite = FAKE + 2 ** 20
+    h.skip_if_nonzero = FAKE + 2 ** 20                      # one counter as both: would race
+    assert _raw_step(pa, 1, FAKE, FAKE + 8192, FAKE + 16384, n, h) == pa.PA_ERR_ALIAS
+    bw = pa.BlockwiseState(FAKE + 2 ** 20, FAKE + 2 ** 21, FAKE + 2 ** 22, FAKE + 2 ** 23,
+                           FAKE + 2 ** 24, FAKE + 2 ** 25, FAKE + 2 ** 26)
+    h = _hyper(pa)
+    h.grad_scale = FAKE + 2 ** 22 + 8                       # inside the v codes
+    assert _raw_step(pa, 3, FAKE, FAKE + 2 ** 18, ctypes.addressof(bw), 2048, h) == pa.PA_ERR_ALIAS

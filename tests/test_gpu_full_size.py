@@ -123,3 +123,47 @@ def test_blockwise_268m_sampled(pa):
     finally:
         del p, g, mc, vc
         torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_llama_7b_grad_stats_exact(pa):
+    """The gradient pre-pass over all 6,738,415,616 gradients of the 291-tensor
+    list, in the launch configuration the benchmark times, against the
+    oracle's exact sum (accumulated tensor by tensor on the host) and its
+    non-finite count."""
+    import math
+    import torch
+    cfg = 4
+    sizes = workloads.sizes(cfg)
+    banner(f"llama-7b grad stats: allocating {sum(sizes) * 4 / 1e9:.1f} GB of gradients")
+    gs = [torch.empty(n, dtype=torch.float32, device="cuda:0") for n in sizes]
+    try:
+        workloads.device_fill_grads(cfg, 1, gs)
+        k = next(i for i, n in enumerate(sizes) if n > 1 << 20 and i > 10)
+        gs[k][12345] = float("inf")
+        s = torch.zeros(1, dtype=torch.float64, device="cuda:0")
+        nf = torch.zeros(1, dtype=torch.int64, device="cuda:0")
+        clip = torch.zeros(1, dtype=torch.float32, device="cuda:0")
+        banner("llama-7b grad stats: one pre-pass over 291 tensors (one infinity planted)")
+        pa.pa_grad_stats_list(gs, s, nf, clip, max_norm=1.0)
+        torch.cuda.synchronize()
+        assert math.isinf(s.item()) and int(nf.item()) == 1 and clip.item() == 0.0
+        gs[k][12345] = 0.0
+        banner("llama-7b grad stats: finite gradients")
+        pa.pa_grad_stats_list(gs, s, nf, clip, max_norm=1.0)
+        torch.cuda.synchronize()
+        acc = oracle.SumsqAcc()
+        for g in gs:
+            oracle.sumsq_add(acc, oracle.DT_F32, to_host(g))
+        want = oracle.sumsq_value(acc)
+        n = sum(sizes)
+        got = s.item()
+        assert acc.nonfinite == 0 and int(nf.item()) == 0
+        assert abs(got - want) <= (n - 1) * 2.0 ** -53 * want, (got, want)
+        c = np.float32(clip.item())
+        assert abs(int(c.view(np.int32)) - int(oracle.clip_scale(want, 1.0).view(np.int32))) <= 1
+        banner(f"llama-7b grad stats: sumsq {got!r} vs exact {want!r} (rel {abs(got - want) / want:.2e})")
+    finally:
+        del gs
+        torch.cuda.empty_cache()
+        pa.pa_release_plans()
