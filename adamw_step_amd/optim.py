@@ -17,7 +17,7 @@ from __future__ import annotations
 
 import torch
 
-from . import PA_FP32, PA_PACKED_E4, PA_PACKED_FP16, StepList, pa_state_bytes
+from . import PA_FP32, PA_PACKED_E4, PA_PACKED_FP16, GradStats, StepList, pa_state_bytes
 
 _MODES = {"e4": PA_PACKED_E4, "fp16": PA_PACKED_FP16, "fp32": PA_FP32}
 
@@ -30,10 +30,19 @@ class PackedAdamW(torch.optim.Optimizer):
     device counter of elements whose new parameter or moment was not finite
     (the optimizer non-finite count of the reference's smoke check); read it
     with ``nonfinite_count()``.
+
+    ``max_grad_norm`` clips the global gradient norm and ``skip_nonfinite``
+    skips an update whose gradients hold NaN or Inf.  Either one adds the
+    gradient pre-pass (pa_grad_stats_list) before the update; its clip
+    coefficient and non-finite count reach the update on the device, with
+    no host synchronisation.  A skipped update does not count as a step:
+    the pre-pass count is copied to pinned host memory and checked at the
+    next ``step()`` (by then long finished), which then reuses the step
+    number.  ``last_grad_norm()`` reads the norm of the latest pre-pass.
     """
 
     def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0,
-                 mode="e4", count_nonfinite=True):
+                 mode="e4", count_nonfinite=True, max_grad_norm=None, skip_nonfinite=False):
         if mode not in _MODES:
             raise ValueError(f"mode must be one of {sorted(_MODES)}")
         defaults = dict(lr=lr, betas=betas, eps=eps, weight_decay=weight_decay)
@@ -56,6 +65,20 @@ class PackedAdamW(torch.optim.Optimizer):
                 raise TypeError("parameters must be contiguous tensors of one dtype on one GPU")
             self._init_state(p)
         self._nonfinite = torch.zeros(1, dtype=torch.int64, device=dev) if count_nonfinite else None
+        if max_grad_norm is not None and not (float(max_grad_norm) > 0.0):
+            raise ValueError("max_grad_norm must be positive")
+        self.max_grad_norm = None if max_grad_norm is None else float(max_grad_norm)
+        self.skip_nonfinite = bool(skip_nonfinite)
+        self.skipped_steps = 0
+        self._stats = None
+        self._stats_key = None
+        if self.max_grad_norm is not None or self.skip_nonfinite:
+            self._sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
+            self._grad_bad = torch.zeros(1, dtype=torch.int64, device=dev)
+            self._clip = torch.ones(1, dtype=torch.float32, device=dev)
+            self._bad_host = torch.zeros(1, dtype=torch.int64, pin_memory=True)
+            self._bad_event = torch.cuda.Event()
+            self._pending = False
 
     def _init_state(self, p):
         st = self.state[p]
@@ -75,6 +98,21 @@ class PackedAdamW(torch.optim.Optimizer):
 
     def nonfinite_count(self):
         return 0 if self._nonfinite is None else int(self._nonfinite.item())
+
+    def last_grad_norm(self):
+        """Global L2 norm of the gradients seen by the latest pre-pass (None without one)."""
+        if self._stats is None:
+            return None
+        return float(self._sumsq.item()) ** 0.5
+
+    def _reconcile(self):
+        # A pre-pass whose count was nonzero skipped its update on the device.
+        if self._stats is not None and self.skip_nonfinite and self._pending:
+            self._bad_event.synchronize()
+            if int(self._bad_host.item()) != 0:
+                self.step_count -= 1
+                self.skipped_steps += 1
+            self._pending = False
 
     @torch.no_grad()
     def step(self, closure=None):
@@ -99,16 +137,33 @@ class PackedAdamW(torch.optim.Optimizer):
         if self._prepared is None or key != self._prepared_key:
             self._prepared = StepList(self._mode, params, grads, states)
             self._prepared_key = key
+        self._reconcile()
         self.step_count += 1
         beta1, beta2 = group["betas"]
         hyper = dict(lr=group["lr"], beta1=beta1, beta2=beta2, eps=group["eps"],
                      weight_decay=group["weight_decay"])
         if self._nonfinite is not None:
             hyper["nonfinite"] = self._nonfinite
+        if self.max_grad_norm is not None or self.skip_nonfinite:
+            gkey = tuple(g.data_ptr() for g in grads)
+            if self._stats is None or gkey != self._stats_key:
+                self._stats = GradStats(grads)
+                self._stats_key = gkey
+            self._stats.run(self._sumsq, self._grad_bad,
+                            self._clip if self.max_grad_norm is not None else None,
+                            max_norm=self.max_grad_norm or 0.0)
+            if self.max_grad_norm is not None:
+                hyper["grad_scale"] = self._clip
+            if self.skip_nonfinite:
+                hyper["skip_if_nonzero"] = self._grad_bad
+                self._bad_host.copy_(self._grad_bad, non_blocking=True)
+                self._bad_event.record()
+                self._pending = True
         self._prepared.step(hyper, self.step_count)
         return loss
 
     def state_dict(self):
+        self._reconcile()
         sd = super().state_dict()
         sd["packed"] = {"mode": self.mode, "step": self.step_count}
         return sd
@@ -142,3 +197,5 @@ class PackedAdamW(torch.optim.Optimizer):
                     st[k] = v.contiguous()
         self.step_count = int(meta.get("step", 0))
         self._prepared = None
+        if self._stats is not None:
+            self._pending = False

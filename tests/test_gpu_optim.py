@@ -107,3 +107,69 @@ def test_short_training_run():
     assert all(np.isfinite(losses)) and opt.nonfinite_count() == 0
     # uniformly random tokens carry nothing to learn: the loss stays near ln(vocab)
     assert abs(np.mean(losses[-10:]) - np.log(12096)) < 0.5
+
+
+def test_optimizer_clipping_matches_oracle():
+    """max_grad_norm: the pre-pass coefficient scales every gradient on the
+    device; the oracle steps on gradients scaled by that same coefficient,
+    and the coefficient itself agrees with the oracle's exact-norm one."""
+    import torch
+    from adamw_step_amd.optim import PackedAdamW
+    sizes = [70000, 4096, 333]
+    ps = _params(torch, sizes, 5)
+    hp = [p.detach().cpu().numpy().copy() for p in ps]
+    hs = [np.zeros(n, np.uint32) for n in sizes]
+    opt = PackedAdamW(ps, lr=1e-3, weight_decay=0.01, mode="e4", max_grad_norm=0.5)
+    r = np.random.Generator(np.random.PCG64(6))
+    for t in range(1, 4):
+        hg = [(r.normal(0, 1e-2, n)).astype(np.float32) for n in sizes]
+        for p, g in zip(ps, hg):
+            p.grad = torch.from_numpy(g).cuda()
+        banner(f"PackedAdamW clipped step {t}")
+        opt.step()
+        torch.cuda.synchronize()
+        c = np.float32(opt._clip.item())
+        _, bad, want_c = oracle.grad_stats(0, hg, max_norm=0.5)
+        assert bad == 0 and c < 1.0
+        assert abs(int(c.view(np.int32)) - int(np.float32(want_c).view(np.int32))) <= 1
+        assert abs(opt.last_grad_norm() - float(np.sqrt(sum(float(np.dot(g.astype(np.float64), g)) for g in hg)))) \
+            <= 1e-9 * opt.last_grad_norm()
+        for i in range(len(sizes)):
+            oracle.step_packed(1, hp[i], oracle.scale_grads(0, hg[i], c), hs[i], scalars(t))
+            assert_words(opt.state[ps[i]]["words"].cpu().numpy().view(np.uint32), hs[i])
+            assert_params(ps[i].detach().cpu().numpy(), hp[i])
+
+
+def test_optimizer_skips_nonfinite_updates():
+    """skip_nonfinite: an update whose gradients hold an Inf changes nothing,
+    and the following update reuses its step number."""
+    import torch
+    from adamw_step_amd.optim import PackedAdamW
+    sizes = [5000, 64]
+    ps = _params(torch, sizes, 9)
+    hp = [p.detach().cpu().numpy().copy() for p in ps]
+    hs = [np.zeros(n, np.uint32) for n in sizes]
+    opt = PackedAdamW(ps, lr=1e-3, weight_decay=0.01, mode="e4", skip_nonfinite=True)
+    r = np.random.Generator(np.random.PCG64(10))
+    plan = ["ok", "inf", "ok", "nan", "ok"]
+    t_oracle = 0
+    for kind in plan:
+        hg = [(r.normal(0, 1e-3, n)).astype(np.float32) for n in sizes]
+        if kind == "inf":
+            hg[0][17] = np.inf
+        elif kind == "nan":
+            hg[1][3] = np.nan
+        for p, g in zip(ps, hg):
+            p.grad = torch.from_numpy(g).cuda()
+        banner(f"PackedAdamW skip test: {kind} gradients")
+        opt.step()
+        torch.cuda.synchronize()
+        if kind == "ok":
+            t_oracle += 1
+            for i in range(len(sizes)):
+                oracle.step_packed(1, hp[i], hg[i], hs[i], scalars(t_oracle))
+        for i in range(len(sizes)):
+            assert_words(opt.state[ps[i]]["words"].cpu().numpy().view(np.uint32), hs[i])
+            assert_params(ps[i].detach().cpu().numpy(), hp[i])
+    opt._reconcile()
+    assert opt.skipped_steps == 2 and opt.step_count == 3 and opt.nonfinite_count() == 0
