@@ -81,6 +81,25 @@ def _load():
     lib.oracle_clip_scale.restype = ctypes.c_float
     lib.oracle_scale_grads.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_float, _f32p, ctypes.c_size_t]
     lib.oracle_scale_grads.restype = None
+    _u64p = ctypes.POINTER(ctypes.c_uint64)
+    lib.oracle_philox4x64.argtypes = [_u64p, _u64p, _u64p]
+    lib.oracle_philox4x64.restype = None
+    lib.oracle_turbo_state_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t]
+    lib.oracle_turbo_state_bytes.restype = ctypes.c_size_t
+    vp = ctypes.c_void_p
+    lib.oracle_turbo_step.argtypes = [_f32p, _f32p, ctypes.c_size_t, ctypes.c_uint32, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, vp, vp, vp, vp, vp, vp, _f32p, _f32p, _f32p, ctypes.c_double,
+                                      ctypes.c_ulonglong, ctypes.c_longlong]
+    lib.oracle_turbo_step.restype = ctypes.c_ulonglong
+    lib.oracle_q1_levels.argtypes = [ctypes.c_uint16, ctypes.c_uint16, ctypes.c_int, _f32p]
+    lib.oracle_q1_levels.restype = None
+    lib.oracle_q1_block.argtypes = [_f32p, ctypes.c_size_t, ctypes.c_int, _f32p, _u8p, _u16p, _f32p]
+    lib.oracle_q1_block.restype = None
+    lib.oracle_ustate_group.argtypes = [_f32p, ctypes.c_size_t, ctypes.c_float, _f32p, _u8p, _u16p,
+                                        ctypes.POINTER(ctypes.c_double)]
+    lib.oracle_ustate_group.restype = None
+    lib.oracle_ustate_decode.argtypes = [_u8p, ctypes.c_size_t, ctypes.c_uint16, ctypes.c_float, _f32p]
+    lib.oracle_ustate_decode.restype = None
     _lib = lib
     return lib
 
@@ -246,4 +265,98 @@ def scale_grads(gdt, g, scale):
     _need(g, _DT_NP[gdt], "g")
     out = np.empty(g.size, np.float32)
     _load().oracle_scale_grads(int(gdt), g.ctypes.data, float(np.float32(scale)), _ptr(out, _f32p), g.size)
+    return out
+
+
+def philox4x64(counter, key):
+    """Philox4x64-10 of a 4-word counter and a 2-word key (four uint64 words)."""
+    c = np.array(counter, np.uint64)
+    k = np.array(key, np.uint64)
+    out = np.zeros(4, np.uint64)
+    u64 = ctypes.POINTER(ctypes.c_uint64)
+    _load().oracle_philox4x64(c.ctypes.data_as(u64), k.ctypes.data_as(u64), out.ctypes.data_as(u64))
+    return out
+
+
+def turbo_state_bytes(compress_m, compress_v, bits, n):
+    return int(_load().oracle_turbo_state_bytes(int(compress_m), int(compress_v), int(bits), int(n)))
+
+
+class TurboState:
+    """Host copy of one tensor's TurboAdam state, zero-filled (the empty state)."""
+
+    def __init__(self, n, compress_m=True, compress_v=True, bits=4):
+        self.n, self.compress_m, self.compress_v, self.bits = n, bool(compress_m), bool(compress_v), bits
+        self.m_codes = np.zeros((n + 15) // 16, np.uint32) if compress_m else None
+        self.m_means = np.zeros((n + 63) // 64, np.uint16) if compress_m else None
+        self.m_fp32 = None if compress_m else np.zeros(n, np.float32)
+        self.v_index = np.zeros((n * bits + 31) // 32, np.uint32) if compress_v else None
+        self.v_ends = np.zeros(2 * ((n + 127) // 128), np.uint16) if compress_v else None
+        self.v_fp32 = None if compress_v else np.zeros(n, np.float32)
+        self.scal = np.zeros(3, np.float32)
+
+    def arrays(self):
+        return dict(m_codes=self.m_codes, m_means=self.m_means, m_fp32=self.m_fp32, v_index=self.v_index,
+                    v_ends=self.v_ends, v_fp32=self.v_fp32, scal=self.scal)
+
+
+def turbo_scalars(beta1, beta2, step):
+    """[bc1, bc1 of the previous step, bc2 of the previous step], each formed in
+    double and rounded once to binary32."""
+    return np.array([1.0 - beta1 ** step, 1.0 - beta1 ** (step - 1), 1.0 - beta2 ** (step - 1)], np.float32)
+
+
+def turbo_step(p, g, st, sc, ts, step, tensor_id=0, factor=1.1, seed=0x12345678):
+    """One TurboAdam step of one tensor, in place on p and the TurboState st.
+    Returns the non-finite count."""
+    _need(p, np.float32, "p")
+    _need(g, np.float32, "g")
+    _need(sc, np.float32, "scalars")
+    _need(ts, np.float32, "turbo scalars")
+    assert p.size == g.size == st.n
+    addr = lambda a: None if a is None else a.ctypes.data
+    return int(_load().oracle_turbo_step(
+        _ptr(p, _f32p), _ptr(g, _f32p), p.size, int(tensor_id), int(st.compress_m), int(st.compress_v), int(st.bits),
+        addr(st.m_codes), addr(st.m_means), addr(st.m_fp32), addr(st.v_index), addr(st.v_ends), addr(st.v_fp32),
+        _ptr(st.scal, _f32p), _ptr(sc, _f32p), _ptr(ts, _f32p), float(factor), int(seed), int(step)))
+
+
+def q1_levels(lo16, hi16, bits):
+    """Decoded value of every 1Q index of a block with fp16 endpoints (bits)."""
+    out = np.zeros(1 << bits, np.float32)
+    _load().oracle_q1_levels(int(lo16), int(hi16), int(bits), _ptr(out, _f32p))
+    return out
+
+
+def q1_block(v, bits, u):
+    """1Q encode of one block (<= 128 values) with draws u: (indices, (lo, hi) fp16 bits, decoded)."""
+    v = np.ascontiguousarray(v, np.float32)
+    u = np.ascontiguousarray(u, np.float32)
+    assert v.size == u.size <= 128
+    idx = np.zeros(v.size, np.uint8)
+    ends = np.zeros(2, np.uint16)
+    dec = np.zeros(v.size, np.float32)
+    _load().oracle_q1_block(_ptr(v, _f32p), v.size, int(bits), _ptr(u, _f32p), _ptr(idx, _u8p), _ptr(ends, _u16p),
+                            _ptr(dec, _f32p))
+    return idx, ends, dec
+
+
+def ustate_group(q, s_enc, u_pair):
+    """UState encode of one group (<= 64 values): (codes, bf16 mean bits, squared residuals)."""
+    q = np.ascontiguousarray(q, np.float32)
+    u_pair = np.ascontiguousarray(u_pair, np.float32)
+    assert q.size <= 64 and u_pair.size >= (q.size + 1) // 2
+    codes = np.zeros(q.size, np.uint8)
+    mean = np.zeros(1, np.uint16)
+    r2 = np.zeros(q.size, np.float64)
+    _load().oracle_ustate_group(_ptr(q, _f32p), q.size, float(np.float32(s_enc)), _ptr(u_pair, _f32p),
+                                _ptr(codes, _u8p), _ptr(mean, _u16p), r2.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    return codes, int(mean[0]), r2
+
+
+def ustate_decode(codes, mean16, s_dec):
+    """UState decode of one group."""
+    codes = np.ascontiguousarray(codes, np.uint8)
+    out = np.zeros(codes.size, np.float32)
+    _load().oracle_ustate_decode(_ptr(codes, _u8p), codes.size, int(mean16), float(np.float32(s_dec)), _ptr(out, _f32p))
     return out

@@ -24,6 +24,11 @@
  *    "quantized-optimizer-state", environment reference, routines
  *    `quantized_adamw_step` and `_requantise`.
  *
+ *  - The gradient pre-pass (exact sum of squares, non-finite count, clip
+ *    coefficient) and the TurboAdam compressed state (UState first moment,
+ *    1Q second moment, Philox4x64-10 draws): see their sections below,
+ *    each with its own readings.
+ *
  * Readings where the pages are silent (kept here as named constants):
  *  - ORACLE_E4_BIAS = 15 for both E4 lanes, IEEE-style gradual underflow at
  *    exponent field 0, every exponent field finite (no Inf/NaN codes),
@@ -47,6 +52,7 @@
  * lane is exact.
  */
 #include <math.h>
+#include <stdlib.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <string.h>
@@ -612,4 +618,338 @@ float oracle_clip_scale(double sumsq, double max_norm) {
 void oracle_scale_grads(int gdt, const void* g, float scale, float* out, size_t n) {
     build_tables();
     for (size_t i = 0; i < n; ++i) out[i] = widen_at(gdt, g, i) * scale;
+}
+
+/* ---------------------------------------------------------------------- */
+/* TurboAdam compressed state: UState first moment, 1Q second moment.     */
+/* ---------------------------------------------------------------------- */
+
+/* TurboAdam package page, "How it works", "UState", "1Q" and "Fused CUDA
+ * path": AdamW from FP32 transient moments, with the first moment persisted
+ * as UState (normalised update units q = (m/bc1) / (sqrt(v_persisted/bc2) +
+ * eps), a four-level code per value, one bf16 mean per 64 values recentred
+ * on decode, antithetic stochastic rounding, a one-step-lagged tensor scale
+ * of 1.1 x the residual RMS) and the second moment persisted as 1Q (a
+ * logarithmic grid per 128-value block between two fp16 log endpoints,
+ * packed indices, stochastic rounding between decoded positive values from
+ * a counter hash).  The page prints no code for any of these; the readings
+ * taken here (parity unpinned where the page is silent) are:
+ *
+ *  1Q, L = 2^bits indices: index 0 is exactly 0; index k in 1..L-1 decodes to
+ *    level_k = RN32(exp2(lo + (hi - lo) * (k - 1) / (L - 2))) in double,
+ *    where lo and hi are the block's fp16 endpoints: log2 (in double) of the
+ *    smallest positive finite v rounded down to fp16, and of the largest
+ *    rounded up.  Encode: 0 -> 0, NaN -> 0, +Inf -> L-1; else the largest k
+ *    with level_k <= v (at least 1), then k+1 with probability
+ *    (v - level_k) / (level_{k+1} - level_k): chosen when u < that fraction.
+ *  UState: codes 0..3 stand for -1.5, -0.5, 0.5, 1.5 times the scale.
+ *    Encode: mean = bf16(RN32(pairwise double sum of q over the group /
+ *    count)); r = q - mean; x = r / s_enc (s_enc = 0: x = 0), clamped to
+ *    [-1.5, 1.5]; the lower bracketing level k, then k+1 when u < x - L_k.
+ *    The two values 2j, 2j+1 of a pair use u and 1 - u (antithetic).
+ *    Decode: q = mean + s_dec * (L_code - Lbar), Lbar the group's mean level,
+ *    which keeps the decoded group mean at the stored mean.
+ *  The first moment of step t-1 is rebuilt as
+ *    m = (q * bc1_{t-1}) * (sqrt(v_persisted / bc2_{t-1}) + eps);
+ *    at t = 1 the state is empty and both prior moments are 0.
+ *  The residual sum of squares is a perfect pairwise tree, in double, over
+ *    r^2 in index order padded with zeros to a power of two; after the
+ *    step s_dec <- s_enc, s_enc <- RN32(factor * sqrt(sum / n)), acc <- 0.
+ *  Random numbers: Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11) with
+ *    key (seed, tensor id) and counter (j, step, 0, 0) for the values
+ *    4j..4j+3: the high 24 bits of word k give the 1Q draw of value 4j+k;
+ *    bits 8..31 of words 0 and 1 give the UState draws of the pairs
+ *    (4j, 4j+1) and (4j+2, 4j+3).  A draw is those 24 bits times 2^-24. */
+
+#define T_GROUP 64
+#define T_BLOCK 128
+
+static void philox4x64_10(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4]) {
+    uint64_t x0 = ctr[0], x1 = ctr[1], x2 = ctr[2], x3 = ctr[3];
+    uint64_t k0 = key[0], k1 = key[1];
+    for (int r = 0; r < 10; ++r) {
+        if (r) {
+            k0 += 0x9E3779B97F4A7C15ull;
+            k1 += 0xBB67AE8584CAA73Bull;
+        }
+        unsigned __int128 p0 = (unsigned __int128)0xD2E7470EE14C6C93ull * x0;
+        unsigned __int128 p1 = (unsigned __int128)0xCA5A826395121157ull * x2;
+        uint64_t hi0 = (uint64_t)(p0 >> 64), lo0 = (uint64_t)p0;
+        uint64_t hi1 = (uint64_t)(p1 >> 64), lo1 = (uint64_t)p1;
+        uint64_t n0 = hi1 ^ x1 ^ k0, n2 = hi0 ^ x3 ^ k1;
+        x0 = n0; x1 = lo1; x2 = n2; x3 = lo0;
+    }
+    out[0] = x0; out[1] = x1; out[2] = x2; out[3] = x3;
+}
+
+void oracle_philox4x64(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4]) {
+    philox4x64_10(ctr, key, out);
+}
+
+/* The draws of values 4j..4j+3: q1[k] for 1Q, us[0..1] for the UState pairs. */
+static void turbo_draws(unsigned long long seed, uint32_t tensor_id, long long step, size_t j,
+                        float q1[4], float us[2]) {
+    uint64_t ctr[4] = {(uint64_t)j, (uint64_t)step, 0, 0}, key[2] = {seed, tensor_id}, w[4];
+    philox4x64_10(ctr, key, w);
+    for (int k = 0; k < 4; ++k) q1[k] = (float)(w[k] >> 40) * 0x1p-24f;
+    for (int k = 0; k < 2; ++k) us[k] = (float)((w[k] & 0xFFFFFFFFu) >> 8) * 0x1p-24f;
+}
+
+/* fp16 value of x rounded toward -Inf (dir < 0) or +Inf (dir > 0), as bits:
+ * the nearest binary16 value on that side, found in the ordered table. */
+static uint16_t f16_directed(double x, int dir) {
+    build_tables();
+    /* tab_h holds the 0x7C01 non-negative binary16 values, ascending. */
+    double a = fabs(x);
+    int neg = x < 0;
+    /* largest non-negative code with value <= a, and smallest with value >= a */
+    unsigned lo = 0, hi = 0x7C00;
+    if (a >= tab_h[0x7C00]) { lo = hi = 0x7C00; }
+    else {
+        while (hi - lo > 1) {
+            unsigned mid = (lo + hi) / 2;
+            if (tab_h[mid] <= a) lo = mid; else hi = mid;
+        }
+        if (tab_h[lo] == a) hi = lo;
+    }
+    /* toward +Inf: for x >= 0 the upper code, for x < 0 the lower magnitude */
+    unsigned mag = (dir > 0) ? (neg ? lo : hi) : (neg ? hi : lo);
+    if (mag == 0) return neg && dir < 0 ? 0x8000u : 0;
+    return (uint16_t)((neg ? 0x8000u : 0u) | mag);
+}
+
+static double f16_value(uint16_t h) {
+    return (double)oracle_decode_f16(h);
+}
+
+static void level_table(uint16_t lo16, uint16_t hi16, int L, float* lev) {
+    double lo = f16_value(lo16), hi = f16_value(hi16);
+    lev[0] = 0.0f;
+    for (int k = 1; k < L; ++k) {
+        double x = lo + ((hi - lo) * (double)(k - 1)) / (double)(L - 2);
+        lev[k] = (float)exp2(x);
+    }
+}
+
+static double pairwise_sum(const double* a, size_t n) {   /* n a power of two */
+    if (n == 1) return a[0];
+    return pairwise_sum(a, n / 2) + pairwise_sum(a + n / 2, n / 2);
+}
+
+/* The decoded values of a block's 2^bits indices. */
+void oracle_q1_levels(uint16_t lo16, uint16_t hi16, int bits, float* lev) {
+    build_tables();
+    level_table(lo16, hi16, 1 << bits, lev);
+}
+
+/* 1Q encode of one block of len (<= 128) second-moment values with draws u:
+ * the fp16 endpoints, each value's index, and the decoded (persisted) value. */
+void oracle_q1_block(const float* v, size_t len, int bits, const float* u, uint8_t* idx, uint16_t ends[2],
+                     float* vdec) {
+    build_tables();
+    const int L = 1 << bits;
+    float vmin = INFINITY, vmax = 0.0f;
+    for (size_t i = 0; i < len; ++i) {
+        if (v[i] > 0.0f && isfinite(v[i])) {
+            if (v[i] < vmin) vmin = v[i];
+            if (v[i] > vmax) vmax = v[i];
+        }
+    }
+    uint16_t lo16 = 0, hi16 = 0;
+    if (vmax > 0.0f) {
+        lo16 = f16_directed(log2((double)vmin), -1);
+        hi16 = f16_directed(log2((double)vmax), +1);
+    }
+    ends[0] = lo16;
+    ends[1] = hi16;
+    float lev[256];
+    level_table(lo16, hi16, L, lev);
+    for (size_t i = 0; i < len; ++i) {
+        float x = v[i];
+        unsigned k;
+        if (!(x > 0.0f)) k = 0;                      /* zero, negative, NaN */
+        else if (isinf(x)) k = (unsigned)(L - 1);
+        else {
+            k = 1;
+            while (k + 1 < (unsigned)L && lev[k + 1] <= x) ++k;
+            if (k < (unsigned)(L - 1) && x > lev[k]) {
+                float f = (x - lev[k]) / (lev[k + 1] - lev[k]);
+                if (u[i] < f) ++k;
+            }
+        }
+        idx[i] = (uint8_t)k;
+        vdec[i] = lev[k];
+    }
+}
+
+static const float T_LEVEL[4] = {-1.5f, -0.5f, 0.5f, 1.5f};
+
+/* UState encode of one group of len (<= 64) values q with encode scale s_enc
+ * and one draw per pair (u_pair[j] for values 2j and 2j+1, the second using
+ * 1 - u): the bf16 mean, each code, and each residual's square (double). */
+void oracle_ustate_group(const float* q, size_t len, float s_enc, const float* u_pair, uint8_t* codes,
+                         uint16_t* mean16, double* r2) {
+    build_tables();
+    double qd[T_GROUP];
+    for (size_t k = 0; k < T_GROUP; ++k) qd[k] = k < len ? (double)q[k] : 0.0;
+    float meanf = (float)(pairwise_sum(qd, T_GROUP) / (double)len);
+    *mean16 = oracle_encode_bf16(meanf);
+    float mean = oracle_decode_bf16(*mean16);
+    for (size_t i = 0; i < len; ++i) {
+        float r = q[i] - mean;
+        r2[i] = (double)r * (double)r;
+        float x = s_enc > 0.0f ? r / s_enc : 0.0f;
+        if (x > 1.5f) x = 1.5f;
+        if (x < -1.5f) x = -1.5f;
+        float u = u_pair[i / 2];
+        if (i % 2) u = 1.0f - u;
+        unsigned k = (x >= -0.5f) + (x >= 0.5f);
+        unsigned code = k;
+        if (x >= 1.5f) code = 3;
+        else if (u < x - T_LEVEL[k]) code = k + 1;
+        codes[i] = (uint8_t)code;
+    }
+}
+
+/* UState decode of one group: mean + s_dec * (level - mean level). */
+void oracle_ustate_decode(const uint8_t* codes, size_t len, uint16_t mean16, float s_dec, float* q) {
+    build_tables();
+    double lsum = 0.0;
+    for (size_t k = 0; k < len; ++k) lsum += T_LEVEL[codes[k]];
+    float lbar = (float)(lsum / (double)len);
+    float mean = oracle_decode_bf16(mean16);
+    for (size_t k = 0; k < len; ++k) q[k] = mean + s_dec * (T_LEVEL[codes[k]] - lbar);
+}
+
+static unsigned get_bits(const uint32_t* w, size_t i, int bits) {
+    size_t per = 32 / (size_t)bits;
+    return (w[i / per] >> (bits * (int)(i % per))) & ((1u << bits) - 1u);
+}
+
+static void put_bits(uint32_t* w, size_t i, int bits, unsigned v) {
+    size_t per = 32 / (size_t)bits;
+    int sh = bits * (int)(i % per);
+    uint32_t mask = ((1u << bits) - 1u) << sh;
+    w[i / per] = (w[i / per] & ~mask) | ((uint32_t)v << sh);
+}
+
+/* Persistent bytes of one tensor of n values (TurboAdam package page,
+ * Persistent memory: UState 2 bits + one bf16 per 64 + 12 bytes per tensor;
+ * 1Q bits per value + two fp16 per 128; an uncompressed moment is FP32). */
+size_t oracle_turbo_state_bytes(int compress_m, int compress_v, int bits, size_t n) {
+    size_t b = 0;
+    b += compress_m ? 4 * ((n + 15) / 16) + 2 * ((n + T_GROUP - 1) / T_GROUP) + 12 : 4 * n;
+    b += compress_v ? 4 * ((n * (size_t)bits + 31) / 32) + 4 * ((n + T_BLOCK - 1) / T_BLOCK) : 4 * n;
+    return b;
+}
+
+/* One TurboAdam step of one tensor of n FP32 parameters, in place.
+ * s: the eight scalars of oracle_scalars for this step.  ts: bc1 = 1-beta1^t,
+ * bc1_prev = 1-beta1^(t-1), bc2_prev = 1-beta2^(t-1), each rounded once to
+ * binary32.  scal: the tensor's s_dec, s_enc, acc (used when compress_m).
+ * Returns the number of values whose p', m' or v' is not finite. */
+unsigned long long oracle_turbo_step(float* p, const float* g, size_t n, uint32_t tensor_id,
+                                     int compress_m, int compress_v, int bits,
+                                     uint32_t* m_codes, uint16_t* m_means, float* m_fp32,
+                                     uint32_t* v_index, uint16_t* v_ends, float* v_fp32,
+                                     float* scal, const float s[8], const float ts[3],
+                                     double factor, unsigned long long seed, long long step) {
+    build_tables();
+    const float bc1 = ts[0], bc1p = ts[1], bc2p = ts[2], bc2 = s[4], eps = s[7];
+    const size_t nb = (n + T_BLOCK - 1) / T_BLOCK;
+    const size_t ng = (n + T_GROUP - 1) / T_GROUP;
+    size_t padded = 1;
+    while (padded < n) padded *= 2;
+    size_t nn = n ? n : 1;
+    double* r2 = (double*)calloc(padded, sizeof(double));
+    float* m1 = (float*)malloc(sizeof(float) * nn);
+    float* v1 = (float*)malloc(sizeof(float) * nn);
+    float* vp = (float*)malloc(sizeof(float) * nn);             /* persisted new v */
+    float* u1 = (float*)malloc(sizeof(float) * nn);             /* 1Q draws */
+    float* up = (float*)malloc(sizeof(float) * (nn / 2 + 2));   /* UState pair draws */
+    float* mprev = (float*)calloc(nn, sizeof(float));
+    float* vprev = (float*)calloc(nn, sizeof(float));
+    unsigned long long bad = 0;
+    const float s_dec = compress_m ? scal[0] : 0.0f, s_enc = compress_m ? scal[1] : 0.0f;
+
+    for (size_t j = 0; j * 4 < n; ++j) {
+        float q1[4], us[2];
+        turbo_draws(seed, tensor_id, step, j, q1, us);
+        for (size_t k = 0; k < 4 && 4 * j + k < n; ++k) u1[4 * j + k] = q1[k];
+        up[2 * j] = us[0];
+        up[2 * j + 1] = us[1];
+    }
+
+    /* 1. prior moments (the state is empty at step 1), the update, new FP32 moments */
+    if (step > 1) {
+        for (size_t b = 0; b < nb; ++b) {
+            size_t i0 = b * T_BLOCK, len = i0 + T_BLOCK < n ? T_BLOCK : n - i0;
+            float lev[256];
+            if (compress_v) oracle_q1_levels(v_ends[2 * b], v_ends[2 * b + 1], bits, lev);
+            for (size_t i = i0; i < i0 + len; ++i)
+                vprev[i] = compress_v ? lev[get_bits(v_index, i, bits)] : v_fp32[i];
+        }
+        for (size_t gi = 0; gi < ng; ++gi) {
+            size_t i0 = gi * T_GROUP, len = i0 + T_GROUP < n ? T_GROUP : n - i0;
+            if (!compress_m) {
+                for (size_t i = i0; i < i0 + len; ++i) mprev[i] = m_fp32[i];
+                continue;
+            }
+            uint8_t codes[T_GROUP];
+            float q[T_GROUP];
+            for (size_t k = 0; k < len; ++k) codes[k] = (uint8_t)get_bits(m_codes, i0 + k, 2);
+            oracle_ustate_decode(codes, len, m_means[gi], s_dec, q);
+            for (size_t k = 0; k < len; ++k) {
+                float den = sqrtf(vprev[i0 + k] / bc2p) + eps;
+                mprev[i0 + k] = (q[k] * bc1p) * den;
+            }
+        }
+    }
+    for (size_t i = 0; i < n; ++i) {
+        oracle_elem e = adamw_element(p[i], g[i], mprev[i], vprev[i], s);
+        p[i] = e.p1;
+        m1[i] = e.m1;
+        v1[i] = e.v1;
+        bad += (unsigned long long)elem_nonfinite(&e);
+    }
+
+    /* 2. second moment: 1Q per block, or FP32 */
+    for (size_t b = 0; b < nb; ++b) {
+        size_t i0 = b * T_BLOCK, len = i0 + T_BLOCK < n ? T_BLOCK : n - i0;
+        if (!compress_v) {
+            for (size_t i = i0; i < i0 + len; ++i) { v_fp32[i] = v1[i]; vp[i] = v1[i]; }
+            continue;
+        }
+        uint8_t idx[T_BLOCK];
+        oracle_q1_block(v1 + i0, len, bits, u1 + i0, idx, v_ends + 2 * b, vp + i0);
+        for (size_t k = 0; k < len; ++k) put_bits(v_index, i0 + k, bits, idx[k]);
+    }
+
+    /* 3. first moment: UState per 64-value group, or FP32 */
+    for (size_t gi = 0; gi < ng; ++gi) {
+        size_t i0 = gi * T_GROUP, len = i0 + T_GROUP < n ? T_GROUP : n - i0;
+        if (!compress_m) {
+            for (size_t i = i0; i < i0 + len; ++i) m_fp32[i] = m1[i];
+            continue;
+        }
+        float q[T_GROUP];
+        for (size_t k = 0; k < len; ++k) {
+            float den = sqrtf(vp[i0 + k] / bc2) + eps;
+            q[k] = (m1[i0 + k] / bc1) / den;
+        }
+        uint8_t codes[T_GROUP];
+        oracle_ustate_group(q, len, s_enc, up + i0 / 2, codes, m_means + gi, r2 + i0);
+        for (size_t k = 0; k < len; ++k) put_bits(m_codes, i0 + k, 2, codes[k]);
+    }
+
+    /* 4. scale rotation: s_dec <- s_enc, s_enc <- factor * residual RMS */
+    if (compress_m) {
+        double total = n ? pairwise_sum(r2, padded) : 0.0;
+        double rms = n ? sqrt(total / (double)n) : 0.0;
+        scal[0] = s_enc;
+        scal[1] = (float)(factor * rms);
+        scal[2] = 0.0f;
+    }
+    free(r2); free(m1); free(v1); free(vp); free(u1); free(up); free(mprev); free(vprev);
+    return bad;
 }

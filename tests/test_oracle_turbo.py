@@ -1,0 +1,266 @@
+"""Pins of the oracle's TurboAdam state (UState first moment, 1Q second
+moment) against what the page prints and what mathematics and independent
+libraries fix: numpy's Philox4x64-10, numpy's binary16 and exp2, torch's
+bfloat16 cast, math.fsum, the plain FP32 AdamW oracle (the uncompressed
+identity), closed forms, and the unbiasedness of stochastic rounding over a
+fine grid of draws.
+
+The page leaves the code levels, the endpoint rule, the scale rule and the
+hash unprinted; those readings are parity unpinned (the tests below pin the
+oracle to them, not them to the page)."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FACTS = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_facts.json")))["turboadam_state"]
+
+
+def _numpy_philox(counter, key):
+    # numpy's Philox advances its 256-bit counter before each block
+    c = [int(x) for x in counter]
+    i = 0
+    while True:                          # subtract one, little-endian, with borrow
+        if c[i] > 0:
+            c[i] -= 1
+            break
+        c[i] = (1 << 64) - 1
+        i += 1
+    return np.random.Philox(counter=np.array(c, np.uint64), key=np.array([int(k) for k in key], np.uint64)).random_raw(4)
+
+
+@pytest.mark.parametrize("counter,key", [
+    ([1, 0, 0, 0], [0, 0]),
+    ([7, 3, 0, 0], [0x12345678, 0]),
+    ([123456789, 42, 0, 0], [0x12345678, 290]),
+    ([0, 5, 0, 0], [0xFFFFFFFFFFFFFFFF, 0xFFFFFFFFFFFFFFFF]),
+    ([0xFFFFFFFFFFFFFFFF, 0xFFFFFFFFFFFFFFFF, 1, 0], [3, 4]),
+])
+def test_philox_matches_numpy(oracle_mod, counter, key):
+    assert np.array_equal(oracle.philox4x64(counter, key), _numpy_philox(counter, key))
+
+
+def test_state_ledger_matches_page(oracle_mod):
+    n = FACTS["values"]
+    ustate = oracle.turbo_state_bytes(1, 0, 4, n) - 4 * n
+    oneq = oracle.turbo_state_bytes(0, 1, 4, n) - 4 * n
+    total = oracle.turbo_state_bytes(1, 1, 4, n)
+    assert (ustate, oneq, total) == (FACTS["ustate_bytes"], FACTS["oneq_bytes"], FACTS["total_bytes"])
+    assert round(total * 8 / n, 6) == FACTS["bits_per_value"]
+    assert round(8 * n / total, 3) == FACTS["vs_two_fp32_moments"]
+    assert oracle.turbo_state_bytes(0, 0, 4, n) == 8 * n
+
+
+@pytest.mark.parametrize("n", [1, 129, 4096, 5003])
+def test_uncompressed_is_exact_adamw(oracle_mod, n):
+    """Both representations off: the step is the plain FP32 AdamW step, bit for bit."""
+    r = np.random.default_rng(n)
+    p0 = r.normal(0, 0.02, n).astype(np.float32)
+    pa, pb = p0.copy(), p0.copy()
+    st = oracle.TurboState(n, compress_m=False, compress_v=False)
+    m, v = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    for t in range(1, 6):
+        g = r.normal(0, 1e-3, n).astype(np.float32)
+        sc = oracle.scalars(1e-3, 0.9, 0.999, 1e-8, 0.01, t)
+        oracle.turbo_step(pa, g, st, sc, oracle.turbo_scalars(0.9, 0.999, t), t)
+        oracle.step_fp32(pb, g, m, v, sc)
+        assert np.array_equal(pa.view(np.uint32), pb.view(np.uint32))
+        assert np.array_equal(st.m_fp32.view(np.uint32), m.view(np.uint32))
+        assert np.array_equal(st.v_fp32.view(np.uint32), v.view(np.uint32))
+
+
+def _f16_bits(x):
+    return int(np.array([x], np.float16).view(np.uint16)[0])
+
+
+def test_q1_endpoints_and_levels(oracle_mod):
+    r = np.random.default_rng(4)
+    for bits in (2, 4, 8):
+        for _ in range(20):
+            v = (10.0 ** r.uniform(-14, 0, 128)).astype(np.float32)
+            idx, ends, dec = oracle.q1_block(v, bits, r.random(128).astype(np.float32))
+            lo, hi = (float(np.array(ends[k:k + 1]).view(np.float16)[0]) for k in (0, 1))
+            l2min, l2max = math.log2(float(v.min())), math.log2(float(v.max()))
+            # lo is the largest binary16 at or below log2(min), hi the smallest at or above log2(max)
+            assert lo <= l2min and float(np.nextafter(np.float16(lo), np.float16(np.inf))) > l2min
+            assert hi >= l2max and float(np.nextafter(np.float16(hi), np.float16(-np.inf))) < l2max
+            lev = oracle.q1_levels(ends[0], ends[1], bits)
+            L = 1 << bits
+            want = [0.0] + [float(np.float32(np.exp2(lo + (hi - lo) * (k - 1) / (L - 2)))) for k in range(1, L)]
+            assert np.array_equal(lev, np.array(want, np.float32))
+            assert lev[1] <= v.min() and lev[-1] >= v.max()
+            assert np.all(np.diff(lev[1:]) >= 0)
+            assert np.array_equal(dec, lev[idx])
+            # each value lands on one of its two bracketing levels
+            for x, k in zip(v, idx):
+                assert lev[k] == x or (k > 1 and lev[k - 1] < x < lev[k]) or (k < L - 1 and lev[k] < x < lev[k + 1])
+
+
+def test_q1_special_values(oracle_mod):
+    v = np.array([0.0, -0.0, np.nan, np.inf, 1e-3, 2e-3, 0.0, 4e-3], np.float32)
+    idx, ends, dec = oracle.q1_block(v, 4, np.full(v.size, 0.5, np.float32))
+    assert list(idx[[0, 1, 2, 6]]) == [0, 0, 0, 0] and idx[3] == 15
+    assert dec[0] == 0.0 and dec[3] == oracle.q1_levels(ends[0], ends[1], 4)[15]
+    idx, ends, dec = oracle.q1_block(np.zeros(7, np.float32), 4, np.zeros(7, np.float32))
+    assert not idx.any() and not dec.any() and not ends.any()
+    # powers of two inside an exact grid: log2 values exact, so the values are levels themselves
+    v = np.array([0.25, 1.0, 4.0, 0.5, 2.0], np.float32)
+    idx, ends, dec = oracle.q1_block(v, 2, np.full(5, 0.999, np.float32))
+    assert ends[0] == _f16_bits(-2.0) and ends[1] == _f16_bits(2.0)
+    assert list(idx[:3]) == [1, 2, 3] and np.array_equal(dec[:3], v[:3])
+
+
+def test_q1_rounding_is_unbiased(oracle_mod):
+    """Over a fine, even grid of draws the mean decoded value is the input:
+    exact up to the grid's resolution."""
+    r = np.random.default_rng(6)
+    v = (10.0 ** r.uniform(-10, -4, 100)).astype(np.float32)
+    N = 4096
+    acc = np.zeros(v.size, np.float64)
+    for j in range(N):
+        _, _, dec = oracle.q1_block(v, 4, np.full(v.size, (j + 0.5) / N, np.float32))
+        acc += dec
+    _, ends, _ = oracle.q1_block(v, 4, np.zeros(v.size, np.float32))
+    lev = oracle.q1_levels(ends[0], ends[1], 4).astype(np.float64)
+    step = np.array([np.diff(lev[1:]).max()] * v.size)
+    assert np.all(np.abs(acc / N - v) <= step / N * 2 + 1e-12 * v)
+
+
+def test_ustate_mean_codes_and_recentering(oracle_mod):
+    import torch
+    r = np.random.default_rng(8)
+    for _ in range(30):
+        n = int(r.integers(1, 65))
+        q = (r.normal(0, 1, n) * 10.0 ** r.uniform(-2, 1)).astype(np.float32)
+        s = np.float32(10.0 ** r.uniform(-2, 1))
+        u = r.random((n + 1) // 2).astype(np.float32)
+        codes, mean16, r2 = oracle.ustate_group(q, s, u)
+        exact_mean = math.fsum(float(x) for x in q) / n
+        want16 = int(torch.tensor([float(np.float32(exact_mean))]).to(torch.bfloat16).view(torch.int16).item()) & 0xFFFF
+        assert mean16 == want16
+        mean = float((np.array([mean16], np.uint32) << 16).view(np.float32)[0])
+        res = q - np.float32(mean)
+        assert np.array_equal(r2, res.astype(np.float64) ** 2)
+        lv = np.array([-1.5, -0.5, 0.5, 1.5])
+        x = np.clip(res / s, -1.5, 1.5)
+        # each code is one of the two levels around x (or x's own level)
+        for xi, c in zip(x, codes):
+            assert lv[c] == xi or abs(lv[c] - xi) < 1.0
+        dec = oracle.ustate_decode(codes, mean16, s)
+        # decoded values: mean + s * (level - mean level); their mean is the stored mean
+        lbar = lv[codes].sum() / n
+        assert np.allclose(dec, np.float32(mean) + s * (lv[codes] - lbar), rtol=0, atol=4e-7 * (abs(mean) + 2 * s))
+        assert abs(dec.astype(np.float64).mean() - mean) <= 4e-7 * (abs(mean) + 2 * s) + 1e-30
+
+
+def test_ustate_antithetic_pairs(oracle_mod):
+    """A pair of equal values with draws u and 1-u moves up by floor(2f) or ceil(2f) steps in total."""
+    r = np.random.default_rng(9)
+    for _ in range(500):
+        x = np.float32(r.uniform(-1.5, 1.5))
+        q = np.array([x, x], np.float32)
+        codes, mean16, _ = oracle.ustate_group(q, 1.0, np.array([r.random()], np.float32))
+        mean = float((np.array([mean16], np.uint32) << 16).view(np.float32)[0])
+        xr = float(np.float32(np.float32(x) - np.float32(mean)))
+        k = int(xr >= -0.5) + int(xr >= 0.5)
+        f = xr - [-1.5, -0.5, 0.5, 1.5][k]
+        ups = int(codes[0] > k) + int(codes[1] > k)
+        assert math.floor(2 * f) <= ups <= math.ceil(2 * f)
+
+
+def test_ustate_rounding_is_unbiased(oracle_mod):
+    r = np.random.default_rng(10)
+    q = r.uniform(-1.2, 1.2, 64).astype(np.float32)
+    N = 2048
+    acc = np.zeros(64)
+    for j in range(N):
+        codes, mean16, _ = oracle.ustate_group(q, 1.0, np.full(32, (j + 0.5) / N, np.float32))
+        acc += np.array([-1.5, -0.5, 0.5, 1.5])[codes]
+    mean = float((np.array([mean16], np.uint32) << 16).view(np.float32)[0])
+    x = (q - np.float32(mean)).astype(np.float64)
+    assert np.all(np.abs(acc / N - x) <= 2.0 / N)
+
+
+def test_scale_rotation_and_empty_first_step(oracle_mod):
+    r = np.random.default_rng(12)
+    n = 3000
+    p = r.normal(0, 0.02, n).astype(np.float32)
+    st = oracle.TurboState(n)
+    g = r.normal(0, 1e-3, n).astype(np.float32)
+    oracle.turbo_step(p, g, st, oracle.scalars(1e-3, 0.9, 0.999, 1e-8, 0.0, 1), oracle.turbo_scalars(0.9, 0.999, 1), 1)
+    s1 = float(st.scal[1])
+    assert st.scal[0] == 0.0 and s1 > 0 and st.scal[2] == 0.0
+    # at step 1 the update is g / (|g| + eps) scaled by lr: the first-moment state is irrelevant
+    g2 = r.normal(0, 1e-3, n).astype(np.float32)
+    oracle.turbo_step(p, g2, st, oracle.scalars(1e-3, 0.9, 0.999, 1e-8, 0.0, 2), oracle.turbo_scalars(0.9, 0.999, 2), 2)
+    assert st.scal[0] == np.float32(s1)
+
+
+def test_rms_sum_is_a_pairwise_double_tree(oracle_mod):
+    """The encode scale is 1.1 * sqrt(sum r^2 / n) with the residuals of the
+    groups: the tree sum agrees with the exact (fsum) sum to double rounding."""
+    r = np.random.default_rng(13)
+    n = 1000
+    p = r.normal(0, 0.02, n).astype(np.float32)
+    st = oracle.TurboState(n, compress_v=False)
+    g = r.normal(0, 1e-3, n).astype(np.float32)
+    pc = p.copy()
+    oracle.turbo_step(pc, g, st, oracle.scalars(1e-3, 0.9, 0.999, 1e-8, 0.01, 1), oracle.turbo_scalars(0.9, 0.999, 1), 1)
+    # rebuild q and the residuals from the FP32 moments of this step
+    m = (np.float32(0.1) * g).astype(np.float32)
+    v = (np.float32(0.001) * g * g).astype(np.float32)
+    sc = oracle.scalars(1e-3, 0.9, 0.999, 1e-8, 0.01, 1)
+    q = ((m / np.float32(0.1)) / (np.sqrt(v / sc[4]) + sc[7])).astype(np.float32)
+    r2 = []
+    for gi in range(0, n, 64):
+        _, _, rr = oracle.ustate_group(q[gi:gi + 64], 0.0, np.zeros(32, np.float32))
+        r2.extend(rr.tolist())
+    want = np.float32(1.1 * math.sqrt(math.fsum(r2) / n))
+    assert abs(int(np.float32(st.scal[1]).view(np.int32)) - int(want.view(np.int32))) <= 1
+
+
+def test_tracks_fp32_adamw(oracle_mod):
+    """Twenty compressed steps against plain AdamW on the same gradients.  With
+    1Q alone the trajectory stays close element by element; with UState the
+    2-bit stochastic codes add per-element noise but the mean movement is
+    AdamW's (the page likewise names UState as the source of the remaining
+    gap, and 1Q alone as within a fraction of a percent of AdamW)."""
+    n = 20000
+    p0 = np.random.default_rng(14).normal(0, 0.02, n).astype(np.float32)
+    res = {}
+    for name, cm, cv in (("1q", False, True), ("both", True, True)):
+        pt, pf = p0.copy(), p0.copy()
+        st = oracle.TurboState(n, compress_m=cm, compress_v=cv)
+        m, v = np.zeros(n, np.float32), np.zeros(n, np.float32)
+        r = np.random.default_rng(5)
+        for t in range(1, 21):
+            g = (r.normal(0, 1, n) * 1e-3 + 0.3e-3).astype(np.float32)
+            sc = oracle.scalars(1e-3, 0.9, 0.999, 1e-8, 0.01, t)
+            assert oracle.turbo_step(pt, g, st, sc, oracle.turbo_scalars(0.9, 0.999, t), t) == 0
+            oracle.step_fp32(pf, g, m, v, sc)
+        dt, df = (pt - p0).astype(np.float64), (pf - p0).astype(np.float64)
+        res[name] = (abs(dt.mean() - df.mean()) / abs(df.mean()), np.corrcoef(dt, df)[0, 1],
+                     np.abs(dt - df).mean() / np.abs(df).mean())
+    assert res["1q"][0] < 0.03 and res["1q"][1] > 0.98 and res["1q"][2] < 0.12, res
+    assert res["both"][0] < 0.06 and res["both"][1] > 0.6, res
+
+
+def test_deterministic_and_counter_driven(oracle_mod):
+    n = 777
+    r = np.random.default_rng(15)
+    p = r.normal(0, 0.02, n).astype(np.float32)
+    g = r.normal(0, 1e-3, n).astype(np.float32)
+    outs = []
+    for seed, tid in ((1, 0), (1, 0), (2, 0), (1, 3)):
+        st = oracle.TurboState(n)
+        pc = p.copy()
+        oracle.turbo_step(pc, g, st, oracle.scalars(1e-3, 0.9, 0.999, 1e-8, 0.01, 1),
+                          oracle.turbo_scalars(0.9, 0.999, 1), 1, tensor_id=tid, seed=seed)
+        outs.append(st.v_index.copy())
+    assert np.array_equal(outs[0], outs[1])
+    assert not np.array_equal(outs[0], outs[2]) and not np.array_equal(outs[0], outs[3])
