@@ -61,6 +61,17 @@ class BlockwiseState(ctypes.Structure):
                 ("p_out_bf16", ctypes.c_void_p)]
 
 
+class TurboStateDesc(ctypes.Structure):
+    _fields_ = [("compress_m", ctypes.c_int), ("compress_v", ctypes.c_int), ("tensor_id", ctypes.c_uint32),
+                ("m_codes", ctypes.c_void_p), ("m_means", ctypes.c_void_p), ("m_fp32", ctypes.c_void_p),
+                ("v_index", ctypes.c_void_p), ("v_ends", ctypes.c_void_p), ("v_fp32", ctypes.c_void_p),
+                ("scalars", ctypes.c_void_p)]
+
+
+class TurboConfig(ctypes.Structure):
+    _fields_ = [("v_bits", ctypes.c_int), ("m_step_factor", ctypes.c_double), ("seed", ctypes.c_ulonglong)]
+
+
 class Format(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int), ("lanes", ctypes.c_int),
                 ("m_sign_bits", ctypes.c_int), ("m_exp_bits", ctypes.c_int),
@@ -75,7 +86,8 @@ class Format(ctypes.Structure):
 
 EXPORTS = ("pa_step", "pa_step_list", "pa_step_typed", "pa_step_list_typed", "pa_state_bytes",
            "pa_format_info", "pa_status_string", "pa_last_hip_error", "pa_release_plans", "pa_debug_codec",
-           "pa_debug_sqrt", "pa_grad_stats_list")
+           "pa_debug_sqrt", "pa_grad_stats_list", "pa_turbo_state_bytes", "pa_turbo_workspace_bytes",
+           "pa_turbo_step_list")
 
 PA_DT_F32, PA_DT_BF16, PA_DT_F16 = 0, 1, 2
 
@@ -120,6 +132,14 @@ def lib():
     L.pa_grad_stats_list.argtypes = [ctypes.c_int, sz, ctypes.POINTER(vp), ctypes.POINTER(sz), ctypes.c_double,
                                      vp, vp, vp, vp]
     L.pa_grad_stats_list.restype = ctypes.c_int
+    L.pa_turbo_state_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, sz]
+    L.pa_turbo_state_bytes.restype = sz
+    L.pa_turbo_workspace_bytes.argtypes = [sz, ctypes.POINTER(TurboStateDesc), ctypes.POINTER(sz)]
+    L.pa_turbo_workspace_bytes.restype = sz
+    L.pa_turbo_step_list.argtypes = [sz, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(TurboStateDesc),
+                                     ctypes.POINTER(sz), ctypes.POINTER(Hyper), ctypes.POINTER(TurboConfig),
+                                     ctypes.c_longlong, vp, sz, vp]
+    L.pa_turbo_step_list.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -388,3 +408,81 @@ def pa_debug_sqrt(inp, out, stream=None):
     if inp.numel() != out.numel():
         raise ValueError("input and output sizes differ")
     _check(lib().pa_debug_sqrt(_ptr(inp), _ptr(out), inp.numel(), _stream(stream)))
+
+
+# ---------------------------------------------------------------- TurboAdam
+
+class TurboState:
+    """Device buffers of one tensor's TurboAdam state, zero-filled (the empty
+    state): UState (compress_m) or an FP32 first moment, 1Q (compress_v) or
+    an FP32 second moment (sizes as in include/pa.h)."""
+
+    def __init__(self, n, device, compress_m=True, compress_v=True, v_bits=4, tensor_id=0):
+        import torch
+        z = lambda k, dt: torch.zeros(k, dtype=dt, device=device)
+        self.n, self.compress_m, self.compress_v, self.v_bits = int(n), bool(compress_m), bool(compress_v), v_bits
+        self.tensor_id = int(tensor_id)
+        self.m_codes = z(4 * ((n + 15) // 16), torch.uint8) if compress_m else None
+        self.m_means = z((n + 63) // 64, torch.int16) if compress_m else None
+        self.scalars = z(3, torch.float32) if compress_m else None
+        self.m_fp32 = None if compress_m else z(n, torch.float32)
+        self.v_index = z(4 * ((n * v_bits + 31) // 32), torch.uint8) if compress_v else None
+        self.v_ends = z(2 * ((n + 127) // 128), torch.int16) if compress_v else None
+        self.v_fp32 = None if compress_v else z(n, torch.float32)
+
+    def desc(self):
+        return TurboStateDesc(int(self.compress_m), int(self.compress_v), self.tensor_id, _ptr(self.m_codes),
+                              _ptr(self.m_means), _ptr(self.m_fp32), _ptr(self.v_index), _ptr(self.v_ends),
+                              _ptr(self.v_fp32), _ptr(self.scalars))
+
+    def tensors(self):
+        return [t for t in (self.m_codes, self.m_means, self.scalars, self.m_fp32, self.v_index, self.v_ends,
+                            self.v_fp32) if t is not None]
+
+    def nbytes(self):
+        return sum(t.numel() * t.element_size() for t in self.tensors())
+
+
+def pa_turbo_state_bytes(compress_m, compress_v, v_bits, n):
+    return int(lib().pa_turbo_state_bytes(int(compress_m), int(compress_v), int(v_bits), int(n)))
+
+
+class TurboList:
+    """A fixed list of FP32 parameters, gradients and TurboState objects,
+    validated and marshalled once; ``step(hyper, t)`` is one
+    pa_turbo_step_list call.  Owns its device workspace."""
+
+    def __init__(self, params, grads, states, v_bits=4, m_step_factor=1.1, seed=0x12345678):
+        import torch
+        k = len(params)
+        if len(grads) != k or len(states) != k:
+            raise ValueError("params, grads and states must have the same length")
+        self._keep = [list(params), list(grads), list(states)]
+        self._P = (ctypes.c_void_p * k)()
+        self._G = (ctypes.c_void_p * k)()
+        self._S = (TurboStateDesc * k)()
+        self._N = (ctypes.c_size_t * k)()
+        for i in range(k):
+            p, g, st = params[i], grads[i], states[i]
+            _tensor_ok(p, "params")
+            _tensor_ok(g, "grads")
+            if p.dtype != torch.float32 or g.dtype != torch.float32:
+                raise TypeError("the TurboAdam step takes float32 parameters and gradients")
+            if g.numel() != p.numel() or st.n != p.numel() or st.v_bits != v_bits:
+                raise ValueError("params, grads and states disagree in size or v_bits")
+            self._P[i], self._G[i] = _ptr(p), _ptr(g)
+            self._S[i] = st.desc()
+            self._N[i] = p.numel()
+        self.count = k
+        self.config = TurboConfig(int(v_bits), float(m_step_factor), int(seed))
+        L = lib()
+        wsb = int(L.pa_turbo_workspace_bytes(k, self._S, self._N)) if k else 0
+        dev = params[0].device if k else "cuda:0"
+        self.workspace = torch.empty(max(wsb // 8, 1), dtype=torch.float64, device=dev)
+        self._wsb = wsb
+        self._fn = L.pa_turbo_step_list
+
+    def step(self, hyper, step, stream=None):
+        h = _hyper(hyper)
+        _check(self._fn(self.count, self._P, self._G, self._S, self._N, ctypes.byref(h), ctypes.byref(self.config),
+                        int(step), _ptr(self.workspace), self._wsb, _stream(stream)))

@@ -18,6 +18,7 @@
 
 #include "../../include/pa.h"
 #include "kernels.hpp"
+#include "turbo.hpp"
 
 namespace {
 
@@ -71,6 +72,7 @@ struct DeviceInfo {
   int blocks_per_cu = 0;      // elementwise kernels
   int bw_blocks_per_cu = 0;   // blockwise kernel
   int stats_blocks_per_cu = 0;   // gradient pre-pass
+  int turbo_blocks_per_cu = 0;   // TurboAdam step
 };
 
 std::mutex g_dev_mu;
@@ -104,6 +106,11 @@ int device_info(int* dev_out, DeviceInfo* info) {
         &st, reinterpret_cast<const void*>(pa::grad_stats_list<pa::kF32>), pa::kThreads, 0);
     if (e != hipSuccess || st < 1) st = 4;
     d.stats_blocks_per_cu = st;
+    int tb = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &tb, reinterpret_cast<const void*>(pa::turbo_list<4, false>), pa::kThreads, 0);
+    if (e != hipSuccess || tb < 1) tb = 2;
+    d.turbo_blocks_per_cu = tb;
   }
   *dev_out = dev;
   *info = d;
@@ -425,6 +432,87 @@ hipError_t launch_stats(const Plan& pl, double max_norm, double* sumsq, unsigned
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- TurboAdam
+
+struct TurboPlan {
+  int device = -1;
+  std::vector<uintptr_t> key;
+  pa::TurboEntry* table = nullptr;          // device: entries + sentinel, then the reduce list
+  pa::TurboReduceEntry* reduce = nullptr;   // inside the same allocation
+  long long tiles = 0;
+  int nreduce = 0;
+  size_t ws_bytes = 0;
+  std::vector<Range> ranges;                // written buffers and gradients, merged
+};
+
+std::list<TurboPlan> g_turbo_plans;         // guarded by g_plan_mu, most recent first
+
+void free_turbo_plan(TurboPlan& pl) {
+  if (pl.table) {
+    int cur = 0;
+    if (hipGetDevice(&cur) == hipSuccess) {
+      if (hipSetDevice(pl.device) == hipSuccess) (void)hipFree(pl.table);
+      (void)hipSetDevice(cur);
+    }
+    pl.table = nullptr;
+  }
+}
+
+long long turbo_tiles(size_t n) { return (long long)((n + pa::kTurboTile - 1) / pa::kTurboTile); }
+
+bool valid_bits(int b) { return b == 2 || b == 4 || b == 8; }
+
+// Checks one tensor's buffers; appends the written ranges to `w` and the
+// gradient range to `r`.
+int check_turbo_tensor(const float* p, const float* g, const pa_turbo_state& st, size_t n, int bits,
+                       std::vector<Range>* w, std::vector<Range>* r) {
+  if (n == 0) return PA_OK;
+  if (p == nullptr || g == nullptr) return PA_ERR_ARG;
+  if (!aligned(p, 16) || !aligned(g, 16)) return PA_ERR_ALIGN;
+  w->push_back(range_of(p, n * 4));
+  r->push_back(range_of(g, n * 4));
+  if (st.compress_m) {
+    if (!st.m_codes || !st.m_means || !st.scalars) return PA_ERR_ARG;
+    if (!aligned(st.m_codes, 4) || !aligned(st.m_means, 2) || !aligned(st.scalars, 4)) return PA_ERR_ALIGN;
+    w->push_back(range_of(st.m_codes, 4 * ((n + 15) / 16)));
+    w->push_back(range_of(st.m_means, 2 * ((n + 63) / 64)));
+    w->push_back(range_of(st.scalars, 12));
+  } else {
+    if (!st.m_fp32) return PA_ERR_ARG;
+    if (!aligned(st.m_fp32, 16)) return PA_ERR_ALIGN;
+    w->push_back(range_of(st.m_fp32, n * 4));
+  }
+  if (st.compress_v) {
+    if (!st.v_index || !st.v_ends) return PA_ERR_ARG;
+    if (!aligned(st.v_index, 4) || !aligned(st.v_ends, 4)) return PA_ERR_ALIGN;
+    w->push_back(range_of(st.v_index, 4 * ((n * (size_t)bits + 31) / 32)));
+    w->push_back(range_of(st.v_ends, 4 * ((n + 127) / 128)));
+  } else {
+    if (!st.v_fp32) return PA_ERR_ARG;
+    if (!aligned(st.v_fp32, 16)) return PA_ERR_ALIGN;
+    w->push_back(range_of(st.v_fp32, n * 4));
+  }
+  return PA_OK;
+}
+
+template <int BITS>
+hipError_t launch_turbo(const TurboPlan& pl, const pa::Scalars& s, const pa::TurboScalars& ts, double* ws,
+                        unsigned long long* nf, double factor, hipStream_t st, const DeviceInfo& d) {
+  const long long wgs = (pl.tiles + pa::kThreads / 64 - 1) / (pa::kThreads / 64);
+  const dim3 grid((unsigned)grid_for(wgs, d, d.turbo_blocks_per_cu)), block(pa::kThreads);
+  if (nf)
+    hipLaunchKernelGGL((pa::turbo_list<BITS, true>), grid, block, 0, st, pl.table, pl.tiles, s, ts, ws, nf);
+  else
+    hipLaunchKernelGGL((pa::turbo_list<BITS, false>), grid, block, 0, st, pl.table, pl.tiles, s, ts, ws, nf);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || pl.nreduce == 0) return e;
+  // The reduce kernel checks the same skip flag: a skipped update leaves
+  // the scales as they were.
+  hipLaunchKernelGGL(pa::turbo_reduce, dim3((unsigned)pl.nreduce), dim3(pa::kThreads), 0, st, pl.reduce, ws, factor,
+                     s.skip);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 // =================================================================== C ABI
@@ -707,6 +795,169 @@ int pa_grad_stats_list(int grad_dtype, size_t count, const void* const* grads, c
   return e == hipSuccess ? PA_OK : hip_failed(e);
 }
 
+size_t pa_turbo_state_bytes(int compress_m, int compress_v, int v_bits, size_t n) {
+  if (!valid_bits(v_bits)) return 0;
+  size_t b = 0;
+  b += compress_m ? 4 * ((n + 15) / 16) + 2 * ((n + 63) / 64) + 12 : 4 * n;
+  b += compress_v ? 4 * ((n * (size_t)v_bits + 31) / 32) + 4 * ((n + 127) / 128) : 4 * n;
+  return b;
+}
+
+size_t pa_turbo_workspace_bytes(size_t count, const pa_turbo_state* states, const size_t* n) {
+  if (count == 0 || states == nullptr || n == nullptr) return 0;
+  size_t b = 0;
+  for (size_t i = 0; i < count; ++i)
+    if (states[i].compress_m && n[i] > 0) b += 8 * (size_t)turbo_tiles(n[i]);
+  return b;
+}
+
+int pa_turbo_step_list(size_t count, float* const* params, const float* const* grads, const pa_turbo_state* states,
+                       const size_t* n, const pa_hyper* hyper, const pa_turbo_config* config, long long step,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (config == nullptr || !valid_bits(config->v_bits) || !std::isfinite(config->m_step_factor) ||
+      !(config->m_step_factor > 0.0))
+    return PA_ERR_ARG;
+  pa::Scalars s;
+  int rc = make_scalars(hyper, step, &s);
+  if (rc) return rc;
+  if (count == 0) return PA_OK;
+  if (params == nullptr || grads == nullptr || states == nullptr || n == nullptr) return PA_ERR_ARG;
+  bool any_m = false;
+  for (size_t i = 0; i < count; ++i) any_m = any_m || (states[i].compress_m && n[i] > 0);
+  if (any_m && !(hyper->beta1 * hyper->beta1 < hyper->beta2)) return PA_ERR_ARG;
+  if (!aligned(workspace, 8)) return PA_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int dev;
+  DeviceInfo d;
+  rc = device_info(&dev, &d);
+  if (rc) return rc;
+
+  std::vector<uintptr_t> key;
+  key.reserve(count * 13 + 1);
+  key.push_back((uintptr_t)config->v_bits);
+  for (size_t i = 0; i < count; ++i) {
+    const pa_turbo_state& t = states[i];
+    for (const void* ptr : {(const void*)params[i], (const void*)grads[i], (const void*)t.m_codes,
+                            (const void*)t.m_means, (const void*)t.m_fp32, (const void*)t.v_index,
+                            (const void*)t.v_ends, (const void*)t.v_fp32, (const void*)t.scalars})
+      key.push_back(reinterpret_cast<uintptr_t>(ptr));
+    key.push_back((uintptr_t)n[i]);
+    key.push_back((uintptr_t)t.tensor_id);
+    key.push_back((uintptr_t)((t.compress_m ? 1 : 0) | (t.compress_v ? 2 : 0)));
+  }
+  std::lock_guard<std::mutex> lk(g_plan_mu);
+  auto it = std::find_if(g_turbo_plans.begin(), g_turbo_plans.end(),
+                         [&](const TurboPlan& p) { return p.device == dev && p.key == key; });
+  if (it == g_turbo_plans.end()) {
+    std::vector<pa::TurboEntry> host;
+    std::vector<pa::TurboReduceEntry> red;
+    std::vector<Range> written, read;
+    long long tiles = 0, ws_slots = 0;
+    for (size_t i = 0; i < count; ++i) {
+      const pa_turbo_state& t = states[i];
+      rc = check_turbo_tensor(params[i], grads[i], t, n[i], config->v_bits, &written, &read);
+      if (rc) return rc;
+      if (n[i] == 0) continue;
+      pa::TurboEntry e;
+      std::memset(&e, 0, sizeof(e));
+      e.p = params[i];
+      e.g = grads[i];
+      e.m_codes = t.compress_m ? t.m_codes : nullptr;
+      e.m_means = t.compress_m ? t.m_means : nullptr;
+      e.m_fp32 = t.compress_m ? nullptr : t.m_fp32;
+      e.v_index = t.compress_v ? t.v_index : nullptr;
+      e.v_ends = t.compress_v ? t.v_ends : nullptr;
+      e.v_fp32 = t.compress_v ? nullptr : t.v_fp32;
+      e.scal = t.compress_m ? t.scalars : nullptr;
+      e.n = (long long)n[i];
+      e.tile0 = tiles;
+      e.ws0 = t.compress_m ? ws_slots : 0;
+      e.tensor_id = t.tensor_id;
+      e.flags = (t.compress_m ? 1 : 0) | (t.compress_v ? 2 : 0);
+      const long long nt = turbo_tiles(n[i]);
+      if (t.compress_m) {
+        pa::TurboReduceEntry r{t.scalars, ws_slots, nt, (long long)n[i]};
+        red.push_back(r);
+        ws_slots += nt;
+      }
+      tiles += nt;
+      host.push_back(e);
+    }
+    {
+      std::vector<Range> w = written;
+      if (any_overlap(w)) return PA_ERR_ALIAS;
+      const std::vector<Range> wm = merged(written);
+      for (const Range& r : read)
+        if (hits_sorted(wm, r)) return PA_ERR_ALIAS;
+    }
+    if (host.empty()) return PA_OK;
+    pa::TurboEntry sentinel;
+    std::memset(&sentinel, 0, sizeof(sentinel));
+    sentinel.tile0 = tiles;
+    host.push_back(sentinel);
+    TurboPlan pl;
+    pl.device = dev;
+    pl.key = key;
+    pl.tiles = tiles;
+    pl.nreduce = (int)red.size();
+    pl.ws_bytes = 8 * (size_t)ws_slots;
+    written.insert(written.end(), read.begin(), read.end());
+    pl.ranges = merged(written);
+    const size_t tb = host.size() * sizeof(pa::TurboEntry);
+    const size_t rb = std::max<size_t>(red.size(), 1) * sizeof(pa::TurboReduceEntry);
+    hipError_t e = hipMalloc(reinterpret_cast<void**>(&pl.table), tb + rb);
+    if (e != hipSuccess) {
+      g_last_hip_error = (int)e;
+      return PA_ERR_NOMEM;
+    }
+    pl.reduce = reinterpret_cast<pa::TurboReduceEntry*>(reinterpret_cast<char*>(pl.table) + tb);
+    e = hipMemcpyAsync(pl.table, host.data(), tb, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess && !red.empty())
+      e = hipMemcpyAsync(pl.reduce, red.data(), red.size() * sizeof(pa::TurboReduceEntry), hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) {
+      (void)hipFree(pl.table);
+      return hip_failed(e);
+    }
+    g_turbo_plans.push_front(std::move(pl));
+    while (g_turbo_plans.size() > kMaxPlans) {
+      free_turbo_plan(g_turbo_plans.back());
+      g_turbo_plans.pop_back();
+    }
+    it = g_turbo_plans.begin();
+  } else if (it != g_turbo_plans.begin()) {
+    g_turbo_plans.splice(g_turbo_plans.begin(), g_turbo_plans, it);
+    it = g_turbo_plans.begin();
+  }
+  if (workspace_bytes < it->ws_bytes || (it->ws_bytes > 0 && workspace == nullptr)) return PA_ERR_ARG;
+  {
+    std::vector<Range> hr;
+    hyper_ranges(hyper, &hr);
+    if (it->ws_bytes > 0) hr.push_back(range_of(workspace, it->ws_bytes));
+    for (const Range& r : hr)
+      if (hits_sorted(it->ranges, r)) return PA_ERR_ALIAS;
+    if (any_overlap(hr)) return PA_ERR_ALIAS;
+  }
+  pa::TurboScalars ts;
+  std::memset(&ts, 0, sizeof(ts));
+  const double b1 = hyper->beta1, b2 = hyper->beta2;
+  ts.bc1 = (float)(1.0 - std::pow(b1, (double)step));
+  ts.bc1p = (float)(1.0 - std::pow(b1, (double)(step - 1)));
+  ts.bc2p = (float)(1.0 - std::pow(b2, (double)(step - 1)));
+  ts.inv_bc1 = 1.0 / (double)ts.bc1;
+  ts.inv_bc2p = step > 1 ? 1.0 / (double)ts.bc2p : 0.0;
+  ts.seed = config->seed;
+  ts.step = step;
+  hipError_t e;
+  double* ws = static_cast<double*>(workspace);
+  switch (config->v_bits) {
+    case 2: e = launch_turbo<2>(*it, s, ts, ws, hyper->nonfinite, config->m_step_factor, st, d); break;
+    case 4: e = launch_turbo<4>(*it, s, ts, ws, hyper->nonfinite, config->m_step_factor, st, d); break;
+    default: e = launch_turbo<8>(*it, s, ts, ws, hyper->nonfinite, config->m_step_factor, st, d); break;
+  }
+  return e == hipSuccess ? PA_OK : hip_failed(e);
+}
+
 size_t pa_state_bytes(int mode, size_t n) {
   switch (mode) {
     case PA_FP32: return 8 * n;
@@ -780,6 +1031,8 @@ void pa_release_plans(void) {
   std::lock_guard<std::mutex> lk(g_plan_mu);
   for (Plan& p : g_plans) free_plan(p);
   g_plans.clear();
+  for (TurboPlan& p : g_turbo_plans) free_turbo_plan(p);
+  g_turbo_plans.clear();
 }
 
 int pa_debug_codec(int lane, int dir, const void* in, void* out, size_t n, void* stream) {

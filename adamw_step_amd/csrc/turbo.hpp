@@ -1,0 +1,488 @@
+// turbo.hpp -- gfx950 kernels of the TurboAdam compressed-state step.
+//
+// TurboAdam package page, "How it works" (UState, 1Q, "The AdamW update
+// remains AdamW", "Fused CUDA path"): the update runs in FP32 on transient
+// moments; the first moment persists as UState (normalised update units,
+// 2-bit codes, one bf16 mean per 64 values, a lagged tensor scale) and the
+// second as 1Q (a log grid per 128-value block between two fp16 endpoints).
+// The page prints neither code nor constants for the grid, the code levels,
+// the scale rule or the rounding hash; the readings implemented here:
+//
+//  * 1Q: index 0 is zero; index k >= 1 decodes to exp2 of the k-th of L-1
+//    evenly spaced points from lo to hi (in double), rounded once to
+//    binary32.  lo and hi are log2 of the block's smallest positive and
+//    largest finite value, rounded to binary16 down and up.  A value goes to
+//    the largest level at or below it, or the next one with probability
+//    equal to its position between the two.
+//  * UState: codes 0..3 are -1.5, -0.5, 0.5, 1.5 times the scale around the
+//    group's bf16 mean; decoding subtracts the group's mean level, so the
+//    decoded mean is the stored one.  Pairs of values use draws u and 1 - u.
+//    The scale for the next encode is 1.1 x the RMS of this step's
+//    residuals; decoding uses the scale the codes were written with.
+//  * Draws: Philox4x64-10 with key (seed, tensor id) and counter
+//    (value index / 4, step, 0, 0); the top 24 bits of word k serve the 1Q
+//    rounding of value 4j + k, bits 8..31 of words 0 and 1 serve the two
+//    UState pairs.
+//  * Sums (group means, the residual sum of squares) are perfect pairwise
+//    trees in double over the values in index order, padded with zeros, so
+//    their results do not depend on the launch.
+//
+// Work split: one wavefront per 256-value tile; lane l holds values 4l..4l+3,
+// lanes 0-31 one 1Q block and lanes 32-63 the next, 16 lanes one UState
+// group.  Every reduction is a butterfly of shuffles inside the wavefront;
+// the per-block level tables sit in a wavefront-private slice of LDS, so no
+// workgroup barrier is ever needed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.hpp"
+
+#pragma clang fp contract(off)
+
+namespace pa {
+
+constexpr int kTurboTile = 256;     // values per wavefront tile
+constexpr int kTurboBlock = 128;    // 1Q block
+constexpr int kTurboGroup = 64;     // UState mean group
+
+struct TurboEntry {
+  float* p;
+  const float* g;
+  uint8_t* m_codes;    // 2-bit codes, 4 per byte (compress_m)
+  uint16_t* m_means;   // bf16 per 64 (compress_m)
+  float* m_fp32;       // (!compress_m)
+  uint8_t* v_index;    // bits per value, little-endian (compress_v)
+  uint16_t* v_ends;    // fp16 lo, hi per 128 (compress_v)
+  float* v_fp32;       // (!compress_v)
+  float* scal;         // s_dec, s_enc, acc (compress_m)
+  long long n;
+  long long tile0;     // first global tile of this tensor
+  long long ws0;       // first workspace slot (one double per tile)
+  uint32_t tensor_id;
+  int flags;           // bit 0: compress_m, bit 1: compress_v
+};
+
+struct TurboScalars {
+  float bc1, bc1p, bc2p, pad_;
+  double inv_bc1, inv_bc2p;       // 1/bc1 and 1/bc2_{t-1} rounded to double
+  unsigned long long seed;
+  long long step;
+};
+
+__device__ __forceinline__ void philox4x64_10(uint64_t c0, uint64_t c1, uint64_t k0, uint64_t k1, uint64_t w[4]) {
+  uint64_t x0 = c0, x1 = c1, x2 = 0, x3 = 0;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B97F4A7C15ull;
+      k1 += 0xBB67AE8584CAA73Bull;
+    }
+    const uint64_t hi0 = __umul64hi(0xD2E7470EE14C6C93ull, x0), lo0 = 0xD2E7470EE14C6C93ull * x0;
+    const uint64_t hi1 = __umul64hi(0xCA5A826395121157ull, x2), lo1 = 0xCA5A826395121157ull * x2;
+    const uint64_t n0 = hi1 ^ x1 ^ k0, n2 = hi0 ^ x3 ^ k1;
+    x0 = n0;
+    x1 = lo1;
+    x2 = n2;
+    x3 = lo0;
+  }
+  w[0] = x0;
+  w[1] = x1;
+  w[2] = x2;
+  w[3] = x3;
+}
+
+// x / d for a uniform binary32 d with rd = RN64(1/d): the correctly rounded
+// quotient (see div_bc2 in kernels.hpp for the argument).
+__device__ __forceinline__ float div_uniform(float x, double rd) { return (float)((double)x * rd); }
+
+// binary16 bit pattern of x rounded toward -Inf (up = false) or +Inf (up =
+// true); |x| is far inside the binary16 range here (a log2 of a float).
+__device__ __forceinline__ uint32_t f16_directed_dev(double x, bool up) {
+  const bool neg = x < 0.0;
+  const double a = neg ? -x : x;
+  // round the magnitude toward zero when the direction points to zero
+  const bool mag_up = neg ? !up : up;
+  uint32_t bits;
+  if (a < 0x1p-14) {                                    // subnormal range: multiples of 2^-24
+    const double q = a * 0x1p24;
+    const double r = mag_up ? __builtin_ceil(q) : __builtin_floor(q);
+    bits = (uint32_t)r;                                 // r <= 1024: 1024 is the smallest normal
+  } else {
+    int e;
+    const double f = __builtin_frexp(a, &e);           // a = f * 2^e, f in [0.5, 1)
+    double q = __builtin_ldexp(f, 11);                  // in [1024, 2048)
+    q = mag_up ? __builtin_ceil(q) : __builtin_floor(q);
+    int be = e - 1 + 15;                                // biased exponent of 2^(e-1)
+    if (q >= 2048.0) {
+      q = 1024.0;
+      be += 1;
+    }
+    bits = ((uint32_t)be << 10) | ((uint32_t)q - 1024u);
+  }
+  if (bits == 0) return 0u;
+  return (neg ? 0x8000u : 0u) | bits;
+}
+
+__device__ __forceinline__ double f16_to_double(uint32_t h) { return (double)f16_decode(h); }
+
+// Level k of a 1Q block, in double then rounded once to binary32.
+__device__ __forceinline__ float q1_level(double lo, double hi, int k, int L) {
+  if (k == 0) return 0.0f;
+  const double x = lo + ((hi - lo) * (double)(k - 1)) / (double)(L - 2);
+  return (float)exp2(x);
+}
+
+template <int BITS>
+__device__ __forceinline__ void build_levels(float* lev, uint32_t ends, int lane_in_half) {
+  constexpr int L = 1 << BITS;
+  const double lo = f16_to_double(ends & 0xFFFFu), hi = f16_to_double(ends >> 16);
+  for (int k = lane_in_half; k < L; k += 32) lev[k] = q1_level(lo, hi, k, L);
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int W>
+__device__ __forceinline__ double butterfly_sum(double x) {
+#pragma unroll
+  for (int off = 1; off < W; off <<= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+template <int W>
+__device__ __forceinline__ int butterfly_isum(int x) {
+#pragma unroll
+  for (int off = 1; off < W; off <<= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+template <int W>
+__device__ __forceinline__ float butterfly_min(float x) {
+#pragma unroll
+  for (int off = 1; off < W; off <<= 1) x = fminf(x, __shfl_xor(x, off, 64));
+  return x;
+}
+
+template <int W>
+__device__ __forceinline__ float butterfly_max(float x) {
+#pragma unroll
+  for (int off = 1; off < W; off <<= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+  return x;
+}
+
+__device__ __forceinline__ float ustate_level(uint32_t c) { return (float)(int)(2 * c) * 0.5f - 1.5f; }
+
+template <int BITS>
+__device__ __forceinline__ uint32_t load_index4(const uint8_t* base, long long lane_word) {
+  if constexpr (BITS == 2) return base[lane_word];
+  else if constexpr (BITS == 4) return reinterpret_cast<const uint16_t*>(base)[lane_word];
+  else return reinterpret_cast<const uint32_t*>(base)[lane_word];
+}
+
+template <int BITS>
+__device__ __forceinline__ void store_index4(uint8_t* base, long long lane_word, uint32_t v) {
+  if constexpr (BITS == 2) base[lane_word] = (uint8_t)v;
+  else if constexpr (BITS == 4) reinterpret_cast<uint16_t*>(base)[lane_word] = (uint16_t)v;
+  else reinterpret_cast<uint32_t*>(base)[lane_word] = v;
+}
+
+// One 256-value tile of one tensor, by one wavefront.
+template <int BITS>
+__device__ __forceinline__ void turbo_tile(const TurboEntry& e, long long tile, const Scalars& s, const TurboScalars& ts,
+                                           float* lev_half, double* ws, uint32_t& bad) {
+  constexpr int L = 1 << BITS;
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5, lane_in_half = lane & 31;
+  const bool cm = e.flags & 1, cv = e.flags & 2;
+  const long long base = tile * kTurboTile;
+  const long long i0 = base + 4 * lane;                 // this lane's first value
+  const long long n = e.n;
+  const bool full = base + kTurboTile <= n;
+  bool valid[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) valid[k] = i0 + k < n;
+  const long long blk = (base >> 7) + half;              // 1Q block of this lane
+  const bool blk_exists = blk * kTurboBlock < n;
+  const long long grp = i0 >> 6;                         // UState group of this lane
+  const long long glen_ll = n - (grp << 6);
+  const int glen = glen_ll >= kTurboGroup ? kTurboGroup : (int)glen_ll;
+
+  // ---- loads
+  float p[4], g[4], mprev[4] = {0.f, 0.f, 0.f, 0.f}, vprev[4] = {0.f, 0.f, 0.f, 0.f};
+  if (full) {
+    const f32x4 pv = stream_load(reinterpret_cast<const f32x4*>(e.p + i0));
+    const f32x4 gv = stream_load(reinterpret_cast<const f32x4*>(e.g + i0));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      p[k] = pv[k];
+      g[k] = gv[k];
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      p[k] = valid[k] ? e.p[i0 + k] : 0.0f;
+      g[k] = valid[k] ? e.g[i0 + k] : 0.0f;
+    }
+  }
+  const float s_dec = cm ? e.scal[0] : 0.0f, s_enc = cm ? e.scal[1] : 0.0f;
+  uint32_t mcodes = 0;
+
+  // ---- decode the prior moments (the state is empty at step 1)
+  if (ts.step > 1) {
+    if (cv) {
+      const uint32_t ends = blk_exists ? *reinterpret_cast<const uint32_t*>(e.v_ends + 2 * blk) : 0u;
+      build_levels<BITS>(lev_half, ends, lane_in_half);
+      wave_lds_sync();
+      const uint32_t idx4 = valid[0] ? load_index4<BITS>(e.v_index, i0 >> 2) : 0u;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) vprev[k] = valid[k] ? lev_half[(idx4 >> (BITS * k)) & (L - 1)] : 0.0f;
+      wave_lds_sync();
+    } else if (full) {
+      const f32x4 vv = *reinterpret_cast<const f32x4*>(e.v_fp32 + i0);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) vprev[k] = vv[k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) vprev[k] = valid[k] ? e.v_fp32[i0 + k] : 0.0f;
+    }
+    if (cm) {
+      mcodes = valid[0] ? e.m_codes[i0 >> 2] : 0u;
+      int s2 = 0;                                        // sum of 2 * level over this lane's values
+#pragma unroll
+      for (int k = 0; k < 4; ++k) s2 += valid[k] ? (int)(2 * ((mcodes >> (2 * k)) & 3u)) - 3 : 0;
+      s2 = butterfly_isum<16>(s2);
+      const float lbar = (float)((double)s2 * 0.5 / (double)glen);
+      const float mean = valid[0] ? __uint_as_float((uint32_t)e.m_means[grp] << 16) : 0.0f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float q = mean + s_dec * (ustate_level((mcodes >> (2 * k)) & 3u) - lbar);
+        const float den = sqrt_rn(div_uniform(vprev[k], ts.inv_bc2p)) + s.eps;
+        mprev[k] = valid[k] ? (q * ts.bc1p) * den : 0.0f;
+      }
+    } else if (full) {
+      const f32x4 mv = *reinterpret_cast<const f32x4*>(e.m_fp32 + i0);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) mprev[k] = mv[k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) mprev[k] = valid[k] ? e.m_fp32[i0 + k] : 0.0f;
+    }
+  }
+
+  // ---- the update with the FP32 moments
+  float m1[4], v1[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float p1;
+    adamw(p[k], g[k] * s.gmul, s.beta1 * mprev[k], vprev[k], s, p1, m1[k], v1[k]);
+    if (valid[k]) bad += nonfinite3(p1, m1[k], v1[k]);
+    p[k] = p1;
+  }
+  if (full) {
+    f32x4 pv;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) pv[k] = p[k];
+    stream_store(reinterpret_cast<f32x4*>(e.p + i0), pv);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (valid[k]) e.p[i0 + k] = p[k];
+  }
+
+  // ---- draws of this lane's four values
+  uint64_t w[4];
+  philox4x64_10((uint64_t)(i0 >> 2), (uint64_t)ts.step, ts.seed, (uint64_t)e.tensor_id, w);
+
+  // ---- second moment: 1Q per block, or FP32
+  float vp[4];
+  if (cv) {
+    float lo_c = __builtin_inff(), hi_c = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float v = v1[k];
+      const bool pos = valid[k] && v > 0.0f && __builtin_isfinite(v);
+      lo_c = pos ? fminf(lo_c, v) : lo_c;
+      hi_c = pos ? fmaxf(hi_c, v) : hi_c;
+    }
+    const float vmin = butterfly_min<32>(lo_c), vmax = butterfly_max<32>(hi_c);
+    uint32_t ends = 0;
+    if (vmax > 0.0f) {
+      ends = f16_directed_dev(log2((double)vmin), false) |
+             (f16_directed_dev(log2((double)vmax), true) << 16);
+    }
+    build_levels<BITS>(lev_half, ends, lane_in_half);
+    wave_lds_sync();
+    const float lo = f16_decode(ends & 0xFFFFu), hi = f16_decode(ends >> 16);
+    uint32_t idx4 = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float v = v1[k];
+      uint32_t idx;
+      if (!(v > 0.0f)) {
+        idx = 0;
+      } else if (__builtin_isinf(v)) {
+        idx = L - 1;
+      } else {
+        // estimate from an approximate log2, then step to the bracketing level
+        int kk = 1;
+        if (hi > lo) {
+          const float t = (__log2f(v) - lo) * (float)(L - 2) / (hi - lo);
+          kk = t < 0.0f ? 1 : (t > (float)(L - 2) ? L - 1 : (int)t + 1);
+        }
+        for (int it = 0; it < L && kk + 1 < L && lev_half[kk + 1] <= v; ++it) ++kk;
+        for (int it = 0; it < L && kk > 1 && lev_half[kk] > v; ++it) --kk;
+        idx = kk;
+        if (kk < L - 1 && v > lev_half[kk]) {
+          const float f = __fdiv_rn(v - lev_half[kk], lev_half[kk + 1] - lev_half[kk]);
+          const float u = (float)(w[k] >> 40) * 0x1p-24f;
+          if (u < f) idx = kk + 1;
+        }
+      }
+      vp[k] = lev_half[idx];
+      idx4 |= valid[k] ? idx << (BITS * k) : 0u;           // padding past the end stays zero
+    }
+    wave_lds_sync();
+    if (valid[0]) store_index4<BITS>(e.v_index, i0 >> 2, idx4);
+    if (lane_in_half == 0 && blk_exists) *reinterpret_cast<uint32_t*>(e.v_ends + 2 * blk) = ends;
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) vp[k] = v1[k];
+    if (full) {
+      f32x4 vv;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) vv[k] = v1[k];
+      *reinterpret_cast<f32x4*>(e.v_fp32 + i0) = vv;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (valid[k]) e.v_fp32[i0 + k] = v1[k];
+    }
+  }
+
+  // ---- first moment: UState per group, or FP32
+  if (cm) {
+    float q[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float den = sqrt_rn(div_bc2(vp[k], s)) + s.eps;
+      q[k] = valid[k] ? __fdiv_rn(div_uniform(m1[k], ts.inv_bc1), den) : 0.0f;
+    }
+    const double gsum = butterfly_sum<16>(((double)q[0] + (double)q[1]) + ((double)q[2] + (double)q[3]));
+    const uint32_t mean16 = bf16_encode((float)(gsum / (double)glen));
+    const float mean = __uint_as_float(mean16 << 16);
+    uint32_t codes = 0;
+    double r2[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float r = q[k] - mean;
+      r2[k] = valid[k] ? (double)r * (double)r : 0.0;
+      float x = s_enc > 0.0f ? __fdiv_rn(r, s_enc) : 0.0f;
+      x = x > 1.5f ? 1.5f : x;
+      x = x < -1.5f ? -1.5f : x;
+      float u = (float)((w[k >> 1] & 0xFFFFFFFFull) >> 8) * 0x1p-24f;
+      if (k & 1) u = 1.0f - u;
+      const uint32_t kk = (uint32_t)(x >= -0.5f) + (uint32_t)(x >= 0.5f);
+      uint32_t code = kk;
+      if (x >= 1.5f) code = 3;
+      else if (u < x - ustate_level(kk)) code = kk + 1;
+      codes |= valid[k] ? code << (2 * k) : 0u;
+    }
+    if (valid[0]) e.m_codes[i0 >> 2] = (uint8_t)codes;
+    if ((lane & 15) == 0 && valid[0]) e.m_means[grp] = (uint16_t)mean16;
+    const double tsum = butterfly_sum<64>((r2[0] + r2[1]) + (r2[2] + r2[3]));
+    if (lane == 0) ws[e.ws0 + tile] = tsum;
+  } else if (full) {
+    f32x4 mv;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) mv[k] = m1[k];
+    *reinterpret_cast<f32x4*>(e.m_fp32 + i0) = mv;
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (valid[k]) e.m_fp32[i0 + k] = m1[k];
+  }
+}
+
+// Persistent launch: global wavefront w takes tiles w, w + W, ...; each
+// wavefront keeps its own cursor in the tensor table (sentinel-terminated).
+template <int BITS, bool COUNT>
+__global__ void __launch_bounds__(kThreads)
+turbo_list(const TurboEntry* __restrict__ table, long long total_tiles, Scalars s, TurboScalars ts, double* ws,
+           unsigned long long* nonfinite) {
+  __shared__ float lev[kThreads / 64][2][256];
+  if (!resolve_inputs(s)) return;
+  const int wave = threadIdx.x >> 6, half = (threadIdx.x >> 5) & 1;
+  const long long gw = (long long)blockIdx.x * (kThreads / 64) + wave;
+  const long long nw = (long long)gridDim.x * (kThreads / 64);
+  uint32_t bad = 0;
+  int t = 0;
+  for (long long tile = gw; tile < total_tiles; tile += nw) {
+    while (tile >= table[t + 1].tile0) ++t;
+    const TurboEntry e = table[t];
+    turbo_tile<BITS>(e, tile - e.tile0, s, ts, lev[wave][half], ws, bad);
+  }
+  if constexpr (COUNT) flush_count(bad, nonfinite);
+}
+
+// Per tensor with a UState first moment: the perfect pairwise tree of its
+// tile sums (chunks of 2048 reduced in LDS, level by level, written back in
+// place), then the scale rotation.  One workgroup per tensor.
+struct TurboReduceEntry {
+  float* scal;
+  long long ws0;
+  long long tiles;
+  long long n;
+};
+
+__global__ void __launch_bounds__(kThreads)
+turbo_reduce(const TurboReduceEntry* __restrict__ list, double* ws, double factor, const unsigned long long* skip) {
+  __shared__ double buf[2048];
+  if (skip != nullptr && *skip != 0ull) return;   // the step was skipped: no new sums, no rotation
+  const TurboReduceEntry r = list[blockIdx.x];
+  double* a = ws + r.ws0;
+  long long m = r.tiles;
+  const int tid = threadIdx.x;
+  while (true) {
+    const long long chunks = (m + 2047) / 2048;
+    for (long long c = 0; c < chunks; ++c) {
+      for (int j = tid; j < 2048; j += kThreads) {
+        const long long idx = c * 2048 + j;
+        buf[j] = idx < m ? a[idx] : 0.0;
+      }
+      __syncthreads();
+      for (int width = 1024; width >= 1; width >>= 1) {
+        double t[1024 / kThreads];                       // this level's sums, then written back
+#pragma unroll
+        for (int q = 0; q < 1024 / kThreads; ++q) {
+          const int j = tid + q * kThreads;
+          t[q] = j < width ? buf[2 * j] + buf[2 * j + 1] : 0.0;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 1024 / kThreads; ++q) {
+          const int j = tid + q * kThreads;
+          if (j < width) buf[j] = t[q];
+        }
+        __syncthreads();
+      }
+      if (tid == 0) a[c] = buf[0];
+      __syncthreads();
+    }
+    if (chunks == 1) break;
+    m = chunks;
+  }
+  if (tid == 0) {
+    const double total = a[0];
+    const float s_enc = r.scal[1];
+    r.scal[0] = s_enc;
+    r.scal[1] = (float)(factor * __builtin_sqrt(total / (double)r.n));
+    r.scal[2] = 0.0f;
+  }
+}
+
+}  // namespace pa

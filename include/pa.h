@@ -212,6 +212,72 @@ int pa_grad_stats_list(int grad_dtype, size_t count, const void* const* grads, c
                        double max_norm, double* sumsq, unsigned long long* nonfinite, float* clip_scale,
                        void* stream);
 
+/* ------------------------------------------------------------------------
+ * TurboAdam compressed state (TurboAdam package page, "How it works": UState
+ * for the first moment, 1Q for the second, "Fused CUDA path").  The update
+ * itself is the FP32 AdamW step above, on moments decoded from the state;
+ * afterwards the second moment is re-encoded with 1Q and the first moment,
+ * in normalised update units q = (m/bc1) / (sqrt(v_persisted/bc2) + eps),
+ * with UState.  Readings of what the page leaves open (code levels, grid,
+ * scale rule, random draws) are stated in adamw_step_amd/csrc/turbo.hpp.
+ *
+ * Per tensor, device buffers (all caller-owned, zero-filled before step 1):
+ *   compress_m != 0 (UState): m_codes 4*ceil(n/16) bytes of 2-bit codes,
+ *     m_means ceil(n/64) bfloat16, scalars 3 floats (decode scale, encode
+ *     scale, accumulator); else m_fp32, n floats.
+ *   compress_v != 0 (1Q): v_index 4*ceil(n*v_bits/32) bytes of indices,
+ *     v_ends 2*ceil(n/128) binary16 (low, high log2 endpoint per 128 values);
+ *     else v_fp32, n floats.
+ *   tensor_id keys the tensor's counter-based random draws (keep it fixed
+ *   across steps and distinct across tensors).
+ * Parameters and gradients are FP32, 16-byte aligned; m_fp32/v_fp32 16-byte,
+ * m_codes/v_index/v_ends/scalars 4-byte, m_means 2-byte aligned
+ * (PA_ERR_ALIGN otherwise).  With compress_m the page requires
+ * beta1^2 < beta2 (PA_ERR_ARG otherwise). */
+typedef struct {
+  int compress_m;
+  int compress_v;
+  uint32_t tensor_id;
+  uint8_t* m_codes;
+  uint16_t* m_means;
+  float* m_fp32;
+  uint8_t* v_index;
+  uint16_t* v_ends;
+  float* v_fp32;
+  float* scalars;
+} pa_turbo_state;
+
+/* v_bits: 1Q index width, 2, 4 (the page's default) or 8.  m_step_factor:
+ * the UState scale factor (the page's default 1.1).  seed: the rounding
+ * seed (the page's default 0x12345678). */
+typedef struct {
+  int v_bits;
+  double m_step_factor;
+  unsigned long long seed;
+} pa_turbo_config;
+
+/* Persistent bytes of one tensor's TurboAdam state (the page's ledger: for
+ * 131,072 values with both representations, 36,876 + 69,632 = 106,508). */
+size_t pa_turbo_state_bytes(int compress_m, int compress_v, int v_bits, size_t n);
+
+/* Device workspace a pa_turbo_step_list call needs: one double per 256
+ * values of every tensor with compress_m (its residual partial sums).  The
+ * contents need no initialisation and are dead after the call. */
+size_t pa_turbo_workspace_bytes(size_t count, const pa_turbo_state* states, const size_t* n);
+
+/* One TurboAdam step over `count` tensors sharing hyper, config and step (>= 1,
+ * counting this update): one persistent launch over all tensors (a
+ * wavefront per 256 values), then one workgroup per UState tensor that
+ * reduces its residual sums and rotates its scales.  `states` is a host
+ * array of count descriptors; `workspace` a device buffer of at least
+ * pa_turbo_workspace_bytes (8-byte aligned).  The launch plan is cached per
+ * distinct list (see pa_release_plans).  Written buffers may not overlap
+ * each other, the gradients or the workspace (PA_ERR_ALIAS).  hyper's
+ * non-finite counter, gradient scale and skip flag work as for pa_step. */
+int pa_turbo_step_list(size_t count, float* const* params, const float* const* grads, const pa_turbo_state* states,
+                       const size_t* n, const pa_hyper* hyper, const pa_turbo_config* config, long long step,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* Persistent optimizer-state bytes for n parameters in `mode` (the state
  * ledger; Packed AdamW Reference README, "The narrow result": 8 bytes per
  * parameter for FP32 AdamW, 4 for the packed word).  Blockwise: two code

@@ -235,3 +235,25 @@ def test_hyper_device_inputs_rules(pa):
     h = _hyper(pa)
     h.grad_scale = FAKE + 2 ** 22 + 8                       # inside the v codes
     assert _raw_step(pa, 3, FAKE, FAKE + 2 ** 18, ctypes.addressof(bw), 2048, h) == pa.PA_ERR_ALIAS
+
+
+def test_turbo_argument_rules(pa):
+    L = pa.lib()
+    h = _hyper(pa)
+    cfg = pa.TurboConfig(4, 1.1, 0x12345678)
+    P = (ctypes.c_void_p * 1)(FAKE)
+    G = (ctypes.c_void_p * 1)(FAKE + 2 ** 20)
+    N = (ctypes.c_size_t * 1)(4096)
+    S = (pa.TurboStateDesc * 1)(pa.TurboStateDesc(1, 1, 0, FAKE + 2 ** 21, FAKE + 2 ** 22, None,
+                                                  FAKE + 2 ** 23, FAKE + 2 ** 24, None, FAKE + 2 ** 25))
+    call = lambda h_, c_, step=1: L.pa_turbo_step_list(1, P, G, S, N, ctypes.byref(h_), ctypes.byref(c_), step,
+                                                        FAKE + 2 ** 26, 1 << 20, None)
+    assert call(h, pa.TurboConfig(3, 1.1, 1)) == pa.PA_ERR_ARG            # index width
+    assert call(h, pa.TurboConfig(4, 0.0, 1)) == pa.PA_ERR_ARG            # scale factor
+    assert call(h, cfg, step=0) == pa.PA_ERR_ARG
+    hb = _hyper(pa, beta1=0.99, beta2=0.98)                               # beta1^2 >= beta2 with UState
+    assert call(hb, cfg) == pa.PA_ERR_ARG
+    assert pa.pa_turbo_state_bytes(1, 1, 4, 131072) == 106508
+    assert pa.pa_turbo_state_bytes(0, 0, 4, 10) == 80
+    assert pa.pa_turbo_state_bytes(1, 1, 3, 10) == 0
+    assert L.pa_turbo_workspace_bytes(1, S, N) == 8 * 16

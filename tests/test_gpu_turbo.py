@@ -1,0 +1,121 @@
+"""TurboAdam compressed-state step (UState + 1Q) through the C ABI against
+the oracle, value by value and bit for bit: parameters, 2-bit codes, bf16
+means, 1Q indices, fp16 endpoints, tensor scales, and the FP32 moments of
+tensors that keep them.  Sizes span tiles, blocks and groups with ragged
+tails; lists mix the four representation pairs and the three index widths."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import assert_params, banner, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+H = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+
+
+@pytest.fixture(scope="module")
+def pa():
+    import adamw_step_amd as pa_mod
+    pa_mod.lib()
+    return pa_mod
+
+
+def _host_words(t, dtype):
+    return None if t is None else to_host(t).view(dtype)
+
+
+def _compare_state(dev, host, what):
+    if host.compress_m:
+        assert np.array_equal(_host_words(dev.m_codes, np.uint32), host.m_codes), f"{what}: UState codes"
+        assert np.array_equal(_host_words(dev.m_means, np.uint16), host.m_means), f"{what}: UState means"
+        assert np.array_equal(_host_words(dev.scalars, np.uint32), host.scal.view(np.uint32)), f"{what}: scales"
+    else:
+        assert np.array_equal(_host_words(dev.m_fp32, np.uint32), host.m_fp32.view(np.uint32)), f"{what}: m"
+    if host.compress_v:
+        got, want = _host_words(dev.v_index, np.uint32), host.v_index
+        diff = np.nonzero(got != want)[0]
+        assert diff.size == 0, f"{what}: 1Q index words differ at {diff[:5]}"
+        assert np.array_equal(_host_words(dev.v_ends, np.uint16), host.v_ends), f"{what}: 1Q endpoints"
+    else:
+        assert np.array_equal(_host_words(dev.v_fp32, np.uint32), host.v_fp32.view(np.uint32)), f"{what}: v"
+
+
+def _run(pa, sizes, flags, bits, steps, seed, grad_scale=1e-3):
+    import torch
+    r = np.random.Generator(np.random.PCG64(seed))
+    hp = [r.normal(0, 0.02, n).astype(np.float32) for n in sizes]
+    dp = [to_dev(a) for a in hp]
+    hs = [oracle.TurboState(n, cm, cv, bits) for n, (cm, cv) in zip(sizes, flags)]
+    ds = [pa.TurboState(n, "cuda:0", cm, cv, bits, tensor_id=i) for i, (n, (cm, cv)) in enumerate(zip(sizes, flags))]
+    grads = [torch.zeros(n, dtype=torch.float32, device="cuda:0") for n in sizes]
+    tl = pa.TurboList(dp, grads, ds, v_bits=bits)
+    same = total = 0
+    for t in range(1, steps + 1):
+        hg = [(r.normal(0, 1, n) * grad_scale * 10.0 ** r.uniform(-2, 1)).astype(np.float32) for n in sizes]
+        for gdev, g in zip(grads, hg):
+            gdev.copy_(torch.from_numpy(g))
+        banner(f"turbo bits {bits} sizes {sizes[:5]}.. step {t}")
+        tl.step(H, t)
+        torch.cuda.synchronize()
+        sc = oracle.scalars(H["lr"], H["beta1"], H["beta2"], H["eps"], H["weight_decay"], t)
+        ts = oracle.turbo_scalars(H["beta1"], H["beta2"], t)
+        for i in range(len(sizes)):
+            oracle.turbo_step(hp[i], hg[i], hs[i], sc, ts, t, tensor_id=i)
+            _compare_state(ds[i], hs[i], f"step {t} tensor {i} (n={sizes[i]}, flags {flags[i]})")
+            s_, _ = assert_params(to_host(dp[i]), hp[i], what=f"step {t} tensor {i} params")
+            same += s_
+            total += sizes[i]
+    banner(f"turbo bits {bits}: bit-identical params {same}/{total}")
+
+
+SIZES = [1, 5, 63, 64, 65, 127, 128, 129, 255, 256, 257, 4096 + 77, 70001]
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_turbo_both_compressed(pa, bits):
+    _run(pa, SIZES, [(True, True)] * len(SIZES), bits, steps=4, seed=100 + bits)
+
+
+def test_turbo_mixed_representations(pa):
+    flags = [(True, True), (False, True), (True, False), (False, False)] * 4
+    sizes = [3, 300, 4097, 128, 64, 1000, 257, 9, 513, 2048, 7, 65536, 129, 255, 1, 12345]
+    _run(pa, sizes, flags, 4, steps=4, seed=7)
+
+
+def test_turbo_large_tensor(pa):
+    _run(pa, [1 << 20, 3 * 65536 + 11], [(True, True), (True, True)], 4, steps=3, seed=9)
+
+
+def test_turbo_skip_and_scale(pa):
+    import torch
+    n = 5000
+    r = np.random.default_rng(3)
+    hp = r.normal(0, 0.02, n).astype(np.float32)
+    dp = to_dev(hp)
+    hs = oracle.TurboState(n)
+    ds = pa.TurboState(n, "cuda:0")
+    g = to_dev(r.normal(0, 1e-3, n).astype(np.float32))
+    tl = pa.TurboList([dp], [g], [ds])
+    scale = torch.tensor([0.25], dtype=torch.float32, device="cuda:0")
+    flag = torch.tensor([1], dtype=torch.int64, device="cuda:0")
+    banner("turbo: skipped step")
+    tl.step(dict(H, skip_if_nonzero=flag), 1)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(dp), hp) and not to_host(ds.scalars).any()
+    flag.zero_()
+    for t in (1, 2):
+        banner(f"turbo: scaled step {t}")
+        tl.step(dict(H, skip_if_nonzero=flag, grad_scale=scale), t)
+        torch.cuda.synchronize()
+        sc = oracle.scalars(H["lr"], H["beta1"], H["beta2"], H["eps"], H["weight_decay"], t)
+        oracle.turbo_step(hp, oracle.scale_grads(0, to_host(g), np.float32(0.25)), hs, sc,
+                          oracle.turbo_scalars(H["beta1"], H["beta2"], t), t)
+        _compare_state(ds, hs, f"scaled step {t}")
+        assert_params(to_host(dp), hp)
+
+
+def test_turbo_state_bytes_match_page(pa):
+    n = 131072
+    ds = pa.TurboState(n, "cuda:0")
+    assert ds.nbytes() == pa.pa_turbo_state_bytes(1, 1, 4, n) == oracle.turbo_state_bytes(1, 1, 4, n) == 106508
