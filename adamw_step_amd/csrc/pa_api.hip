@@ -835,6 +835,7 @@ int pa_turbo_step_list(size_t count, float* const* params, const float* const* g
   std::vector<uintptr_t> key;
   key.reserve(count * 13 + 1);
   key.push_back((uintptr_t)config->v_bits);
+  key.push_back((uintptr_t)config->seed);
   for (size_t i = 0; i < count; ++i) {
     const pa_turbo_state& t = states[i];
     for (const void* ptr : {(const void*)params[i], (const void*)grads[i], (const void*)t.m_codes,
@@ -873,6 +874,7 @@ int pa_turbo_step_list(size_t count, float* const* params, const float* const* g
       e.tile0 = tiles;
       e.ws0 = t.compress_m ? ws_slots : 0;
       e.tensor_id = t.tensor_id;
+      e.seed = config->seed;
       e.flags = (t.compress_m ? 1 : 0) | (t.compress_v ? 2 : 0);
       const long long nt = turbo_tiles(n[i]);
       if (t.compress_m) {

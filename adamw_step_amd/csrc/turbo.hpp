@@ -60,6 +60,9 @@ struct TurboEntry {
   long long n;
   long long tile0;     // first global tile of this tensor
   long long ws0;       // first workspace slot (one double per tile)
+  unsigned long long seed;   // the call's rounding seed (kept here so the
+                             // Philox key schedule is formed per tile, not
+                             // hoisted into scalar registers for the launch)
   uint32_t tensor_id;
   int flags;           // bit 0: compress_m, bit 1: compress_v
 };
@@ -192,9 +195,12 @@ __device__ __forceinline__ void store_index4(uint8_t* base, long long lane_word,
 }
 
 // One 256-value tile of one tensor, by one wavefront.
+// The entry is read through a pointer at each use: held whole, its fields
+// crowd the scalar registers and spill.
 template <int BITS>
-__device__ __forceinline__ void turbo_tile(const TurboEntry& e, long long tile, const Scalars& s, const TurboScalars& ts,
-                                           float* lev_half, double* ws, uint32_t& bad) {
+__device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, long long tile, const Scalars& s,
+                                           const TurboScalars& ts, float* lev_half, double* ws, uint32_t& bad) {
+  const TurboEntry& e = *ep;
   constexpr int L = 1 << BITS;
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5, lane_in_half = lane & 31;
@@ -296,7 +302,7 @@ __device__ __forceinline__ void turbo_tile(const TurboEntry& e, long long tile, 
 
   // ---- draws of this lane's four values
   uint64_t w[4];
-  philox4x64_10((uint64_t)(i0 >> 2), (uint64_t)ts.step, ts.seed, (uint64_t)e.tensor_id, w);
+  philox4x64_10((uint64_t)(i0 >> 2), (uint64_t)ts.step, e.seed, (uint64_t)e.tensor_id, w);
 
   // ---- second moment: 1Q per block, or FP32
   float vp[4];
@@ -310,39 +316,34 @@ __device__ __forceinline__ void turbo_tile(const TurboEntry& e, long long tile, 
       hi_c = pos ? fmaxf(hi_c, v) : hi_c;
     }
     const float vmin = butterfly_min<32>(lo_c), vmax = butterfly_max<32>(hi_c);
-    uint32_t ends = 0;
-    if (vmax > 0.0f) {
-      ends = f16_directed_dev(log2((double)vmin), false) |
-             (f16_directed_dev(log2((double)vmax), true) << 16);
-    }
+    // Endpoints: lanes 0 and 1 of each half take log2 of the minimum and of
+    // the maximum (one pass of the double log2 for both), then broadcast.
+    const double lg = log2((double)(lane_in_half == 0 ? vmin : vmax));
+    const uint32_t e16 = f16_directed_dev(lg, lane_in_half != 0);
+    const int src = half << 5;
+    const uint32_t lo16 = (uint32_t)__shfl((int)e16, src, 64), hi16 = (uint32_t)__shfl((int)e16, src + 1, 64);
+    const uint32_t ends = vmax > 0.0f ? (lo16 | (hi16 << 16)) : 0u;
     build_levels<BITS>(lev_half, ends, lane_in_half);
     wave_lds_sync();
-    const float lo = f16_decode(ends & 0xFFFFu), hi = f16_decode(ends >> 16);
     uint32_t idx4 = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const float v = v1[k];
-      uint32_t idx;
-      if (!(v > 0.0f)) {
-        idx = 0;
-      } else if (__builtin_isinf(v)) {
-        idx = L - 1;
-      } else {
-        // estimate from an approximate log2, then step to the bracketing level
-        int kk = 1;
-        if (hi > lo) {
-          const float t = (__log2f(v) - lo) * (float)(L - 2) / (hi - lo);
-          kk = t < 0.0f ? 1 : (t > (float)(L - 2) ? L - 1 : (int)t + 1);
-        }
-        for (int it = 0; it < L && kk + 1 < L && lev_half[kk + 1] <= v; ++it) ++kk;
-        for (int it = 0; it < L && kk > 1 && lev_half[kk] > v; ++it) --kk;
-        idx = kk;
-        if (kk < L - 1 && v > lev_half[kk]) {
-          const float f = __fdiv_rn(v - lev_half[kk], lev_half[kk + 1] - lev_half[kk]);
-          const float u = (float)(w[k] >> 40) * 0x1p-24f;
-          if (u < f) idx = kk + 1;
-        }
+      // The largest level at or below v, by binary lifting over the sorted
+      // table (exact for any non-decreasing table, no data-dependent branch).
+      int kk = 1;
+#pragma unroll
+      for (int step = L >> 1; step >= 1; step >>= 1) {
+        const int c = kk + step;
+        kk = (c < L && lev_half[c < L ? c : L - 1] <= v) ? c : kk;
       }
+      const float lk = lev_half[kk], lk1 = lev_half[kk < L - 1 ? kk + 1 : kk];
+      const float f = __fdiv_rn(v - lk, lk1 - lk);
+      const float u = (float)(w[k] >> 40) * 0x1p-24f;
+      const uint32_t up = (kk < L - 1 && v > lk && u < f) ? 1u : 0u;
+      uint32_t idx = (uint32_t)kk + up;
+      idx = __builtin_isinf(v) ? (uint32_t)(L - 1) : idx;
+      idx = v > 0.0f ? idx : 0u;                            // zero, negative, NaN
       vp[k] = lev_half[idx];
       idx4 |= valid[k] ? idx << (BITS * k) : 0u;           // padding past the end stays zero
     }
@@ -423,8 +424,7 @@ turbo_list(const TurboEntry* __restrict__ table, long long total_tiles, Scalars 
   int t = 0;
   for (long long tile = gw; tile < total_tiles; tile += nw) {
     while (tile >= table[t + 1].tile0) ++t;
-    const TurboEntry e = table[t];
-    turbo_tile<BITS>(e, tile - e.tile0, s, ts, lev[wave][half], ws, bad);
+    turbo_tile<BITS>(table + t, tile - table[t].tile0, s, ts, lev[wave][half], ws, bad);
   }
   if constexpr (COUNT) flush_count(bad, nonfinite);
 }

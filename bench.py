@@ -28,6 +28,9 @@ Other flags:
                           chunks, in order, and time the E4 step with its
                           parameters on one chunk and its state words on
                           another, for a grid of chunk pairs
+  --mode turbo            the TurboAdam compressed-state step (UState first
+                          moment, 4-bit 1Q second moment; tensors below 4096
+                          values keep FP32 moments, as the page's thresholds)
   --mode gradstats        instead of the step: time the gradient pre-pass
                           (pa_grad_stats_list: sum of squares, non-finite
                           count and clip coefficient) over the workload's
@@ -45,7 +48,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "packed-AdamW step: params/s and achieved HBM GB/s (% of 8 TB/s) at 7B"
 PEAK_GBPS = 8000.0
-BYTES_PER_PARAM = {"e4": 20, "fp16": 20, "fp32": 28, "blockwise8": 14, "gradstats": 4}
+BYTES_PER_PARAM = {"e4": 20, "fp16": 20, "fp32": 28, "blockwise8": 14, "gradstats": 4, "turbo": None}
 WORKLOADS = {"single-262k": 1, "gpt-11m": 2, "gpt2-small-124m": 3, "llama-7b": 4, "blockwise-268m": 5}
 KERNEL_SOURCES = ("adamw_step_amd/csrc/kernels.hpp", "adamw_step_amd/csrc/codec.hpp",
                   "adamw_step_amd/csrc/pa_api.hip")
@@ -124,7 +127,10 @@ def calibrate_copy(nbytes):
     print(json.dumps({"calibrate_copy_bytes": nbytes, "launches": 3}), flush=True)
 
 
-def build_blockwise(cfg):
+def build_blockwise(cfg, layout="regions"):
+    """The blockwise workload.  layout "regions" puts the state the step
+    writes (codes, absmax values, BF16 output) one HBM region below the
+    parameters and gradients in allocation order."""
     import torch
     import workloads
     n = workloads.total(cfg)
@@ -133,14 +139,19 @@ def build_blockwise(cfg):
     zero_m = int((torch.from_numpy(qm) == 0).nonzero()[0])
     p = torch.empty(n, dtype=torch.float32, device="cuda:0")
     g = torch.empty(n, dtype=torch.float32, device="cuda:0")
-    workloads.device_fill_params(cfg, [p])
-    workloads.device_fill_grads(cfg, 1, [g])
+    spacer = None
+    if layout == "regions":
+        spacer = torch.empty(max(region_bytes() - 8 * n, 0), dtype=torch.uint8, device="cuda:0")
     state = (torch.full((n,), zero_m, dtype=torch.uint8, device="cuda:0"),
              torch.zeros(nb, dtype=torch.float32, device="cuda:0"),
              torch.zeros(n, dtype=torch.uint8, device="cuda:0"),
              torch.zeros(nb, dtype=torch.float32, device="cuda:0"),
              torch.from_numpy(qm).to("cuda:0"), torch.from_numpy(qv).to("cuda:0"),
              torch.empty(n, dtype=torch.int16, device="cuda:0"))
+    del spacer
+    torch.cuda.empty_cache()
+    workloads.device_fill_params(cfg, [p])
+    workloads.device_fill_grads(cfg, 1, [g])
     torch.cuda.synchronize()
     return [n], [p], [g], [state]
 
@@ -163,7 +174,7 @@ def build_workload(cfg, mode, param_dtype="fp32", layout="regions"):
     import torch
     import workloads
     if mode == "blockwise8":
-        return build_blockwise(cfg)
+        return build_blockwise(cfg, layout)
     sizes = workloads.sizes(cfg)
     log(f"allocating {workloads.NAMES[cfg]}: {len(sizes)} tensors, {sum(sizes)} params, layout {layout}")
     dt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[param_dtype]
@@ -341,6 +352,85 @@ def region_map(stride=12, max_chunks=276):
                                      "gbps_rows_params_cols_state": rows}}), flush=True)
 
 
+def run_turbo(args, cfg):
+    """Time the TurboAdam step over the workload's tensor list."""
+    import torch
+    import adamw_step_amd as pa
+    import workloads
+    sizes = workloads.sizes(cfg)
+    log(f"allocating {workloads.NAMES[cfg]} with TurboAdam state: {len(sizes)} tensors, {sum(sizes)} params")
+    ps = [torch.empty(n, dtype=torch.float32, device="cuda:0") for n in sizes]
+    gs = [torch.empty(n, dtype=torch.float32, device="cuda:0") for n in sizes]
+    spacer = None
+    if args.layout == "regions":
+        spacer = torch.empty(max(region_bytes() - 8 * sum(sizes), 0), dtype=torch.uint8, device="cuda:0")
+    states = [pa.TurboState(n, "cuda:0", compress_m=n >= 4096, compress_v=n >= 4096, v_bits=4, tensor_id=i)
+              for i, n in enumerate(sizes)]
+    del spacer
+    torch.cuda.empty_cache()
+    workloads.device_fill_params(cfg, ps)
+    workloads.device_fill_grads(cfg, 1, gs)
+    tl = pa.TurboList(ps, gs, states)
+    h = dict(workloads.HYPER)
+    torch.cuda.synchronize()
+    t = 0
+    for _ in range(args.warmup):
+        t += 1
+        tl.step(h, t)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        t += 1
+        evs[k][0].record(stream)
+        tl.step(h, t)
+        evs[k][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in evs]
+    mean_ms = sum(launch_ms) / len(launch_ms)
+    n = sum(sizes)
+    state = sum(st.nbytes() for st in states)
+    tiles = sum((k + 255) // 256 for k in sizes if k >= 4096)
+    algo = 12 * n + 2 * state + 16 * tiles     # p, g read; p written; state read and written; residual sums
+    achieved = algo / (mean_ms / 1e3) / 1e9
+    log(f"timed {args.steps} TurboAdam steps: {mean_ms:.3f} ms/step (events), state {state / n:.4f} B/param")
+    out = {"metric": "TurboAdam step (UState + 4-bit 1Q state): params/s", "value": round(n * args.steps / elapsed, 1),
+           "unit": "params/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(elapsed * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": args.workload, "params": n, "tensors": len(sizes), "mode": "turbo-ustate-1q4",
+                      "state_bytes": state, "state_bits_per_param": round(8 * state / n, 4),
+                      "layout": args.layout},
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                        "frac": round(achieved / PEAK_GBPS, 4), "traffic": None,
+                        "kernel": "turbo_list<4> + turbo_reduce", "algorithmic_bytes_per_launch": algo,
+                        "mean_launch_ms": round(mean_ms, 4), "kernel_sha": kernel_sha()}}
+    if not args.no_cpu_baseline:
+        import numpy as np
+        import oracle
+        picked, total = [], 0
+        for i, k in enumerate(sizes):
+            if total + k > args.cpu_sample_params // 8 and picked:
+                break
+            picked.append(i)
+            total += k
+        hp = [ps[i].cpu().numpy() for i in picked]
+        hg = [gs[i].cpu().numpy() for i in picked]
+        hs = [oracle.TurboState(sizes[i], sizes[i] >= 4096, sizes[i] >= 4096, 4) for i in picked]
+        sc = oracle.scalars(h["lr"], h["beta1"], h["beta2"], h["eps"], h["weight_decay"], 1)
+        ts = oracle.turbo_scalars(h["beta1"], h["beta2"], 1)
+        t1 = time.perf_counter()
+        for j, i in enumerate(picked):
+            oracle.turbo_step(hp[j], hg[j], hs[j], sc, ts, 1, tensor_id=i)
+        dt_cpu = time.perf_counter() - t1
+        out["cpu_baseline"] = {"value": round(total / dt_cpu, 1), "unit": "params/s", "cores": 1, "kind": "oracle",
+                               "sample": f"one step over the first {len(picked)} tensors ({total} params), "
+                                         f"{dt_cpu:.1f} s wall, single-threaded"}
+    print(json.dumps(out), flush=True)
+
+
 def load_traffic(workload, mode):
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{mode}.json")
     if not os.path.exists(path):
@@ -398,6 +488,12 @@ def main():
 
     cfg = WORKLOADS[args.workload]
     mode = args.mode
+    if mode == "turbo":
+        if cfg == 5:
+            print("bench.py: the turbo mode runs on the list workloads", file=sys.stderr)
+            sys.exit(2)
+        run_turbo(args, cfg)
+        return
     if mode == "gradstats":
         if cfg == 5:
             print("bench.py: the gradstats mode runs on the list workloads", file=sys.stderr)
