@@ -10,6 +10,7 @@ arguments.
 
 Modes: "e4" (one uint32 word per parameter: E4M11 first moment, E4M12 RMS),
 "fp16" (the same word with binary16 lanes) and "fp32" (two FP32 moments).
+TurboAdam (UState + 1Q compressed state) has its own class below.
 The blockwise 8-bit mode writes BF16 parameters to a separate buffer and
 needs 2048-multiple tensors, so it is driven through pa_step directly.
 """
@@ -199,3 +200,126 @@ class PackedAdamW(torch.optim.Optimizer):
         self._prepared = None
         if self._stats is not None:
             self._pending = False
+
+
+class TurboAdam(torch.optim.Optimizer):
+    """AdamW whose moments persist as TurboAdam state: UState for the first
+    moment, 1Q for the second (TurboAdam package page, API and "How it
+    works"), every update one pa_turbo_step_list launch plus the scale
+    rotation, with the page's defaults.
+
+    Arguments follow the page's API: lr, betas, eps, weight_decay,
+    block_size (128 only here), v_bits (2, 4 or 8 here; the page also has 3
+    and 6), compress_m, compress_v, min_m_compress_elements and
+    min_v_compress_elements (a tensor below the threshold keeps that
+    moment in FP32), m_block_size (64 only here), m_step_factor and
+    rounding_seed.  The page's validation of beta1^2 < beta2 with UState
+    on is kept.  One parameter group of contiguous FP32 tensors on one GPU;
+    ``count_nonfinite``, ``nonfinite_count()`` and ``state_bytes()`` as for
+    PackedAdamW.
+    """
+
+    def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0, block_size=128, v_bits=4,
+                 compress_m=True, compress_v=True, min_m_compress_elements=4096, min_v_compress_elements=4096,
+                 m_block_size=64, m_step_factor=1.1, rounding_seed=0x12345678, count_nonfinite=True):
+        from . import TurboList, TurboState
+        if block_size != 128 or m_block_size != 64:
+            raise ValueError("this implementation has 128-value 1Q blocks and 64-value UState groups")
+        if v_bits not in (2, 4, 8):
+            raise ValueError("v_bits must be 2, 4 or 8 here")
+        if compress_m and not betas[0] ** 2 < betas[1]:
+            raise ValueError("UState needs beta1**2 < beta2")
+        defaults = dict(lr=lr, betas=betas, eps=eps, weight_decay=weight_decay)
+        super().__init__(params, defaults)
+        if len(self.param_groups) != 1:
+            raise ValueError("TurboAdam here takes one parameter group (one lr, one step for all)")
+        plist = self.param_groups[0]["params"]
+        if not plist:
+            raise ValueError("no parameters")
+        dev = plist[0].device
+        for p in plist:
+            if p.dtype != torch.float32 or not p.is_cuda or not p.is_contiguous() or p.device != dev:
+                raise TypeError("parameters must be contiguous float32 tensors on one GPU")
+        self.v_bits, self.m_step_factor, self.seed = v_bits, float(m_step_factor), int(rounding_seed)
+        self.step_count = 0
+        self._TurboList = TurboList
+        self._states = []
+        for i, p in enumerate(plist):
+            n = p.numel()
+            st = TurboState(n, dev, compress_m=compress_m and n >= min_m_compress_elements,
+                            compress_v=compress_v and n >= min_v_compress_elements, v_bits=v_bits, tensor_id=i)
+            self._states.append(st)
+            self.state[p]["turbo"] = st
+        self._prepared = None
+        self._prepared_key = None
+        self._nonfinite = torch.zeros(1, dtype=torch.int64, device=dev) if count_nonfinite else None
+
+    def state_bytes(self):
+        """Persistent optimizer-state bytes: codes, means, indices, endpoints,
+        per-tensor scales, and the FP32 moments of uncompressed tensors."""
+        return sum(st.nbytes() for st in self._states)
+
+    def nonfinite_count(self):
+        return 0 if self._nonfinite is None else int(self._nonfinite.item())
+
+    @torch.no_grad()
+    def step(self, closure=None):
+        loss = None
+        if closure is not None:
+            with torch.enable_grad():
+                loss = closure()
+        group = self.param_groups[0]
+        params = group["params"]
+        grads = []
+        for p in params:
+            if p.grad is None or p.grad.is_sparse:
+                raise RuntimeError("every parameter needs a dense gradient on every update")
+            grads.append(p.grad if p.grad.is_contiguous() else p.grad.contiguous())
+        key = tuple(g.data_ptr() for g in grads)
+        if self._prepared is None or key != self._prepared_key:
+            self._prepared = self._TurboList(params, grads, self._states, v_bits=self.v_bits,
+                                             m_step_factor=self.m_step_factor, seed=self.seed)
+            self._prepared_key = key
+        self.step_count += 1
+        beta1, beta2 = group["betas"]
+        hyper = dict(lr=group["lr"], beta1=beta1, beta2=beta2, eps=group["eps"], weight_decay=group["weight_decay"])
+        if self._nonfinite is not None:
+            hyper["nonfinite"] = self._nonfinite
+        self._prepared.step(hyper, self.step_count)
+        return loss
+
+    def state_dict(self):
+        """Hyperparameters and, per parameter, the raw state tensors (codes,
+        means, indices, endpoints, scales or FP32 moments) and the step."""
+        groups = [{k: v for k, v in g.items() if k != "params"} for g in self.param_groups]
+        state = {}
+        for i, st in enumerate(self._states):
+            state[i] = {name: t.detach().clone() for name, t in (
+                ("m_codes", st.m_codes), ("m_means", st.m_means), ("scalars", st.scalars), ("m_fp32", st.m_fp32),
+                ("v_index", st.v_index), ("v_ends", st.v_ends), ("v_fp32", st.v_fp32)) if t is not None}
+        return {"state": state, "param_groups": groups,
+                "turbo": {"step": self.step_count, "v_bits": self.v_bits, "seed": self.seed,
+                          "m_step_factor": self.m_step_factor}}
+
+    def load_state_dict(self, state_dict):
+        """Restore a checkpoint written by state_dict(), bit for bit."""
+        meta = state_dict["turbo"]
+        if meta["v_bits"] != self.v_bits or meta["seed"] != self.seed:
+            raise ValueError("checkpoint was written with another v_bits or rounding seed")
+        for g, saved in zip(self.param_groups, state_dict["param_groups"]):
+            for k, v in saved.items():
+                g[k] = v
+        for i, st in enumerate(self._states):
+            saved = state_dict["state"][i]
+            for name in ("m_codes", "m_means", "scalars", "m_fp32", "v_index", "v_ends", "v_fp32"):
+                t = getattr(st, name)
+                if (t is None) != (name not in saved):
+                    raise ValueError(f"checkpoint tensor {i} has a different state layout")
+                if t is not None:
+                    src = saved[name]
+                    if src.numel() != t.numel() or src.dtype != t.dtype:
+                        raise ValueError(f"checkpoint tensor {i}: {name} differs in size or type")
+                    t.copy_(src.to(t.device))
+        self.step_count = int(meta["step"])
+        self.m_step_factor = float(meta["m_step_factor"])
+        self._prepared = None

@@ -167,3 +167,51 @@ def test_llama_7b_grad_stats_exact(pa):
         del gs
         torch.cuda.empty_cache()
         pa.pa_release_plans()
+
+
+@pytest.mark.timeout(900)
+def test_llama_7b_turbo_sampled_tensors(pa):
+    """The TurboAdam step over the whole 291-tensor list in the benchmark's
+    launch configuration; three whole tensors (tensors are independent:
+    each has its own draws, groups, blocks and scales) against the oracle
+    for two steps: the first RMSNorm gain, the first query projection and
+    the final norm."""
+    import torch
+    cfg = 4
+    sizes = workloads.sizes(cfg)
+    banner(f"llama-7b TurboAdam: allocating {sum(sizes) * 8 / 1e9:.1f} GB of params and grads")
+    ps = [torch.empty(n, dtype=torch.float32, device="cuda:0") for n in sizes]
+    gs = [torch.empty(n, dtype=torch.float32, device="cuda:0") for n in sizes]
+    states = [pa.TurboState(n, "cuda:0", n >= 4096, n >= 4096, 4, tensor_id=i) for i, n in enumerate(sizes)]
+    pick = [i for i, (name, _) in enumerate(workloads.shapes(cfg)) if "norm" in name][:1]
+    pick += [i for i, (name, _) in enumerate(workloads.shapes(cfg)) if "q_proj" in name][:1]
+    pick += [len(sizes) - 2 if "norm" in workloads.shapes(cfg)[-2][0] else len(sizes) - 1]
+    try:
+        workloads.device_fill_params(cfg, ps)
+        tl = pa.TurboList(ps, gs, states)
+        hp = {i: to_host(ps[i]).copy() for i in pick}
+        hs = {i: oracle.TurboState(sizes[i], sizes[i] >= 4096, sizes[i] >= 4096, 4) for i in pick}
+        for t in (1, 2):
+            workloads.device_fill_grads(cfg, t, gs)
+            torch.cuda.synchronize()
+            hg = {i: to_host(gs[i]).copy() for i in pick}
+            banner(f"llama-7b TurboAdam step {t}: one launch over 291 tensors")
+            tl.step(dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01), t)
+            torch.cuda.synchronize()
+            sc = scalars(t)
+            ts = oracle.turbo_scalars(0.9, 0.999, t)
+            for i in pick:
+                oracle.turbo_step(hp[i], hg[i], hs[i], sc, ts, t, tensor_id=i)
+                st = states[i]
+                if hs[i].compress_m:
+                    assert np.array_equal(to_host(st.m_codes).view(np.uint32), hs[i].m_codes), f"tensor {i} codes"
+                    assert np.array_equal(to_host(st.m_means).view(np.uint16), hs[i].m_means), f"tensor {i} means"
+                    assert np.array_equal(to_host(st.scalars).view(np.uint32), hs[i].scal.view(np.uint32))
+                    assert np.array_equal(to_host(st.v_index).view(np.uint32), hs[i].v_index), f"tensor {i} index"
+                    assert np.array_equal(to_host(st.v_ends).view(np.uint16), hs[i].v_ends), f"tensor {i} ends"
+                assert_params(to_host(ps[i]), hp[i], what=f"tensor {i} params")
+            banner(f"llama-7b TurboAdam step {t}: tensors {pick} bit-exact")
+    finally:
+        del ps, gs, states
+        torch.cuda.empty_cache()
+        pa.pa_release_plans()

@@ -173,3 +173,82 @@ def test_optimizer_skips_nonfinite_updates():
             assert_params(ps[i].detach().cpu().numpy(), hp[i])
     opt._reconcile()
     assert opt.skipped_steps == 2 and opt.step_count == 3 and opt.nonfinite_count() == 0
+
+
+def _turbo_oracle_states(sizes, thr=4096, bits=4):
+    return [oracle.TurboState(n, n >= thr, n >= thr, bits) for n in sizes]
+
+
+def test_turboadam_optimizer_matches_oracle():
+    """TurboAdam front end: three steps of every state word and parameter
+    against the oracle; tensors below 4096 values keep FP32 moments."""
+    import torch
+    from adamw_step_amd.optim import TurboAdam
+    sizes = [70000, 4096, 4095, 300, 131072]
+    ps = _params(torch, sizes, 21)
+    hp = [p.detach().cpu().numpy().copy() for p in ps]
+    opt = TurboAdam(ps, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01)
+    hs = _turbo_oracle_states(sizes)
+    r = np.random.Generator(np.random.PCG64(22))
+    for t in range(1, 4):
+        hg = [(r.normal(0, 1e-3, n)).astype(np.float32) for n in sizes]
+        for p, g in zip(ps, hg):
+            p.grad = torch.from_numpy(g).cuda()
+        banner(f"TurboAdam step {t}")
+        opt.step()
+        torch.cuda.synchronize()
+        sc = scalars(t)
+        ts = oracle.turbo_scalars(0.9, 0.999, t)
+        for i in range(len(sizes)):
+            oracle.turbo_step(hp[i], hg[i], hs[i], sc, ts, t, tensor_id=i)
+            st = opt._states[i]
+            if hs[i].compress_m:
+                assert np.array_equal(st.m_codes.cpu().numpy().view(np.uint32), hs[i].m_codes)
+                assert np.array_equal(st.m_means.cpu().numpy().view(np.uint16), hs[i].m_means)
+                assert np.array_equal(st.scalars.cpu().numpy().view(np.uint32), hs[i].scal.view(np.uint32))
+                assert np.array_equal(st.v_index.cpu().numpy().view(np.uint32), hs[i].v_index)
+                assert np.array_equal(st.v_ends.cpu().numpy().view(np.uint16), hs[i].v_ends)
+            else:
+                assert np.array_equal(st.m_fp32.cpu().numpy().view(np.uint32), hs[i].m_fp32.view(np.uint32))
+                assert np.array_equal(st.v_fp32.cpu().numpy().view(np.uint32), hs[i].v_fp32.view(np.uint32))
+            assert_params(ps[i].detach().cpu().numpy(), hp[i])
+    assert opt.nonfinite_count() == 0
+    n = 131072
+    assert opt._states[4].nbytes() == 106508 == oracle.turbo_state_bytes(1, 1, 4, n)
+
+
+def test_turboadam_checkpoint_resume_is_bit_exact():
+    import torch
+    from adamw_step_amd.optim import TurboAdam
+    sizes = [40000, 5000, 77]
+    r = np.random.Generator(np.random.PCG64(23))
+    grads = [[torch.from_numpy(r.normal(0, 1e-3, n).astype(np.float32)).cuda() for n in sizes] for _ in range(6)]
+
+    def run(ps, opt, steps):
+        for gs in steps:
+            for p, g in zip(ps, gs):
+                p.grad = g.clone()
+            opt.step()
+
+    ps_a = _params(torch, sizes, 24)
+    opt_a = TurboAdam(ps_a, lr=1e-3, weight_decay=0.01)
+    banner("TurboAdam checkpoint: six straight steps")
+    run(ps_a, opt_a, grads)
+    ps_b = _params(torch, sizes, 24)
+    opt_b = TurboAdam(ps_b, lr=1e-3, weight_decay=0.01)
+    run(ps_b, opt_b, grads[:3])
+    buf = io.BytesIO()
+    torch.save({"p": [p.detach().cpu() for p in ps_b], "opt": opt_b.state_dict()}, buf)
+    buf.seek(0)
+    ck = torch.load(buf, weights_only=True)
+    ps_c = [torch.nn.Parameter(t.cuda()) for t in ck["p"]]
+    opt_c = TurboAdam(ps_c, lr=1e-3, weight_decay=0.01)
+    opt_c.load_state_dict(ck["opt"])
+    banner("TurboAdam checkpoint: three steps, save, load, three steps")
+    run(ps_c, opt_c, grads[3:])
+    torch.cuda.synchronize()
+    for a, c in zip(ps_a, ps_c):
+        assert torch.equal(a.detach(), c.detach())
+    for sa, sc_ in zip(opt_a._states, opt_c._states):
+        for ta, tc in zip(sa.tensors(), sc_.tensors()):
+            assert torch.equal(ta, tc)
