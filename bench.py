@@ -48,10 +48,13 @@ sys.path.insert(0, ROOT)
 
 METRIC = "packed-AdamW step: params/s and achieved HBM GB/s (% of 8 TB/s) at 7B"
 PEAK_GBPS = 8000.0
+# VALU issue peak of MI355X: 256 CUs x 64 lanes (one wave64 vector
+# instruction per CU per cycle) x 2.4 GHz, in G lane-instructions per second.
+PEAK_VALU_GLANE = 256 * 64 * 2.4
 BYTES_PER_PARAM = {"e4": 20, "fp16": 20, "fp32": 28, "blockwise8": 14, "gradstats": 4, "turbo": None}
 WORKLOADS = {"single-262k": 1, "gpt-11m": 2, "gpt2-small-124m": 3, "llama-7b": 4, "blockwise-268m": 5}
 KERNEL_SOURCES = ("adamw_step_amd/csrc/kernels.hpp", "adamw_step_amd/csrc/codec.hpp",
-                  "adamw_step_amd/csrc/pa_api.hip")
+                  "adamw_step_amd/csrc/turbo.hpp", "adamw_step_amd/csrc/pa_api.hip")
 
 
 def kernel_sha():
@@ -396,6 +399,16 @@ def run_turbo(args, cfg):
     algo = 12 * n + 2 * state + 16 * tiles     # p, g read; p written; state read and written; residual sums
     achieved = algo / (mean_ms / 1e3) / 1e9
     log(f"timed {args.steps} TurboAdam steps: {mean_ms:.3f} ms/step (events), state {state / n:.4f} B/param")
+    # The step is bound by vector ALU issue, not HBM: its roofline is the
+    # VALU lane-instruction rate, from the instructions per parameter that
+    # the counters measured for this kernel source (profiles/), if current.
+    valu = None
+    vpath = os.path.join(ROOT, "profiles", f"valu_{args.workload}_turbo.json")
+    if os.path.exists(vpath):
+        with open(vpath) as f:
+            vj = json.load(f)
+        if vj.get("kernel_sha") == kernel_sha():
+            valu = vj["valu_lane_instr_per_param"]
     out = {"metric": "TurboAdam step (UState + 4-bit 1Q state): params/s", "value": round(n * args.steps / elapsed, 1),
            "unit": "params/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(elapsed * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak",
@@ -403,10 +416,16 @@ def run_turbo(args, cfg):
            "config": {"workload": args.workload, "params": n, "tensors": len(sizes), "mode": "turbo-ustate-1q4",
                       "state_bytes": state, "state_bits_per_param": round(8 * state / n, 4),
                       "layout": args.layout},
-           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
-                        "frac": round(achieved / PEAK_GBPS, 4), "traffic": None,
-                        "kernel": "turbo_list<4> + turbo_reduce", "algorithmic_bytes_per_launch": algo,
-                        "mean_launch_ms": round(mean_ms, 4), "kernel_sha": kernel_sha()}}
+           "roofline": ({"bound": "alu", "achieved": round(valu * n / (mean_ms / 1e3) / 1e9, 1),
+                         "peak": PEAK_VALU_GLANE, "unit": "G VALU lane-instr/s",
+                         "frac": round(valu * n / (mean_ms / 1e3) / 1e9 / PEAK_VALU_GLANE, 4),
+                         "valu_lane_instr_per_param": valu} if valu is not None else
+                        {"bound": "alu", "achieved": None, "peak": PEAK_VALU_GLANE, "unit": "G VALU lane-instr/s",
+                         "frac": None}) | {
+                        "hbm_achieved_gbps": round(achieved, 1), "hbm_frac": round(achieved / PEAK_GBPS, 4),
+                        "traffic": None, "kernel": "turbo_list<4> + turbo_reduce",
+                        "algorithmic_bytes_per_launch": algo, "mean_launch_ms": round(mean_ms, 4),
+                        "kernel_sha": kernel_sha()}}
     if not args.no_cpu_baseline:
         import numpy as np
         import oracle
