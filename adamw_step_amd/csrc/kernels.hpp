@@ -383,28 +383,37 @@ struct BlockwiseArgs {
 
 // Midpoint search through a bucket table.
 //
-// A float's bit pattern, with the sign bit set for non-negative values and
-// every bit flipped for negative ones, is an unsigned key in the numeric
-// order of the floats.  Its top 13 bits pick one of 8192 buckets (a
-// sixteenth of a binade each); base[b] is the number of midpoints below the
-// bucket's smallest float.  A value's code, the number of midpoints strictly
-// below it, is base[b] plus the number of the bucket's own midpoints below
-// it.  When no bucket holds more than NCMP midpoints that is a plain count
-// over mid[base .. base+NCMP) (midpoints past the bucket are above the value,
-// and mid[255..258] = +Inf pads the end); fuller maps take a bisection over
-// the bucket, whose size is base[b+1] - base[b].  Ties go to the lower map
-// entry; NaN is ordered above every number.
+// The top 13 bits of a float's bit pattern (sign, exponent, 4 mantissa
+// bits) pick one of 8192 buckets, a sixteenth of a binade of one sign each;
+// the floats of a bucket form one contiguous numeric range (for negative
+// buckets the range runs from the largest magnitude up).  base[b] is the
+// number of midpoints below the bucket's smallest float.  A value's code,
+// the number of midpoints strictly below it, is base[b] plus the number of
+// the bucket's own midpoints below it.  When no bucket holds more than NCMP
+// midpoints that is a plain count over mid[base .. base+NCMP) (midpoints
+// past the bucket are above the value, and mid[255..258] = +Inf pads the
+// end); fuller maps take a bisection over the bucket, whose size is the
+// base of the numerically next bucket minus base[b].  Ties go to the lower
+// map entry; NaN is ordered above every number.
 constexpr int kBucketShift = 19;
 constexpr int kBuckets = 1 << (32 - kBucketShift);
 constexpr int kMidPad = 260;
 
-__device__ __forceinline__ uint32_t order_key(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+__device__ __forceinline__ uint32_t bucket_of(float x) { return __float_as_uint(x) >> kBucketShift; }
+
+// Smallest and largest float of bucket b.
+__device__ __forceinline__ float bucket_lo(uint32_t b) {
+  return __uint_as_float(b < (uint32_t)kBuckets / 2 ? b << kBucketShift : ((b + 1) << kBucketShift) - 1u);
+}
+__device__ __forceinline__ float bucket_hi(uint32_t b) {
+  return __uint_as_float(b < (uint32_t)kBuckets / 2 ? ((b + 1) << kBucketShift) - 1u : b << kBucketShift);
 }
 
-__device__ __forceinline__ float key_float(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+// The numerically next bucket (kBuckets, a pad of 255, after the last
+// positive one; the first positive one after the smallest negative one).
+__device__ __forceinline__ uint32_t bucket_next(uint32_t b) {
+  constexpr uint32_t h = (uint32_t)kBuckets / 2;
+  return b + 1 < h ? b + 1 : (b + 1 == h ? (uint32_t)kBuckets : (b == h ? 0u : b - 1));
 }
 
 // Number of sorted midpoints (mid[0..254]) below x, or at most x.
@@ -421,7 +430,7 @@ __device__ __forceinline__ uint32_t count_below(const float* mid, float x, bool 
 
 template <int NCMP>
 __device__ __forceinline__ uint32_t search_mid(const float* mid, const uint8_t* base, float c) {
-  const uint32_t b = order_key(c) >> kBucketShift;
+  const uint32_t b = bucket_of(c);
   uint32_t lo = base[b];
   if constexpr (NCMP > 0) {
     uint32_t code = lo;
@@ -429,7 +438,8 @@ __device__ __forceinline__ uint32_t search_mid(const float* mid, const uint8_t* 
     for (int k = 0; k < NCMP; ++k) code += mid[lo + k] < c ? 1u : 0u;
     lo = code;
   } else {
-    uint32_t n = base[b + 1] > lo ? base[b + 1] - lo : 0u;
+    const uint32_t nb = base[bucket_next(b)];
+    uint32_t n = nb > lo ? nb - lo : 0u;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const uint32_t half = n >> 1;
@@ -503,8 +513,8 @@ __device__ __forceinline__ void build_map(const float* lut, MapTables& t, uint32
   __syncthreads();
   uint32_t fullest = 0, near_zero = 0;
   for (int b = tid; b < kBuckets; b += kThreads) {
-    const float lo = key_float((uint32_t)b << kBucketShift);
-    const float hi = key_float((((uint32_t)b + 1) << kBucketShift) - 1u);
+    const float lo = bucket_lo((uint32_t)b);
+    const float hi = bucket_hi((uint32_t)b);
     const uint32_t below = count_below(t.mid, lo, false), upto = count_below(t.mid, hi, true);
     t.base[b] = (uint8_t)below;
     fullest = max(fullest, upto > below ? upto - below : 0u);
