@@ -497,7 +497,7 @@ def main():
         return
     if args.train_gpt:
         from trainer.loop import measure
-        rows = [measure(kind, steps=args.steps, warmup=args.warmup) for kind in ("e4", "fp32", "torch-fused")]
+        rows = [measure(kind, steps=args.steps, warmup=args.warmup) for kind in ("e4", "fp32", "turbo", "torch-fused")]
         for r in rows:
             r["opt_share"] = round(r["opt_ms"] / r["step_ms"], 4)
             log(f"train {r['optimizer']}: {r['step_ms']:.3f} ms/step, optimizer {r['opt_ms']:.3f} ms")

@@ -42,6 +42,31 @@ int main() {
     std::printf("list alias: got %d\n", rc);
     ++bad;
   }
+  // gradient pre-pass: argument rules checked before any device work
+  const void* gl[1] = {reinterpret_cast<void*>(F)};
+  size_t gn[1] = {64};
+  expect(pa_grad_stats_list(7, 1, gl, gn, 0.0, reinterpret_cast<double*>(F + 4096), nullptr, nullptr, nullptr),
+         PA_ERR_ARG, "stats dtype");
+  expect(pa_grad_stats_list(0, 1, gl, gn, 0.0, reinterpret_cast<double*>(F + 4100), nullptr, nullptr, nullptr),
+         PA_ERR_ALIGN, "stats align");
+  expect(pa_grad_stats_list(0, 1, gl, gn, 1.0, reinterpret_cast<double*>(F + 4096),
+                            reinterpret_cast<unsigned long long*>(F + 4096), nullptr, nullptr),
+         PA_ERR_ALIAS, "stats alias");
+  // TurboAdam step: configuration and beta rules checked before any device work
+  pa_turbo_state ts{1, 1, 0, reinterpret_cast<uint8_t*>(F + (1 << 21)), reinterpret_cast<uint16_t*>(F + (1 << 22)),
+                    nullptr, reinterpret_cast<uint8_t*>(F + (1 << 23)), reinterpret_cast<uint16_t*>(F + (1 << 24)),
+                    nullptr, P(F + (1 << 25))};
+  pa_turbo_config tc{3, 1.1, 1};
+  float* tp[1] = {P(F)};
+  const float* tg[1] = {P(F + (1 << 20))};
+  size_t tn[1] = {4096};
+  expect(pa_turbo_step_list(1, tp, tg, &ts, tn, &h, &tc, 1, reinterpret_cast<void*>(F + (1 << 26)), 1 << 20, nullptr),
+         PA_ERR_ARG, "turbo bits");
+  pa_hyper hb{1e-3, 0.99, 0.98, 1e-8, 0.01, nullptr, nullptr, nullptr};
+  pa_turbo_config tc4{4, 1.1, 1};
+  expect(pa_turbo_step_list(1, tp, tg, &ts, tn, &hb, &tc4, 1, reinterpret_cast<void*>(F + (1 << 26)), 1 << 20, nullptr),
+         PA_ERR_ARG, "turbo betas");
+  if (pa_turbo_state_bytes(1, 1, 4, 131072) != 106508 || pa_turbo_workspace_bytes(1, &ts, tn) != 128) ++bad;
   pa_format pf;
   for (int m = 0; m < 4; ++m) expect(pa_format_info(m, &pf), PA_OK, "format");
   expect(pa_format_info(9, &pf), PA_ERR_ARG, "format mode");

@@ -119,3 +119,57 @@ def test_turbo_state_bytes_match_page(pa):
     n = 131072
     ds = pa.TurboState(n, "cuda:0")
     assert ds.nbytes() == pa.pa_turbo_state_bytes(1, 1, 4, n) == oracle.turbo_state_bytes(1, 1, 4, n) == 106508
+
+
+def _same_f32(got, want):
+    got, want = np.asarray(got, np.float32), np.asarray(want, np.float32)
+    nan = np.isnan(want)
+    return np.array_equal(np.isnan(got), nan) and np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
+
+
+def _same_bf16(got, want):
+    wide = lambda a: (np.asarray(a, np.uint16).astype(np.uint32) << 16).view(np.float32)
+    return _same_f32(wide(got), wide(want))
+
+
+def test_turbo_nonfinite_gradients(pa):
+    """NaN and infinite gradients: the 1Q and UState codes follow the
+    readings (NaN and zero to index 0 and code 0, +Inf to the top index)
+    exactly; floating results compare by NaN class, since a NaN's sign and
+    payload are not part of the result."""
+    import torch
+    sizes = [4096 + 33, 2000]
+    flags = [(True, True), (False, False)]
+    r = np.random.default_rng(17)
+    hp = [r.normal(0, 0.02, n).astype(np.float32) for n in sizes]
+    dp = [to_dev(a) for a in hp]
+    hs = [oracle.TurboState(n, cm, cv, 4) for n, (cm, cv) in zip(sizes, flags)]
+    ds = [pa.TurboState(n, "cuda:0", cm, cv, 4, tensor_id=i) for i, (n, (cm, cv)) in enumerate(zip(sizes, flags))]
+    grads = [torch.zeros(n, dtype=torch.float32, device="cuda:0") for n in sizes]
+    tl = pa.TurboList(dp, grads, ds)
+    counter = torch.zeros(1, dtype=torch.int64, device="cuda:0")
+    total_bad = 0
+    for t in (1, 2, 3):
+        hg = [(r.normal(0, 1e-3, n)).astype(np.float32) for n in sizes]
+        hg[0][[5, 300, 4100]] = [np.nan, np.inf, -np.inf]
+        hg[1][[0, 1999]] = [np.inf, np.nan]
+        for gdev, g in zip(grads, hg):
+            gdev.copy_(torch.from_numpy(g))
+        banner(f"turbo non-finite gradients, step {t}")
+        tl.step(dict(H, nonfinite=counter), t)
+        torch.cuda.synchronize()
+        sc = oracle.scalars(H["lr"], H["beta1"], H["beta2"], H["eps"], H["weight_decay"], t)
+        ts = oracle.turbo_scalars(H["beta1"], H["beta2"], t)
+        for i in range(len(sizes)):
+            total_bad += oracle.turbo_step(hp[i], hg[i], hs[i], sc, ts, t, tensor_id=i)
+            assert _same_f32(to_host(dp[i]), hp[i]), f"step {t} tensor {i} params"
+            st, ho = ds[i], hs[i]
+            if ho.compress_m:
+                assert np.array_equal(_host_words(st.m_codes, np.uint32), ho.m_codes)
+                assert _same_bf16(_host_words(st.m_means, np.uint16), ho.m_means)
+                assert _same_f32(to_host(st.scalars), ho.scal)
+                assert np.array_equal(_host_words(st.v_index, np.uint32), ho.v_index)
+                assert np.array_equal(_host_words(st.v_ends, np.uint16), ho.v_ends)
+            else:
+                assert _same_f32(to_host(st.m_fp32), ho.m_fp32) and _same_f32(to_host(st.v_fp32), ho.v_fp32)
+    assert int(counter.item()) == total_bad > 0

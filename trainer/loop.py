@@ -40,6 +40,9 @@ def make_optimizer(model, kind, lr, weight_decay=0.01):
     if kind in ("e4", "fp16", "fp32"):
         from adamw_step_amd.optim import PackedAdamW
         return PackedAdamW(model.parameters(), lr=lr, weight_decay=weight_decay, mode=kind)
+    if kind == "turbo":
+        from adamw_step_amd.optim import TurboAdam
+        return TurboAdam(model.parameters(), lr=lr, weight_decay=weight_decay)
     if kind == "torch-fused":
         return torch.optim.AdamW(model.parameters(), lr=lr, weight_decay=weight_decay, fused=True)
     raise ValueError(kind)
