@@ -464,6 +464,10 @@ bool valid_bits(int b) { return b == 2 || b == 4 || b == 8; }
 
 // Checks one tensor's buffers; appends the written ranges to `w` and the
 // gradient range to `r`.
+// The draws' counter words hold value index / 4 and the step in 32 bits.
+constexpr size_t kTurboMaxValues = size_t(1) << 34;
+constexpr long long kTurboMaxStep = 0xFFFFFFFFll;
+
 int check_turbo_tensor(const float* p, const float* g, const pa_turbo_state& st, size_t n, int bits,
                        std::vector<Range>* w, std::vector<Range>* r) {
   if (n == 0) return PA_OK;
@@ -817,13 +821,17 @@ int pa_turbo_step_list(size_t count, float* const* params, const float* const* g
   if (config == nullptr || !valid_bits(config->v_bits) || !std::isfinite(config->m_step_factor) ||
       !(config->m_step_factor > 0.0))
     return PA_ERR_ARG;
+  if (step > kTurboMaxStep) return PA_ERR_ARG;
   pa::Scalars s;
   int rc = make_scalars(hyper, step, &s);
   if (rc) return rc;
   if (count == 0) return PA_OK;
   if (params == nullptr || grads == nullptr || states == nullptr || n == nullptr) return PA_ERR_ARG;
   bool any_m = false;
-  for (size_t i = 0; i < count; ++i) any_m = any_m || (states[i].compress_m && n[i] > 0);
+  for (size_t i = 0; i < count; ++i) {
+    if (n[i] > kTurboMaxValues) return PA_ERR_ARG;
+    any_m = any_m || (states[i].compress_m && n[i] > 0);
+  }
   if (any_m && !(hyper->beta1 * hyper->beta1 < hyper->beta2)) return PA_ERR_ARG;
   if (!aligned(workspace, 8)) return PA_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -19,10 +19,12 @@
 //    decoded mean is the stored one.  Pairs of values use draws u and 1 - u.
 //    The scale for the next encode is 1.1 x the RMS of this step's
 //    residuals; decoding uses the scale the codes were written with.
-//  * Draws: Philox4x64-10 with key (seed, tensor id) and counter
-//    (value index / 4, step, 0, 0); the top 24 bits of word k serve the 1Q
-//    rounding of value 4j + k, bits 8..31 of words 0 and 1 serve the two
-//    UState pairs.
+//  * Draws: Philox4x32-10, the counter-based generator Triton builds in, so
+//    one counter hash for a PyTorch and a Triton path.  Key: the seed's low
+//    and high 32 bits; counter (value index / 4, step, tensor id, stream),
+//    the entry point keeping index / 4 and step below 2^32.  Stream 0: the
+//    top 24 bits of word k serve the 1Q rounding of value 4j + k.  Stream 1:
+//    the top 24 bits of words 0 and 1 serve the two UState pairs.
 //  * Sums (group means, the residual sum of squares) are perfect pairwise
 //    trees in double over the values in index order, padded with zeros, so
 //    their results do not depend on the launch.
@@ -74,21 +76,24 @@ struct TurboScalars {
   long long step;
 };
 
-__device__ __forceinline__ void philox4x64_10(uint64_t c0, uint64_t c1, uint64_t k0, uint64_t k1, uint64_t w[4]) {
-  uint64_t x0 = c0, x1 = c1, x2 = 0, x3 = 0;
+// Ten rounds of the Philox-4x32 bijection: words 0 and 2 times the two round
+// multipliers; each product's high half xors the other odd word and a key
+// word; the key steps by the two Weyl constants between rounds.
+__device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                              uint32_t k1, uint32_t w[4]) {
+  uint32_t x0 = c0, x1 = c1, x2 = c2, x3 = c3;
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     if (r) {
-      k0 += 0x9E3779B97F4A7C15ull;
-      k1 += 0xBB67AE8584CAA73Bull;
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
     }
-    const uint64_t hi0 = __umul64hi(0xD2E7470EE14C6C93ull, x0), lo0 = 0xD2E7470EE14C6C93ull * x0;
-    const uint64_t hi1 = __umul64hi(0xCA5A826395121157ull, x2), lo1 = 0xCA5A826395121157ull * x2;
-    const uint64_t n0 = hi1 ^ x1 ^ k0, n2 = hi0 ^ x3 ^ k1;
+    const uint64_t p0 = (uint64_t)0xD2511F53u * x0, p1 = (uint64_t)0xCD9E8D57u * x2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ x1 ^ k0, n2 = (uint32_t)(p0 >> 32) ^ x3 ^ k1;
     x0 = n0;
-    x1 = lo1;
+    x1 = (uint32_t)p1;
     x2 = n2;
-    x3 = lo0;
+    x3 = (uint32_t)p0;
   }
   w[0] = x0;
   w[1] = x1;
@@ -301,12 +306,14 @@ __device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, lo
   }
 
   // ---- draws of this lane's four values
-  uint64_t w[4];
-  philox4x64_10((uint64_t)(i0 >> 2), (uint64_t)ts.step, e.seed, (uint64_t)e.tensor_id, w);
+  const uint32_t ctr = (uint32_t)(i0 >> 2), stp = (uint32_t)ts.step, tid = e.tensor_id;
+  const uint32_t sk0 = (uint32_t)e.seed, sk1 = (uint32_t)(e.seed >> 32);
 
   // ---- second moment: 1Q per block, or FP32
   float vp[4];
   if (cv) {
+    uint32_t w[4];
+    philox4x32_10(ctr, stp, tid, 0u, sk0, sk1, w);
     float lo_c = __builtin_inff(), hi_c = 0.0f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -339,7 +346,7 @@ __device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, lo
       }
       const float lk = lev_half[kk], lk1 = lev_half[kk < L - 1 ? kk + 1 : kk];
       const float f = __fdiv_rn(v - lk, lk1 - lk);
-      const float u = (float)(w[k] >> 40) * 0x1p-24f;
+      const float u = (float)(w[k] >> 8) * 0x1p-24f;
       const uint32_t up = (kk < L - 1 && v > lk && u < f) ? 1u : 0u;
       uint32_t idx = (uint32_t)kk + up;
       idx = __builtin_isinf(v) ? (uint32_t)(L - 1) : idx;
@@ -367,6 +374,8 @@ __device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, lo
 
   // ---- first moment: UState per group, or FP32
   if (cm) {
+    uint32_t w[4];
+    philox4x32_10(ctr, stp, tid, 1u, sk0, sk1, w);
     float q[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -385,7 +394,7 @@ __device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, lo
       float x = s_enc > 0.0f ? __fdiv_rn(r, s_enc) : 0.0f;
       x = x > 1.5f ? 1.5f : x;
       x = x < -1.5f ? -1.5f : x;
-      float u = (float)((w[k >> 1] & 0xFFFFFFFFull) >> 8) * 0x1p-24f;
+      float u = (float)(w[k >> 1] >> 8) * 0x1p-24f;
       if (k & 1) u = 1.0f - u;
       const uint32_t kk = (uint32_t)(x >= -0.5f) + (uint32_t)(x >= 0.5f);
       uint32_t code = kk;

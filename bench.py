@@ -53,13 +53,17 @@ PEAK_GBPS = 8000.0
 PEAK_VALU_GLANE = 256 * 64 * 2.4
 BYTES_PER_PARAM = {"e4": 20, "fp16": 20, "fp32": 28, "blockwise8": 14, "gradstats": 4, "turbo": None}
 WORKLOADS = {"single-262k": 1, "gpt-11m": 2, "gpt2-small-124m": 3, "llama-7b": 4, "blockwise-268m": 5}
-KERNEL_SOURCES = ("adamw_step_amd/csrc/kernels.hpp", "adamw_step_amd/csrc/codec.hpp",
-                  "adamw_step_amd/csrc/turbo.hpp", "adamw_step_amd/csrc/pa_api.hip")
+# Device sources each kernel family is compiled from: a stored counter
+# reading stays valid while these bytes are unchanged.
+KERNEL_SOURCES = {
+    "elementwise": ("adamw_step_amd/csrc/kernels.hpp", "adamw_step_amd/csrc/codec.hpp"),
+    "turbo": ("adamw_step_amd/csrc/kernels.hpp", "adamw_step_amd/csrc/codec.hpp", "adamw_step_amd/csrc/turbo.hpp"),
+}
 
 
-def kernel_sha():
+def kernel_sha(family="elementwise"):
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[family]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -407,7 +411,7 @@ def run_turbo(args, cfg):
     if os.path.exists(vpath):
         with open(vpath) as f:
             vj = json.load(f)
-        if vj.get("kernel_sha") == kernel_sha():
+        if vj.get("kernel_sha") == kernel_sha("turbo"):
             valu = vj["valu_lane_instr_per_param"]
     out = {"metric": "TurboAdam step (UState + 4-bit 1Q state): params/s", "value": round(n * args.steps / elapsed, 1),
            "unit": "params/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -425,7 +429,7 @@ def run_turbo(args, cfg):
                         "hbm_achieved_gbps": round(achieved, 1), "hbm_frac": round(achieved / PEAK_GBPS, 4),
                         "traffic": None, "kernel": "turbo_list<4> + turbo_reduce",
                         "algorithmic_bytes_per_launch": algo, "mean_launch_ms": round(mean_ms, 4),
-                        "kernel_sha": kernel_sha()}}
+                        "kernel_sha": kernel_sha("turbo")}}
     if not args.no_cpu_baseline:
         import numpy as np
         import oracle

@@ -233,7 +233,9 @@ int pa_grad_stats_list(int grad_dtype, size_t count, const void* const* grads, c
  * Parameters and gradients are FP32, 16-byte aligned; m_fp32/v_fp32 16-byte,
  * m_codes/v_index/v_ends/scalars 4-byte, m_means 2-byte aligned
  * (PA_ERR_ALIGN otherwise).  With compress_m the page requires
- * beta1^2 < beta2 (PA_ERR_ARG otherwise). */
+ * beta1^2 < beta2 (PA_ERR_ARG otherwise).  The draws' counter holds the
+ * value index / 4 and the step in 32 bits each, so a tensor holds at most
+ * 2^34 values (PA_ERR_ARG beyond). */
 typedef struct {
   int compress_m;
   int compress_v;
@@ -265,8 +267,8 @@ size_t pa_turbo_state_bytes(int compress_m, int compress_v, int v_bits, size_t n
  * contents need no initialisation and are dead after the call. */
 size_t pa_turbo_workspace_bytes(size_t count, const pa_turbo_state* states, const size_t* n);
 
-/* One TurboAdam step over `count` tensors sharing hyper, config and step (>= 1,
- * counting this update): one persistent launch over all tensors (a
+/* One TurboAdam step over `count` tensors sharing hyper, config and step (1 to
+ * 2^32 - 1, counting this update; PA_ERR_ARG outside): one persistent launch over all tensors (a
  * wavefront per 256 values), then one workgroup per UState tensor that
  * reduces its residual sums and rotates its scales.  `states` is a host
  * array of count descriptors; `workspace` a device buffer of at least

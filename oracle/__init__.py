@@ -81,9 +81,8 @@ def _load():
     lib.oracle_clip_scale.restype = ctypes.c_float
     lib.oracle_scale_grads.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_float, _f32p, ctypes.c_size_t]
     lib.oracle_scale_grads.restype = None
-    _u64p = ctypes.POINTER(ctypes.c_uint64)
-    lib.oracle_philox4x64.argtypes = [_u64p, _u64p, _u64p]
-    lib.oracle_philox4x64.restype = None
+    lib.oracle_philox4x32.argtypes = [_u32p, _u32p, _u32p]
+    lib.oracle_philox4x32.restype = None
     lib.oracle_turbo_state_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t]
     lib.oracle_turbo_state_bytes.restype = ctypes.c_size_t
     vp = ctypes.c_void_p
@@ -268,13 +267,12 @@ def scale_grads(gdt, g, scale):
     return out
 
 
-def philox4x64(counter, key):
-    """Philox4x64-10 of a 4-word counter and a 2-word key (four uint64 words)."""
-    c = np.array(counter, np.uint64)
-    k = np.array(key, np.uint64)
-    out = np.zeros(4, np.uint64)
-    u64 = ctypes.POINTER(ctypes.c_uint64)
-    _load().oracle_philox4x64(c.ctypes.data_as(u64), k.ctypes.data_as(u64), out.ctypes.data_as(u64))
+def philox4x32(counter, key):
+    """Philox4x32-10 of a 4-word counter and a 2-word key (four uint32 words)."""
+    c = np.array(counter, np.uint32)
+    k = np.array(key, np.uint32)
+    out = np.zeros(4, np.uint32)
+    _load().oracle_philox4x32(_ptr(c, _u32p), _ptr(k, _u32p), _ptr(out, _u32p))
     return out
 
 

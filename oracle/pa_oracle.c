@@ -26,7 +26,7 @@
  *
  *  - The gradient pre-pass (exact sum of squares, non-finite count, clip
  *    coefficient) and the TurboAdam compressed state (UState first moment,
- *    1Q second moment, Philox4x64-10 draws): see their sections below,
+ *    1Q second moment, Philox4x32-10 draws): see their sections below,
  *    each with its own readings.
  *
  * Readings where the pages are silent (kept here as named constants):
@@ -655,44 +655,54 @@ void oracle_scale_grads(int gdt, const void* g, float scale, float* out, size_t 
  *  The residual sum of squares is a perfect pairwise tree, in double, over
  *    r^2 in index order padded with zeros to a power of two; after the
  *    step s_dec <- s_enc, s_enc <- RN32(factor * sqrt(sum / n)), acc <- 0.
- *  Random numbers: Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11) with
- *    key (seed, tensor id) and counter (j, step, 0, 0) for the values
- *    4j..4j+3: the high 24 bits of word k give the 1Q draw of value 4j+k;
- *    bits 8..31 of words 0 and 1 give the UState draws of the pairs
- *    (4j, 4j+1) and (4j+2, 4j+3).  A draw is those 24 bits times 2^-24. */
+ *  Random numbers: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11), the
+ *    counter-based generator Triton builds in, so the counter hash that a
+ *    PyTorch path and a Triton path can share.  Key (low and high 32 bits of
+ *    the seed); counter (j, step, tensor id, stream) for the values
+ *    4j..4j+3, with j and step taken modulo 2^32.  Stream 0: the high 24
+ *    bits of word k give the 1Q draw of value 4j+k.  Stream 1: the high 24
+ *    bits of words 0 and 1 give the UState draws of the pairs (4j, 4j+1)
+ *    and (4j+2, 4j+3).  A draw is those 24 bits times 2^-24. */
 
 #define T_GROUP 64
 #define T_BLOCK 128
 
-static void philox4x64_10(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4]) {
-    uint64_t x0 = ctr[0], x1 = ctr[1], x2 = ctr[2], x3 = ctr[3];
-    uint64_t k0 = key[0], k1 = key[1];
+/* Ten rounds of the Philox-4x32 bijection.  A round multiplies words 0 and 2
+ * by the two round multipliers, xors each product's high half with the other
+ * odd word and a key word, and permutes; the key is bumped by the two Weyl
+ * constants before every round but the first. */
+static void philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+    uint32_t x0 = ctr[0], x1 = ctr[1], x2 = ctr[2], x3 = ctr[3];
+    uint32_t k0 = key[0], k1 = key[1];
     for (int r = 0; r < 10; ++r) {
         if (r) {
-            k0 += 0x9E3779B97F4A7C15ull;
-            k1 += 0xBB67AE8584CAA73Bull;
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
         }
-        unsigned __int128 p0 = (unsigned __int128)0xD2E7470EE14C6C93ull * x0;
-        unsigned __int128 p1 = (unsigned __int128)0xCA5A826395121157ull * x2;
-        uint64_t hi0 = (uint64_t)(p0 >> 64), lo0 = (uint64_t)p0;
-        uint64_t hi1 = (uint64_t)(p1 >> 64), lo1 = (uint64_t)p1;
-        uint64_t n0 = hi1 ^ x1 ^ k0, n2 = hi0 ^ x3 ^ k1;
+        uint64_t p0 = (uint64_t)0xD2511F53u * x0;
+        uint64_t p1 = (uint64_t)0xCD9E8D57u * x2;
+        uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+        uint32_t n0 = hi1 ^ x1 ^ k0, n2 = hi0 ^ x3 ^ k1;
         x0 = n0; x1 = lo1; x2 = n2; x3 = lo0;
     }
     out[0] = x0; out[1] = x1; out[2] = x2; out[3] = x3;
 }
 
-void oracle_philox4x64(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4]) {
-    philox4x64_10(ctr, key, out);
+void oracle_philox4x32(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+    philox4x32_10(ctr, key, out);
 }
 
 /* The draws of values 4j..4j+3: q1[k] for 1Q, us[0..1] for the UState pairs. */
 static void turbo_draws(unsigned long long seed, uint32_t tensor_id, long long step, size_t j,
                         float q1[4], float us[2]) {
-    uint64_t ctr[4] = {(uint64_t)j, (uint64_t)step, 0, 0}, key[2] = {seed, tensor_id}, w[4];
-    philox4x64_10(ctr, key, w);
-    for (int k = 0; k < 4; ++k) q1[k] = (float)(w[k] >> 40) * 0x1p-24f;
-    for (int k = 0; k < 2; ++k) us[k] = (float)((w[k] & 0xFFFFFFFFu) >> 8) * 0x1p-24f;
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t ctr[4] = {(uint32_t)j, (uint32_t)step, tensor_id, 0u}, w[4];
+    philox4x32_10(ctr, key, w);
+    for (int k = 0; k < 4; ++k) q1[k] = (float)(w[k] >> 8) * 0x1p-24f;
+    ctr[3] = 1u;
+    philox4x32_10(ctr, key, w);
+    for (int k = 0; k < 2; ++k) us[k] = (float)(w[k] >> 8) * 0x1p-24f;
 }
 
 /* fp16 value of x rounded toward -Inf (dir < 0) or +Inf (dir > 0), as bits:

@@ -251,6 +251,10 @@ def test_turbo_argument_rules(pa):
     assert call(h, pa.TurboConfig(3, 1.1, 1)) == pa.PA_ERR_ARG            # index width
     assert call(h, pa.TurboConfig(4, 0.0, 1)) == pa.PA_ERR_ARG            # scale factor
     assert call(h, cfg, step=0) == pa.PA_ERR_ARG
+    assert call(h, cfg, step=2 ** 32) == pa.PA_ERR_ARG                    # the draws' 32-bit step word
+    N[0] = 2 ** 34 + 4                                                    # the draws' 32-bit index word
+    assert call(h, cfg) == pa.PA_ERR_ARG
+    N[0] = 4096
     hb = _hyper(pa, beta1=0.99, beta2=0.98)                               # beta1^2 >= beta2 with UState
     assert call(hb, cfg) == pa.PA_ERR_ARG
     assert pa.pa_turbo_state_bytes(1, 1, 4, 131072) == 106508
