@@ -87,14 +87,25 @@ __device__ __forceinline__ uint32_t f16_encode(float x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
-// bfloat16, round to nearest even on the bit pattern (a carry out of the
-// mantissa moves to the next binade and past the largest finite value to
-// Inf); NaN becomes a quiet NaN with the input's sign.
+// bfloat16, round to nearest even: the bit pattern plus 0x7FFF plus its own
+// bit 16, shifted down (a carry out of the mantissa moves to the next binade
+// and past the largest finite value to Inf; binary32 subnormals round like
+// any other pattern); NaN stays a quiet NaN with the input's sign and top
+// payload bits.  gfx950's conversion instruction computes exactly this with
+// the FP32 denormals this library keeps; the tests compare it with the
+// oracle's bfloat16 rounding on every binary32 bit pattern.
 __device__ __forceinline__ uint32_t bf16_encode(float x) {
-  const uint32_t b = __float_as_uint(x);
-  const uint32_t rounded = (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
-  const uint32_t qnan = (b >> 16) | 0x0040u;
-  return (b & 0x7FFFFFFFu) > kInfBits ? qnan : rounded;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// Two values in one word, `lo` in the low half (one conversion instruction).
+__device__ __forceinline__ uint32_t bf16_encode2(float lo, float hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  f2 v;
+  v.x = lo;
+  v.y = hi;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
 }
 
 }  // namespace pa

@@ -401,31 +401,11 @@ constexpr int kMidPad = 260;
 
 __device__ __forceinline__ uint32_t bucket_of(float x) { return __float_as_uint(x) >> kBucketShift; }
 
-// Smallest and largest float of bucket b.
-__device__ __forceinline__ float bucket_lo(uint32_t b) {
-  return __uint_as_float(b < (uint32_t)kBuckets / 2 ? b << kBucketShift : ((b + 1) << kBucketShift) - 1u);
-}
-__device__ __forceinline__ float bucket_hi(uint32_t b) {
-  return __uint_as_float(b < (uint32_t)kBuckets / 2 ? ((b + 1) << kBucketShift) - 1u : b << kBucketShift);
-}
-
 // The numerically next bucket (kBuckets, a pad of 255, after the last
 // positive one; the first positive one after the smallest negative one).
 __device__ __forceinline__ uint32_t bucket_next(uint32_t b) {
   constexpr uint32_t h = (uint32_t)kBuckets / 2;
   return b + 1 < h ? b + 1 : (b + 1 == h ? (uint32_t)kBuckets : (b == h ? 0u : b - 1));
-}
-
-// Number of sorted midpoints (mid[0..254]) below x, or at most x.
-__device__ __forceinline__ uint32_t count_below(const float* mid, float x, bool or_equal) {
-  uint32_t lo = 0, n = 255;
-  while (n > 0) {
-    const uint32_t half = n >> 1;
-    const float m = mid[lo + half];
-    const bool take = or_equal ? (m <= x) : (m < x);
-    if (take) { lo += half + 1; n -= half + 1; } else { n = half; }
-  }
-  return lo;
 }
 
 template <int NCMP>
@@ -506,30 +486,80 @@ struct MapTables {
   uint8_t base[kBuckets + 4];
 };
 
+// The bucket table as a histogram and one scan: each midpoint adds one to
+// its bucket's byte counter (four counters per LDS word; at most 255
+// midpoints, so no counter carries into the next), and an exclusive scan in
+// numeric bucket order (the negative buckets from the most negative, then
+// the positive ones) turns the counts into base[].  A midpoint of -0 counts
+// with +0: it compares like +0 with every value.  NaN midpoints (outside the
+// ascending-map contract) are never below a value and are not counted.
+// Thread t owns the 32 buckets of numeric positions 32t..32t+31, so the two
+// halves of the workgroup scan the two signs and each wavefront's order is
+// uniform.
 __device__ __forceinline__ void build_map(const float* lut, MapTables& t, uint32_t* red, int& ncmp, bool& guard) {
-  const int tid = threadIdx.x;
+  static_assert(kThreads == 256 && kBuckets == 32 * kThreads, "one thread per 32 buckets");
+  const int tid = threadIdx.x, lane = tid & 63;
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(t.base);
   for (int j = tid; j < kMidPad; j += kThreads)
     t.mid[j] = j < 255 ? (lut[j] + lut[j + 1]) * 0.5f : __builtin_inff();
+  for (int w = tid; w < (kBuckets + 4) / 4; w += kThreads) cnt[w] = 0u;
   __syncthreads();
-  uint32_t fullest = 0, near_zero = 0;
-  for (int b = tid; b < kBuckets; b += kThreads) {
-    const float lo = bucket_lo((uint32_t)b);
-    const float hi = bucket_hi((uint32_t)b);
-    const uint32_t below = count_below(t.mid, lo, false), upto = count_below(t.mid, hi, true);
-    t.base[b] = (uint8_t)below;
-    fullest = max(fullest, upto > below ? upto - below : 0u);
+  uint32_t near_zero = 0;
+  if (tid < 255) {
+    const float m = t.mid[tid];
+    near_zero = __builtin_fabsf(m) < 0x1p-125f ? 1u : 0u;
+    if (m == m) {
+      const uint32_t b = __float_as_uint(m) == 0x80000000u ? 0u : bucket_of(m);
+      atomicAdd(&cnt[b >> 2], 1u << (8 * (b & 3u)));
+    }
   }
-  if (tid < 4) t.base[kBuckets + tid] = 255;
-  for (int j = tid; j < 255; j += kThreads) near_zero |= __builtin_fabsf(t.mid[j]) < 0x1p-125f ? 1u : 0u;
+  __syncthreads();
+  const bool neg = tid < kThreads / 2;
+  const uint32_t w0 = neg ? (uint32_t)(kBuckets - 32 * (tid + 1)) / 4 : (uint32_t)(32 * (tid - kThreads / 2)) / 4;
+  uint32_t words[8], total = 0, fullest = 0;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) words[q] = cnt[w0 + q];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const uint32_t c = (words[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+    total += c;
+    fullest = max(fullest, c);
+  }
+  uint32_t incl = total;                           // inclusive scan over the wavefront
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = (uint32_t)__shfl_up((int)incl, d, 64);
+    incl += lane >= d ? y : 0u;
+  }
   fullest = wave_max_u32(fullest);
   near_zero = wave_max_u32(near_zero);
-  if ((tid & 63) == 0) red[tid >> 6] = fullest | (near_zero << 31);
+  if (lane == 63) red[tid >> 6] = incl | (fullest << 12) | (near_zero << 31);
   __syncthreads();
-  uint32_t f = 0, nz = 0;
+  uint32_t run = incl - total, f = 0, nz = 0;
+#pragma unroll
   for (int w = 0; w < kThreads / 64; ++w) {
-    f = max(f, red[w] & 0x7FFFFFFFu);
-    nz |= red[w] >> 31;
+    const uint32_t r = red[w];
+    run += w < (tid >> 6) ? (r & 0xFFFu) : 0u;
+    f = max(f, (r >> 12) & 0xFFFu);
+    nz |= r >> 31;
   }
+  uint32_t out[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (neg) {                                       // numeric order runs down the bucket index
+#pragma unroll
+    for (int k = 31; k >= 0; --k) {
+      out[k >> 2] |= run << (8 * (k & 3));
+      run += (words[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      out[k >> 2] |= run << (8 * (k & 3));
+      run += (words[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) cnt[w0 + q] = out[q];
+  if (tid == 0) cnt[kBuckets / 4] = 0xFFFFFFFFu;   // base[kBuckets..+3] = 255
   guard = nz != 0;
   ncmp = f == 0 ? 1 : (f <= 4 ? (int)f : 0);
   __syncthreads();
@@ -579,7 +609,7 @@ blockwise_kernel(BlockwiseArgs a, Scalars s, unsigned long long* nonfinite) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const long long e0 = base + h * 1024 + tid * 4;
-      uint32_t bf[4];
+      float po[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const float m = lut_m[(cur.mc[h] >> (8 * k)) & 0xFFu] * am;
@@ -587,11 +617,11 @@ blockwise_kernel(BlockwiseArgs a, Scalars s, unsigned long long* nonfinite) {
         float p1;
         adamw(cur.p[h][k], cur.g[h][k] * s.gmul, s.beta1 * m, v, s, p1, m1[h * 4 + k], v1[h * 4 + k]);
         bad += nonfinite3(p1, m1[h * 4 + k], v1[h * 4 + k]);
-        bf[k] = bf16_encode(p1);
+        po[k] = p1;
       }
       uint2 out;
-      out.x = bf[0] | (bf[1] << 16);
-      out.y = bf[2] | (bf[3] << 16);
+      out.x = bf16_encode2(po[0], po[1]);
+      out.y = bf16_encode2(po[2], po[3]);
       *reinterpret_cast<uint2*>(a.p_out + e0) = out;
     }
     // Block absmax: on non-negative floats (and NaN with the sign cleared)
@@ -784,11 +814,17 @@ codec_kernel(int lane_kind, int dir, const void* in, void* out, long long n) {
   for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < n; i += (long long)gridDim.x * kThreads) {
     if (dir == 0) {
       const float x = static_cast<const float*>(in)[i];
-      uint32_t c = lane_kind == 0 ? e4_encode_m(x) : lane_kind == 1 ? e4_encode_r(x) : f16_encode(x);
+      uint32_t c = lane_kind == 0   ? e4_encode_m(x)
+                   : lane_kind == 1 ? e4_encode_r(x)
+                   : lane_kind == 2 ? f16_encode(x)
+                                    : bf16_encode(x);
       static_cast<uint16_t*>(out)[i] = (uint16_t)c;
     } else {
       const uint32_t c = static_cast<const uint16_t*>(in)[i];
-      float x = lane_kind == 0 ? e4_decode_m(c) : lane_kind == 1 ? e4_decode_r(c << 16) : f16_decode(c);
+      float x = lane_kind == 0   ? e4_decode_m(c)
+                : lane_kind == 1 ? e4_decode_r(c << 16)
+                : lane_kind == 2 ? f16_decode(c)
+                                 : __uint_as_float(c << 16);
       static_cast<float*>(out)[i] = x;
     }
   }

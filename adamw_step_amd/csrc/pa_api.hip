@@ -1046,7 +1046,7 @@ void pa_release_plans(void) {
 }
 
 int pa_debug_codec(int lane, int dir, const void* in, void* out, size_t n, void* stream) {
-  if (lane < 0 || lane > 2 || dir < 0 || dir > 1) return PA_ERR_ARG;
+  if (lane < 0 || lane > 3 || dir < 0 || dir > 1) return PA_ERR_ARG;
   if (n == 0) return PA_OK;
   if (in == nullptr || out == nullptr) return PA_ERR_ARG;
   if (!aligned(in, dir == 0 ? 4 : 2) || !aligned(out, dir == 0 ? 2 : 4)) return PA_ERR_ALIGN;

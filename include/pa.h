@@ -312,7 +312,8 @@ int pa_last_hip_error(void);
 void pa_release_plans(void);
 
 /* Codec self-test export: apply one lane codec of the GPU path to n device
- * values.  lane 0 = E4M11 first moment, 1 = E4M12 RMS, 2 = binary16.
+ * values.  lane 0 = E4M11 first moment, 1 = E4M12 RMS, 2 = binary16,
+ * 3 = bfloat16 (the 16-bit parameter and blockwise output rounding).
  * dir 0 encodes float -> uint16 (in: float*, out: uint16_t*), dir 1 decodes
  * uint16 -> float.  Device pointers, asynchronous on `stream`.  Used by the
  * tests to check every code of every lane on the device. */

@@ -134,7 +134,8 @@ def test_list_argument_rules(pa):
 
 def test_debug_codec_rules(pa):
     L = pa.lib()
-    assert L.pa_debug_codec(3, 0, FAKE, FAKE + 4096, 4, None) == pa.PA_ERR_ARG
+    assert L.pa_debug_codec(4, 0, FAKE, FAKE + 4096, 4, None) == pa.PA_ERR_ARG
+    assert L.pa_debug_codec(-1, 0, FAKE, FAKE + 4096, 4, None) == pa.PA_ERR_ARG
     assert L.pa_debug_codec(0, 2, FAKE, FAKE + 4096, 4, None) == pa.PA_ERR_ARG
     assert L.pa_debug_codec(0, 0, FAKE + 2, FAKE + 4096, 4, None) == pa.PA_ERR_ALIGN
     assert L.pa_debug_codec(0, 0, None, None, 0, None) == pa.PA_OK

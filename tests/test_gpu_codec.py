@@ -40,7 +40,7 @@ def _binade(e):
     return ((np.uint32((e + 127) << 23)) + np.arange(1 << 23, dtype=np.uint32)).view(np.float32)
 
 
-@pytest.mark.parametrize("lane", [0, 1, 2])
+@pytest.mark.parametrize("lane", [0, 1, 2, 3])
 def test_decode_every_code(pa, lane):
     banner(f"decode all codes lane {lane}")
     codes = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
@@ -81,6 +81,32 @@ def test_decode_encode_identity_on_device(pa, lane):
     codes = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
     back = _encode_gpu(pa, lane, _decode_gpu(pa, lane, codes))
     np.testing.assert_array_equal(back, codes)
+
+
+def test_bf16_encode_every_float(pa):
+    """The GPU's bfloat16 rounding (gfx950's conversion instruction, used for
+    16-bit parameters, the blockwise output and TurboAdam's group means)
+    equals the oracle's nearest-even bfloat16 on all 2^32 bit patterns; NaN
+    stays NaN with its sign."""
+    import torch
+    chunk = 1 << 28
+    bad = 0
+    for c in range(1 << 4):
+        banner(f"bf16 encode chunk {c}/16")
+        bits = torch.arange(c * chunk, (c + 1) * chunk, dtype=torch.int64, device="cuda:0")
+        x = bits.to(torch.int32).view(torch.float32)        # wraps to the bit pattern
+        out = torch.empty(chunk, dtype=torch.int16, device="cuda:0")
+        pa.pa_debug_codec(3, 0, x, out)
+        torch.cuda.synchronize()
+        hx = to_host(x)
+        got = to_host(out, np.uint16)
+        want = oracle.encode(3, hx)
+        nan = np.isnan(hx)
+        bad += int((got[~nan] != want[~nan]).sum())
+        assert np.all(((got[nan] & 0x7F80) == 0x7F80) & ((got[nan] & 0x7F) != 0))
+        assert np.array_equal(got[nan] >> 15, want[nan] >> 15)
+        del bits, x, out
+    assert bad == 0, f"{bad} bfloat16 roundings differ from the oracle"
 
 
 def test_sqrt_every_float(pa):
