@@ -86,7 +86,7 @@ class Format(ctypes.Structure):
 
 EXPORTS = ("pa_step", "pa_step_list", "pa_step_typed", "pa_step_list_typed", "pa_state_bytes",
            "pa_format_info", "pa_status_string", "pa_last_hip_error", "pa_release_plans", "pa_debug_codec",
-           "pa_debug_sqrt", "pa_grad_stats_list", "pa_turbo_state_bytes", "pa_turbo_workspace_bytes",
+           "pa_debug_sqrt", "pa_debug_q1_ends", "pa_grad_stats_list", "pa_turbo_state_bytes", "pa_turbo_workspace_bytes",
            "pa_turbo_step_list")
 
 PA_DT_F32, PA_DT_BF16, PA_DT_F16 = 0, 1, 2
@@ -129,6 +129,8 @@ def lib():
     L.pa_debug_codec.restype = ctypes.c_int
     L.pa_debug_sqrt.argtypes = [vp, vp, sz, vp]
     L.pa_debug_sqrt.restype = ctypes.c_int
+    L.pa_debug_q1_ends.argtypes = [vp, vp, sz, vp]
+    L.pa_debug_q1_ends.restype = ctypes.c_int
     L.pa_grad_stats_list.argtypes = [ctypes.c_int, sz, ctypes.POINTER(vp), ctypes.POINTER(sz), ctypes.c_double,
                                      vp, vp, vp, vp]
     L.pa_grad_stats_list.restype = ctypes.c_int
@@ -408,6 +410,16 @@ def pa_debug_sqrt(inp, out, stream=None):
     if inp.numel() != out.numel():
         raise ValueError("input and output sizes differ")
     _check(lib().pa_debug_sqrt(_ptr(inp), _ptr(out), inp.numel(), _stream(stream)))
+
+
+def pa_debug_q1_ends(inp, out, stream=None):
+    """out (int32, bit pattern) = the two 1Q endpoints of each positive float32
+    in inp: binary16 of log2 rounded down (low half) and up (high half)."""
+    _tensor_ok(inp, "input")
+    _tensor_ok(out, "output")
+    if inp.numel() != out.numel() or out.element_size() != 4:
+        raise ValueError("output must hold one 32-bit word per input")
+    _check(lib().pa_debug_q1_ends(_ptr(inp), _ptr(out), inp.numel(), _stream(stream)))
 
 
 # ---------------------------------------------------------------- TurboAdam

@@ -1062,6 +1062,21 @@ int pa_debug_codec(int lane, int dir, const void* in, void* out, size_t n, void*
   return e == hipSuccess ? PA_OK : hip_failed(e);
 }
 
+int pa_debug_q1_ends(const float* in, uint32_t* out, size_t n, void* stream) {
+  if (n == 0) return PA_OK;
+  if (in == nullptr || out == nullptr) return PA_ERR_ARG;
+  if (!aligned(in, 4) || !aligned(out, 4)) return PA_ERR_ALIGN;
+  int dev;
+  DeviceInfo d;
+  int rc = device_info(&dev, &d);
+  if (rc) return rc;
+  const long long blocks = ((long long)n + pa::kThreads - 1) / pa::kThreads;
+  const dim3 grid((unsigned)grid_for(blocks, d, d.blocks_per_cu)), block(pa::kThreads);
+  hipLaunchKernelGGL(pa::q1_ends_kernel, grid, block, 0, static_cast<hipStream_t>(stream), in, out, (long long)n);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PA_OK : hip_failed(e);
+}
+
 int pa_debug_sqrt(const float* in, float* out, size_t n, void* stream) {
   if (n == 0) return PA_OK;
   if (in == nullptr || out == nullptr) return PA_ERR_ARG;

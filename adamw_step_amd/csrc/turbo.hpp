@@ -135,6 +135,55 @@ __device__ __forceinline__ uint32_t f16_directed_dev(double x, bool up) {
 
 __device__ __forceinline__ double f16_to_double(uint32_t h) { return (double)f16_decode(h); }
 
+// One binary16 step up or down in value from pattern h (not +-Inf, not -0);
+// a zero result is +0.  The magnitude grows when the direction and the sign
+// agree; a step down from +0 lands on the smallest negative subnormal.
+// Written as selects: `up` differs between lanes.
+__device__ __forceinline__ uint32_t f16_step(uint32_t h, bool up) {
+  const uint32_t grow = (up ? 1u : 0u) ^ (h >> 15);
+  uint32_t r = h + (grow ? 1u : 0xFFFFFFFFu);
+  r = ((h & 0x7FFFu) == 0u && !up) ? 0x8001u : r;
+  return r == 0x8000u ? 0u : r;
+}
+
+// x rounded to binary16 toward -Inf (up = false) or +Inf (up = true), for
+// |x| far inside the binary16 range: the nearest-even conversion, moved one
+// step when it landed on the wrong side of x; a zero result is +0 (as
+// f16_directed_dev).
+__device__ __forceinline__ uint32_t f16_directed_f32(float x, bool up) {
+  uint32_t h = f16_encode(x);
+  h = h == 0x8000u ? 0u : h;
+  const float hv = f16_decode(h);
+  const bool wrong = (hv < x && up) || (hv > x && !up);
+  const uint32_t stepped = f16_step(h, up);
+  return wrong ? stepped : h;
+}
+
+// The exact endpoint through the double log2 (out of line, as build_levels).
+__device__ __attribute__((noinline)) uint32_t log2_directed16_exact(float v, bool up) {
+  return f16_directed_dev(log2((double)v), up);
+}
+
+// A 1Q endpoint: log2(v) rounded to binary16 down (up = false) or up, for a
+// positive finite v.  The hardware log2 (v below 2^-64 scaled by 2^64 first)
+// is within one binary32 ulp of log2(v) for every positive binary32, which
+// was measured on gfx950 against the double log2 over all of them.  So
+// log2(v) lies in [y - d, y + d] with d = |y| 2^-21 + 2^-60 (four times that
+// bound, which also covers the rounding of y - 64 and of the interval ends),
+// and when both ends round to the same binary16 value, so does log2(v), and
+// so does any double within 2^-52 of it.  Otherwise (a binary16 point inside
+// the interval: about one value in a thousand, and every power of two) the
+// double log2 decides, on the lanes that are `active`.
+__device__ __forceinline__ uint32_t log2_directed16(float v, bool up, bool active) {
+  const bool small = v < 0x1p-64f;
+  float y = __builtin_amdgcn_logf(small ? v * 0x1p64f : v);
+  y = small ? y - 64.0f : y;
+  const float d = __builtin_fabsf(y) * 0x1p-21f + 0x1p-60f;
+  const uint32_t a = f16_directed_f32(y - d, up), b = f16_directed_f32(y + d, up);
+  if (active && a != b) return log2_directed16_exact(v, up);
+  return a;
+}
+
 // Level k of a 1Q block, in double then rounded once to binary32.
 __device__ __forceinline__ float q1_level(double lo, double hi, int k, int L) {
   if (k == 0) return 0.0f;
@@ -142,8 +191,13 @@ __device__ __forceinline__ float q1_level(double lo, double hi, int k, int L) {
   return (float)exp2(x);
 }
 
+// The double-precision exp2 and log2 below are called out of line on
+// purpose: inlined, their polynomial coefficients were hoisted out of the
+// tile loop into about 40 vector registers held for the whole kernel, which
+// cut occupancy from 7 to 4 wavefronts per SIMD; a call per table costs a
+// few instructions against thousands per tile.
 template <int BITS>
-__device__ __forceinline__ void build_levels(float* lev, uint32_t ends, int lane_in_half) {
+__device__ __attribute__((noinline)) void build_levels(float* lev, uint32_t ends, int lane_in_half) {
   constexpr int L = 1 << BITS;
   const double lo = f16_to_double(ends & 0xFFFFu), hi = f16_to_double(ends >> 16);
   for (int k = lane_in_half; k < L; k += 32) lev[k] = q1_level(lo, hi, k, L);
@@ -323,10 +377,10 @@ __device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, lo
       hi_c = pos ? fmaxf(hi_c, v) : hi_c;
     }
     const float vmin = butterfly_min<32>(lo_c), vmax = butterfly_max<32>(hi_c);
-    // Endpoints: lanes 0 and 1 of each half take log2 of the minimum and of
-    // the maximum (one pass of the double log2 for both), then broadcast.
-    const double lg = log2((double)(lane_in_half == 0 ? vmin : vmax));
-    const uint32_t e16 = f16_directed_dev(lg, lane_in_half != 0);
+    // Endpoints: lanes 0 and 1 of each half round log2 of the minimum down
+    // and of the maximum up (one pass for both), then broadcast.
+    const bool ends_lane = lane_in_half < 2 && vmax > 0.0f;
+    const uint32_t e16 = log2_directed16(lane_in_half == 0 ? vmin : vmax, lane_in_half != 0, ends_lane);
     const int src = half << 5;
     const uint32_t lo16 = (uint32_t)__shfl((int)e16, src, 64), hi16 = (uint32_t)__shfl((int)e16, src + 1, 64);
     const uint32_t ends = vmax > 0.0f ? (lo16 | (hi16 << 16)) : 0u;
@@ -491,6 +545,15 @@ turbo_reduce(const TurboReduceEntry* __restrict__ list, double* ws, double facto
     r.scal[0] = s_enc;
     r.scal[1] = (float)(factor * __builtin_sqrt(total / (double)r.n));
     r.scal[2] = 0.0f;
+  }
+}
+
+// Self-test of the endpoint rounding: for each positive finite in[i], the
+// two endpoints of a one-value block, low half down, high half up.
+__global__ void __launch_bounds__(kThreads) q1_ends_kernel(const float* in, uint32_t* out, long long n) {
+  for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < n; i += (long long)gridDim.x * kThreads) {
+    const float v = in[i];
+    out[i] = log2_directed16(v, false, true) | (log2_directed16(v, true, true) << 16);
   }
 }
 

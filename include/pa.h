@@ -325,6 +325,13 @@ int pa_debug_codec(int lane, int dir, const void* in, void* out, size_t n, void*
  * the tests compare it with the host's IEEE square root on every float. */
 int pa_debug_sqrt(const float* in, float* out, size_t n, void* stream);
 
+/* 1Q endpoint self-test export: for n positive finite device floats in[i],
+ * out[i] = binary16 of log2(in[i]) rounded down (low 16 bits) and up (high
+ * 16 bits), as the TurboAdam step computes a block's endpoints (TurboAdam
+ * package page, 1Q).  The tests compare it with the oracle on every
+ * positive binary32.  Asynchronous on `stream`. */
+int pa_debug_q1_ends(const float* in, uint32_t* out, size_t n, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

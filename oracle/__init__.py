@@ -92,6 +92,8 @@ def _load():
     lib.oracle_turbo_step.restype = ctypes.c_ulonglong
     lib.oracle_q1_levels.argtypes = [ctypes.c_uint16, ctypes.c_uint16, ctypes.c_int, _f32p]
     lib.oracle_q1_levels.restype = None
+    lib.oracle_q1_ends_batch.argtypes = [_f32p, _u32p, ctypes.c_size_t]
+    lib.oracle_q1_ends_batch.restype = None
     lib.oracle_q1_block.argtypes = [_f32p, ctypes.c_size_t, ctypes.c_int, _f32p, _u8p, _u16p, _f32p]
     lib.oracle_q1_block.restype = None
     lib.oracle_ustate_group.argtypes = [_f32p, ctypes.c_size_t, ctypes.c_float, _f32p, _u8p, _u16p,
@@ -324,6 +326,15 @@ def q1_levels(lo16, hi16, bits):
     out = np.zeros(1 << bits, np.float32)
     _load().oracle_q1_levels(int(lo16), int(hi16), int(bits), _ptr(out, _f32p))
     return out
+
+
+def q1_ends(v):
+    """(RD16(log2 v), RU16(log2 v)) as binary16 bit patterns, for each
+    positive finite float32 v: the endpoints of a one-value 1Q block."""
+    v = np.ascontiguousarray(v, np.float32)
+    out = np.empty(v.size, np.uint32)
+    _load().oracle_q1_ends_batch(_ptr(v, _f32p), _ptr(out, _u32p), v.size)
+    return (out & 0xFFFF).astype(np.uint16), (out >> 16).astype(np.uint16)
 
 
 def q1_block(v, bits, u):

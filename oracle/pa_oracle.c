@@ -746,6 +746,18 @@ static double pairwise_sum(const double* a, size_t n) {   /* n a power of two */
     return pairwise_sum(a, n / 2) + pairwise_sum(a + n / 2, n / 2);
 }
 
+/* The two 1Q endpoints a one-value block holding v would get, for n values
+ * (tests): low half RD16(log2 v), high half RU16(log2 v). */
+void oracle_q1_ends_batch(const float* v, uint32_t* out, size_t n) {
+    build_tables();
+    ptrdiff_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < (ptrdiff_t)n; ++i) {
+        const double y = log2((double)v[i]);
+        out[i] = (uint32_t)f16_directed(y, -1) | ((uint32_t)f16_directed(y, +1) << 16);
+    }
+}
+
 /* The decoded values of a block's 2^bits indices. */
 void oracle_q1_levels(uint16_t lo16, uint16_t hi16, int bits, float* lev) {
     build_tables();

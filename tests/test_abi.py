@@ -139,6 +139,9 @@ def test_debug_codec_rules(pa):
     assert L.pa_debug_codec(0, 2, FAKE, FAKE + 4096, 4, None) == pa.PA_ERR_ARG
     assert L.pa_debug_codec(0, 0, FAKE + 2, FAKE + 4096, 4, None) == pa.PA_ERR_ALIGN
     assert L.pa_debug_codec(0, 0, None, None, 0, None) == pa.PA_OK
+    assert L.pa_debug_q1_ends(None, None, 0, None) == pa.PA_OK
+    assert L.pa_debug_q1_ends(None, FAKE, 4, None) == pa.PA_ERR_ARG
+    assert L.pa_debug_q1_ends(FAKE + 2, FAKE + 4096, 4, None) == pa.PA_ERR_ALIGN
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):

@@ -1,8 +1,9 @@
 """Full-size workloads, in the launch configuration the benchmark times,
 checked against the oracle on sampled outputs.
 
-  * llama-7b: 291 tensors, 6,738,415,616 parameters, packed E4, two steps of
-    one persistent launch each; sampled: every tensor's first and last 64 Ki
+  * llama-7b: 291 tensors, 6,738,415,616 parameters, in each elementwise
+    mode (packed E4, packed FP16, FP32), two steps of one persistent launch
+    each; sampled: every tensor's first and last 64 Ki
     elements plus a seeded 1/1024 of its 64 Ki-element tiles.  The step is
     elementwise, so the sampled inputs, gathered from the device before the
     step, determine the sampled outputs exactly.
@@ -42,38 +43,58 @@ def _sample_index(n, rng):
 
 
 @pytest.mark.timeout(900)
-def test_llama_7b_e4_sampled(pa):
+@pytest.mark.parametrize("mode", ["e4", "fp16", "fp32"])
+def test_llama_7b_sampled(pa, mode):
     import torch
     cfg = 4
     sizes = workloads.sizes(cfg)
-    banner(f"llama-7b: allocating {sum(sizes) * 12 / 1e9:.1f} GB")
+    state_bytes = 8 if mode == "fp32" else 4
+    banner(f"llama-7b {mode}: allocating {sum(sizes) * (8 + state_bytes) / 1e9:.1f} GB")
     ps = [torch.empty(n, dtype=torch.float32, device="cuda:0") for n in sizes]
     gs = [torch.empty(n, dtype=torch.float32, device="cuda:0") for n in sizes]
-    ws = [torch.zeros(n, dtype=torch.int32, device="cuda:0") for n in sizes]
+    if mode == "fp32":
+        ss = [(torch.zeros(n, dtype=torch.float32, device="cuda:0"), torch.zeros(n, dtype=torch.float32, device="cuda:0"))
+              for n in sizes]
+    else:
+        ss = [torch.zeros(n, dtype=torch.int32, device="cuda:0") for n in sizes]
+    code = {"fp32": 0, "e4": 1, "fp16": 2}[mode]
     workloads.device_fill_params(cfg, ps)
-    rng = np.random.Generator(np.random.PCG64(4242))
+    rng = np.random.Generator(np.random.PCG64(4242 + code))
     idx = [_sample_index(n, rng) for n in sizes]
     didx = [torch.from_numpy(i).to("cuda:0") for i in idx]
     total = sum(i.size for i in idx)
+
+    def gather_state(k):
+        if mode == "fp32":
+            return tuple(to_host(x[didx[k]]) for x in ss[k])
+        return to_host(ss[k][didx[k]], np.uint32)
+
     try:
         for t in (1, 2):
             workloads.device_fill_grads(cfg, t, gs)
             torch.cuda.synchronize()
             hp = [to_host(p[i]) for p, i in zip(ps, didx)]
             hg = [to_host(g[i]) for g, i in zip(gs, didx)]
-            hw = [to_host(w[i], np.uint32) for w, i in zip(ws, didx)]
-            banner(f"llama-7b step {t}: one persistent launch over 291 tensors")
-            pa.pa_step_list(1, ps, gs, ws, hyper(), t)
+            hs = [gather_state(k) for k in range(len(sizes))]
+            banner(f"llama-7b {mode} step {t}: one persistent launch over 291 tensors")
+            pa.pa_step_list(code, ps, gs, ss, hyper(), t)
             torch.cuda.synchronize()
             sc = scalars(t)
             same = 0
             for k in range(len(sizes)):
-                oracle.step_packed(1, hp[k], hg[k], hw[k], sc)
-                assert_words(to_host(ws[k][didx[k]], np.uint32), hw[k], what=f"tensor {k} words")
+                if mode == "fp32":
+                    m, v = hs[k]
+                    oracle.step_fp32(hp[k], hg[k], m, v, sc)
+                    gm, gv = gather_state(k)
+                    assert_words(gm, m, what=f"tensor {k} m")
+                    assert_words(gv, v, what=f"tensor {k} v")
+                else:
+                    oracle.step_packed(code, hp[k], hg[k], hs[k], sc)
+                    assert_words(gather_state(k), hs[k], fp16=mode == "fp16", what=f"tensor {k} words")
                 same += assert_params(to_host(ps[k][didx[k]]), hp[k], what=f"tensor {k} params")[0]
-            banner(f"llama-7b step {t}: {total} sampled elements, bit-identical params {same}")
+            banner(f"llama-7b {mode} step {t}: {total} sampled elements, bit-identical params {same}")
     finally:
-        del ps, gs, ws
+        del ps, gs, ss
         torch.cuda.empty_cache()
         pa.pa_release_plans()
 

@@ -173,3 +173,30 @@ def test_turbo_nonfinite_gradients(pa):
             else:
                 assert _same_f32(to_host(st.m_fp32), ho.m_fp32) and _same_f32(to_host(st.v_fp32), ho.v_fp32)
     assert int(counter.item()) == total_bad > 0
+
+
+def test_q1_endpoints_every_float(pa):
+    """A block's 1Q endpoints (binary16 of log2 rounded down and up, through
+    the hardware log2 with an exact fallback) equal the oracle's on every
+    positive finite binary32: one-value blocks over all 2^31 - 2^23 - 1."""
+    import torch
+    top = 0x7F800000
+    chunk = 1 << 27
+    bad = 0
+    for c in range((top + chunk - 1) // chunk):
+        lo_bits, hi_bits = max(1, c * chunk), min(top, (c + 1) * chunk)
+        banner(f"1Q endpoints chunk {c}: patterns {lo_bits:#x}..{hi_bits:#x}")
+        bits = torch.arange(lo_bits, hi_bits, dtype=torch.int64, device="cuda:0")
+        x = bits.to(torch.int32).view(torch.float32)
+        out = torch.empty(x.numel(), dtype=torch.int32, device="cuda:0")
+        pa.pa_debug_q1_ends(x, out)
+        torch.cuda.synchronize()
+        got = to_host(out).view(np.uint32)
+        lo, hi = oracle.q1_ends(to_host(x))
+        want = lo.astype(np.uint32) | (hi.astype(np.uint32) << 16)
+        diff = np.nonzero(got != want)[0]
+        bad += diff.size
+        assert diff.size == 0, (f"{diff.size} endpoint pairs differ, first at pattern "
+                                f"{lo_bits + int(diff[0]):#x}: {got[diff[0]]:#010x} vs {want[diff[0]]:#010x}")
+        del bits, x, out
+    assert bad == 0

@@ -297,3 +297,15 @@ def test_deterministic_and_counter_driven(oracle_mod):
         outs.append(st.v_index.copy())
     assert np.array_equal(outs[0], outs[1])
     assert not np.array_equal(outs[0], outs[2]) and not np.array_equal(outs[0], outs[3])
+
+
+def test_q1_ends_batch_is_one_value_block(oracle_mod):
+    """The batch endpoint routine the GPU test uses gives what a one-value
+    block gets from the block encoder, on specials and random floats."""
+    rng = np.random.default_rng(21)
+    v = np.concatenate([np.array([1.0, 2.0, 0.5, 3.0, 1e-45, 1.1754944e-38, 3.4028235e38], np.float32),
+                        (rng.integers(1, 0x7F800000, 300, dtype=np.int64)).astype(np.uint32).view(np.float32)])
+    lo, hi = oracle.q1_ends(v)
+    for k, x in enumerate(v):
+        _, ends, _ = oracle.q1_block(np.array([x], np.float32), 4, np.zeros(1, np.float32))
+        assert (int(ends[0]), int(ends[1])) == (int(lo[k]), int(hi[k])), x
