@@ -695,7 +695,10 @@ __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long x)
   return x;
 }
 
-template <int GT>
+// NT: nontemporal loads, for lists too large for the last-level cache (the
+// step that follows reads the gradients again; a list that fits the cache
+// keeps plain loads so that it stays there).
+template <int GT, bool NT>
 __device__ __forceinline__ void stats_tile(const Entry& e, long long tile, double& acc, uint32_t& bad) {
   using GE = Elem<GT>;
   using GV = typename GE::vec4;
@@ -704,13 +707,14 @@ __device__ __forceinline__ void stats_tile(const Entry& e, long long tile, doubl
   const int tid = threadIdx.x;
   const typename GE::scalar* g = static_cast<const typename GE::scalar*>(e.g);
   if (v0 >= e.phase && v0 + kTile <= vend) {
-    // The step reads these gradients right after: plain loads, so that a
-    // list that fits the last-level cache stays there.
     const GV* G = reinterpret_cast<const GV*>(g - e.phase);
     const long long q0 = v0 / 4 + tid;
     GV x[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) x[u] = G[q0 + (long long)u * kThreads];
+    for (int u = 0; u < kUnroll; ++u) {
+      const GV* a = G + q0 + (long long)u * kThreads;
+      x[u] = NT ? __builtin_nontemporal_load(a) : *a;
+    }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
@@ -726,7 +730,7 @@ __device__ __forceinline__ void stats_tile(const Entry& e, long long tile, doubl
   }
 }
 
-template <int GT>
+template <int GT, bool NT>
 __global__ void __launch_bounds__(kThreads)
 grad_stats_list(const Entry* __restrict__ table, long long total_tiles, double* part_sum,
                 unsigned long long* part_bad) {
@@ -738,7 +742,7 @@ grad_stats_list(const Entry* __restrict__ table, long long total_tiles, double* 
   for (long long tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
     while (tile >= table[t + 1].tile0) ++t;
     const Entry e = table[t];
-    stats_tile<GT>(e, tile - e.tile0, acc, bad);
+    stats_tile<GT, NT>(e, tile - e.tile0, acc, bad);
   }
   const int tid = threadIdx.x;
   acc = wave_sum_f64(acc);

@@ -103,7 +103,7 @@ int device_info(int* dev_out, DeviceInfo* info) {
     d.bw_blocks_per_cu = bw;
     int st = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &st, reinterpret_cast<const void*>(pa::grad_stats_list<pa::kF32>), pa::kThreads, 0);
+        &st, reinterpret_cast<const void*>(pa::grad_stats_list<pa::kF32, true>), pa::kThreads, 0);
     if (e != hipSuccess || st < 1) st = 4;
     d.stats_blocks_per_cu = st;
     int tb = 0;
@@ -418,12 +418,23 @@ std::vector<Range> merged(std::vector<Range> r) {
   return out;
 }
 
+// Gradient lists above this size read with nontemporal loads: the step that
+// follows would miss the last-level cache (256 MB on MI355X) for them anyway,
+// and streaming loads read HBM about 11% faster (7B list: 4.4 -> 3.95 ms).
+constexpr double kStatsStreamBytes = 128.0 * 1024 * 1024;
+
 template <int GT>
 hipError_t launch_stats(const Plan& pl, double max_norm, double* sumsq, unsigned long long* nonfinite,
                         float* clip, hipStream_t st) {
   if (pl.nparts > 0) {
-    hipLaunchKernelGGL((pa::grad_stats_list<GT>), dim3((unsigned)pl.nparts), dim3(pa::kThreads), 0, st, pl.table,
-                       pl.tiles, pl.part_sum, pl.part_bad);
+    const double bytes = (double)pl.tiles * pa::kTile * (GT == pa::kF32 ? 4 : 2);
+    const dim3 grid((unsigned)pl.nparts), block(pa::kThreads);
+    if (bytes > kStatsStreamBytes)
+      hipLaunchKernelGGL((pa::grad_stats_list<GT, true>), grid, block, 0, st, pl.table, pl.tiles, pl.part_sum,
+                         pl.part_bad);
+    else
+      hipLaunchKernelGGL((pa::grad_stats_list<GT, false>), grid, block, 0, st, pl.table, pl.tiles, pl.part_sum,
+                         pl.part_bad);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

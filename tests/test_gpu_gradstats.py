@@ -118,6 +118,46 @@ def test_stats_large_single_tensor(pa):
 
 
 @pytest.mark.parametrize("gdt", [0, 1, 2])
+def test_stats_streaming_list(pa, gdt):
+    """A list above 128 MiB of gradients, which the pre-pass reads with
+    nontemporal loads: the same exact-sum bound, the non-finite count, and a
+    repeat that gives the same bits."""
+    torch = _torch()
+    rng = np.random.default_rng(300 + gdt)
+    esz = 4 if gdt == 0 else 2
+    big = (160 << 20) // esz                     # 160 MiB in the first tensor
+    sizes = [big + 7, 3, 100003]
+    phases = [1, 0, 3]
+    hg = [_grads(rng, n, gdt) for n in sizes]
+    bad_at = [(0, 5), (0, big - 11), (2, 777)]
+    specials = {0: np.array([np.nan, np.inf, -np.inf], np.float32),     # NaN, +Inf, -Inf
+                1: np.array([0x7FC0, 0x7F80, 0xFF80], np.uint16),
+                2: np.array([0x7E00, 0x7C00, 0xFC00], np.uint16)}[gdt]
+    for k, (t, i) in enumerate(bad_at):
+        hg[t][i] = specials[k]
+    dg, _keep = _views(hg, phases, gdt)
+    s, nf, clip = _outs()
+    banner(f"grad stats streaming dtype {gdt}: {sum(sizes) * esz / 2**20:.0f} MiB")
+    pa.pa_grad_stats_list(dg, s, nf, clip, max_norm=1.0)
+    torch.cuda.synchronize()
+    want_s, want_nf, _ = oracle.grad_stats(gdt, hg, max_norm=1.0)
+    assert int(nf.item()) == want_nf == 3
+    assert math.isnan(float(s.item())) and math.isnan(want_s)
+    for t, i in bad_at:                          # finite again: the sum itself
+        hg[t][i] = 0
+    dg, _keep = _views(hg, phases, gdt)
+    pa.pa_grad_stats_list(dg, s, nf, clip, max_norm=1.0)
+    torch.cuda.synchronize()
+    want_s, want_nf, _ = oracle.grad_stats(gdt, hg, max_norm=1.0)
+    _check_sum(float(s.item()), want_s, sum(sizes), f"dtype {gdt} streaming sumsq")
+    assert int(nf.item()) == want_nf == 0
+    again = _outs()[0]
+    pa.pa_grad_stats_list(dg, again)
+    torch.cuda.synchronize()
+    assert again.item() == s.item()
+
+
+@pytest.mark.parametrize("gdt", [0, 1, 2])
 def test_stats_nonfinite(pa, gdt):
     torch = _torch()
     rng = np.random.default_rng(31)
