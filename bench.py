@@ -82,6 +82,10 @@ def probe_lib():
     L.pa_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
     L.pa_probe_stream5.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                    ctypes.c_int, ctypes.c_void_p]
+    L.pa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    L.pa_probe_write.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    L.pa_probe_mix.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                               ctypes.c_int, ctypes.c_void_p]
     return L
 
 
@@ -100,7 +104,7 @@ def time_probe(fn, reps):
     return sorted(ts)[len(ts) // 2]
 
 
-def run_probes(grid):
+def run_probes(grid, stream_bytes=0):
     import torch
     L = probe_lib()
     st = torch.cuda.current_stream().cuda_stream
@@ -117,8 +121,50 @@ def run_probes(grid):
     stream_gbps = 5 * nbytes / ms5 / 1e6
     del a, b, c
     torch.cuda.empty_cache()
-    return {"copy_gbps": round(copy_gbps, 1), "stream_3in_2out_gbps": round(stream_gbps, 1),
-            "bytes": nbytes, "grid": grid}
+    out = {"copy_gbps": round(copy_gbps, 1), "stream_3in_2out_gbps": round(stream_gbps, 1),
+           "bytes": nbytes, "grid": grid}
+    if stream_bytes:
+        out["step_layout"] = step_layout_ceilings(L, stream_bytes, grid)
+    return out
+
+
+def step_layout_ceilings(L, stream_bytes, grid):
+    """Ceilings of the packed step's own access forms in the benchmark's
+    layout: three streams of `stream_bytes` (the step's p, g and w), the first
+    two at the start of device memory and the third one HBM region further on
+    in allocation order.  Nontemporal read and write of one stream; the
+    step's 3-read/2-write traffic with nontemporal 16-byte accesses, with no
+    arithmetic and with 80 binary32 instructions per value (the step issues
+    about 78)."""
+    import torch
+    st = torch.cuda.current_stream().cuda_stream
+    stream_bytes -= stream_bytes % 16
+    n16 = stream_bytes // 16
+    a = torch.zeros(stream_bytes // 4, dtype=torch.float32, device="cuda:0")
+    b = torch.zeros_like(a)
+    spacer = torch.empty(max(region_bytes() - 2 * stream_bytes, 0), dtype=torch.uint8, device="cuda:0")
+    c = torch.zeros_like(a)
+    del spacer
+    torch.cuda.empty_cache()
+    sink = torch.zeros(4, dtype=torch.float32, device="cuda:0")
+
+    def gbps(moved, fn):
+        return round(moved / time_probe(fn, 5) / 1e6, 1)
+
+    def ok(rc):
+        assert rc == 0, "probe launch failed"
+
+    res = {"stream_bytes": stream_bytes,
+           "read_nt_gbps": gbps(stream_bytes, lambda: ok(L.pa_probe_read(a.data_ptr(), n16, sink.data_ptr(), grid, st))),
+           "write_nt_gbps": gbps(stream_bytes, lambda: ok(L.pa_probe_write(a.data_ptr(), n16, grid, st))),
+           "mix_3r2w_gbps": gbps(5 * stream_bytes, lambda: ok(L.pa_probe_mix(a.data_ptr(), b.data_ptr(), c.data_ptr(),
+                                                                               n16, 0, grid, st))),
+           "mix_3r2w_80valu_gbps": gbps(5 * stream_bytes,
+                                        lambda: ok(L.pa_probe_mix(a.data_ptr(), b.data_ptr(), c.data_ptr(), n16, 80,
+                                                                  grid, st)))}
+    del a, b, c, sink
+    torch.cuda.empty_cache()
+    return res
 
 
 def calibrate_copy(nbytes):
@@ -601,7 +647,7 @@ def main():
         import adamw_step_amd as _p  # noqa: F401
         del ps, gs, states
         torch.cuda.empty_cache()
-        out["probes"] = run_probes(grid=2048)
+        out["probes"] = run_probes(grid=2048, stream_bytes=4 * n_params if mode == "e4" else 0)
         log(f"probes: {out['probes']}")
     if not args.no_cpu_baseline and not args.probe and mode != "blockwise8" and args.param_dtype == "fp32":
         log("timing the CPU oracle on a bounded sample")
