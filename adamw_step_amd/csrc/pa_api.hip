@@ -452,6 +452,7 @@ struct TurboPlan {
   pa::TurboReduceEntry* reduce = nullptr;   // inside the same allocation
   long long tiles = 0;
   int nreduce = 0;
+  long long nchunks = 0;                    // chunks of tile sums over all UState tensors
   size_t ws_bytes = 0;
   std::vector<Range> ranges;                // written buffers and gradients, merged
 };
@@ -470,6 +471,7 @@ void free_turbo_plan(TurboPlan& pl) {
 }
 
 long long turbo_tiles(size_t n) { return (long long)((n + pa::kTurboTile - 1) / pa::kTurboTile); }
+long long turbo_chunks_of(long long tiles) { return (tiles + pa::kTurboChunk - 1) / pa::kTurboChunk; }
 
 bool valid_bits(int b) { return b == 2 || b == 4 || b == 8; }
 
@@ -521,6 +523,10 @@ hipError_t launch_turbo(const TurboPlan& pl, const pa::Scalars& s, const pa::Tur
     hipLaunchKernelGGL((pa::turbo_list<BITS, false>), grid, block, 0, st, pl.table, pl.tiles, s, ts, ws, nf);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.nreduce == 0) return e;
+  hipLaunchKernelGGL(pa::turbo_chunks, dim3((unsigned)pl.nchunks), dim3(pa::kThreads), 0, st, pl.reduce,
+                     pl.nreduce, ws);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   // The reduce kernel checks the same skip flag: a skipped update leaves
   // the scales as they were.
   hipLaunchKernelGGL(pa::turbo_reduce, dim3((unsigned)pl.nreduce), dim3(pa::kThreads), 0, st, pl.reduce, ws, factor,
@@ -822,7 +828,10 @@ size_t pa_turbo_workspace_bytes(size_t count, const pa_turbo_state* states, cons
   if (count == 0 || states == nullptr || n == nullptr) return 0;
   size_t b = 0;
   for (size_t i = 0; i < count; ++i)
-    if (states[i].compress_m && n[i] > 0) b += 8 * (size_t)turbo_tiles(n[i]);
+    if (states[i].compress_m && n[i] > 0) {
+      const long long t = turbo_tiles(n[i]);
+      b += 8 * (size_t)(t + turbo_chunks_of(t));
+    }
   return b;
 }
 
@@ -897,7 +906,7 @@ int pa_turbo_step_list(size_t count, float* const* params, const float* const* g
       e.flags = (t.compress_m ? 1 : 0) | (t.compress_v ? 2 : 0);
       const long long nt = turbo_tiles(n[i]);
       if (t.compress_m) {
-        pa::TurboReduceEntry r{t.scalars, ws_slots, nt, (long long)n[i]};
+        pa::TurboReduceEntry r{t.scalars, ws_slots, nt, (long long)n[i], 0, 0, turbo_chunks_of(nt)};
         red.push_back(r);
         ws_slots += nt;
       }
@@ -916,12 +925,19 @@ int pa_turbo_step_list(size_t count, float* const* params, const float* const* g
     std::memset(&sentinel, 0, sizeof(sentinel));
     sentinel.tile0 = tiles;
     host.push_back(sentinel);
+    long long chunk_slots = 0;                 // chunk sums follow the tile sums
+    for (pa::TurboReduceEntry& r : red) {
+      r.cs0 = ws_slots + chunk_slots;
+      r.chunk0 = chunk_slots;
+      chunk_slots += r.chunks;
+    }
     TurboPlan pl;
     pl.device = dev;
     pl.key = key;
     pl.tiles = tiles;
     pl.nreduce = (int)red.size();
-    pl.ws_bytes = 8 * (size_t)ws_slots;
+    pl.nchunks = chunk_slots;
+    pl.ws_bytes = 8 * (size_t)(ws_slots + chunk_slots);
     written.insert(written.end(), read.begin(), read.end());
     pl.ranges = merged(written);
     const size_t tb = host.size() * sizeof(pa::TurboEntry);

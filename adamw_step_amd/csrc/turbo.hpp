@@ -492,54 +492,88 @@ turbo_list(const TurboEntry* __restrict__ table, long long total_tiles, Scalars 
   if constexpr (COUNT) flush_count(bad, nonfinite);
 }
 
-// Per tensor with a UState first moment: the perfect pairwise tree of its
-// tile sums (chunks of 2048 reduced in LDS, level by level, written back in
-// place), then the scale rotation.  One workgroup per tensor.
+// The residual sums of the tensors with a UState first moment.  Each tile
+// wrote one double; a tensor's sum is the perfect pairwise tree over its
+// tile sums in index order, zero-padded to a power of two.  turbo_chunks
+// reduces every 2048-sum chunk of every tensor in parallel; the chunks are
+// aligned subtrees of each tensor's tree (a padded length above 2048 is a
+// multiple of 2048, and zero subtrees add exactly), so turbo_reduce, run
+// over the chunk sums, completes exactly the same tree.
 struct TurboReduceEntry {
   float* scal;
-  long long ws0;
+  long long ws0;       // first tile sum in the workspace
   long long tiles;
   long long n;
+  long long cs0;       // first chunk sum in the workspace
+  long long chunk0;    // global index of the tensor's first chunk
+  long long chunks;    // ceil(tiles / 2048)
 };
 
+constexpr int kTurboChunk = 2048;
+
+// Perfect pairwise tree over a[0..m) zero-padded to kTurboChunk values, in
+// LDS, by the whole workgroup; returns the sum in every thread.
+__device__ __forceinline__ double chunk_tree(const double* a, long long m, double* buf) {
+  const int tid = threadIdx.x;
+  for (int j = tid; j < kTurboChunk; j += kThreads) buf[j] = j < m ? a[j] : 0.0;
+  __syncthreads();
+  for (int width = kTurboChunk / 2; width >= 1; width >>= 1) {
+    double t[kTurboChunk / 2 / kThreads];           // this level's sums, then written back
+#pragma unroll
+    for (int q = 0; q < kTurboChunk / 2 / kThreads; ++q) {
+      const int j = tid + q * kThreads;
+      t[q] = j < width ? buf[2 * j] + buf[2 * j + 1] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kTurboChunk / 2 / kThreads; ++q) {
+      const int j = tid + q * kThreads;
+      if (j < width) buf[j] = t[q];
+    }
+    __syncthreads();
+  }
+  const double r = buf[0];
+  __syncthreads();                                   // buf is refilled by the next call
+  return r;
+}
+
+// One workgroup per chunk of tile sums over all tensors.
+__global__ void __launch_bounds__(kThreads)
+turbo_chunks(const TurboReduceEntry* __restrict__ list, int nreduce, double* ws) {
+  __shared__ double buf[kTurboChunk];
+  const long long c = blockIdx.x;
+  int lo = 0, hi = nreduce - 1;                      // the last entry with chunk0 <= c
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (list[mid].chunk0 <= c) lo = mid;
+    else hi = mid - 1;
+  }
+  const TurboReduceEntry r = list[lo];
+  const long long k = c - r.chunk0;
+  const double sum = chunk_tree(ws + r.ws0 + k * kTurboChunk, r.tiles - k * kTurboChunk, buf);
+  if (threadIdx.x == 0) ws[r.cs0 + k] = sum;
+}
+
+// One workgroup per tensor: the rest of the tree over its chunk sums (in
+// chunks of 2048, level by level, written back in place), then the scale
+// rotation.
 __global__ void __launch_bounds__(kThreads)
 turbo_reduce(const TurboReduceEntry* __restrict__ list, double* ws, double factor, const unsigned long long* skip) {
-  __shared__ double buf[2048];
+  __shared__ double buf[kTurboChunk];
   if (skip != nullptr && *skip != 0ull) return;   // the step was skipped: no new sums, no rotation
   const TurboReduceEntry r = list[blockIdx.x];
-  double* a = ws + r.ws0;
-  long long m = r.tiles;
-  const int tid = threadIdx.x;
-  while (true) {
-    const long long chunks = (m + 2047) / 2048;
-    for (long long c = 0; c < chunks; ++c) {
-      for (int j = tid; j < 2048; j += kThreads) {
-        const long long idx = c * 2048 + j;
-        buf[j] = idx < m ? a[idx] : 0.0;
-      }
-      __syncthreads();
-      for (int width = 1024; width >= 1; width >>= 1) {
-        double t[1024 / kThreads];                       // this level's sums, then written back
-#pragma unroll
-        for (int q = 0; q < 1024 / kThreads; ++q) {
-          const int j = tid + q * kThreads;
-          t[q] = j < width ? buf[2 * j] + buf[2 * j + 1] : 0.0;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < 1024 / kThreads; ++q) {
-          const int j = tid + q * kThreads;
-          if (j < width) buf[j] = t[q];
-        }
-        __syncthreads();
-      }
-      if (tid == 0) a[c] = buf[0];
+  double* a = ws + r.cs0;
+  long long m = r.chunks;
+  while (m > 1) {
+    const long long groups = (m + kTurboChunk - 1) / kTurboChunk;
+    for (long long c = 0; c < groups; ++c) {
+      const double sum = chunk_tree(a + c * kTurboChunk, m - c * kTurboChunk, buf);
+      if (threadIdx.x == 0) a[c] = sum;
       __syncthreads();
     }
-    if (chunks == 1) break;
-    m = chunks;
+    m = groups;
   }
-  if (tid == 0) {
+  if (threadIdx.x == 0) {
     const double total = a[0];
     const float s_enc = r.scal[1];
     r.scal[0] = s_enc;

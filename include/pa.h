@@ -262,15 +262,17 @@ typedef struct {
  * 131,072 values with both representations, 36,876 + 69,632 = 106,508). */
 size_t pa_turbo_state_bytes(int compress_m, int compress_v, int v_bits, size_t n);
 
-/* Device workspace a pa_turbo_step_list call needs: one double per 256
- * values of every tensor with compress_m (its residual partial sums).  The
- * contents need no initialisation and are dead after the call. */
+/* Device workspace a pa_turbo_step_list call needs, for every tensor with
+ * compress_m: one double per 256 values (its residual partial sums) plus
+ * one per 2048 of those partial sums (their chunk sums).  The contents need
+ * no initialisation and are dead after the call. */
 size_t pa_turbo_workspace_bytes(size_t count, const pa_turbo_state* states, const size_t* n);
 
 /* One TurboAdam step over `count` tensors sharing hyper, config and step (1 to
  * 2^32 - 1, counting this update; PA_ERR_ARG outside): one persistent launch over all tensors (a
- * wavefront per 256 values), then one workgroup per UState tensor that
- * reduces its residual sums and rotates its scales.  `states` is a host
+ * wavefront per 256 values), then one workgroup per 2048 residual partial
+ * sums and one per UState tensor that completes the sum and rotates its
+ * scales.  `states` is a host
  * array of count descriptors; `workspace` a device buffer of at least
  * pa_turbo_workspace_bytes (8-byte aligned).  The launch plan is cached per
  * distinct list (see pa_release_plans).  Written buffers may not overlap

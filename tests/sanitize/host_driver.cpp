@@ -66,7 +66,7 @@ int main() {
   pa_turbo_config tc4{4, 1.1, 1};
   expect(pa_turbo_step_list(1, tp, tg, &ts, tn, &hb, &tc4, 1, reinterpret_cast<void*>(F + (1 << 26)), 1 << 20, nullptr),
          PA_ERR_ARG, "turbo betas");
-  if (pa_turbo_state_bytes(1, 1, 4, 131072) != 106508 || pa_turbo_workspace_bytes(1, &ts, tn) != 128) ++bad;
+  if (pa_turbo_state_bytes(1, 1, 4, 131072) != 106508 || pa_turbo_workspace_bytes(1, &ts, tn) != 136) ++bad;
   pa_format pf;
   for (int m = 0; m < 4; ++m) expect(pa_format_info(m, &pf), PA_OK, "format");
   expect(pa_format_info(9, &pf), PA_ERR_ARG, "format mode");

@@ -264,4 +264,7 @@ def test_turbo_argument_rules(pa):
     assert pa.pa_turbo_state_bytes(1, 1, 4, 131072) == 106508
     assert pa.pa_turbo_state_bytes(0, 0, 4, 10) == 80
     assert pa.pa_turbo_state_bytes(1, 1, 3, 10) == 0
-    assert L.pa_turbo_workspace_bytes(1, S, N) == 8 * 16
+    assert L.pa_turbo_workspace_bytes(1, S, N) == 8 * (16 + 1)           # 16 tile sums, 1 chunk sum
+    N[0] = 2048 * 256 + 1                                                 # 2049 tile sums, 2 chunk sums
+    assert L.pa_turbo_workspace_bytes(1, S, N) == 8 * (2049 + 2)
+    N[0] = 4096

@@ -200,3 +200,37 @@ def test_q1_endpoints_every_float(pa):
                                 f"{lo_bits + int(diff[0]):#x}: {got[diff[0]]:#010x} vs {want[diff[0]]:#010x}")
         del bits, x, out
     assert bad == 0
+
+
+def test_turbo_residual_tree_past_one_chunk_level(pa):
+    """A UState tensor of 2^30 + 12,345 values has 4,194,353 tile sums and
+    2,049 chunk sums, so the scale's tree takes the chunk pass and two
+    levels of the per-tensor pass.  The new scale must equal the perfect
+    pairwise tree, computed on the host, over the tile sums the step left in
+    its workspace: RN32(1.1 * sqrt(sum / n))."""
+    import torch
+    n = (1 << 30) + 12345
+    banner(f"TurboAdam residual tree: one tensor of {n} values")
+    gen = torch.Generator(device="cuda:0").manual_seed(77)
+    p = torch.randn(n, generator=gen, device="cuda:0") * 0.02
+    g = torch.randn(n, generator=gen, device="cuda:0") * 1e-3
+    st = pa.TurboState(n, "cuda:0", True, True, 4, tensor_id=5)
+    tl = pa.TurboList([p], [g], [st])
+    try:
+        tl.step(H, 1)
+        torch.cuda.synchronize()
+        tiles = (n + 255) // 256
+        assert tl.workspace.numel() >= tiles + (tiles + 2047) // 2048
+        a = to_host(tl.workspace[:tiles]).astype(np.float64)
+        size = 1 << int(np.ceil(np.log2(tiles)))
+        a = np.concatenate([a, np.zeros(size - tiles)])
+        while a.size > 1:
+            a = a[0::2] + a[1::2]
+        scal = to_host(st.scalars)
+        want = np.float32(1.1 * np.sqrt(a[0] / n))
+        banner(f"residual sum {a[0]!r}, scale {scal[1]!r} vs {want!r}")
+        assert scal[0] == 0.0 and scal[2] == 0.0
+        assert scal[1].view(np.uint32) == want.view(np.uint32)
+    finally:
+        del p, g, st, tl
+        torch.cuda.empty_cache()
