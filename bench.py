@@ -292,10 +292,28 @@ def cpu_baseline(cfg, mode, ps, gs, states, budget_params):
         else:
             oracle.step_packed(oracle.PACKED_E4 if mode == "e4" else oracle.PACKED_F16, hp[i], hg[i], hs[i], sc)
     dt = time.perf_counter() - t0
-    return {"value": round(total / dt, 1), "unit": "params/s", "cores": oracle.num_threads(),
+    cores = oracle.num_threads()
+    # The same oracle on one core, over the first 32 Mi values of the first
+    # tensor (inputs as left by the step above: any valid state will do).
+    k = min(hp[0].size, 32 << 20)
+    p1, g1 = hp[0][:k].copy(), hg[0][:k].copy()
+    s1 = (hs[0][0][:k].copy(), hs[0][1][:k].copy()) if mode == "fp32" else hs[0][:k].copy()
+    oracle.set_num_threads(1)
+    try:
+        t1 = time.perf_counter()
+        if mode == "fp32":
+            oracle.step_fp32(p1, g1, s1[0], s1[1], sc)
+        else:
+            oracle.step_packed(oracle.PACKED_E4 if mode == "e4" else oracle.PACKED_F16, p1, g1, s1, sc)
+        dt1 = time.perf_counter() - t1
+    finally:
+        oracle.set_num_threads(cores)
+    return {"value": round(total / dt, 1), "unit": "params/s", "cores": cores,
             "kind": "oracle",
             "sample": f"one step over the first {len(picked)} tensors of the list "
-                      f"({names[0]}..{names[-1]}, {total} params), {dt:.1f} s wall"}
+                      f"({names[0]}..{names[-1]}, {total} params), {dt:.1f} s wall",
+            "one_core": {"value": round(k / dt1, 1), "unit": "params/s",
+                         "sample": f"one step over the first {k} values of {names[0]}, {dt1:.1f} s wall"}}
 
 
 def run_gradstats(args, cfg):
@@ -641,7 +659,9 @@ def main():
                      "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "blockwise_kernel" if mode == "blockwise8" else f"elementwise_list<{mode}>",
                      "algorithmic_bytes_per_launch": algo_bytes,
-                     "mean_launch_ms": round(mean_launch_ms, 4), "kernel_sha": kernel_sha()},
+                     "mean_launch_ms": round(mean_launch_ms, 4),
+                     "median_launch_ms": round(sorted(launch_ms)[len(launch_ms) // 2], 4),
+                     "kernel_sha": kernel_sha()},
     }
     if args.probe:
         import adamw_step_amd as _p  # noqa: F401

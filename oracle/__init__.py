@@ -71,6 +71,8 @@ def _load():
     lib.oracle_search_codes.argtypes = [_f32p, _f32p, _u8p, ctypes.c_size_t]
     lib.oracle_search_codes.restype = None
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_num_threads.restype = None
     lib.oracle_block_len.restype = ctypes.c_int
     lib.oracle_e4_bias.restype = ctypes.c_int
     lib.oracle_sumsq_add.argtypes = [ctypes.POINTER(SumsqAcc), ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t]
@@ -227,6 +229,11 @@ def search_codes(qmap, c):
 
 def num_threads():
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(k):
+    """Threads the batch routines use from now on."""
+    _load().oracle_set_num_threads(int(k))
 
 
 def e4_bias():

@@ -484,6 +484,15 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Threads the batch routines use from now on (tests and timing). */
+void oracle_set_num_threads(int k) {
+#ifdef _OPENMP
+    if (k > 0) omp_set_num_threads(k);
+#else
+    (void)k;
+#endif
+}
+
 int oracle_block_len(void) { return ORACLE_BLOCK; }
 int oracle_e4_bias(void) { return ORACLE_E4_BIAS; }
 
