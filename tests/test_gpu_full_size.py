@@ -236,3 +236,101 @@ def test_llama_7b_turbo_sampled_tensors(pa):
         del ps, gs, states
         torch.cuda.empty_cache()
         pa.pa_release_plans()
+
+
+
+def _fill(t, seed, std):
+    import torch
+    gen = torch.Generator(device="cuda:0").manual_seed(seed)
+    step = 1 << 28
+    for i in range(0, t.numel(), step):
+        t[i:i + step].normal_(0.0, std, generator=gen)
+
+
+def _gather(t, ranges, dtype=None):
+    """Host copy of t over contiguous [a, b) ranges, through slice copies:
+    torch's advanced-indexing kernel faults on tensors of more than 2^31
+    elements on this stack, so these tests never index such a tensor."""
+    return np.concatenate([to_host(t[a:b], dtype) for a, b in ranges])
+
+
+@pytest.mark.timeout(600)
+def test_e4_single_tensor_past_int32(pa):
+    """One tensor of 2^31 + 1237 elements (64-bit element indexing, a ragged
+    tail), two steps of the packed E4 update; sampled: the first and last
+    64 Ki elements, 64 Ki around element 2^31, and 64 seeded 64 Ki tiles."""
+    import torch
+    n = (1 << 31) + 1237
+    banner(f"E4 single tensor of {n} elements: allocating {12 * n / 1e9:.1f} GB")
+    p = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    g = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    w = torch.zeros(n, dtype=torch.int32, device="cuda:0")
+    rng = np.random.Generator(np.random.PCG64(2031))
+    ranges = [(0, CHUNK), (n - CHUNK, n), ((1 << 31) - CHUNK // 2, (1 << 31) + CHUNK // 2)]
+    ranges += [(int(t) * CHUNK, (int(t) + 1) * CHUNK) for t in rng.choice(n // CHUNK, 64, replace=False)]
+    try:
+        _fill(p, 11, 0.02)
+        for t in (1, 2):
+            _fill(g, 100 + t, 1e-3)
+            torch.cuda.synchronize()
+            hp, hg, hw = _gather(p, ranges), _gather(g, ranges), _gather(w, ranges, np.uint32)
+            banner(f"E4 single tensor step {t}")
+            pa.pa_step(1, p, g, w, hyper(), t)
+            torch.cuda.synchronize()
+            oracle.step_packed(1, hp, hg, hw, scalars(t))
+            assert_words(_gather(w, ranges, np.uint32), hw, what="words")
+            same = assert_params(_gather(p, ranges), hp)[0]
+            banner(f"E4 single tensor step {t}: {hp.size} sampled elements, bit-identical params {same}")
+    finally:
+        del p, g, w
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(600)
+def test_blockwise_single_tensor_past_int32(pa):
+    """One blockwise tensor of 2^31 + 5 * 2048 elements (1,048,581 blocks),
+    two steps; sampled: the first and last blocks, the two blocks on either
+    side of element 2^31, and 60 seeded blocks."""
+    import torch
+    nb = (1 << 20) + 5
+    n = nb * 2048
+    qm, qv = workloads.code_maps()
+    zero_m = int(np.nonzero(qm == 0.0)[0][0])
+    banner(f"blockwise single tensor of {n} elements: allocating {14 * n / 1e9:.1f} GB")
+    p = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    g = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    mc = torch.full((n,), zero_m, dtype=torch.uint8, device="cuda:0")
+    vc = torch.zeros(n, dtype=torch.uint8, device="cuda:0")
+    ma = torch.zeros(nb, dtype=torch.float32, device="cuda:0")
+    va = torch.zeros(nb, dtype=torch.float32, device="cuda:0")
+    dqm, dqv = torch.from_numpy(qm).to("cuda:0"), torch.from_numpy(qv).to("cuda:0")
+    pout = torch.empty(n, dtype=torch.int16, device="cuda:0")
+    rng = np.random.Generator(np.random.PCG64(2032))
+    blocks = np.union1d([0, nb - 1, (1 << 20) - 1, 1 << 20], rng.choice(nb, 60, replace=False)).tolist()
+    er = [(b * 2048, (b + 1) * 2048) for b in blocks]
+    br = [(b, b + 1) for b in blocks]
+    try:
+        _fill(p, 12, 0.02)
+        for t in (1, 2):
+            _fill(g, 200 + t, 1e-3)
+            torch.cuda.synchronize()
+            hp, hg = _gather(p, er), _gather(g, er)
+            hmc, hvc = _gather(mc, er).copy(), _gather(vc, er).copy()
+            hma, hva = _gather(ma, br).copy(), _gather(va, br).copy()
+            banner(f"blockwise single tensor step {t}")
+            pa.pa_step(3, p, g, (mc, ma, vc, va, dqm, dqv, pout), hyper(), t)
+            torch.cuda.synchronize()
+            hout = np.zeros(hp.size, np.uint16)
+            oracle.step_blockwise(hp, hg, hmc, hma, hvc, hva, qm, qv, hout, scalars(t))
+            assert np.array_equal(_gather(mc, er), hmc) and np.array_equal(_gather(vc, er), hvc), "codes"
+            assert np.array_equal(_gather(ma, br).view(np.uint32), hma.view(np.uint32)), "m absmax"
+            assert np.array_equal(_gather(va, br).view(np.uint32), hva.view(np.uint32)), "v absmax"
+            got = _gather(pout, er).view(np.uint16)
+            assert np.array_equal(got, hout), f"{int((got != hout).sum())} bf16 outputs differ"
+            widened = (hout.astype(np.uint32) << 16).view(np.float32)
+            for k, (a, b) in enumerate(er):             # the next step's parameters, sampled blocks only
+                p[a:b].copy_(torch.from_numpy(widened[k * 2048:(k + 1) * 2048]))
+            banner(f"blockwise single tensor step {t}: {len(blocks)} sampled blocks bit-exact")
+    finally:
+        del p, g, mc, vc, ma, va, pout
+        torch.cuda.empty_cache()
