@@ -1,6 +1,7 @@
 """GPU lane codecs against the oracle's, through the C ABI (pa_debug_codec):
-every code of every lane decoded, and every rounding boundary (with its
-FP32 neighbours), whole FP32 binades and random bit patterns encoded."""
+every code of every lane decoded, every rounding boundary (with its FP32
+neighbours), whole FP32 binades and random bit patterns encoded, and then
+every one of the 2^32 binary32 bit patterns encoded."""
 import numpy as np
 import pytest
 
@@ -81,6 +82,34 @@ def test_decode_encode_identity_on_device(pa, lane):
     codes = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
     back = _encode_gpu(pa, lane, _decode_gpu(pa, lane, codes))
     np.testing.assert_array_equal(back, codes)
+
+
+@pytest.mark.parametrize("lane", [0, 1, 2])
+def test_encode_every_float(pa, lane):
+    """Each lane's GPU encoder equals the oracle's nearest-in-table encoder on
+    all 2^32 binary32 bit patterns (binary16 NaNs by class and sign)."""
+    import torch
+    chunk = 1 << 28
+    bad = 0
+    for c in range(1 << 4):
+        banner(f"encode lane {lane} chunk {c}/16")
+        bits = torch.arange(c * chunk, (c + 1) * chunk, dtype=torch.int64, device="cuda:0")
+        x = bits.to(torch.int32).view(torch.float32)        # wraps to the bit pattern
+        out = torch.empty(chunk, dtype=torch.int16, device="cuda:0")
+        pa.pa_debug_codec(lane, 0, x, out)
+        torch.cuda.synchronize()
+        hx = to_host(x)
+        got = to_host(out, np.uint16)
+        want = oracle.encode(lane, hx)
+        if lane == 2:
+            nan = np.isnan(hx)
+            bad += int((got[~nan] != want[~nan]).sum())
+            assert np.all(((got[nan] & 0x7C00) == 0x7C00) & ((got[nan] & 0x3FF) != 0))
+            assert np.array_equal(got[nan] >> 15, want[nan] >> 15)
+        else:
+            bad += int((got != want).sum())
+        del bits, x, out
+    assert bad == 0, f"lane {lane}: {bad} codes differ from the oracle"
 
 
 def test_bf16_encode_every_float(pa):
