@@ -537,6 +537,8 @@ def main():
     ap.add_argument("--workload", default="llama-7b", choices=sorted(WORKLOADS))
     ap.add_argument("--mode", default="e4", choices=sorted(BYTES_PER_PARAM))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the step-layout bandwidth probes after the timed region (E4 mode)")
     ap.add_argument("--cpu-sample-params", type=int, default=1_300_000_000)
     ap.add_argument("--probe", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0)
@@ -666,12 +668,29 @@ def main():
     if args.probe:
         import adamw_step_amd as _p  # noqa: F401
         del ps, gs, states
+        prepared = None              # it holds the tensors too
         torch.cuda.empty_cache()
         out["probes"] = run_probes(grid=2048, stream_bytes=4 * n_params if mode == "e4" else 0)
         log(f"probes: {out['probes']}")
     if not args.no_cpu_baseline and not args.probe and mode != "blockwise8" and args.param_dtype == "fp32":
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(cfg, mode, ps, gs, states, args.cpu_sample_params)
+    if mode == "e4" and args.param_dtype == "fp32" and not args.probe and not args.no_ceiling:
+        # What this HBM delivers for the step's own traffic and access forms,
+        # measured after the step's buffers are freed (context for `frac`).
+        del ps, gs, states
+        prepared = None
+        torch.cuda.empty_cache()
+        try:
+            import adamw_step_amd as _p  # noqa: F401
+            ceil = step_layout_ceilings(probe_lib(), 4 * n_params, 2048)
+            ceil["frac_of_traffic_probe"] = round(achieved / ceil["mix_3r2w_gbps"], 4)
+            ceil["frac_of_traffic_and_valu_probe"] = round(achieved / ceil["mix_3r2w_80valu_gbps"], 4)
+            out["roofline"]["measured_ceilings"] = ceil
+            log(f"measured ceilings: {ceil}")
+        except Exception as ex:      # a probe problem must not cost the result line
+            out["roofline"]["measured_ceilings"] = None
+            log(f"ceiling probes failed: {ex!r}")
     print(json.dumps(out), flush=True)
 
 
