@@ -256,7 +256,10 @@ __device__ __forceinline__ void store_index4(uint8_t* base, long long lane_word,
 // One 256-value tile of one tensor, by one wavefront.
 // The entry is read through a pointer at each use: held whole, its fields
 // crowd the scalar registers and spill.
-template <int BITS>
+// FULL: the tile lies wholly inside its tensor, so every validity test below
+// folds away (one instantiation per case; the partial one runs only on a
+// tensor's last tile).
+template <int BITS, bool FULL>
 __device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, long long tile, const Scalars& s,
                                            const TurboScalars& ts, float* lev_half, double* ws, uint32_t& bad) {
   const TurboEntry& e = *ep;
@@ -267,15 +270,15 @@ __device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, lo
   const long long base = tile * kTurboTile;
   const long long i0 = base + 4 * lane;                 // this lane's first value
   const long long n = e.n;
-  const bool full = base + kTurboTile <= n;
+  const bool full = FULL;
   bool valid[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) valid[k] = i0 + k < n;
+  for (int k = 0; k < 4; ++k) valid[k] = FULL || i0 + k < n;
   const long long blk = (base >> 7) + half;              // 1Q block of this lane
-  const bool blk_exists = blk * kTurboBlock < n;
+  const bool blk_exists = FULL || blk * kTurboBlock < n;
   const long long grp = i0 >> 6;                         // UState group of this lane
   const long long glen_ll = n - (grp << 6);
-  const int glen = glen_ll >= kTurboGroup ? kTurboGroup : (int)glen_ll;
+  const int glen = (FULL || glen_ll >= kTurboGroup) ? kTurboGroup : (int)glen_ll;
 
   // ---- loads
   float p[4], g[4], mprev[4] = {0.f, 0.f, 0.f, 0.f}, vprev[4] = {0.f, 0.f, 0.f, 0.f};
@@ -487,7 +490,11 @@ turbo_list(const TurboEntry* __restrict__ table, long long total_tiles, Scalars 
   int t = 0;
   for (long long tile = gw; tile < total_tiles; tile += nw) {
     while (tile >= table[t + 1].tile0) ++t;
-    turbo_tile<BITS>(table + t, tile - table[t].tile0, s, ts, lev[wave][half], ws, bad);
+    const long long local = tile - table[t].tile0;
+    if ((local + 1) * kTurboTile <= table[t].n)
+      turbo_tile<BITS, true>(table + t, local, s, ts, lev[wave][half], ws, bad);
+    else
+      turbo_tile<BITS, false>(table + t, local, s, ts, lev[wave][half], ws, bad);
   }
   if constexpr (COUNT) flush_count(bad, nonfinite);
 }
