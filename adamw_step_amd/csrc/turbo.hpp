@@ -483,7 +483,11 @@ turbo_list(const TurboEntry* __restrict__ table, long long total_tiles, Scalars 
            unsigned long long* nonfinite) {
   __shared__ float lev[kThreads / 64][2][256];
   if (!resolve_inputs(s)) return;
-  const int wave = threadIdx.x >> 6, half = (threadIdx.x >> 5) & 1;
+  // The wavefront index is uniform across the wavefront; saying so lets the
+  // compiler keep the tile, the table cursor and every field of the entry
+  // in scalar registers (scalar loads, the Philox key schedule on the
+  // scalar unit) instead of repeating them in every lane.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), half = (threadIdx.x >> 5) & 1;
   const long long gw = (long long)blockIdx.x * (kThreads / 64) + wave;
   const long long nw = (long long)gridDim.x * (kThreads / 64);
   uint32_t bad = 0;
