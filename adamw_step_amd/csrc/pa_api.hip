@@ -72,7 +72,7 @@ struct DeviceInfo {
   int blocks_per_cu = 0;      // elementwise kernels
   int bw_blocks_per_cu = 0;   // blockwise kernel
   int stats_blocks_per_cu = 0;   // gradient pre-pass
-  int turbo_blocks_per_cu = 0;   // TurboAdam step
+  int turbo_blocks_per_cu[3] = {0, 0, 0};   // TurboAdam step, 2-, 4- and 8-bit indices
 };
 
 std::mutex g_dev_mu;
@@ -106,11 +106,14 @@ int device_info(int* dev_out, DeviceInfo* info) {
         &st, reinterpret_cast<const void*>(pa::grad_stats_list<pa::kF32, true>), pa::kThreads, 0);
     if (e != hipSuccess || st < 1) st = 4;
     d.stats_blocks_per_cu = st;
-    int tb = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &tb, reinterpret_cast<const void*>(pa::turbo_list<4, false>), pa::kThreads, 0);
-    if (e != hipSuccess || tb < 1) tb = 2;
-    d.turbo_blocks_per_cu = tb;
+    const void* turbo[3] = {reinterpret_cast<const void*>(pa::turbo_list<2, false>),
+                            reinterpret_cast<const void*>(pa::turbo_list<4, false>),
+                            reinterpret_cast<const void*>(pa::turbo_list<8, false>)};
+    for (int i = 0; i < 3; ++i) {
+      int tb = 0;
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&tb, turbo[i], pa::kThreads, 0);
+      d.turbo_blocks_per_cu[i] = (e != hipSuccess || tb < 1) ? 2 : tb;
+    }
   }
   *dev_out = dev;
   *info = d;
@@ -516,7 +519,8 @@ template <int BITS>
 hipError_t launch_turbo(const TurboPlan& pl, const pa::Scalars& s, const pa::TurboScalars& ts, double* ws,
                         unsigned long long* nf, double factor, hipStream_t st, const DeviceInfo& d) {
   const long long wgs = (pl.tiles + pa::kThreads / 64 - 1) / (pa::kThreads / 64);
-  const dim3 grid((unsigned)grid_for(wgs, d, d.turbo_blocks_per_cu)), block(pa::kThreads);
+  const dim3 grid((unsigned)grid_for(wgs, d, d.turbo_blocks_per_cu[BITS == 2 ? 0 : BITS == 4 ? 1 : 2])),
+      block(pa::kThreads);
   if (nf)
     hipLaunchKernelGGL((pa::turbo_list<BITS, true>), grid, block, 0, st, pl.table, pl.tiles, s, ts, ws, nf);
   else
