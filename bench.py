@@ -551,7 +551,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only; every GPU box here has a single GPU, "
+        print("bench.py: this benchmark runs on one GPU only (one process, one device), "
               "so --gpus must be 1", file=sys.stderr)
         sys.exit(2)
 
