@@ -193,10 +193,12 @@ def test_llama_7b_grad_stats_exact(pa):
 @pytest.mark.timeout(900)
 def test_llama_7b_turbo_sampled_tensors(pa):
     """The TurboAdam step over the whole 291-tensor list in the benchmark's
-    launch configuration; three whole tensors (tensors are independent:
-    each has its own draws, groups, blocks and scales) against the oracle
-    for two steps: the first RMSNorm gain, the first query projection and
-    the final norm."""
+    launch configuration; five whole tensors (tensors are independent: each
+    has its own draws, groups, blocks and scales) against the oracle for
+    three steps, so that codes written with a nonzero scale are decoded: the
+    embedding (131 M values, 256 chunks of residual sums), the first RMSNorm
+    gain (FP32 moments), the first query and gate projections, and the final
+    norm."""
     import torch
     cfg = 4
     sizes = workloads.sizes(cfg)
@@ -207,12 +209,14 @@ def test_llama_7b_turbo_sampled_tensors(pa):
     pick = [i for i, (name, _) in enumerate(workloads.shapes(cfg)) if "norm" in name][:1]
     pick += [i for i, (name, _) in enumerate(workloads.shapes(cfg)) if "q_proj" in name][:1]
     pick += [len(sizes) - 2 if "norm" in workloads.shapes(cfg)[-2][0] else len(sizes) - 1]
+    pick += [0] + [i for i, (name, _) in enumerate(workloads.shapes(cfg)) if "gate_proj" in name][:1]
+    pick = sorted(set(pick))
     try:
         workloads.device_fill_params(cfg, ps)
         tl = pa.TurboList(ps, gs, states)
         hp = {i: to_host(ps[i]).copy() for i in pick}
         hs = {i: oracle.TurboState(sizes[i], sizes[i] >= 4096, sizes[i] >= 4096, 4) for i in pick}
-        for t in (1, 2):
+        for t in (1, 2, 3):
             workloads.device_fill_grads(cfg, t, gs)
             torch.cuda.synchronize()
             hg = {i: to_host(gs[i]).copy() for i in pick}
