@@ -435,13 +435,14 @@ def run_turbo(args, cfg):
     spacer = None
     if args.layout == "regions":
         spacer = torch.empty(max(region_bytes() - 8 * sum(sizes), 0), dtype=torch.uint8, device="cuda:0")
-    states = [pa.TurboState(n, "cuda:0", compress_m=n >= 4096, compress_v=n >= 4096, v_bits=4, tensor_id=i)
+    states = [pa.TurboState(n, "cuda:0", compress_m=n >= 4096, compress_v=n >= 4096, v_bits=args.turbo_bits,
+                            tensor_id=i)
               for i, n in enumerate(sizes)]
     del spacer
     torch.cuda.empty_cache()
     workloads.device_fill_params(cfg, ps)
     workloads.device_fill_grads(cfg, 1, gs)
-    tl = pa.TurboList(ps, gs, states)
+    tl = pa.TurboList(ps, gs, states, v_bits=args.turbo_bits)
     h = dict(workloads.HYPER)
     torch.cuda.synchronize()
     t = 0
@@ -472,16 +473,16 @@ def run_turbo(args, cfg):
     # the counters measured for this kernel source (profiles/), if current.
     valu = None
     vpath = os.path.join(ROOT, "profiles", f"valu_{args.workload}_turbo.json")
-    if os.path.exists(vpath):
+    if os.path.exists(vpath) and args.turbo_bits == 4:      # the counters were taken on the 4-bit kernel
         with open(vpath) as f:
             vj = json.load(f)
         if vj.get("kernel_sha") == kernel_sha("turbo"):
             valu = vj["valu_lane_instr_per_param"]
-    out = {"metric": "TurboAdam step (UState + 4-bit 1Q state): params/s", "value": round(n * args.steps / elapsed, 1),
+    out = {"metric": f"TurboAdam step (UState + {args.turbo_bits}-bit 1Q state): params/s", "value": round(n * args.steps / elapsed, 1),
            "unit": "params/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(elapsed * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-           "config": {"workload": args.workload, "params": n, "tensors": len(sizes), "mode": "turbo-ustate-1q4",
+           "config": {"workload": args.workload, "params": n, "tensors": len(sizes), "mode": f"turbo-ustate-1q{args.turbo_bits}",
                       "state_bytes": state, "state_bits_per_param": round(8 * state / n, 4),
                       "layout": args.layout},
            "roofline": ({"bound": "alu", "achieved": round(valu * n / (mean_ms / 1e3) / 1e9, 1),
@@ -491,7 +492,7 @@ def run_turbo(args, cfg):
                         {"bound": "alu", "achieved": None, "peak": PEAK_VALU_GLANE, "unit": "G VALU lane-instr/s",
                          "frac": None}) | {
                         "hbm_achieved_gbps": round(achieved, 1), "hbm_frac": round(achieved / PEAK_GBPS, 4),
-                        "traffic": None, "kernel": "turbo_list<4> + turbo_reduce",
+                        "traffic": None, "kernel": f"turbo_list<{args.turbo_bits}> + turbo_chunks + turbo_reduce",
                         "algorithmic_bytes_per_launch": algo, "mean_launch_ms": round(mean_ms, 4),
                         "kernel_sha": kernel_sha("turbo")}}
     if not args.no_cpu_baseline:
@@ -546,6 +547,8 @@ def main():
     ap.add_argument("--param-dtype", default="fp32", choices=["fp32", "bf16", "fp16"],
                     help="element type of parameters and gradients (state unchanged)")
     ap.add_argument("--region-map", action="store_true")
+    ap.add_argument("--turbo-bits", type=int, default=4, choices=[2, 4, 8],
+                    help="1Q index width of the TurboAdam mode (the page's default is 4)")
     ap.add_argument("--layout", default="regions", choices=["regions", "plain"],
                     help="HBM placement of the state streams (see build_workload)")
     args = ap.parse_args()
