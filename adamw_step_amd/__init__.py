@@ -86,7 +86,7 @@ class Format(ctypes.Structure):
 
 EXPORTS = ("pa_step", "pa_step_list", "pa_step_typed", "pa_step_list_typed", "pa_state_bytes",
            "pa_format_info", "pa_status_string", "pa_last_hip_error", "pa_release_plans", "pa_debug_codec",
-           "pa_debug_sqrt", "pa_debug_q1_ends", "pa_grad_stats_list", "pa_turbo_state_bytes", "pa_turbo_workspace_bytes",
+           "pa_debug_sqrt", "pa_debug_q1_ends", "pa_debug_q1_levels", "pa_grad_stats_list", "pa_turbo_state_bytes", "pa_turbo_workspace_bytes",
            "pa_turbo_step_list")
 
 PA_DT_F32, PA_DT_BF16, PA_DT_F16 = 0, 1, 2
@@ -131,6 +131,8 @@ def lib():
     L.pa_debug_sqrt.restype = ctypes.c_int
     L.pa_debug_q1_ends.argtypes = [vp, vp, sz, vp]
     L.pa_debug_q1_ends.restype = ctypes.c_int
+    L.pa_debug_q1_levels.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp, sz, vp]
+    L.pa_debug_q1_levels.restype = ctypes.c_int
     L.pa_grad_stats_list.argtypes = [ctypes.c_int, sz, ctypes.POINTER(vp), ctypes.POINTER(sz), ctypes.c_double,
                                      vp, vp, vp, vp]
     L.pa_grad_stats_list.restype = ctypes.c_int
@@ -420,6 +422,23 @@ def pa_debug_q1_ends(inp, out, stream=None):
     if inp.numel() != out.numel() or out.element_size() != 4:
         raise ValueError("output must hold one 32-bit word per input")
     _check(lib().pa_debug_q1_ends(_ptr(inp), _ptr(out), inp.numel(), _stream(stream)))
+
+
+
+def pa_debug_q1_levels(ends, bits, exact, out, stream=None):
+    """out (float32, len(ends) * 2^bits) = the 1Q levels of each endpoint word
+    in ends (int32 bit patterns: fp16 lower endpoint low, upper high);
+    exact=True takes every level through the double-double evaluation."""
+    import torch
+
+    _tensor_ok(ends, "endpoints")
+    _tensor_ok(out, "output")
+    if ends.element_size() != 4 or out.dtype != torch.float32:
+        raise ValueError("endpoints must be 32-bit words and the output float32")
+    if out.numel() != ends.numel() << int(bits):
+        raise ValueError("output must hold 2^bits levels per endpoint word")
+    _check(lib().pa_debug_q1_levels(_ptr(ends), int(bits), 1 if exact else 0, _ptr(out), ends.numel(),
+                                    _stream(stream)))
 
 
 # ---------------------------------------------------------------- TurboAdam

@@ -1108,6 +1108,24 @@ int pa_debug_q1_ends(const float* in, uint32_t* out, size_t n, void* stream) {
   return e == hipSuccess ? PA_OK : hip_failed(e);
 }
 
+int pa_debug_q1_levels(const uint32_t* ends, int bits, int exact, float* out, size_t n, void* stream) {
+  if (bits != 2 && bits != 4 && bits != 8) return PA_ERR_ARG;
+  if (n == 0) return PA_OK;
+  if (ends == nullptr || out == nullptr || n > ((size_t)1 << 40)) return PA_ERR_ARG;
+  if (!aligned(ends, 4) || !aligned(out, 4)) return PA_ERR_ALIGN;
+  int dev;
+  DeviceInfo d;
+  int rc = device_info(&dev, &d);
+  if (rc) return rc;
+  const long long total = (long long)n << bits;
+  const long long blocks = (total + pa::kThreads - 1) / pa::kThreads;
+  const dim3 grid((unsigned)grid_for(blocks, d, d.blocks_per_cu)), block(pa::kThreads);
+  hipLaunchKernelGGL(pa::q1_levels_kernel, grid, block, 0, static_cast<hipStream_t>(stream), ends, bits,
+                     exact ? 1 : 0, out, total);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PA_OK : hip_failed(e);
+}
+
 int pa_debug_sqrt(const float* in, float* out, size_t n, void* stream) {
   if (n == 0) return PA_OK;
   if (in == nullptr || out == nullptr) return PA_ERR_ARG;

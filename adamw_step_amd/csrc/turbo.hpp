@@ -8,9 +8,9 @@
 // The page prints neither code nor constants for the grid, the code levels,
 // the scale rule or the rounding hash; the readings implemented here:
 //
-//  * 1Q: index 0 is zero; index k >= 1 decodes to exp2 of the k-th of L-1
-//    evenly spaced points from lo to hi (in double), rounded once to
-//    binary32.  lo and hi are log2 of the block's smallest positive and
+//  * 1Q: index 0 is zero; index k >= 1 decodes to the exact power 2^x of
+//    the k-th of L-1 evenly spaced points x from lo to hi (computed in
+//    double), rounded once to binary32.  lo and hi are log2 of the block's smallest positive and
 //    largest finite value, rounded to binary16 down and up.  A value goes to
 //    the largest level at or below it, or the next one with probability
 //    equal to its position between the two.
@@ -40,6 +40,7 @@
 #include <stdint.h>
 
 #include "kernels.hpp"
+#include "pow2.hpp"
 
 #pragma clang fp contract(off)
 
@@ -184,23 +185,57 @@ __device__ __forceinline__ uint32_t log2_directed16(float v, bool up, bool activ
   return a;
 }
 
-// Level k of a 1Q block, in double then rounded once to binary32.
-__device__ __forceinline__ float q1_level(double lo, double hi, int k, int L) {
-  if (k == 0) return 0.0f;
-  const double x = lo + ((hi - lo) * (double)(k - 1)) / (double)(L - 2);
-  return (float)exp2(x);
+// The exponent of level k >= 1 of a 1Q block, in double.
+__device__ __forceinline__ double q1_level_x(double lo, double hi, int k, int L) {
+  return lo + ((hi - lo) * (double)(k - 1)) / (double)(L - 2);
+}
+
+// The double-double decision, out of line for the self-test export.
+__device__ __attribute__((noinline)) float pow2_rn32_slow(double x) { return pow2_rn32_dd(x); }
+
+// Level k >= 1 of a 1Q block is the exact 2^x rounded once to binary32.  The
+// device exp2 is within one double ulp (2^-52 relative) of 2^x; when every
+// value within 2^-48 of its result rounds to the same binary32 value, so
+// does 2^x (the products below are monotone and off by at most 2^-53), and
+// this returns true with the level in *out.  Otherwise (2^x near a binary32
+// midpoint: about one level in 2^23) the double-double evaluation decides.
+__device__ __forceinline__ bool q1_level_fast(double x, float* out) {
+  const double y = exp2(x);
+  const float a = (float)(y * (1.0 - 0x1p-48)), b = (float)(y * (1.0 + 0x1p-48));
+  *out = a;
+  return a == b;
 }
 
 // The double-precision exp2 and log2 below are called out of line on
 // purpose: inlined, their polynomial coefficients were hoisted out of the
 // tile loop into about 40 vector registers held for the whole kernel, which
 // cut occupancy from 7 to 4 wavefronts per SIMD; a call per table costs a
-// few instructions against thousands per tile.
+// few instructions against thousands per tile.  The levels the device exp2
+// leaves undecided are redone afterwards in one rolled loop, so that the
+// double-double code appears once and its registers stay few.
 template <int BITS>
 __device__ __attribute__((noinline)) void build_levels(float* lev, uint32_t ends, int lane_in_half) {
   constexpr int L = 1 << BITS;
   const double lo = f16_to_double(ends & 0xFFFFu), hi = f16_to_double(ends >> 16);
-  for (int k = lane_in_half; k < L; k += 32) lev[k] = q1_level(lo, hi, k, L);
+  uint32_t undecided = 0;   // bit j: level lane_in_half + 32 j
+#pragma unroll
+  for (int j = 0; j * 32 < L; ++j) {
+    const int k = lane_in_half + 32 * j;
+    if (k >= L) break;
+    if (k == 0) {
+      lev[0] = 0.0f;
+      continue;
+    }
+    float a;
+    if (!q1_level_fast(q1_level_x(lo, hi, k, L), &a)) undecided |= 1u << j;
+    lev[k] = a;
+  }
+  while (undecided) {
+    const int j = __builtin_ctz(undecided);
+    undecided &= undecided - 1;
+    const int k = lane_in_half + 32 * j;
+    lev[k] = pow2_rn32_dd(q1_level_x(lo, hi, k, L));
+  }
 }
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -599,6 +634,26 @@ __global__ void __launch_bounds__(kThreads) q1_ends_kernel(const float* in, uint
   for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < n; i += (long long)gridDim.x * kThreads) {
     const float v = in[i];
     out[i] = log2_directed16(v, false, true) | (log2_directed16(v, true, true) << 16);
+  }
+}
+
+// Self-test export: level k of the endpoint word ends[i / L] at out[i], for
+// i < total = n L; exact != 0 takes every level through the double-double
+// path.
+__global__ void __launch_bounds__(kThreads) q1_levels_kernel(const uint32_t* ends, int bits, int exact,
+                                                            float* out, long long total) {
+  const int L = 1 << bits;
+  for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < total; i += (long long)gridDim.x * kThreads) {
+    const uint32_t w = ends[i >> bits];
+    const int k = (int)(i & (L - 1));
+    const double lo = f16_to_double(w & 0xFFFFu), hi = f16_to_double(w >> 16);
+    if (k == 0) {
+      out[i] = 0.0f;
+      continue;
+    }
+    const double x = q1_level_x(lo, hi, k, L);
+    float a;
+    out[i] = (!exact && q1_level_fast(x, &a)) ? a : pow2_rn32_slow(x);
   }
 }
 

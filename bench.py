@@ -57,7 +57,8 @@ WORKLOADS = {"single-262k": 1, "gpt-11m": 2, "gpt2-small-124m": 3, "llama-7b": 4
 # reading stays valid while these bytes are unchanged.
 KERNEL_SOURCES = {
     "elementwise": ("adamw_step_amd/csrc/kernels.hpp", "adamw_step_amd/csrc/codec.hpp"),
-    "turbo": ("adamw_step_amd/csrc/kernels.hpp", "adamw_step_amd/csrc/codec.hpp", "adamw_step_amd/csrc/turbo.hpp"),
+    "turbo": ("adamw_step_amd/csrc/kernels.hpp", "adamw_step_amd/csrc/codec.hpp", "adamw_step_amd/csrc/turbo.hpp",
+              "adamw_step_amd/csrc/pow2.hpp"),
 }
 
 

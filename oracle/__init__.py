@@ -94,6 +94,8 @@ def _load():
     lib.oracle_turbo_step.restype = ctypes.c_ulonglong
     lib.oracle_q1_levels.argtypes = [ctypes.c_uint16, ctypes.c_uint16, ctypes.c_int, _f32p]
     lib.oracle_q1_levels.restype = None
+    lib.oracle_q1_levels_batch.argtypes = [_u32p, ctypes.c_size_t, ctypes.c_int, _f32p]
+    lib.oracle_q1_levels_batch.restype = None
     lib.oracle_q1_ends_batch.argtypes = [_f32p, _u32p, ctypes.c_size_t]
     lib.oracle_q1_ends_batch.restype = None
     lib.oracle_q1_block.argtypes = [_f32p, ctypes.c_size_t, ctypes.c_int, _f32p, _u8p, _u16p, _f32p]
@@ -332,6 +334,15 @@ def q1_levels(lo16, hi16, bits):
     """Decoded value of every 1Q index of a block with fp16 endpoints (bits)."""
     out = np.zeros(1 << bits, np.float32)
     _load().oracle_q1_levels(int(lo16), int(hi16), int(bits), _ptr(out, _f32p))
+    return out
+
+
+def q1_levels_batch(ends, bits):
+    """The levels of every block whose endpoint word (fp16 lower endpoint in
+    the low half) is in ends: shape (len(ends), 2^bits)."""
+    e = np.ascontiguousarray(ends, np.uint32)
+    out = np.zeros((e.size, 1 << bits), np.float32)
+    _load().oracle_q1_levels_batch(_ptr(e, _u32p), e.size, int(bits), _ptr(out, _f32p))
     return out
 
 

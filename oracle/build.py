@@ -23,7 +23,7 @@ CFLAGS = [
 
 def build(verbose: bool = False) -> str:
     tmp = OUT + ".tmp%d" % os.getpid()
-    cmd = ["gcc", *CFLAGS, SRC, "-o", tmp, "-lm"]
+    cmd = ["gcc", *CFLAGS, SRC, "-o", tmp, "-lquadmath", "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)

@@ -52,6 +52,8 @@
  * lane is exact.
  */
 #include <math.h>
+#include <quadmath.h>
+#include <stdio.h>
 #include <stdlib.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -645,8 +647,8 @@ void oracle_scale_grads(int gdt, const void* g, float scale, float* out, size_t 
  * taken here (parity unpinned where the page is silent) are:
  *
  *  1Q, L = 2^bits indices: index 0 is exactly 0; index k in 1..L-1 decodes to
- *    level_k = RN32(exp2(lo + (hi - lo) * (k - 1) / (L - 2))) in double,
- *    where lo and hi are the block's fp16 endpoints: log2 (in double) of the
+ *    level_k = RN32(2^x), x = lo + (hi - lo) * (k - 1) / (L - 2) in double
+ *    and 2^x the exact power (not a double exp2 rounded again), where lo and hi are the block's fp16 endpoints: log2 (in double) of the
  *    smallest positive finite v rounded down to fp16, and of the largest
  *    rounded up.  Encode: 0 -> 0, NaN -> 0, +Inf -> L-1; else the largest k
  *    with level_k <= v (at least 1), then k+1 with probability
@@ -741,12 +743,37 @@ static double f16_value(uint16_t h) {
     return (double)oracle_decode_f16(h);
 }
 
+/* RN32(2^x), the exact power of two rounded once to binary32, for a double
+ * x.  For an integer x the power is a power of two (a binary32 value, or the
+ * midpoint 2^-150 that rounds to even 0, or beyond the range); for any other
+ * x it is irrational, so it never lies on a binary32 midpoint and the
+ * rounding is well defined.  The 64-bit-significand exp2l is within a few
+ * of its ulps (2^-62 relative): when every value within 2^-56 of its result
+ * rounds to the same binary32 value, that is the answer.  Otherwise (about
+ * one x in 2^31) the binary128 exp2q (error below 2^-110) decides with a
+ * 2^-100 margin; a power closer than that to a midpoint stops the oracle
+ * rather than let it guess. */
+static float exp2_rn32(double x) {
+    if (isnan(x)) return NAN;
+    if (x >= 128.0) return INFINITY;
+    if (x <= -150.0) return 0.0f;
+    if (x == nearbyint(x)) return ldexpf(1.0f, (int)x);
+    const long double y = exp2l((long double)x);
+    const float a = (float)(y * (1.0L - 0x1p-56L)), b = (float)(y * (1.0L + 0x1p-56L));
+    if (a == b) return a;
+    const __float128 q = exp2q((__float128)x), m = (__float128)0x1p-100;
+    const float c = (float)(q * (1 - m)), d = (float)(q * (1 + m));
+    if (c == d) return c;
+    fprintf(stderr, "oracle: 2^%a lies within 2^-100 of a binary32 midpoint\n", x);
+    abort();
+}
+
 static void level_table(uint16_t lo16, uint16_t hi16, int L, float* lev) {
     double lo = f16_value(lo16), hi = f16_value(hi16);
     lev[0] = 0.0f;
     for (int k = 1; k < L; ++k) {
         double x = lo + ((hi - lo) * (double)(k - 1)) / (double)(L - 2);
-        lev[k] = (float)exp2(x);
+        lev[k] = exp2_rn32(x);
     }
 }
 
@@ -771,6 +798,15 @@ void oracle_q1_ends_batch(const float* v, uint32_t* out, size_t n) {
 void oracle_q1_levels(uint16_t lo16, uint16_t hi16, int bits, float* lev) {
     build_tables();
     level_table(lo16, hi16, 1 << bits, lev);
+}
+
+/* The levels of n blocks at once: ends[i] holds block i's fp16 endpoints
+ * (lower in the low 16 bits), lev[i * 2^bits + k] its level k. */
+void oracle_q1_levels_batch(const uint32_t* ends, size_t n, int bits, float* lev) {
+    build_tables();
+    const int L = 1 << bits;
+    for (size_t i = 0; i < n; ++i)
+        level_table((uint16_t)(ends[i] & 0xFFFFu), (uint16_t)(ends[i] >> 16), L, lev + i * (size_t)L);
 }
 
 /* 1Q encode of one block of len (<= 128) second-moment values with draws u:

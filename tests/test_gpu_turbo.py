@@ -3,6 +3,9 @@ the oracle, value by value and bit for bit: parameters, 2-bit codes, bf16
 means, 1Q indices, fp16 endpoints, tensor scales, and the FP32 moments of
 tensors that keep them.  Sizes span tiles, blocks and groups with ragged
 tails; lists mix the four representation pairs and the three index widths."""
+import json
+import os
+
 import numpy as np
 import pytest
 
@@ -200,6 +203,57 @@ def test_q1_endpoints_every_float(pa):
                                 f"{lo_bits + int(diff[0]):#x}: {got[diff[0]]:#010x} vs {want[diff[0]]:#010x}")
         del bits, x, out
     assert bad == 0
+
+
+TIES = json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                                   "q1_level_ties.json")))["rows"]
+
+
+def _f16_code(x):
+    return int(np.array([x], np.float16).view(np.uint16)[0])
+
+
+def _endpoint_words(r, n):
+    """n random endpoint words, lower <= upper, over every finite fp16 in [-149, 128]."""
+    codes = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = codes.view(np.float16).astype(np.float64)
+    pool = codes[np.isfinite(vals) & (vals >= -149) & (vals <= 128)]
+    a, b = r.choice(pool, n), r.choice(pool, n)
+    swap = a.view(np.float16) > b.view(np.float16)
+    lo, hi = np.where(swap, b, a), np.where(swap, a, b)
+    return lo.astype(np.uint32) | (hi.astype(np.uint32) << 16)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_q1_levels_match_oracle(pa, bits):
+    """1Q grid levels (the exact 2^x rounded once to binary32) equal the
+    oracle's bit for bit, through the step's own route (the device exp2,
+    with the double-double evaluation near binary32 midpoints) and through
+    the double-double evaluation alone: 16M levels of random blocks across
+    the whole endpoint range, the committed near-midpoint blocks, one-level
+    blocks, and the range ends (+inf at 128, the smallest subnormal at -149)."""
+    import torch
+    n = {2: 1 << 22, 4: 1 << 20, 8: 1 << 16}[bits]
+    words = _endpoint_words(np.random.default_rng(40 + bits), n)
+    sel = [t for t in TIES if t["bits"] == bits]
+    ties = [int(t["lo16"], 16) | (int(t["hi16"], 16) << 16) for t in sel]
+    ends = [_f16_code(e) * 0x10001 for e in (-149, -126, -1, 0, 1, 127, 128)]
+    ends += [_f16_code(120) | (_f16_code(128) << 16), _f16_code(-149) | (_f16_code(-100) << 16)]
+    words = np.concatenate([np.array(ties + ends, np.uint32), words])
+    want = oracle.q1_levels_batch(words, bits)
+    d_words = to_dev(words)
+    for exact in (False, True):
+        banner(f"1Q levels: {bits}-bit, {words.size} blocks, exact={exact}")
+        out = torch.empty(words.size << bits, dtype=torch.float32, device="cuda:0")
+        pa.pa_debug_q1_levels(d_words, bits, exact, out)
+        torch.cuda.synchronize()
+        got = to_host(out).reshape(words.size, 1 << bits)
+        bad = np.argwhere(got.view(np.uint32) != want.view(np.uint32))
+        assert bad.size == 0, (f"exact={exact}: {len(bad)} levels differ, first block {words[bad[0][0]]:#010x} "
+                               f"level {bad[0][1]}: {got[tuple(bad[0])]!r} vs {want[tuple(bad[0])]!r}")
+        for j, t in enumerate(sel):
+            assert f"{int(got[j, t['k']:t['k'] + 1].view(np.uint32)[0]):08x}" == t["level_hex"], t
+        del out
 
 
 def test_turbo_residual_tree_past_one_chunk_level(pa):

@@ -1,8 +1,8 @@
 """Pins of the oracle's TurboAdam state (UState first moment, 1Q second
 moment) against what the page prints and what mathematics and independent
 libraries fix: Philox4x32-10's published known-answer vectors and Triton's
-own philox (run by its CPU interpreter), numpy's binary16 and exp2, torch's
-bfloat16 cast, math.fsum, the plain FP32 AdamW oracle (the uncompressed
+own philox (run by its CPU interpreter), numpy's binary16, a 60-digit decimal
+power of two (the grid levels), torch's bfloat16 cast, math.fsum, the plain FP32 AdamW oracle (the uncompressed
 identity), closed forms, and the unbiasedness of stochastic rounding over a
 fine grid of draws.
 
@@ -17,6 +17,7 @@ import numpy as np
 import pytest
 
 import oracle
+from exact_pow2 import grid_x as _grid_x, rn32_pow2 as _rn32_pow2
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 FACTS = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_facts.json")))["turboadam_state"]
@@ -111,6 +112,7 @@ def _f16_bits(x):
     return int(np.array([x], np.float16).view(np.uint16)[0])
 
 
+
 def test_q1_endpoints_and_levels(oracle_mod):
     r = np.random.default_rng(4)
     for bits in (2, 4, 8):
@@ -124,7 +126,7 @@ def test_q1_endpoints_and_levels(oracle_mod):
             assert hi >= l2max and float(np.nextafter(np.float16(hi), np.float16(-np.inf))) < l2max
             lev = oracle.q1_levels(ends[0], ends[1], bits)
             L = 1 << bits
-            want = [0.0] + [float(np.float32(np.exp2(lo + (hi - lo) * (k - 1) / (L - 2)))) for k in range(1, L)]
+            want = [np.float32(0)] + [_rn32_pow2(_grid_x(lo, hi, k, L))[0] for k in range(1, L)]
             assert np.array_equal(lev, np.array(want, np.float32))
             assert lev[1] <= v.min() and lev[-1] >= v.max()
             assert np.all(np.diff(lev[1:]) >= 0)
@@ -132,6 +134,49 @@ def test_q1_endpoints_and_levels(oracle_mod):
             # each value lands on one of its two bracketing levels
             for x, k in zip(v, idx):
                 assert lev[k] == x or (k > 1 and lev[k - 1] < x < lev[k]) or (k < L - 1 and lev[k] < x < lev[k + 1])
+
+
+TIES = json.load(open(os.path.join(ROOT, "tests", "golden", "q1_level_ties.json")))
+
+
+def _f16(code):
+    return float(np.array([code], np.uint16).view(np.float16)[0])
+
+
+@pytest.mark.parametrize("row", TIES["rows"], ids=lambda r: f"{r['lo16']}-{r['hi16']}-{r['bits']}-{r['k']}")
+def test_q1_level_near_midpoint(oracle_mod, row):
+    """Levels whose power of two lies within 2^-47 of a binary32 midpoint: the
+    stored oracle level is the exact power rounded once (a double exp2 with a
+    one-ulp error may round these to the other side)."""
+    lo16, hi16, bits, k = int(row["lo16"], 16), int(row["hi16"], 16), row["bits"], row["k"]
+    x = _grid_x(_f16(lo16), _f16(hi16), k, 1 << bits)
+    want, dist = _rn32_pow2(x)
+    assert dist < 2.0 ** -47
+    assert f"{int(np.array([want]).view(np.uint32)[0]):08x}" == row["level_hex"]
+    lev = oracle.q1_levels(lo16, hi16, bits)
+    assert lev[k] == want
+
+
+def test_q1_levels_exact_powers_and_range_ends(oracle_mod):
+    """Integer exponents give exact powers of two; lo = hi gives one level;
+    the grid's top at 128 is +inf and its bottom at -149 the smallest
+    subnormal; random endpoint pairs across the whole range match the exact
+    power."""
+    for e in (-149, -126, -1, 0, 1, 127):
+        lev = oracle.q1_levels(_f16_bits(e), _f16_bits(e), 4)
+        assert lev[0] == 0 and np.all(lev[1:] == np.float32(2.0 ** e))
+    lev = oracle.q1_levels(_f16_bits(120.0), _f16_bits(128.0), 2)
+    assert lev[3] == np.inf and lev[2] == np.float32(2.0 ** 124) and lev[1] == np.float32(2.0 ** 120)
+    lev = oracle.q1_levels(_f16_bits(-149.0), _f16_bits(-133.0), 4)
+    assert lev[1] == np.float32(2.0 ** -149)
+    r = np.random.default_rng(12)
+    for _ in range(60):
+        a, b = np.sort(r.uniform(-149, 128, 2)).astype(np.float16)
+        bits = int(r.choice([2, 4, 8]))
+        L = 1 << bits
+        lev = oracle.q1_levels(_f16_bits(a), _f16_bits(b), bits)
+        for k in r.integers(1, L, 4):
+            assert lev[k] == _rn32_pow2(_grid_x(float(a), float(b), int(k), L))[0], (a, b, bits, k)
 
 
 def test_q1_special_values(oracle_mod):

@@ -26,7 +26,7 @@ def test_oracle_under_asan_ubsan(tmp_path):
     exe = str(tmp_path / "oracle_driver")
     b = _run(["gcc", "-O1", "-g", "-std=c11", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
               "-ffp-contract=off", "-o", exe, os.path.join(SAN, "oracle_driver.c"),
-              os.path.join(ROOT, "oracle", "pa_oracle.c"), "-lm"])
+              os.path.join(ROOT, "oracle", "pa_oracle.c"), "-lquadmath", "-lm"])
     assert b.returncode == 0, b.stderr[-4000:]
     r = _run([exe], timeout=600)
     assert r.returncode == 0, (r.stdout + r.stderr)[-4000:]
