@@ -206,6 +206,11 @@ __device__ __forceinline__ bool q1_level_fast(double x, float* out) {
   return a == b;
 }
 
+// A pointer into LDS.  The out-of-line table builders take their tables as
+// such, so that they write them with 32-bit LDS addresses (a plain pointer
+// would arrive as a 64-bit flat address).
+typedef __attribute__((address_space(3))) float lds_float;
+
 // The double-precision exp2 and log2 below are called out of line on
 // purpose: inlined, their polynomial coefficients were hoisted out of the
 // tile loop into about 40 vector registers held for the whole kernel, which
@@ -214,7 +219,7 @@ __device__ __forceinline__ bool q1_level_fast(double x, float* out) {
 // leaves undecided are redone afterwards in one rolled loop, so that the
 // double-double code appears once and its registers stay few.
 template <int BITS>
-__device__ __attribute__((noinline)) void build_levels(float* lev, uint32_t ends, int lane_in_half) {
+__device__ __attribute__((noinline)) void build_levels(lds_float* lev, uint32_t ends, int lane_in_half) {
   constexpr int L = 1 << BITS;
   const double lo = f16_to_double(ends & 0xFFFFu), hi = f16_to_double(ends >> 16);
   uint32_t undecided = 0;   // bit j: level lane_in_half + 32 j
@@ -236,6 +241,42 @@ __device__ __attribute__((noinline)) void build_levels(float* lev, uint32_t ends
     const int k = lane_in_half + 32 * j;
     lev[k] = pow2_rn32_dd(q1_level_x(lo, hi, k, L));
   }
+}
+
+// Offset, within a half-wavefront's LDS slice, of the decode table when
+// indices have at most 4 bits (the encode table sits at 0).
+constexpr int kDecodeTable = 128;
+
+// Tables for indices of at most 4 bits (L <= 16 levels): entry k is the pair
+// (level k, sqrt(level k / bc) + eps), the second being the denominator the
+// UState codec takes from the persisted second moment (bc the bias
+// correction of the step that persisted it, r = RN64(1/bc)).  A block's
+// persisted values are its levels, so each denominator is computed once per
+// level instead of once per value; it is the same correctly rounded
+// function of the same input either way.
+//
+// Lanes 0..L-1 of each half build the table of `ends` at lev (reciprocal
+// r), and, when `two`, lanes 16..16+L-1 build the table of `ends2` at lev2
+// (reciprocal r2) in the same pass.  The encode pass of a tile thus also
+// builds the decode table of the wavefront's next tile on lanes that would
+// otherwise idle.
+template <int BITS>
+__device__ __attribute__((noinline)) void build_tables(lds_float* lev, uint32_t ends, double r, lds_float* lev2,
+                                                       uint32_t ends2, double r2, bool two, float eps, int lane_in_half) {
+  constexpr int L = 1 << BITS;
+  static_assert(L <= 16, "one level per lane");
+  const bool second = lane_in_half >= 16;
+  const int k = lane_in_half & 15;
+  if (k >= L || (second && !two)) return;
+  float a = 0.0f;
+  if (k > 0) {
+    const uint32_t w = second ? ends2 : ends;
+    const double x = q1_level_x(f16_to_double(w & 0xFFFFu), f16_to_double(w >> 16), k, L);
+    if (!q1_level_fast(x, &a)) a = pow2_rn32_dd(x);
+  }
+  lds_float* dst = (second ? lev2 : lev) + 2 * k;
+  dst[0] = a;
+  dst[1] = sqrt_rn(div_uniform(a, second ? r2 : r)) + eps;
 }
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -294,9 +335,14 @@ __device__ __forceinline__ void store_index4(uint8_t* base, long long lane_word,
 // FULL: the tile lies wholly inside its tensor, so every validity test below
 // folds away (one instantiation per case; the partial one runs only on a
 // tensor's last tile).
+// With indices of at most 4 bits, `have_dec` says the decode table is
+// already in the slice (built by the previous tile's encode pass), and
+// `next_dec` asks this tile's encode pass to build the next tile's from the
+// endpoint word `next_ends`.
 template <int BITS, bool FULL>
 __device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, long long tile, const Scalars& s,
-                                           const TurboScalars& ts, float* lev_half, double* ws, uint32_t& bad) {
+                                           const TurboScalars& ts, float* lev_half, double* ws, uint32_t& bad,
+                                           bool have_dec, bool next_dec, uint32_t next_ends) {
   const TurboEntry& e = *ep;
   constexpr int L = 1 << BITS;
   const int lane = threadIdx.x & 63;
@@ -317,6 +363,10 @@ __device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, lo
 
   // ---- loads
   float p[4], g[4], mprev[4] = {0.f, 0.f, 0.f, 0.f}, vprev[4] = {0.f, 0.f, 0.f, 0.f};
+  // The UState decode denominators sqrt(vprev / bc2_{t-1}) + eps, from the
+  // decode table (indices of at most 4 bits, 1Q second moment).
+  constexpr bool kDenTables = BITS <= 4;
+  float dprev[4] = {0.f, 0.f, 0.f, 0.f};
   if (full) {
     const f32x4 pv = stream_load(reinterpret_cast<const f32x4*>(e.p + i0));
     const f32x4 gv = stream_load(reinterpret_cast<const f32x4*>(e.g + i0));
@@ -332,18 +382,41 @@ __device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, lo
       g[k] = valid[k] ? e.g[i0 + k] : 0.0f;
     }
   }
+  // The state words of the prior moments, loaded together with p and g so
+  // that one memory latency covers them all.
+  uint32_t idx4 = 0, mcodes = 0, mean16 = 0;
+  if (ts.step > 1 && valid[0]) {
+    if (cv) idx4 = load_index4<BITS>(e.v_index, i0 >> 2);
+    if (cm) {
+      mcodes = e.m_codes[i0 >> 2];
+      mean16 = e.m_means[grp];
+    }
+  }
   const float s_dec = cm ? e.scal[0] : 0.0f, s_enc = cm ? e.scal[1] : 0.0f;
-  uint32_t mcodes = 0;
 
   // ---- decode the prior moments (the state is empty at step 1)
   if (ts.step > 1) {
     if (cv) {
-      const uint32_t ends = blk_exists ? *reinterpret_cast<const uint32_t*>(e.v_ends + 2 * blk) : 0u;
-      build_levels<BITS>(lev_half, ends, lane_in_half);
-      wave_lds_sync();
-      const uint32_t idx4 = valid[0] ? load_index4<BITS>(e.v_index, i0 >> 2) : 0u;
+      float* dec = BITS <= 4 ? lev_half + kDecodeTable : lev_half;
+      if (BITS > 4 || !have_dec) {
+        const uint32_t ends = blk_exists ? *reinterpret_cast<const uint32_t*>(e.v_ends + 2 * blk) : 0u;
+        if constexpr (BITS <= 4)
+          build_tables<BITS>((lds_float*)dec, ends, ts.inv_bc2p, (lds_float*)dec, 0u, 0.0, false, s.eps, lane_in_half);
+        else
+          build_levels<BITS>((lds_float*)dec, ends, lane_in_half);
+        wave_lds_sync();
+      }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) vprev[k] = valid[k] ? lev_half[(idx4 >> (BITS * k)) & (L - 1)] : 0.0f;
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t ix = (idx4 >> (BITS * k)) & (L - 1);
+        if constexpr (BITS <= 4) {
+          const float2 entry = reinterpret_cast<const float2*>(dec)[ix];
+          vprev[k] = valid[k] ? entry.x : 0.0f;
+          dprev[k] = entry.y;
+        } else {
+          vprev[k] = valid[k] ? dec[ix] : 0.0f;
+        }
+      }
       wave_lds_sync();
     } else if (full) {
       const f32x4 vv = *reinterpret_cast<const f32x4*>(e.v_fp32 + i0);
@@ -354,17 +427,16 @@ __device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, lo
       for (int k = 0; k < 4; ++k) vprev[k] = valid[k] ? e.v_fp32[i0 + k] : 0.0f;
     }
     if (cm) {
-      mcodes = valid[0] ? e.m_codes[i0 >> 2] : 0u;
       int s2 = 0;                                        // sum of 2 * level over this lane's values
 #pragma unroll
       for (int k = 0; k < 4; ++k) s2 += valid[k] ? (int)(2 * ((mcodes >> (2 * k)) & 3u)) - 3 : 0;
       s2 = butterfly_isum<16>(s2);
       const float lbar = (float)((double)s2 * 0.5 / (double)glen);
-      const float mean = valid[0] ? __uint_as_float((uint32_t)e.m_means[grp] << 16) : 0.0f;
+      const float mean = __uint_as_float(mean16 << 16);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const float q = mean + s_dec * (ustate_level((mcodes >> (2 * k)) & 3u) - lbar);
-        const float den = sqrt_rn(div_uniform(vprev[k], ts.inv_bc2p)) + s.eps;
+        const float den = (kDenTables && cv) ? dprev[k] : sqrt_rn(div_uniform(vprev[k], ts.inv_bc2p)) + s.eps;
         mprev[k] = valid[k] ? (q * ts.bc1p) * den : 0.0f;
       }
     } else if (full) {
@@ -402,7 +474,10 @@ __device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, lo
   const uint32_t sk0 = (uint32_t)e.seed, sk1 = (uint32_t)(e.seed >> 32);
 
   // ---- second moment: 1Q per block, or FP32
-  float vp[4];
+  // vq: with a 1Q table of at most 4-bit indices, the UState encode
+  // denominator sqrt(v_persisted / bc2) + eps looked up with each value's
+  // index; otherwise the persisted second moment it is computed from.
+  float vq[4];
   if (cv) {
     uint32_t w[4];
     philox4x32_10(ctr, stp, tid, 0u, sk0, sk1, w);
@@ -422,7 +497,13 @@ __device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, lo
     const int src = half << 5;
     const uint32_t lo16 = (uint32_t)__shfl((int)e16, src, 64), hi16 = (uint32_t)__shfl((int)e16, src + 1, 64);
     const uint32_t ends = vmax > 0.0f ? (lo16 | (hi16 << 16)) : 0u;
-    build_levels<BITS>(lev_half, ends, lane_in_half);
+    if constexpr (BITS <= 4)
+      build_tables<BITS>((lds_float*)lev_half, ends, s.inv_bc2, (lds_float*)(lev_half + kDecodeTable), next_ends,
+                         ts.inv_bc2p, next_dec, s.eps, lane_in_half);
+    else
+      build_levels<BITS>((lds_float*)lev_half, ends, lane_in_half);
+    // level k of the encode table
+    constexpr int kStride = BITS <= 4 ? 2 : 1;
     wave_lds_sync();
     uint32_t idx4 = 0;
 #pragma unroll
@@ -434,16 +515,17 @@ __device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, lo
 #pragma unroll
       for (int step = L >> 1; step >= 1; step >>= 1) {
         const int c = kk + step;
-        kk = (c < L && lev_half[c < L ? c : L - 1] <= v) ? c : kk;
+        kk = (c < L && lev_half[kStride * (c < L ? c : L - 1)] <= v) ? c : kk;
       }
-      const float lk = lev_half[kk], lk1 = lev_half[kk < L - 1 ? kk + 1 : kk];
+      const float lk = lev_half[kStride * kk], lk1 = lev_half[kStride * (kk < L - 1 ? kk + 1 : kk)];
       const float f = __fdiv_rn(v - lk, lk1 - lk);
       const float u = (float)(w[k] >> 8) * 0x1p-24f;
       const uint32_t up = (kk < L - 1 && v > lk && u < f) ? 1u : 0u;
       uint32_t idx = (uint32_t)kk + up;
       idx = __builtin_isinf(v) ? (uint32_t)(L - 1) : idx;
       idx = v > 0.0f ? idx : 0u;                            // zero, negative, NaN
-      vp[k] = lev_half[idx];
+      if constexpr (BITS <= 4) vq[k] = reinterpret_cast<const float2*>(lev_half)[idx].y;
+      else vq[k] = lev_half[idx];
       idx4 |= valid[k] ? idx << (BITS * k) : 0u;           // padding past the end stays zero
     }
     wave_lds_sync();
@@ -451,7 +533,7 @@ __device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, lo
     if (lane_in_half == 0 && blk_exists) *reinterpret_cast<uint32_t*>(e.v_ends + 2 * blk) = ends;
   } else {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) vp[k] = v1[k];
+    for (int k = 0; k < 4; ++k) vq[k] = v1[k];
     if (full) {
       f32x4 vv;
 #pragma unroll
@@ -471,7 +553,7 @@ __device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, lo
     float q[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const float den = sqrt_rn(div_bc2(vp[k], s)) + s.eps;
+      const float den = (kDenTables && cv) ? vq[k] : sqrt_rn(div_bc2(vq[k], s)) + s.eps;
       q[k] = valid[k] ? __fdiv_rn(div_uniform(m1[k], ts.inv_bc1), den) : 0.0f;
     }
     const double gsum = butterfly_sum<16>(((double)q[0] + (double)q[1]) + ((double)q[2] + (double)q[3]));
@@ -513,7 +595,7 @@ __device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, lo
 // Persistent launch: global wavefront w takes tiles w, w + W, ...; each
 // wavefront keeps its own cursor in the tensor table (sentinel-terminated).
 template <int BITS, bool COUNT>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(COUNT ? 1 : BITS <= 4 ? 7 : 6)))
 turbo_list(const TurboEntry* __restrict__ table, long long total_tiles, Scalars s, TurboScalars ts, double* ws,
            unsigned long long* nonfinite) {
   __shared__ float lev[kThreads / 64][2][256];
@@ -527,13 +609,38 @@ turbo_list(const TurboEntry* __restrict__ table, long long total_tiles, Scalars 
   const long long nw = (long long)gridDim.x * (kThreads / 64);
   uint32_t bad = 0;
   int t = 0;
+  if (gw < total_tiles)
+    while (gw >= table[t + 1].tile0) ++t;
+  bool have_dec = false;   // the decode table of this tile is in the slice
   for (long long tile = gw; tile < total_tiles; tile += nw) {
-    while (tile >= table[t + 1].tile0) ++t;
     const long long local = tile - table[t].tile0;
+    // The wavefront's next tile: its entry, and (indices of at most 4 bits,
+    // step > 1, both tensors with 1Q state) the endpoints of its block, so
+    // that this tile's encode pass builds its decode table.
+    const long long nt = tile + nw;
+    int u = t;
+    bool next_dec = false;
+    uint32_t next_ends = 0u;
+    if constexpr (BITS <= 4) {
+      if (nt < total_tiles)
+        while (nt >= table[u + 1].tile0) ++u;
+      if (ts.step > 1 && nt < total_tiles && (table[t].flags & 2) && (table[u].flags & 2)) {
+        next_dec = true;
+        const long long nblk = (nt - table[u].tile0) * (kTurboTile / kTurboBlock) + half;
+        if (nblk * kTurboBlock < table[u].n)
+          next_ends = *reinterpret_cast<const uint32_t*>(table[u].v_ends + 2 * nblk);
+      }
+    }
     if ((local + 1) * kTurboTile <= table[t].n)
-      turbo_tile<BITS, true>(table + t, local, s, ts, lev[wave][half], ws, bad);
+      turbo_tile<BITS, true>(table + t, local, s, ts, lev[wave][half], ws, bad, have_dec, next_dec, next_ends);
     else
-      turbo_tile<BITS, false>(table + t, local, s, ts, lev[wave][half], ws, bad);
+      turbo_tile<BITS, false>(table + t, local, s, ts, lev[wave][half], ws, bad, have_dec, next_dec, next_ends);
+    have_dec = next_dec;
+    if constexpr (BITS <= 4) {
+      t = u;
+    } else if (nt < total_tiles) {
+      while (nt >= table[t + 1].tile0) ++t;
+    }
   }
   if constexpr (COUNT) flush_count(bad, nonfinite);
 }
