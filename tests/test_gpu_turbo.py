@@ -86,6 +86,21 @@ def test_turbo_mixed_representations(pa):
     _run(pa, sizes, flags, 4, steps=4, seed=7)
 
 
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_turbo_several_tiles_per_wavefront(pa, bits):
+    """A list of about 27,800 tiles, over three times the wavefronts a full
+    grid holds (256 CUs x 8 workgroups x 4), so every wavefront takes tiles
+    of several tensors in turn. That exercises, across tensors of every
+    representation pair and across ragged tails: the next tile's decode
+    table built during this tile's encode pass (indices of at most 4 bits),
+    the endpoint word loaded for it, and the cursor over the tensor table."""
+    sizes = [1500001, 3, 900017, 129, 1200003, 257, 700007, 65, 1000011, 4097, 800013, 1, 600009, 12345,
+             400001, 255]
+    flags = [(True, True), (False, True), (True, False), (False, False)] * 4
+    assert sum((n + 255) // 256 for n in sizes) > 3 * 256 * 8 * 4
+    _run(pa, sizes, flags, bits, steps=3, seed=40 + bits)
+
+
 def test_turbo_large_tensor(pa):
     _run(pa, [1 << 20, 3 * 65536 + 11], [(True, True), (True, True)], 4, steps=3, seed=9)
 
