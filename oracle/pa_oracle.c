@@ -648,7 +648,8 @@ void oracle_scale_grads(int gdt, const void* g, float scale, float* out, size_t 
  *
  *  1Q, L = 2^bits indices: index 0 is exactly 0; index k in 1..L-1 decodes to
  *    level_k = RN32(2^x), x = lo + (hi - lo) * (k - 1) / (L - 2) in double
- *    and 2^x the exact power (not a double exp2 rounded again), where lo and hi are the block's fp16 endpoints: log2 (in double) of the
+ *    and 2^x the exact power (not a double exp2 rounded again), where lo
+ *    and hi are the block's fp16 endpoints: log2 (in double) of the
  *    smallest positive finite v rounded down to fp16, and of the largest
  *    rounded up.  Encode: 0 -> 0, NaN -> 0, +Inf -> L-1; else the largest k
  *    with level_k <= v (at least 1), then k+1 with probability
