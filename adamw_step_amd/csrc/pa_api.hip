@@ -1117,11 +1117,17 @@ int pa_debug_q1_levels(const uint32_t* ends, int bits, int exact, float* out, si
   DeviceInfo d;
   int rc = device_info(&dev, &d);
   if (rc) return rc;
-  const long long total = (long long)n << bits;
-  const long long blocks = (total + pa::kThreads - 1) / pa::kThreads;
+  // One half-wavefront per endpoint word: eight words per workgroup.
+  const long long blocks = ((long long)n + 2 * (pa::kThreads / 64) - 1) / (2 * (pa::kThreads / 64));
   const dim3 grid((unsigned)grid_for(blocks, d, d.blocks_per_cu)), block(pa::kThreads);
-  hipLaunchKernelGGL(pa::q1_levels_kernel, grid, block, 0, static_cast<hipStream_t>(stream), ends, bits,
-                     exact ? 1 : 0, out, total);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int ex = exact ? 1 : 0;
+  if (bits == 2)
+    hipLaunchKernelGGL(pa::q1_levels_kernel<2>, grid, block, 0, st, ends, ex, out, (long long)n);
+  else if (bits == 4)
+    hipLaunchKernelGGL(pa::q1_levels_kernel<4>, grid, block, 0, st, ends, ex, out, (long long)n);
+  else
+    hipLaunchKernelGGL(pa::q1_levels_kernel<8>, grid, block, 0, st, ends, ex, out, (long long)n);
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? PA_OK : hip_failed(e);
 }

@@ -211,34 +211,51 @@ __device__ __forceinline__ bool q1_level_fast(double x, float* out) {
 // would arrive as a 64-bit flat address).
 typedef __attribute__((address_space(3))) float lds_float;
 
-// The double-precision exp2 and log2 below are called out of line on
-// purpose: inlined, their polynomial coefficients were hoisted out of the
-// tile loop into about 40 vector registers held for the whole kernel, which
-// cut occupancy from 7 to 4 wavefronts per SIMD; a call per table costs a
-// few instructions against thousands per tile.  The levels the device exp2
-// leaves undecided are redone afterwards in one rolled loop, so that the
+// The table builders and the exact log2 below are called out of line on
+// purpose: inlined, the double-precision polynomial coefficients were
+// hoisted out of the tile loop into about 40 vector registers held for the
+// whole kernel, which cut occupancy from 7 to 4 wavefronts per SIMD; a call
+// per table costs a few instructions against thousands per tile.  Levels
+// left undecided are redone afterwards in one rolled loop, so that the
 // double-double code appears once and its registers stay few.
+//
+// 8-bit tables (L = 256): lane j of a half builds levels j, j + 32, ...,
+// j + 224 (lane 0 starts at 32; level 0 is 0).  The levels form a geometric
+// grid, so after its first level y = exp2(x_k0) the lane multiplies by
+// C = exp2(32 d), d = RN64((hi - lo) / (L - 2)), instead of calling exp2
+// for each level.  Level k is the exact power 2^x_k of its own double x_k
+// (q1_level_x).  With |lo|, |hi| <= 256 the product is within 2^-42
+// (relative) of it: the exponents differ by the roundings in x_k, x_k0 and
+// 32 m d (below 2^-42 absolute together, scaled by ln 2 in the value), and
+// the two exp2 and up to seven products add below 2^-48.  So when every
+// value within 2^-40 of the product rounds to the same binary32 value, so
+// does 2^x_k; otherwise (about one level in 2^15) the double-double
+// evaluation decides, as it does for every level of endpoints outside that
+// range (no block has them: its endpoints lie in [-149, 128]).
 template <int BITS>
 __device__ __attribute__((noinline)) void build_levels(lds_float* lev, uint32_t ends, int lane_in_half) {
   constexpr int L = 1 << BITS;
+  static_assert(L == 256, "32 lanes, 8 levels each");
   const double lo = f16_to_double(ends & 0xFFFFu), hi = f16_to_double(ends >> 16);
-  uint32_t undecided = 0;   // bit j: level lane_in_half + 32 j
+  const int k0 = lane_in_half == 0 ? 32 : lane_in_half;
+  if (lane_in_half == 0) lev[0] = 0.0f;
+  double y = exp2(q1_level_x(lo, hi, k0, L));
+  const double c = exp2(32.0 * ((hi - lo) / (double)(L - 2)));
+  const bool in_range = __builtin_fabs(lo) <= 256.0 && __builtin_fabs(hi) <= 256.0;
+  uint32_t undecided = 0;   // bit j: level k0 + 32 j
 #pragma unroll
-  for (int j = 0; j * 32 < L; ++j) {
-    const int k = lane_in_half + 32 * j;
+  for (int j = 0; j < 8; ++j) {
+    const int k = k0 + 32 * j;
     if (k >= L) break;
-    if (k == 0) {
-      lev[0] = 0.0f;
-      continue;
-    }
-    float a;
-    if (!q1_level_fast(q1_level_x(lo, hi, k, L), &a)) undecided |= 1u << j;
+    const float a = (float)(y * (1.0 - 0x1p-40)), b = (float)(y * (1.0 + 0x1p-40));
+    if (!in_range || a != b) undecided |= 1u << j;
     lev[k] = a;
+    y *= c;
   }
   while (undecided) {
     const int j = __builtin_ctz(undecided);
     undecided &= undecided - 1;
-    const int k = lane_in_half + 32 * j;
+    const int k = k0 + 32 * j;
     lev[k] = pow2_rn32_dd(q1_level_x(lo, hi, k, L));
   }
 }
@@ -744,23 +761,36 @@ __global__ void __launch_bounds__(kThreads) q1_ends_kernel(const float* in, uint
   }
 }
 
-// Self-test export: level k of the endpoint word ends[i / L] at out[i], for
-// i < total = n L; exact != 0 takes every level through the double-double
-// path.
-__global__ void __launch_bounds__(kThreads) q1_levels_kernel(const uint32_t* ends, int bits, int exact,
-                                                            float* out, long long total) {
-  const int L = 1 << bits;
-  for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < total; i += (long long)gridDim.x * kThreads) {
-    const uint32_t w = ends[i >> bits];
-    const int k = (int)(i & (L - 1));
-    const double lo = f16_to_double(w & 0xFFFFu), hi = f16_to_double(w >> 16);
-    if (k == 0) {
-      out[i] = 0.0f;
+// Self-test export: the levels of endpoint word ends[w] at out[w L + k],
+// one half-wavefront per word.  exact = 0: through the step's own table
+// builders (build_tables for indices of at most 4 bits, build_levels for
+// 8); exact != 0: every level through the double-double evaluation.
+template <int BITS>
+__global__ void __launch_bounds__(kThreads) q1_levels_kernel(const uint32_t* ends, int exact, float* out, long long n) {
+  constexpr int L = 1 << BITS;
+  __shared__ float lev[kThreads / 64][2][256];
+  const int lane = threadIdx.x & 63, half = lane >> 5, lane_in_half = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  float* t = lev[wave][half];
+  const long long nw = (long long)gridDim.x * (kThreads / 64);
+  for (long long pw = (long long)blockIdx.x * (kThreads / 64) + wave; 2 * pw < n; pw += nw) {
+    const long long w = 2 * pw + half;
+    const uint32_t word = w < n ? ends[w] : 0u;
+    if (exact) {
+      const double lo = f16_to_double(word & 0xFFFFu), hi = f16_to_double(word >> 16);
+      for (int k = lane_in_half; k < L; k += 32)
+        if (w < n) out[w * L + k] = k == 0 ? 0.0f : pow2_rn32_slow(q1_level_x(lo, hi, k, L));
       continue;
     }
-    const double x = q1_level_x(lo, hi, k, L);
-    float a;
-    out[i] = (!exact && q1_level_fast(x, &a)) ? a : pow2_rn32_slow(x);
+    if constexpr (BITS <= 4)
+      build_tables<BITS>((lds_float*)t, word, 1.0, (lds_float*)t, 0u, 1.0, false, 0.0f, lane_in_half);
+    else
+      build_levels<BITS>((lds_float*)t, word, lane_in_half);
+    wave_lds_sync();
+    constexpr int kStride = BITS <= 4 ? 2 : 1;
+    for (int k = lane_in_half; k < L; k += 32)
+      if (w < n) out[w * L + k] = t[kStride * k];
+    wave_lds_sync();
   }
 }
 

@@ -339,9 +339,10 @@ int pa_debug_q1_ends(const float* in, uint32_t* out, size_t n, void* stream);
  * L = 2^bits (bits 2, 4 or 8), out[i*L + k] = level k of that block as the
  * TurboAdam step decodes it (TurboAdam package page, 1Q): 0 for k = 0, else
  * the exact power 2^x, x = lo + (hi - lo)(k - 1)/(L - 2) in double, rounded
- * once to binary32.  exact = 0 takes the step's own route (the device exp2,
- * with the double-double evaluation deciding near binary32 midpoints);
- * exact != 0 takes every level through the double-double evaluation.  out
+ * once to binary32.  exact = 0 takes the step's own table builders (the
+ * device exp2, or for 8-bit indices a geometric recurrence, with a
+ * double-double evaluation deciding near binary32 midpoints); exact != 0
+ * takes every level through the double-double evaluation.  out
  * holds n*L floats.  PA_ERR_ARG for another width, null pointers or
  * n > 2^40.  Asynchronous on `stream`. */
 int pa_debug_q1_levels(const uint32_t* ends, int bits, int exact, float* out, size_t n, void* stream);

@@ -242,9 +242,10 @@ def _endpoint_words(r, n):
 @pytest.mark.parametrize("bits", [2, 4, 8])
 def test_q1_levels_match_oracle(pa, bits):
     """1Q grid levels (the exact 2^x rounded once to binary32) equal the
-    oracle's bit for bit, through the step's own route (the device exp2,
-    with the double-double evaluation near binary32 midpoints) and through
-    the double-double evaluation alone: 16M levels of random blocks across
+    oracle's bit for bit, through the step's own table builders (the device
+    exp2, or the geometric recurrence of 8-bit tables, with the
+    double-double evaluation near binary32 midpoints) and through the
+    double-double evaluation alone: 16M levels of random blocks across
     the whole endpoint range, the committed near-midpoint blocks, one-level
     blocks, and the range ends (+inf at 128, the smallest subnormal at -149)."""
     import torch
