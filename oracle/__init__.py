@@ -96,6 +96,8 @@ def _load():
     lib.oracle_q1_levels.restype = None
     lib.oracle_q1_levels_batch.argtypes = [_u32p, ctypes.c_size_t, ctypes.c_int, _f32p]
     lib.oracle_q1_levels_batch.restype = None
+    lib.oracle_exp2_rn32_batch.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.c_size_t, _f32p]
+    lib.oracle_exp2_rn32_batch.restype = None
     lib.oracle_q1_ends_batch.argtypes = [_f32p, _u32p, ctypes.c_size_t]
     lib.oracle_q1_ends_batch.restype = None
     lib.oracle_q1_block.argtypes = [_f32p, ctypes.c_size_t, ctypes.c_int, _f32p, _u8p, _u16p, _f32p]
@@ -334,6 +336,15 @@ def q1_levels(lo16, hi16, bits):
     """Decoded value of every 1Q index of a block with fp16 endpoints (bits)."""
     out = np.zeros(1 << bits, np.float32)
     _load().oracle_q1_levels(int(lo16), int(hi16), int(bits), _ptr(out, _f32p))
+    return out
+
+
+def exp2_rn32(x):
+    """RN32 of the exact power 2^x for each double x: the rounding of the 1Q
+    grid levels on its own."""
+    a = np.ascontiguousarray(x, np.float64)
+    out = np.zeros(a.size, np.float32)
+    _load().oracle_exp2_rn32_batch(a.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), a.size, _ptr(out, _f32p))
     return out
 
 

@@ -801,6 +801,12 @@ void oracle_q1_levels(uint16_t lo16, uint16_t hi16, int bits, float* lev) {
     level_table(lo16, hi16, 1 << bits, lev);
 }
 
+/* RN32(2^x) for n doubles x (the level rounding of exp2_rn32 alone, so
+ * that the tests can reach its binary128 branch with x near midpoints). */
+void oracle_exp2_rn32_batch(const double* x, size_t n, float* out) {
+    for (size_t i = 0; i < n; ++i) out[i] = exp2_rn32(x[i]);
+}
+
 /* The levels of n blocks at once: ends[i] holds block i's fp16 endpoints
  * (lower in the low 16 bits), lev[i * 2^bits + k] its level k. */
 void oracle_q1_levels_batch(const uint32_t* ends, size_t n, int bits, float* lev) {

@@ -52,3 +52,21 @@ def rn32_pow2(x):
 def grid_x(lo, hi, k, L):
     """The exponent of 1Q level k >= 1 between fp16 log2 endpoints lo and hi."""
     return lo + ((hi - lo) * (k - 1)) / (L - 2)
+
+
+def near_midpoint_exponents(seed, n_near_one=6000, n_wide=2000):
+    """Doubles x whose power 2^x lies very close to a binary32 midpoint:
+    x = log2(m), rounded to double, for seeded random midpoints m between
+    adjacent binary32 values.  Most m have exponents in [-6, 5], where |x|
+    is small and its double is fine enough that 2^x often falls within
+    2^-56 of m; the rest span every binade, the subnormal ones included.
+    Input construction only (numpy's long-double log2 picks x)."""
+    r = np.random.default_rng(seed)
+    e = r.integers(-6, 6, n_near_one)
+    mant = r.integers(0, 1 << 23, n_near_one)
+    near = ((e + 127).astype(np.uint32) << 23) | mant.astype(np.uint32)
+    wide = r.integers(1, 0x7F7FFFFF, n_wide, dtype=np.int64).astype(np.uint32)
+    a = np.concatenate([near, wide]).view(np.float32)
+    b = np.nextafter(a, np.float32(np.inf))
+    m = (a.astype(np.longdouble) + b.astype(np.longdouble)) / 2
+    return np.log2(m).astype(np.float64)

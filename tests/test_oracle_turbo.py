@@ -17,7 +17,7 @@ import numpy as np
 import pytest
 
 import oracle
-from exact_pow2 import grid_x as _grid_x, rn32_pow2 as _rn32_pow2
+from exact_pow2 import grid_x as _grid_x, near_midpoint_exponents, rn32_pow2 as _rn32_pow2
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 FACTS = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_facts.json")))["turboadam_state"]
@@ -177,6 +177,20 @@ def test_q1_levels_exact_powers_and_range_ends(oracle_mod):
         lev = oracle.q1_levels(_f16_bits(a), _f16_bits(b), bits)
         for k in r.integers(1, L, 4):
             assert lev[k] == _rn32_pow2(_grid_x(float(a), float(b), int(k), L))[0], (a, b, bits, k)
+
+
+def test_level_rounding_within_2m56_of_midpoints(oracle_mod):
+    """The level rounding RN32(2^x) on x whose power lies within 2^-56 of a
+    binary32 midpoint, where the 64-bit-significand exp2l cannot decide and
+    the oracle takes its binary128 branch: every one equals the decimal
+    arbiter (about a thousand, some within 2^-64)."""
+    xs = near_midpoint_exponents(11)
+    res = [_rn32_pow2(float(x)) for x in xs]
+    close = np.array([d < 2.0 ** -56 for _, d in res])
+    assert close.sum() > 500 and min(d for _, d in res) < 2.0 ** -64
+    want = np.array([v for v, _ in res], np.float32)
+    got = oracle.exp2_rn32(xs)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
 
 
 def test_q1_special_values(oracle_mod):

@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 import oracle
-from exact_pow2 import grid_x, rn32_pow2
+from exact_pow2 import grid_x, near_midpoint_exponents, rn32_pow2
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 TIES = json.load(open(os.path.join(ROOT, "tests", "golden", "q1_level_ties.json")))["rows"]
@@ -102,3 +102,13 @@ def test_range_ends_and_thresholds(dd):
     for x, g in zip(xs, got):
         want, _ = rn32_pow2(float(x))
         assert (np.isnan(want) and np.isnan(g)) or g.view(np.uint32) == want.view(np.uint32), (x, g, want)
+
+
+def test_within_2m56_of_midpoints(dd):
+    """x whose power lies within 2^-56 of a binary32 midpoint (some within
+    2^-64): the double-double decision equals the decimal arbiter."""
+    xs = near_midpoint_exponents(12)
+    got = dd(xs)
+    for x, g in zip(xs, got):
+        want, _ = rn32_pow2(float(x))
+        assert g.view(np.uint32) == want.view(np.uint32), (x, g, want)
