@@ -86,7 +86,7 @@ class Format(ctypes.Structure):
 
 EXPORTS = ("pa_step", "pa_step_list", "pa_step_typed", "pa_step_list_typed", "pa_state_bytes",
            "pa_format_info", "pa_status_string", "pa_last_hip_error", "pa_release_plans", "pa_debug_codec",
-           "pa_debug_sqrt", "pa_debug_q1_ends", "pa_debug_q1_levels", "pa_grad_stats_list", "pa_turbo_state_bytes", "pa_turbo_workspace_bytes",
+           "pa_debug_sqrt", "pa_debug_q1_ends", "pa_debug_q1_levels", "pa_debug_pow2_rn32", "pa_grad_stats_list", "pa_turbo_state_bytes", "pa_turbo_workspace_bytes",
            "pa_turbo_step_list")
 
 PA_DT_F32, PA_DT_BF16, PA_DT_F16 = 0, 1, 2
@@ -133,6 +133,8 @@ def lib():
     L.pa_debug_q1_ends.restype = ctypes.c_int
     L.pa_debug_q1_levels.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp, sz, vp]
     L.pa_debug_q1_levels.restype = ctypes.c_int
+    L.pa_debug_pow2_rn32.argtypes = [vp, ctypes.c_int, vp, sz, vp]
+    L.pa_debug_pow2_rn32.restype = ctypes.c_int
     L.pa_grad_stats_list.argtypes = [ctypes.c_int, sz, ctypes.POINTER(vp), ctypes.POINTER(sz), ctypes.c_double,
                                      vp, vp, vp, vp]
     L.pa_grad_stats_list.restype = ctypes.c_int
@@ -439,6 +441,19 @@ def pa_debug_q1_levels(ends, bits, exact, out, stream=None):
         raise ValueError("output must hold 2^bits levels per endpoint word")
     _check(lib().pa_debug_q1_levels(_ptr(ends), int(bits), 1 if exact else 0, _ptr(out), ends.numel(),
                                     _stream(stream)))
+
+
+
+def pa_debug_pow2_rn32(x, exact, out, stream=None):
+    """out (float32) = RN32(2^x) for each float64 x, through the 4-bit tables'
+    route or (exact=True) the double-double evaluation alone."""
+    import torch
+
+    _tensor_ok(x, "input")
+    _tensor_ok(out, "output")
+    if x.dtype != torch.float64 or out.dtype != torch.float32 or x.numel() != out.numel():
+        raise ValueError("input must be float64 and output float32, of one size")
+    _check(lib().pa_debug_pow2_rn32(_ptr(x), 1 if exact else 0, _ptr(out), x.numel(), _stream(stream)))
 
 
 # ---------------------------------------------------------------- TurboAdam

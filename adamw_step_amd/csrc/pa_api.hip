@@ -1132,6 +1132,22 @@ int pa_debug_q1_levels(const uint32_t* ends, int bits, int exact, float* out, si
   return e == hipSuccess ? PA_OK : hip_failed(e);
 }
 
+int pa_debug_pow2_rn32(const double* x, int exact, float* out, size_t n, void* stream) {
+  if (n == 0) return PA_OK;
+  if (x == nullptr || out == nullptr) return PA_ERR_ARG;
+  if (!aligned(x, 8) || !aligned(out, 4)) return PA_ERR_ALIGN;
+  int dev;
+  DeviceInfo d;
+  int rc = device_info(&dev, &d);
+  if (rc) return rc;
+  const long long blocks = ((long long)n + pa::kThreads - 1) / pa::kThreads;
+  const dim3 grid((unsigned)grid_for(blocks, d, d.blocks_per_cu)), block(pa::kThreads);
+  hipLaunchKernelGGL(pa::pow2_rn32_kernel, grid, block, 0, static_cast<hipStream_t>(stream), x, exact ? 1 : 0, out,
+                     (long long)n);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PA_OK : hip_failed(e);
+}
+
 int pa_debug_sqrt(const float* in, float* out, size_t n, void* stream) {
   if (n == 0) return PA_OK;
   if (in == nullptr || out == nullptr) return PA_ERR_ARG;

@@ -761,6 +761,17 @@ __global__ void __launch_bounds__(kThreads) q1_ends_kernel(const float* in, uint
   }
 }
 
+// Self-test export: out[i] = RN32(2^x[i]) as the 4-bit tables decide it
+// (the device exp2 with its 2^-48 margin, then the double-double
+// evaluation), or with exact != 0 through the double-double evaluation
+// alone.
+__global__ void __launch_bounds__(kThreads) pow2_rn32_kernel(const double* x, int exact, float* out, long long n) {
+  for (long long i = (long long)blockIdx.x * kThreads + threadIdx.x; i < n; i += (long long)gridDim.x * kThreads) {
+    float a;
+    out[i] = (!exact && q1_level_fast(x[i], &a)) ? a : pow2_rn32_slow(x[i]);
+  }
+}
+
 // Self-test export: the levels of endpoint word ends[w] at out[w L + k],
 // one half-wavefront per word.  exact = 0: through the step's own table
 // builders (build_tables for indices of at most 4 bits, build_levels for

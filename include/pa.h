@@ -347,6 +347,16 @@ int pa_debug_q1_ends(const float* in, uint32_t* out, size_t n, void* stream);
  * n > 2^40.  Asynchronous on `stream`. */
 int pa_debug_q1_levels(const uint32_t* ends, int bits, int exact, float* out, size_t n, void* stream);
 
+/* 1Q level rounding self-test export: out[i] = RN32(2^x[i]), the exact
+ * power of two of the double x[i] rounded once to binary32 (TurboAdam
+ * package page, 1Q: the grid levels), for n device doubles.  exact = 0
+ * takes the route of the 2- and 4-bit tables (the device exp2 decides when
+ * every value within 2^-48 of its result rounds alike, else the
+ * double-double evaluation); exact != 0 takes the double-double evaluation
+ * alone.  x 8-byte aligned, out 4-byte aligned (PA_ERR_ALIGN), non-null
+ * (PA_ERR_ARG).  Asynchronous on `stream`. */
+int pa_debug_pow2_rn32(const double* x, int exact, float* out, size_t n, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -148,6 +148,9 @@ def test_debug_codec_rules(pa):
     assert L.pa_debug_q1_levels(None, 4, 0, FAKE, 4, None) == pa.PA_ERR_ARG
     assert L.pa_debug_q1_levels(FAKE, 4, 1, FAKE + 4096, (1 << 40) + 1, None) == pa.PA_ERR_ARG
     assert L.pa_debug_q1_levels(FAKE + 2, 4, 0, FAKE + 4096, 4, None) == pa.PA_ERR_ALIGN
+    assert L.pa_debug_pow2_rn32(None, 0, None, 0, None) == pa.PA_OK
+    assert L.pa_debug_pow2_rn32(None, 0, FAKE, 4, None) == pa.PA_ERR_ARG
+    assert L.pa_debug_pow2_rn32(FAKE + 4, 0, FAKE + 4096, 4, None) == pa.PA_ERR_ALIGN
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):

@@ -272,6 +272,31 @@ def test_q1_levels_match_oracle(pa, bits):
         del out
 
 
+def test_level_rounding_adversarial_exponents(pa):
+    """RN32(2^x) on the device, through the 4-bit tables' route and through
+    the double-double evaluation alone, equals the oracle's on x whose
+    power lies within 2^-56 (some within 2^-64) of a binary32 midpoint, on
+    x around the overflow threshold and the subnormal midpoints, and on
+    random x over the whole range and past both ends."""
+    import torch
+    from exact_pow2 import near_midpoint_exponents
+    r = np.random.default_rng(13)
+    thr = 128.0 + np.log2(1.0 - 2.0 ** -25)
+    edges = [thr, 128.0, -150.0, -149.0 + np.log2(1.5), -126.0]
+    xs = np.concatenate([near_midpoint_exponents(14), r.uniform(-152, 130, 200000),
+                         np.concatenate([[np.nextafter(e, -np.inf), e, np.nextafter(e, np.inf)] for e in edges])])
+    want = oracle.exp2_rn32(xs)
+    dx = torch.from_numpy(xs).to("cuda:0")
+    for exact in (False, True):
+        banner(f"pow2 rounding: {xs.size} exponents, exact={exact}")
+        out = torch.empty(xs.size, dtype=torch.float32, device="cuda:0")
+        pa.pa_debug_pow2_rn32(dx, exact, out)
+        torch.cuda.synchronize()
+        got = to_host(out)
+        bad = np.nonzero(got.view(np.uint32) != want.view(np.uint32))[0]
+        assert bad.size == 0, f"exact={exact}: {bad.size} differ, first x={xs[bad[0]]!r}: {got[bad[0]]!r} vs {want[bad[0]]!r}"
+
+
 def test_turbo_residual_tree_past_one_chunk_level(pa):
     """A UState tensor of 2^30 + 12,345 values has 4,194,353 tile sums and
     2,049 chunk sums, so the scale's tree takes the chunk pass and two
