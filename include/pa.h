@@ -268,12 +268,12 @@ size_t pa_turbo_state_bytes(int compress_m, int compress_v, int v_bits, size_t n
  * no initialisation and are dead after the call. */
 size_t pa_turbo_workspace_bytes(size_t count, const pa_turbo_state* states, const size_t* n);
 
-/* One TurboAdam step over `count` tensors sharing hyper, config and step (1 to
- * 2^32 - 1, counting this update; PA_ERR_ARG outside): one persistent launch over all tensors (a
- * wavefront per 256 values), then one workgroup per 2048 residual partial
- * sums and one per UState tensor that completes the sum and rotates its
- * scales.  `states` is a host
- * array of count descriptors; `workspace` a device buffer of at least
+/* One TurboAdam step over `count` tensors sharing hyper, config and step
+ * (1 to 2^32 - 1, counting this update; PA_ERR_ARG outside): one persistent
+ * launch over all tensors (a wavefront per 256 values), then one workgroup
+ * per 2048 residual partial sums and one per UState tensor that completes
+ * the sum and rotates its scales.  `states` is a host array of count
+ * descriptors; `workspace` a device buffer of at least
  * pa_turbo_workspace_bytes (8-byte aligned).  The launch plan is cached per
  * distinct list (see pa_release_plans).  Written buffers may not overlap
  * each other, the gradients or the workspace (PA_ERR_ALIAS).  hyper's
