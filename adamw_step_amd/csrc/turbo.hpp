@@ -612,7 +612,7 @@ __device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, lo
 // Persistent launch: global wavefront w takes tiles w, w + W, ...; each
 // wavefront keeps its own cursor in the tensor table (sentinel-terminated).
 template <int BITS, bool COUNT>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(COUNT ? 1 : BITS <= 4 ? 7 : 6)))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BITS <= 4 ? 7 : 6)))
 turbo_list(const TurboEntry* __restrict__ table, long long total_tiles, Scalars s, TurboScalars ts, double* ws,
            unsigned long long* nonfinite) {
   __shared__ float lev[kThreads / 64][2][256];

@@ -31,6 +31,9 @@ Other flags:
   --mode turbo            the TurboAdam compressed-state step (UState first
                           moment, 4-bit 1Q second moment; tensors below 4096
                           values keep FP32 moments, as the page's thresholds)
+  --turbo-bits B          with --mode turbo: 1Q index width, 2, 4 or 8
+  --count-nonfinite       with --mode turbo: count non-finite values, as the
+                          optimizers do by default (the counting kernel)
   --mode gradstats        instead of the step: time the gradient pre-pass
                           (pa_grad_stats_list: sum of squares, non-finite
                           count and clip coefficient) over the workload's
@@ -445,6 +448,8 @@ def run_turbo(args, cfg):
     workloads.device_fill_grads(cfg, 1, gs)
     tl = pa.TurboList(ps, gs, states, v_bits=args.turbo_bits)
     h = dict(workloads.HYPER)
+    if args.count_nonfinite:   # the optimizers' default: the kernel variant that counts
+        h["nonfinite"] = torch.zeros(1, dtype=torch.int64, device="cuda:0")
     torch.cuda.synchronize()
     t = 0
     for _ in range(args.warmup):
@@ -474,7 +479,7 @@ def run_turbo(args, cfg):
     # the counters measured for this kernel source (profiles/), if current.
     valu = None
     vpath = os.path.join(ROOT, "profiles", f"valu_{args.workload}_turbo.json")
-    if os.path.exists(vpath) and args.turbo_bits == 4:      # the counters were taken on the 4-bit kernel
+    if os.path.exists(vpath) and args.turbo_bits == 4 and not args.count_nonfinite:   # the counters' kernel
         with open(vpath) as f:
             vj = json.load(f)
         if vj.get("kernel_sha") == kernel_sha("turbo"):
@@ -485,7 +490,7 @@ def run_turbo(args, cfg):
            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
            "config": {"workload": args.workload, "params": n, "tensors": len(sizes), "mode": f"turbo-ustate-1q{args.turbo_bits}",
                       "state_bytes": state, "state_bits_per_param": round(8 * state / n, 4),
-                      "layout": args.layout},
+                      "layout": args.layout, "count_nonfinite": bool(args.count_nonfinite)},
            "roofline": ({"bound": "alu", "achieved": round(valu * n / (mean_ms / 1e3) / 1e9, 1),
                          "peak": PEAK_VALU_GLANE, "unit": "G VALU lane-instr/s",
                          "frac": round(valu * n / (mean_ms / 1e3) / 1e9 / PEAK_VALU_GLANE, 4),
@@ -493,7 +498,9 @@ def run_turbo(args, cfg):
                         {"bound": "alu", "achieved": None, "peak": PEAK_VALU_GLANE, "unit": "G VALU lane-instr/s",
                          "frac": None}) | {
                         "hbm_achieved_gbps": round(achieved, 1), "hbm_frac": round(achieved / PEAK_GBPS, 4),
-                        "traffic": None, "kernel": f"turbo_list<{args.turbo_bits}> + turbo_chunks + turbo_reduce",
+                        "traffic": None,
+                        "kernel": f"turbo_list<{args.turbo_bits}, {'true' if args.count_nonfinite else 'false'}>"
+                                  " + turbo_chunks + turbo_reduce",
                         "algorithmic_bytes_per_launch": algo, "mean_launch_ms": round(mean_ms, 4),
                         "kernel_sha": kernel_sha("turbo")}}
     if not args.no_cpu_baseline:
@@ -507,7 +514,7 @@ def run_turbo(args, cfg):
             total += k
         hp = [ps[i].cpu().numpy() for i in picked]
         hg = [gs[i].cpu().numpy() for i in picked]
-        hs = [oracle.TurboState(sizes[i], sizes[i] >= 4096, sizes[i] >= 4096, 4) for i in picked]
+        hs = [oracle.TurboState(sizes[i], sizes[i] >= 4096, sizes[i] >= 4096, args.turbo_bits) for i in picked]
         sc = oracle.scalars(h["lr"], h["beta1"], h["beta2"], h["eps"], h["weight_decay"], 1)
         ts = oracle.turbo_scalars(h["beta1"], h["beta2"], 1)
         t1 = time.perf_counter()
@@ -550,6 +557,8 @@ def main():
     ap.add_argument("--region-map", action="store_true")
     ap.add_argument("--turbo-bits", type=int, default=4, choices=[2, 4, 8],
                     help="1Q index width of the TurboAdam mode (the page's default is 4)")
+    ap.add_argument("--count-nonfinite", action="store_true",
+                    help="TurboAdam mode: count non-finite values, as the optimizers do by default")
     ap.add_argument("--layout", default="regions", choices=["regions", "plain"],
                     help="HBM placement of the state streams (see build_workload)")
     args = ap.parse_args()
