@@ -44,7 +44,7 @@ def _compare_state(dev, host, what):
         assert np.array_equal(_host_words(dev.v_fp32, np.uint32), host.v_fp32.view(np.uint32)), f"{what}: v"
 
 
-def _run(pa, sizes, flags, bits, steps, seed, grad_scale=1e-3):
+def _run(pa, sizes, flags, bits, steps, seed, grad_scale=1e-3, count=False):
     import torch
     r = np.random.Generator(np.random.PCG64(seed))
     hp = [r.normal(0, 0.02, n).astype(np.float32) for n in sizes]
@@ -53,14 +53,19 @@ def _run(pa, sizes, flags, bits, steps, seed, grad_scale=1e-3):
     ds = [pa.TurboState(n, "cuda:0", cm, cv, bits, tensor_id=i) for i, (n, (cm, cv)) in enumerate(zip(sizes, flags))]
     grads = [torch.zeros(n, dtype=torch.float32, device="cuda:0") for n in sizes]
     tl = pa.TurboList(dp, grads, ds, v_bits=bits)
+    hyper = dict(H)
+    if count:   # the kernel variant that counts non-finite values (the optimizers' default)
+        hyper["nonfinite"] = torch.zeros(1, dtype=torch.int64, device="cuda:0")
     same = total = 0
     for t in range(1, steps + 1):
         hg = [(r.normal(0, 1, n) * grad_scale * 10.0 ** r.uniform(-2, 1)).astype(np.float32) for n in sizes]
         for gdev, g in zip(grads, hg):
             gdev.copy_(torch.from_numpy(g))
         banner(f"turbo bits {bits} sizes {sizes[:5]}.. step {t}")
-        tl.step(H, t)
+        tl.step(hyper, t)
         torch.cuda.synchronize()
+        if count:
+            assert int(hyper["nonfinite"].item()) == 0
         sc = oracle.scalars(H["lr"], H["beta1"], H["beta2"], H["eps"], H["weight_decay"], t)
         ts = oracle.turbo_scalars(H["beta1"], H["beta2"], t)
         for i in range(len(sizes)):
@@ -86,19 +91,20 @@ def test_turbo_mixed_representations(pa):
     _run(pa, sizes, flags, 4, steps=4, seed=7)
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
-def test_turbo_several_tiles_per_wavefront(pa, bits):
+@pytest.mark.parametrize("bits,count", [(2, False), (4, False), (8, False), (4, True), (8, True)])
+def test_turbo_several_tiles_per_wavefront(pa, bits, count):
     """A list of about 27,800 tiles, over three times the wavefronts a full
     grid holds (256 CUs x 8 workgroups x 4), so every wavefront takes tiles
     of several tensors in turn. That exercises, across tensors of every
     representation pair and across ragged tails: the next tile's decode
     table built during this tile's encode pass (indices of at most 4 bits),
-    the endpoint word loaded for it, and the cursor over the tensor table."""
+    the endpoint word loaded for it, and the cursor over the tensor table;
+    in both kernel variants (with and without the non-finite count)."""
     sizes = [1500001, 3, 900017, 129, 1200003, 257, 700007, 65, 1000011, 4097, 800013, 1, 600009, 12345,
              400001, 255]
     flags = [(True, True), (False, True), (True, False), (False, False)] * 4
     assert sum((n + 255) // 256 for n in sizes) > 3 * 256 * 8 * 4
-    _run(pa, sizes, flags, bits, steps=3, seed=40 + bits)
+    _run(pa, sizes, flags, bits, steps=3, seed=40 + bits, count=count)
 
 
 def test_turbo_large_tensor(pa):
