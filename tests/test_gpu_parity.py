@@ -148,7 +148,10 @@ def test_single_262k_e4_ten_steps(pa):
     banner(f"single-262k: bit-identical params {same}/{10 * p.size}")
 
 
-def _list_workload(pa, cfg, mode, steps):
+def _list_workload(pa, cfg, mode, steps, count=False, grad_scale=None):
+    """The workload's tensor list over `steps` steps against the oracle.
+    count: pass a non-finite counter (the kernel variant that counts);
+    grad_scale: a device gradient scale (the variant that scales)."""
     torch = _torch()
     hp = workloads.host_params(cfg)
     sizes = [a.size for a in hp]
@@ -159,25 +162,39 @@ def _list_workload(pa, cfg, mode, steps):
     else:
         hs = [np.zeros(n, np.uint32) for n in sizes]
         ds = [to_dev(s) for s in hs]
+    extra = {}
+    if count:
+        extra["nonfinite"] = torch.zeros(1, dtype=torch.int64, device="cuda:0")
+    if grad_scale is not None:
+        extra["grad_scale"] = torch.tensor([grad_scale], dtype=torch.float32, device="cuda:0")
     same = total = 0
     for t in range(1, steps + 1):
         hg = workloads.host_grads(cfg, t)
+        if count:   # non-finite gradients in the first, a middle and the last tensor
+            for i in (0, len(hg) // 2, len(hg) - 1):
+                hg[i][[1, hg[i].size // 2, hg[i].size - 1]] = [np.nan, np.inf, -np.inf]
         dg = [to_dev(g) for g in hg]
-        banner(f"{workloads.NAMES[cfg]} mode {mode} step {t}")
-        pa.pa_step_list(mode, dp, dg, ds, hyper(), t)
+        banner(f"{workloads.NAMES[cfg]} mode {mode} step {t} count={count} grad_scale={grad_scale}")
+        pa.pa_step_list(mode, dp, dg, ds, hyper(**extra), t)
         torch.cuda.synchronize()
+        if grad_scale is not None:
+            hg = [oracle.scale_grads(0, g, np.float32(grad_scale)) for g in hg]
         sc = scalars(t)
+        bad = 0
         for i in range(len(sizes)):
             if mode == F32:
-                oracle.step_fp32(hp[i], hg[i], hs[i][0], hs[i][1], sc)
+                bad += oracle.step_fp32(hp[i], hg[i], hs[i][0], hs[i][1], sc)
                 assert_words(to_host(ds[i][0]).view(np.uint32), hs[i][0].view(np.uint32), what="m")
                 assert_words(to_host(ds[i][1]).view(np.uint32), hs[i][1].view(np.uint32), what="v")
             else:
-                oracle.step_packed(mode, hp[i], hg[i], hs[i], sc)
+                bad += oracle.step_packed(mode, hp[i], hg[i], hs[i], sc)
                 assert_words(to_host(ds[i], np.uint32), hs[i], fp16=(mode == F16))
             s, _ = assert_params(to_host(dp[i]), hp[i])
             same += s
             total += sizes[i]
+        if count:
+            assert bad > 0 and int(extra["nonfinite"].item()) == bad
+            extra["nonfinite"].zero_()
     banner(f"{workloads.NAMES[cfg]} mode {mode}: bit-identical params {same}/{total}")
 
 
@@ -188,6 +205,15 @@ def test_gpt_11m_list_e4(pa):
 @pytest.mark.parametrize("mode", [E4, F32, F16])
 def test_gpt2_small_124m_list(pa, mode):
     _list_workload(pa, 3, mode, steps=2)
+
+
+@pytest.mark.parametrize("mode", [E4, F32])
+def test_gpt2_small_124m_list_counting_and_scaled(pa, mode):
+    """The kernel variant that counts non-finite values and scales the
+    gradients (the optimizers' clipped path) over a list of about 30,000
+    tiles, some two dozen per workgroup: bit-exact, and the count equals
+    the oracle's."""
+    _list_workload(pa, 3, mode, steps=2, count=True, grad_scale=0.37)
 
 
 @pytest.mark.parametrize("mode", [E4, F16, F32])
