@@ -270,6 +270,53 @@ def test_determinism_and_plan_cache(pa):
     pa.pa_release_plans()
 
 
+def test_blockwise_counting_many_blocks_per_workgroup(pa):
+    """The counting variant of the blockwise kernel (its own register
+    allocation) on 16,384 blocks, some thirteen per workgroup, over two
+    steps, with NaN and infinite gradients planted in a few blocks: codes,
+    absmax values and BF16 output bit-exact, and the count the oracle's."""
+    torch = _torch()
+    nb = 16384
+    n = nb * 2048
+    qm, qv = workloads.code_maps()
+    r = np.random.Generator(np.random.PCG64(57))
+    p = r.normal(0, 0.02, n).astype(np.float32)
+    mc, vc = np.zeros(n, np.uint8), np.zeros(n, np.uint8)
+    mc[:] = int(np.nonzero(qm == 0.0)[0][0])
+    ma, va = np.zeros(nb, np.float32), np.zeros(nb, np.float32)
+    dmc, dvc = torch.from_numpy(mc.copy()).cuda(), torch.from_numpy(vc.copy()).cuda()
+    dma, dva = to_dev(ma), to_dev(va)
+    dqm, dqv = to_dev(qm), to_dev(qv)
+    pout = torch.zeros(n, dtype=torch.int16, device="cuda:0")
+    hpout = np.zeros(n, np.uint16)
+    dp = to_dev(p)
+    counter = torch.zeros(1, dtype=torch.int64, device="cuda:0")
+    want_bad = 0
+    for t in (1, 2):
+        g = (r.normal(0, 1e-3, n) * np.repeat(10.0 ** r.uniform(-2, 1, nb), 2048)).astype(np.float32)
+        for b, x in ((3, np.nan), (nb // 2 + 1, np.inf), (nb - 2, -np.inf)):
+            g[b * 2048 + 100 * t] = x
+        banner(f"blockwise counting, {nb} blocks, step {t}")
+        pa.pa_step(BW, dp, to_dev(g), (dmc, dma, dvc, dva, dqm, dqv, pout), hyper(nonfinite=counter), t)
+        torch.cuda.synchronize()
+        want_bad += oracle.step_blockwise(p, g, mc, ma, vc, va, qm, qv, hpout, scalars(t))
+        got = to_host(pout, np.uint16)
+        nan_w = ((hpout & 0x7F80) == 0x7F80) & ((hpout & 0x7F) != 0)
+        nan_g = ((got & 0x7F80) == 0x7F80) & ((got & 0x7F) != 0)
+        assert np.array_equal(nan_g, nan_w)
+        np.testing.assert_array_equal(got[~nan_w], hpout[~nan_w])
+        np.testing.assert_array_equal(to_host(dmc), mc)
+        np.testing.assert_array_equal(to_host(dvc), vc)
+        for got, want in ((to_host(dma), ma), (to_host(dva), va)):
+            nan = np.isnan(want)
+            assert np.array_equal(np.isnan(got), nan)
+            np.testing.assert_array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
+        p = (hpout.astype(np.uint32) << 16).view(np.float32)
+        p = np.where(np.isnan(p), np.float32(0), p).astype(np.float32)
+        dp = to_dev(p)
+    assert want_bad > 0 and int(counter.item()) == want_bad
+
+
 def test_blockwise_small_multi_step(pa):
     """Blockwise 8-bit mode on 64 blocks, 5 steps, full oracle; between steps
     the BF16 output becomes the next step's FP32 parameters on both sides."""
