@@ -498,6 +498,66 @@ def test_typed_params_and_grads(pa, mode, pdt, gdt):
             _typed_case(pa, mode, pdt, gdt, n, phase, steps=2, seed=n + phase)
 
 
+@pytest.mark.parametrize("pdt,gdt,count", [(1, 1, False), (2, 0, False), (1, 1, True)])
+def test_typed_lists_several_tiles_per_workgroup(pa, pdt, gdt, count):
+    """16-bit parameter lists of about 20 M values (some 5,000 tiles, about
+    four per workgroup) through StepList, packed E4, two steps: BF16
+    parameters and gradients, FP16 parameters with FP32 gradients, and the
+    BF16 pair through the variant that counts non-finite values and scales
+    the gradients (NaN and infinities planted). New parameters (in their
+    own type) and state words equal the oracle's bit for bit."""
+    torch = _torch()
+    tdt = {0: torch.float32, 1: torch.bfloat16, 2: torch.float16}
+    sizes = [4096 * 1500 + 7, 3, 4096 * 1200 + 1, 70001, 4096 * 2300 + 99]
+    r = np.random.Generator(np.random.PCG64(200 + 10 * pdt + gdt + count))
+
+    def host(x, dt):
+        return x if dt == 0 else oracle.encode(3 if dt == 1 else 2, x)
+
+    def dev(h, dt):
+        if dt == 0:
+            return to_dev(h)
+        return torch.from_numpy(h.view(np.int16).copy()).cuda().view(tdt[dt])
+
+    hp = [host(r.normal(0, 0.02, n).astype(np.float32), pdt) for n in sizes]
+    dp = [dev(h, pdt) for h in hp]
+    dg = [torch.empty(n, dtype=tdt[gdt], device="cuda:0") for n in sizes]
+    hw = [np.zeros(n, np.uint32) for n in sizes]
+    dw = [torch.zeros(n, dtype=torch.int32, device="cuda:0") for n in sizes]
+    sl = pa.StepList(E4, dp, dg, dw)
+    extra, scale = {}, None
+    if count:
+        scale = np.float32(0.5)
+        extra = {"nonfinite": torch.zeros(1, dtype=torch.int64, device="cuda:0"),
+                 "grad_scale": torch.tensor([float(scale)], dtype=torch.float32, device="cuda:0")}
+    for t in (1, 2):
+        g32 = [(r.normal(0, 1, n) * 1e-3).astype(np.float32) for n in sizes]
+        if count:
+            for i in (0, 2, 4):
+                g32[i][[5, sizes[i] // 2, sizes[i] - 1]] = [np.nan, np.inf, -np.inf]
+        hg = [host(g, gdt) for g in g32]
+        for d, g in zip(dg, hg):
+            d.copy_(dev(g, gdt))
+        banner(f"typed list pdt {pdt} gdt {gdt} count {count} step {t}")
+        sl.step(hyper(**extra), t)
+        torch.cuda.synchronize()
+        bad = 0
+        for i in range(len(sizes)):
+            if scale is not None:
+                bad += oracle.step_typed(1, pdt, 0, hp[i], oracle.scale_grads(gdt, hg[i], scale), hw[i], scalars(t))
+            else:
+                bad += oracle.step_typed(1, pdt, gdt, hp[i], hg[i], hw[i], scalars(t))
+            got = dp[i].cpu().view(torch.int16).numpy().view(np.uint16)
+            want = hp[i]
+            nan = (((want & 0x7F80) == 0x7F80) & ((want & 0x7F) != 0) if pdt == 1
+                   else ((want & 0x7C00) == 0x7C00) & ((want & 0x3FF) != 0))
+            np.testing.assert_array_equal(got[~nan], want[~nan])
+            assert_words(dw[i].cpu().numpy().view(np.uint32), hw[i])
+        if count:
+            assert bad > 0 and int(extra["nonfinite"].item()) == bad
+            extra["nonfinite"].zero_()
+
+
 def test_typed_list_bf16(pa):
     """A bfloat16 parameter list through StepList (one launch)."""
     torch = _torch()
