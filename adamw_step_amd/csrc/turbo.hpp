@@ -521,18 +521,41 @@ __device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, lo
       build_levels<BITS>((lds_float*)lev_half, ends, lane_in_half);
     // level k of the encode table
     constexpr int kStride = BITS <= 4 ? 2 : 1;
+    // 8-bit tables: the grid is uniform in log2 between the endpoints, so
+    // a value's bracket is first estimated from the hardware log2.
+    float est_lo = 0.0f, est_scale = 0.0f;
+    if constexpr (BITS == 8) {
+      est_lo = f16_decode(ends & 0xFFFFu);
+      est_scale = (float)(L - 2) / (f16_decode(ends >> 16) - est_lo);
+    }
     wave_lds_sync();
     uint32_t idx4 = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const float v = v1[k];
-      // The largest level at or below v, by binary lifting over the sorted
-      // table (exact for any non-decreasing table, no data-dependent branch).
+      // The largest level k >= 1 at or below v (1 when none is): by binary
+      // lifting over the sorted table (exact for any non-decreasing table,
+      // no data-dependent branch).  8-bit tables try the log2 estimate
+      // first and keep it when the table confirms it; values that are not
+      // positive and finite get their index from the special cases below,
+      // so their estimate is kept unchecked.
       int kk = 1;
+      bool found = false;
+      if constexpr (BITS == 8) {
+        float t = (__builtin_amdgcn_logf(v) - est_lo) * est_scale + 1.0f;
+        t = t >= 1.0f ? t : 1.0f;   // also NaN
+        t = t <= (float)(L - 1) ? t : (float)(L - 1);
+        kk = (int)t;
+        const bool special = !(v > 0.0f) || __builtin_isinf(v);
+        found = special || (lev_half[kk] <= v && (kk == L - 1 || lev_half[kk < L - 1 ? kk + 1 : kk] > v));
+        if (!found) kk = 1;
+      }
+      if (!found) {
 #pragma unroll
-      for (int step = L >> 1; step >= 1; step >>= 1) {
-        const int c = kk + step;
-        kk = (c < L && lev_half[kStride * (c < L ? c : L - 1)] <= v) ? c : kk;
+        for (int step = L >> 1; step >= 1; step >>= 1) {
+          const int c = kk + step;
+          kk = (c < L && lev_half[kStride * (c < L ? c : L - 1)] <= v) ? c : kk;
+        }
       }
       const float lk = lev_half[kStride * kk], lk1 = lev_half[kStride * (kk < L - 1 ? kk + 1 : kk)];
       const float f = __fdiv_rn(v - lk, lk1 - lk);
