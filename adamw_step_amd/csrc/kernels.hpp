@@ -247,8 +247,13 @@ __device__ __forceinline__ void scalar_elem(const Entry& e, long long i, const S
 
 // Tile `tile` (local to tensor e).  Each thread moves four elements per
 // vector access of each stream: 16 bytes for FP32 data, 8 for 16-bit data.
-template <int MODE, int PT, int GT, bool SCALE>
+// SPLIT > 1 takes a whole tile in that many rounds of loads, arithmetic and
+// stores, one after the other: fewer values live at once, so more
+// wavefronts fit (the variants that also count or scale need it).
+template <int MODE, int PT, int GT, bool SCALE, int SPLIT = 1>
 __device__ __forceinline__ void run_tile(const Entry& e, long long tile, const Scalars& s, uint32_t& bad) {
+  static_assert(kUnroll % SPLIT == 0, "whole rounds");
+  constexpr int U = kUnroll / SPLIT;
   using PE = Elem<PT>;
   using GE = Elem<GT>;
   using PV = typename PE::vec4;
@@ -264,59 +269,65 @@ __device__ __forceinline__ void run_tile(const Entry& e, long long tile, const S
     if constexpr (MODE == kModeFp32) {
       f32x4* M = reinterpret_cast<f32x4*>(static_cast<float*>(e.s0) - e.phase);
       f32x4* V = reinterpret_cast<f32x4*>(e.s1 - e.phase);
-      PV p[kUnroll];
-      GV g[kUnroll];
-      f32x4 m[kUnroll], v[kUnroll];
+#pragma unroll 1
+      for (int r = 0; r < SPLIT; ++r) {
+        PV p[U];
+        GV g[U];
+        f32x4 m[U], v[U];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const long long q = q0 + (long long)u * kThreads;
-        p[u] = stream_load(P + q);
-        g[u] = stream_load(G + q);
-        m[u] = stream_load(M + q);
-        v[u] = stream_load(V + q);
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          float pk = PE::widen(p[u][k]), mk = m[u][k], vk = v[u][k];
-          fp32_elem(pk, scaled<SCALE>(GE::widen(g[u][k]), s), mk, vk, s, bad);
-          p[u][k] = PE::narrow(pk);
-          m[u][k] = mk;
-          v[u][k] = vk;
+        for (int u = 0; u < U; ++u) {
+          const long long q = q0 + (long long)(r * U + u) * kThreads;
+          p[u] = stream_load(P + q);
+          g[u] = stream_load(G + q);
+          m[u] = stream_load(M + q);
+          v[u] = stream_load(V + q);
         }
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const long long q = q0 + (long long)u * kThreads;
-        stream_store(P + q, p[u]);
-        stream_store(M + q, m[u]);
-        stream_store(V + q, v[u]);
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            float pk = PE::widen(p[u][k]), mk = m[u][k], vk = v[u][k];
+            fp32_elem(pk, scaled<SCALE>(GE::widen(g[u][k]), s), mk, vk, s, bad);
+            p[u][k] = PE::narrow(pk);
+            m[u][k] = mk;
+            v[u][k] = vk;
+          }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const long long q = q0 + (long long)(r * U + u) * kThreads;
+          stream_store(P + q, p[u]);
+          stream_store(M + q, m[u]);
+          stream_store(V + q, v[u]);
+        }
       }
     } else {
       u32x4* W = reinterpret_cast<u32x4*>(static_cast<uint32_t*>(e.s0) - e.phase);
-      PV p[kUnroll];
-      GV g[kUnroll];
-      u32x4 w[kUnroll];
+#pragma unroll 1
+      for (int r = 0; r < SPLIT; ++r) {
+        PV p[U];
+        GV g[U];
+        u32x4 w[U];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const long long q = q0 + (long long)u * kThreads;
-        p[u] = stream_load(P + q);
-        g[u] = stream_load(G + q);
-        w[u] = stream_load(W + q);
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          float pk = PE::widen(p[u][k]);
-          w[u][k] = packed_elem<MODE>(pk, scaled<SCALE>(GE::widen(g[u][k]), s), w[u][k], s, bad);
-          p[u][k] = PE::narrow(pk);
+        for (int u = 0; u < U; ++u) {
+          const long long q = q0 + (long long)(r * U + u) * kThreads;
+          p[u] = stream_load(P + q);
+          g[u] = stream_load(G + q);
+          w[u] = stream_load(W + q);
         }
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const long long q = q0 + (long long)u * kThreads;
-        stream_store(P + q, p[u]);
-        stream_store(W + q, w[u]);
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            float pk = PE::widen(p[u][k]);
+            w[u][k] = packed_elem<MODE>(pk, scaled<SCALE>(GE::widen(g[u][k]), s), w[u][k], s, bad);
+            p[u][k] = PE::narrow(pk);
+          }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const long long q = q0 + (long long)(r * U + u) * kThreads;
+          stream_store(P + q, p[u]);
+          stream_store(W + q, w[u]);
+        }
       }
     }
   } else {
@@ -349,7 +360,7 @@ elementwise_list(const Entry* __restrict__ table, long long total_tiles, Scalars
   for (long long tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
     while (tile >= table[t + 1].tile0) ++t;
     const Entry e = table[t];
-    run_tile<MODE, PT, GT, SCALE>(e, tile - e.tile0, s, bad);
+    run_tile<MODE, PT, GT, SCALE, (COUNT || SCALE) ? 2 : 1>(e, tile - e.tile0, s, bad);
   }
   if constexpr (COUNT) flush_count(bad, nonfinite);
 }
@@ -361,7 +372,7 @@ elementwise_one(Entry e, long long total_tiles, Scalars s, unsigned long long* n
   if (!resolve_inputs(s)) return;
   uint32_t bad = 0;
   for (long long tile = blockIdx.x; tile < total_tiles; tile += gridDim.x)
-    run_tile<MODE, PT, GT, SCALE>(e, tile, s, bad);
+    run_tile<MODE, PT, GT, SCALE, (COUNT || SCALE) ? 2 : 1>(e, tile, s, bad);
   if constexpr (COUNT) flush_count(bad, nonfinite);
 }
 

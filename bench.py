@@ -32,8 +32,8 @@ Other flags:
                           moment, 4-bit 1Q second moment; tensors below 4096
                           values keep FP32 moments, as the page's thresholds)
   --turbo-bits B          with --mode turbo: 1Q index width, 2, 4 or 8
-  --count-nonfinite       with --mode turbo: count non-finite values, as the
-                          optimizers do by default (the counting kernel)
+  --count-nonfinite       count non-finite values, as the optimizers do by
+                          default (the counting kernel variant)
   --mode gradstats        instead of the step: time the gradient pre-pass
                           (pa_grad_stats_list: sum of squares, non-finite
                           count and clip coefficient) over the workload's
@@ -558,7 +558,7 @@ def main():
     ap.add_argument("--turbo-bits", type=int, default=4, choices=[2, 4, 8],
                     help="1Q index width of the TurboAdam mode (the page's default is 4)")
     ap.add_argument("--count-nonfinite", action="store_true",
-                    help="TurboAdam mode: count non-finite values, as the optimizers do by default")
+                    help="count non-finite values, as the optimizers do by default (the counting kernel)")
     ap.add_argument("--layout", default="regions", choices=["regions", "plain"],
                     help="HBM placement of the state streams (see build_workload)")
     args = ap.parse_args()
@@ -611,6 +611,8 @@ def main():
     sizes, ps, gs, states = build_workload(cfg, mode, args.param_dtype, args.layout)
     n_params = sum(sizes)
     h = dict(workloads.HYPER)
+    if args.count_nonfinite:   # the optimizers' default: the kernel variant that counts
+        h["nonfinite"] = torch.zeros(1, dtype=torch.int64, device="cuda:0")
     t = 0
     prepared = None if mode == "blockwise8" else pa.StepList(mode, ps, gs, states)
 
@@ -648,7 +650,8 @@ def main():
     if mode == "blockwise8":
         algo_bytes += 16 * (n_params // 2048)     # absmax read and write, both moments
     achieved = algo_bytes / (mean_launch_ms / 1e3) / 1e9
-    traffic = load_traffic(args.workload, mode)
+    # The stored counters are those of the plain kernel (FP32 parameters, no count).
+    traffic = None if (args.count_nonfinite or args.param_dtype != "fp32") else load_traffic(args.workload, mode)
     out = {
         "metric": METRIC,
         "value": round(n_params * args.steps / elapsed, 1),
@@ -667,6 +670,7 @@ def main():
                             "blockwise8": "blockwise-8bit-2048"}[mode],
                    "state_bytes_per_param": pa.pa_state_bytes(mode, 1),
                    "param_dtype": args.param_dtype,
+                   "count_nonfinite": bool(args.count_nonfinite),
                    "layout": ("state one HBM region (a third of device memory) below the parameters "
                               "in allocation order" if args.layout == "regions" else "back to back"),
                    "grads": "drawn once on the device, reused every step"},
