@@ -86,7 +86,7 @@ class Format(ctypes.Structure):
 
 EXPORTS = ("pa_step", "pa_step_list", "pa_step_typed", "pa_step_list_typed", "pa_state_bytes",
            "pa_format_info", "pa_status_string", "pa_last_hip_error", "pa_release_plans", "pa_debug_codec",
-           "pa_debug_sqrt", "pa_debug_q1_ends", "pa_debug_q1_levels", "pa_debug_pow2_rn32", "pa_grad_stats_list", "pa_turbo_state_bytes", "pa_turbo_workspace_bytes",
+           "pa_debug_sqrt", "pa_debug_scalars", "pa_debug_q1_ends", "pa_debug_q1_levels", "pa_debug_pow2_rn32", "pa_grad_stats_list", "pa_turbo_state_bytes", "pa_turbo_workspace_bytes",
            "pa_turbo_step_list")
 
 PA_DT_F32, PA_DT_BF16, PA_DT_F16 = 0, 1, 2
@@ -127,6 +127,8 @@ def lib():
     L.pa_release_plans.restype = None
     L.pa_debug_codec.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, sz, vp]
     L.pa_debug_codec.restype = ctypes.c_int
+    L.pa_debug_scalars.argtypes = [ctypes.POINTER(Hyper), ctypes.c_longlong, vp, vp]
+    L.pa_debug_scalars.restype = ctypes.c_int
     L.pa_debug_sqrt.argtypes = [vp, vp, sz, vp]
     L.pa_debug_sqrt.restype = ctypes.c_int
     L.pa_debug_q1_ends.argtypes = [vp, vp, sz, vp]
@@ -405,6 +407,19 @@ def pa_debug_codec(lane, direction, inp, out, stream=None):
         raise ValueError("input and output sizes differ")
     _check(lib().pa_debug_codec(int(lane), int(direction), _ptr(inp), _ptr(out), inp.numel(),
                                 _stream(stream)))
+
+
+def pa_debug_scalars(hyper, step):
+    """The per-call binary32 scalars the kernels receive (host only): a
+    float32 array [beta1, 1-beta1, beta2, 1-beta2, bc2, lr/bc1, 1-lr*wd, eps,
+    beta1*2^112] and the double 1/bc2 (see include/pa.h)."""
+    import numpy as np
+    out = np.zeros(9, np.float32)
+    inv = ctypes.c_double(0.0)
+    h = Hyper(float(hyper["lr"]), float(hyper["beta1"]), float(hyper["beta2"]), float(hyper["eps"]),
+              float(hyper["weight_decay"]), None, None, None)
+    _check(lib().pa_debug_scalars(ctypes.byref(h), int(step), out.ctypes.data, ctypes.byref(inv)))
+    return out, inv.value
 
 
 def pa_debug_sqrt(inp, out, stream=None):

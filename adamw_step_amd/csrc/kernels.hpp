@@ -1,11 +1,11 @@
 // kernels.hpp -- gfx950 kernels of the packed-AdamW step.
 //
-// Elementwise modes (packed E4, packed FP16, FP32): one persistent launch
-// walks a table of tensors cut into 4096-element tiles.  Each thread moves
-// 16-byte vectors of parameter, gradient and state (one read and one write
-// per word), keeps the whole update in registers, and never touches LDS.
-// The table is read with scalar loads; a workgroup's tensor cursor only moves
-// forward, so finding the tensor of a tile costs nothing per element.
+// Elementwise modes (packed E4, packed FP16, FP32): one launch covers a
+// table of tensors cut into 4096-element tiles, one tile per workgroup, in
+// tile order.  Each thread moves 16-byte vectors of parameter, gradient and
+// state (one read and one write per word), keeps the whole update in
+// registers, and never touches LDS.  A workgroup finds its tensor by a
+// bisection over the table on scalar loads.
 //
 // Blockwise 8-bit mode: a persistent grid over 2048-element blocks, one
 // 256-thread workgroup per block at a time; the code maps and their
@@ -348,31 +348,45 @@ __device__ __forceinline__ void flush_count(uint32_t bad, unsigned long long* co
   if ((threadIdx.x & 63) == 0 && bad != 0u) atomicAdd(counter, (unsigned long long)bad);
 }
 
-// Persistent multi-tensor launch.  table[count].tile0 holds the total tile
-// count (a sentinel), so the cursor never runs past the table.
+// The tensor of a tile: table[0..count) holds the tensors' first tiles in
+// increasing order and table[count].tile0 the total, so a bisection over
+// the first tiles finds the entry.  `tile` is uniform across the workgroup,
+// so the search runs on scalar loads and registers.
+__device__ __forceinline__ int tensor_of_tile(const Entry* table, int count, long long tile) {
+  int lo = 0, hi = count;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (table[mid].tile0 <= tile) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// Multi-tensor launch, one tile per workgroup: the workgroups of one launch
+// cover tiles tile_base .. tile_base + gridDim.x - 1 of the list.  The
+// hardware hands out workgroups in index order, so the tiles in flight at
+// any moment form one compact, advancing window of every stream (measured
+// on MI355X: a write stream runs at about 6.8 TB/s in this order against
+// about 5.5 TB/s for a persistent grid striding over the same tiles).
 template <int MODE, int PT, int GT, bool COUNT, bool SCALE>
 __global__ void __launch_bounds__(kThreads)
-elementwise_list(const Entry* __restrict__ table, long long total_tiles, Scalars s,
+elementwise_list(const Entry* __restrict__ table, int count, long long tile_base, Scalars s,
                  unsigned long long* nonfinite) {
   if (!resolve_inputs(s)) return;
+  const long long tile = tile_base + blockIdx.x;
+  const Entry e = table[tensor_of_tile(table, count, tile)];
   uint32_t bad = 0;
-  int t = 0;
-  for (long long tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
-    while (tile >= table[t + 1].tile0) ++t;
-    const Entry e = table[t];
-    run_tile<MODE, PT, GT, SCALE, (COUNT || SCALE) ? 2 : 1>(e, tile - e.tile0, s, bad);
-  }
+  run_tile<MODE, PT, GT, SCALE, (COUNT || SCALE) ? 2 : 1>(e, tile - e.tile0, s, bad);
   if constexpr (COUNT) flush_count(bad, nonfinite);
 }
 
 // Single tensor, its entry passed by value (no table in device memory).
 template <int MODE, int PT, int GT, bool COUNT, bool SCALE>
 __global__ void __launch_bounds__(kThreads)
-elementwise_one(Entry e, long long total_tiles, Scalars s, unsigned long long* nonfinite) {
+elementwise_one(Entry e, long long tile_base, Scalars s, unsigned long long* nonfinite) {
   if (!resolve_inputs(s)) return;
   uint32_t bad = 0;
-  for (long long tile = blockIdx.x; tile < total_tiles; tile += gridDim.x)
-    run_tile<MODE, PT, GT, SCALE, (COUNT || SCALE) ? 2 : 1>(e, tile, s, bad);
+  run_tile<MODE, PT, GT, SCALE, (COUNT || SCALE) ? 2 : 1>(e, tile_base + blockIdx.x, s, bad);
   if constexpr (COUNT) flush_count(bad, nonfinite);
 }
 

@@ -244,39 +244,63 @@ long long tiles_of(const pa::Entry& e) { return (e.n + e.phase + pa::kTile - 1) 
 
 // ---------------------------------------------------------------- launches
 
+// Workgroups of one launch of the one-tile-per-workgroup kernels: a launch
+// of more tiles is split into several (the dispatch packet counts work
+// items in 32 bits).
+constexpr long long kMaxLaunchTiles = 1LL << 22;
+
+// One elementwise kernel over `tiles` tiles, one workgroup per tile, in
+// launches of at most kMaxLaunchTiles workgroups; `launch(kernel, grid,
+// tile_base)` issues one launch.
+template <typename K, typename F>
+hipError_t launch_tiles(long long tiles, K kernel, F&& launch) {
+  for (long long base = 0; base < tiles; base += kMaxLaunchTiles) {
+    launch(kernel, dim3((unsigned)std::min(kMaxLaunchTiles, tiles - base)), base);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int MODE, int PT, int GT, bool COUNT, bool SCALE>
+hipError_t launch_one_v(const pa::Entry& e, long long tiles, const pa::Scalars& s, unsigned long long* nf,
+                        hipStream_t st, const DeviceInfo& d) {
+  (void)d;
+  return launch_tiles(tiles, pa::elementwise_one<MODE, PT, GT, COUNT, SCALE>, [&](auto k, dim3 grid, long long base) {
+    hipLaunchKernelGGL(k, grid, dim3(pa::kThreads), 0, st, e, base, s, nf);
+  });
+}
+
 // Kernel variant: with or without the non-finite counter, and with or
 // without a device gradient scale.
 template <int MODE, int PT, int GT>
 hipError_t launch_one(const pa::Entry& e, long long tiles, const pa::Scalars& s, unsigned long long* nf,
                       hipStream_t st, const DeviceInfo& d) {
-  const dim3 grid((unsigned)grid_for(tiles, d, d.blocks_per_cu)), block(pa::kThreads);
   const bool sc = s.gscale != nullptr;
-  if (nf && sc)
-    hipLaunchKernelGGL((pa::elementwise_one<MODE, PT, GT, true, true>), grid, block, 0, st, e, tiles, s, nf);
-  else if (nf)
-    hipLaunchKernelGGL((pa::elementwise_one<MODE, PT, GT, true, false>), grid, block, 0, st, e, tiles, s, nf);
-  else if (sc)
-    hipLaunchKernelGGL((pa::elementwise_one<MODE, PT, GT, false, true>), grid, block, 0, st, e, tiles, s, nf);
-  else
-    hipLaunchKernelGGL((pa::elementwise_one<MODE, PT, GT, false, false>), grid, block, 0, st, e, tiles, s, nf);
-  return hipGetLastError();
+  if (nf && sc) return launch_one_v<MODE, PT, GT, true, true>(e, tiles, s, nf, st, d);
+  if (nf) return launch_one_v<MODE, PT, GT, true, false>(e, tiles, s, nf, st, d);
+  if (sc) return launch_one_v<MODE, PT, GT, false, true>(e, tiles, s, nf, st, d);
+  return launch_one_v<MODE, PT, GT, false, false>(e, tiles, s, nf, st, d);
+}
+
+template <int MODE, int PT, int GT, bool COUNT, bool SCALE>
+hipError_t launch_list_v(const pa::Entry* table, int count, long long tiles, const pa::Scalars& s,
+                         unsigned long long* nf, hipStream_t st, const DeviceInfo& d) {
+  (void)d;
+  return launch_tiles(tiles, pa::elementwise_list<MODE, PT, GT, COUNT, SCALE>,
+                      [&](auto k, dim3 grid, long long base) {
+                        hipLaunchKernelGGL(k, grid, dim3(pa::kThreads), 0, st, table, count, base, s, nf);
+                      });
 }
 
 template <int MODE, int PT, int GT>
-hipError_t launch_list(const pa::Entry* table, long long tiles, const pa::Scalars& s, unsigned long long* nf,
-                       hipStream_t st, const DeviceInfo& d) {
-  const dim3 grid((unsigned)grid_for(tiles, d, d.blocks_per_cu)), block(pa::kThreads);
+hipError_t launch_list(const pa::Entry* table, int count, long long tiles, const pa::Scalars& s,
+                       unsigned long long* nf, hipStream_t st, const DeviceInfo& d) {
   const bool sc = s.gscale != nullptr;
-  if (nf && sc)
-    hipLaunchKernelGGL((pa::elementwise_list<MODE, PT, GT, true, true>), grid, block, 0, st, table, tiles, s, nf);
-  else if (nf)
-    hipLaunchKernelGGL((pa::elementwise_list<MODE, PT, GT, true, false>), grid, block, 0, st, table, tiles, s, nf);
-  else if (sc)
-    hipLaunchKernelGGL((pa::elementwise_list<MODE, PT, GT, false, true>), grid, block, 0, st, table, tiles, s, nf);
-  else
-    hipLaunchKernelGGL((pa::elementwise_list<MODE, PT, GT, false, false>), grid, block, 0, st, table, tiles, s,
-                       nf);
-  return hipGetLastError();
+  if (nf && sc) return launch_list_v<MODE, PT, GT, true, true>(table, count, tiles, s, nf, st, d);
+  if (nf) return launch_list_v<MODE, PT, GT, true, false>(table, count, tiles, s, nf, st, d);
+  if (sc) return launch_list_v<MODE, PT, GT, false, true>(table, count, tiles, s, nf, st, d);
+  return launch_list_v<MODE, PT, GT, false, false>(table, count, tiles, s, nf, st, d);
 }
 
 // One launch for a (mode, parameter type, gradient type) triple; `L` is
@@ -314,10 +338,11 @@ hipError_t dispatch_one(int mode, int pdt, int gdt, const pa::Entry& e, long lon
   });
 }
 
-hipError_t dispatch_list(int mode, int pdt, int gdt, const pa::Entry* table, long long tiles, const pa::Scalars& s,
-                         unsigned long long* nf, hipStream_t st, const DeviceInfo& d) {
+hipError_t dispatch_list(int mode, int pdt, int gdt, const pa::Entry* table, int count, long long tiles,
+                         const pa::Scalars& s, unsigned long long* nf, hipStream_t st, const DeviceInfo& d) {
   return by_mode(mode, pdt, gdt, [&](auto m, auto pt, auto gt) {
-    return launch_list<decltype(m)::value, decltype(pt)::value, decltype(gt)::value>(table, tiles, s, nf, st, d);
+    return launch_list<decltype(m)::value, decltype(pt)::value, decltype(gt)::value>(table, count, tiles, s, nf, st,
+                                                                                     d);
   });
 }
 
@@ -383,6 +408,7 @@ struct Plan {
   int pdt = 0, gdt = 0;
   std::vector<uintptr_t> key;   // per tensor: p, g, s0, s1, n
   pa::Entry* table = nullptr;   // device memory, count+1 entries (+ partials of a pre-pass plan)
+  int count = 0;                // tensors in the table (the sentinel not counted)
   long long tiles = 0;
   std::vector<Range> ranges;    // the tensors' buffers, sorted and disjoint
   double* part_sum = nullptr;   // pre-pass plans: per-workgroup partials, inside `table`'s block
@@ -670,6 +696,7 @@ int pa_step_list_typed(int mode, int param_dtype, int grad_dtype, size_t count, 
     }
     if (any_overlap(ranges)) return PA_ERR_ALIAS;
     if (host.empty()) return PA_OK;
+    if (host.size() > (size_t)INT32_MAX) return PA_ERR_ARG;
     pa::Entry sentinel;
     std::memset(&sentinel, 0, sizeof(sentinel));
     sentinel.tile0 = tiles;
@@ -680,6 +707,7 @@ int pa_step_list_typed(int mode, int param_dtype, int grad_dtype, size_t count, 
     pl.pdt = param_dtype;
     pl.gdt = grad_dtype;
     pl.key = key;
+    pl.count = (int)(host.size() - 1);
     pl.tiles = tiles;
     pl.ranges = ranges;
     hipError_t e = hipMalloc(reinterpret_cast<void**>(&pl.table), host.size() * sizeof(pa::Entry));
@@ -710,7 +738,8 @@ int pa_step_list_typed(int mode, int param_dtype, int grad_dtype, size_t count, 
       if (hits_sorted(it->ranges, r)) return PA_ERR_ALIAS;
     if (any_overlap(hr)) return PA_ERR_ALIAS;
   }
-  hipError_t e = dispatch_list(mode, param_dtype, grad_dtype, it->table, it->tiles, s, hyper->nonfinite, st, d);
+  hipError_t e =
+      dispatch_list(mode, param_dtype, grad_dtype, it->table, it->count, it->tiles, s, hyper->nonfinite, st, d);
   return e == hipSuccess ? PA_OK : hip_failed(e);
 }
 
@@ -1074,6 +1103,18 @@ void pa_release_plans(void) {
   g_plans.clear();
   for (TurboPlan& p : g_turbo_plans) free_turbo_plan(p);
   g_turbo_plans.clear();
+}
+
+int pa_debug_scalars(const pa_hyper* hyper, long long step, float* out, double* inv_bc2) {
+  if (out == nullptr || inv_bc2 == nullptr) return PA_ERR_ARG;
+  pa::Scalars s;
+  const int rc = make_scalars(hyper, step, &s);
+  if (rc) return rc;
+  const float v[9] = {s.beta1, s.one_m_beta1, s.beta2, s.one_m_beta2, s.bc2,
+                      s.lr_over_bc1, s.decay, s.eps, s.beta1_x2p112};
+  std::memcpy(out, v, sizeof(v));
+  *inv_bc2 = s.inv_bc2;
+  return PA_OK;
 }
 
 int pa_debug_codec(int lane, int dir, const void* in, void* out, size_t n, void* stream) {

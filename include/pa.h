@@ -150,7 +150,10 @@ typedef struct {
 } pa_blockwise_state;
 
 /* One tensor of n parameters, updated in place, step t = `step` (>= 1,
- * counting this update).
+ * counting this update): the update at the top of this file (KBench
+ * quantized-optimizer-state reference, `quantized_adamw_step`: params,
+ * grads, state, step and hyperparameters in, new params and state out; the
+ * packed word of the Packed AdamW Reference README, introduction).
  *   PA_PACKED_E4 / PA_PACKED_FP16: `state` is a device uint32_t* of n words.
  *   PA_FP32:       `state` is a host pa_fp32_state*.
  *   PA_BLOCKWISE8: `state` is a host pa_blockwise_state*.
@@ -158,12 +161,15 @@ typedef struct {
 int pa_step(int mode, float* params, const float* grads, void* state, size_t n,
             const pa_hyper* hyper, long long step, void* stream);
 
-/* `count` tensors sharing one hyperparameter set and one step, updated by
- * one persistent launch (elementwise modes) that walks a table of all of
- * them.  params[i], grads[i], states[i] and n[i] describe tensor i exactly
- * as for pa_step.  The table is uploaded once per distinct pointer/size
- * list and cached (see pa_release_plans).  Tensors of length 0 are
- * skipped. */
+/* `count` tensors sharing one hyperparameter set and one step (project
+ * page, Execution contract table: one parameter group, one global step;
+ * the update of each element as for pa_step).  Elementwise modes: one
+ * launch over a table of all of them, cut into 4096-element tiles, one
+ * workgroup per tile (a list of more than 2^22 tiles takes one launch per
+ * 2^22).  Blockwise mode: one launch per tensor.  params[i], grads[i],
+ * states[i] and n[i] describe tensor i exactly as for pa_step.  The table is
+ * uploaded once per distinct pointer/size list and cached (see
+ * pa_release_plans).  Tensors of length 0 are skipped. */
 int pa_step_list(int mode, size_t count, float* const* params, const float* const* grads,
                  void* const* states, const size_t* n, const pa_hyper* hyper, long long step,
                  void* stream);
@@ -289,7 +295,13 @@ int pa_turbo_step_list(size_t count, float* const* params, const float* const* g
  * a multiple of 2048).  Returns 0 for an unknown mode. */
 size_t pa_state_bytes(int mode, size_t n);
 
-/* Description of one mode's lanes (for inspection and tests). */
+/* Description of one mode's lanes (for inspection and tests): the Packed
+ * AdamW Reference README, introduction (E4M11 signed first moment, E4M12
+ * unsigned RMS, the FP16-first/FP16-RMS comparison word) and its section
+ * "Dependency-light inspection"; the KBench reference's 2048-element blocks
+ * of 8-bit codes.  Exponent bias 15 of the E4 lanes is this library's
+ * reading (the pages do not print it).  PA_ERR_ARG for a null `out` or an
+ * unknown mode. */
 typedef struct {
   int mode;
   int lanes;              /* values per parameter in the persistent state */
@@ -312,6 +324,20 @@ int pa_last_hip_error(void);
 /* Free every cached launch-plan table (device memory).  Waits for the
  * device first.  Safe to call at any time outside a running call. */
 void pa_release_plans(void);
+
+/* Scalar self-test export (host only, no device work): the per-call
+ * binary32 scalars the kernels receive, formed from `hyper` and `step`
+ * exactly as every step entry point forms them (KBench quantized-optimizer-
+ * state reference, `quantized_adamw_step`: the bias corrections and their
+ * quotients are Python floats that meet the FP32 tensors).  out (host, 9
+ * floats): beta1, 1-beta1, beta2, 1-beta2, 1-beta2^t, lr/(1-beta1^t),
+ * 1-lr*wd and eps, each formed in double and rounded once to binary32, then
+ * beta1 * 2^112 (exact: the factor that meets the E4 first moment decoded
+ * without its 2^-112 scale); *inv_bc2 (host) = 1/(the binary32 1-beta2^t)
+ * rounded to double (the quotient v'/bc2 is taken as a product with it).
+ * Validates hyper and step as pa_step does (PA_ERR_ARG, PA_ERR_ALIGN);
+ * null out or inv_bc2 is PA_ERR_ARG. */
+int pa_debug_scalars(const pa_hyper* hyper, long long step, float* out, double* inv_bc2);
 
 /* Codec self-test export: apply one lane codec of the GPU path to n device
  * values.  lane 0 = E4M11 first moment, 1 = E4M12 RMS, 2 = binary16,

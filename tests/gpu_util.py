@@ -36,6 +36,16 @@ def to_host(t, dtype=None):
     return a
 
 
+def gather(t, idx):
+    """t[idx] on the device, for a 1-D tensor t and an index tensor idx.
+    Refuses tensors of 2^31 elements or more: torch's advanced-indexing
+    kernel has faulted the GPU on such a gather, so large tensors are read
+    through contiguous slices instead."""
+    assert t.dim() == 1 and t.numel() < (1 << 31), (
+        f"advanced indexing on a tensor of {t.numel()} elements (2^31 or more): use contiguous slices")
+    return t[idx]
+
+
 def hyper(step_unused=None, nonfinite=None, **kw):
     h = dict(H)
     h.update(kw)

@@ -17,7 +17,7 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import assert_params, assert_words, banner, hyper, scalars, to_host
+from gpu_util import assert_params, assert_words, banner, gather, hyper, scalars, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -66,8 +66,8 @@ def test_llama_7b_sampled(pa, mode):
 
     def gather_state(k):
         if mode == "fp32":
-            return tuple(to_host(x[didx[k]]) for x in ss[k])
-        return to_host(ss[k][didx[k]], np.uint32)
+            return tuple(to_host(gather(x, didx[k])) for x in ss[k])
+        return to_host(gather(ss[k], didx[k]), np.uint32)
 
     try:
         for t in (1, 2):
@@ -91,7 +91,7 @@ def test_llama_7b_sampled(pa, mode):
                 else:
                     oracle.step_packed(code, hp[k], hg[k], hs[k], sc)
                     assert_words(gather_state(k), hs[k], fp16=mode == "fp16", what=f"tensor {k} words")
-                same += assert_params(to_host(ps[k][didx[k]]), hp[k], what=f"tensor {k} params")[0]
+                same += assert_params(to_host(gather(ps[k], didx[k])), hp[k], what=f"tensor {k} params")[0]
             banner(f"llama-7b {mode} step {t}: {total} sampled elements, bit-identical params {same}")
     finally:
         del ps, gs, ss
@@ -125,20 +125,20 @@ def test_blockwise_268m_sampled(pa):
         for t in (1, 2, 3):
             workloads.device_fill_grads(cfg, t, [g])
             torch.cuda.synchronize()
-            hp, hg = to_host(p[eidx]), to_host(g[eidx])
-            hmc, hvc = to_host(mc[eidx]).copy(), to_host(vc[eidx]).copy()
-            hma, hva = to_host(ma[bidx]).copy(), to_host(va[bidx]).copy()
+            hp, hg = to_host(gather(p, eidx)), to_host(gather(g, eidx))
+            hmc, hvc = to_host(gather(mc, eidx)).copy(), to_host(gather(vc, eidx)).copy()
+            hma, hva = to_host(gather(ma, bidx)).copy(), to_host(gather(va, bidx)).copy()
             banner(f"blockwise-268m step {t}")
             pa.pa_step(3, p, g, (mc, ma, vc, va, dqm, dqv, pout), hyper(), t)
             torch.cuda.synchronize()
             hout = np.zeros(hp.size, np.uint16)
             oracle.step_blockwise(hp, hg, hmc, hma, hvc, hva, qm, qv, hout, scalars(t))
-            np.testing.assert_array_equal(to_host(pout[eidx], np.uint16), hout)
-            np.testing.assert_array_equal(to_host(mc[eidx]), hmc)
-            np.testing.assert_array_equal(to_host(vc[eidx]), hvc)
-            assert_words(to_host(ma[bidx]).view(np.uint32), hma.view(np.uint32), what="m absmax")
-            assert_words(to_host(va[bidx]).view(np.uint32), hva.view(np.uint32), what="v absmax")
-            assert_params(to_host(pout[eidx].view(torch.bfloat16).float()),
+            np.testing.assert_array_equal(to_host(gather(pout, eidx), np.uint16), hout)
+            np.testing.assert_array_equal(to_host(gather(mc, eidx)), hmc)
+            np.testing.assert_array_equal(to_host(gather(vc, eidx)), hvc)
+            assert_words(to_host(gather(ma, bidx)).view(np.uint32), hma.view(np.uint32), what="m absmax")
+            assert_words(to_host(gather(va, bidx)).view(np.uint32), hva.view(np.uint32), what="v absmax")
+            assert_params(to_host(gather(pout, eidx).view(torch.bfloat16).float()),
                           (hout.astype(np.uint32) << 16).view(np.float32))
             p = pout.view(torch.bfloat16).float()
     finally:

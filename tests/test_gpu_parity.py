@@ -318,8 +318,9 @@ def test_blockwise_counting_many_blocks_per_workgroup(pa):
 
 
 def test_blockwise_small_multi_step(pa):
-    """Blockwise 8-bit mode on 64 blocks, 5 steps, full oracle; between steps
-    the BF16 output becomes the next step's FP32 parameters on both sides."""
+    """Blockwise 8-bit mode on 64 blocks for the blockwise configuration's own
+    20 steps, full oracle; between steps the BF16 output becomes the next
+    step's FP32 parameters on both sides."""
     torch = _torch()
     nb = 64
     n = nb * 2048
@@ -337,7 +338,7 @@ def test_blockwise_small_multi_step(pa):
     dp = to_dev(p)
     counter = torch.zeros(1, dtype=torch.int64, device="cuda:0")
     want_bad = 0
-    for t in range(1, 6):
+    for t in range(1, 21):
         g = (r.normal(0, 1e-3, n) * np.repeat(10.0 ** r.uniform(-2, 1, nb), 2048)).astype(np.float32)
         if t == 3:
             g[5 * 2048 + 17] = np.nan
