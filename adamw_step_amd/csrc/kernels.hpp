@@ -433,7 +433,7 @@ __device__ __forceinline__ uint32_t bucket_next(uint32_t b) {
   return b + 1 < h ? b + 1 : (b + 1 == h ? (uint32_t)kBuckets : (b == h ? 0u : b - 1));
 }
 
-template <int NCMP>
+template <int NCMP, bool SLOW>
 __device__ __forceinline__ uint32_t search_mid(const float* mid, const uint8_t* base, float c) {
   const uint32_t b = bucket_of(c);
   uint32_t lo = base[b];
@@ -453,24 +453,27 @@ __device__ __forceinline__ uint32_t search_mid(const float* mid, const uint8_t* 
       n = lt ? n - half - 1 : half;
     }
   }
-  return (c != c) ? 255u : lo;
+  if constexpr (SLOW) return (c != c) ? 255u : lo;
+  else return lo;
 }
 
-// c / d for the block normaliser d (a positive normal binary32): the double
-// product with rd = 1/d rounded to double, rounded once to binary32, is the
-// correctly rounded quotient (the quotient of two binary32 numbers is either
-// one itself or at least 2^-49 relative away from every binary32 midpoint,
-// while the product is within 2^-52).  The one case that argument leaves
-// open is a quotient exactly on a midpoint of the subnormal range.  With
-// GUARD, nonzero products below the normal range take the hardware division
-// instead; without it (used when no map midpoint lies within 2^-125 of
-// zero) every quotient in that range gets the same code anyway.
-template <bool GUARD>
+// c / d for the block normaliser d (a positive normal binary32, or +Inf or
+// NaN on the slow path): the double product with rd = 1/d rounded to
+// double, rounded once to binary32, is the correctly rounded quotient (the
+// quotient of two binary32 numbers is either one itself or at least 2^-49
+// relative away from every binary32 midpoint, while the product is within
+// 2^-52).  The one case that argument leaves open is a quotient exactly on
+// a midpoint of the subnormal range: the slow path takes the hardware
+// division for nonzero products below the normal range.  The fast path is
+// used when no map midpoint lies within 2^-125 of zero (every quotient in
+// that range then gets the same code) and d is finite.
+template <bool SLOW>
 __device__ __forceinline__ float div_block(float x, float d, double rd) {
   const double q = (double)x * rd;
   float c = (float)q;
-  if constexpr (GUARD) {
+  if constexpr (SLOW) {
     if (__builtin_expect(q != 0.0 && __builtin_fabs(q) < 0x1p-126, 0)) c = __fdiv_rn(x, d);
+    if (__builtin_expect(!(__builtin_fabsf(d) < __builtin_inff()), 0)) c = __fdiv_rn(x, d);
   }
   return c;
 }
@@ -482,24 +485,23 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
 }
 
 // Codes of four values normalised by d, packed little-endian in 32 bits.
-template <int NCMP, bool GUARD>
-__device__ __forceinline__ uint32_t codes4(const float* x, float d, double rd, const float* mid,
-                                           const uint8_t* base) {
+template <int NCMP, bool SLOW>
+__device__ __forceinline__ uint32_t codes4(const float* x, float d, double rd, const float* mid, const uint8_t* base) {
   uint32_t out = 0;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) out |= search_mid<NCMP>(mid, base, div_block<GUARD>(x[k], d, rd)) << (8 * k);
+  for (int k = 0; k < 4; ++k) out |= search_mid<NCMP, SLOW>(mid, base, div_block<SLOW>(x[k], d, rd)) << (8 * k);
   return out;
 }
 
-template <bool GUARD>
-__device__ __forceinline__ uint32_t codes4_dispatch(int ncmp, const float* x, float d, double rd,
-                                                    const float* mid, const uint8_t* base) {
+template <bool SLOW>
+__device__ __forceinline__ uint32_t codes4_dispatch(int ncmp, const float* x, float d, double rd, const float* mid,
+                                                    const uint8_t* base) {
   switch (ncmp) {   // uniform across the workgroup
-    case 1: return codes4<1, GUARD>(x, d, rd, mid, base);
-    case 2: return codes4<2, GUARD>(x, d, rd, mid, base);
-    case 3: return codes4<3, GUARD>(x, d, rd, mid, base);
-    case 4: return codes4<4, GUARD>(x, d, rd, mid, base);
-    default: return codes4<0, GUARD>(x, d, rd, mid, base);
+    case 1: return codes4<1, SLOW>(x, d, rd, mid, base);
+    case 2: return codes4<2, SLOW>(x, d, rd, mid, base);
+    case 3: return codes4<3, SLOW>(x, d, rd, mid, base);
+    case 4: return codes4<4, SLOW>(x, d, rd, mid, base);
+    default: return codes4<0, SLOW>(x, d, rd, mid, base);
   }
 }
 
@@ -590,12 +592,22 @@ __device__ __forceinline__ void build_map(const float* lut, MapTables& t, uint32
   __syncthreads();
 }
 
-template <bool COUNT>
-__global__ void __launch_bounds__(kThreads)
+// Persistent grid over the 2048-element blocks, one 256-thread workgroup per
+// block at a time (eight values per thread), the search tables built once
+// per workgroup.  The loads of a workgroup's next block are issued before
+// the current one is reduced and encoded.  The block absmax goes through
+// one of two LDS slots, the slots alternating between consecutive blocks, so
+// one barrier per block suffices: a wavefront can only rewrite a slot after
+// every wavefront has passed the barrier of the block in between, that is
+// after every read of the slot.  Four wavefronts per SIMD are asked of the
+// register allocator: with fewer the loads in flight do not cover the
+// memory latency.
+template <bool COUNT, bool SCALE>
+__global__ void __launch_bounds__(kThreads, 4)
 blockwise_kernel(BlockwiseArgs a, Scalars s, unsigned long long* nonfinite) {
   __shared__ float lut_m[256], lut_v[256];
   __shared__ MapTables tab_m, tab_v;
-  __shared__ uint32_t wave_max[2][kThreads / 64];
+  __shared__ uint32_t wave_max[2][2][kThreads / 64];   // [slot][moment][wavefront]
   if (!resolve_inputs(s)) return;   // uniform: before any barrier
   const int tid = threadIdx.x;
   lut_m[tid] = a.qmap_m[tid];
@@ -603,8 +615,8 @@ blockwise_kernel(BlockwiseArgs a, Scalars s, unsigned long long* nonfinite) {
   __syncthreads();
   int ncmp_m, ncmp_v;
   bool guard_m, guard_v;
-  build_map(lut_m, tab_m, wave_max[0], ncmp_m, guard_m);
-  build_map(lut_v, tab_v, wave_max[1], ncmp_v, guard_v);
+  build_map(lut_m, tab_m, wave_max[0][0], ncmp_m, guard_m);
+  build_map(lut_v, tab_v, wave_max[0][1], ncmp_v, guard_v);
 
   // The 1e-30 lower clamp of the normaliser, as a binary32 bit pattern.
   const uint32_t floor_bits = __float_as_uint((float)1e-30);
@@ -613,6 +625,7 @@ blockwise_kernel(BlockwiseArgs a, Scalars s, unsigned long long* nonfinite) {
   struct BlockIn {
     f32x4 p[2], g[2];
     uint32_t mc[2], vc[2];
+    float am, av;
   };
   auto load_block = [&](long long blk, BlockIn& in) {
 #pragma unroll
@@ -623,13 +636,14 @@ blockwise_kernel(BlockwiseArgs a, Scalars s, unsigned long long* nonfinite) {
       in.mc[h] = *reinterpret_cast<const uint32_t*>(a.m_code + e0);
       in.vc[h] = *reinterpret_cast<const uint32_t*>(a.v_code + e0);
     }
+    in.am = a.m_absmax[blk];
+    in.av = a.v_absmax[blk];
   };
-  BlockIn cur;
-  for (long long b = blockIdx.x; b < a.nblocks; b += gridDim.x) {
+  BlockIn cur, nxt;
+  if (blockIdx.x < a.nblocks) load_block(blockIdx.x, cur);
+  int slot = 0;
+  for (long long b = blockIdx.x; b < a.nblocks; b += gridDim.x, slot ^= 1) {
     const long long base = b * kBlock;
-    const float am = a.m_absmax[b];
-    const float av = a.v_absmax[b];
-    load_block(b, cur);
     float m1[8], v1[8];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -637,11 +651,11 @@ blockwise_kernel(BlockwiseArgs a, Scalars s, unsigned long long* nonfinite) {
       float po[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float m = lut_m[(cur.mc[h] >> (8 * k)) & 0xFFu] * am;
-        const float v = lut_v[(cur.vc[h] >> (8 * k)) & 0xFFu] * av;
+        const float m = lut_m[(cur.mc[h] >> (8 * k)) & 0xFFu] * cur.am;
+        const float v = lut_v[(cur.vc[h] >> (8 * k)) & 0xFFu] * cur.av;
         float p1;
-        adamw(cur.p[h][k], cur.g[h][k] * s.gmul, s.beta1 * m, v, s, p1, m1[h * 4 + k], v1[h * 4 + k]);
-        bad += nonfinite3(p1, m1[h * 4 + k], v1[h * 4 + k]);
+        adamw(cur.p[h][k], scaled<SCALE>(cur.g[h][k], s), s.beta1 * m, v, s, p1, m1[h * 4 + k], v1[h * 4 + k]);
+        if constexpr (COUNT) bad += nonfinite3(p1, m1[h * 4 + k], v1[h * 4 + k]);
         po[k] = p1;
       }
       uint2 out;
@@ -649,6 +663,9 @@ blockwise_kernel(BlockwiseArgs a, Scalars s, unsigned long long* nonfinite) {
       out.y = bf16_encode2(po[2], po[3]);
       *reinterpret_cast<uint2*>(a.p_out + e0) = out;
     }
+    // The next block's loads go out before this block's reduction and
+    // encoding, so their latency hides behind that work.
+    if (b + gridDim.x < a.nblocks) load_block(b + gridDim.x, nxt);
     // Block absmax: on non-negative floats (and NaN with the sign cleared)
     // the unsigned order of the bit patterns is the numeric order, with NaN
     // above everything, so an integer max propagates NaN as the reference's
@@ -662,27 +679,29 @@ blockwise_kernel(BlockwiseArgs a, Scalars s, unsigned long long* nonfinite) {
     xm = wave_max_u32(xm);
     xv = wave_max_u32(xv);
     if ((tid & 63) == 0) {
-      wave_max[0][tid >> 6] = xm;
-      wave_max[1][tid >> 6] = xv;
+      wave_max[slot][0][tid >> 6] = xm;
+      wave_max[slot][1][tid >> 6] = xv;
     }
     __syncthreads();
-    uint32_t Am = wave_max[0][0], Av = wave_max[1][0];
+    uint32_t Am = wave_max[slot][0][0], Av = wave_max[slot][1][0];
 #pragma unroll
     for (int w = 1; w < kThreads / 64; ++w) {
-      Am = max(Am, wave_max[0][w]);
-      Av = max(Av, wave_max[1][w]);
+      Am = max(Am, wave_max[slot][0][w]);
+      Av = max(Av, wave_max[slot][1][w]);
     }
-    __syncthreads();   // wave_max is rewritten by the next block
     const float dm = __uint_as_float(max(Am, floor_bits));
     const float dv = __uint_as_float(max(Av, floor_bits));
     const double rdm = 1.0 / (double)dm;   // correctly rounded double division
     const double rdv = 1.0 / (double)dv;
+    // Inf or NaN in a block (absmax at or above the Inf pattern) takes the
+    // slow path, which also orders NaN quotients above every midpoint.
+    const bool slow_m = guard_m || Am >= kInfBits, slow_v = guard_v || Av >= kInfBits;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const uint32_t cm = guard_m ? codes4_dispatch<true>(ncmp_m, m1 + 4 * h, dm, rdm, tab_m.mid, tab_m.base)
-                                  : codes4_dispatch<false>(ncmp_m, m1 + 4 * h, dm, rdm, tab_m.mid, tab_m.base);
-      const uint32_t cv = guard_v ? codes4_dispatch<true>(ncmp_v, v1 + 4 * h, dv, rdv, tab_v.mid, tab_v.base)
-                                  : codes4_dispatch<false>(ncmp_v, v1 + 4 * h, dv, rdv, tab_v.mid, tab_v.base);
+      const uint32_t cm = slow_m ? codes4_dispatch<true>(ncmp_m, m1 + 4 * h, dm, rdm, tab_m.mid, tab_m.base)
+                                 : codes4_dispatch<false>(ncmp_m, m1 + 4 * h, dm, rdm, tab_m.mid, tab_m.base);
+      const uint32_t cv = slow_v ? codes4_dispatch<true>(ncmp_v, v1 + 4 * h, dv, rdv, tab_v.mid, tab_v.base)
+                                 : codes4_dispatch<false>(ncmp_v, v1 + 4 * h, dv, rdv, tab_v.mid, tab_v.base);
       const long long e0 = base + h * 1024 + tid * 4;
       *reinterpret_cast<uint32_t*>(a.m_code + e0) = cm;
       *reinterpret_cast<uint32_t*>(a.v_code + e0) = cv;
@@ -691,6 +710,7 @@ blockwise_kernel(BlockwiseArgs a, Scalars s, unsigned long long* nonfinite) {
       a.m_absmax[b] = __uint_as_float(Am);
       a.v_absmax[b] = __uint_as_float(Av);
     }
+    cur = nxt;
   }
   if constexpr (COUNT) flush_count(bad, nonfinite);
 }

@@ -96,7 +96,7 @@ int device_info(int* dev_out, DeviceInfo* info) {
     if (e != hipSuccess || per < 1) per = 4;
     int bw = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &bw, reinterpret_cast<const void*>(pa::blockwise_kernel<false>), pa::kThreads, 0);
+        &bw, reinterpret_cast<const void*>(pa::blockwise_kernel<false, false>), pa::kThreads, 0);
     if (e != hipSuccess || bw < 1) bw = 2;
     d.cus = cus;
     d.blocks_per_cu = per;
@@ -393,10 +393,11 @@ int blockwise_inputs_clear(const pa::BlockwiseArgs& a, size_t n, std::vector<Ran
 hipError_t launch_blockwise(const pa::BlockwiseArgs& a, const pa::Scalars& s, unsigned long long* nf,
                             hipStream_t st, const DeviceInfo& d) {
   const dim3 grid((unsigned)grid_for(a.nblocks, d, d.bw_blocks_per_cu)), block(pa::kThreads);
-  if (nf)
-    hipLaunchKernelGGL((pa::blockwise_kernel<true>), grid, block, 0, st, a, s, nf);
-  else
-    hipLaunchKernelGGL((pa::blockwise_kernel<false>), grid, block, 0, st, a, s, nf);
+  const bool sc = s.gscale != nullptr;
+  if (nf && sc) hipLaunchKernelGGL((pa::blockwise_kernel<true, true>), grid, block, 0, st, a, s, nf);
+  else if (nf) hipLaunchKernelGGL((pa::blockwise_kernel<true, false>), grid, block, 0, st, a, s, nf);
+  else if (sc) hipLaunchKernelGGL((pa::blockwise_kernel<false, true>), grid, block, 0, st, a, s, nf);
+  else hipLaunchKernelGGL((pa::blockwise_kernel<false, false>), grid, block, 0, st, a, s, nf);
   return hipGetLastError();
 }
 
