@@ -16,7 +16,8 @@ CPU oracle's throughput on a bounded sample of the same workload.
 
 Other flags:
   --no-cpu-baseline       skip the oracle timing
-  --probe                 also time a plain copy and a 3-in/2-out stream probe
+  --probe                 after the step, time the step-layout probes and
+                          references (see step_layout_ceilings) in any mode
   --calibrate-copy BYTES  only run the plain copy probe (for counter calibration)
   --train-gpt             instead: time a synthetic-token training step of the
                           gpt-11m model (trainer/) with each optimizer and
@@ -24,10 +25,6 @@ Other flags:
   --layout plain          allocate parameters, gradients and state back to
                           back (default: state one HBM region below the
                           parameters, see build_workload)
-  --region-map            instead: allocate the device memory in 1 GiB
-                          chunks, in order, and time the E4 step with its
-                          parameters on one chunk and its state words on
-                          another, for a grid of chunk pairs
   --mode turbo            the TurboAdam compressed-state step (UState first
                           moment, 4-bit 1Q second moment; tensors below 4096
                           values keep FP32 moments, as the page's thresholds)
@@ -59,9 +56,10 @@ WORKLOADS = {"single-262k": 1, "gpt-11m": 2, "gpt2-small-124m": 3, "llama-7b": 4
 # Device sources each kernel family is compiled from: a stored counter
 # reading stays valid while these bytes are unchanged.
 KERNEL_SOURCES = {
-    "elementwise": ("adamw_step_amd/csrc/kernels.hpp", "adamw_step_amd/csrc/codec.hpp"),
+    "elementwise": ("adamw_step_amd/csrc/kernels.hpp", "adamw_step_amd/csrc/codec.hpp",
+                    "adamw_step_amd/csrc/pa_api.hip", "adamw_step_amd/build.py"),
     "turbo": ("adamw_step_amd/csrc/kernels.hpp", "adamw_step_amd/csrc/codec.hpp", "adamw_step_amd/csrc/turbo.hpp",
-              "adamw_step_amd/csrc/pow2.hpp"),
+              "adamw_step_amd/csrc/pow2.hpp", "adamw_step_amd/csrc/pa_api.hip", "adamw_step_amd/build.py"),
 }
 
 
@@ -83,13 +81,12 @@ def probe_lib():
     pa.lib()
     path = os.path.join(ROOT, "adamw_step_amd", "libpa_probe.so")
     L = ctypes.CDLL(path)
-    L.pa_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
-    L.pa_probe_stream5.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
-                                   ctypes.c_int, ctypes.c_void_p]
-    L.pa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
-    L.pa_probe_write.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
-    L.pa_probe_mix.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
-                               ctypes.c_int, ctypes.c_void_p]
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    L.pa_probe_copy.argtypes = [vp, vp, sz, ctypes.c_int, vp]
+    L.pa_probe_read.argtypes = [vp, sz, vp, vp]
+    L.pa_probe_write.argtypes = [vp, sz, vp]
+    L.pa_probe_mix.argtypes = [vp, vp, vp, sz, ctypes.c_int, vp]
+    L.pa_probe_runtime_copy.argtypes = [vp, vp, sz, vp]
     return L
 
 
@@ -108,38 +105,23 @@ def time_probe(fn, reps):
     return sorted(ts)[len(ts) // 2]
 
 
-def run_probes(grid, stream_bytes=0):
-    import torch
-    L = probe_lib()
-    st = torch.cuda.current_stream().cuda_stream
-    nbytes = 8 << 30
-    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0")
-    b = torch.empty_like(a)
-    a.fill_(1.0)
-    ms = time_probe(lambda: L.pa_probe_copy(a.data_ptr(), b.data_ptr(), nbytes, grid, st), 10)
-    copy_gbps = 2 * nbytes / ms / 1e6
-    c = torch.empty_like(a)
-    c.fill_(2.0)
-    n16 = nbytes // 16
-    ms5 = time_probe(lambda: L.pa_probe_stream5(a.data_ptr(), b.data_ptr(), c.data_ptr(), n16, grid, st), 10)
-    stream_gbps = 5 * nbytes / ms5 / 1e6
-    del a, b, c
-    torch.cuda.empty_cache()
-    out = {"copy_gbps": round(copy_gbps, 1), "stream_3in_2out_gbps": round(stream_gbps, 1),
-           "bytes": nbytes, "grid": grid}
-    if stream_bytes:
-        out["step_layout"] = step_layout_ceilings(L, stream_bytes, grid)
-    return out
+def step_layout_ceilings(L, stream_bytes):
+    """Ceilings of the packed step's traffic on this HBM, in the benchmark's
+    layout: three streams of `stream_bytes` (the step's p, g and w), the
+    first two at the start of device memory and the third one HBM region
+    further on in allocation order.
 
-
-def step_layout_ceilings(L, stream_bytes, grid):
-    """Ceilings of the packed step's own access forms in the benchmark's
-    layout: three streams of `stream_bytes` (the step's p, g and w), the first
-    two at the start of device memory and the third one HBM region further on
-    in allocation order.  Nontemporal read and write of one stream; the
-    step's 3-read/2-write traffic with nontemporal 16-byte accesses, with no
-    arithmetic and with 80 binary32 instructions per value (the step issues
-    about 78)."""
+    This library's probes (libpa_probe.so, one tile per workgroup in tile
+    order, as the step): a nontemporal read of one stream, a write of one
+    stream, and the step's 3-read/2-write mix in place with no arithmetic
+    and with 80 binary32 instructions per value (the step issues about
+    78).  References that are not code of this library, on the same
+    streams: torch's fill_ (one write stream), the HIP runtime's
+    device-to-device copy (one read and one write stream), torch's add of
+    two streams into a third (two reads, one write), and torch's sum (one
+    read).  `read_then_write_bound_gbps` is the rate of the step's bytes if
+    its reads ran at the best read rate measured here and its writes, one
+    after the other, at the best write rate: 5 / (3 / read + 2 / write)."""
     import torch
     st = torch.cuda.current_stream().cuda_stream
     stream_bytes -= stream_bytes % 16
@@ -158,14 +140,22 @@ def step_layout_ceilings(L, stream_bytes, grid):
     def ok(rc):
         assert rc == 0, "probe launch failed"
 
-    res = {"stream_bytes": stream_bytes,
-           "read_nt_gbps": gbps(stream_bytes, lambda: ok(L.pa_probe_read(a.data_ptr(), n16, sink.data_ptr(), grid, st))),
-           "write_nt_gbps": gbps(stream_bytes, lambda: ok(L.pa_probe_write(a.data_ptr(), n16, grid, st))),
-           "mix_3r2w_gbps": gbps(5 * stream_bytes, lambda: ok(L.pa_probe_mix(a.data_ptr(), b.data_ptr(), c.data_ptr(),
-                                                                               n16, 0, grid, st))),
-           "mix_3r2w_80valu_gbps": gbps(5 * stream_bytes,
-                                        lambda: ok(L.pa_probe_mix(a.data_ptr(), b.data_ptr(), c.data_ptr(), n16, 80,
-                                                                  grid, st)))}
+    S = stream_bytes
+    res = {"stream_bytes": S,
+           "read_nt_gbps": gbps(S, lambda: ok(L.pa_probe_read(a.data_ptr(), n16, sink.data_ptr(), st))),
+           "write_gbps": gbps(S, lambda: ok(L.pa_probe_write(c.data_ptr(), n16, st))),
+           "mix_3r2w_gbps": gbps(5 * S, lambda: ok(L.pa_probe_mix(a.data_ptr(), b.data_ptr(), c.data_ptr(), n16, 0,
+                                                                  st))),
+           "mix_3r2w_80valu_gbps": gbps(5 * S, lambda: ok(L.pa_probe_mix(a.data_ptr(), b.data_ptr(), c.data_ptr(),
+                                                                         n16, 80, st)))}
+    refs = {"torch_fill_gbps": gbps(S, lambda: c.fill_(1.0)),
+            "hip_memcpy_d2d_gbps": gbps(2 * S, lambda: ok(L.pa_probe_runtime_copy(a.data_ptr(), c.data_ptr(), S, st))),
+            "torch_add_2r1w_gbps": gbps(3 * S, lambda: torch.add(a, b, out=c)),
+            "torch_sum_gbps": gbps(S, lambda: a.sum())}
+    res["references"] = refs
+    best_read = max(res["read_nt_gbps"], refs["torch_sum_gbps"])
+    best_write = max(res["write_gbps"], refs["torch_fill_gbps"])
+    res["read_then_write_bound_gbps"] = round(5.0 / (3.0 / best_read + 2.0 / best_write), 1)
     del a, b, c, sink
     torch.cuda.empty_cache()
     return res
@@ -267,9 +257,14 @@ def build_workload(cfg, mode, param_dtype="fp32", layout="regions"):
     return sizes, ps, gs, states
 
 
-def cpu_baseline(cfg, mode, ps, gs, states, budget_params):
-    """Time the oracle (as it stands) on a bounded sample of the same workload:
-    the leading tensors of the list, up to `budget_params` parameters, one step."""
+def cpu_baseline(cfg, mode, ps, gs, states, budget_params, one_core_params=64 << 20):
+    """Time the oracle (as it stands) on the host cores: one step over the
+    workload's whole list when it holds at most `budget_params` parameters
+    (single-262k, gpt-11m, gpt2-small-124m, blockwise-268m), else over the
+    leading tensors of the list up to that many; then the same oracle on one
+    core over the first `one_core_params` values of that sample (the whole
+    sample if smaller).  Inputs are the device buffers as the benchmark left
+    them (any valid state will do for timing)."""
     import numpy as np
     import oracle
     import workloads
@@ -282,40 +277,52 @@ def cpu_baseline(cfg, mode, ps, gs, states, budget_params):
             break
         picked.append(k)
         total += n
+    whole = len(picked) == len(ps)
+    names = [workloads.shapes(cfg)[k][0] for k in picked]
     hp = [ps[k].cpu().numpy() for k in picked]
     hg = [gs[k].cpu().numpy() for k in picked]
-    if mode == "fp32":
-        hs = [(np.zeros(ps[k].numel(), np.float32), np.zeros(ps[k].numel(), np.float32)) for k in picked]
+    if mode == "blockwise8":
+        mc, ma, vc, va, qm, qv, _ = states[0]
+        hs = [(mc.cpu().numpy(), ma.cpu().numpy(), vc.cpu().numpy(), va.cpu().numpy(), qm.cpu().numpy(),
+               qv.cpu().numpy())]
+    elif mode == "fp32":
+        hs = [(states[k][0].cpu().numpy(), states[k][1].cpu().numpy()) for k in picked]
     else:
-        hs = [np.zeros(ps[k].numel(), np.uint32) for k in picked]
-    names = [workloads.shapes(cfg)[k][0] for k in picked]
+        hs = [states[k].cpu().numpy().view(np.uint32) for k in picked]
+
+    def step(p, g, st, lo, hi):
+        # contiguous views: the oracle updates the host copies in place
+        if mode == "blockwise8":
+            mc, ma, vc, va, qm, qv = st
+            nb0, nb1 = lo // 2048, hi // 2048
+            out = np.empty(hi - lo, np.uint16)
+            oracle.step_blockwise(p[lo:hi], g[lo:hi], mc[lo:hi], ma[nb0:nb1], vc[lo:hi], va[nb0:nb1], qm, qv, out, sc)
+        elif mode == "fp32":
+            oracle.step_fp32(p[lo:hi], g[lo:hi], st[0][lo:hi], st[1][lo:hi], sc)
+        else:
+            oracle.step_packed(oracle.PACKED_E4 if mode == "e4" else oracle.PACKED_F16, p[lo:hi], g[lo:hi],
+                               st[lo:hi], sc)
+
     t0 = time.perf_counter()
     for i in range(len(picked)):
-        if mode == "fp32":
-            oracle.step_fp32(hp[i], hg[i], hs[i][0], hs[i][1], sc)
-        else:
-            oracle.step_packed(oracle.PACKED_E4 if mode == "e4" else oracle.PACKED_F16, hp[i], hg[i], hs[i], sc)
+        step(hp[i], hg[i], hs[i], 0, hp[i].size)
     dt = time.perf_counter() - t0
     cores = oracle.num_threads()
-    # The same oracle on one core, over the first 32 Mi values of the first
-    # tensor (inputs as left by the step above: any valid state will do).
-    k = min(hp[0].size, 32 << 20)
-    p1, g1 = hp[0][:k].copy(), hg[0][:k].copy()
-    s1 = (hs[0][0][:k].copy(), hs[0][1][:k].copy()) if mode == "fp32" else hs[0][:k].copy()
+    k = min(hp[0].size, one_core_params)
+    if mode == "blockwise8":
+        k -= k % 2048
     oracle.set_num_threads(1)
     try:
         t1 = time.perf_counter()
-        if mode == "fp32":
-            oracle.step_fp32(p1, g1, s1[0], s1[1], sc)
-        else:
-            oracle.step_packed(oracle.PACKED_E4 if mode == "e4" else oracle.PACKED_F16, p1, g1, s1, sc)
+        step(hp[0], hg[0], hs[0], 0, k)
         dt1 = time.perf_counter() - t1
     finally:
         oracle.set_num_threads(cores)
+    what = (f"one step over the whole list ({len(picked)} tensors, {total} params)" if whole else
+            f"one step over the first {len(picked)} tensors of the list ({names[0]}..{names[-1]}, {total} params)")
     return {"value": round(total / dt, 1), "unit": "params/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"one step over the first {len(picked)} tensors of the list "
-                      f"({names[0]}..{names[-1]}, {total} params), {dt:.1f} s wall",
+            "sample": f"{what}, {dt:.1f} s wall",
             "one_core": {"value": round(k / dt1, 1), "unit": "params/s",
                          "sample": f"one step over the first {k} values of {names[0]}, {dt1:.1f} s wall"}}
 
@@ -380,51 +387,6 @@ def run_gradstats(args, cfg):
                                "kind": "oracle", "sample": f"the first {len(picked)} gradient tensors "
                                f"({total} values), exact accumulation, {dt_cpu:.1f} s wall"}
     print(json.dumps(out), flush=True)
-
-
-def region_map(stride=12, max_chunks=276):
-    """GB/s of the E4 step (one 2^28-element tensor) with the parameters on
-    chunk i and the state words on chunk k of 1 GiB chunks allocated in order,
-    gradients on a fixed middle chunk."""
-    import torch
-    import adamw_step_amd as pa
-    import workloads
-    n = 1 << 28
-    chunks = []
-    for _ in range(max_chunks):
-        try:
-            chunks.append(torch.empty(n, dtype=torch.float32, device="cuda:0"))
-        except torch.OutOfMemoryError:
-            break
-    nc = len(chunks)
-    gi = nc // 2
-    chunks[gi].fill_(1e-3)
-    h = dict(workloads.HYPER)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    idx = [i for i in range(0, nc, stride) if i != gi]
-    rows = []
-    for i in idx:
-        row = []
-        for k in idx:
-            if k == i:
-                row.append(None)
-                continue
-            chunks[i].fill_(0.01)
-            w = chunks[k].view(torch.int32)
-            w.zero_()
-            best = 1e9
-            for t in (1, 2, 3):
-                a.record()
-                pa.pa_step("e4", chunks[i], chunks[gi], w, h, t)
-                b.record()
-                b.synchronize()
-                if t > 1:
-                    best = min(best, a.elapsed_time(b))
-            row.append(round(20 * n / (best * 1e6)))
-        rows.append(row)
-        log(f"params on chunk {i}: {row}")
-    print(json.dumps({"region_map": {"chunk_bytes": 4 * n, "chunks": nc, "grad_chunk": gi, "index": idx,
-                                     "gbps_rows_params_cols_state": rows}}), flush=True)
 
 
 def run_turbo(args, cfg):
@@ -554,7 +516,6 @@ def main():
     ap.add_argument("--train-gpt", action="store_true")
     ap.add_argument("--param-dtype", default="fp32", choices=["fp32", "bf16", "fp16"],
                     help="element type of parameters and gradients (state unchanged)")
-    ap.add_argument("--region-map", action="store_true")
     ap.add_argument("--turbo-bits", type=int, default=4, choices=[2, 4, 8],
                     help="1Q index width of the TurboAdam mode (the page's default is 4)")
     ap.add_argument("--count-nonfinite", action="store_true",
@@ -574,9 +535,6 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
-        return
-    if args.region_map:
-        region_map()
         return
     if args.train_gpt:
         from trainer.loop import measure
@@ -683,13 +641,12 @@ def main():
                      "kernel_sha": kernel_sha()},
     }
     if args.probe:
-        import adamw_step_amd as _p  # noqa: F401
         del ps, gs, states
         prepared = None              # it holds the tensors too
         torch.cuda.empty_cache()
-        out["probes"] = run_probes(grid=2048, stream_bytes=4 * n_params if mode == "e4" else 0)
+        out["probes"] = step_layout_ceilings(probe_lib(), 4 * n_params)
         log(f"probes: {out['probes']}")
-    if not args.no_cpu_baseline and not args.probe and mode != "blockwise8" and args.param_dtype == "fp32":
+    if not args.no_cpu_baseline and not args.probe and args.param_dtype == "fp32":
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(cfg, mode, ps, gs, states, args.cpu_sample_params)
     if mode == "e4" and args.param_dtype == "fp32" and not args.probe and not args.no_ceiling:
@@ -700,9 +657,10 @@ def main():
         torch.cuda.empty_cache()
         try:
             import adamw_step_amd as _p  # noqa: F401
-            ceil = step_layout_ceilings(probe_lib(), 4 * n_params, 2048)
+            ceil = step_layout_ceilings(probe_lib(), 4 * n_params)
             ceil["frac_of_traffic_probe"] = round(achieved / ceil["mix_3r2w_gbps"], 4)
             ceil["frac_of_traffic_and_valu_probe"] = round(achieved / ceil["mix_3r2w_80valu_gbps"], 4)
+            ceil["frac_of_read_then_write_bound"] = round(achieved / ceil["read_then_write_bound_gbps"], 4)
             out["roofline"]["measured_ceilings"] = ceil
             log(f"measured ceilings: {ceil}")
         except Exception as ex:      # a probe problem must not cost the result line
