@@ -169,28 +169,31 @@ class PackedAdamW(torch.optim.Optimizer):
         sd["packed"] = {"mode": self.mode, "step": self.step_count}
         return sd
 
+    _RAW_STATE = {"words": torch.int32, "exp_avg": torch.float32, "exp_avg_sq": torch.float32}
+
     def load_state_dict(self, state_dict):
-        """Restore a checkpoint.  The packed words are put back bit for bit:
-        torch's loader would convert non-float state to the parameters'
-        dtype, which would turn the words into float values."""
+        """Restore a checkpoint.  The state tensors are put back bit for bit
+        in their own dtypes: torch's loader would convert floating-point
+        state to the parameters' dtype (bfloat16 moments for bfloat16
+        parameters) and non-float state to float values."""
         meta = state_dict.get("packed", {})
         if meta.get("mode", self.mode) != self.mode:
             raise ValueError(f"checkpoint holds mode {meta.get('mode')}, optimizer uses {self.mode}")
-        words, rest = {}, {}
+        raw, rest = {}, {}
         for idx, st in state_dict["state"].items():
             st = dict(st)
-            if "words" in st:
-                words[idx] = st.pop("words")
+            raw[idx] = {k: st.pop(k) for k in self._RAW_STATE if k in st}
             rest[idx] = st
         base = {k: v for k, v in state_dict.items() if k not in ("packed", "state")}
         base["state"] = rest
         super().load_state_dict(base)
         params = self.param_groups[0]["params"]
-        for idx, w in words.items():
+        for idx, tensors in raw.items():
             p = params[idx]
-            if w.numel() != p.numel():
-                raise ValueError("checkpoint words do not match the parameter sizes")
-            self.state[p]["words"] = w.to(device=p.device, dtype=torch.int32).contiguous().clone()
+            for k, t in tensors.items():
+                if t.numel() != p.numel() or t.dtype != self._RAW_STATE[k]:
+                    raise ValueError(f"checkpoint {k} does not match the parameter size or its dtype")
+                self.state[p][k] = t.to(device=p.device).contiguous().clone()
         for p in params:
             st = self.state[p]
             for k, v in st.items():

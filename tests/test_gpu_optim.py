@@ -47,14 +47,19 @@ def test_optimizer_matches_oracle(mode):
     assert opt.state_bytes() == (8 if mode == "fp32" else 4) * sum(sizes)
 
 
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16", "float16"])
 @pytest.mark.parametrize("mode", ["e4", "fp32"])
-def test_checkpoint_resume_is_bit_exact(mode):
-    """6 steps straight == 3 steps, save to bytes, load into fresh objects, 3 steps."""
+def test_checkpoint_resume_is_bit_exact(mode, dtype):
+    """6 steps straight == 3 steps, save to bytes, load into fresh objects, 3
+    steps; with FP32, BF16 and FP16 parameters (the FP32 moments and the
+    packed words must come back in their own dtypes)."""
     import torch
     from adamw_step_amd.optim import PackedAdamW
+    dt = getattr(torch, dtype)
     sizes = [40000, 4096, 77]
     r = np.random.Generator(np.random.PCG64(8))
-    grads = [[torch.from_numpy(r.normal(0, 1e-3, n).astype(np.float32)).cuda() for n in sizes] for _ in range(6)]
+    grads = [[torch.from_numpy(r.normal(0, 1e-3, n).astype(np.float32)).to(dt).cuda() for n in sizes]
+             for _ in range(6)]
 
     def run(ps, opt, steps):
         for gs in steps:
@@ -62,11 +67,14 @@ def test_checkpoint_resume_is_bit_exact(mode):
                 p.grad = g.clone()
             opt.step()
 
-    a = _params(torch, sizes, 5)
+    def params():
+        return [torch.nn.Parameter(p.detach().to(dt)) for p in _params(torch, sizes, 5)]
+
+    a = params()
     oa = PackedAdamW(a, weight_decay=0.01, mode=mode)
     run(a, oa, grads)
 
-    b = _params(torch, sizes, 5)
+    b = params()
     ob = PackedAdamW(b, weight_decay=0.01, mode=mode)
     run(b, ob, grads[:3])
     buf = io.BytesIO()
@@ -77,13 +85,17 @@ def test_checkpoint_resume_is_bit_exact(mode):
     oc = PackedAdamW(c, weight_decay=0.01, mode=mode)
     oc.load_state_dict(ck["opt"])
     assert oc.step_count == 3
-    banner(f"resume {mode}: 3 more steps after the round trip")
+    for pc in c:
+        for k, t in oc.state[pc].items():
+            assert t.dtype == (torch.int32 if k == "words" else torch.float32), (k, t.dtype)
+    banner(f"resume {mode} {dtype}: 3 more steps after the round trip")
     run(c, oc, grads[3:])
     torch.cuda.synchronize()
-    key = "words" if mode == "e4" else "exp_avg"
+    keys = ["words"] if mode == "e4" else ["exp_avg", "exp_avg_sq"]
     for pa_, pc in zip(a, c):
         assert torch.equal(pa_.detach(), pc.detach())
-        assert torch.equal(oa.state[pa_][key], oc.state[pc][key])
+        for key in keys:
+            assert torch.equal(oa.state[pa_][key], oc.state[pc][key])
 
 
 def test_smoke_gates():
