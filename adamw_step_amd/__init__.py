@@ -35,6 +35,8 @@ MODES = {"fp32": PA_FP32, "e4": PA_PACKED_E4, "fp16": PA_PACKED_FP16, "blockwise
 BLOCK = 2048
 
 PA_OK, PA_ERR_ARG, PA_ERR_ALIGN, PA_ERR_SHAPE, PA_ERR_ALIAS, PA_ERR_DEVICE, PA_ERR_NOMEM = 0, -1, -2, -3, -4, -5, -6
+PA_ERR_CAPACITY = -7
+PA_NOALLOC_MAX_TENSORS = 4095   # include/pa.h
 
 
 class PAError(RuntimeError):
@@ -87,7 +89,7 @@ class Format(ctypes.Structure):
 EXPORTS = ("pa_step", "pa_step_list", "pa_step_typed", "pa_step_list_typed", "pa_state_bytes",
            "pa_format_info", "pa_status_string", "pa_last_hip_error", "pa_release_plans", "pa_debug_codec",
            "pa_debug_sqrt", "pa_debug_scalars", "pa_debug_q1_ends", "pa_debug_q1_levels", "pa_debug_pow2_rn32", "pa_grad_stats_list", "pa_turbo_state_bytes", "pa_turbo_workspace_bytes",
-           "pa_turbo_step_list")
+           "pa_turbo_step_list", "pa_step_list_noalloc")
 
 PA_DT_F32, PA_DT_BF16, PA_DT_F16 = 0, 1, 2
 
@@ -117,6 +119,8 @@ def lib():
                                      ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(sz),
                                      ctypes.POINTER(Hyper), ctypes.c_longlong, vp]
     L.pa_step_list_typed.restype = ctypes.c_int
+    L.pa_step_list_noalloc.argtypes = L.pa_step_list_typed.argtypes
+    L.pa_step_list_noalloc.restype = ctypes.c_int
     L.pa_state_bytes.argtypes = [ctypes.c_int, sz]
     L.pa_state_bytes.restype = sz
     L.pa_format_info.argtypes = [ctypes.c_int, ctypes.POINTER(Format)]
@@ -265,8 +269,10 @@ def pa_step(mode, params, grads, state, hyper, step, stream=None):
                                int(step), _stream(stream)))
 
 
-def pa_step_list(mode, params, grads, states, hyper, step, stream=None):
-    """A list of tensors sharing one hyperparameter set and step, one launch."""
+def pa_step_list(mode, params, grads, states, hyper, step, stream=None, noalloc=False):
+    """A list of tensors sharing one hyperparameter set and step, one launch.
+    noalloc=True calls pa_step_list_noalloc (no device allocation; the table
+    in the library's static device array, see include/pa.h)."""
     mode = _mode(mode)
     k = len(params)
     if len(grads) != k or len(states) != k:
@@ -288,8 +294,8 @@ def pa_step_list(mode, params, grads, states, hyper, step, stream=None):
         raise TypeError("all tensors of one call must share the params' and the grads' dtypes")
     pdt, gdt = types.pop() if types else (PA_DT_F32, PA_DT_F32)
     h = _hyper(hyper)
-    _check(lib().pa_step_list_typed(mode, pdt, gdt, k, P, G, S, N, ctypes.byref(h), int(step),
-                                    _stream(stream)))
+    fn = lib().pa_step_list_noalloc if noalloc else lib().pa_step_list_typed
+    _check(fn(mode, pdt, gdt, k, P, G, S, N, ctypes.byref(h), int(step), _stream(stream)))
 
 
 class StepList:

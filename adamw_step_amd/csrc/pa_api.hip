@@ -401,6 +401,98 @@ hipError_t launch_blockwise(const pa::BlockwiseArgs& a, const pa::Scalars& s, un
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- tables
+
+// Validates the tensors of an elementwise list and builds its table: the
+// tensors of length 0 left out, a sentinel whose tile0 is the total tile
+// count appended (none for an empty list).  `ranges` receives every buffer
+// of the list, sorted and checked disjoint.
+int build_elem_table(int mode, int pdt, int gdt, size_t count, void* const* params, const void* const* grads,
+                     void* const* states, const size_t* n, std::vector<pa::Entry>* host, std::vector<Range>* ranges,
+                     long long* tiles_out) {
+  long long tiles = 0;
+  for (size_t i = 0; i < count; ++i) {
+    ElemTensor t;
+    const int rc = check_elem_tensor(mode, pdt, gdt, params[i], grads[i], states[i], n[i], &t, ranges);
+    if (rc) return rc;
+    if (t.n == 0) continue;
+    pa::Entry e = make_entry(t, tiles);
+    tiles += tiles_of(e);
+    host->push_back(e);
+  }
+  if (any_overlap(*ranges)) return PA_ERR_ALIAS;
+  if (host->size() > (size_t)INT32_MAX) return PA_ERR_ARG;
+  if (!host->empty()) {
+    pa::Entry sentinel;
+    std::memset(&sentinel, 0, sizeof(sentinel));
+    sentinel.tile0 = tiles;
+    host->push_back(sentinel);
+  }
+  *tiles_out = tiles;
+  return PA_OK;
+}
+
+// The device words named by a pa_hyper against the list's buffers (sorted,
+// disjoint) and against each other.
+int hyper_clear(const pa_hyper* hyper, const std::vector<Range>& sorted) {
+  std::vector<Range> hr;
+  hyper_ranges(hyper, &hr);
+  for (const Range& r : hr)
+    if (hits_sorted(sorted, r)) return PA_ERR_ALIAS;
+  if (any_overlap(hr)) return PA_ERR_ALIAS;
+  return PA_OK;
+}
+
+// ---------------------------------------------------------------- no-allocation tables
+
+// The tensor table of pa_step_list_noalloc lives in this array: each GPU the
+// library runs on holds its own copy until the process ends.  Host code
+// never uses the array's name as an address; it takes the device address
+// from hipGetSymbolAddress, once per device (scratch_table).
+static __device__ __align__(256) unsigned char scratch[(PA_NOALLOC_MAX_TENSORS + 1) * sizeof(pa::Entry)];
+
+std::mutex g_scratch_mu;
+pa::Entry* g_scratch_table[64] = {};
+
+// The device address of `scratch` on device `dev` (the current device).
+int scratch_table(int dev, pa::Entry** out) {
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_table[dev] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) return hip_failed(e != hipSuccess ? e : hipErrorInvalidSymbol);
+    g_scratch_table[dev] = static_cast<pa::Entry*>(ptr);
+  }
+  *out = g_scratch_table[dev];
+  return PA_OK;
+}
+
+// Table entries written by kernels whose arguments carry them: the upload is
+// ordered on the stream like the step that reads it, and keeps no host
+// buffer alive past the call.
+constexpr int kUploadEntries = 32;
+struct EntryChunk {
+  pa::Entry e[kUploadEntries];
+};
+
+__global__ void __launch_bounds__(64) upload_entries(pa::Entry* dst, EntryChunk chunk, int n) {
+  const int i = threadIdx.x;
+  if (i < n) dst[i] = chunk.e[i];
+}
+
+hipError_t upload_table(pa::Entry* dst, const std::vector<pa::Entry>& host, hipStream_t st) {
+  for (size_t i = 0; i < host.size(); i += kUploadEntries) {
+    EntryChunk c;
+    std::memset(&c, 0, sizeof(c));
+    const int m = (int)std::min<size_t>(kUploadEntries, host.size() - i);
+    std::memcpy(c.e, host.data() + i, (size_t)m * sizeof(pa::Entry));
+    hipLaunchKernelGGL(upload_entries, dim3(1), dim3(64), 0, st, dst + i, c, m);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 // ---------------------------------------------------------------- plans
 
 struct Plan {
@@ -614,9 +706,15 @@ int pa_step(int mode, float* params, const float* grads, void* state, size_t n, 
   return pa_step_typed(mode, PA_DT_F32, PA_DT_F32, params, grads, state, n, hyper, step, stream);
 }
 
-int pa_step_list_typed(int mode, int param_dtype, int grad_dtype, size_t count, void* const* params,
-                       const void* const* grads, void* const* states, const size_t* n, const pa_hyper* hyper,
-                       long long step, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// pa_step_list_typed (noalloc false: the table in a cached plan) and
+// pa_step_list_noalloc (noalloc true: the table in `scratch`).
+int step_list(bool noalloc, int mode, int param_dtype, int grad_dtype, size_t count, void* const* params,
+              const void* const* grads, void* const* states, const size_t* n, const pa_hyper* hyper, long long step,
+              void* stream) {
   if (!valid_mode(mode) || !valid_dtype_pair(param_dtype, grad_dtype)) return PA_ERR_ARG;
   if (mode == PA_BLOCKWISE8 && (param_dtype != PA_DT_F32 || grad_dtype != PA_DT_F32)) return PA_ERR_ARG;
   pa::Scalars s;
@@ -657,6 +755,28 @@ int pa_step_list_typed(int mode, int param_dtype, int grad_dtype, size_t count, 
     return PA_OK;
   }
 
+  if (noalloc) {
+    std::vector<pa::Entry> host;
+    std::vector<Range> ranges;
+    long long tiles = 0;
+    rc = build_elem_table(mode, param_dtype, grad_dtype, count, params, grads, states, n, &host, &ranges, &tiles);
+    if (rc) return rc;
+    if (host.empty()) return PA_OK;
+    if (host.size() > (size_t)PA_NOALLOC_MAX_TENSORS + 1) return PA_ERR_CAPACITY;
+    rc = hyper_clear(hyper, ranges);
+    if (rc) return rc;
+    rc = device_info(&dev, &d);
+    if (rc) return rc;
+    pa::Entry* table = nullptr;
+    rc = scratch_table(dev, &table);
+    if (rc) return rc;
+    hipError_t e = upload_table(table, host, st);
+    if (e == hipSuccess)
+      e = dispatch_list(mode, param_dtype, grad_dtype, table, (int)(host.size() - 1), tiles, s, hyper->nonfinite,
+                        st, d);
+    return e == hipSuccess ? PA_OK : hip_failed(e);
+  }
+
   rc = device_info(&dev, &d);
   if (rc) return rc;
 
@@ -686,22 +806,9 @@ int pa_step_list_typed(int mode, int param_dtype, int grad_dtype, size_t count, 
     std::vector<pa::Entry> host;
     std::vector<Range> ranges;
     long long tiles = 0;
-    for (size_t i = 0; i < count; ++i) {
-      ElemTensor t;
-      rc = check_elem_tensor(mode, param_dtype, grad_dtype, params[i], grads[i], states[i], n[i], &t, &ranges);
-      if (rc) return rc;
-      if (t.n == 0) continue;
-      pa::Entry e = make_entry(t, tiles);
-      tiles += tiles_of(e);
-      host.push_back(e);
-    }
-    if (any_overlap(ranges)) return PA_ERR_ALIAS;
+    rc = build_elem_table(mode, param_dtype, grad_dtype, count, params, grads, states, n, &host, &ranges, &tiles);
+    if (rc) return rc;
     if (host.empty()) return PA_OK;
-    if (host.size() > (size_t)INT32_MAX) return PA_ERR_ARG;
-    pa::Entry sentinel;
-    std::memset(&sentinel, 0, sizeof(sentinel));
-    sentinel.tile0 = tiles;
-    host.push_back(sentinel);
     Plan pl;
     pl.device = dev;
     pl.mode = mode;
@@ -732,17 +839,30 @@ int pa_step_list_typed(int mode, int param_dtype, int grad_dtype, size_t count, 
     g_plans.splice(g_plans.begin(), g_plans, it);
     it = g_plans.begin();
   }
-  {
-    std::vector<Range> hr;
-    hyper_ranges(hyper, &hr);
-    for (const Range& r : hr)
-      if (hits_sorted(it->ranges, r)) return PA_ERR_ALIAS;
-    if (any_overlap(hr)) return PA_ERR_ALIAS;
-  }
+  rc = hyper_clear(hyper, it->ranges);
+  if (rc) return rc;
   hipError_t e =
       dispatch_list(mode, param_dtype, grad_dtype, it->table, it->count, it->tiles, s, hyper->nonfinite, st, d);
   return e == hipSuccess ? PA_OK : hip_failed(e);
 }
+
+}  // namespace
+
+extern "C" {
+
+int pa_step_list_typed(int mode, int param_dtype, int grad_dtype, size_t count, void* const* params,
+                       const void* const* grads, void* const* states, const size_t* n, const pa_hyper* hyper,
+                       long long step, void* stream) {
+  return step_list(false, mode, param_dtype, grad_dtype, count, params, grads, states, n, hyper, step, stream);
+}
+
+int pa_step_list_noalloc(int mode, int param_dtype, int grad_dtype, size_t count, void* const* params,
+                         const void* const* grads, void* const* states, const size_t* n, const pa_hyper* hyper,
+                         long long step, void* stream) {
+  return step_list(true, mode, param_dtype, grad_dtype, count, params, grads, states, n, hyper, step, stream);
+}
+
+
 
 int pa_step_list(int mode, size_t count, float* const* params, const float* const* grads, void* const* states,
                  const size_t* n, const pa_hyper* hyper, long long step, void* stream) {
@@ -1092,6 +1212,7 @@ const char* pa_status_string(int status) {
     case PA_ERR_ALIAS: return "buffers overlap";
     case PA_ERR_DEVICE: return "HIP runtime error";
     case PA_ERR_NOMEM: return "device allocation of the launch plan failed";
+    case PA_ERR_CAPACITY: return "more tensors than the no-allocation table holds (PA_NOALLOC_MAX_TENSORS)";
     default: return "unknown status";
   }
 }

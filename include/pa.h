@@ -97,7 +97,9 @@ enum {
   PA_ERR_SHAPE = -3,  /* blockwise length not a multiple of 2048 */
   PA_ERR_ALIAS = -4,  /* two buffers of one call overlap */
   PA_ERR_DEVICE = -5, /* the HIP runtime refused a launch or a copy */
-  PA_ERR_NOMEM = -6   /* the launch plan table could not be allocated */
+  PA_ERR_NOMEM = -6,  /* the launch plan table could not be allocated */
+  PA_ERR_CAPACITY = -7 /* pa_step_list_noalloc: more non-empty tensors than
+                          PA_NOALLOC_MAX_TENSORS */
 };
 
 /* Hyperparameters, host doubles (TurboAdam package page, API section: lr,
@@ -189,6 +191,25 @@ int pa_step_typed(int mode, int param_dtype, int grad_dtype, void* params, const
 int pa_step_list_typed(int mode, int param_dtype, int grad_dtype, size_t count, void* const* params,
                        const void* const* grads, void* const* states, const size_t* n,
                        const pa_hyper* hyper, long long step, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * pa_step_list_typed with the same arguments, results and errors, except
+ * that the tensor table lives in a static device array of the library
+ * (one per GPU, held until the process ends) instead of a cached plan.
+ * The call makes no hipMalloc, hipFree or other allocating device call: it
+ * writes the list's table into that array with small kernels on `stream`
+ * and then launches the step, every call (nothing is cached).  At most
+ * PA_NOALLOC_MAX_TENSORS non-empty tensors per call (PA_ERR_CAPACITY
+ * beyond, before anything is enqueued).  Every call on one GPU shares the
+ * array: calls that overlap on one GPU (on different streams, or from
+ * different threads without ordering) race on it and may update the wrong
+ * tensors; calls ordered on one stream are safe.  Blockwise mode uses no
+ * table and behaves exactly as pa_step_list_typed. */
+#define PA_NOALLOC_MAX_TENSORS 4095
+int pa_step_list_noalloc(int mode, int param_dtype, int grad_dtype, size_t count, void* const* params,
+                         const void* const* grads, void* const* states, const size_t* n,
+                         const pa_hyper* hyper, long long step, void* stream);
 
 /* Gradient pre-pass over `count` gradient tensors of one element type
  * (PA_DT_F32, PA_DT_BF16 or PA_DT_F16; grads[i] points to n[i] device

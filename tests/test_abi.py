@@ -64,7 +64,7 @@ def test_format_info_agrees_with_oracle(pa, oracle_mod):
 
 
 def test_status_strings(pa):
-    for rc in range(0, -7, -1):
+    for rc in range(0, -8, -1):
         assert pa.pa_status_string(rc) != "unknown status"
     assert pa.pa_status_string(-99) == "unknown status"
 
@@ -277,3 +277,22 @@ def test_turbo_argument_rules(pa):
     N[0] = 2048 * 256 + 1                                                 # 2049 tile sums, 2 chunk sums
     assert L.pa_turbo_workspace_bytes(1, S, N) == 8 * (2049 + 2)
     N[0] = 4096
+
+
+def test_noalloc_refuses_a_list_over_capacity_before_any_device_call(pa):
+    """pa_step_list_noalloc checks the list against the capacity of its
+    static table on the host (fake device addresses are never touched), and
+    the binding's constant is the header's."""
+    import re
+    with open(os.path.join(ROOT, "include", "pa.h")) as f:
+        cap = int(re.search(r"#define PA_NOALLOC_MAX_TENSORS (\d+)", f.read()).group(1))
+    assert cap == pa.PA_NOALLOC_MAX_TENSORS
+    L = pa.lib()
+    k = cap + 1
+    P = (ctypes.c_void_p * k)(*[FAKE + 64 * i for i in range(k)])
+    G = (ctypes.c_void_p * k)(*[FAKE + (1 << 24) + 64 * i for i in range(k)])
+    S = (ctypes.c_void_p * k)(*[FAKE + (1 << 25) + 64 * i for i in range(k)])
+    N = (ctypes.c_size_t * k)(*([4] * k))
+    h = pa._hyper(dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0))
+    assert L.pa_step_list_noalloc(1, 0, 0, k, P, G, S, N, ctypes.byref(h), 1, None) == pa.PA_ERR_CAPACITY
+    assert L.pa_step_list_noalloc(1, 0, 0, 2, P, G, S, N, ctypes.byref(h), 0, None) == pa.PA_ERR_ARG
