@@ -103,7 +103,15 @@ __device__ __forceinline__ void stream_store(T* p, T v) {
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = PA_TILE_UNROLL;
-constexpr int kTile = kThreads * 4 * kUnroll;   // elements per tile
+constexpr int kTile = kThreads * 4 * kUnroll;   // elements per tile of a large list
+// Lists of fewer elements than this take tiles a quarter as large (one
+// 16-byte vector per thread per stream): more workgroups, so the last
+// workgroups to finish hold less work.
+#ifndef PA_SMALL_LIST_ELEMS
+#define PA_SMALL_LIST_ELEMS (32LL << 20)
+#endif
+constexpr long long kSmallList = PA_SMALL_LIST_ELEMS;
+constexpr int kSmallUnroll = 1;
 constexpr int kBlock = 2048;                    // blockwise quantisation block
 
 enum { kModeFp32 = 0, kModeE4 = 1, kModeF16 = 2 };
@@ -250,10 +258,13 @@ __device__ __forceinline__ void scalar_elem(const Entry& e, long long i, const S
 // SPLIT > 1 takes a whole tile in that many rounds of loads, arithmetic and
 // stores, one after the other: fewer values live at once, so more
 // wavefronts fit (the variants that also count or scale need it).
-template <int MODE, int PT, int GT, bool SCALE, int SPLIT = 1>
+// UNROLL: 16-byte vectors per thread per stream in a tile (a tile holds
+// 1024 * UNROLL elements).
+template <int MODE, int PT, int GT, bool SCALE, int SPLIT = 1, int UNROLL = kUnroll>
 __device__ __forceinline__ void run_tile(const Entry& e, long long tile, const Scalars& s, uint32_t& bad) {
-  static_assert(kUnroll % SPLIT == 0, "whole rounds");
-  constexpr int U = kUnroll / SPLIT;
+  static_assert(UNROLL % SPLIT == 0, "whole rounds");
+  constexpr int U = UNROLL / SPLIT;
+  constexpr int kTile = kThreads * 4 * UNROLL;
   using PE = Elem<PT>;
   using GE = Elem<GT>;
   using PV = typename PE::vec4;
@@ -332,7 +343,7 @@ __device__ __forceinline__ void run_tile(const Entry& e, long long tile, const S
     }
   } else {
     // Ragged tile (first tile of a misaligned tensor, or the last one).
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < UNROLL; ++u) {
       const long long vb = v0 + ((long long)u * kThreads + tid) * 4;
       for (int k = 0; k < 4; ++k) {
         const long long vi = vb + k;
@@ -368,7 +379,7 @@ __device__ __forceinline__ int tensor_of_tile(const Entry* table, int count, lon
 // any moment form one compact, advancing window of every stream (measured
 // on MI355X: a write stream runs at about 6.8 TB/s in this order against
 // about 5.5 TB/s for a persistent grid striding over the same tiles).
-template <int MODE, int PT, int GT, bool COUNT, bool SCALE>
+template <int MODE, int PT, int GT, bool COUNT, bool SCALE, int UNROLL>
 __global__ void __launch_bounds__(kThreads)
 elementwise_list(const Entry* __restrict__ table, int count, long long tile_base, Scalars s,
                  unsigned long long* nonfinite) {
@@ -376,17 +387,17 @@ elementwise_list(const Entry* __restrict__ table, int count, long long tile_base
   const long long tile = tile_base + blockIdx.x;
   const Entry e = table[tensor_of_tile(table, count, tile)];
   uint32_t bad = 0;
-  run_tile<MODE, PT, GT, SCALE, (COUNT || SCALE) ? 2 : 1>(e, tile - e.tile0, s, bad);
+  run_tile<MODE, PT, GT, SCALE, ((COUNT || SCALE) && UNROLL > 1) ? 2 : 1, UNROLL>(e, tile - e.tile0, s, bad);
   if constexpr (COUNT) flush_count(bad, nonfinite);
 }
 
 // Single tensor, its entry passed by value (no table in device memory).
-template <int MODE, int PT, int GT, bool COUNT, bool SCALE>
+template <int MODE, int PT, int GT, bool COUNT, bool SCALE, int UNROLL>
 __global__ void __launch_bounds__(kThreads)
 elementwise_one(Entry e, long long tile_base, Scalars s, unsigned long long* nonfinite) {
   if (!resolve_inputs(s)) return;
   uint32_t bad = 0;
-  run_tile<MODE, PT, GT, SCALE, (COUNT || SCALE) ? 2 : 1>(e, tile_base + blockIdx.x, s, bad);
+  run_tile<MODE, PT, GT, SCALE, ((COUNT || SCALE) && UNROLL > 1) ? 2 : 1, UNROLL>(e, tile_base + blockIdx.x, s, bad);
   if constexpr (COUNT) flush_count(bad, nonfinite);
 }
 

@@ -91,7 +91,7 @@ int device_info(int* dev_out, DeviceInfo* info) {
     if (e != hipSuccess) return hip_failed(e);
     int per = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per, reinterpret_cast<const void*>(pa::elementwise_list<pa::kModeE4, pa::kF32, pa::kF32, false, false>),
+        &per, reinterpret_cast<const void*>(pa::elementwise_list<pa::kModeE4, pa::kF32, pa::kF32, false, false, pa::kUnroll>),
         pa::kThreads, 0);
     if (e != hipSuccess || per < 1) per = 4;
     int bw = 0;
@@ -240,7 +240,14 @@ pa::Entry make_entry(const ElemTensor& t, long long tile0) {
   return e;
 }
 
-long long tiles_of(const pa::Entry& e) { return (e.n + e.phase + pa::kTile - 1) / pa::kTile; }
+// Tiles of a tensor at `unroll` vectors per thread (1024 * unroll elements).
+long long tiles_of(const pa::Entry& e, int unroll = pa::kUnroll) {
+  const long long t = 1024LL * unroll;
+  return (e.n + e.phase + t - 1) / t;
+}
+
+// The tile size of a list of `total` elements (see kSmallList).
+int unroll_for(unsigned long long total) { return total < (unsigned long long)pa::kSmallList ? pa::kSmallUnroll : pa::kUnroll; }
 
 // ---------------------------------------------------------------- launches
 
@@ -262,45 +269,58 @@ hipError_t launch_tiles(long long tiles, K kernel, F&& launch) {
   return hipSuccess;
 }
 
-template <int MODE, int PT, int GT, bool COUNT, bool SCALE>
+template <int MODE, int PT, int GT, bool COUNT, bool SCALE, int UNROLL>
 hipError_t launch_one_v(const pa::Entry& e, long long tiles, const pa::Scalars& s, unsigned long long* nf,
-                        hipStream_t st, const DeviceInfo& d) {
-  (void)d;
-  return launch_tiles(tiles, pa::elementwise_one<MODE, PT, GT, COUNT, SCALE>, [&](auto k, dim3 grid, long long base) {
-    hipLaunchKernelGGL(k, grid, dim3(pa::kThreads), 0, st, e, base, s, nf);
-  });
+                        hipStream_t st) {
+  return launch_tiles(tiles, pa::elementwise_one<MODE, PT, GT, COUNT, SCALE, UNROLL>,
+                      [&](auto k, dim3 grid, long long base) {
+                        hipLaunchKernelGGL(k, grid, dim3(pa::kThreads), 0, st, e, base, s, nf);
+                      });
 }
 
-// Kernel variant: with or without the non-finite counter, and with or
-// without a device gradient scale.
-template <int MODE, int PT, int GT>
-hipError_t launch_one(const pa::Entry& e, long long tiles, const pa::Scalars& s, unsigned long long* nf,
-                      hipStream_t st, const DeviceInfo& d) {
+// Kernel variant: with or without the non-finite counter, with or without
+// a device gradient scale, and the tile size.
+template <int MODE, int PT, int GT, int UNROLL>
+hipError_t launch_one_u(const pa::Entry& e, long long tiles, const pa::Scalars& s, unsigned long long* nf,
+                        hipStream_t st) {
   const bool sc = s.gscale != nullptr;
-  if (nf && sc) return launch_one_v<MODE, PT, GT, true, true>(e, tiles, s, nf, st, d);
-  if (nf) return launch_one_v<MODE, PT, GT, true, false>(e, tiles, s, nf, st, d);
-  if (sc) return launch_one_v<MODE, PT, GT, false, true>(e, tiles, s, nf, st, d);
-  return launch_one_v<MODE, PT, GT, false, false>(e, tiles, s, nf, st, d);
+  if (nf && sc) return launch_one_v<MODE, PT, GT, true, true, UNROLL>(e, tiles, s, nf, st);
+  if (nf) return launch_one_v<MODE, PT, GT, true, false, UNROLL>(e, tiles, s, nf, st);
+  if (sc) return launch_one_v<MODE, PT, GT, false, true, UNROLL>(e, tiles, s, nf, st);
+  return launch_one_v<MODE, PT, GT, false, false, UNROLL>(e, tiles, s, nf, st);
 }
 
-template <int MODE, int PT, int GT, bool COUNT, bool SCALE>
+template <int MODE, int PT, int GT>
+hipError_t launch_one(const pa::Entry& e, int unroll, long long tiles, const pa::Scalars& s, unsigned long long* nf,
+                      hipStream_t st) {
+  if (unroll == pa::kSmallUnroll) return launch_one_u<MODE, PT, GT, pa::kSmallUnroll>(e, tiles, s, nf, st);
+  return launch_one_u<MODE, PT, GT, pa::kUnroll>(e, tiles, s, nf, st);
+}
+
+template <int MODE, int PT, int GT, bool COUNT, bool SCALE, int UNROLL>
 hipError_t launch_list_v(const pa::Entry* table, int count, long long tiles, const pa::Scalars& s,
-                         unsigned long long* nf, hipStream_t st, const DeviceInfo& d) {
-  (void)d;
-  return launch_tiles(tiles, pa::elementwise_list<MODE, PT, GT, COUNT, SCALE>,
+                         unsigned long long* nf, hipStream_t st) {
+  return launch_tiles(tiles, pa::elementwise_list<MODE, PT, GT, COUNT, SCALE, UNROLL>,
                       [&](auto k, dim3 grid, long long base) {
                         hipLaunchKernelGGL(k, grid, dim3(pa::kThreads), 0, st, table, count, base, s, nf);
                       });
 }
 
-template <int MODE, int PT, int GT>
-hipError_t launch_list(const pa::Entry* table, int count, long long tiles, const pa::Scalars& s,
-                       unsigned long long* nf, hipStream_t st, const DeviceInfo& d) {
+template <int MODE, int PT, int GT, int UNROLL>
+hipError_t launch_list_u(const pa::Entry* table, int count, long long tiles, const pa::Scalars& s,
+                         unsigned long long* nf, hipStream_t st) {
   const bool sc = s.gscale != nullptr;
-  if (nf && sc) return launch_list_v<MODE, PT, GT, true, true>(table, count, tiles, s, nf, st, d);
-  if (nf) return launch_list_v<MODE, PT, GT, true, false>(table, count, tiles, s, nf, st, d);
-  if (sc) return launch_list_v<MODE, PT, GT, false, true>(table, count, tiles, s, nf, st, d);
-  return launch_list_v<MODE, PT, GT, false, false>(table, count, tiles, s, nf, st, d);
+  if (nf && sc) return launch_list_v<MODE, PT, GT, true, true, UNROLL>(table, count, tiles, s, nf, st);
+  if (nf) return launch_list_v<MODE, PT, GT, true, false, UNROLL>(table, count, tiles, s, nf, st);
+  if (sc) return launch_list_v<MODE, PT, GT, false, true, UNROLL>(table, count, tiles, s, nf, st);
+  return launch_list_v<MODE, PT, GT, false, false, UNROLL>(table, count, tiles, s, nf, st);
+}
+
+template <int MODE, int PT, int GT>
+hipError_t launch_list(const pa::Entry* table, int count, int unroll, long long tiles, const pa::Scalars& s,
+                       unsigned long long* nf, hipStream_t st) {
+  if (unroll == pa::kSmallUnroll) return launch_list_u<MODE, PT, GT, pa::kSmallUnroll>(table, count, tiles, s, nf, st);
+  return launch_list_u<MODE, PT, GT, pa::kUnroll>(table, count, tiles, s, nf, st);
 }
 
 // One launch for a (mode, parameter type, gradient type) triple; `L` is
@@ -331,18 +351,18 @@ hipError_t by_mode(int mode, int pdt, int gdt, F&& f) {
   }
 }
 
-hipError_t dispatch_one(int mode, int pdt, int gdt, const pa::Entry& e, long long tiles, const pa::Scalars& s,
-                        unsigned long long* nf, hipStream_t st, const DeviceInfo& d) {
+hipError_t dispatch_one(int mode, int pdt, int gdt, const pa::Entry& e, int unroll, long long tiles,
+                        const pa::Scalars& s, unsigned long long* nf, hipStream_t st) {
   return by_mode(mode, pdt, gdt, [&](auto m, auto pt, auto gt) {
-    return launch_one<decltype(m)::value, decltype(pt)::value, decltype(gt)::value>(e, tiles, s, nf, st, d);
+    return launch_one<decltype(m)::value, decltype(pt)::value, decltype(gt)::value>(e, unroll, tiles, s, nf, st);
   });
 }
 
-hipError_t dispatch_list(int mode, int pdt, int gdt, const pa::Entry* table, int count, long long tiles,
-                         const pa::Scalars& s, unsigned long long* nf, hipStream_t st, const DeviceInfo& d) {
+hipError_t dispatch_list(int mode, int pdt, int gdt, const pa::Entry* table, int count, int unroll, long long tiles,
+                         const pa::Scalars& s, unsigned long long* nf, hipStream_t st) {
   return by_mode(mode, pdt, gdt, [&](auto m, auto pt, auto gt) {
-    return launch_list<decltype(m)::value, decltype(pt)::value, decltype(gt)::value>(table, count, tiles, s, nf, st,
-                                                                                     d);
+    return launch_list<decltype(m)::value, decltype(pt)::value, decltype(gt)::value>(table, count, unroll, tiles, s,
+                                                                                     nf, st);
   });
 }
 
@@ -408,8 +428,8 @@ hipError_t launch_blockwise(const pa::BlockwiseArgs& a, const pa::Scalars& s, un
 // count appended (none for an empty list).  `ranges` receives every buffer
 // of the list, sorted and checked disjoint.
 int build_elem_table(int mode, int pdt, int gdt, size_t count, void* const* params, const void* const* grads,
-                     void* const* states, const size_t* n, std::vector<pa::Entry>* host, std::vector<Range>* ranges,
-                     long long* tiles_out) {
+                     void* const* states, const size_t* n, int unroll, std::vector<pa::Entry>* host,
+                     std::vector<Range>* ranges, long long* tiles_out) {
   long long tiles = 0;
   for (size_t i = 0; i < count; ++i) {
     ElemTensor t;
@@ -417,7 +437,7 @@ int build_elem_table(int mode, int pdt, int gdt, size_t count, void* const* para
     if (rc) return rc;
     if (t.n == 0) continue;
     pa::Entry e = make_entry(t, tiles);
-    tiles += tiles_of(e);
+    tiles += tiles_of(e, unroll);
     host->push_back(e);
   }
   if (any_overlap(*ranges)) return PA_ERR_ALIAS;
@@ -697,7 +717,8 @@ int pa_step_typed(int mode, int param_dtype, int grad_dtype, void* params, const
   rc = device_info(&dev, &d);
   if (rc) return rc;
   const pa::Entry e = make_entry(t, 0);
-  hipError_t err = dispatch_one(mode, param_dtype, grad_dtype, e, tiles_of(e), s, hyper->nonfinite, st, d);
+  const int unroll = unroll_for(n);
+  hipError_t err = dispatch_one(mode, param_dtype, grad_dtype, e, unroll, tiles_of(e, unroll), s, hyper->nonfinite, st);
   return err == hipSuccess ? PA_OK : hip_failed(err);
 }
 
@@ -755,11 +776,15 @@ int step_list(bool noalloc, int mode, int param_dtype, int grad_dtype, size_t co
     return PA_OK;
   }
 
+  unsigned long long total = 0;
+  for (size_t i = 0; i < count; ++i) total += n[i];
+  const int unroll = unroll_for(total);
   if (noalloc) {
     std::vector<pa::Entry> host;
     std::vector<Range> ranges;
     long long tiles = 0;
-    rc = build_elem_table(mode, param_dtype, grad_dtype, count, params, grads, states, n, &host, &ranges, &tiles);
+    rc = build_elem_table(mode, param_dtype, grad_dtype, count, params, grads, states, n, unroll, &host, &ranges,
+                          &tiles);
     if (rc) return rc;
     if (host.empty()) return PA_OK;
     if (host.size() > (size_t)PA_NOALLOC_MAX_TENSORS + 1) return PA_ERR_CAPACITY;
@@ -772,8 +797,8 @@ int step_list(bool noalloc, int mode, int param_dtype, int grad_dtype, size_t co
     if (rc) return rc;
     hipError_t e = upload_table(table, host, st);
     if (e == hipSuccess)
-      e = dispatch_list(mode, param_dtype, grad_dtype, table, (int)(host.size() - 1), tiles, s, hyper->nonfinite,
-                        st, d);
+      e = dispatch_list(mode, param_dtype, grad_dtype, table, (int)(host.size() - 1), unroll, tiles, s,
+                        hyper->nonfinite, st);
     return e == hipSuccess ? PA_OK : hip_failed(e);
   }
 
@@ -806,7 +831,8 @@ int step_list(bool noalloc, int mode, int param_dtype, int grad_dtype, size_t co
     std::vector<pa::Entry> host;
     std::vector<Range> ranges;
     long long tiles = 0;
-    rc = build_elem_table(mode, param_dtype, grad_dtype, count, params, grads, states, n, &host, &ranges, &tiles);
+    rc = build_elem_table(mode, param_dtype, grad_dtype, count, params, grads, states, n, unroll, &host, &ranges,
+                          &tiles);
     if (rc) return rc;
     if (host.empty()) return PA_OK;
     Plan pl;
@@ -842,7 +868,7 @@ int step_list(bool noalloc, int mode, int param_dtype, int grad_dtype, size_t co
   rc = hyper_clear(hyper, it->ranges);
   if (rc) return rc;
   hipError_t e =
-      dispatch_list(mode, param_dtype, grad_dtype, it->table, it->count, it->tiles, s, hyper->nonfinite, st, d);
+      dispatch_list(mode, param_dtype, grad_dtype, it->table, it->count, unroll, it->tiles, s, hyper->nonfinite, st);
   return e == hipSuccess ? PA_OK : hip_failed(e);
 }
 
@@ -889,8 +915,12 @@ int pa_grad_stats_list(int grad_dtype, size_t count, const void* const* grads, c
   int rc = device_info(&dev, &d);
   if (rc) return rc;
 
+  // Key: the list and the stream.  The plan holds the per-workgroup
+  // partials, so calls on different streams get plans of their own and
+  // cannot overwrite each other's partials.
   std::vector<uintptr_t> key;
-  key.reserve(count * 2);
+  key.reserve(count * 2 + 1);
+  key.push_back(reinterpret_cast<uintptr_t>(stream));
   for (size_t i = 0; i < count; ++i) {
     key.push_back(reinterpret_cast<uintptr_t>(grads[i]));
     key.push_back((uintptr_t)n[i]);

@@ -233,7 +233,9 @@ int pa_step_list_noalloc(int mode, int param_dtype, int grad_dtype, size_t count
  * optimizer count (Packed AdamW Reference README, One-update smoke test).
  * Gradients must be aligned to their element size and must not overlap the
  * outputs.  The tensor table and per-workgroup partials are cached per
- * distinct list like the step's plans (see pa_release_plans).  count == 0,
+ * distinct list and stream like the step's plans (see pa_release_plans):
+ * calls on different streams use separate partials; two calls on one
+ * stream are ordered by it.  count == 0,
  * or only empty tensors, writes 0, 0 and the coefficient of a zero norm. */
 int pa_grad_stats_list(int grad_dtype, size_t count, const void* const* grads, const size_t* n,
                        double max_norm, double* sumsq, unsigned long long* nonfinite, float* clip_scale,
