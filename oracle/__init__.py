@@ -85,11 +85,15 @@ def _load():
     lib.oracle_scale_grads.restype = None
     lib.oracle_philox4x32.argtypes = [_u32p, _u32p, _u32p]
     lib.oracle_philox4x32.restype = None
-    lib.oracle_turbo_state_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t]
+    lib.oracle_turbo_state_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_size_t]
+    lib.oracle_turbo_layout_ok.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.oracle_turbo_layout_ok.restype = ctypes.c_int
     lib.oracle_turbo_state_bytes.restype = ctypes.c_size_t
     vp = ctypes.c_void_p
     lib.oracle_turbo_step.argtypes = [_f32p, _f32p, ctypes.c_size_t, ctypes.c_uint32, ctypes.c_int, ctypes.c_int,
-                                      ctypes.c_int, vp, vp, vp, vp, vp, vp, _f32p, _f32p, _f32p, ctypes.c_double,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, _f32p, _f32p,
+                                      _f32p, ctypes.c_double,
                                       ctypes.c_ulonglong, ctypes.c_longlong]
     lib.oracle_turbo_step.restype = ctypes.c_ulonglong
     lib.oracle_q1_levels.argtypes = [ctypes.c_uint16, ctypes.c_uint16, ctypes.c_int, _f32p]
@@ -102,7 +106,7 @@ def _load():
     lib.oracle_q1_ends_batch.restype = None
     lib.oracle_q1_block.argtypes = [_f32p, ctypes.c_size_t, ctypes.c_int, _f32p, _u8p, _u16p, _f32p]
     lib.oracle_q1_block.restype = None
-    lib.oracle_ustate_group.argtypes = [_f32p, ctypes.c_size_t, ctypes.c_float, _f32p, _u8p, _u16p,
+    lib.oracle_ustate_group.argtypes = [_f32p, ctypes.c_size_t, ctypes.c_size_t, ctypes.c_float, _f32p, _u8p, _u16p,
                                         ctypes.POINTER(ctypes.c_double)]
     lib.oracle_ustate_group.restype = None
     lib.oracle_ustate_decode.argtypes = [_u8p, ctypes.c_size_t, ctypes.c_uint16, ctypes.c_float, _f32p]
@@ -289,20 +293,30 @@ def philox4x32(counter, key):
     return out
 
 
-def turbo_state_bytes(compress_m, compress_v, bits, n):
-    return int(_load().oracle_turbo_state_bytes(int(compress_m), int(compress_v), int(bits), int(n)))
+def turbo_layout_ok(bits, block, group):
+    """Whether the oracle takes this index width, 1Q block and UState group."""
+    return bool(_load().oracle_turbo_layout_ok(int(bits), int(block), int(group)))
+
+
+def turbo_state_bytes(compress_m, compress_v, bits, n, block=128, group=64):
+    return int(_load().oracle_turbo_state_bytes(int(compress_m), int(compress_v), int(bits), int(block), int(group),
+                                                int(n)))
 
 
 class TurboState:
-    """Host copy of one tensor's TurboAdam state, zero-filled (the empty state)."""
+    """Host copy of one tensor's TurboAdam state, zero-filled (the empty state).
+    block: the 1Q block (values per endpoint pair); group: the UState group
+    (values per mean)."""
 
-    def __init__(self, n, compress_m=True, compress_v=True, bits=4):
+    def __init__(self, n, compress_m=True, compress_v=True, bits=4, block=128, group=64):
+        assert turbo_layout_ok(bits, block, group), (bits, block, group)
         self.n, self.compress_m, self.compress_v, self.bits = n, bool(compress_m), bool(compress_v), bits
+        self.block, self.group = block, group
         self.m_codes = np.zeros((n + 15) // 16, np.uint32) if compress_m else None
-        self.m_means = np.zeros((n + 63) // 64, np.uint16) if compress_m else None
+        self.m_means = np.zeros((n + group - 1) // group, np.uint16) if compress_m else None
         self.m_fp32 = None if compress_m else np.zeros(n, np.float32)
         self.v_index = np.zeros((n * bits + 31) // 32, np.uint32) if compress_v else None
-        self.v_ends = np.zeros(2 * ((n + 127) // 128), np.uint16) if compress_v else None
+        self.v_ends = np.zeros(2 * ((n + block - 1) // block), np.uint16) if compress_v else None
         self.v_fp32 = None if compress_v else np.zeros(n, np.float32)
         self.scal = np.zeros(3, np.float32)
 
@@ -328,7 +342,7 @@ def turbo_step(p, g, st, sc, ts, step, tensor_id=0, factor=1.1, seed=0x12345678)
     addr = lambda a: None if a is None else a.ctypes.data
     return int(_load().oracle_turbo_step(
         _ptr(p, _f32p), _ptr(g, _f32p), p.size, int(tensor_id), int(st.compress_m), int(st.compress_v), int(st.bits),
-        addr(st.m_codes), addr(st.m_means), addr(st.m_fp32), addr(st.v_index), addr(st.v_ends), addr(st.v_fp32),
+        int(st.block), int(st.group), addr(st.m_codes), addr(st.m_means), addr(st.m_fp32), addr(st.v_index), addr(st.v_ends), addr(st.v_fp32),
         _ptr(st.scal, _f32p), _ptr(sc, _f32p), _ptr(ts, _f32p), float(factor), int(seed), int(step)))
 
 
@@ -367,10 +381,10 @@ def q1_ends(v):
 
 
 def q1_block(v, bits, u):
-    """1Q encode of one block (<= 128 values) with draws u: (indices, (lo, hi) fp16 bits, decoded)."""
+    """1Q encode of one block (<= 1024 values) with draws u: (indices, (lo, hi) fp16 bits, decoded)."""
     v = np.ascontiguousarray(v, np.float32)
     u = np.ascontiguousarray(u, np.float32)
-    assert v.size == u.size <= 128
+    assert v.size == u.size <= 1024
     idx = np.zeros(v.size, np.uint8)
     ends = np.zeros(2, np.uint16)
     dec = np.zeros(v.size, np.float32)
@@ -379,15 +393,16 @@ def q1_block(v, bits, u):
     return idx, ends, dec
 
 
-def ustate_group(q, s_enc, u_pair):
-    """UState encode of one group (<= 64 values): (codes, bf16 mean bits, squared residuals)."""
+def ustate_group(q, s_enc, u_pair, group=64):
+    """UState encode of one group (<= group values, group a power of two up
+    to 1024): (codes, bf16 mean bits, squared residuals)."""
     q = np.ascontiguousarray(q, np.float32)
     u_pair = np.ascontiguousarray(u_pair, np.float32)
-    assert q.size <= 64 and u_pair.size >= (q.size + 1) // 2
+    assert q.size <= group <= 1024 and group & (group - 1) == 0 and u_pair.size >= (q.size + 1) // 2
     codes = np.zeros(q.size, np.uint8)
     mean = np.zeros(1, np.uint16)
     r2 = np.zeros(q.size, np.float64)
-    _load().oracle_ustate_group(_ptr(q, _f32p), q.size, float(np.float32(s_enc)), _ptr(u_pair, _f32p),
+    _load().oracle_ustate_group(_ptr(q, _f32p), q.size, int(group), float(np.float32(s_enc)), _ptr(u_pair, _f32p),
                                 _ptr(codes, _u8p), _ptr(mean, _u16p), r2.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
     return codes, int(mean[0]), r2
 

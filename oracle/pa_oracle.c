@@ -667,6 +667,15 @@ void oracle_scale_grads(int gdt, const void* g, float scale, float* out, size_t 
  *  The residual sum of squares is a perfect pairwise tree, in double, over
  *    r^2 in index order padded with zeros to a power of two; after the
  *    step s_dec <- s_enc, s_enc <- RN32(factor * sqrt(sum / n)), acc <- 0.
+ *  Layout (the page's "Fused CUDA path": power-of-two storage blocks from
+ *    32 to 1024 values, UState mean blocks that divide the storage block,
+ *    and 2, 3, 4, 6 or 8 index bits; defaults 128, 64 and 4): a 1Q block
+ *    of B values shares one pair of endpoints; a UState group of G values
+ *    (G a power of two dividing B) shares one mean; the storage block
+ *    does not otherwise enter the arithmetic.  Indices are packed densely,
+ *    value i in bits [b*i, b*i + b) of the little-endian bit stream of the
+ *    index words (so 3- and 6-bit indices straddle words); UState codes
+ *    likewise at 2 bits.
  *  Random numbers: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11), the
  *    counter-based generator Triton builds in, so the counter hash that a
  *    PyTorch path and a Triton path can share.  Key (low and high 32 bits of
@@ -676,8 +685,7 @@ void oracle_scale_grads(int gdt, const void* g, float scale, float* out, size_t 
  *    bits of words 0 and 1 give the UState draws of the pairs (4j, 4j+1)
  *    and (4j+2, 4j+3).  A draw is those 24 bits times 2^-24. */
 
-#define T_GROUP 64
-#define T_BLOCK 128
+#define T_MAX_BLOCK 1024
 
 /* Ten rounds of the Philox-4x32 bijection.  A round multiplies words 0 and 2
  * by the two round multipliers, xors each product's high half with the other
@@ -816,7 +824,7 @@ void oracle_q1_levels_batch(const uint32_t* ends, size_t n, int bits, float* lev
         level_table((uint16_t)(ends[i] & 0xFFFFu), (uint16_t)(ends[i] >> 16), L, lev + i * (size_t)L);
 }
 
-/* 1Q encode of one block of len (<= 128) second-moment values with draws u:
+/* 1Q encode of one block of len (<= 1024) second-moment values with draws u:
  * the fp16 endpoints, each value's index, and the decoded (persisted) value. */
 void oracle_q1_block(const float* v, size_t len, int bits, const float* u, uint8_t* idx, uint16_t ends[2],
                      float* vdec) {
@@ -858,15 +866,17 @@ void oracle_q1_block(const float* v, size_t len, int bits, const float* u, uint8
 
 static const float T_LEVEL[4] = {-1.5f, -0.5f, 0.5f, 1.5f};
 
-/* UState encode of one group of len (<= 64) values q with encode scale s_enc
- * and one draw per pair (u_pair[j] for values 2j and 2j+1, the second using
- * 1 - u): the bf16 mean, each code, and each residual's square (double). */
-void oracle_ustate_group(const float* q, size_t len, float s_enc, const float* u_pair, uint8_t* codes,
+/* UState encode of one group of len (<= group) values q, group a power of
+ * two up to 1024, with encode scale s_enc and one draw per pair (u_pair[j]
+ * for values 2j and 2j+1, the second using 1 - u): the bf16 mean (the
+ * pairwise tree over the group's values padded with zeros to `group`,
+ * divided by len), each code, and each residual's square (double). */
+void oracle_ustate_group(const float* q, size_t len, size_t group, float s_enc, const float* u_pair, uint8_t* codes,
                          uint16_t* mean16, double* r2) {
     build_tables();
-    double qd[T_GROUP];
-    for (size_t k = 0; k < T_GROUP; ++k) qd[k] = k < len ? (double)q[k] : 0.0;
-    float meanf = (float)(pairwise_sum(qd, T_GROUP) / (double)len);
+    double qd[T_MAX_BLOCK];
+    for (size_t k = 0; k < group; ++k) qd[k] = k < len ? (double)q[k] : 0.0;
+    float meanf = (float)(pairwise_sum(qd, group) / (double)len);
     *mean16 = oracle_encode_bf16(meanf);
     float mean = oracle_decode_bf16(*mean16);
     for (size_t i = 0; i < len; ++i) {
@@ -895,25 +905,47 @@ void oracle_ustate_decode(const uint8_t* codes, size_t len, uint16_t mean16, flo
     for (size_t k = 0; k < len; ++k) q[k] = mean + s_dec * (T_LEVEL[codes[k]] - lbar);
 }
 
+/* Value i of a dense little-endian bit stream of `bits`-bit fields: bit j
+ * of the field is stream bit bits*i + j, stream bit k is bit k % 32 of word
+ * k / 32.  Taken one bit at a time, so that straddling a word needs no
+ * case of its own. */
 static unsigned get_bits(const uint32_t* w, size_t i, int bits) {
-    size_t per = 32 / (size_t)bits;
-    return (w[i / per] >> (bits * (int)(i % per))) & ((1u << bits) - 1u);
+    unsigned v = 0;
+    for (int j = 0; j < bits; ++j) {
+        size_t k = (size_t)bits * i + (size_t)j;
+        v |= ((w[k / 32] >> (k % 32)) & 1u) << j;
+    }
+    return v;
 }
 
 static void put_bits(uint32_t* w, size_t i, int bits, unsigned v) {
-    size_t per = 32 / (size_t)bits;
-    int sh = bits * (int)(i % per);
-    uint32_t mask = ((1u << bits) - 1u) << sh;
-    w[i / per] = (w[i / per] & ~mask) | ((uint32_t)v << sh);
+    for (int j = 0; j < bits; ++j) {
+        size_t k = (size_t)bits * i + (size_t)j;
+        uint32_t m = 1u << (k % 32);
+        w[k / 32] = ((v >> j) & 1u) ? (w[k / 32] | m) : (w[k / 32] & ~m);
+    }
+}
+
+/* The layouts the page's fused path takes: index widths 2, 3, 4, 6, 8;
+ * storage blocks a power of two from 32 to 1024; mean groups a power of two
+ * dividing the block. */
+int oracle_turbo_layout_ok(int bits, int block, int group) {
+    if (bits != 2 && bits != 3 && bits != 4 && bits != 6 && bits != 8) return 0;
+    if (block < 32 || block > T_MAX_BLOCK || (block & (block - 1))) return 0;
+    if (group < 1 || group > block || (group & (group - 1))) return 0;
+    return 1;
 }
 
 /* Persistent bytes of one tensor of n values (TurboAdam package page,
- * Persistent memory: UState 2 bits + one bf16 per 64 + 12 bytes per tensor;
- * 1Q bits per value + two fp16 per 128; an uncompressed moment is FP32). */
-size_t oracle_turbo_state_bytes(int compress_m, int compress_v, int bits, size_t n) {
+ * Persistent memory: UState 2 bits + one bf16 per group + 12 bytes per
+ * tensor; 1Q bits per value + two fp16 per block; an uncompressed moment is
+ * FP32), in 32-bit words for the packed streams.  0 for a layout outside
+ * oracle_turbo_layout_ok. */
+size_t oracle_turbo_state_bytes(int compress_m, int compress_v, int bits, int block, int group, size_t n) {
+    if (!oracle_turbo_layout_ok(bits, block, group)) return 0;
     size_t b = 0;
-    b += compress_m ? 4 * ((n + 15) / 16) + 2 * ((n + T_GROUP - 1) / T_GROUP) + 12 : 4 * n;
-    b += compress_v ? 4 * ((n * (size_t)bits + 31) / 32) + 4 * ((n + T_BLOCK - 1) / T_BLOCK) : 4 * n;
+    b += compress_m ? 4 * ((n + 15) / 16) + 2 * ((n + (size_t)group - 1) / (size_t)group) + 12 : 4 * n;
+    b += compress_v ? 4 * ((n * (size_t)bits + 31) / 32) + 4 * ((n + (size_t)block - 1) / (size_t)block) : 4 * n;
     return b;
 }
 
@@ -921,17 +953,21 @@ size_t oracle_turbo_state_bytes(int compress_m, int compress_v, int bits, size_t
  * s: the eight scalars of oracle_scalars for this step.  ts: bc1 = 1-beta1^t,
  * bc1_prev = 1-beta1^(t-1), bc2_prev = 1-beta2^(t-1), each rounded once to
  * binary32.  scal: the tensor's s_dec, s_enc, acc (used when compress_m).
+ * bits, block, group: the index width, the 1Q block and the UState group
+ * (a layout oracle_turbo_layout_ok accepts; the oracle stops otherwise).
  * Returns the number of values whose p', m' or v' is not finite. */
 unsigned long long oracle_turbo_step(float* p, const float* g, size_t n, uint32_t tensor_id,
-                                     int compress_m, int compress_v, int bits,
+                                     int compress_m, int compress_v, int bits, int block, int group,
                                      uint32_t* m_codes, uint16_t* m_means, float* m_fp32,
                                      uint32_t* v_index, uint16_t* v_ends, float* v_fp32,
                                      float* scal, const float s[8], const float ts[3],
                                      double factor, unsigned long long seed, long long step) {
     build_tables();
     const float bc1 = ts[0], bc1p = ts[1], bc2p = ts[2], bc2 = s[4], eps = s[7];
-    const size_t nb = (n + T_BLOCK - 1) / T_BLOCK;
-    const size_t ng = (n + T_GROUP - 1) / T_GROUP;
+    if (!oracle_turbo_layout_ok(bits, block, group)) abort();
+    const size_t B = (size_t)block, G = (size_t)group;
+    const size_t nb = (n + B - 1) / B;
+    const size_t ng = (n + G - 1) / G;
     size_t padded = 1;
     while (padded < n) padded *= 2;
     size_t nn = n ? n : 1;
@@ -957,20 +993,20 @@ unsigned long long oracle_turbo_step(float* p, const float* g, size_t n, uint32_
     /* 1. prior moments (the state is empty at step 1), the update, new FP32 moments */
     if (step > 1) {
         for (size_t b = 0; b < nb; ++b) {
-            size_t i0 = b * T_BLOCK, len = i0 + T_BLOCK < n ? T_BLOCK : n - i0;
+            size_t i0 = b * B, len = i0 + B < n ? B : n - i0;
             float lev[256];
             if (compress_v) oracle_q1_levels(v_ends[2 * b], v_ends[2 * b + 1], bits, lev);
             for (size_t i = i0; i < i0 + len; ++i)
                 vprev[i] = compress_v ? lev[get_bits(v_index, i, bits)] : v_fp32[i];
         }
         for (size_t gi = 0; gi < ng; ++gi) {
-            size_t i0 = gi * T_GROUP, len = i0 + T_GROUP < n ? T_GROUP : n - i0;
+            size_t i0 = gi * G, len = i0 + G < n ? G : n - i0;
             if (!compress_m) {
                 for (size_t i = i0; i < i0 + len; ++i) mprev[i] = m_fp32[i];
                 continue;
             }
-            uint8_t codes[T_GROUP];
-            float q[T_GROUP];
+            uint8_t codes[T_MAX_BLOCK];
+            float q[T_MAX_BLOCK];
             for (size_t k = 0; k < len; ++k) codes[k] = (uint8_t)get_bits(m_codes, i0 + k, 2);
             oracle_ustate_decode(codes, len, m_means[gi], s_dec, q);
             for (size_t k = 0; k < len; ++k) {
@@ -989,30 +1025,30 @@ unsigned long long oracle_turbo_step(float* p, const float* g, size_t n, uint32_
 
     /* 2. second moment: 1Q per block, or FP32 */
     for (size_t b = 0; b < nb; ++b) {
-        size_t i0 = b * T_BLOCK, len = i0 + T_BLOCK < n ? T_BLOCK : n - i0;
+        size_t i0 = b * B, len = i0 + B < n ? B : n - i0;
         if (!compress_v) {
             for (size_t i = i0; i < i0 + len; ++i) { v_fp32[i] = v1[i]; vp[i] = v1[i]; }
             continue;
         }
-        uint8_t idx[T_BLOCK];
+        uint8_t idx[T_MAX_BLOCK];
         oracle_q1_block(v1 + i0, len, bits, u1 + i0, idx, v_ends + 2 * b, vp + i0);
         for (size_t k = 0; k < len; ++k) put_bits(v_index, i0 + k, bits, idx[k]);
     }
 
-    /* 3. first moment: UState per 64-value group, or FP32 */
+    /* 3. first moment: UState per group of G values, or FP32 */
     for (size_t gi = 0; gi < ng; ++gi) {
-        size_t i0 = gi * T_GROUP, len = i0 + T_GROUP < n ? T_GROUP : n - i0;
+        size_t i0 = gi * G, len = i0 + G < n ? G : n - i0;
         if (!compress_m) {
             for (size_t i = i0; i < i0 + len; ++i) m_fp32[i] = m1[i];
             continue;
         }
-        float q[T_GROUP];
+        float q[T_MAX_BLOCK];
         for (size_t k = 0; k < len; ++k) {
             float den = sqrtf(vp[i0 + k] / bc2) + eps;
             q[k] = (m1[i0 + k] / bc1) / den;
         }
-        uint8_t codes[T_GROUP];
-        oracle_ustate_group(q, len, s_enc, up + i0 / 2, codes, m_means + gi, r2 + i0);
+        uint8_t codes[T_MAX_BLOCK];
+        oracle_ustate_group(q, len, G, s_enc, up + i0 / 2, codes, m_means + gi, r2 + i0);
         for (size_t k = 0; k < len; ++k) put_bits(m_codes, i0 + k, 2, codes[k]);
     }
 

@@ -115,10 +115,12 @@ def _f16_bits(x):
 
 def test_q1_endpoints_and_levels(oracle_mod):
     r = np.random.default_rng(4)
-    for bits in (2, 4, 8):
-        for _ in range(20):
-            v = (10.0 ** r.uniform(-14, 0, 128)).astype(np.float32)
-            idx, ends, dec = oracle.q1_block(v, bits, r.random(128).astype(np.float32))
+    for bits in (2, 3, 4, 6, 8):
+        for length in (128, 32, 1024):
+            if length != 128 and bits in (2, 4, 8):
+                continue
+            v = (10.0 ** r.uniform(-14, 0, length)).astype(np.float32)
+            idx, ends, dec = oracle.q1_block(v, bits, r.random(length).astype(np.float32))
             lo, hi = (float(np.array(ends[k:k + 1]).view(np.float16)[0]) for k in (0, 1))
             l2min, l2max = math.log2(float(v.min())), math.log2(float(v.max()))
             # lo is the largest binary16 at or below log2(min), hi the smallest at or above log2(max)
@@ -368,3 +370,154 @@ def test_q1_ends_batch_is_one_value_block(oracle_mod):
     for k, x in enumerate(v):
         _, ends, _ = oracle.q1_block(np.array([x], np.float32), 4, np.zeros(1, np.float32))
         assert (int(ends[0]), int(ends[1])) == (int(lo[k]), int(hi[k])), x
+
+
+# ------------------------------------------------------------- other layouts
+# The page's fused path takes power-of-two storage blocks from 32 to 1024
+# values, UState mean blocks that divide the storage block, and 2, 3, 4, 6
+# or 8 index bits (TurboAdam package page, "Fused CUDA path"; API
+# block_size, v_bits, m_block_size).
+
+
+def test_layouts_taken(oracle_mod):
+    for bits in range(0, 10):
+        for block in (0, 16, 32, 48, 64, 128, 256, 512, 1024, 2048):
+            for group in (0, 1, 2, 3, 4, 48, 64, 128, 1024, 2048):
+                want = (bits in (2, 3, 4, 6, 8) and block in (32, 64, 128, 256, 512, 1024)
+                        and group >= 1 and group & (group - 1) == 0 and block % group == 0)
+                assert oracle.turbo_layout_ok(bits, block, group) == want, (bits, block, group)
+                if not want:
+                    assert oracle.turbo_state_bytes(1, 1, bits, 4096, block, group) == 0
+
+
+def test_ledger_other_layouts(oracle_mod):
+    """Per value the page's tables give 2 code bits and 16 bits of mean per
+    group for UState, b index bits and 32 bits of endpoints per block for
+    1Q; per tensor 12 bytes of scales.  At the defaults this is the page's
+    6.500732 bits per value."""
+    n = FACTS["values"]
+    for bits in (2, 3, 4, 6, 8):
+        for block in (32, 128, 1024):
+            for group in (1, 16, 64, block):
+                if group > block:
+                    continue
+                total = oracle.turbo_state_bytes(1, 1, bits, n, block, group)
+                assert total * 8 == n * (2 + bits) + n * 16 // group + n * 32 // block + 96, (bits, block, group)
+    assert oracle.turbo_state_bytes(1, 1, 4, n, 128, 64) == FACTS["total_bytes"]
+
+
+def _unpack(words, bits, n):
+    """Field i of the dense little-endian bit stream held in `words`, read
+    with numpy's own little-endian bit order."""
+    b = np.unpackbits(np.ascontiguousarray(words, "<u4").view(np.uint8), bitorder="little")
+    return (b[: n * bits].reshape(n, bits).astype(np.int64) << np.arange(bits)).sum(1), b[n * bits:]
+
+
+def _f16v(code):
+    return float(np.array([code], np.uint16).view(np.float16)[0])
+
+
+@pytest.mark.parametrize("bits,block", [(3, 32), (3, 1024), (6, 128), (6, 512), (2, 64), (8, 256), (4, 32)])
+def test_dense_indices_and_block_endpoints(oracle_mod, bits, block):
+    """Step 1 from the empty state, 1Q only: the new second moment is the
+    FP32 oracle's.  Unpacked in numpy's little-endian bit order, every index
+    decodes, with its own block's endpoints, to one of the two levels around
+    that value (0 for a zero); each block's endpoints are the tightest
+    binary16 bounds of log2 over its positive values; the bits past the last
+    value are zero."""
+    r = np.random.default_rng(100 + bits * 7 + block)
+    n = 3 * block + 37
+    p = r.normal(0, 0.02, n).astype(np.float32)
+    g = (r.normal(0, 1, n) * 10.0 ** r.uniform(-5, -1, n)).astype(np.float32)
+    g[r.integers(0, n, 5)] = 0.0
+    st = oracle.TurboState(n, compress_m=False, compress_v=True, bits=bits, block=block, group=min(64, block))
+    sc = oracle.scalars(1e-3, 0.9, 0.999, 1e-8, 0.0, 1)
+    oracle.turbo_step(p.copy(), g, st, sc, oracle.turbo_scalars(0.9, 0.999, 1), 1)
+    m, v = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    oracle.step_fp32(p.copy(), g, m, v, sc)
+    idx, tail = _unpack(st.v_index, bits, n)
+    assert not tail.any()
+    L = 1 << bits
+    assert idx.min() >= 0 and idx.max() < L
+    for b in range((n + block - 1) // block):
+        sl = slice(b * block, min(n, (b + 1) * block))
+        vb = v[sl]
+        pos = vb[vb > 0]
+        lo16, hi16 = int(st.v_ends[2 * b]), int(st.v_ends[2 * b + 1])
+        lo, hi = _f16v(lo16), _f16v(hi16)
+        l2min, l2max = math.log2(float(pos.min())), math.log2(float(pos.max()))
+        assert lo <= l2min and float(np.nextafter(np.float16(lo), np.float16(np.inf))) > l2min
+        assert hi >= l2max and float(np.nextafter(np.float16(hi), np.float16(-np.inf))) < l2max
+        lev = oracle.q1_levels(lo16, hi16, bits)
+        for x, k in zip(vb, idx[sl]):
+            if x == 0:
+                assert k == 0
+            else:
+                assert k >= 1 and (lev[k] == x or (k > 1 and lev[k - 1] < x < lev[k])
+                                   or (k < L - 1 and lev[k] < x < lev[k + 1])), (x, k)
+
+
+@pytest.mark.parametrize("group", [1, 2, 8, 128, 1024])
+def test_group_means_and_scale_other_sizes(oracle_mod, group):
+    """Step 1, UState over groups of `group` values with 1Q off, so the
+    persisted second moment is v' itself.  q comes from the FP32 oracle's
+    moments through numpy's IEEE float32 operations.  Each stored mean is
+    torch's bfloat16 of the float32-rounded exact (fsum) group mean; the
+    next encode scale is 1.1 x the exact RMS of q minus its group's mean,
+    within one binary32 ulp."""
+    import torch
+    r = np.random.default_rng(200 + group)
+    n = 2 * 1024 + 300
+    p = r.normal(0, 0.02, n).astype(np.float32)
+    g = (r.normal(0, 1e-3, n) + 2e-4).astype(np.float32)
+    st = oracle.TurboState(n, compress_m=True, compress_v=False, bits=4, block=1024, group=group)
+    sc = oracle.scalars(1e-3, 0.9, 0.999, 1e-8, 0.0, 1)
+    oracle.turbo_step(p.copy(), g, st, sc, oracle.turbo_scalars(0.9, 0.999, 1), 1)
+    m, v = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    oracle.step_fp32(p.copy(), g, m, v, sc)
+    bc1 = oracle.turbo_scalars(0.9, 0.999, 1)[0]
+    q = ((m / bc1) / (np.sqrt(v / sc[4]) + sc[7])).astype(np.float32)
+    assert st.m_means.size == (n + group - 1) // group
+    r2 = []
+    for gi in range(st.m_means.size):
+        qs = q[gi * group:(gi + 1) * group]
+        exact = math.fsum(float(x) for x in qs) / qs.size
+        want = int(torch.tensor([float(np.float32(exact))]).to(torch.bfloat16).view(torch.int16).item()) & 0xFFFF
+        assert int(st.m_means[gi]) == want, gi
+        mean = np.float32((np.array([want], np.uint32) << 16).view(np.float32)[0])
+        r2.extend(((qs - mean).astype(np.float64) ** 2).tolist())
+    s_enc = np.float32(1.1 * math.sqrt(math.fsum(r2) / n))
+    assert abs(int(np.float32(st.scal[1]).view(np.int32)) - int(s_enc.view(np.int32))) <= 1
+
+
+@pytest.mark.parametrize("group", [1, 2, 16, 256, 1024])
+def test_ustate_recentering_other_group_sizes(oracle_mod, group):
+    """Decoding a group of any size keeps the stored mean: mean + s (level -
+    mean level) averages to the mean."""
+    r = np.random.default_rng(300 + group)
+    for _ in range(10):
+        n = int(r.integers(1, group + 1))
+        q = (r.normal(0, 1, n) * 10.0 ** r.uniform(-2, 1)).astype(np.float32)
+        s = np.float32(10.0 ** r.uniform(-2, 1))
+        codes, mean16, _ = oracle.ustate_group(q, s, r.random((n + 1) // 2).astype(np.float32), group)
+        mean = float((np.array([mean16], np.uint32) << 16).view(np.float32)[0])
+        dec = oracle.ustate_decode(codes, mean16, s)
+        assert abs(dec.astype(np.float64).mean() - mean) <= 4e-7 * (abs(mean) + 2 * s) + 1e-30
+
+
+def test_default_layout_is_the_original(oracle_mod):
+    """Block 128 and group 64 are the defaults: naming them changes nothing."""
+    r = np.random.default_rng(400)
+    n = 5003
+    p0 = r.normal(0, 0.02, n).astype(np.float32)
+    outs = []
+    for kw in ({}, dict(block=128, group=64)):
+        st = oracle.TurboState(n, **kw)
+        p = p0.copy()
+        for t in (1, 2, 3):
+            g = np.random.default_rng(t).normal(0, 1e-3, n).astype(np.float32)
+            oracle.turbo_step(p, g, st, oracle.scalars(1e-3, 0.9, 0.999, 1e-8, 0.01, t),
+                              oracle.turbo_scalars(0.9, 0.999, t), t)
+        outs.append((p.copy(), st.v_index.copy(), st.m_codes.copy(), st.m_means.copy(), st.scal.copy()))
+    for a, b in zip(*outs):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
