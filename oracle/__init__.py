@@ -106,7 +106,8 @@ def _load():
     lib.oracle_q1_ends_batch.restype = None
     lib.oracle_q1_block.argtypes = [_f32p, ctypes.c_size_t, ctypes.c_int, _f32p, _u8p, _u16p, _f32p]
     lib.oracle_q1_block.restype = None
-    lib.oracle_ustate_group.argtypes = [_f32p, ctypes.c_size_t, ctypes.c_size_t, ctypes.c_float, _f32p, _u8p, _u16p,
+    lib.oracle_ustate_group.argtypes = [_f32p, ctypes.c_size_t, ctypes.c_size_t, ctypes.c_size_t, ctypes.c_float, _f32p,
+                                        _u8p, _u16p,
                                         ctypes.POINTER(ctypes.c_double)]
     lib.oracle_ustate_group.restype = None
     lib.oracle_ustate_decode.argtypes = [_u8p, ctypes.c_size_t, ctypes.c_uint16, ctypes.c_float, _f32p]
@@ -393,16 +394,18 @@ def q1_block(v, bits, u):
     return idx, ends, dec
 
 
-def ustate_group(q, s_enc, u_pair, group=64):
+def ustate_group(q, s_enc, u_pair, group=64, first=0):
     """UState encode of one group (<= group values, group a power of two up
-    to 1024): (codes, bf16 mean bits, squared residuals)."""
+    to 1024) whose first value has index `first` in its tensor: (codes, bf16
+    mean bits, squared residuals)."""
     q = np.ascontiguousarray(q, np.float32)
     u_pair = np.ascontiguousarray(u_pair, np.float32)
     assert q.size <= group <= 1024 and group & (group - 1) == 0 and u_pair.size >= (q.size + 1) // 2
     codes = np.zeros(q.size, np.uint8)
     mean = np.zeros(1, np.uint16)
     r2 = np.zeros(q.size, np.float64)
-    _load().oracle_ustate_group(_ptr(q, _f32p), q.size, int(group), float(np.float32(s_enc)), _ptr(u_pair, _f32p),
+    _load().oracle_ustate_group(_ptr(q, _f32p), q.size, int(group), int(first), float(np.float32(s_enc)),
+                                _ptr(u_pair, _f32p),
                                 _ptr(codes, _u8p), _ptr(mean, _u16p), r2.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
     return codes, int(mean[0]), r2
 

@@ -867,12 +867,15 @@ void oracle_q1_block(const float* v, size_t len, int bits, const float* u, uint8
 static const float T_LEVEL[4] = {-1.5f, -0.5f, 0.5f, 1.5f};
 
 /* UState encode of one group of len (<= group) values q, group a power of
- * two up to 1024, with encode scale s_enc and one draw per pair (u_pair[j]
- * for values 2j and 2j+1, the second using 1 - u): the bf16 mean (the
- * pairwise tree over the group's values padded with zeros to `group`,
- * divided by len), each code, and each residual's square (double). */
-void oracle_ustate_group(const float* q, size_t len, size_t group, float s_enc, const float* u_pair, uint8_t* codes,
-                         uint16_t* mean16, double* r2) {
+ * two up to 1024, whose first value has index `first` in its tensor, with
+ * encode scale s_enc and one draw per pair of the tensor's values 2j and
+ * 2j+1 (the second using 1 - u; u_pair[0] is the draw of the pair holding
+ * the group's first value, so a one-value group at an odd index takes
+ * 1 - u): the bf16 mean (the pairwise tree over the group's values padded
+ * with zeros to `group`, divided by len), each code, and each residual's
+ * square (double). */
+void oracle_ustate_group(const float* q, size_t len, size_t group, size_t first, float s_enc, const float* u_pair,
+                         uint8_t* codes, uint16_t* mean16, double* r2) {
     build_tables();
     double qd[T_MAX_BLOCK];
     for (size_t k = 0; k < group; ++k) qd[k] = k < len ? (double)q[k] : 0.0;
@@ -885,8 +888,8 @@ void oracle_ustate_group(const float* q, size_t len, size_t group, float s_enc, 
         float x = s_enc > 0.0f ? r / s_enc : 0.0f;
         if (x > 1.5f) x = 1.5f;
         if (x < -1.5f) x = -1.5f;
-        float u = u_pair[i / 2];
-        if (i % 2) u = 1.0f - u;
+        float u = u_pair[(first + i) / 2 - first / 2];
+        if ((first + i) % 2) u = 1.0f - u;
         unsigned k = (x >= -0.5f) + (x >= 0.5f);
         unsigned code = k;
         if (x >= 1.5f) code = 3;
@@ -1048,7 +1051,7 @@ unsigned long long oracle_turbo_step(float* p, const float* g, size_t n, uint32_
             q[k] = (m1[i0 + k] / bc1) / den;
         }
         uint8_t codes[T_MAX_BLOCK];
-        oracle_ustate_group(q, len, G, s_enc, up + i0 / 2, codes, m_means + gi, r2 + i0);
+        oracle_ustate_group(q, len, G, i0, s_enc, up + i0 / 2, codes, m_means + gi, r2 + i0);
         for (size_t k = 0; k < len; ++k) put_bits(m_codes, i0 + k, 2, codes[k]);
     }
 

@@ -521,3 +521,18 @@ def test_default_layout_is_the_original(oracle_mod):
         outs.append((p.copy(), st.v_index.copy(), st.m_codes.copy(), st.m_means.copy(), st.scal.copy()))
     for a, b in zip(*outs):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_antithetic_pairs_follow_the_tensor_index(oracle_mod):
+    """The pairs are the tensor's values 2j and 2j+1 whatever the group size:
+    a one-value group at an odd index takes 1 - u.  With s = 1 a value whose
+    residual is almost 0 sits half-way from level -0.5 to level 0.5, so
+    u = 0.3 rounds it up and 1 - u = 0.7 does not."""
+    q = np.array([0.3], np.float32)             # bf16(0.3) differs from 0.3 by < 2^-9
+    u = np.array([0.3], np.float32)
+    up, _, _ = oracle.ustate_group(q, 1.0, u, group=1, first=4)
+    down, _, _ = oracle.ustate_group(q, 1.0, u, group=1, first=5)
+    assert (int(up[0]), int(down[0])) == (2, 1)
+    # in a two-value group the second value is the odd one of the pair
+    both, _, _ = oracle.ustate_group(np.array([0.3, 0.3], np.float32), 1.0, u, group=2, first=4)
+    assert both.tolist() == [2, 1]
