@@ -71,7 +71,8 @@ class TurboStateDesc(ctypes.Structure):
 
 
 class TurboConfig(ctypes.Structure):
-    _fields_ = [("v_bits", ctypes.c_int), ("m_step_factor", ctypes.c_double), ("seed", ctypes.c_ulonglong)]
+    _fields_ = [("v_bits", ctypes.c_int), ("m_step_factor", ctypes.c_double), ("seed", ctypes.c_ulonglong),
+                ("block_size", ctypes.c_int), ("m_block_size", ctypes.c_int), ("path", ctypes.c_int)]
 
 
 class Format(ctypes.Structure):
@@ -88,7 +89,7 @@ class Format(ctypes.Structure):
 
 EXPORTS = ("pa_step", "pa_step_list", "pa_step_typed", "pa_step_list_typed", "pa_state_bytes",
            "pa_format_info", "pa_status_string", "pa_last_hip_error", "pa_release_plans", "pa_debug_codec",
-           "pa_debug_sqrt", "pa_debug_scalars", "pa_debug_q1_ends", "pa_debug_q1_levels", "pa_debug_pow2_rn32", "pa_grad_stats_list", "pa_turbo_state_bytes", "pa_turbo_workspace_bytes",
+           "pa_debug_sqrt", "pa_debug_scalars", "pa_debug_q1_ends", "pa_debug_q1_levels", "pa_debug_pow2_rn32", "pa_grad_stats_list", "pa_turbo_state_bytes", "pa_turbo_layout_bytes", "pa_turbo_workspace_bytes",
            "pa_turbo_step_list", "pa_step_list_noalloc")
 
 PA_DT_F32, PA_DT_BF16, PA_DT_F16 = 0, 1, 2
@@ -146,6 +147,8 @@ def lib():
     L.pa_grad_stats_list.restype = ctypes.c_int
     L.pa_turbo_state_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, sz]
     L.pa_turbo_state_bytes.restype = sz
+    L.pa_turbo_layout_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, sz]
+    L.pa_turbo_layout_bytes.restype = sz
     L.pa_turbo_workspace_bytes.argtypes = [sz, ctypes.POINTER(TurboStateDesc), ctypes.POINTER(sz)]
     L.pa_turbo_workspace_bytes.restype = sz
     L.pa_turbo_step_list.argtypes = [sz, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(TurboStateDesc),
@@ -482,19 +485,26 @@ def pa_debug_pow2_rn32(x, exact, out, stream=None):
 class TurboState:
     """Device buffers of one tensor's TurboAdam state, zero-filled (the empty
     state): UState (compress_m) or an FP32 first moment, 1Q (compress_v) or
-    an FP32 second moment (sizes as in include/pa.h)."""
+    an FP32 second moment (sizes as in include/pa.h).  block_size: values
+    per 1Q endpoint pair; m_block_size: values per UState mean."""
 
-    def __init__(self, n, device, compress_m=True, compress_v=True, v_bits=4, tensor_id=0):
+    def __init__(self, n, device, compress_m=True, compress_v=True, v_bits=4, tensor_id=0, block_size=128,
+                 m_block_size=64):
         import torch
+        if not turbo_layout_ok(v_bits, block_size, m_block_size):
+            raise ValueError(f"TurboAdam layout not taken: v_bits={v_bits}, block_size={block_size}, "
+                             f"m_block_size={m_block_size}")
         z = lambda k, dt: torch.zeros(k, dtype=dt, device=device)
         self.n, self.compress_m, self.compress_v, self.v_bits = int(n), bool(compress_m), bool(compress_v), v_bits
+        self.block_size, self.m_block_size = int(block_size), int(m_block_size)
         self.tensor_id = int(tensor_id)
+        B, G = self.block_size, self.m_block_size
         self.m_codes = z(4 * ((n + 15) // 16), torch.uint8) if compress_m else None
-        self.m_means = z((n + 63) // 64, torch.int16) if compress_m else None
+        self.m_means = z((n + G - 1) // G, torch.int16) if compress_m else None
         self.scalars = z(3, torch.float32) if compress_m else None
         self.m_fp32 = None if compress_m else z(n, torch.float32)
         self.v_index = z(4 * ((n * v_bits + 31) // 32), torch.uint8) if compress_v else None
-        self.v_ends = z(2 * ((n + 127) // 128), torch.int16) if compress_v else None
+        self.v_ends = z(2 * ((n + B - 1) // B), torch.int16) if compress_v else None
         self.v_fp32 = None if compress_v else z(n, torch.float32)
 
     def desc(self):
@@ -514,12 +524,26 @@ def pa_turbo_state_bytes(compress_m, compress_v, v_bits, n):
     return int(lib().pa_turbo_state_bytes(int(compress_m), int(compress_v), int(v_bits), int(n)))
 
 
+def pa_turbo_layout_bytes(compress_m, compress_v, v_bits, block_size, m_block_size, n):
+    return int(lib().pa_turbo_layout_bytes(int(compress_m), int(compress_v), int(v_bits), int(block_size),
+                                           int(m_block_size), int(n)))
+
+
+def turbo_layout_ok(v_bits, block_size, m_block_size):
+    """The layouts of the TurboAdam fused path: 2, 3, 4, 6 or 8 index bits, a
+    power-of-two block from 32 to 1024 values, a power-of-two mean group
+    dividing it (the library refuses any other with PA_ERR_ARG)."""
+    b, B, G = int(v_bits), int(block_size), int(m_block_size)
+    return (b in (2, 3, 4, 6, 8) and 32 <= B <= 1024 and B & (B - 1) == 0 and 1 <= G <= B and G & (G - 1) == 0)
+
+
 class TurboList:
     """A fixed list of FP32 parameters, gradients and TurboState objects,
     validated and marshalled once; ``step(hyper, t)`` is one
     pa_turbo_step_list call.  Owns its device workspace."""
 
-    def __init__(self, params, grads, states, v_bits=4, m_step_factor=1.1, seed=0x12345678):
+    def __init__(self, params, grads, states, v_bits=4, m_step_factor=1.1, seed=0x12345678, block_size=128,
+                 m_block_size=64, general=False):
         import torch
         k = len(params)
         if len(grads) != k or len(states) != k:
@@ -537,11 +561,14 @@ class TurboList:
                 raise TypeError("the TurboAdam step takes float32 parameters and gradients")
             if g.numel() != p.numel() or st.n != p.numel() or st.v_bits != v_bits:
                 raise ValueError("params, grads and states disagree in size or v_bits")
+            if (st.block_size, st.m_block_size) != (block_size, m_block_size):
+                raise ValueError("states disagree with the list's block_size or m_block_size")
             self._P[i], self._G[i] = _ptr(p), _ptr(g)
             self._S[i] = st.desc()
             self._N[i] = p.numel()
         self.count = k
-        self.config = TurboConfig(int(v_bits), float(m_step_factor), int(seed))
+        self.config = TurboConfig(int(v_bits), float(m_step_factor), int(seed), int(block_size), int(m_block_size),
+                                  1 if general else 0)
         L = lib()
         wsb = int(L.pa_turbo_workspace_bytes(k, self._S, self._N)) if k else 0
         dev = params[0].device if k else "cuda:0"

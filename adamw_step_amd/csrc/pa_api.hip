@@ -592,7 +592,10 @@ struct TurboPlan {
   std::vector<uintptr_t> key;
   pa::TurboEntry* table = nullptr;          // device: entries + sentinel, then the reduce list
   pa::TurboReduceEntry* reduce = nullptr;   // inside the same allocation
-  long long tiles = 0;
+  long long tiles = 0;                      // 256-value tiles, or 1024-value ones on the general path
+  int count = 0;                            // entries before the sentinel
+  bool general = false;                     // turbo_general instead of turbo_list
+  int blog = 7, glog = 6;                   // log2 of the 1Q block and of the UState group
   int nreduce = 0;
   long long nchunks = 0;                    // chunks of tile sums over all UState tensors
   size_t ws_bytes = 0;
@@ -615,7 +618,31 @@ void free_turbo_plan(TurboPlan& pl) {
 long long turbo_tiles(size_t n) { return (long long)((n + pa::kTurboTile - 1) / pa::kTurboTile); }
 long long turbo_chunks_of(long long tiles) { return (tiles + pa::kTurboChunk - 1) / pa::kTurboChunk; }
 
-bool valid_bits(int b) { return b == 2 || b == 4 || b == 8; }
+// A layout the page's fused path takes: 2, 3, 4, 6 or 8 index bits, a
+// power-of-two 1Q block from 32 to 1024 values, a power-of-two UState group
+// dividing it.  The tuned kernel (turbo_list) covers 128-value blocks,
+// 64-value groups and 2, 4 or 8 bits; turbo_general covers all of them.
+struct TurboLayout {
+  int bits = 4, block = 128, group = 64;
+  bool general = false;
+};
+
+int log2_exact(int x) { return 31 - __builtin_clz((unsigned)x); }
+
+bool layout_ok(int bits, int block, int group) {
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 6 && bits != 8) return false;
+  if (block < 32 || block > 1024 || (block & (block - 1))) return false;
+  return group >= 1 && group <= block && (group & (group - 1)) == 0;
+}
+
+int turbo_layout(const pa_turbo_config* c, TurboLayout* out) {
+  out->bits = c->v_bits;
+  out->block = c->block_size ? c->block_size : 128;
+  out->group = c->m_block_size ? c->m_block_size : 64;
+  if (!layout_ok(out->bits, out->block, out->group) || (c->path != 0 && c->path != 1)) return PA_ERR_ARG;
+  out->general = c->path == 1 || out->block != 128 || out->group != 64 || out->bits == 3 || out->bits == 6;
+  return PA_OK;
+}
 
 // Checks one tensor's buffers; appends the written ranges to `w` and the
 // gradient range to `r`.
@@ -623,8 +650,9 @@ bool valid_bits(int b) { return b == 2 || b == 4 || b == 8; }
 constexpr size_t kTurboMaxValues = size_t(1) << 34;
 constexpr long long kTurboMaxStep = 0xFFFFFFFFll;
 
-int check_turbo_tensor(const float* p, const float* g, const pa_turbo_state& st, size_t n, int bits,
+int check_turbo_tensor(const float* p, const float* g, const pa_turbo_state& st, size_t n, const TurboLayout& lay,
                        std::vector<Range>* w, std::vector<Range>* r) {
+  const size_t bits = (size_t)lay.bits, B = (size_t)lay.block, G = (size_t)lay.group;
   if (n == 0) return PA_OK;
   if (p == nullptr || g == nullptr) return PA_ERR_ARG;
   if (!aligned(p, 16) || !aligned(g, 16)) return PA_ERR_ALIGN;
@@ -634,7 +662,7 @@ int check_turbo_tensor(const float* p, const float* g, const pa_turbo_state& st,
     if (!st.m_codes || !st.m_means || !st.scalars) return PA_ERR_ARG;
     if (!aligned(st.m_codes, 4) || !aligned(st.m_means, 2) || !aligned(st.scalars, 4)) return PA_ERR_ALIGN;
     w->push_back(range_of(st.m_codes, 4 * ((n + 15) / 16)));
-    w->push_back(range_of(st.m_means, 2 * ((n + 63) / 64)));
+    w->push_back(range_of(st.m_means, 2 * ((n + G - 1) / G)));
     w->push_back(range_of(st.scalars, 12));
   } else {
     if (!st.m_fp32) return PA_ERR_ARG;
@@ -644,14 +672,30 @@ int check_turbo_tensor(const float* p, const float* g, const pa_turbo_state& st,
   if (st.compress_v) {
     if (!st.v_index || !st.v_ends) return PA_ERR_ARG;
     if (!aligned(st.v_index, 4) || !aligned(st.v_ends, 4)) return PA_ERR_ALIGN;
-    w->push_back(range_of(st.v_index, 4 * ((n * (size_t)bits + 31) / 32)));
-    w->push_back(range_of(st.v_ends, 4 * ((n + 127) / 128)));
+    w->push_back(range_of(st.v_index, 4 * ((n * bits + 31) / 32)));
+    w->push_back(range_of(st.v_ends, 4 * ((n + B - 1) / B)));
   } else {
     if (!st.v_fp32) return PA_ERR_ARG;
     if (!aligned(st.v_fp32, 16)) return PA_ERR_ALIGN;
     w->push_back(range_of(st.v_fp32, n * 4));
   }
   return PA_OK;
+}
+
+// The residual sums' chunk pass and the per-tensor completion with the
+// scale rotation, after either step kernel.
+hipError_t launch_turbo_reduce(const TurboPlan& pl, const pa::Scalars& s, double* ws, double factor,
+                               hipStream_t st) {
+  if (pl.nreduce == 0) return hipSuccess;
+  hipLaunchKernelGGL(pa::turbo_chunks, dim3((unsigned)pl.nchunks), dim3(pa::kThreads), 0, st, pl.reduce,
+                     pl.nreduce, ws);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // The reduce kernel checks the same skip flag: a skipped update leaves
+  // the scales as they were.
+  hipLaunchKernelGGL(pa::turbo_reduce, dim3((unsigned)pl.nreduce), dim3(pa::kThreads), 0, st, pl.reduce, ws, factor,
+                     s.skip);
+  return hipGetLastError();
 }
 
 template <int BITS>
@@ -665,16 +709,27 @@ hipError_t launch_turbo(const TurboPlan& pl, const pa::Scalars& s, const pa::Tur
   else
     hipLaunchKernelGGL((pa::turbo_list<BITS, false>), grid, block, 0, st, pl.table, pl.tiles, s, ts, ws, nf);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || pl.nreduce == 0) return e;
-  hipLaunchKernelGGL(pa::turbo_chunks, dim3((unsigned)pl.nchunks), dim3(pa::kThreads), 0, st, pl.reduce,
-                     pl.nreduce, ws);
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // The reduce kernel checks the same skip flag: a skipped update leaves
-  // the scales as they were.
-  hipLaunchKernelGGL(pa::turbo_reduce, dim3((unsigned)pl.nreduce), dim3(pa::kThreads), 0, st, pl.reduce, ws, factor,
-                     s.skip);
-  return hipGetLastError();
+  return launch_turbo_reduce(pl, s, ws, factor, st);
+}
+
+// The general kernel: one workgroup per 1024-value tile, in launches of at
+// most kMaxLaunchTiles workgroups.
+template <int BITS>
+hipError_t launch_general(const TurboPlan& pl, const pa::Scalars& s, const pa::TurboScalars& ts, double* ws,
+                          unsigned long long* nf, double factor, hipStream_t st) {
+  for (long long t0 = 0; t0 < pl.tiles; t0 += kMaxLaunchTiles) {
+    const long long nt = std::min(kMaxLaunchTiles, pl.tiles - t0);
+    if (nf)
+      hipLaunchKernelGGL((pa::turbo_general<BITS, true>), dim3((unsigned)nt), dim3(pa::kThreads), 0, st, pl.table,
+                         pl.count, t0, s, ts, pl.blog, pl.glog, ws, nf);
+    else
+      hipLaunchKernelGGL((pa::turbo_general<BITS, false>), dim3((unsigned)nt), dim3(pa::kThreads), 0, st, pl.table,
+                         pl.count, t0, s, ts, pl.blog, pl.glog, ws, nf);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_turbo_reduce(pl, s, ws, factor, st);
 }
 
 }  // namespace
@@ -1000,12 +1055,17 @@ int pa_grad_stats_list(int grad_dtype, size_t count, const void* const* grads, c
   return e == hipSuccess ? PA_OK : hip_failed(e);
 }
 
-size_t pa_turbo_state_bytes(int compress_m, int compress_v, int v_bits, size_t n) {
-  if (!valid_bits(v_bits)) return 0;
+size_t pa_turbo_layout_bytes(int compress_m, int compress_v, int v_bits, int block_size, int m_block_size, size_t n) {
+  if (!layout_ok(v_bits, block_size, m_block_size)) return 0;
+  const size_t B = (size_t)block_size, G = (size_t)m_block_size;
   size_t b = 0;
-  b += compress_m ? 4 * ((n + 15) / 16) + 2 * ((n + 63) / 64) + 12 : 4 * n;
-  b += compress_v ? 4 * ((n * (size_t)v_bits + 31) / 32) + 4 * ((n + 127) / 128) : 4 * n;
+  b += compress_m ? 4 * ((n + 15) / 16) + 2 * ((n + G - 1) / G) + 12 : 4 * n;
+  b += compress_v ? 4 * ((n * (size_t)v_bits + 31) / 32) + 4 * ((n + B - 1) / B) : 4 * n;
   return b;
+}
+
+size_t pa_turbo_state_bytes(int compress_m, int compress_v, int v_bits, size_t n) {
+  return pa_turbo_layout_bytes(compress_m, compress_v, v_bits, 128, 64, n);
 }
 
 size_t pa_turbo_workspace_bytes(size_t count, const pa_turbo_state* states, const size_t* n) {
@@ -1022,9 +1082,10 @@ size_t pa_turbo_workspace_bytes(size_t count, const pa_turbo_state* states, cons
 int pa_turbo_step_list(size_t count, float* const* params, const float* const* grads, const pa_turbo_state* states,
                        const size_t* n, const pa_hyper* hyper, const pa_turbo_config* config, long long step,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  if (config == nullptr || !valid_bits(config->v_bits) || !std::isfinite(config->m_step_factor) ||
-      !(config->m_step_factor > 0.0))
+  if (config == nullptr || !std::isfinite(config->m_step_factor) || !(config->m_step_factor > 0.0))
     return PA_ERR_ARG;
+  TurboLayout lay;
+  if (turbo_layout(config, &lay)) return PA_ERR_ARG;
   if (step > kTurboMaxStep) return PA_ERR_ARG;
   pa::Scalars s;
   int rc = make_scalars(hyper, step, &s);
@@ -1045,8 +1106,11 @@ int pa_turbo_step_list(size_t count, float* const* params, const float* const* g
   if (rc) return rc;
 
   std::vector<uintptr_t> key;
-  key.reserve(count * 13 + 1);
-  key.push_back((uintptr_t)config->v_bits);
+  key.reserve(count * 13 + 5);
+  key.push_back((uintptr_t)lay.bits);
+  key.push_back((uintptr_t)lay.block);
+  key.push_back((uintptr_t)lay.group);
+  key.push_back((uintptr_t)lay.general);
   key.push_back((uintptr_t)config->seed);
   for (size_t i = 0; i < count; ++i) {
     const pa_turbo_state& t = states[i];
@@ -1068,7 +1132,7 @@ int pa_turbo_step_list(size_t count, float* const* params, const float* const* g
     long long tiles = 0, ws_slots = 0;
     for (size_t i = 0; i < count; ++i) {
       const pa_turbo_state& t = states[i];
-      rc = check_turbo_tensor(params[i], grads[i], t, n[i], config->v_bits, &written, &read);
+      rc = check_turbo_tensor(params[i], grads[i], t, n[i], lay, &written, &read);
       if (rc) return rc;
       if (n[i] == 0) continue;
       pa::TurboEntry e;
@@ -1083,8 +1147,8 @@ int pa_turbo_step_list(size_t count, float* const* params, const float* const* g
       e.v_fp32 = t.compress_v ? nullptr : t.v_fp32;
       e.scal = t.compress_m ? t.scalars : nullptr;
       e.n = (long long)n[i];
-      e.tile0 = tiles;
-      e.ws0 = t.compress_m ? ws_slots : 0;
+      e.tile0 = tiles;                        // in units of the chosen kernel's tile
+      e.ws0 = t.compress_m ? ws_slots : 0;    // in 256-value partial sums either way
       e.tensor_id = t.tensor_id;
       e.seed = config->seed;
       e.flags = (t.compress_m ? 1 : 0) | (t.compress_v ? 2 : 0);
@@ -1094,7 +1158,7 @@ int pa_turbo_step_list(size_t count, float* const* params, const float* const* g
         red.push_back(r);
         ws_slots += nt;
       }
-      tiles += nt;
+      tiles += lay.general ? (long long)((n[i] + pa::kGenTile - 1) / pa::kGenTile) : nt;
       host.push_back(e);
     }
     {
@@ -1119,6 +1183,10 @@ int pa_turbo_step_list(size_t count, float* const* params, const float* const* g
     pl.device = dev;
     pl.key = key;
     pl.tiles = tiles;
+    pl.count = (int)host.size() - 1;
+    pl.general = lay.general;
+    pl.blog = log2_exact(lay.block);
+    pl.glog = log2_exact(lay.group);
     pl.nreduce = (int)red.size();
     pl.nchunks = chunk_slots;
     pl.ws_bytes = 8 * (size_t)(ws_slots + chunk_slots);
@@ -1171,10 +1239,22 @@ int pa_turbo_step_list(size_t count, float* const* params, const float* const* g
   ts.step = step;
   hipError_t e;
   double* ws = static_cast<double*>(workspace);
-  switch (config->v_bits) {
-    case 2: e = launch_turbo<2>(*it, s, ts, ws, hyper->nonfinite, config->m_step_factor, st, d); break;
-    case 4: e = launch_turbo<4>(*it, s, ts, ws, hyper->nonfinite, config->m_step_factor, st, d); break;
-    default: e = launch_turbo<8>(*it, s, ts, ws, hyper->nonfinite, config->m_step_factor, st, d); break;
+  const double f = config->m_step_factor;
+  unsigned long long* nf = hyper->nonfinite;
+  if (it->general) {
+    switch (lay.bits) {
+      case 2: e = launch_general<2>(*it, s, ts, ws, nf, f, st); break;
+      case 3: e = launch_general<3>(*it, s, ts, ws, nf, f, st); break;
+      case 4: e = launch_general<4>(*it, s, ts, ws, nf, f, st); break;
+      case 6: e = launch_general<6>(*it, s, ts, ws, nf, f, st); break;
+      default: e = launch_general<8>(*it, s, ts, ws, nf, f, st); break;
+    }
+  } else {
+    switch (lay.bits) {
+      case 2: e = launch_turbo<2>(*it, s, ts, ws, nf, f, st, d); break;
+      case 4: e = launch_turbo<4>(*it, s, ts, ws, nf, f, st, d); break;
+      default: e = launch_turbo<8>(*it, s, ts, ws, nf, f, st, d); break;
+    }
   }
   return e == hipSuccess ? PA_OK : hip_failed(e);
 }

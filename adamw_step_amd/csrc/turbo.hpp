@@ -685,6 +685,327 @@ turbo_list(const TurboEntry* __restrict__ table, long long total_tiles, Scalars 
   if constexpr (COUNT) flush_count(bad, nonfinite);
 }
 
+// ---------------------------------------------------------------------------
+// The general step: every layout of the page's fused path (1Q blocks of 32
+// to 1024 values, UState groups of a power of two dividing the block, 2, 3,
+// 4, 6 or 8 index bits), with the arithmetic and draws of turbo_tile.  One
+// 256-thread workgroup per 1024-value tile of one tensor, so a tile holds
+// whole blocks and whole groups; thread t holds values 4t..4t+3 of its
+// tile.  Levels are computed per value (the same exact power as the table
+// builders) instead of from per-block tables, whose size would grow with
+// the number of levels over small blocks.  Reductions over a block or a
+// group are xor butterflies over its lanes; segments wider than a
+// wavefront finish through LDS as further levels of the same tree.  The
+// residual partial sums go to turbo_list's workspace slots (one per 256
+// values), so turbo_chunks and turbo_reduce complete them unchanged.
+constexpr int kGenTile = 1024;
+
+// x reduced over aligned segments of `seg` lanes of the workgroup (a power
+// of two from 1 to 256), every lane receiving its segment's result.  Every
+// thread must call it (segments above 64 lanes synchronise the workgroup);
+// slot is four LDS entries.
+template <class T, class Op>
+__device__ __forceinline__ T seg_reduce(T x, int seg, Op op, T* slot) {
+  const int inwave = seg < 64 ? seg : 64;
+  for (int off = 1; off < inwave; off <<= 1) x = op(x, __shfl_xor(x, off, 64));
+  if (seg > 64) {
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) slot[wave] = x;
+    __syncthreads();
+    const int first = wave & ~(seg / 64 - 1);
+    x = seg == 128 ? op(slot[first], slot[first + 1])
+                   : op(op(slot[first], slot[first + 1]), op(slot[first + 2], slot[first + 3]));
+    __syncthreads();   // the slots are reused by the next call
+  }
+  return x;
+}
+
+// Level k >= 1 of a block whose endpoints decode to lo and hi.
+__device__ __forceinline__ float q1_level(double lo, double hi, int k, int L) {
+  const double x = q1_level_x(lo, hi, k, L);
+  float a;
+  if (!q1_level_fast(x, &a)) a = pow2_rn32_slow(x);
+  return a;
+}
+
+template <int BITS, bool COUNT>
+__global__ void __launch_bounds__(kThreads)
+turbo_general(const TurboEntry* __restrict__ table, int count, long long tile_base, Scalars s, TurboScalars ts,
+              int blog, int glog, double* ws, unsigned long long* nonfinite) {
+  constexpr int L = 1 << BITS;
+  constexpr int kWords = kGenTile * BITS / 32;       // index words of a tile
+  __shared__ uint32_t words[kWords];
+  __shared__ float fslot[4];
+  __shared__ double dslot[4];
+  __shared__ int islot[4];
+  if (!resolve_inputs(s)) return;   // uniform: before any barrier
+  const long long tile = tile_base + blockIdx.x;
+  int lo_t = 0, hi_t = count - 1;                    // the last entry with tile0 <= tile
+  while (lo_t < hi_t) {
+    const int mid = (lo_t + hi_t + 1) >> 1;
+    if (table[mid].tile0 <= tile) lo_t = mid;
+    else hi_t = mid - 1;
+  }
+  const TurboEntry& e = table[lo_t];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const long long local = tile - e.tile0;
+  const long long i0 = local * kGenTile + 4 * tid;  // this thread's first value
+  const long long n = e.n;
+  const bool cm = e.flags & 1, cv = e.flags & 2;
+  const int B = 1 << blog, G = 1 << glog;
+  bool valid[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) valid[k] = i0 + k < n;
+  const bool full = valid[3];
+  uint32_t bad = 0;
+  for (int j = tid; j < kWords; j += kThreads) words[j] = 0u;
+
+  // ---- loads
+  float p[4], g[4], mprev[4] = {0.f, 0.f, 0.f, 0.f}, vprev[4] = {0.f, 0.f, 0.f, 0.f};
+  if (full) {
+    const f32x4 pv = stream_load(reinterpret_cast<const f32x4*>(e.p + i0));
+    const f32x4 gv = stream_load(reinterpret_cast<const f32x4*>(e.g + i0));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      p[k] = pv[k];
+      g[k] = gv[k];
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      p[k] = valid[k] ? e.p[i0 + k] : 0.0f;
+      g[k] = valid[k] ? e.g[i0 + k] : 0.0f;
+    }
+  }
+  const long long blk = i0 >> blog;                  // 1Q block of this thread's values
+  const float s_dec = cm ? e.scal[0] : 0.0f, s_enc = cm ? e.scal[1] : 0.0f;
+
+  // ---- decode the prior moments (the state is empty at step 1)
+  if (ts.step > 1) {
+    if (cv) {
+      uint32_t field = 0, ends = 0;
+      if (valid[0]) {
+        // this thread's 4*BITS-bit field of the dense stream, read from the
+        // words it touches (the second only when its own values reach it)
+        const uint32_t* w32 = reinterpret_cast<const uint32_t*>(e.v_index);
+        const long long bit0 = i0 * BITS, bit_end = (valid[3] ? i0 + 4 : n) * BITS;
+        const long long w0 = bit0 >> 5;
+        const int sh = (int)(bit0 & 31);
+        unsigned long long both = w32[w0];
+        if (bit_end > (w0 + 1) * 32) both |= (unsigned long long)w32[w0 + 1] << 32;
+        field = (uint32_t)(both >> sh);
+        ends = reinterpret_cast<const uint32_t*>(e.v_ends)[blk];
+      }
+      const double lo = f16_to_double(ends & 0xFFFFu), hi = f16_to_double(ends >> 16);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int ix = (int)((field >> (BITS * k)) & (uint32_t)(L - 1));
+        vprev[k] = (valid[k] && ix > 0) ? q1_level(lo, hi, ix, L) : 0.0f;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) vprev[k] = valid[k] ? e.v_fp32[i0 + k] : 0.0f;
+    }
+  }
+  // The group mean level, summed as integers (2 x level), is exact in any
+  // order; every thread takes part in the reduction (it may synchronise).
+  uint32_t mcodes = 0;
+  if (cm && ts.step > 1 && valid[0]) mcodes = e.m_codes[i0 >> 2];
+  int s2[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) s2[k] = valid[k] ? (int)(2 * ((mcodes >> (2 * k)) & 3u)) - 3 : 0;
+  if (G >= 4) {
+    const int t = seg_reduce(s2[0] + s2[1] + s2[2] + s2[3], G / 4, [](int a, int b) { return a + b; }, islot);
+    s2[0] = s2[1] = s2[2] = s2[3] = t;
+  } else if (G == 2) {
+    s2[0] = s2[1] = s2[0] + s2[1];
+    s2[2] = s2[3] = s2[2] + s2[3];
+  }
+  if (ts.step > 1) {
+    if (cm) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (!valid[k]) continue;
+        const long long g0 = ((i0 + k) >> glog) << glog;
+        const long long glen = n - g0 < G ? n - g0 : G;
+        const float lbar = (float)((double)s2[k] * 0.5 / (double)glen);
+        const float mean = __uint_as_float((uint32_t)e.m_means[(i0 + k) >> glog] << 16);
+        const float q = mean + s_dec * (ustate_level((mcodes >> (2 * k)) & 3u) - lbar);
+        const float den = sqrt_rn(div_uniform(vprev[k], ts.inv_bc2p)) + s.eps;
+        mprev[k] = (q * ts.bc1p) * den;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) mprev[k] = valid[k] ? e.m_fp32[i0 + k] : 0.0f;
+    }
+  }
+
+  // ---- the update with the FP32 moments
+  float m1[4], v1[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float p1;
+    adamw(p[k], g[k] * s.gmul, s.beta1 * mprev[k], vprev[k], s, p1, m1[k], v1[k]);
+    if (valid[k]) bad += nonfinite3(p1, m1[k], v1[k]);
+    p[k] = p1;
+  }
+  if (full) {
+    f32x4 pv;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) pv[k] = p[k];
+    stream_store(reinterpret_cast<f32x4*>(e.p + i0), pv);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (valid[k]) e.p[i0 + k] = p[k];
+  }
+
+  const uint32_t ctr = (uint32_t)(i0 >> 2), stp = (uint32_t)ts.step, tsr = e.tensor_id;
+  const uint32_t sk0 = (uint32_t)e.seed, sk1 = (uint32_t)(e.seed >> 32);
+
+  // ---- second moment: 1Q per block, or FP32
+  float vq[4];
+  {
+    float lo_c = __builtin_inff(), hi_c = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float v = v1[k];
+      const bool pos = valid[k] && v > 0.0f && __builtin_isfinite(v);
+      lo_c = pos ? fminf(lo_c, v) : lo_c;
+      hi_c = pos ? fmaxf(hi_c, v) : hi_c;
+    }
+    // every thread takes part (the reductions may synchronise)
+    const float vmin = seg_reduce(lo_c, B / 4, [](float a, float b) { return fminf(a, b); }, fslot);
+    const float vmax = seg_reduce(hi_c, B / 4, [](float a, float b) { return fmaxf(a, b); }, fslot);
+    if (cv) {
+      uint32_t w[4];
+      philox4x32_10(ctr, stp, tsr, 0u, sk0, sk1, w);
+      // every lane of the block forms the same endpoints
+      const bool any = vmax > 0.0f;
+      const uint32_t lo16 = log2_directed16(vmin, false, any), hi16 = log2_directed16(vmax, true, any);
+      const uint32_t ends = any ? (lo16 | (hi16 << 16)) : 0u;
+      const double lo = f16_to_double(ends & 0xFFFFu), hi = f16_to_double(ends >> 16);
+      const float est_lo = f16_decode(ends & 0xFFFFu);
+      const float est_scale = (float)(L - 2) / (f16_decode(ends >> 16) - est_lo);
+      uint32_t field = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float v = v1[k];
+        uint32_t idx = 0;
+        float keep = 0.0f;
+        if (valid[k] && v > 0.0f) {
+          // the largest level k >= 1 at or below v (1 when none is): from
+          // the log2 estimate, moved down while the level is above v and up
+          // while the next level is not (levels do not decrease with k)
+          float t = (__builtin_amdgcn_logf(v) - est_lo) * est_scale + 1.0f;
+          t = t >= 1.0f ? t : 1.0f;   // also NaN
+          t = t <= (float)(L - 1) ? t : (float)(L - 1);
+          int kk = (int)t;
+          float lk = q1_level(lo, hi, kk, L);
+          while (kk > 1 && lk > v) lk = q1_level(lo, hi, --kk, L);
+          float lk1 = kk < L - 1 ? q1_level(lo, hi, kk + 1, L) : lk;
+          while (kk < L - 1 && lk1 <= v) {
+            ++kk;
+            lk = lk1;
+            lk1 = kk < L - 1 ? q1_level(lo, hi, kk + 1, L) : lk;
+          }
+          const float f = __fdiv_rn(v - lk, lk1 - lk);
+          const float u = (float)(w[k] >> 8) * 0x1p-24f;
+          const bool up = kk < L - 1 && v > lk && u < f;
+          idx = (uint32_t)kk + (up ? 1u : 0u);
+          keep = up ? lk1 : lk;
+          if (__builtin_isinf(v)) {
+            idx = (uint32_t)(L - 1);
+            keep = lk;   // kk reached L - 1
+          }
+        }
+        vq[k] = keep;
+        field |= idx << (BITS * k);
+      }
+      // the tile's index words, assembled in LDS (fields straddle words)
+      __syncthreads();   // words cleared
+      const int b0 = 4 * tid * BITS, sh = b0 & 31;
+      if (field) {
+        atomicOr(&words[b0 >> 5], field << sh);
+        if (sh + 4 * BITS > 32) atomicOr(&words[(b0 >> 5) + 1], field >> (32 - sh));
+      }
+      __syncthreads();
+      const long long nwords = (n * BITS + 31) >> 5, base_w = local * kWords;
+      uint32_t* out = reinterpret_cast<uint32_t*>(e.v_index);
+      for (int j = tid; j < kWords; j += kThreads)
+        if (base_w + j < nwords) out[base_w + j] = words[j];
+      if ((tid & (B / 4 - 1)) == 0 && valid[0]) reinterpret_cast<uint32_t*>(e.v_ends)[blk] = ends;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        vq[k] = v1[k];
+        if (valid[k]) e.v_fp32[i0 + k] = v1[k];
+      }
+    }
+  }
+
+  // ---- first moment: UState per group, or FP32
+  {
+    float q[4] = {0.f, 0.f, 0.f, 0.f};
+    if (cm) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float den = sqrt_rn(div_bc2(vq[k], s)) + s.eps;
+        q[k] = valid[k] ? __fdiv_rn(div_uniform(m1[k], ts.inv_bc1), den) : 0.0f;
+      }
+    }
+    // group sums: a perfect pairwise tree in double (zero padding past the end)
+    double gs[4];
+    if (G >= 4) {
+      const double t = seg_reduce(((double)q[0] + (double)q[1]) + ((double)q[2] + (double)q[3]), G / 4,
+                                  [](double a, double b) { return a + b; }, dslot);
+      gs[0] = gs[1] = gs[2] = gs[3] = t;
+    } else if (G == 2) {
+      gs[0] = gs[1] = (double)q[0] + (double)q[1];
+      gs[2] = gs[3] = (double)q[2] + (double)q[3];
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) gs[k] = (double)q[k];
+    }
+    if (cm) {
+      uint32_t w[4];
+      philox4x32_10(ctr, stp, tsr, 1u, sk0, sk1, w);
+      uint32_t codes = 0;
+      double r2[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const long long g0 = ((i0 + k) >> glog) << glog;
+        const long long glen = n - g0 < G ? n - g0 : G;
+        const uint32_t mean16 = bf16_encode((float)(gs[k] / (double)glen));
+        const float mean = __uint_as_float(mean16 << 16);
+        const float r = q[k] - mean;
+        r2[k] = valid[k] ? (double)r * (double)r : 0.0;
+        float x = s_enc > 0.0f ? __fdiv_rn(r, s_enc) : 0.0f;
+        x = x > 1.5f ? 1.5f : x;
+        x = x < -1.5f ? -1.5f : x;
+        float u = (float)(w[k >> 1] >> 8) * 0x1p-24f;
+        if (k & 1) u = 1.0f - u;
+        const uint32_t kk = (uint32_t)(x >= -0.5f) + (uint32_t)(x >= 0.5f);
+        uint32_t code = kk;
+        if (x >= 1.5f) code = 3;
+        else if (u < x - ustate_level(kk)) code = kk + 1;
+        codes |= valid[k] ? code << (2 * k) : 0u;
+        // the first value of each group stores its mean
+        if (valid[k] && i0 + k == g0) e.m_means[(i0 + k) >> glog] = (uint16_t)mean16;
+      }
+      if (valid[0]) e.m_codes[i0 >> 2] = (uint8_t)codes;
+      const double tsum = butterfly_sum<64>((r2[0] + r2[1]) + (r2[2] + r2[3]));
+      const long long sub = local * (kGenTile / kTurboTile) + wave;   // this wavefront's 256 values
+      if (lane == 0 && sub * kTurboTile < n) ws[e.ws0 + sub] = tsum;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (valid[k]) e.m_fp32[i0 + k] = m1[k];
+    }
+  }
+  if constexpr (COUNT) flush_count(bad, nonfinite);
+}
+
 // The residual sums of the tensors with a UState first moment.  Each tile
 // wrote one double; a tensor's sum is the perfect pairwise tree over its
 // tile sums in index order, zero-padded to a power of two.  turbo_chunks

@@ -212,11 +212,12 @@ class TurboAdam(torch.optim.Optimizer):
     rotation, with the page's defaults.
 
     Arguments follow the page's API: lr, betas, eps, weight_decay,
-    block_size (128 only here), v_bits (2, 4 or 8 here; the page also has 3
-    and 6), compress_m, compress_v, min_m_compress_elements and
+    block_size (a power of two from 32 to 1024), v_bits (2, 3, 4, 6 or 8),
+    compress_m, compress_v, min_m_compress_elements and
     min_v_compress_elements (a tensor below the threshold keeps that
-    moment in FP32), m_block_size (64 only here), m_step_factor and
-    rounding_seed.  The page's validation of beta1^2 < beta2 with UState
+    moment in FP32), m_block_size (a power of two dividing block_size),
+    m_step_factor and rounding_seed.  The default layout (128, 4 bits, 64)
+    runs the tuned kernel, every other one the general kernel.  The page's validation of beta1^2 < beta2 with UState
     on is kept.  One parameter group of contiguous FP32 tensors on one GPU;
     ``count_nonfinite``, ``nonfinite_count()`` and ``state_bytes()`` as for
     PackedAdamW.
@@ -225,11 +226,10 @@ class TurboAdam(torch.optim.Optimizer):
     def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0, block_size=128, v_bits=4,
                  compress_m=True, compress_v=True, min_m_compress_elements=4096, min_v_compress_elements=4096,
                  m_block_size=64, m_step_factor=1.1, rounding_seed=0x12345678, count_nonfinite=True):
-        from . import TurboList, TurboState
-        if block_size != 128 or m_block_size != 64:
-            raise ValueError("this implementation has 128-value 1Q blocks and 64-value UState groups")
-        if v_bits not in (2, 4, 8):
-            raise ValueError("v_bits must be 2, 4 or 8 here")
+        from . import TurboList, TurboState, turbo_layout_ok
+        if not turbo_layout_ok(v_bits, block_size, m_block_size):
+            raise ValueError("v_bits must be 2, 3, 4, 6 or 8, block_size a power of two from 32 to 1024 and "
+                             "m_block_size a power of two dividing block_size")
         if compress_m and not betas[0] ** 2 < betas[1]:
             raise ValueError("UState needs beta1**2 < beta2")
         defaults = dict(lr=lr, betas=betas, eps=eps, weight_decay=weight_decay)
@@ -244,13 +244,15 @@ class TurboAdam(torch.optim.Optimizer):
             if p.dtype != torch.float32 or not p.is_cuda or not p.is_contiguous() or p.device != dev:
                 raise TypeError("parameters must be contiguous float32 tensors on one GPU")
         self.v_bits, self.m_step_factor, self.seed = v_bits, float(m_step_factor), int(rounding_seed)
+        self.block_size, self.m_block_size = int(block_size), int(m_block_size)
         self.step_count = 0
         self._TurboList = TurboList
         self._states = []
         for i, p in enumerate(plist):
             n = p.numel()
             st = TurboState(n, dev, compress_m=compress_m and n >= min_m_compress_elements,
-                            compress_v=compress_v and n >= min_v_compress_elements, v_bits=v_bits, tensor_id=i)
+                            compress_v=compress_v and n >= min_v_compress_elements, v_bits=v_bits, tensor_id=i,
+                            block_size=block_size, m_block_size=m_block_size)
             self._states.append(st)
             self.state[p]["turbo"] = st
         self._prepared = None
@@ -281,7 +283,8 @@ class TurboAdam(torch.optim.Optimizer):
         key = tuple(g.data_ptr() for g in grads)
         if self._prepared is None or key != self._prepared_key:
             self._prepared = self._TurboList(params, grads, self._states, v_bits=self.v_bits,
-                                             m_step_factor=self.m_step_factor, seed=self.seed)
+                                             m_step_factor=self.m_step_factor, seed=self.seed,
+                                             block_size=self.block_size, m_block_size=self.m_block_size)
             self._prepared_key = key
         self.step_count += 1
         beta1, beta2 = group["betas"]
@@ -302,13 +305,16 @@ class TurboAdam(torch.optim.Optimizer):
                 ("v_index", st.v_index), ("v_ends", st.v_ends), ("v_fp32", st.v_fp32)) if t is not None}
         return {"state": state, "param_groups": groups,
                 "turbo": {"step": self.step_count, "v_bits": self.v_bits, "seed": self.seed,
-                          "m_step_factor": self.m_step_factor}}
+                          "m_step_factor": self.m_step_factor, "block_size": self.block_size,
+                          "m_block_size": self.m_block_size}}
 
     def load_state_dict(self, state_dict):
         """Restore a checkpoint written by state_dict(), bit for bit."""
         meta = state_dict["turbo"]
         if meta["v_bits"] != self.v_bits or meta["seed"] != self.seed:
             raise ValueError("checkpoint was written with another v_bits or rounding seed")
+        if (meta.get("block_size", 128), meta.get("m_block_size", 64)) != (self.block_size, self.m_block_size):
+            raise ValueError("checkpoint was written with another block_size or m_block_size")
         for g, saved in zip(self.param_groups, state_dict["param_groups"]):
             for k, v in saved.items():
                 g[k] = v

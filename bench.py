@@ -28,7 +28,12 @@ Other flags:
   --mode turbo            the TurboAdam compressed-state step (UState first
                           moment, 4-bit 1Q second moment; tensors below 4096
                           values keep FP32 moments, as the page's thresholds)
-  --turbo-bits B          with --mode turbo: 1Q index width, 2, 4 or 8
+  --turbo-bits B          with --mode turbo: 1Q index width, 2, 3, 4, 6 or 8
+  --turbo-block B, --turbo-group G
+                          with --mode turbo: 1Q block (32 to 1024) and UState
+                          group (dividing it); defaults 128 and 64
+  --turbo-general         with --mode turbo: run the general kernel even at
+                          the default layout
   --count-nonfinite       count non-finite values, as the optimizers do by
                           default (the counting kernel variant)
   --mode gradstats        instead of the step: time the gradient pre-pass
@@ -401,14 +406,17 @@ def run_turbo(args, cfg):
     spacer = None
     if args.layout == "regions":
         spacer = torch.empty(max(region_bytes() - 8 * sum(sizes), 0), dtype=torch.uint8, device="cuda:0")
+    B, G = args.turbo_block, args.turbo_group
+    general = args.turbo_general or (B, G) != (128, 64) or args.turbo_bits in (3, 6)
     states = [pa.TurboState(n, "cuda:0", compress_m=n >= 4096, compress_v=n >= 4096, v_bits=args.turbo_bits,
-                            tensor_id=i)
+                            tensor_id=i, block_size=B, m_block_size=G)
               for i, n in enumerate(sizes)]
     del spacer
     torch.cuda.empty_cache()
     workloads.device_fill_params(cfg, ps)
     workloads.device_fill_grads(cfg, 1, gs)
-    tl = pa.TurboList(ps, gs, states, v_bits=args.turbo_bits)
+    tl = pa.TurboList(ps, gs, states, v_bits=args.turbo_bits, block_size=B, m_block_size=G,
+                      general=args.turbo_general)
     h = dict(workloads.HYPER)
     if args.count_nonfinite:   # the optimizers' default: the kernel variant that counts
         h["nonfinite"] = torch.zeros(1, dtype=torch.int64, device="cuda:0")
@@ -432,7 +440,7 @@ def run_turbo(args, cfg):
     mean_ms = sum(launch_ms) / len(launch_ms)
     n = sum(sizes)
     state = sum(st.nbytes() for st in states)
-    tiles = sum((k + 255) // 256 for k in sizes if k >= 4096)
+    tiles = sum((k + 255) // 256 for k in sizes if k >= 4096)   # residual partial sums, either kernel
     algo = 12 * n + 2 * state + 16 * tiles     # p, g read; p written; state read and written; residual sums
     achieved = algo / (mean_ms / 1e3) / 1e9
     log(f"timed {args.steps} TurboAdam steps: {mean_ms:.3f} ms/step (events), state {state / n:.4f} B/param")
@@ -441,7 +449,7 @@ def run_turbo(args, cfg):
     # the counters measured for this kernel source (profiles/), if current.
     valu = None
     vpath = os.path.join(ROOT, "profiles", f"valu_{args.workload}_turbo.json")
-    if os.path.exists(vpath) and args.turbo_bits == 4 and not args.count_nonfinite:   # the counters' kernel
+    if os.path.exists(vpath) and args.turbo_bits == 4 and not args.count_nonfinite and not general:
         with open(vpath) as f:
             vj = json.load(f)
         if vj.get("kernel_sha") == kernel_sha("turbo"):
@@ -451,6 +459,7 @@ def run_turbo(args, cfg):
            "ms_per_step": round(elapsed * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
            "config": {"workload": args.workload, "params": n, "tensors": len(sizes), "mode": f"turbo-ustate-1q{args.turbo_bits}",
+                      "block_size": B, "m_block_size": G,
                       "state_bytes": state, "state_bits_per_param": round(8 * state / n, 4),
                       "layout": args.layout, "count_nonfinite": bool(args.count_nonfinite)},
            "roofline": ({"bound": "alu", "achieved": round(valu * n / (mean_ms / 1e3) / 1e9, 1),
@@ -461,8 +470,8 @@ def run_turbo(args, cfg):
                          "frac": None}) | {
                         "hbm_achieved_gbps": round(achieved, 1), "hbm_frac": round(achieved / PEAK_GBPS, 4),
                         "traffic": None,
-                        "kernel": f"turbo_list<{args.turbo_bits}, {'true' if args.count_nonfinite else 'false'}>"
-                                  " + turbo_chunks + turbo_reduce",
+                        "kernel": f"{'turbo_general' if general else 'turbo_list'}<{args.turbo_bits}, "
+                                  f"{'true' if args.count_nonfinite else 'false'}> + turbo_chunks + turbo_reduce",
                         "algorithmic_bytes_per_launch": algo, "mean_launch_ms": round(mean_ms, 4),
                         "kernel_sha": kernel_sha("turbo")}}
     if not args.no_cpu_baseline:
@@ -476,7 +485,7 @@ def run_turbo(args, cfg):
             total += k
         hp = [ps[i].cpu().numpy() for i in picked]
         hg = [gs[i].cpu().numpy() for i in picked]
-        hs = [oracle.TurboState(sizes[i], sizes[i] >= 4096, sizes[i] >= 4096, args.turbo_bits) for i in picked]
+        hs = [oracle.TurboState(sizes[i], sizes[i] >= 4096, sizes[i] >= 4096, args.turbo_bits, B, G) for i in picked]
         sc = oracle.scalars(h["lr"], h["beta1"], h["beta2"], h["eps"], h["weight_decay"], 1)
         ts = oracle.turbo_scalars(h["beta1"], h["beta2"], 1)
         t1 = time.perf_counter()
@@ -516,8 +525,12 @@ def main():
     ap.add_argument("--train-gpt", action="store_true")
     ap.add_argument("--param-dtype", default="fp32", choices=["fp32", "bf16", "fp16"],
                     help="element type of parameters and gradients (state unchanged)")
-    ap.add_argument("--turbo-bits", type=int, default=4, choices=[2, 4, 8],
+    ap.add_argument("--turbo-bits", type=int, default=4, choices=[2, 3, 4, 6, 8],
                     help="1Q index width of the TurboAdam mode (the page's default is 4)")
+    ap.add_argument("--turbo-block", type=int, default=128, help="1Q block of the TurboAdam mode (32 to 1024)")
+    ap.add_argument("--turbo-group", type=int, default=64, help="UState group of the TurboAdam mode (divides the block)")
+    ap.add_argument("--turbo-general", action="store_true",
+                    help="run the general TurboAdam kernel even at the default layout")
     ap.add_argument("--count-nonfinite", action="store_true",
                     help="count non-finite values, as the optimizers do by default (the counting kernel)")
     ap.add_argument("--layout", default="regions", choices=["regions", "plain"],

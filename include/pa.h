@@ -250,12 +250,20 @@ int pa_grad_stats_list(int grad_dtype, size_t count, const void* const* grads, c
  * with UState.  Readings of what the page leaves open (code levels, grid,
  * scale rule, random draws) are stated in adamw_step_amd/csrc/turbo.hpp.
  *
+ * Layout (TurboAdam package page, "Fused CUDA path" and API: block_size,
+ * m_block_size, v_bits): a 1Q block of B values (a power of two from 32 to
+ * 1024, default 128) shares one pair of log2 endpoints; a UState group of G
+ * values (a power of two dividing B, default 64) shares one mean; indices
+ * have 2, 3, 4, 6 or 8 bits (default 4), packed densely: value i occupies
+ * bits [v_bits*i, v_bits*i + v_bits) of the little-endian bit stream of
+ * 32-bit words, so 3- and 6-bit indices straddle words.
+ *
  * Per tensor, device buffers (all caller-owned, zero-filled before step 1):
  *   compress_m != 0 (UState): m_codes 4*ceil(n/16) bytes of 2-bit codes,
- *     m_means ceil(n/64) bfloat16, scalars 3 floats (decode scale, encode
+ *     m_means ceil(n/G) bfloat16, scalars 3 floats (decode scale, encode
  *     scale, accumulator); else m_fp32, n floats.
  *   compress_v != 0 (1Q): v_index 4*ceil(n*v_bits/32) bytes of indices,
- *     v_ends 2*ceil(n/128) binary16 (low, high log2 endpoint per 128 values);
+ *     v_ends 2*ceil(n/B) binary16 (low, high log2 endpoint per block);
  *     else v_fp32, n floats.
  *   tensor_id keys the tensor's counter-based random draws (keep it fixed
  *   across steps and distinct across tensors).
@@ -278,18 +286,30 @@ typedef struct {
   float* scalars;
 } pa_turbo_state;
 
-/* v_bits: 1Q index width, 2, 4 (the page's default) or 8.  m_step_factor:
- * the UState scale factor (the page's default 1.1).  seed: the rounding
- * seed (the page's default 0x12345678). */
+/* v_bits: 1Q index width, 2, 3, 4 (the page's default), 6 or 8.
+ * m_step_factor: the UState scale factor (the page's default 1.1).  seed:
+ * the rounding seed (the page's default 0x12345678).  block_size,
+ * m_block_size: B and G above, 0 for the defaults 128 and 64.  path: 0
+ * picks the kernel (a tuned one for B = 128, G = 64 and 2, 4 or 8 bits,
+ * the general one otherwise); 1 runs the general kernel for every layout
+ * (the results are the same; for tests and measurement).  PA_ERR_ARG for
+ * any other value or layout. */
 typedef struct {
   int v_bits;
   double m_step_factor;
   unsigned long long seed;
+  int block_size;
+  int m_block_size;
+  int path;
 } pa_turbo_config;
 
-/* Persistent bytes of one tensor's TurboAdam state (the page's ledger: for
- * 131,072 values with both representations, 36,876 + 69,632 = 106,508). */
+/* Persistent bytes of one tensor's TurboAdam state at the default layout
+ * (the page's ledger: for 131,072 values with both representations,
+ * 36,876 + 69,632 = 106,508), and at any layout above.  0 for an index
+ * width or layout the step does not take. */
 size_t pa_turbo_state_bytes(int compress_m, int compress_v, int v_bits, size_t n);
+size_t pa_turbo_layout_bytes(int compress_m, int compress_v, int v_bits, int block_size, int m_block_size,
+                             size_t n);
 
 /* Device workspace a pa_turbo_step_list call needs, for every tensor with
  * compress_m: one double per 256 values (its residual partial sums) plus
@@ -298,10 +318,11 @@ size_t pa_turbo_state_bytes(int compress_m, int compress_v, int v_bits, size_t n
 size_t pa_turbo_workspace_bytes(size_t count, const pa_turbo_state* states, const size_t* n);
 
 /* One TurboAdam step over `count` tensors sharing hyper, config and step
- * (1 to 2^32 - 1, counting this update; PA_ERR_ARG outside): one persistent
- * launch over all tensors (a wavefront per 256 values), then one workgroup
- * per 2048 residual partial sums and one per UState tensor that completes
- * the sum and rotates its scales.  `states` is a host array of count
+ * (1 to 2^32 - 1, counting this update; PA_ERR_ARG outside): one launch over
+ * all tensors (the tuned kernel: a persistent grid, a wavefront per 256
+ * values; the general one: a workgroup per 1024 values), then one
+ * workgroup per 2048 residual partial sums and one per UState tensor that
+ * completes the sum and rotates its scales.  `states` is a host array of count
  * descriptors; `workspace` a device buffer of at least
  * pa_turbo_workspace_bytes (8-byte aligned).  The launch plan is cached per
  * distinct list (see pa_release_plans).  Written buffers may not overlap

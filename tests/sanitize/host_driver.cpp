@@ -56,14 +56,21 @@ int main() {
   pa_turbo_state ts{1, 1, 0, reinterpret_cast<uint8_t*>(F + (1 << 21)), reinterpret_cast<uint16_t*>(F + (1 << 22)),
                     nullptr, reinterpret_cast<uint8_t*>(F + (1 << 23)), reinterpret_cast<uint16_t*>(F + (1 << 24)),
                     nullptr, P(F + (1 << 25))};
-  pa_turbo_config tc{3, 1.1, 1};
+  pa_turbo_config tc{5, 1.1, 1, 0, 0, 0};
   float* tp[1] = {P(F)};
   const float* tg[1] = {P(F + (1 << 20))};
   size_t tn[1] = {4096};
   expect(pa_turbo_step_list(1, tp, tg, &ts, tn, &h, &tc, 1, reinterpret_cast<void*>(F + (1 << 26)), 1 << 20, nullptr),
          PA_ERR_ARG, "turbo bits");
+  pa_turbo_config tcb{3, 1.1, 1, 96, 32, 0};
+  expect(pa_turbo_step_list(1, tp, tg, &ts, tn, &h, &tcb, 1, reinterpret_cast<void*>(F + (1 << 26)), 1 << 20, nullptr),
+         PA_ERR_ARG, "turbo block");
+  pa_turbo_config tcg{6, 1.1, 1, 64, 128, 0};
+  expect(pa_turbo_step_list(1, tp, tg, &ts, tn, &h, &tcg, 1, reinterpret_cast<void*>(F + (1 << 26)), 1 << 20, nullptr),
+         PA_ERR_ARG, "turbo group");
+  if (pa_turbo_layout_bytes(1, 1, 3, 32, 8, 1000) != 4 * 63 + 2 * 125 + 12 + 4 * 94 + 4 * 32) ++bad;
   pa_hyper hb{1e-3, 0.99, 0.98, 1e-8, 0.01, nullptr, nullptr, nullptr};
-  pa_turbo_config tc4{4, 1.1, 1};
+  pa_turbo_config tc4{4, 1.1, 1, 0, 0, 0};
   expect(pa_turbo_step_list(1, tp, tg, &ts, tn, &hb, &tc4, 1, reinterpret_cast<void*>(F + (1 << 26)), 1 << 20, nullptr),
          PA_ERR_ARG, "turbo betas");
   if (pa_turbo_state_bytes(1, 1, 4, 131072) != 106508 || pa_turbo_workspace_bytes(1, &ts, tn) != 136) ++bad;

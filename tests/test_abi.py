@@ -261,7 +261,11 @@ def test_turbo_argument_rules(pa):
                                                   FAKE + 2 ** 23, FAKE + 2 ** 24, None, FAKE + 2 ** 25))
     call = lambda h_, c_, step=1: L.pa_turbo_step_list(1, P, G, S, N, ctypes.byref(h_), ctypes.byref(c_), step,
                                                         FAKE + 2 ** 26, 1 << 20, None)
-    assert call(h, pa.TurboConfig(3, 1.1, 1)) == pa.PA_ERR_ARG            # index width
+    for bits in (0, 1, 5, 7, 9):                                          # index width
+        assert call(h, pa.TurboConfig(bits, 1.1, 1)) == pa.PA_ERR_ARG
+    for block, group in ((16, 8), (2048, 64), (96, 32), (64, 128), (128, 3), (128, -4), (-128, 64)):
+        assert call(h, pa.TurboConfig(4, 1.1, 1, block, group)) == pa.PA_ERR_ARG, (block, group)
+    assert call(h, pa.TurboConfig(4, 1.1, 1, 0, 0, 2)) == pa.PA_ERR_ARG   # kernel choice
     assert call(h, pa.TurboConfig(4, 0.0, 1)) == pa.PA_ERR_ARG            # scale factor
     assert call(h, cfg, step=0) == pa.PA_ERR_ARG
     assert call(h, cfg, step=2 ** 32) == pa.PA_ERR_ARG                    # the draws' 32-bit step word
@@ -272,7 +276,17 @@ def test_turbo_argument_rules(pa):
     assert call(hb, cfg) == pa.PA_ERR_ARG
     assert pa.pa_turbo_state_bytes(1, 1, 4, 131072) == 106508
     assert pa.pa_turbo_state_bytes(0, 0, 4, 10) == 80
-    assert pa.pa_turbo_state_bytes(1, 1, 3, 10) == 0
+    assert pa.pa_turbo_state_bytes(1, 1, 5, 10) == 0
+    import oracle
+    for bits in (2, 3, 4, 6, 8):
+        for block, group in ((32, 1), (32, 32), (128, 64), (256, 2), (1024, 1024), (1024, 16)):
+            for cm, cv in ((1, 1), (1, 0), (0, 1)):
+                for n in (1, 31, 4096, 100003):
+                    got = pa.pa_turbo_layout_bytes(cm, cv, bits, block, group, n)
+                    assert got == oracle.turbo_state_bytes(cm, cv, bits, n, block, group), (bits, block, group, n)
+                    if (block, group) == (128, 64):
+                        assert got == pa.pa_turbo_state_bytes(cm, cv, bits, n)
+    assert pa.pa_turbo_layout_bytes(1, 1, 4, 64, 128, 10) == 0
     assert L.pa_turbo_workspace_bytes(1, S, N) == 8 * (16 + 1)           # 16 tile sums, 1 chunk sum
     N[0] = 2048 * 256 + 1                                                 # 2049 tile sums, 2 chunk sums
     assert L.pa_turbo_workspace_bytes(1, S, N) == 8 * (2049 + 2)

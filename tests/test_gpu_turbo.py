@@ -2,7 +2,10 @@
 the oracle, value by value and bit for bit: parameters, 2-bit codes, bf16
 means, 1Q indices, fp16 endpoints, tensor scales, and the FP32 moments of
 tensors that keep them.  Sizes span tiles, blocks and groups with ragged
-tails; lists mix the four representation pairs and the three index widths."""
+tails; lists mix the four representation pairs and the index widths.  Every
+layout of the page's fused path runs through the general kernel (blocks of
+32 to 1024 values, groups of 1 to 1024, 2 to 8 index bits), and so does the
+default layout, against the same oracle."""
 import json
 import os
 
@@ -44,15 +47,16 @@ def _compare_state(dev, host, what):
         assert np.array_equal(_host_words(dev.v_fp32, np.uint32), host.v_fp32.view(np.uint32)), f"{what}: v"
 
 
-def _run(pa, sizes, flags, bits, steps, seed, grad_scale=1e-3, count=False):
+def _run(pa, sizes, flags, bits, steps, seed, grad_scale=1e-3, count=False, block=128, group=64, general=False):
     import torch
     r = np.random.Generator(np.random.PCG64(seed))
     hp = [r.normal(0, 0.02, n).astype(np.float32) for n in sizes]
     dp = [to_dev(a) for a in hp]
-    hs = [oracle.TurboState(n, cm, cv, bits) for n, (cm, cv) in zip(sizes, flags)]
-    ds = [pa.TurboState(n, "cuda:0", cm, cv, bits, tensor_id=i) for i, (n, (cm, cv)) in enumerate(zip(sizes, flags))]
+    hs = [oracle.TurboState(n, cm, cv, bits, block, group) for n, (cm, cv) in zip(sizes, flags)]
+    ds = [pa.TurboState(n, "cuda:0", cm, cv, bits, tensor_id=i, block_size=block, m_block_size=group)
+          for i, (n, (cm, cv)) in enumerate(zip(sizes, flags))]
     grads = [torch.zeros(n, dtype=torch.float32, device="cuda:0") for n in sizes]
-    tl = pa.TurboList(dp, grads, ds, v_bits=bits)
+    tl = pa.TurboList(dp, grads, ds, v_bits=bits, block_size=block, m_block_size=group, general=general)
     hyper = dict(H)
     if count:   # the kernel variant that counts non-finite values (the optimizers' default)
         hyper["nonfinite"] = torch.zeros(1, dtype=torch.int64, device="cuda:0")
@@ -61,7 +65,7 @@ def _run(pa, sizes, flags, bits, steps, seed, grad_scale=1e-3, count=False):
         hg = [(r.normal(0, 1, n) * grad_scale * 10.0 ** r.uniform(-2, 1)).astype(np.float32) for n in sizes]
         for gdev, g in zip(grads, hg):
             gdev.copy_(torch.from_numpy(g))
-        banner(f"turbo bits {bits} sizes {sizes[:5]}.. step {t}")
+        banner(f"turbo bits {bits} block {block} group {group} general {general} sizes {sizes[:5]}.. step {t}")
         tl.step(hyper, t)
         torch.cuda.synchronize()
         if count:
@@ -74,7 +78,7 @@ def _run(pa, sizes, flags, bits, steps, seed, grad_scale=1e-3, count=False):
             s_, _ = assert_params(to_host(dp[i]), hp[i], what=f"step {t} tensor {i} params")
             same += s_
             total += sizes[i]
-    banner(f"turbo bits {bits}: bit-identical params {same}/{total}")
+    banner(f"turbo bits {bits} block {block} group {group}: bit-identical params {same}/{total}")
 
 
 SIZES = [1, 5, 63, 64, 65, 127, 128, 129, 255, 256, 257, 4096 + 77, 70001]
@@ -105,6 +109,37 @@ def test_turbo_several_tiles_per_wavefront(pa, bits, count):
     flags = [(True, True), (False, True), (True, False), (False, False)] * 4
     assert sum((n + 255) // 256 for n in sizes) > 3 * 256 * 8 * 4
     _run(pa, sizes, flags, bits, steps=3, seed=40 + bits, count=count)
+
+
+# (index bits, 1Q block, UState group): the widths that straddle words, the
+# smallest and largest blocks and groups, and segments of one lane up to
+# four wavefronts.
+LAYOUTS = [(3, 128, 64), (6, 128, 64), (2, 32, 32), (4, 32, 8), (8, 1024, 1024), (3, 1024, 2), (6, 256, 1),
+           (4, 512, 128), (2, 64, 4), (8, 32, 16), (3, 256, 256), (6, 1024, 512)]
+LAYOUT_SIZES = [1, 5, 31, 32, 33, 255, 1023, 1024, 1025, 2047, 4096 + 77, 70001]
+
+
+@pytest.mark.parametrize("bits,block,group", LAYOUTS, ids=lambda x: str(x))
+def test_turbo_other_layouts(pa, bits, block, group):
+    flags = [(True, True)] * 8 + [(False, True), (True, False), (True, True), (False, False)]
+    _run(pa, LAYOUT_SIZES, flags, bits, steps=3, seed=500 + 7 * bits + block + group, block=block, group=group)
+
+
+@pytest.mark.parametrize("bits,count", [(2, False), (4, False), (8, False), (4, True)])
+def test_turbo_general_kernel_at_default_layout(pa, bits, count):
+    """The general kernel forced at the tuned kernel's layout gives the same
+    (oracle) results."""
+    _run(pa, SIZES, [(True, True)] * len(SIZES), bits, steps=3, seed=600 + bits, count=count, general=True)
+
+
+@pytest.mark.parametrize("bits,block,group,count", [(3, 128, 64, True), (6, 64, 2, False)])
+def test_turbo_general_many_tiles(pa, bits, block, group, count):
+    """About 4,300 general-kernel tiles over sixteen tensors of every
+    representation pair: the tensor search of each workgroup and the
+    residual partial sums of many tiles per tensor."""
+    sizes = [1500001, 3, 900017, 129, 1200003, 257, 100007, 65, 300011, 4097, 200013, 1, 60009, 12345, 40001, 255]
+    flags = [(True, True), (False, True), (True, False), (False, False)] * 4
+    _run(pa, sizes, flags, bits, steps=3, seed=700 + bits, count=count, block=block, group=group)
 
 
 def test_turbo_large_tensor(pa):
