@@ -691,9 +691,11 @@ turbo_list(const TurboEntry* __restrict__ table, long long total_tiles, Scalars 
 // 4, 6 or 8 index bits), with the arithmetic and draws of turbo_tile.  One
 // 256-thread workgroup per 1024-value tile of one tensor, so a tile holds
 // whole blocks and whole groups; thread t holds values 4t..4t+3 of its
-// tile.  Levels are computed per value (the same exact power as the table
-// builders) instead of from per-block tables, whose size would grow with
-// the number of levels over small blocks.  Reductions over a block or a
+// tile.  When a block has at least as many values as levels (L <= B), the
+// lanes of each block build its decode and encode tables in LDS, each entry
+// the pair (level, UState denominator) as in build_tables; otherwise the
+// levels are computed per value (the same exact power), since per-block
+// tables would cost more levels than the block has values.  Reductions over a block or a
 // group are xor butterflies over its lanes; segments wider than a
 // wavefront finish through LDS as further levels of the same tree.  The
 // residual partial sums go to turbo_list's workspace slots (one per 256
@@ -735,6 +737,7 @@ turbo_general(const TurboEntry* __restrict__ table, int count, long long tile_ba
   constexpr int L = 1 << BITS;
   constexpr int kWords = kGenTile * BITS / 32;       // index words of a tile
   __shared__ uint32_t words[kWords];
+  __shared__ float2 tabs[2][kGenTile];               // decode, encode tables (L <= B)
   __shared__ float fslot[4];
   __shared__ double dslot[4];
   __shared__ int islot[4];
@@ -753,6 +756,10 @@ turbo_general(const TurboEntry* __restrict__ table, int count, long long tile_ba
   const long long n = e.n;
   const bool cm = e.flags & 1, cv = e.flags & 2;
   const int B = 1 << blog, G = 1 << glog;
+  const bool use_tab = L <= B;                       // uniform
+  const int lb = tid & (B / 4 - 1);                  // lane within the block
+  float2* const dec_tab = tabs[0] + ((4 * tid) >> blog) * L;
+  float2* const enc_tab = tabs[1] + ((4 * tid) >> blog) * L;
   bool valid[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) valid[k] = i0 + k < n;
@@ -762,6 +769,7 @@ turbo_general(const TurboEntry* __restrict__ table, int count, long long tile_ba
 
   // ---- loads
   float p[4], g[4], mprev[4] = {0.f, 0.f, 0.f, 0.f}, vprev[4] = {0.f, 0.f, 0.f, 0.f};
+  float dprev[4] = {0.f, 0.f, 0.f, 0.f};              // UState decode denominators (tables)
   if (full) {
     const f32x4 pv = stream_load(reinterpret_cast<const f32x4*>(e.p + i0));
     const f32x4 gv = stream_load(reinterpret_cast<const f32x4*>(e.g + i0));
@@ -778,6 +786,7 @@ turbo_general(const TurboEntry* __restrict__ table, int count, long long tile_ba
     }
   }
   const long long blk = i0 >> blog;                  // 1Q block of this thread's values
+  const bool blk_exists = (blk << blog) < n;
   const float s_dec = cm ? e.scal[0] : 0.0f, s_enc = cm ? e.scal[1] : 0.0f;
 
   // ---- decode the prior moments (the state is empty at step 1)
@@ -794,13 +803,29 @@ turbo_general(const TurboEntry* __restrict__ table, int count, long long tile_ba
         unsigned long long both = w32[w0];
         if (bit_end > (w0 + 1) * 32) both |= (unsigned long long)w32[w0 + 1] << 32;
         field = (uint32_t)(both >> sh);
-        ends = reinterpret_cast<const uint32_t*>(e.v_ends)[blk];
       }
+      // every lane of an existing block needs its endpoints (table builders
+      // past the tensor's end included)
+      if (blk_exists) ends = reinterpret_cast<const uint32_t*>(e.v_ends)[blk];
       const double lo = f16_to_double(ends & 0xFFFFu), hi = f16_to_double(ends >> 16);
+      if (use_tab) {
+        for (int k = lb; k < L; k += B / 4) {
+          const float a = k ? q1_level(lo, hi, k, L) : 0.0f;
+          dec_tab[k] = make_float2(a, sqrt_rn(div_uniform(a, ts.inv_bc2p)) + s.eps);
+        }
+        __syncthreads();
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int ix = (int)((field >> (BITS * k)) & (uint32_t)(L - 1));
-        vprev[k] = (valid[k] && ix > 0) ? q1_level(lo, hi, ix, L) : 0.0f;
+        for (int k = 0; k < 4; ++k) {
+          const float2 t = dec_tab[(field >> (BITS * k)) & (uint32_t)(L - 1)];
+          vprev[k] = valid[k] ? t.x : 0.0f;
+          dprev[k] = t.y;
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int ix = (int)((field >> (BITS * k)) & (uint32_t)(L - 1));
+          vprev[k] = (valid[k] && ix > 0) ? q1_level(lo, hi, ix, L) : 0.0f;
+        }
       }
     } else {
 #pragma unroll
@@ -831,7 +856,7 @@ turbo_general(const TurboEntry* __restrict__ table, int count, long long tile_ba
         const float lbar = (float)((double)s2[k] * 0.5 / (double)glen);
         const float mean = __uint_as_float((uint32_t)e.m_means[(i0 + k) >> glog] << 16);
         const float q = mean + s_dec * (ustate_level((mcodes >> (2 * k)) & 3u) - lbar);
-        const float den = sqrt_rn(div_uniform(vprev[k], ts.inv_bc2p)) + s.eps;
+        const float den = (use_tab && cv) ? dprev[k] : sqrt_rn(div_uniform(vprev[k], ts.inv_bc2p)) + s.eps;
         mprev[k] = (q * ts.bc1p) * den;
       }
     } else {
@@ -864,7 +889,7 @@ turbo_general(const TurboEntry* __restrict__ table, int count, long long tile_ba
   const uint32_t sk0 = (uint32_t)e.seed, sk1 = (uint32_t)(e.seed >> 32);
 
   // ---- second moment: 1Q per block, or FP32
-  float vq[4];
+  float vq[4];       // the persisted second moment, or (tables) its UState denominator
   {
     float lo_c = __builtin_inff(), hi_c = 0.0f;
 #pragma unroll
@@ -887,13 +912,37 @@ turbo_general(const TurboEntry* __restrict__ table, int count, long long tile_ba
       const double lo = f16_to_double(ends & 0xFFFFu), hi = f16_to_double(ends >> 16);
       const float est_lo = f16_decode(ends & 0xFFFFu);
       const float est_scale = (float)(L - 2) / (f16_decode(ends >> 16) - est_lo);
+      if (use_tab) {
+        for (int k = lb; k < L; k += B / 4) {
+          const float a = k ? q1_level(lo, hi, k, L) : 0.0f;
+          enc_tab[k] = make_float2(a, sqrt_rn(div_bc2(a, s)) + s.eps);
+        }
+      }
+      __syncthreads();   // the encode tables built; the index words cleared
       uint32_t field = 0;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const float v = v1[k];
         uint32_t idx = 0;
         float keep = 0.0f;
-        if (valid[k] && v > 0.0f) {
+        if (use_tab) {
+          // the largest level k >= 1 at or below v (1 when none is), by
+          // binary lifting over the sorted table
+          int kk = 1;
+#pragma unroll
+          for (int step = L >> 1; step >= 1; step >>= 1) {
+            const int c = kk + step;
+            kk = (c < L && enc_tab[c < L ? c : L - 1].x <= v) ? c : kk;
+          }
+          const float lk = enc_tab[kk].x, lk1 = enc_tab[kk < L - 1 ? kk + 1 : kk].x;
+          const float f = __fdiv_rn(v - lk, lk1 - lk);
+          const float u = (float)(w[k] >> 8) * 0x1p-24f;
+          const uint32_t up = (kk < L - 1 && v > lk && u < f) ? 1u : 0u;
+          idx = (uint32_t)kk + up;
+          idx = __builtin_isinf(v) ? (uint32_t)(L - 1) : idx;
+          idx = (valid[k] && v > 0.0f) ? idx : 0u;           // zero, negative, NaN
+          keep = enc_tab[idx].y;
+        } else if (valid[k] && v > 0.0f) {
           // the largest level k >= 1 at or below v (1 when none is): from
           // the log2 estimate, moved down while the level is above v and up
           // while the next level is not (levels do not decrease with k)
@@ -923,7 +972,6 @@ turbo_general(const TurboEntry* __restrict__ table, int count, long long tile_ba
         field |= idx << (BITS * k);
       }
       // the tile's index words, assembled in LDS (fields straddle words)
-      __syncthreads();   // words cleared
       const int b0 = 4 * tid * BITS, sh = b0 & 31;
       if (field) {
         atomicOr(&words[b0 >> 5], field << sh);
@@ -950,7 +998,7 @@ turbo_general(const TurboEntry* __restrict__ table, int count, long long tile_ba
     if (cm) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float den = sqrt_rn(div_bc2(vq[k], s)) + s.eps;
+        const float den = (use_tab && cv) ? vq[k] : sqrt_rn(div_bc2(vq[k], s)) + s.eps;
         q[k] = valid[k] ? __fdiv_rn(div_uniform(m1[k], ts.inv_bc1), den) : 0.0f;
       }
     }

@@ -187,11 +187,17 @@ def test_optimizer_skips_nonfinite_updates():
     assert opt.skipped_steps == 2 and opt.step_count == 3 and opt.nonfinite_count() == 0
 
 
-def _turbo_oracle_states(sizes, thr=4096, bits=4):
-    return [oracle.TurboState(n, n >= thr, n >= thr, bits) for n in sizes]
+def _turbo_oracle_states(sizes, thr=4096, bits=4, block=128, group=64):
+    return [oracle.TurboState(n, n >= thr, n >= thr, bits, block, group) for n in sizes]
 
 
-def test_turboadam_optimizer_matches_oracle():
+# (v_bits, block_size, m_block_size): the page's defaults, then two layouts
+# of the general kernel
+TURBO_LAYOUTS = [(4, 128, 64), (3, 256, 16), (6, 64, 64)]
+
+
+@pytest.mark.parametrize("bits,block,group", TURBO_LAYOUTS, ids=lambda x: str(x))
+def test_turboadam_optimizer_matches_oracle(bits, block, group):
     """TurboAdam front end: three steps of every state word and parameter
     against the oracle; tensors below 4096 values keep FP32 moments."""
     import torch
@@ -199,8 +205,9 @@ def test_turboadam_optimizer_matches_oracle():
     sizes = [70000, 4096, 4095, 300, 131072]
     ps = _params(torch, sizes, 21)
     hp = [p.detach().cpu().numpy().copy() for p in ps]
-    opt = TurboAdam(ps, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01)
-    hs = _turbo_oracle_states(sizes)
+    opt = TurboAdam(ps, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01, v_bits=bits, block_size=block,
+                    m_block_size=group)
+    hs = _turbo_oracle_states(sizes, bits=bits, block=block, group=group)
     r = np.random.Generator(np.random.PCG64(22))
     for t in range(1, 4):
         hg = [(r.normal(0, 1e-3, n)).astype(np.float32) for n in sizes]
@@ -226,12 +233,16 @@ def test_turboadam_optimizer_matches_oracle():
             assert_params(ps[i].detach().cpu().numpy(), hp[i])
     assert opt.nonfinite_count() == 0
     n = 131072
-    assert opt._states[4].nbytes() == 106508 == oracle.turbo_state_bytes(1, 1, 4, n)
+    assert opt._states[4].nbytes() == oracle.turbo_state_bytes(1, 1, bits, n, block, group)
+    if (bits, block, group) == (4, 128, 64):
+        assert opt._states[4].nbytes() == 106508
 
 
-def test_turboadam_checkpoint_resume_is_bit_exact():
+@pytest.mark.parametrize("bits,block,group", TURBO_LAYOUTS, ids=lambda x: str(x))
+def test_turboadam_checkpoint_resume_is_bit_exact(bits, block, group):
     import torch
     from adamw_step_amd.optim import TurboAdam
+    lay = dict(v_bits=bits, block_size=block, m_block_size=group)
     sizes = [40000, 5000, 77]
     r = np.random.Generator(np.random.PCG64(23))
     grads = [[torch.from_numpy(r.normal(0, 1e-3, n).astype(np.float32)).cuda() for n in sizes] for _ in range(6)]
@@ -243,18 +254,22 @@ def test_turboadam_checkpoint_resume_is_bit_exact():
             opt.step()
 
     ps_a = _params(torch, sizes, 24)
-    opt_a = TurboAdam(ps_a, lr=1e-3, weight_decay=0.01)
+    opt_a = TurboAdam(ps_a, lr=1e-3, weight_decay=0.01, **lay)
     banner("TurboAdam checkpoint: six straight steps")
     run(ps_a, opt_a, grads)
     ps_b = _params(torch, sizes, 24)
-    opt_b = TurboAdam(ps_b, lr=1e-3, weight_decay=0.01)
+    opt_b = TurboAdam(ps_b, lr=1e-3, weight_decay=0.01, **lay)
     run(ps_b, opt_b, grads[:3])
     buf = io.BytesIO()
     torch.save({"p": [p.detach().cpu() for p in ps_b], "opt": opt_b.state_dict()}, buf)
     buf.seek(0)
     ck = torch.load(buf, weights_only=True)
     ps_c = [torch.nn.Parameter(t.cuda()) for t in ck["p"]]
-    opt_c = TurboAdam(ps_c, lr=1e-3, weight_decay=0.01)
+    if (block, group) != (128, 64):   # a checkpoint of another layout is refused
+        other = TurboAdam([torch.nn.Parameter(t.cuda()) for t in ck["p"]], lr=1e-3, v_bits=bits)
+        with pytest.raises(ValueError):
+            other.load_state_dict(ck["opt"])
+    opt_c = TurboAdam(ps_c, lr=1e-3, weight_decay=0.01, **lay)
     opt_c.load_state_dict(ck["opt"])
     banner("TurboAdam checkpoint: three steps, save, load, three steps")
     run(ps_c, opt_c, grads[3:])
