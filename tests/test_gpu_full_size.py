@@ -191,21 +191,24 @@ def test_llama_7b_grad_stats_exact(pa):
 
 
 @pytest.mark.timeout(900)
-def test_llama_7b_turbo_sampled_tensors(pa):
+@pytest.mark.parametrize("bits,block,group", [(4, 128, 64), (3, 128, 64)], ids=["default", "3bit-general"])
+def test_llama_7b_turbo_sampled_tensors(pa, bits, block, group):
     """The TurboAdam step over the whole 291-tensor list in the benchmark's
     launch configuration; five whole tensors (tensors are independent: each
     has its own draws, groups, blocks and scales) against the oracle for
     three steps, so that codes written with a nonzero scale are decoded: the
     embedding (131 M values, 256 chunks of residual sums), the first RMSNorm
     gain (FP32 moments), the first query and gate projections, and the final
-    norm."""
+    norm.  Once with the tuned kernel at the page's defaults, once with the
+    general kernel at 3-bit indices (the benchmark's --turbo-bits 3)."""
     import torch
     cfg = 4
     sizes = workloads.sizes(cfg)
     banner(f"llama-7b TurboAdam: allocating {sum(sizes) * 8 / 1e9:.1f} GB of params and grads")
     ps = [torch.empty(n, dtype=torch.float32, device="cuda:0") for n in sizes]
     gs = [torch.empty(n, dtype=torch.float32, device="cuda:0") for n in sizes]
-    states = [pa.TurboState(n, "cuda:0", n >= 4096, n >= 4096, 4, tensor_id=i) for i, n in enumerate(sizes)]
+    states = [pa.TurboState(n, "cuda:0", n >= 4096, n >= 4096, bits, tensor_id=i, block_size=block,
+                            m_block_size=group) for i, n in enumerate(sizes)]
     pick = [i for i, (name, _) in enumerate(workloads.shapes(cfg)) if "norm" in name][:1]
     pick += [i for i, (name, _) in enumerate(workloads.shapes(cfg)) if "q_proj" in name][:1]
     pick += [len(sizes) - 2 if "norm" in workloads.shapes(cfg)[-2][0] else len(sizes) - 1]
@@ -213,14 +216,14 @@ def test_llama_7b_turbo_sampled_tensors(pa):
     pick = sorted(set(pick))
     try:
         workloads.device_fill_params(cfg, ps)
-        tl = pa.TurboList(ps, gs, states)
+        tl = pa.TurboList(ps, gs, states, v_bits=bits, block_size=block, m_block_size=group)
         hp = {i: to_host(ps[i]).copy() for i in pick}
-        hs = {i: oracle.TurboState(sizes[i], sizes[i] >= 4096, sizes[i] >= 4096, 4) for i in pick}
+        hs = {i: oracle.TurboState(sizes[i], sizes[i] >= 4096, sizes[i] >= 4096, bits, block, group) for i in pick}
         for t in (1, 2, 3):
             workloads.device_fill_grads(cfg, t, gs)
             torch.cuda.synchronize()
             hg = {i: to_host(gs[i]).copy() for i in pick}
-            banner(f"llama-7b TurboAdam step {t}: one launch over 291 tensors")
+            banner(f"llama-7b TurboAdam ({bits} bits, {block}/{group}) step {t}: one launch over 291 tensors")
             tl.step(dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01), t)
             torch.cuda.synchronize()
             sc = scalars(t)
