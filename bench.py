@@ -23,8 +23,8 @@ Other flags:
                           gpt-11m model (trainer/) with each optimizer and
                           report the optimizer's share of the step
   --layout plain          allocate parameters, gradients and state back to
-                          back (default: state one HBM region below the
-                          parameters, see build_workload)
+                          back, as PackedAdamW does (default: state one HBM
+                          region below the parameters, see build_workload)
   --mode turbo            the TurboAdam compressed-state step (UState first
                           moment, 4-bit 1Q second moment; tensors below 4096
                           values keep FP32 moments, as the page's thresholds)
@@ -110,11 +110,12 @@ def time_probe(fn, reps):
     return sorted(ts)[len(ts) // 2]
 
 
-def step_layout_ceilings(L, stream_bytes):
+def step_layout_ceilings(L, stream_bytes, layout="regions"):
     """Ceilings of the packed step's traffic on this HBM, in the benchmark's
     layout: three streams of `stream_bytes` (the step's p, g and w), the
     first two at the start of device memory and the third one HBM region
-    further on in allocation order.
+    further on in allocation order (layout "regions"), or all three back to
+    back (layout "plain").
 
     This library's probes (libpa_probe.so, one tile per workgroup in tile
     order, as the step): a nontemporal read of one stream, a write of one
@@ -133,7 +134,9 @@ def step_layout_ceilings(L, stream_bytes):
     n16 = stream_bytes // 16
     a = torch.zeros(stream_bytes // 4, dtype=torch.float32, device="cuda:0")
     b = torch.zeros_like(a)
-    spacer = torch.empty(max(region_bytes() - 2 * stream_bytes, 0), dtype=torch.uint8, device="cuda:0")
+    spacer = None
+    if layout == "regions":
+        spacer = torch.empty(max(region_bytes() - 2 * stream_bytes, 0), dtype=torch.uint8, device="cuda:0")
     c = torch.zeros_like(a)
     del spacer
     torch.cuda.empty_cache()
@@ -211,8 +214,11 @@ def build_blockwise(cfg, layout="regions"):
 def region_bytes():
     """One HBM region: a third of the device memory.  Measured on MI355X
     (288 GB of HBM3E): in allocation order the device memory falls into three
-    equal regions, and the step runs about 13% faster when its written
-    streams (parameters and state) lie in different regions."""
+    equal regions; with a persistent launch the step ran about 13% faster
+    when its written streams (parameters and state) lay in different
+    regions.  With one tile per workgroup the layouts converge after a few
+    processes on a box, but in the first ones the back-to-back layout still
+    runs up to 10% slower."""
     import torch
     return torch.cuda.get_device_properties(0).total_memory // 3
 
@@ -657,7 +663,7 @@ def main():
         del ps, gs, states
         prepared = None              # it holds the tensors too
         torch.cuda.empty_cache()
-        out["probes"] = step_layout_ceilings(probe_lib(), 4 * n_params)
+        out["probes"] = step_layout_ceilings(probe_lib(), 4 * n_params, args.layout)
         log(f"probes: {out['probes']}")
     if not args.no_cpu_baseline and not args.probe and args.param_dtype == "fp32":
         log("timing the CPU oracle on a bounded sample")
@@ -673,7 +679,7 @@ def main():
         torch.cuda.empty_cache()
         try:
             import adamw_step_amd as _p  # noqa: F401
-            ceil = step_layout_ceilings(probe_lib(), 4 * n_params)
+            ceil = step_layout_ceilings(probe_lib(), 4 * n_params, args.layout)
             ceil["frac_of_traffic_probe"] = round(achieved / ceil["mix_3r2w_gbps"], 4)
             ceil["frac_of_traffic_and_valu_probe"] = round(achieved / ceil["mix_3r2w_80valu_gbps"], 4)
             ceil["frac_of_read_then_write_bound"] = round(achieved / ceil["read_then_write_bound_gbps"], 4)
