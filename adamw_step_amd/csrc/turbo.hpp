@@ -730,45 +730,30 @@ __device__ __forceinline__ float q1_level(double lo, double hi, int k, int L) {
   return a;
 }
 
-// Six wavefronts per SIMD: measured faster than the five the registers
-// allow unasked (4-6% at table layouts) and than seven or eight, where the
-// spills grow.
-template <int BITS, bool COUNT>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6)))
-turbo_general(const TurboEntry* __restrict__ table, int count, long long tile_base, Scalars s, TurboScalars ts,
-              int blog, int glog, double* ws, unsigned long long* nonfinite) {
+// One 1024-value tile of the general step (the workgroup's), its LDS
+// passed in.  FULL: the tile lies wholly inside its tensor, so every
+// validity test folds away (the partial copy runs on a tensor's last tile).
+template <int BITS, bool FULL>
+__device__ __forceinline__ void general_tile(const TurboEntry* __restrict__ ep, long long local, const Scalars& s,
+                                             const TurboScalars& ts, int blog, int glog, double* ws, uint32_t& bad,
+                                             uint32_t* words, float2* tabs, uint32_t* eslot, float* fslot,
+                                             double* dslot, int* islot) {
   constexpr int L = 1 << BITS;
   constexpr int kWords = kGenTile * BITS / 32;       // index words of a tile
-  __shared__ uint32_t words[kWords];
-  __shared__ float2 tabs[2][kGenTile];               // decode, encode tables (L <= B)
-  __shared__ uint32_t eslot[2 * kGenTile / 32];      // each block's two endpoints
-  __shared__ float fslot[4];
-  __shared__ double dslot[4];
-  __shared__ int islot[4];
-  if (!resolve_inputs(s)) return;   // uniform: before any barrier
-  const long long tile = tile_base + blockIdx.x;
-  int lo_t = 0, hi_t = count - 1;                    // the last entry with tile0 <= tile
-  while (lo_t < hi_t) {
-    const int mid = (lo_t + hi_t + 1) >> 1;
-    if (table[mid].tile0 <= tile) lo_t = mid;
-    else hi_t = mid - 1;
-  }
-  const TurboEntry& e = table[lo_t];
+  const TurboEntry& e = *ep;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const long long local = tile - e.tile0;
   const long long i0 = local * kGenTile + 4 * tid;  // this thread's first value
   const long long n = e.n;
   const bool cm = e.flags & 1, cv = e.flags & 2;
   const int B = 1 << blog, G = 1 << glog;
   const bool use_tab = L <= B;                       // uniform
   const int lb = tid & (B / 4 - 1);                  // lane within the block
-  float2* const dec_tab = tabs[0] + ((4 * tid) >> blog) * L;
-  float2* const enc_tab = tabs[1] + ((4 * tid) >> blog) * L;
+  float2* const dec_tab = tabs + ((4 * tid) >> blog) * L;
+  float2* const enc_tab = tabs + kGenTile + ((4 * tid) >> blog) * L;
   bool valid[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) valid[k] = i0 + k < n;
-  const bool full = valid[3];
-  uint32_t bad = 0;
+  for (int k = 0; k < 4; ++k) valid[k] = FULL || i0 + k < n;
+  const bool full = FULL || valid[3];
   for (int j = tid; j < kWords; j += kThreads) words[j] = 0u;
 
   // ---- loads
@@ -790,7 +775,7 @@ turbo_general(const TurboEntry* __restrict__ table, int count, long long tile_ba
     }
   }
   const long long blk = i0 >> blog;                  // 1Q block of this thread's values
-  const bool blk_exists = (blk << blog) < n;
+  const bool blk_exists = FULL || (blk << blog) < n;
   const float s_dec = cm ? e.scal[0] : 0.0f, s_enc = cm ? e.scal[1] : 0.0f;
 
   // ---- decode the prior moments (the state is empty at step 1)
@@ -1059,6 +1044,36 @@ turbo_general(const TurboEntry* __restrict__ table, int count, long long tile_ba
         if (valid[k]) e.m_fp32[i0 + k] = m1[k];
     }
   }
+}
+
+// Six wavefronts per SIMD: measured faster than the five the registers
+// allow unasked (4-6% at table layouts) and than seven or eight, where the
+// spills grow.
+template <int BITS, bool COUNT>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6)))
+turbo_general(const TurboEntry* __restrict__ table, int count, long long tile_base, Scalars s, TurboScalars ts,
+              int blog, int glog, double* ws, unsigned long long* nonfinite) {
+  __shared__ uint32_t words[kGenTile * BITS / 32];   // the tile's index words
+  __shared__ float2 tabs[2 * kGenTile];              // decode, encode tables (L <= B)
+  __shared__ uint32_t eslot[2 * kGenTile / 32];      // each block's two endpoints
+  __shared__ float fslot[4];
+  __shared__ double dslot[4];
+  __shared__ int islot[4];
+  if (!resolve_inputs(s)) return;   // uniform: before any barrier
+  const long long tile = tile_base + blockIdx.x;
+  int lo_t = 0, hi_t = count - 1;                    // the last entry with tile0 <= tile
+  while (lo_t < hi_t) {
+    const int mid = (lo_t + hi_t + 1) >> 1;
+    if (table[mid].tile0 <= tile) lo_t = mid;
+    else hi_t = mid - 1;
+  }
+  const TurboEntry* ep = table + lo_t;
+  const long long local = tile - ep->tile0;
+  uint32_t bad = 0;
+  if ((local + 1) * kGenTile <= ep->n)
+    general_tile<BITS, true>(ep, local, s, ts, blog, glog, ws, bad, words, tabs, eslot, fslot, dslot, islot);
+  else
+    general_tile<BITS, false>(ep, local, s, ts, blog, glog, ws, bad, words, tabs, eslot, fslot, dslot, islot);
   if constexpr (COUNT) flush_count(bad, nonfinite);
 }
 
