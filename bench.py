@@ -53,9 +53,12 @@ sys.path.insert(0, ROOT)
 
 METRIC = "packed-AdamW step: params/s and achieved HBM GB/s (% of 8 TB/s) at 7B"
 PEAK_GBPS = 8000.0
-# VALU issue peak of MI355X: 256 CUs x 64 lanes (one wave64 vector
-# instruction per CU per cycle) x 2.4 GHz, in G lane-instructions per second.
-PEAK_VALU_GLANE = 256 * 64 * 2.4
+# Vector ALU peak of MI355X in G lane-operations per second: its FP32
+# vector rate, 157.3 TFLOP/s (256 CUs x 2.4 GHz x 256 flops), counting a
+# lane's FMA as two flops, so 128 lane-operations per CU per clock.  One
+# wave64 instruction per SIMD every four cycles (half of this) is not a
+# ceiling on gfx950: the general TurboAdam kernel's counters exceed it.
+PEAK_VALU_GLANE = 256 * 128 * 2.4
 BYTES_PER_PARAM = {"e4": 20, "fp16": 20, "fp32": 28, "blockwise8": 14, "gradstats": 4, "turbo": None}
 WORKLOADS = {"single-262k": 1, "gpt-11m": 2, "gpt2-small-124m": 3, "llama-7b": 4, "blockwise-268m": 5}
 # Device sources each kernel family is compiled from: a stored counter
