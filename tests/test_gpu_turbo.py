@@ -146,16 +146,22 @@ def test_turbo_large_tensor(pa):
     _run(pa, [1 << 20, 3 * 65536 + 11], [(True, True), (True, True)], 4, steps=3, seed=9)
 
 
-def test_turbo_skip_and_scale(pa):
+# (v_bits, block, group, general kernel): the tuned kernel at the defaults,
+# the general kernel at the defaults and at a 3-bit, 64/8 layout
+PATHS = [(4, 128, 64, False), (4, 128, 64, True), (3, 64, 8, True)]
+
+
+@pytest.mark.parametrize("bits,block,group,general", PATHS, ids=lambda x: str(x))
+def test_turbo_skip_and_scale(pa, bits, block, group, general):
     import torch
     n = 5000
     r = np.random.default_rng(3)
     hp = r.normal(0, 0.02, n).astype(np.float32)
     dp = to_dev(hp)
-    hs = oracle.TurboState(n)
-    ds = pa.TurboState(n, "cuda:0")
+    hs = oracle.TurboState(n, True, True, bits, block, group)
+    ds = pa.TurboState(n, "cuda:0", True, True, bits, block_size=block, m_block_size=group)
     g = to_dev(r.normal(0, 1e-3, n).astype(np.float32))
-    tl = pa.TurboList([dp], [g], [ds])
+    tl = pa.TurboList([dp], [g], [ds], v_bits=bits, block_size=block, m_block_size=group, general=general)
     scale = torch.tensor([0.25], dtype=torch.float32, device="cuda:0")
     flag = torch.tensor([1], dtype=torch.int64, device="cuda:0")
     banner("turbo: skipped step")
@@ -191,7 +197,8 @@ def _same_bf16(got, want):
     return _same_f32(wide(got), wide(want))
 
 
-def test_turbo_nonfinite_gradients(pa):
+@pytest.mark.parametrize("bits,block,group,general", PATHS, ids=lambda x: str(x))
+def test_turbo_nonfinite_gradients(pa, bits, block, group, general):
     """NaN and infinite gradients: the 1Q and UState codes follow the
     readings (NaN and zero to index 0 and code 0, +Inf to the top index)
     exactly; floating results compare by NaN class, since a NaN's sign and
@@ -202,10 +209,11 @@ def test_turbo_nonfinite_gradients(pa):
     r = np.random.default_rng(17)
     hp = [r.normal(0, 0.02, n).astype(np.float32) for n in sizes]
     dp = [to_dev(a) for a in hp]
-    hs = [oracle.TurboState(n, cm, cv, 4) for n, (cm, cv) in zip(sizes, flags)]
-    ds = [pa.TurboState(n, "cuda:0", cm, cv, 4, tensor_id=i) for i, (n, (cm, cv)) in enumerate(zip(sizes, flags))]
+    hs = [oracle.TurboState(n, cm, cv, bits, block, group) for n, (cm, cv) in zip(sizes, flags)]
+    ds = [pa.TurboState(n, "cuda:0", cm, cv, bits, tensor_id=i, block_size=block, m_block_size=group)
+          for i, (n, (cm, cv)) in enumerate(zip(sizes, flags))]
     grads = [torch.zeros(n, dtype=torch.float32, device="cuda:0") for n in sizes]
-    tl = pa.TurboList(dp, grads, ds)
+    tl = pa.TurboList(dp, grads, ds, v_bits=bits, block_size=block, m_block_size=group, general=general)
     counter = torch.zeros(1, dtype=torch.int64, device="cuda:0")
     total_bad = 0
     for t in (1, 2, 3):
@@ -338,7 +346,8 @@ def test_level_rounding_adversarial_exponents(pa):
         assert bad.size == 0, f"exact={exact}: {bad.size} differ, first x={xs[bad[0]]!r}: {got[bad[0]]!r} vs {want[bad[0]]!r}"
 
 
-def test_turbo_residual_tree_past_one_chunk_level(pa):
+@pytest.mark.parametrize("general", [False, True], ids=["tuned", "general"])
+def test_turbo_residual_tree_past_one_chunk_level(pa, general):
     """A UState tensor of 2^30 + 12,345 values has 4,194,353 tile sums and
     2,049 chunk sums, so the scale's tree takes the chunk pass and two
     levels of the per-tensor pass.  The new scale must equal the perfect
@@ -351,7 +360,7 @@ def test_turbo_residual_tree_past_one_chunk_level(pa):
     p = torch.randn(n, generator=gen, device="cuda:0") * 0.02
     g = torch.randn(n, generator=gen, device="cuda:0") * 1e-3
     st = pa.TurboState(n, "cuda:0", True, True, 4, tensor_id=5)
-    tl = pa.TurboList([p], [g], [st])
+    tl = pa.TurboList([p], [g], [st], general=general)
     try:
         tl.step(H, 1)
         torch.cuda.synchronize()
