@@ -171,7 +171,10 @@ int pa_step(int mode, float* params, const float* grads, void* state, size_t n,
  * 2^22).  Blockwise mode: one launch per tensor.  params[i], grads[i],
  * states[i] and n[i] describe tensor i exactly as for pa_step.  The table is
  * uploaded once per distinct pointer/size list and cached (see
- * pa_release_plans).  Tensors of length 0 are skipped. */
+ * pa_release_plans).  Tensors of length 0 are skipped.  Once a list's table
+ * exists, a call enqueues its kernel launch and nothing else (no allocation,
+ * copy, memset or synchronisation), so it can be captured in a HIP graph;
+ * a captured call keeps the step and scalars it was captured with. */
 int pa_step_list(int mode, size_t count, float* const* params, const float* const* grads,
                  void* const* states, const size_t* n, const pa_hyper* hyper, long long step,
                  void* stream);
