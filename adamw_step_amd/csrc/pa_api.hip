@@ -72,7 +72,6 @@ struct DeviceInfo {
   int blocks_per_cu = 0;      // elementwise kernels
   int bw_blocks_per_cu = 0;   // blockwise kernel
   int stats_blocks_per_cu = 0;   // gradient pre-pass
-  int turbo_blocks_per_cu[3] = {0, 0, 0};   // TurboAdam step, 2-, 4- and 8-bit indices
 };
 
 std::mutex g_dev_mu;
@@ -106,14 +105,6 @@ int device_info(int* dev_out, DeviceInfo* info) {
         &st, reinterpret_cast<const void*>(pa::grad_stats_list<pa::kF32, true>), pa::kThreads, 0);
     if (e != hipSuccess || st < 1) st = 4;
     d.stats_blocks_per_cu = st;
-    const void* turbo[3] = {reinterpret_cast<const void*>(pa::turbo_list<2, false>),
-                            reinterpret_cast<const void*>(pa::turbo_list<4, false>),
-                            reinterpret_cast<const void*>(pa::turbo_list<8, false>)};
-    for (int i = 0; i < 3; ++i) {
-      int tb = 0;
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&tb, turbo[i], pa::kThreads, 0);
-      d.turbo_blocks_per_cu[i] = (e != hipSuccess || tb < 1) ? 2 : tb;
-    }
   }
   *dev_out = dev;
   *info = d;
@@ -698,18 +689,24 @@ hipError_t launch_turbo_reduce(const TurboPlan& pl, const pa::Scalars& s, double
   return hipGetLastError();
 }
 
+// The tuned kernel: one wavefront per 256-value tile, four per workgroup,
+// in launches of at most kMaxLaunchTiles workgroups.
 template <int BITS>
 hipError_t launch_turbo(const TurboPlan& pl, const pa::Scalars& s, const pa::TurboScalars& ts, double* ws,
-                        unsigned long long* nf, double factor, hipStream_t st, const DeviceInfo& d) {
-  const long long wgs = (pl.tiles + pa::kThreads / 64 - 1) / (pa::kThreads / 64);
-  const dim3 grid((unsigned)grid_for(wgs, d, d.turbo_blocks_per_cu[BITS == 2 ? 0 : BITS == 4 ? 1 : 2])),
-      block(pa::kThreads);
-  if (nf)
-    hipLaunchKernelGGL((pa::turbo_list<BITS, true>), grid, block, 0, st, pl.table, pl.tiles, s, ts, ws, nf);
-  else
-    hipLaunchKernelGGL((pa::turbo_list<BITS, false>), grid, block, 0, st, pl.table, pl.tiles, s, ts, ws, nf);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+                        unsigned long long* nf, double factor, hipStream_t st) {
+  constexpr long long kWaves = pa::kThreads / 64;
+  const long long wgs = (pl.tiles + kWaves - 1) / kWaves;
+  for (long long w0 = 0; w0 < wgs; w0 += kMaxLaunchTiles) {
+    const long long nw = std::min(kMaxLaunchTiles, wgs - w0);
+    if (nf)
+      hipLaunchKernelGGL((pa::turbo_list<BITS, true>), dim3((unsigned)nw), dim3(pa::kThreads), 0, st, pl.table,
+                         pl.count, pl.tiles, w0 * kWaves, s, ts, ws, nf);
+    else
+      hipLaunchKernelGGL((pa::turbo_list<BITS, false>), dim3((unsigned)nw), dim3(pa::kThreads), 0, st, pl.table,
+                         pl.count, pl.tiles, w0 * kWaves, s, ts, ws, nf);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   return launch_turbo_reduce(pl, s, ws, factor, st);
 }
 
@@ -1251,9 +1248,9 @@ int pa_turbo_step_list(size_t count, float* const* params, const float* const* g
     }
   } else {
     switch (lay.bits) {
-      case 2: e = launch_turbo<2>(*it, s, ts, ws, nf, f, st, d); break;
-      case 4: e = launch_turbo<4>(*it, s, ts, ws, nf, f, st, d); break;
-      default: e = launch_turbo<8>(*it, s, ts, ws, nf, f, st, d); break;
+      case 2: e = launch_turbo<2>(*it, s, ts, ws, nf, f, st); break;
+      case 4: e = launch_turbo<4>(*it, s, ts, ws, nf, f, st); break;
+      default: e = launch_turbo<8>(*it, s, ts, ws, nf, f, st); break;
     }
   }
   return e == hipSuccess ? PA_OK : hip_failed(e);

@@ -270,30 +270,23 @@ constexpr int kDecodeTable = 128;
 // correction of the step that persisted it, r = RN64(1/bc)).  A block's
 // persisted values are its levels, so each denominator is computed once per
 // level instead of once per value; it is the same correctly rounded
-// function of the same input either way.
-//
-// Lanes 0..L-1 of each half build the table of `ends` at lev (reciprocal
-// r), and, when `two`, lanes 16..16+L-1 build the table of `ends2` at lev2
-// (reciprocal r2) in the same pass.  The encode pass of a tile thus also
-// builds the decode table of the wavefront's next tile on lanes that would
-// otherwise idle.
+// function of the same input either way.  Lanes 0..L-1 of each half build
+// the table of `ends` at lev.
 template <int BITS>
-__device__ __attribute__((noinline)) void build_tables(lds_float* lev, uint32_t ends, double r, lds_float* lev2,
-                                                       uint32_t ends2, double r2, bool two, float eps, int lane_in_half) {
+__device__ __attribute__((noinline)) void build_tables(lds_float* lev, uint32_t ends, double r, float eps,
+                                                       int lane_in_half) {
   constexpr int L = 1 << BITS;
   static_assert(L <= 16, "one level per lane");
-  const bool second = lane_in_half >= 16;
-  const int k = lane_in_half & 15;
-  if (k >= L || (second && !two)) return;
+  const int k = lane_in_half;
+  if (k >= L) return;
   float a = 0.0f;
   if (k > 0) {
-    const uint32_t w = second ? ends2 : ends;
-    const double x = q1_level_x(f16_to_double(w & 0xFFFFu), f16_to_double(w >> 16), k, L);
+    const double x = q1_level_x(f16_to_double(ends & 0xFFFFu), f16_to_double(ends >> 16), k, L);
     if (!q1_level_fast(x, &a)) a = pow2_rn32_dd(x);
   }
-  lds_float* dst = (second ? lev2 : lev) + 2 * k;
+  lds_float* dst = lev + 2 * k;
   dst[0] = a;
-  dst[1] = sqrt_rn(div_uniform(a, second ? r2 : r)) + eps;
+  dst[1] = sqrt_rn(div_uniform(a, r)) + eps;
 }
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -352,14 +345,9 @@ __device__ __forceinline__ void store_index4(uint8_t* base, long long lane_word,
 // FULL: the tile lies wholly inside its tensor, so every validity test below
 // folds away (one instantiation per case; the partial one runs only on a
 // tensor's last tile).
-// With indices of at most 4 bits, `have_dec` says the decode table is
-// already in the slice (built by the previous tile's encode pass), and
-// `next_dec` asks this tile's encode pass to build the next tile's from the
-// endpoint word `next_ends`.
 template <int BITS, bool FULL>
 __device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, long long tile, const Scalars& s,
-                                           const TurboScalars& ts, float* lev_half, double* ws, uint32_t& bad,
-                                           bool have_dec, bool next_dec, uint32_t next_ends) {
+                                           const TurboScalars& ts, float* lev_half, double* ws, uint32_t& bad) {
   const TurboEntry& e = *ep;
   constexpr int L = 1 << BITS;
   const int lane = threadIdx.x & 63;
@@ -415,10 +403,10 @@ __device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, lo
   if (ts.step > 1) {
     if (cv) {
       float* dec = BITS <= 4 ? lev_half + kDecodeTable : lev_half;
-      if (BITS > 4 || !have_dec) {
+      {
         const uint32_t ends = blk_exists ? *reinterpret_cast<const uint32_t*>(e.v_ends + 2 * blk) : 0u;
         if constexpr (BITS <= 4)
-          build_tables<BITS>((lds_float*)dec, ends, ts.inv_bc2p, (lds_float*)dec, 0u, 0.0, false, s.eps, lane_in_half);
+          build_tables<BITS>((lds_float*)dec, ends, ts.inv_bc2p, s.eps, lane_in_half);
         else
           build_levels<BITS>((lds_float*)dec, ends, lane_in_half);
         wave_lds_sync();
@@ -515,8 +503,7 @@ __device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, lo
     const uint32_t lo16 = (uint32_t)__shfl((int)e16, src, 64), hi16 = (uint32_t)__shfl((int)e16, src + 1, 64);
     const uint32_t ends = vmax > 0.0f ? (lo16 | (hi16 << 16)) : 0u;
     if constexpr (BITS <= 4)
-      build_tables<BITS>((lds_float*)lev_half, ends, s.inv_bc2, (lds_float*)(lev_half + kDecodeTable), next_ends,
-                         ts.inv_bc2p, next_dec, s.eps, lane_in_half);
+      build_tables<BITS>((lds_float*)lev_half, ends, s.inv_bc2, s.eps, lane_in_half);
     else
       build_levels<BITS>((lds_float*)lev_half, ends, lane_in_half);
     // level k of the encode table
@@ -632,55 +619,37 @@ __device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, lo
   }
 }
 
-// Persistent launch: global wavefront w takes tiles w, w + W, ...; each
-// wavefront keeps its own cursor in the tensor table (sentinel-terminated).
+// One tile per wavefront, in dispatch order: wavefront w of the launch takes
+// tile tile_base + w, so the tiles in flight form one compact window that
+// advances through the list (faster than a persistent grid striding over
+// the tiles: the hardware starts each new wavefront as one finishes, and
+// its loads overlap the work of the wavefronts around it).  The tile's
+// tensor is found by a bisection over the table's first tiles.
 template <int BITS, bool COUNT>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BITS <= 4 ? 7 : 6)))
-turbo_list(const TurboEntry* __restrict__ table, long long total_tiles, Scalars s, TurboScalars ts, double* ws,
-           unsigned long long* nonfinite) {
+turbo_list(const TurboEntry* __restrict__ table, int count, long long total_tiles, long long tile_base, Scalars s,
+           TurboScalars ts, double* ws, unsigned long long* nonfinite) {
   __shared__ float lev[kThreads / 64][2][256];
   if (!resolve_inputs(s)) return;
   // The wavefront index is uniform across the wavefront; saying so lets the
-  // compiler keep the tile, the table cursor and every field of the entry
+  // compiler keep the tile, the table search and every field of the entry
   // in scalar registers (scalar loads, the Philox key schedule on the
   // scalar unit) instead of repeating them in every lane.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), half = (threadIdx.x >> 5) & 1;
-  const long long gw = (long long)blockIdx.x * (kThreads / 64) + wave;
-  const long long nw = (long long)gridDim.x * (kThreads / 64);
+  const long long tile = tile_base + (long long)blockIdx.x * (kThreads / 64) + wave;
   uint32_t bad = 0;
-  int t = 0;
-  if (gw < total_tiles)
-    while (gw >= table[t + 1].tile0) ++t;
-  bool have_dec = false;   // the decode table of this tile is in the slice
-  for (long long tile = gw; tile < total_tiles; tile += nw) {
-    const long long local = tile - table[t].tile0;
-    // The wavefront's next tile: its entry, and (indices of at most 4 bits,
-    // step > 1, both tensors with 1Q state) the endpoints of its block, so
-    // that this tile's encode pass builds its decode table.
-    const long long nt = tile + nw;
-    int u = t;
-    bool next_dec = false;
-    uint32_t next_ends = 0u;
-    if constexpr (BITS <= 4) {
-      if (nt < total_tiles)
-        while (nt >= table[u + 1].tile0) ++u;
-      if (ts.step > 1 && nt < total_tiles && (table[t].flags & 2) && (table[u].flags & 2)) {
-        next_dec = true;
-        const long long nblk = (nt - table[u].tile0) * (kTurboTile / kTurboBlock) + half;
-        if (nblk * kTurboBlock < table[u].n)
-          next_ends = *reinterpret_cast<const uint32_t*>(table[u].v_ends + 2 * nblk);
-      }
+  if (tile < total_tiles) {
+    int lo = 0, hi = count - 1;                      // the last entry with tile0 <= tile
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (table[mid].tile0 <= tile) lo = mid;
+      else hi = mid - 1;
     }
-    if ((local + 1) * kTurboTile <= table[t].n)
-      turbo_tile<BITS, true>(table + t, local, s, ts, lev[wave][half], ws, bad, have_dec, next_dec, next_ends);
+    const long long local = tile - table[lo].tile0;
+    if ((local + 1) * kTurboTile <= table[lo].n)
+      turbo_tile<BITS, true>(table + lo, local, s, ts, lev[wave][half], ws, bad);
     else
-      turbo_tile<BITS, false>(table + t, local, s, ts, lev[wave][half], ws, bad, have_dec, next_dec, next_ends);
-    have_dec = next_dec;
-    if constexpr (BITS <= 4) {
-      t = u;
-    } else if (nt < total_tiles) {
-      while (nt >= table[t + 1].tile0) ++t;
-    }
+      turbo_tile<BITS, false>(table + lo, local, s, ts, lev[wave][half], ws, bad);
   }
   if constexpr (COUNT) flush_count(bad, nonfinite);
 }
@@ -1209,7 +1178,7 @@ __global__ void __launch_bounds__(kThreads) q1_levels_kernel(const uint32_t* end
       continue;
     }
     if constexpr (BITS <= 4)
-      build_tables<BITS>((lds_float*)t, word, 1.0, (lds_float*)t, 0u, 1.0, false, 0.0f, lane_in_half);
+      build_tables<BITS>((lds_float*)t, word, 1.0, 0.0f, lane_in_half);
     else
       build_levels<BITS>((lds_float*)t, word, lane_in_half);
     wave_lds_sync();

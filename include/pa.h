@@ -322,8 +322,8 @@ size_t pa_turbo_workspace_bytes(size_t count, const pa_turbo_state* states, cons
 
 /* One TurboAdam step over `count` tensors sharing hyper, config and step
  * (1 to 2^32 - 1, counting this update; PA_ERR_ARG outside): one launch over
- * all tensors (the tuned kernel: a persistent grid, a wavefront per 256
- * values; the general one: a workgroup per 1024 values), then one
+ * all tensors (the tuned kernel: a wavefront per 256 values; the general
+ * one: a workgroup per 1024 values; both in dispatch order), then one
  * workgroup per 2048 residual partial sums and one per UState tensor that
  * completes the sum and rotates its scales.  `states` is a host array of count
  * descriptors; `workspace` a device buffer of at least
