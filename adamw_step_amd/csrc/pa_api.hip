@@ -611,8 +611,8 @@ long long turbo_chunks_of(long long tiles) { return (tiles + pa::kTurboChunk - 1
 
 // A layout the page's fused path takes: 2, 3, 4, 6 or 8 index bits, a
 // power-of-two 1Q block from 32 to 1024 values, a power-of-two UState group
-// dividing it.  The tuned kernel (turbo_list) covers 128-value blocks,
-// 64-value groups and 2, 4 or 8 bits; turbo_general covers all of them.
+// dividing it.  The tuned kernel (turbo_list) covers 128-value blocks and
+// 64-value groups at every width; turbo_general covers every layout.
 struct TurboLayout {
   int bits = 4, block = 128, group = 64;
   bool general = false;
@@ -631,7 +631,7 @@ int turbo_layout(const pa_turbo_config* c, TurboLayout* out) {
   out->block = c->block_size ? c->block_size : 128;
   out->group = c->m_block_size ? c->m_block_size : 64;
   if (!layout_ok(out->bits, out->block, out->group) || (c->path != 0 && c->path != 1)) return PA_ERR_ARG;
-  out->general = c->path == 1 || out->block != 128 || out->group != 64 || out->bits == 3 || out->bits == 6;
+  out->general = c->path == 1 || out->block != 128 || out->group != 64;
   return PA_OK;
 }
 
@@ -1249,7 +1249,9 @@ int pa_turbo_step_list(size_t count, float* const* params, const float* const* g
   } else {
     switch (lay.bits) {
       case 2: e = launch_turbo<2>(*it, s, ts, ws, nf, f, st); break;
+      case 3: e = launch_turbo<3>(*it, s, ts, ws, nf, f, st); break;
       case 4: e = launch_turbo<4>(*it, s, ts, ws, nf, f, st); break;
+      case 6: e = launch_turbo<6>(*it, s, ts, ws, nf, f, st); break;
       default: e = launch_turbo<8>(*it, s, ts, ws, nf, f, st); break;
     }
   }

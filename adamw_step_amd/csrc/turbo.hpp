@@ -219,8 +219,8 @@ typedef __attribute__((address_space(3))) float lds_float;
 // left undecided are redone afterwards in one rolled loop, so that the
 // double-double code appears once and its registers stay few.
 //
-// 8-bit tables (L = 256): lane j of a half builds levels j, j + 32, ...,
-// j + 224 (lane 0 starts at 32; level 0 is 0).  The levels form a geometric
+// 6- and 8-bit tables (L = 64, 256): lane j of a half builds levels j,
+// j + 32, ..., below L (lane 0 starts at 32; level 0 is 0).  The levels form a geometric
 // grid, so after its first level y = exp2(x_k0) the lane multiplies by
 // C = exp2(32 d), d = RN64((hi - lo) / (L - 2)), instead of calling exp2
 // for each level.  Level k is the exact power 2^x_k of its own double x_k
@@ -235,7 +235,7 @@ typedef __attribute__((address_space(3))) float lds_float;
 template <int BITS>
 __device__ __attribute__((noinline)) void build_levels(lds_float* lev, uint32_t ends, int lane_in_half) {
   constexpr int L = 1 << BITS;
-  static_assert(L == 256, "32 lanes, 8 levels each");
+  static_assert(L == 64 || L == 256, "32 lanes, L / 32 levels each");
   const double lo = f16_to_double(ends & 0xFFFFu), hi = f16_to_double(ends >> 16);
   const int k0 = lane_in_half == 0 ? 32 : lane_in_half;
   if (lane_in_half == 0) lev[0] = 0.0f;
@@ -244,7 +244,7 @@ __device__ __attribute__((noinline)) void build_levels(lds_float* lev, uint32_t 
   const bool in_range = __builtin_fabs(lo) <= 256.0 && __builtin_fabs(hi) <= 256.0;
   uint32_t undecided = 0;   // bit j: level k0 + 32 j
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < L / 32; ++j) {
     const int k = k0 + 32 * j;
     if (k >= L) break;
     const float a = (float)(y * (1.0 - 0x1p-40)), b = (float)(y * (1.0 + 0x1p-40));
@@ -332,6 +332,48 @@ __device__ __forceinline__ uint32_t load_index4(const uint8_t* base, long long l
   else return reinterpret_cast<const uint32_t*>(base)[lane_word];
 }
 
+// The 4 * BITS-bit field of values i0..i0+3 of a dense little-endian index
+// stream of n values.  Widths that straddle 32-bit words (3, 6) read the
+// word holding the field's first bit and, when the field's valid bits reach
+// it, the next one.
+template <int BITS>
+__device__ __forceinline__ uint32_t load_field(const uint8_t* base, long long i0, long long n) {
+  if constexpr (BITS == 2 || BITS == 4 || BITS == 8) {
+    return load_index4<BITS>(base, i0 >> 2);
+  } else {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(base);
+    const long long b0 = i0 * BITS, b_end = (i0 + 4 < n ? i0 + 4 : n) * BITS;
+    const long long w0 = b0 >> 5;
+    unsigned long long both = w[w0];
+    if (b_end > (w0 + 1) * 32) both |= (unsigned long long)w[w0 + 1] << 32;
+    return (uint32_t)(both >> (b0 & 31)) & ((1u << (4 * BITS)) - 1u);
+  }
+}
+
+// For widths that straddle words (3, 6): the 128 indices of the
+// half-wavefront's block as its 4 * BITS dense words, each gathered by
+// shuffles from the (at most 32 / (4 * BITS) + 2) lane fields it overlaps,
+// and stored by the half's first 4 * BITS lanes (words past the stream's
+// end are not written).  Called by every lane of the wavefront.
+template <int BITS>
+__device__ __forceinline__ void store_fields_dense(uint8_t* base, long long blk, long long n, uint32_t field, int half,
+                                                   int lane_in_half) {
+  constexpr int F = 4 * BITS;                       // field bits per lane, and words per block
+  constexpr int Q = 32 / F + 2;
+  const int w = lane_in_half;
+  const int first = (32 * w) / F;
+  uint32_t word = 0;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int src = first + q;
+    const uint32_t f = (uint32_t)__shfl((int)field, (half << 5) + (src < 32 ? src : 31), 64);
+    const int off = src * F - 32 * w;               // the field's first bit, relative to the word
+    if (src < 32 && off < 32 && off + F > 0) word |= off >= 0 ? f << off : f >> -off;
+  }
+  const long long gw = blk * F + w, nwords = (n * BITS + 31) >> 5;
+  if (w < F && gw < nwords) reinterpret_cast<uint32_t*>(base)[gw] = word;
+}
+
 template <int BITS>
 __device__ __forceinline__ void store_index4(uint8_t* base, long long lane_word, uint32_t v) {
   if constexpr (BITS == 2) base[lane_word] = (uint8_t)v;
@@ -391,7 +433,7 @@ __device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, lo
   // that one memory latency covers them all.
   uint32_t idx4 = 0, mcodes = 0, mean16 = 0;
   if (ts.step > 1 && valid[0]) {
-    if (cv) idx4 = load_index4<BITS>(e.v_index, i0 >> 2);
+    if (cv) idx4 = load_field<BITS>(e.v_index, i0, n);
     if (cm) {
       mcodes = e.m_codes[i0 >> 2];
       mean16 = e.m_means[grp];
@@ -556,7 +598,10 @@ __device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, lo
       idx4 |= valid[k] ? idx << (BITS * k) : 0u;           // padding past the end stays zero
     }
     wave_lds_sync();
-    if (valid[0]) store_index4<BITS>(e.v_index, i0 >> 2, idx4);
+    if constexpr (BITS == 3 || BITS == 6)
+      store_fields_dense<BITS>(e.v_index, blk, n, idx4, half, lane_in_half);
+    else if (valid[0])
+      store_index4<BITS>(e.v_index, i0 >> 2, idx4);
     if (lane_in_half == 0 && blk_exists) *reinterpret_cast<uint32_t*>(e.v_ends + 2 * blk) = ends;
   } else {
 #pragma unroll

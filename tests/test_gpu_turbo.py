@@ -84,7 +84,7 @@ def _run(pa, sizes, flags, bits, steps, seed, grad_scale=1e-3, count=False, bloc
 SIZES = [1, 5, 63, 64, 65, 127, 128, 129, 255, 256, 257, 4096 + 77, 70001]
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 6, 8])
 def test_turbo_both_compressed(pa, bits):
     _run(pa, SIZES, [(True, True)] * len(SIZES), bits, steps=4, seed=100 + bits)
 
@@ -95,15 +95,15 @@ def test_turbo_mixed_representations(pa):
     _run(pa, sizes, flags, 4, steps=4, seed=7)
 
 
-@pytest.mark.parametrize("bits,count", [(2, False), (4, False), (8, False), (4, True), (8, True)])
-def test_turbo_several_tiles_per_wavefront(pa, bits, count):
-    """A list of about 27,800 tiles, over three times the wavefronts a full
-    grid holds (256 CUs x 8 workgroups x 4), so every wavefront takes tiles
-    of several tensors in turn. That exercises, across tensors of every
-    representation pair and across ragged tails: the next tile's decode
-    table built during this tile's encode pass (indices of at most 4 bits),
-    the endpoint word loaded for it, and the cursor over the tensor table;
-    in both kernel variants (with and without the non-finite count)."""
+@pytest.mark.parametrize("bits,count", [(2, False), (3, False), (4, False), (6, True), (8, False), (4, True),
+                                        (8, True)])
+def test_turbo_large_list(pa, bits, count):
+    """A list of about 27,800 tiles, one wavefront each, more than a full
+    grid of the chip holds at once, over sixteen tensors of every
+    representation pair with ragged tails: the tensor search of every
+    wavefront, the dense index words of the 3- and 6-bit widths across
+    blocks and tensor ends, in both kernel variants (with and without the
+    non-finite count)."""
     sizes = [1500001, 3, 900017, 129, 1200003, 257, 700007, 65, 1000011, 4097, 800013, 1, 600009, 12345,
              400001, 255]
     flags = [(True, True), (False, True), (True, False), (False, False)] * 4
@@ -125,7 +125,7 @@ def test_turbo_other_layouts(pa, bits, block, group):
     _run(pa, LAYOUT_SIZES, flags, bits, steps=3, seed=500 + 7 * bits + block + group, block=block, group=group)
 
 
-@pytest.mark.parametrize("bits,count", [(2, False), (4, False), (8, False), (4, True)])
+@pytest.mark.parametrize("bits,count", [(2, False), (3, False), (4, False), (6, False), (8, False), (4, True)])
 def test_turbo_general_kernel_at_default_layout(pa, bits, count):
     """The general kernel forced at the tuned kernel's layout gives the same
     (oracle) results."""
