@@ -416,7 +416,7 @@ def run_turbo(args, cfg):
     if args.layout == "regions":
         spacer = torch.empty(max(region_bytes() - 8 * sum(sizes), 0), dtype=torch.uint8, device="cuda:0")
     B, G = args.turbo_block, args.turbo_group
-    general = args.turbo_general or (B, G) != (128, 64) or args.turbo_bits in (3, 6)
+    general = args.turbo_general or (B, G) != (128, 64)
     states = [pa.TurboState(n, "cuda:0", compress_m=n >= 4096, compress_v=n >= 4096, v_bits=args.turbo_bits,
                             tensor_id=i, block_size=B, m_block_size=G)
               for i, n in enumerate(sizes)]
