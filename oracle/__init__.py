@@ -96,6 +96,11 @@ def _load():
                                       _f32p, ctypes.c_double,
                                       ctypes.c_ulonglong, ctypes.c_longlong]
     lib.oracle_turbo_step.restype = ctypes.c_ulonglong
+    lib.oracle_turbo_step_typed.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_size_t, ctypes.c_uint32,
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp,
+                                            vp, vp, vp, vp, _f32p, _f32p, _f32p, ctypes.c_double, ctypes.c_ulonglong,
+                                            ctypes.c_longlong]
+    lib.oracle_turbo_step_typed.restype = ctypes.c_ulonglong
     lib.oracle_q1_levels.argtypes = [ctypes.c_uint16, ctypes.c_uint16, ctypes.c_int, _f32p]
     lib.oracle_q1_levels.restype = None
     lib.oracle_q1_levels_batch.argtypes = [_u32p, ctypes.c_size_t, ctypes.c_int, _f32p]
@@ -345,6 +350,23 @@ def turbo_step(p, g, st, sc, ts, step, tensor_id=0, factor=1.1, seed=0x12345678)
         _ptr(p, _f32p), _ptr(g, _f32p), p.size, int(tensor_id), int(st.compress_m), int(st.compress_v), int(st.bits),
         int(st.block), int(st.group), addr(st.m_codes), addr(st.m_means), addr(st.m_fp32), addr(st.v_index), addr(st.v_ends), addr(st.v_fp32),
         _ptr(st.scal, _f32p), _ptr(sc, _f32p), _ptr(ts, _f32p), float(factor), int(seed), int(step)))
+
+
+def turbo_step_typed(pdt, gdt, p, g, st, sc, ts, step, tensor_id=0, factor=1.1, seed=0x12345678):
+    """turbo_step with typed parameters and gradients: float32 arrays (dtype 0)
+    or uint16 bit patterns of bfloat16 (1) / binary16 (2), as for step_typed.
+    In place on p and st; returns the non-finite count."""
+    _need(p, _DT_NP[pdt], "p")
+    _need(g, _DT_NP[gdt], "g")
+    _need(sc, np.float32, "scalars")
+    _need(ts, np.float32, "turbo scalars")
+    assert p.size == g.size == st.n
+    addr = lambda a: None if a is None else a.ctypes.data
+    return int(_load().oracle_turbo_step_typed(
+        int(pdt), int(gdt), p.ctypes.data, g.ctypes.data, p.size, int(tensor_id), int(st.compress_m),
+        int(st.compress_v), int(st.bits), int(st.block), int(st.group), addr(st.m_codes), addr(st.m_means),
+        addr(st.m_fp32), addr(st.v_index), addr(st.v_ends), addr(st.v_fp32), _ptr(st.scal, _f32p), _ptr(sc, _f32p),
+        _ptr(ts, _f32p), float(factor), int(seed), int(step)))
 
 
 def q1_levels(lo16, hi16, bits):

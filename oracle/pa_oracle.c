@@ -1066,3 +1066,32 @@ unsigned long long oracle_turbo_step(float* p, const float* g, size_t n, uint32_
     free(r2); free(m1); free(v1); free(vp); free(u1); free(up); free(mprev); free(vprev);
     return bad;
 }
+
+/* oracle_turbo_step with typed parameters (pdt) and gradients (gdt), as for
+ * oracle_step_typed (TurboAdam package page, Verification: its tests run
+ * fp16, bf16 and fp32 parameters).  The page's update reads the parameter
+ * only in its own line ("The AdamW update remains AdamW"): the moments,
+ * their compression and the scales never see it.  So the step widens both
+ * inputs exactly, takes the FP32 step, and rounds only the new parameter
+ * back to its type. */
+unsigned long long oracle_turbo_step_typed(int pdt, int gdt, void* p, const void* g, size_t n, uint32_t tensor_id,
+                                           int compress_m, int compress_v, int bits, int block, int group,
+                                           uint32_t* m_codes, uint16_t* m_means, float* m_fp32,
+                                           uint32_t* v_index, uint16_t* v_ends, float* v_fp32,
+                                           float* scal, const float s[8], const float ts[3],
+                                           double factor, unsigned long long seed, long long step) {
+    size_t nn = n ? n : 1;
+    float* pw = (float*)calloc(nn, sizeof(float));
+    float* gw = (float*)calloc(nn, sizeof(float));
+    for (size_t i = 0; i < n; ++i) {
+        pw[i] = widen_at(pdt, p, i);
+        gw[i] = widen_at(gdt, g, i);
+    }
+    unsigned long long bad = oracle_turbo_step(pw, gw, n, tensor_id, compress_m, compress_v, bits, block, group,
+                                               m_codes, m_means, m_fp32, v_index, v_ends, v_fp32, scal, s, ts,
+                                               factor, seed, step);
+    for (size_t i = 0; i < n; ++i) narrow_at(pdt, p, i, pw[i]);
+    free(pw);
+    free(gw);
+    return bad;
+}

@@ -536,3 +536,69 @@ def test_antithetic_pairs_follow_the_tensor_index(oracle_mod):
     # in a two-value group the second value is the odd one of the pair
     both, _, _ = oracle.ustate_group(np.array([0.3, 0.3], np.float32), 1.0, u, group=2, first=4)
     assert both.tolist() == [2, 1]
+
+
+def _bf16_rne(x):
+    """bfloat16 bits of float32 values, rounded to nearest even by integer
+    arithmetic on the bit patterns (finite and infinite inputs)."""
+    u = np.ascontiguousarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _to_type(x32, dt):
+    if dt == oracle.DT_F32:
+        return np.ascontiguousarray(x32, np.float32)
+    if dt == oracle.DT_BF16:
+        return _bf16_rne(x32)
+    with np.errstate(over="ignore"):
+        return np.ascontiguousarray(x32, np.float32).astype(np.float16).view(np.uint16)
+
+
+def _widen(a, dt):
+    if dt == oracle.DT_F32:
+        return a.copy()
+    if dt == oracle.DT_BF16:
+        return (a.astype(np.uint32) << 16).view(np.float32)
+    return a.view(np.float16).astype(np.float32)
+
+
+@pytest.mark.parametrize("pdt,gdt", [(1, 1), (2, 2), (1, 0), (2, 0)], ids=["bf16", "f16", "bf16-f32g", "f16-f32g"])
+@pytest.mark.parametrize("bits,block,group", [(4, 128, 64), (3, 256, 32)])
+@pytest.mark.parametrize("lr,wd", [(1e-3, 0.01), (30.0, 0.0)])
+def test_typed_parameters_round_only_the_parameter(oracle_mod, pdt, gdt, bits, block, group, lr, wd):
+    """16-bit parameters and gradients (the TurboAdam page's Verification runs
+    fp16, bf16 and fp32 parameters): over three steps, the new parameter is
+    numpy's binary16 rounding, or a round-to-nearest-even on the bfloat16 bit
+    pattern, of the FP32 step's result on the widened values, and the state
+    and non-finite count are the FP32 step's exactly (the page's update reads
+    the parameter only in its own line).  lr = 30 with no decay drives binary16
+    parameters near its largest finite value past it, to Inf."""
+    n = 3000
+    r = np.random.default_rng(61 + 7 * pdt + gdt)
+    p32 = r.normal(0, 0.02, n).astype(np.float32)
+    p32[:6] = [65504.0, -65504.0, 65000.0, 1.5, -3.0e-8, 6.1e-5]
+    pt = _to_type(p32, pdt)
+    st_t = oracle.TurboState(n, bits=bits, block=block, group=group)
+    st_f = oracle.TurboState(n, bits=bits, block=block, group=group)
+    for t in range(1, 4):
+        g32 = (r.normal(0, 1e-3, n) - 2e-4).astype(np.float32)
+        g32[:6] = [-1e-3, 1e-3, -1e-3, 0.0, 2e-3, -5e-4]
+        gt = _to_type(g32, gdt)
+        sc = oracle.scalars(lr, 0.9, 0.999, 1e-8, wd, t)
+        ts = oracle.turbo_scalars(0.9, 0.999, t)
+        pf = _widen(pt, pdt)
+        bad_f = oracle.turbo_step(pf, _widen(gt, gdt), st_f, sc, ts, t, tensor_id=5)
+        bad_t = oracle.turbo_step_typed(pdt, gdt, pt, gt, st_t, sc, ts, t, tensor_id=5)
+        assert bad_t == bad_f
+        want = _to_type(pf, pdt)
+        assert np.array_equal(pt.view(np.uint16), want.view(np.uint16)), f"step {t}"
+        for name, a in st_t.arrays().items():
+            b = st_f.arrays()[name]
+            assert (a is None) == (b is None)
+            if a is not None:
+                assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), (t, name)
+    if pdt == oracle.DT_F16 and lr == 30.0:
+        assert np.isinf(pt[:2].view(np.float16)).all(), pt[:2].view(np.float16)
+    # bfloat16 rounding itself: ties go to even, and a value just above a tie up
+    x = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -8 + 2.0 ** -20], np.float32)
+    assert list(_bf16_rne(x)) == [0x3F80, 0x3F82, 0x3F81]
