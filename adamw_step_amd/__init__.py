@@ -90,7 +90,7 @@ class Format(ctypes.Structure):
 EXPORTS = ("pa_step", "pa_step_list", "pa_step_typed", "pa_step_list_typed", "pa_state_bytes",
            "pa_format_info", "pa_status_string", "pa_last_hip_error", "pa_release_plans", "pa_debug_codec",
            "pa_debug_sqrt", "pa_debug_scalars", "pa_debug_q1_ends", "pa_debug_q1_levels", "pa_debug_pow2_rn32", "pa_grad_stats_list", "pa_turbo_state_bytes", "pa_turbo_layout_bytes", "pa_turbo_workspace_bytes",
-           "pa_turbo_step_list", "pa_step_list_noalloc")
+           "pa_turbo_step_list", "pa_turbo_step_list_typed", "pa_step_list_noalloc")
 
 PA_DT_F32, PA_DT_BF16, PA_DT_F16 = 0, 1, 2
 
@@ -155,6 +155,8 @@ def lib():
                                      ctypes.POINTER(sz), ctypes.POINTER(Hyper), ctypes.POINTER(TurboConfig),
                                      ctypes.c_longlong, vp, sz, vp]
     L.pa_turbo_step_list.restype = ctypes.c_int
+    L.pa_turbo_step_list_typed.argtypes = [ctypes.c_int, ctypes.c_int] + L.pa_turbo_step_list.argtypes
+    L.pa_turbo_step_list_typed.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -538,9 +540,11 @@ def turbo_layout_ok(v_bits, block_size, m_block_size):
 
 
 class TurboList:
-    """A fixed list of FP32 parameters, gradients and TurboState objects,
+    """A fixed list of parameters, gradients and TurboState objects,
     validated and marshalled once; ``step(hyper, t)`` is one
-    pa_turbo_step_list call.  Owns its device workspace."""
+    pa_turbo_step_list_typed call.  Parameters are float32, bfloat16 or
+    float16, all of one type; gradients are of the parameters' type or
+    float32 (the pairs of pa_step_typed).  Owns its device workspace."""
 
     def __init__(self, params, grads, states, v_bits=4, m_step_factor=1.1, seed=0x12345678, block_size=128,
                  m_block_size=64, general=False):
@@ -553,12 +557,14 @@ class TurboList:
         self._G = (ctypes.c_void_p * k)()
         self._S = (TurboStateDesc * k)()
         self._N = (ctypes.c_size_t * k)()
+        self.pdt = _dtype_code(params[0]) if k else PA_DT_F32
+        self.gdt = _dtype_code(grads[0]) if k else PA_DT_F32
         for i in range(k):
             p, g, st = params[i], grads[i], states[i]
             _tensor_ok(p, "params")
             _tensor_ok(g, "grads")
-            if p.dtype != torch.float32 or g.dtype != torch.float32:
-                raise TypeError("the TurboAdam step takes float32 parameters and gradients")
+            if _dtype_code(p) != self.pdt or _dtype_code(g) != self.gdt:
+                raise TypeError("every parameter must share one dtype, and every gradient one dtype")
             if g.numel() != p.numel() or st.n != p.numel() or st.v_bits != v_bits:
                 raise ValueError("params, grads and states disagree in size or v_bits")
             if (st.block_size, st.m_block_size) != (block_size, m_block_size):
@@ -574,9 +580,9 @@ class TurboList:
         dev = params[0].device if k else "cuda:0"
         self.workspace = torch.empty(max(wsb // 8, 1), dtype=torch.float64, device=dev)
         self._wsb = wsb
-        self._fn = L.pa_turbo_step_list
+        self._fn = L.pa_turbo_step_list_typed
 
     def step(self, hyper, step, stream=None):
         h = _hyper(hyper)
-        _check(self._fn(self.count, self._P, self._G, self._S, self._N, ctypes.byref(h), ctypes.byref(self.config),
-                        int(step), _ptr(self.workspace), self._wsb, _stream(stream)))
+        _check(self._fn(self.pdt, self.gdt, self.count, self._P, self._G, self._S, self._N, ctypes.byref(h),
+                        ctypes.byref(self.config), int(step), _ptr(self.workspace), self._wsb, _stream(stream)))

@@ -578,6 +578,9 @@ hipError_t launch_stats(const Plan& pl, double max_norm, double* sumsq, unsigned
 
 // ---------------------------------------------------------------- TurboAdam
 
+// Table entries carry the element types as the kernels' type codes.
+static_assert(PA_DT_F32 == pa::kF32 && PA_DT_BF16 == pa::kBF16 && PA_DT_F16 == pa::kF16, "dtype codes");
+
 struct TurboPlan {
   int device = -1;
   std::vector<uintptr_t> key;
@@ -586,6 +589,7 @@ struct TurboPlan {
   long long tiles = 0;                      // 256-value tiles, or 1024-value ones on the general path
   int count = 0;                            // entries before the sentinel
   bool general = false;                     // turbo_general instead of turbo_list
+  bool typed = false;                       // 16-bit parameters or gradients
   int blog = 7, glog = 6;                   // log2 of the 1Q block and of the UState group
   int nreduce = 0;
   long long nchunks = 0;                    // chunks of tile sums over all UState tensors
@@ -641,14 +645,15 @@ int turbo_layout(const pa_turbo_config* c, TurboLayout* out) {
 constexpr size_t kTurboMaxValues = size_t(1) << 34;
 constexpr long long kTurboMaxStep = 0xFFFFFFFFll;
 
-int check_turbo_tensor(const float* p, const float* g, const pa_turbo_state& st, size_t n, const TurboLayout& lay,
-                       std::vector<Range>* w, std::vector<Range>* r) {
+int check_turbo_tensor(int pdt, int gdt, const void* p, const void* g, const pa_turbo_state& st, size_t n,
+                       const TurboLayout& lay, std::vector<Range>* w, std::vector<Range>* r) {
   const size_t bits = (size_t)lay.bits, B = (size_t)lay.block, G = (size_t)lay.group;
   if (n == 0) return PA_OK;
   if (p == nullptr || g == nullptr) return PA_ERR_ARG;
-  if (!aligned(p, 16) || !aligned(g, 16)) return PA_ERR_ALIGN;
-  w->push_back(range_of(p, n * 4));
-  r->push_back(range_of(g, n * 4));
+  // A lane reads and writes four consecutive values as one vector.
+  if (!aligned(p, 4 * dtype_size(pdt)) || !aligned(g, 4 * dtype_size(gdt))) return PA_ERR_ALIGN;
+  w->push_back(range_of(p, n * dtype_size(pdt)));
+  r->push_back(range_of(g, n * dtype_size(gdt)));
   if (st.compress_m) {
     if (!st.m_codes || !st.m_means || !st.scalars) return PA_ERR_ARG;
     if (!aligned(st.m_codes, 4) || !aligned(st.m_means, 2) || !aligned(st.scalars, 4)) return PA_ERR_ALIGN;
@@ -691,42 +696,56 @@ hipError_t launch_turbo_reduce(const TurboPlan& pl, const pa::Scalars& s, double
 
 // The tuned kernel: one wavefront per 256-value tile, four per workgroup,
 // in launches of at most kMaxLaunchTiles workgroups.
-template <int BITS>
-hipError_t launch_turbo(const TurboPlan& pl, const pa::Scalars& s, const pa::TurboScalars& ts, double* ws,
-                        unsigned long long* nf, double factor, hipStream_t st) {
+template <int BITS, bool TYPED>
+hipError_t launch_turbo_as(const TurboPlan& pl, const pa::Scalars& s, const pa::TurboScalars& ts, double* ws,
+                           unsigned long long* nf, double factor, hipStream_t st) {
   constexpr long long kWaves = pa::kThreads / 64;
   const long long wgs = (pl.tiles + kWaves - 1) / kWaves;
   for (long long w0 = 0; w0 < wgs; w0 += kMaxLaunchTiles) {
     const long long nw = std::min(kMaxLaunchTiles, wgs - w0);
     if (nf)
-      hipLaunchKernelGGL((pa::turbo_list<BITS, true>), dim3((unsigned)nw), dim3(pa::kThreads), 0, st, pl.table,
-                         pl.count, pl.tiles, w0 * kWaves, s, ts, ws, nf);
+      hipLaunchKernelGGL((pa::turbo_list<BITS, true, TYPED>), dim3((unsigned)nw), dim3(pa::kThreads), 0, st,
+                         pl.table, pl.count, pl.tiles, w0 * kWaves, s, ts, ws, nf);
     else
-      hipLaunchKernelGGL((pa::turbo_list<BITS, false>), dim3((unsigned)nw), dim3(pa::kThreads), 0, st, pl.table,
-                         pl.count, pl.tiles, w0 * kWaves, s, ts, ws, nf);
+      hipLaunchKernelGGL((pa::turbo_list<BITS, false, TYPED>), dim3((unsigned)nw), dim3(pa::kThreads), 0, st,
+                         pl.table, pl.count, pl.tiles, w0 * kWaves, s, ts, ws, nf);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return launch_turbo_reduce(pl, s, ws, factor, st);
 }
 
+template <int BITS>
+hipError_t launch_turbo(const TurboPlan& pl, const pa::Scalars& s, const pa::TurboScalars& ts, double* ws,
+                        unsigned long long* nf, double factor, hipStream_t st) {
+  return pl.typed ? launch_turbo_as<BITS, true>(pl, s, ts, ws, nf, factor, st)
+                  : launch_turbo_as<BITS, false>(pl, s, ts, ws, nf, factor, st);
+}
+
 // The general kernel: one workgroup per 1024-value tile, in launches of at
 // most kMaxLaunchTiles workgroups.
-template <int BITS>
-hipError_t launch_general(const TurboPlan& pl, const pa::Scalars& s, const pa::TurboScalars& ts, double* ws,
-                          unsigned long long* nf, double factor, hipStream_t st) {
+template <int BITS, bool TYPED>
+hipError_t launch_general_as(const TurboPlan& pl, const pa::Scalars& s, const pa::TurboScalars& ts, double* ws,
+                             unsigned long long* nf, double factor, hipStream_t st) {
   for (long long t0 = 0; t0 < pl.tiles; t0 += kMaxLaunchTiles) {
     const long long nt = std::min(kMaxLaunchTiles, pl.tiles - t0);
     if (nf)
-      hipLaunchKernelGGL((pa::turbo_general<BITS, true>), dim3((unsigned)nt), dim3(pa::kThreads), 0, st, pl.table,
-                         pl.count, t0, s, ts, pl.blog, pl.glog, ws, nf);
+      hipLaunchKernelGGL((pa::turbo_general<BITS, true, TYPED>), dim3((unsigned)nt), dim3(pa::kThreads), 0, st,
+                         pl.table, pl.count, t0, s, ts, pl.blog, pl.glog, ws, nf);
     else
-      hipLaunchKernelGGL((pa::turbo_general<BITS, false>), dim3((unsigned)nt), dim3(pa::kThreads), 0, st, pl.table,
-                         pl.count, t0, s, ts, pl.blog, pl.glog, ws, nf);
+      hipLaunchKernelGGL((pa::turbo_general<BITS, false, TYPED>), dim3((unsigned)nt), dim3(pa::kThreads), 0, st,
+                         pl.table, pl.count, t0, s, ts, pl.blog, pl.glog, ws, nf);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return launch_turbo_reduce(pl, s, ws, factor, st);
+}
+
+template <int BITS>
+hipError_t launch_general(const TurboPlan& pl, const pa::Scalars& s, const pa::TurboScalars& ts, double* ws,
+                          unsigned long long* nf, double factor, hipStream_t st) {
+  return pl.typed ? launch_general_as<BITS, true>(pl, s, ts, ws, nf, factor, st)
+                  : launch_general_as<BITS, false>(pl, s, ts, ws, nf, factor, st);
 }
 
 }  // namespace
@@ -1079,6 +1098,16 @@ size_t pa_turbo_workspace_bytes(size_t count, const pa_turbo_state* states, cons
 int pa_turbo_step_list(size_t count, float* const* params, const float* const* grads, const pa_turbo_state* states,
                        const size_t* n, const pa_hyper* hyper, const pa_turbo_config* config, long long step,
                        void* workspace, size_t workspace_bytes, void* stream) {
+  return pa_turbo_step_list_typed(PA_DT_F32, PA_DT_F32, count, reinterpret_cast<void* const*>(params),
+                                  reinterpret_cast<const void* const*>(grads), states, n, hyper, config, step,
+                                  workspace, workspace_bytes, stream);
+}
+
+int pa_turbo_step_list_typed(int param_dtype, int grad_dtype, size_t count, void* const* params,
+                             const void* const* grads, const pa_turbo_state* states, const size_t* n,
+                             const pa_hyper* hyper, const pa_turbo_config* config, long long step, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (!valid_dtype_pair(param_dtype, grad_dtype)) return PA_ERR_ARG;
   if (config == nullptr || !std::isfinite(config->m_step_factor) || !(config->m_step_factor > 0.0))
     return PA_ERR_ARG;
   TurboLayout lay;
@@ -1103,7 +1132,9 @@ int pa_turbo_step_list(size_t count, float* const* params, const float* const* g
   if (rc) return rc;
 
   std::vector<uintptr_t> key;
-  key.reserve(count * 13 + 5);
+  key.reserve(count * 13 + 7);
+  key.push_back((uintptr_t)param_dtype);
+  key.push_back((uintptr_t)grad_dtype);
   key.push_back((uintptr_t)lay.bits);
   key.push_back((uintptr_t)lay.block);
   key.push_back((uintptr_t)lay.group);
@@ -1129,13 +1160,13 @@ int pa_turbo_step_list(size_t count, float* const* params, const float* const* g
     long long tiles = 0, ws_slots = 0;
     for (size_t i = 0; i < count; ++i) {
       const pa_turbo_state& t = states[i];
-      rc = check_turbo_tensor(params[i], grads[i], t, n[i], lay, &written, &read);
+      rc = check_turbo_tensor(param_dtype, grad_dtype, params[i], grads[i], t, n[i], lay, &written, &read);
       if (rc) return rc;
       if (n[i] == 0) continue;
       pa::TurboEntry e;
       std::memset(&e, 0, sizeof(e));
-      e.p = params[i];
-      e.g = grads[i];
+      e.p = static_cast<float*>(params[i]);
+      e.g = static_cast<const float*>(grads[i]);
       e.m_codes = t.compress_m ? t.m_codes : nullptr;
       e.m_means = t.compress_m ? t.m_means : nullptr;
       e.m_fp32 = t.compress_m ? nullptr : t.m_fp32;
@@ -1148,7 +1179,7 @@ int pa_turbo_step_list(size_t count, float* const* params, const float* const* g
       e.ws0 = t.compress_m ? ws_slots : 0;    // in 256-value partial sums either way
       e.tensor_id = t.tensor_id;
       e.seed = config->seed;
-      e.flags = (t.compress_m ? 1 : 0) | (t.compress_v ? 2 : 0);
+      e.flags = (t.compress_m ? 1 : 0) | (t.compress_v ? 2 : 0) | (param_dtype << 2) | (grad_dtype << 4);
       const long long nt = turbo_tiles(n[i]);
       if (t.compress_m) {
         pa::TurboReduceEntry r{t.scalars, ws_slots, nt, (long long)n[i], 0, 0, turbo_chunks_of(nt)};
@@ -1182,6 +1213,7 @@ int pa_turbo_step_list(size_t count, float* const* params, const float* const* g
     pl.tiles = tiles;
     pl.count = (int)host.size() - 1;
     pl.general = lay.general;
+    pl.typed = param_dtype != PA_DT_F32 || grad_dtype != PA_DT_F32;
     pl.blog = log2_exact(lay.block);
     pl.glog = log2_exact(lay.group);
     pl.nreduce = (int)red.size();

@@ -51,8 +51,8 @@ constexpr int kTurboBlock = 128;    // 1Q block
 constexpr int kTurboGroup = 64;     // UState mean group
 
 struct TurboEntry {
-  float* p;
-  const float* g;
+  float* p;            // parameters: FP32, or 16-bit patterns (flags bits 2-3)
+  const float* g;      // gradients: FP32, or 16-bit patterns (flags bits 4-5)
   uint8_t* m_codes;    // 2-bit codes, 4 per byte (compress_m)
   uint16_t* m_means;   // bf16 per 64 (compress_m)
   float* m_fp32;       // (!compress_m)
@@ -67,8 +67,60 @@ struct TurboEntry {
                              // Philox key schedule is formed per tile, not
                              // hoisted into scalar registers for the launch)
   uint32_t tensor_id;
-  int flags;           // bit 0: compress_m, bit 1: compress_v
+  int flags;           // bit 0: compress_m, bit 1: compress_v, bits 2-3 and
+                       // 4-5: parameter and gradient type (kF32, kBF16, kF16)
 };
+
+// Four consecutive parameters or gradients from i0 (a multiple of four),
+// widened to FP32: one vector load for a whole quad, else one load per
+// valid value (0 for the others).  The type is uniform across the
+// wavefront, so the branch is a scalar one.
+template <int T>
+__device__ __forceinline__ void load4_as(const void* base, long long i0, bool full, const bool valid[4],
+                                         float out[4]) {
+  using E = Elem<T>;
+  const typename E::scalar* b = static_cast<const typename E::scalar*>(base);
+  if (full) {
+    const typename E::vec4 v = stream_load(reinterpret_cast<const typename E::vec4*>(b + i0));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) out[k] = E::widen(v[k]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) out[k] = valid[k] ? E::widen(b[i0 + k]) : 0.0f;
+  }
+}
+
+__device__ __forceinline__ void load4_typed(int t, const void* base, long long i0, bool full, const bool valid[4],
+                                            float out[4]) {
+  if (t == kBF16) load4_as<kBF16>(base, i0, full, valid, out);
+  else if (t == kF16) load4_as<kF16>(base, i0, full, valid, out);
+  else load4_as<kF32>(base, i0, full, valid, out);
+}
+
+// The new parameters, rounded to their type (to nearest even).
+template <int T>
+__device__ __forceinline__ void store4_as(void* base, long long i0, bool full, const bool valid[4], const float x[4]) {
+  using E = Elem<T>;
+  typename E::scalar* b = static_cast<typename E::scalar*>(base);
+  if (full) {
+    typename E::vec4 v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = E::narrow(x[k]);
+    stream_store(reinterpret_cast<typename E::vec4*>(b + i0), v);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (valid[k]) b[i0 + k] = E::narrow(x[k]);
+  }
+}
+
+__device__ __forceinline__ void store4_typed(int t, void* base, long long i0, bool full, const bool valid[4],
+                                             const float x[4]) {
+  if (t == kBF16) store4_as<kBF16>(base, i0, full, valid, x);
+  else if (t == kF16) store4_as<kF16>(base, i0, full, valid, x);
+  else store4_as<kF32>(base, i0, full, valid, x);
+}
+
 
 struct TurboScalars {
   float bc1, bc1p, bc2p, pad_;
@@ -386,8 +438,9 @@ __device__ __forceinline__ void store_index4(uint8_t* base, long long lane_word,
 // crowd the scalar registers and spill.
 // FULL: the tile lies wholly inside its tensor, so every validity test below
 // folds away (one instantiation per case; the partial one runs only on a
-// tensor's last tile).
-template <int BITS, bool FULL>
+// tensor's last tile).  TYPED: parameters and gradients of the entry's
+// element types (else FP32).
+template <int BITS, bool FULL, bool TYPED>
 __device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, long long tile, const Scalars& s,
                                            const TurboScalars& ts, float* lev_half, double* ws, uint32_t& bad) {
   const TurboEntry& e = *ep;
@@ -414,7 +467,10 @@ __device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, lo
   // decode table (indices of at most 4 bits, 1Q second moment).
   constexpr bool kDenTables = BITS <= 4;
   float dprev[4] = {0.f, 0.f, 0.f, 0.f};
-  if (full) {
+  if constexpr (TYPED) {
+    load4_typed((e.flags >> 2) & 3, e.p, i0, full, valid, p);
+    load4_typed((e.flags >> 4) & 3, e.g, i0, full, valid, g);
+  } else if (full) {
     const f32x4 pv = stream_load(reinterpret_cast<const f32x4*>(e.p + i0));
     const f32x4 gv = stream_load(reinterpret_cast<const f32x4*>(e.g + i0));
 #pragma unroll
@@ -505,7 +561,9 @@ __device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, lo
     if (valid[k]) bad += nonfinite3(p1, m1[k], v1[k]);
     p[k] = p1;
   }
-  if (full) {
+  if constexpr (TYPED) {
+    store4_typed((e.flags >> 2) & 3, e.p, i0, full, valid, p);
+  } else if (full) {
     f32x4 pv;
 #pragma unroll
     for (int k = 0; k < 4; ++k) pv[k] = p[k];
@@ -670,7 +728,7 @@ __device__ __forceinline__ void turbo_tile(const TurboEntry* __restrict__ ep, lo
 // the tiles: the hardware starts each new wavefront as one finishes, and
 // its loads overlap the work of the wavefronts around it).  The tile's
 // tensor is found by a bisection over the table's first tiles.
-template <int BITS, bool COUNT>
+template <int BITS, bool COUNT, bool TYPED>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BITS <= 4 ? 7 : 6)))
 turbo_list(const TurboEntry* __restrict__ table, int count, long long total_tiles, long long tile_base, Scalars s,
            TurboScalars ts, double* ws, unsigned long long* nonfinite) {
@@ -692,9 +750,9 @@ turbo_list(const TurboEntry* __restrict__ table, int count, long long total_tile
     }
     const long long local = tile - table[lo].tile0;
     if ((local + 1) * kTurboTile <= table[lo].n)
-      turbo_tile<BITS, true>(table + lo, local, s, ts, lev[wave][half], ws, bad);
+      turbo_tile<BITS, true, TYPED>(table + lo, local, s, ts, lev[wave][half], ws, bad);
     else
-      turbo_tile<BITS, false>(table + lo, local, s, ts, lev[wave][half], ws, bad);
+      turbo_tile<BITS, false, TYPED>(table + lo, local, s, ts, lev[wave][half], ws, bad);
   }
   if constexpr (COUNT) flush_count(bad, nonfinite);
 }
@@ -747,7 +805,8 @@ __device__ __forceinline__ float q1_level(double lo, double hi, int k, int L) {
 // One 1024-value tile of the general step (the workgroup's), its LDS
 // passed in.  FULL: the tile lies wholly inside its tensor, so every
 // validity test folds away (the partial copy runs on a tensor's last tile).
-template <int BITS, bool FULL>
+// TYPED as for turbo_tile.
+template <int BITS, bool FULL, bool TYPED>
 __device__ __forceinline__ void general_tile(const TurboEntry* __restrict__ ep, long long local, const Scalars& s,
                                              const TurboScalars& ts, int blog, int glog, double* ws, uint32_t& bad,
                                              uint32_t* words, float2* tabs, uint32_t* eslot, float* fslot,
@@ -773,7 +832,10 @@ __device__ __forceinline__ void general_tile(const TurboEntry* __restrict__ ep, 
   // ---- loads
   float p[4], g[4], mprev[4] = {0.f, 0.f, 0.f, 0.f}, vprev[4] = {0.f, 0.f, 0.f, 0.f};
   float dprev[4] = {0.f, 0.f, 0.f, 0.f};              // UState decode denominators (tables)
-  if (full) {
+  if constexpr (TYPED) {
+    load4_typed((e.flags >> 2) & 3, e.p, i0, full, valid, p);
+    load4_typed((e.flags >> 4) & 3, e.g, i0, full, valid, g);
+  } else if (full) {
     const f32x4 pv = stream_load(reinterpret_cast<const f32x4*>(e.p + i0));
     const f32x4 gv = stream_load(reinterpret_cast<const f32x4*>(e.g + i0));
 #pragma unroll
@@ -877,7 +939,9 @@ __device__ __forceinline__ void general_tile(const TurboEntry* __restrict__ ep, 
     if (valid[k]) bad += nonfinite3(p1, m1[k], v1[k]);
     p[k] = p1;
   }
-  if (full) {
+  if constexpr (TYPED) {
+    store4_typed((e.flags >> 2) & 3, e.p, i0, full, valid, p);
+  } else if (full) {
     f32x4 pv;
 #pragma unroll
     for (int k = 0; k < 4; ++k) pv[k] = p[k];
@@ -1063,7 +1127,7 @@ __device__ __forceinline__ void general_tile(const TurboEntry* __restrict__ ep, 
 // Six wavefronts per SIMD: measured faster than the five the registers
 // allow unasked (4-6% at table layouts) and than seven or eight, where the
 // spills grow.
-template <int BITS, bool COUNT>
+template <int BITS, bool COUNT, bool TYPED>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6)))
 turbo_general(const TurboEntry* __restrict__ table, int count, long long tile_base, Scalars s, TurboScalars ts,
               int blog, int glog, double* ws, unsigned long long* nonfinite) {
@@ -1085,9 +1149,9 @@ turbo_general(const TurboEntry* __restrict__ table, int count, long long tile_ba
   const long long local = tile - ep->tile0;
   uint32_t bad = 0;
   if ((local + 1) * kGenTile <= ep->n)
-    general_tile<BITS, true>(ep, local, s, ts, blog, glog, ws, bad, words, tabs, eslot, fslot, dslot, islot);
+    general_tile<BITS, true, TYPED>(ep, local, s, ts, blog, glog, ws, bad, words, tabs, eslot, fslot, dslot, islot);
   else
-    general_tile<BITS, false>(ep, local, s, ts, blog, glog, ws, bad, words, tabs, eslot, fslot, dslot, islot);
+    general_tile<BITS, false, TYPED>(ep, local, s, ts, blog, glog, ws, bad, words, tabs, eslot, fslot, dslot, islot);
   if constexpr (COUNT) flush_count(bad, nonfinite);
 }
 

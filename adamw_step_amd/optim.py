@@ -217,10 +217,13 @@ class TurboAdam(torch.optim.Optimizer):
     min_v_compress_elements (a tensor below the threshold keeps that
     moment in FP32), m_block_size (a power of two dividing block_size),
     m_step_factor and rounding_seed.  The default layout (128, 4 bits, 64)
-    runs the tuned kernel, every other one the general kernel.  The page's validation of beta1^2 < beta2 with UState
-    on is kept.  One parameter group of contiguous FP32 tensors on one GPU;
-    ``count_nonfinite``, ``nonfinite_count()`` and ``state_bytes()`` as for
-    PackedAdamW.
+    runs the tuned kernel at every index width, every other layout the
+    general kernel.  The page's validation of beta1^2 < beta2 with UState on
+    is kept.  One parameter group of contiguous tensors of one dtype on one
+    GPU: float32, bfloat16 or float16 (the page's tests run all three; the
+    update runs in FP32 and only the new parameter is rounded back), with
+    gradients of the same dtype; ``count_nonfinite``, ``nonfinite_count()``
+    and ``state_bytes()`` as for PackedAdamW.
     """
 
     def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0, block_size=128, v_bits=4,
@@ -239,10 +242,12 @@ class TurboAdam(torch.optim.Optimizer):
         plist = self.param_groups[0]["params"]
         if not plist:
             raise ValueError("no parameters")
-        dev = plist[0].device
+        dev, dt = plist[0].device, plist[0].dtype
+        if dt not in (torch.float32, torch.bfloat16, torch.float16):
+            raise TypeError("parameters must be float32, bfloat16 or float16")
         for p in plist:
-            if p.dtype != torch.float32 or not p.is_cuda or not p.is_contiguous() or p.device != dev:
-                raise TypeError("parameters must be contiguous float32 tensors on one GPU")
+            if p.dtype != dt or not p.is_cuda or not p.is_contiguous() or p.device != dev:
+                raise TypeError("parameters must be contiguous tensors of one dtype on one GPU")
         self.v_bits, self.m_step_factor, self.seed = v_bits, float(m_step_factor), int(rounding_seed)
         self.block_size, self.m_block_size = int(block_size), int(m_block_size)
         self.step_count = 0

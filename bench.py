@@ -410,11 +410,13 @@ def run_turbo(args, cfg):
     import workloads
     sizes = workloads.sizes(cfg)
     log(f"allocating {workloads.NAMES[cfg]} with TurboAdam state: {len(sizes)} tensors, {sum(sizes)} params")
-    ps = [torch.empty(n, dtype=torch.float32, device="cuda:0") for n in sizes]
-    gs = [torch.empty(n, dtype=torch.float32, device="cuda:0") for n in sizes]
+    dt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[args.param_dtype]
+    esz = 4 if args.param_dtype == "fp32" else 2
+    ps = [torch.empty(n, dtype=dt, device="cuda:0") for n in sizes]
+    gs = [torch.empty(n, dtype=dt, device="cuda:0") for n in sizes]
     spacer = None
     if args.layout == "regions":
-        spacer = torch.empty(max(region_bytes() - 8 * sum(sizes), 0), dtype=torch.uint8, device="cuda:0")
+        spacer = torch.empty(max(region_bytes() - 2 * esz * sum(sizes), 0), dtype=torch.uint8, device="cuda:0")
     B, G = args.turbo_block, args.turbo_group
     general = args.turbo_general or (B, G) != (128, 64)
     states = [pa.TurboState(n, "cuda:0", compress_m=n >= 4096, compress_v=n >= 4096, v_bits=args.turbo_bits,
@@ -450,7 +452,7 @@ def run_turbo(args, cfg):
     n = sum(sizes)
     state = sum(st.nbytes() for st in states)
     tiles = sum((k + 255) // 256 for k in sizes if k >= 4096)   # residual partial sums, either kernel
-    algo = 12 * n + 2 * state + 16 * tiles     # p, g read; p written; state read and written; residual sums
+    algo = 3 * esz * n + 2 * state + 16 * tiles   # p, g read; p written; state read and written; residual sums
     achieved = algo / (mean_ms / 1e3) / 1e9
     log(f"timed {args.steps} TurboAdam steps: {mean_ms:.3f} ms/step (events), state {state / n:.4f} B/param")
     # The step is bound by vector ALU issue, not HBM: its roofline is the
@@ -458,7 +460,8 @@ def run_turbo(args, cfg):
     # the counters measured for this kernel source (profiles/), if current.
     valu = None
     vpath = os.path.join(ROOT, "profiles", f"valu_{args.workload}_turbo.json")
-    if os.path.exists(vpath) and args.turbo_bits == 4 and not args.count_nonfinite and not general:
+    if (os.path.exists(vpath) and args.turbo_bits == 4 and not args.count_nonfinite and not general
+            and args.param_dtype == "fp32"):
         with open(vpath) as f:
             vj = json.load(f)
         if vj.get("kernel_sha") == kernel_sha("turbo"):
@@ -466,8 +469,11 @@ def run_turbo(args, cfg):
     out = {"metric": f"TurboAdam step (UState + {args.turbo_bits}-bit 1Q state): params/s", "value": round(n * args.steps / elapsed, 1),
            "unit": "params/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(elapsed * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "vs_baseline": None,
+           "dtype": "f32" if args.param_dtype == "fp32" else f"f32 math, {args.param_dtype} params and grads",
+           "data": "synthetic",
            "config": {"workload": args.workload, "params": n, "tensors": len(sizes), "mode": f"turbo-ustate-1q{args.turbo_bits}",
+                      "param_dtype": args.param_dtype,
                       "block_size": B, "m_block_size": G,
                       "state_bytes": state, "state_bits_per_param": round(8 * state / n, 4),
                       "layout": args.layout, "count_nonfinite": bool(args.count_nonfinite)},
@@ -480,10 +486,11 @@ def run_turbo(args, cfg):
                         "hbm_achieved_gbps": round(achieved, 1), "hbm_frac": round(achieved / PEAK_GBPS, 4),
                         "traffic": None,
                         "kernel": f"{'turbo_general' if general else 'turbo_list'}<{args.turbo_bits}, "
-                                  f"{'true' if args.count_nonfinite else 'false'}> + turbo_chunks + turbo_reduce",
+                                  f"{'true' if args.count_nonfinite else 'false'}, "
+                                  f"{'false' if args.param_dtype == 'fp32' else 'true'}> + turbo_chunks + turbo_reduce",
                         "algorithmic_bytes_per_launch": algo, "mean_launch_ms": round(mean_ms, 4),
                         "kernel_sha": kernel_sha("turbo")}}
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.param_dtype == "fp32":
         import numpy as np
         import oracle
         picked, total = [], 0

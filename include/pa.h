@@ -270,7 +270,8 @@ int pa_grad_stats_list(int grad_dtype, size_t count, const void* const* grads, c
  *     else v_fp32, n floats.
  *   tensor_id keys the tensor's counter-based random draws (keep it fixed
  *   across steps and distinct across tensors).
- * Parameters and gradients are FP32, 16-byte aligned; m_fp32/v_fp32 16-byte,
+ * Parameters and gradients are FP32, 16-byte aligned (pa_turbo_step_list_typed
+ * also takes 16-bit ones, 8-byte aligned); m_fp32/v_fp32 16-byte,
  * m_codes/v_index/v_ends/scalars 4-byte, m_means 2-byte aligned
  * (PA_ERR_ALIGN otherwise).  With compress_m the page requires
  * beta1^2 < beta2 (PA_ERR_ARG otherwise).  The draws' counter holds the
@@ -293,7 +294,7 @@ typedef struct {
  * m_step_factor: the UState scale factor (the page's default 1.1).  seed:
  * the rounding seed (the page's default 0x12345678).  block_size,
  * m_block_size: B and G above, 0 for the defaults 128 and 64.  path: 0
- * picks the kernel (a tuned one for B = 128, G = 64 and 2, 4 or 8 bits,
+ * picks the kernel (a tuned one for B = 128, G = 64 at every index width,
  * the general one otherwise); 1 runs the general kernel for every layout
  * (the results are the same; for tests and measurement).  PA_ERR_ARG for
  * any other value or layout. */
@@ -334,6 +335,23 @@ size_t pa_turbo_workspace_bytes(size_t count, const pa_turbo_state* states, cons
 int pa_turbo_step_list(size_t count, float* const* params, const float* const* grads, const pa_turbo_state* states,
                        const size_t* n, const pa_hyper* hyper, const pa_turbo_config* config, long long step,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* pa_turbo_step_list with 16-bit parameters and/or gradients (the TurboAdam
+ * package page, Verification: its tests run fp16, bf16 and fp32
+ * parameters).  The pairs of pa_step_typed: (F32, F32), (BF16, BF16),
+ * (F16, F16), (BF16, F32), (F16, F32); PA_ERR_ARG for any other.  The
+ * update runs in FP32 exactly as for FP32 tensors: 16-bit values widen
+ * exactly and only the new parameter is rounded back to its type, to
+ * nearest even, so the state (which never depends on the parameters) is
+ * the state of the FP32 step on the widened values.  params[i] and
+ * grads[i] hold n[i] elements of their type (bfloat16 / binary16 as uint16
+ * bit patterns), aligned to four elements (16 bytes for FP32, 8 for 16-bit
+ * types; PA_ERR_ALIGN otherwise).  All other arguments, results and errors
+ * as for pa_turbo_step_list, which is the (F32, F32) case. */
+int pa_turbo_step_list_typed(int param_dtype, int grad_dtype, size_t count, void* const* params,
+                             const void* const* grads, const pa_turbo_state* states, const size_t* n,
+                             const pa_hyper* hyper, const pa_turbo_config* config, long long step, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /* Persistent optimizer-state bytes for n parameters in `mode` (the state
  * ledger; Packed AdamW Reference README, "The narrow result": 8 bytes per

@@ -73,6 +73,14 @@ int main() {
   pa_turbo_config tc4{4, 1.1, 1, 0, 0, 0};
   expect(pa_turbo_step_list(1, tp, tg, &ts, tn, &hb, &tc4, 1, reinterpret_cast<void*>(F + (1 << 26)), 1 << 20, nullptr),
          PA_ERR_ARG, "turbo betas");
+  void* tpv[1] = {P(F)};
+  const void* tgv[1] = {P(F + (1 << 20))};
+  expect(pa_turbo_step_list_typed(PA_DT_F32, PA_DT_BF16, 1, tpv, tgv, &ts, tn, &h, &tc4, 1,
+                                  reinterpret_cast<void*>(F + (1 << 26)), 1 << 20, nullptr),
+         PA_ERR_ARG, "turbo typed pair");
+  expect(pa_turbo_step_list_typed(PA_DT_BF16, PA_DT_BF16, 1, tpv, tgv, &ts, tn, &hb, &tc4, 1,
+                                  reinterpret_cast<void*>(F + (1 << 26)), 1 << 20, nullptr),
+         PA_ERR_ARG, "turbo typed betas");
   if (pa_turbo_state_bytes(1, 1, 4, 131072) != 106508 || pa_turbo_workspace_bytes(1, &ts, tn) != 136) ++bad;
   pa_format pf;
   for (int m = 0; m < 4; ++m) expect(pa_format_info(m, &pf), PA_OK, "format");

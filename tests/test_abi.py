@@ -274,6 +274,13 @@ def test_turbo_argument_rules(pa):
     N[0] = 4096
     hb = _hyper(pa, beta1=0.99, beta2=0.98)                               # beta1^2 >= beta2 with UState
     assert call(hb, cfg) == pa.PA_ERR_ARG
+    # the typed entry: the type pairs of pa_step_typed, checked before anything else
+    typed = lambda pdt, gdt: L.pa_turbo_step_list_typed(pdt, gdt, 1, P, G, S, N, ctypes.byref(hb), ctypes.byref(cfg),
+                                                         1, FAKE + 2 ** 26, 1 << 20, None)
+    for pdt, gdt in ((0, 1), (0, 2), (1, 2), (2, 1), (3, 0), (0, -1)):
+        assert typed(pdt, gdt) == pa.PA_ERR_ARG, (pdt, gdt)
+    for pdt, gdt in ((0, 0), (1, 1), (2, 2), (1, 0), (2, 0)):   # valid pairs reach the beta rule
+        assert typed(pdt, gdt) == pa.PA_ERR_ARG, (pdt, gdt)
     assert pa.pa_turbo_state_bytes(1, 1, 4, 131072) == 106508
     assert pa.pa_turbo_state_bytes(0, 0, 4, 10) == 80
     assert pa.pa_turbo_state_bytes(1, 1, 5, 10) == 0

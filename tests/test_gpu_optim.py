@@ -279,3 +279,68 @@ def test_turboadam_checkpoint_resume_is_bit_exact(bits, block, group):
     for sa, sc_ in zip(opt_a._states, opt_c._states):
         for ta, tc in zip(sa.tensors(), sc_.tensors()):
             assert torch.equal(ta, tc)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_turboadam_16bit_parameters_match_oracle_and_resume(dtype):
+    """TurboAdam over bfloat16 or float16 parameters (the TurboAdam package
+    page's tests run fp16, bf16 and fp32 parameters), gradients of the same
+    type, as torch's autograd leaves them: three steps against the oracle's
+    typed step, every state word and every 16-bit parameter bit for bit, then
+    a checkpoint written and restored mid-run continues bit for bit, the
+    packed codes keeping their dtypes."""
+    import torch
+    from adamw_step_amd.optim import TurboAdam
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16}[dtype]
+    pdt = {"bf16": oracle.DT_BF16, "fp16": oracle.DT_F16}[dtype]
+    sizes = [70000, 4096, 4095, 300]
+    r = np.random.Generator(np.random.PCG64(71))
+    ps = [torch.nn.Parameter(torch.from_numpy(r.normal(0, 0.02, n).astype(np.float32)).to(tdt).cuda())
+          for n in sizes]
+    hp = [p.detach().cpu().view(torch.int16).numpy().view(np.uint16).copy() for p in ps]
+    opt = TurboAdam(ps, lr=1e-3, weight_decay=0.01)
+    hs = _turbo_oracle_states(sizes)
+    grads = [[torch.from_numpy(r.normal(0, 1e-3, n).astype(np.float32)).to(tdt).cuda() for n in sizes]
+             for _ in range(6)]
+    for t in range(1, 4):
+        for p, g in zip(ps, grads[t - 1]):
+            p.grad = g.clone()
+        banner(f"TurboAdam {dtype} step {t}")
+        opt.step()
+        torch.cuda.synchronize()
+        sc = scalars(t)
+        ts = oracle.turbo_scalars(0.9, 0.999, t)
+        for i in range(len(sizes)):
+            hg = grads[t - 1][i].cpu().view(torch.int16).numpy().view(np.uint16).copy()
+            oracle.turbo_step_typed(pdt, pdt, hp[i], hg, hs[i], sc, ts, t, tensor_id=i)
+            got = ps[i].detach().cpu().view(torch.int16).numpy().view(np.uint16)
+            assert np.array_equal(got, hp[i]), f"step {t} tensor {i}: 16-bit parameters"
+            st = opt._states[i]
+            if hs[i].compress_m:
+                assert np.array_equal(st.m_codes.cpu().numpy().view(np.uint32), hs[i].m_codes)
+                assert np.array_equal(st.v_index.cpu().numpy().view(np.uint32), hs[i].v_index)
+                assert np.array_equal(st.scalars.cpu().numpy().view(np.uint32), hs[i].scal.view(np.uint32))
+            else:
+                assert np.array_equal(st.m_fp32.cpu().numpy().view(np.uint32), hs[i].m_fp32.view(np.uint32))
+    assert opt.nonfinite_count() == 0
+    buf = io.BytesIO()
+    torch.save({"p": [p.detach().cpu() for p in ps], "opt": opt.state_dict()}, buf)
+    buf.seek(0)
+    ck = torch.load(buf, weights_only=True)
+    ps_c = [torch.nn.Parameter(t.cuda()) for t in ck["p"]]
+    opt_c = TurboAdam(ps_c, lr=1e-3, weight_decay=0.01)
+    opt_c.load_state_dict(ck["opt"])
+    for sa, sc_ in zip(opt._states, opt_c._states):
+        for ta, tc in zip(sa.tensors(), sc_.tensors()):
+            assert ta.dtype == tc.dtype and torch.equal(ta, tc)
+    for run_ps, run_opt in ((ps, opt), (ps_c, opt_c)):
+        for gs in grads[3:]:
+            for p, g in zip(run_ps, gs):
+                p.grad = g.clone()
+            run_opt.step()
+    torch.cuda.synchronize()
+    for a, c in zip(ps, ps_c):
+        assert a.dtype == tdt and torch.equal(a.detach(), c.detach())
+    for sa, sc_ in zip(opt._states, opt_c._states):
+        for ta, tc in zip(sa.tensors(), sc_.tensors()):
+            assert torch.equal(ta, tc)
