@@ -2,11 +2,13 @@
 
 Follows the reference's execution contract (project page, Execution contract
 table): contiguous parameters and dense gradients on one device (FP32, or
-bfloat16/float16 with the update still in FP32),
-one parameter group, one global step, ordinary PyTorch forward and backward
-around it.  Every update is one pa_step_list launch over all parameters
-(see include/pa.h); this module only holds the state tensors and marshals
-arguments.
+bfloat16/float16 with the update still in FP32), one global step, ordinary
+PyTorch forward and backward around it.  Parameter groups (the TurboAdam
+page's API takes "parameters or parameter groups") each carry their own
+lr, betas, eps and weight decay; every update is one pa_step_list launch
+per group (see include/pa.h), all groups sharing the step number, the
+non-finite counter and one gradient pre-pass over every gradient.  This
+module only holds the state tensors and marshals arguments.
 
 Modes: "e4" (one uint32 word per parameter: E4M11 first moment, E4M12 RMS),
 "fp16" (the same word with binary16 lanes) and "fp32" (two FP32 moments).
@@ -23,11 +25,51 @@ from . import PA_FP32, PA_PACKED_E4, PA_PACKED_FP16, GradStats, StepList, pa_sta
 _MODES = {"e4": PA_PACKED_E4, "fp16": PA_PACKED_FP16, "fp32": PA_FP32}
 
 
+def _check_group_params(opt, group):
+    """Every parameter of the optimizer: contiguous, on one GPU, one dtype
+    (float32, bfloat16 or float16)."""
+    for p in group["params"]:
+        if opt._dtype is None:
+            if p.dtype not in (torch.float32, torch.bfloat16, torch.float16):
+                raise TypeError("parameters must be float32, bfloat16 or float16")
+            opt._dtype, opt._device = p.dtype, p.device
+        if p.dtype != opt._dtype or not p.is_cuda or not p.is_contiguous() or p.device != opt._device:
+            raise TypeError("parameters must be contiguous tensors of one dtype on one GPU")
+
+
+def _add_group(opt, param_group, init):
+    """torch's add_param_group, then the checks and the state of the new
+    parameters; a group that fails the checks is taken back out."""
+    torch.optim.Optimizer.add_param_group(opt, param_group)
+    group = opt.param_groups[-1]
+    try:
+        opt._check_group(group)
+        _check_group_params(opt, group)
+    except Exception:
+        opt.param_groups.pop()
+        raise
+    for p in group["params"]:
+        init(p)
+    opt._prepared = {}
+
+
+def _grads_of(params):
+    grads = []
+    for p in params:
+        g = p.grad
+        if g is None:
+            raise RuntimeError("every parameter needs a dense gradient on every update")
+        if g.is_sparse:
+            raise RuntimeError("sparse gradients are not supported")
+        grads.append(g if g.is_contiguous() else g.contiguous())
+    return grads
+
+
 class PackedAdamW(torch.optim.Optimizer):
     """AdamW with decoupled weight decay whose moments persist in packed form.
 
     Arguments keep their usual AdamW meaning (TurboAdam package page, API
-    section: lr, betas, eps, weight_decay).  ``count_nonfinite`` keeps a
+    section: lr, betas, eps, weight_decay), per parameter group.  ``count_nonfinite`` keeps a
     device counter of elements whose new parameter or moment was not finite
     (the optimizer non-finite count of the reference's smoke check); read it
     with ``nonfinite_count()``.
@@ -46,25 +88,16 @@ class PackedAdamW(torch.optim.Optimizer):
                  mode="e4", count_nonfinite=True, max_grad_norm=None, skip_nonfinite=False):
         if mode not in _MODES:
             raise ValueError(f"mode must be one of {sorted(_MODES)}")
-        defaults = dict(lr=lr, betas=betas, eps=eps, weight_decay=weight_decay)
-        super().__init__(params, defaults)
-        if len(self.param_groups) != 1:
-            raise ValueError("PackedAdamW takes one parameter group (one lr, one step for all)")
         self.mode = mode
         self._mode = _MODES[mode]
-        self.step_count = 0
-        self._prepared = None
-        self._prepared_key = None
-        plist = self.param_groups[0]["params"]
-        if not plist:
+        self._dtype = self._device = None
+        self._prepared = {}                 # group index -> (pointer key, StepList)
+        defaults = dict(lr=lr, betas=betas, eps=eps, weight_decay=weight_decay)
+        super().__init__(params, defaults)
+        if not any(g["params"] for g in self.param_groups):
             raise ValueError("no parameters")
-        dev, dt = plist[0].device, plist[0].dtype
-        if dt not in (torch.float32, torch.bfloat16, torch.float16):
-            raise TypeError("parameters must be float32, bfloat16 or float16")
-        for p in plist:
-            if p.dtype != dt or not p.is_cuda or not p.is_contiguous() or p.device != dev:
-                raise TypeError("parameters must be contiguous tensors of one dtype on one GPU")
-            self._init_state(p)
+        self.step_count = 0
+        dev = self._device
         self._nonfinite = torch.zeros(1, dtype=torch.int64, device=dev) if count_nonfinite else None
         if max_grad_norm is not None and not (float(max_grad_norm) > 0.0):
             raise ValueError("max_grad_norm must be positive")
@@ -81,6 +114,15 @@ class PackedAdamW(torch.optim.Optimizer):
             self._bad_event = torch.cuda.Event()
             self._pending = False
 
+    def add_param_group(self, param_group):
+        _add_group(self, param_group, self._init_state)
+
+    def _check_group(self, group):
+        pass
+
+    def _params(self):
+        return [p for g in self.param_groups for p in g["params"]]
+
     def _init_state(self, p):
         st = self.state[p]
         if self._mode == PA_FP32:
@@ -95,7 +137,7 @@ class PackedAdamW(torch.optim.Optimizer):
 
     def state_bytes(self):
         """Persistent optimizer-state bytes (the ledger): 4 per parameter packed, 8 for FP32."""
-        return sum(pa_state_bytes(self._mode, p.numel()) for p in self.param_groups[0]["params"])
+        return sum(pa_state_bytes(self._mode, p.numel()) for p in self._params())
 
     def nonfinite_count(self):
         return 0 if self._nonfinite is None else int(self._nonfinite.item())
@@ -121,46 +163,44 @@ class PackedAdamW(torch.optim.Optimizer):
         if closure is not None:
             with torch.enable_grad():
                 loss = closure()
-        group = self.param_groups[0]
-        params = group["params"]
-        grads = []
-        for p in params:
-            g = p.grad
-            if g is None:
-                raise RuntimeError("every parameter needs a dense gradient on every update")
-            if g.is_sparse:
-                raise RuntimeError("sparse gradients are not supported")
-            if not g.is_contiguous():
-                g = g.contiguous()
-            grads.append(g)
-        states = [self._state_of(p) for p in params]
-        key = tuple(g.data_ptr() for g in grads) + tuple(p.data_ptr() for p in params)
-        if self._prepared is None or key != self._prepared_key:
-            self._prepared = StepList(self._mode, params, grads, states)
-            self._prepared_key = key
+        work, all_grads = [], []
+        for gi, group in enumerate(self.param_groups):
+            if not group["params"]:
+                continue
+            grads = _grads_of(group["params"])
+            work.append((gi, group, grads))
+            all_grads += grads
         self._reconcile()
         self.step_count += 1
-        beta1, beta2 = group["betas"]
-        hyper = dict(lr=group["lr"], beta1=beta1, beta2=beta2, eps=group["eps"],
-                     weight_decay=group["weight_decay"])
+        common = {}
         if self._nonfinite is not None:
-            hyper["nonfinite"] = self._nonfinite
+            common["nonfinite"] = self._nonfinite
         if self.max_grad_norm is not None or self.skip_nonfinite:
-            gkey = tuple(g.data_ptr() for g in grads)
+            gkey = tuple(g.data_ptr() for g in all_grads)
             if self._stats is None or gkey != self._stats_key:
-                self._stats = GradStats(grads)
+                self._stats = GradStats(all_grads)
                 self._stats_key = gkey
             self._stats.run(self._sumsq, self._grad_bad,
                             self._clip if self.max_grad_norm is not None else None,
                             max_norm=self.max_grad_norm or 0.0)
             if self.max_grad_norm is not None:
-                hyper["grad_scale"] = self._clip
+                common["grad_scale"] = self._clip
             if self.skip_nonfinite:
-                hyper["skip_if_nonzero"] = self._grad_bad
+                common["skip_if_nonzero"] = self._grad_bad
                 self._bad_host.copy_(self._grad_bad, non_blocking=True)
                 self._bad_event.record()
                 self._pending = True
-        self._prepared.step(hyper, self.step_count)
+        for gi, group, grads in work:
+            params = group["params"]
+            key = tuple(g.data_ptr() for g in grads) + tuple(p.data_ptr() for p in params)
+            cached = self._prepared.get(gi)
+            if cached is None or cached[0] != key:
+                cached = (key, StepList(self._mode, params, grads, [self._state_of(p) for p in params]))
+                self._prepared[gi] = cached
+            beta1, beta2 = group["betas"]
+            hyper = dict(lr=group["lr"], beta1=beta1, beta2=beta2, eps=group["eps"],
+                         weight_decay=group["weight_decay"], **common)
+            cached[1].step(hyper, self.step_count)
         return loss
 
     def state_dict(self):
@@ -187,7 +227,7 @@ class PackedAdamW(torch.optim.Optimizer):
         base = {k: v for k, v in state_dict.items() if k not in ("packed", "state")}
         base["state"] = rest
         super().load_state_dict(base)
-        params = self.param_groups[0]["params"]
+        params = self._params()
         for idx, tensors in raw.items():
             p = params[idx]
             for k, t in tensors.items():
@@ -200,7 +240,7 @@ class PackedAdamW(torch.optim.Optimizer):
                 if torch.is_tensor(v) and not v.is_contiguous():
                     st[k] = v.contiguous()
         self.step_count = int(meta.get("step", 0))
-        self._prepared = None
+        self._prepared = {}
         if self._stats is not None:
             self._pending = False
 
@@ -219,11 +259,15 @@ class TurboAdam(torch.optim.Optimizer):
     m_step_factor and rounding_seed.  The default layout (128, 4 bits, 64)
     runs the tuned kernel at every index width, every other layout the
     general kernel.  The page's validation of beta1^2 < beta2 with UState on
-    is kept.  One parameter group of contiguous tensors of one dtype on one
-    GPU: float32, bfloat16 or float16 (the page's tests run all three; the
-    update runs in FP32 and only the new parameter is rounded back), with
-    gradients of the same dtype; ``count_nonfinite``, ``nonfinite_count()``
-    and ``state_bytes()`` as for PackedAdamW.
+    is kept, per parameter group.  Parameter groups carry their own lr,
+    betas, eps and weight decay (one launch each); the layout, thresholds,
+    scale factor and seed are the optimizer's.  Contiguous tensors of one
+    dtype on one GPU: float32, bfloat16 or float16 (the page's tests run all
+    three; the update runs in FP32 and only the new parameter is rounded
+    back), with gradients of the same dtype.  Tensors are numbered across
+    the groups in order; the number keys their random draws.
+    ``count_nonfinite``, ``nonfinite_count()`` and ``state_bytes()`` as for
+    PackedAdamW.
     """
 
     def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0, block_size=128, v_bits=4,
@@ -233,36 +277,37 @@ class TurboAdam(torch.optim.Optimizer):
         if not turbo_layout_ok(v_bits, block_size, m_block_size):
             raise ValueError("v_bits must be 2, 3, 4, 6 or 8, block_size a power of two from 32 to 1024 and "
                              "m_block_size a power of two dividing block_size")
-        if compress_m and not betas[0] ** 2 < betas[1]:
-            raise ValueError("UState needs beta1**2 < beta2")
-        defaults = dict(lr=lr, betas=betas, eps=eps, weight_decay=weight_decay)
-        super().__init__(params, defaults)
-        if len(self.param_groups) != 1:
-            raise ValueError("TurboAdam here takes one parameter group (one lr, one step for all)")
-        plist = self.param_groups[0]["params"]
-        if not plist:
-            raise ValueError("no parameters")
-        dev, dt = plist[0].device, plist[0].dtype
-        if dt not in (torch.float32, torch.bfloat16, torch.float16):
-            raise TypeError("parameters must be float32, bfloat16 or float16")
-        for p in plist:
-            if p.dtype != dt or not p.is_cuda or not p.is_contiguous() or p.device != dev:
-                raise TypeError("parameters must be contiguous tensors of one dtype on one GPU")
         self.v_bits, self.m_step_factor, self.seed = v_bits, float(m_step_factor), int(rounding_seed)
         self.block_size, self.m_block_size = int(block_size), int(m_block_size)
-        self.step_count = 0
-        self._TurboList = TurboList
+        self._compress = (bool(compress_m), bool(compress_v), int(min_m_compress_elements),
+                          int(min_v_compress_elements))
+        self._TurboList, self._TurboState = TurboList, TurboState
+        self._dtype = self._device = None
         self._states = []
-        for i, p in enumerate(plist):
-            n = p.numel()
-            st = TurboState(n, dev, compress_m=compress_m and n >= min_m_compress_elements,
-                            compress_v=compress_v and n >= min_v_compress_elements, v_bits=v_bits, tensor_id=i,
-                            block_size=block_size, m_block_size=m_block_size)
-            self._states.append(st)
-            self.state[p]["turbo"] = st
-        self._prepared = None
-        self._prepared_key = None
-        self._nonfinite = torch.zeros(1, dtype=torch.int64, device=dev) if count_nonfinite else None
+        self._prepared = {}                 # group index -> (pointer key, TurboList)
+        defaults = dict(lr=lr, betas=betas, eps=eps, weight_decay=weight_decay)
+        super().__init__(params, defaults)
+        if not self._states:
+            raise ValueError("no parameters")
+        self.step_count = 0
+        self._nonfinite = torch.zeros(1, dtype=torch.int64, device=self._device) if count_nonfinite else None
+
+    def add_param_group(self, param_group):
+        _add_group(self, param_group, self._init_state)
+
+    def _check_group(self, group):
+        beta1, beta2 = group["betas"]
+        if self._compress[0] and not beta1 ** 2 < beta2:
+            raise ValueError("UState needs beta1**2 < beta2")
+
+    def _init_state(self, p):
+        cm, cv, min_m, min_v = self._compress
+        n = p.numel()
+        st = self._TurboState(n, p.device, compress_m=cm and n >= min_m, compress_v=cv and n >= min_v,
+                              v_bits=self.v_bits, tensor_id=len(self._states), block_size=self.block_size,
+                              m_block_size=self.m_block_size)
+        self._states.append(st)
+        self.state[p]["turbo"] = st
 
     def state_bytes(self):
         """Persistent optimizer-state bytes: codes, means, indices, endpoints,
@@ -278,25 +323,25 @@ class TurboAdam(torch.optim.Optimizer):
         if closure is not None:
             with torch.enable_grad():
                 loss = closure()
-        group = self.param_groups[0]
-        params = group["params"]
-        grads = []
-        for p in params:
-            if p.grad is None or p.grad.is_sparse:
-                raise RuntimeError("every parameter needs a dense gradient on every update")
-            grads.append(p.grad if p.grad.is_contiguous() else p.grad.contiguous())
-        key = tuple(g.data_ptr() for g in grads)
-        if self._prepared is None or key != self._prepared_key:
-            self._prepared = self._TurboList(params, grads, self._states, v_bits=self.v_bits,
-                                             m_step_factor=self.m_step_factor, seed=self.seed,
-                                             block_size=self.block_size, m_block_size=self.m_block_size)
-            self._prepared_key = key
+        work = [(gi, group, _grads_of(group["params"])) for gi, group in enumerate(self.param_groups)
+                if group["params"]]
         self.step_count += 1
-        beta1, beta2 = group["betas"]
-        hyper = dict(lr=group["lr"], beta1=beta1, beta2=beta2, eps=group["eps"], weight_decay=group["weight_decay"])
-        if self._nonfinite is not None:
-            hyper["nonfinite"] = self._nonfinite
-        self._prepared.step(hyper, self.step_count)
+        for gi, group, grads in work:
+            params = group["params"]
+            key = tuple(g.data_ptr() for g in grads) + tuple(p.data_ptr() for p in params)
+            cached = self._prepared.get(gi)
+            if cached is None or cached[0] != key:
+                states = [self.state[p]["turbo"] for p in params]
+                cached = (key, self._TurboList(params, grads, states, v_bits=self.v_bits,
+                                               m_step_factor=self.m_step_factor, seed=self.seed,
+                                               block_size=self.block_size, m_block_size=self.m_block_size))
+                self._prepared[gi] = cached
+            beta1, beta2 = group["betas"]
+            hyper = dict(lr=group["lr"], beta1=beta1, beta2=beta2, eps=group["eps"],
+                         weight_decay=group["weight_decay"])
+            if self._nonfinite is not None:
+                hyper["nonfinite"] = self._nonfinite
+            cached[1].step(hyper, self.step_count)
         return loss
 
     def state_dict(self):
@@ -320,6 +365,8 @@ class TurboAdam(torch.optim.Optimizer):
             raise ValueError("checkpoint was written with another v_bits or rounding seed")
         if (meta.get("block_size", 128), meta.get("m_block_size", 64)) != (self.block_size, self.m_block_size):
             raise ValueError("checkpoint was written with another block_size or m_block_size")
+        if len(state_dict["param_groups"]) != len(self.param_groups) or len(state_dict["state"]) != len(self._states):
+            raise ValueError("checkpoint has another number of parameter groups or tensors")
         for g, saved in zip(self.param_groups, state_dict["param_groups"]):
             for k, v in saved.items():
                 g[k] = v
@@ -336,4 +383,4 @@ class TurboAdam(torch.optim.Optimizer):
                     t.copy_(src.to(t.device))
         self.step_count = int(meta["step"])
         self.m_step_factor = float(meta["m_step_factor"])
-        self._prepared = None
+        self._prepared = {}
