@@ -1,11 +1,16 @@
 """Synthetic-tape training loop, checkpoints and the one-update smoke gates.
 
-Tapes: seeded uint32 tokens below the vocabulary size, read sequentially
-without wrapping (Packed AdamW Reference README, Training on prepared tapes:
-sequential, never wraps).  Smoke gates (same README, One-update smoke
-test): finite train and validation loss, zero optimizer non-finite count, a
-one-word state ledger, and a checkpoint that round-trips.
+Tapes (Packed AdamW Reference README, Training on prepared tapes): a
+little-endian uint32 token tape and an optional aligned little-endian uint16
+tape of each token's length in bytes, memory-mapped from files, or seeded
+synthetic tokens below the vocabulary size; either is read sequentially and
+never wraps.  With byte lengths, evaluation reports bits per byte: the
+summed cross-entropy of the predicted tokens in bits over their bytes.
+Smoke gates (same README, One-update smoke test): finite train and
+validation loss, zero optimizer non-finite count, a one-word state ledger,
+and a checkpoint that round-trips.
 """
+import math
 import time
 
 import numpy as np
@@ -15,8 +20,11 @@ from .gpt import GPT, count_params, lr_at
 
 
 class Tape:
-    def __init__(self, tokens, batch, seq):
+    def __init__(self, tokens, batch, seq, byte_lengths=None):
+        if byte_lengths is not None and len(byte_lengths) != len(tokens):
+            raise ValueError("the byte-length tape must hold one length per token")
         self.tokens = tokens
+        self.byte_lengths = byte_lengths
         self.batch, self.seq = batch, seq
         self.cursor = 0
 
@@ -25,15 +33,58 @@ class Tape:
         r = np.random.Generator(np.random.PCG64(seed))
         return Tape(r.integers(0, vocab, n_tokens, dtype=np.int64), 1, 1)
 
-    def next(self, device):
+    @staticmethod
+    def from_files(tokens_path, batch, seq, byte_lengths_path=None):
+        """Memory-map a little-endian uint32 token tape and, optionally, its
+        aligned little-endian uint16 byte-length tape."""
+        tokens = np.memmap(tokens_path, dtype="<u4", mode="r")
+        lengths = None if byte_lengths_path is None else np.memmap(byte_lengths_path, dtype="<u2", mode="r")
+        return Tape(tokens, batch, seq, lengths)
+
+    def _take(self):
         need = self.batch * self.seq + 1
-        if self.cursor + need > self.tokens.size:
+        if self.cursor + need > len(self.tokens):
             raise RuntimeError("token tape exhausted (the trainer does not wrap)")
-        chunk = torch.from_numpy(self.tokens[self.cursor:self.cursor + need])
+        a = self.cursor
         self.cursor += self.batch * self.seq
+        return a, need
+
+    def next(self, device):
+        x, y, _ = self.next_with_bytes(device)
+        return x, y
+
+    def next_with_bytes(self, device):
+        """The next window; the third value is the byte count of its predicted
+        tokens (None without a byte-length tape)."""
+        a, need = self._take()
+        chunk = torch.from_numpy(np.asarray(self.tokens[a:a + need], dtype=np.int64))
         x = chunk[:-1].view(self.batch, self.seq)
         y = chunk[1:].view(self.batch, self.seq)
-        return x.to(device), y.to(device)
+        nbytes = None
+        if self.byte_lengths is not None:
+            nbytes = int(np.asarray(self.byte_lengths[a + 1:a + need], dtype=np.int64).sum())
+        return x.to(device), y.to(device), nbytes
+
+
+def bits_per_byte(nats, nbytes):
+    """Cross-entropy summed over predicted tokens (nats), in bits per byte."""
+    return nats / (math.log(2.0) * nbytes)
+
+
+@torch.no_grad()
+def evaluate(model, tape, batches, device):
+    """Mean cross-entropy per token over `batches` windows, and bits per byte
+    when the tape carries byte lengths."""
+    nats, tokens, nbytes = 0.0, 0, 0
+    for _ in range(batches):
+        x, y, b = tape.next_with_bytes(device)
+        loss = float(model(x, y))
+        nats += loss * y.numel()
+        tokens += y.numel()
+        if b is not None:
+            nbytes += b
+    mean = nats / max(1, tokens)
+    return mean, (bits_per_byte(nats, nbytes) if tape.byte_lengths is not None and nbytes > 0 else None)
 
 
 def make_optimizer(model, kind, lr, weight_decay=0.01):
