@@ -191,22 +191,32 @@ def test_llama_7b_grad_stats_exact(pa):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("bits,block,group", [(4, 128, 64), (3, 128, 64)], ids=["default", "3bit-general"])
-def test_llama_7b_turbo_sampled_tensors(pa, bits, block, group):
+@pytest.mark.parametrize("bits,block,group,general,dtype",
+                         [(4, 128, 64, False, "fp32"), (3, 128, 64, False, "fp32"), (3, 128, 64, True, "fp32"),
+                          (4, 128, 64, False, "bf16")],
+                         ids=["default", "3bit", "3bit-general", "bf16"])
+def test_llama_7b_turbo_sampled_tensors(pa, bits, block, group, general, dtype):
     """The TurboAdam step over the whole 291-tensor list in the benchmark's
     launch configuration; five whole tensors (tensors are independent: each
     has its own draws, groups, blocks and scales) against the oracle for
     three steps, so that codes written with a nonzero scale are decoded: the
     embedding (131 M values, 256 chunks of residual sums), the first RMSNorm
     gain (FP32 moments), the first query and gate projections, and the final
-    norm.  Once with the tuned kernel at the page's defaults, once with the
-    general kernel at 3-bit indices (the benchmark's --turbo-bits 3)."""
+    norm.  The configurations the benchmark times: the page's defaults and
+    3-bit indices on the tuned kernel, 3-bit indices on the general kernel
+    (--turbo-general), and bfloat16 parameters and gradients
+    (--param-dtype bf16)."""
     import torch
     cfg = 4
     sizes = workloads.sizes(cfg)
-    banner(f"llama-7b TurboAdam: allocating {sum(sizes) * 8 / 1e9:.1f} GB of params and grads")
-    ps = [torch.empty(n, dtype=torch.float32, device="cuda:0") for n in sizes]
-    gs = [torch.empty(n, dtype=torch.float32, device="cuda:0") for n in sizes]
+    tdt = {"fp32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    pdt = {"fp32": oracle.DT_F32, "bf16": oracle.DT_BF16}[dtype]
+
+    def host(t):
+        return to_host(t).copy() if dtype == "fp32" else to_host(t.view(torch.int16)).view(np.uint16).copy()
+    banner(f"llama-7b TurboAdam ({dtype}): allocating params and grads for {sum(sizes) / 1e9:.2f} G values")
+    ps = [torch.empty(n, dtype=tdt, device="cuda:0") for n in sizes]
+    gs = [torch.empty(n, dtype=tdt, device="cuda:0") for n in sizes]
     states = [pa.TurboState(n, "cuda:0", n >= 4096, n >= 4096, bits, tensor_id=i, block_size=block,
                             m_block_size=group) for i, n in enumerate(sizes)]
     pick = [i for i, (name, _) in enumerate(workloads.shapes(cfg)) if "norm" in name][:1]
@@ -216,20 +226,21 @@ def test_llama_7b_turbo_sampled_tensors(pa, bits, block, group):
     pick = sorted(set(pick))
     try:
         workloads.device_fill_params(cfg, ps)
-        tl = pa.TurboList(ps, gs, states, v_bits=bits, block_size=block, m_block_size=group)
-        hp = {i: to_host(ps[i]).copy() for i in pick}
+        tl = pa.TurboList(ps, gs, states, v_bits=bits, block_size=block, m_block_size=group, general=general)
+        hp = {i: host(ps[i]) for i in pick}
         hs = {i: oracle.TurboState(sizes[i], sizes[i] >= 4096, sizes[i] >= 4096, bits, block, group) for i in pick}
         for t in (1, 2, 3):
             workloads.device_fill_grads(cfg, t, gs)
             torch.cuda.synchronize()
-            hg = {i: to_host(gs[i]).copy() for i in pick}
-            banner(f"llama-7b TurboAdam ({bits} bits, {block}/{group}) step {t}: one launch over 291 tensors")
+            hg = {i: host(gs[i]) for i in pick}
+            banner(f"llama-7b TurboAdam ({bits} bits, {block}/{group}, general {general}, {dtype}) step {t}: "
+                   "one launch over 291 tensors")
             tl.step(dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01), t)
             torch.cuda.synchronize()
             sc = scalars(t)
             ts = oracle.turbo_scalars(0.9, 0.999, t)
             for i in pick:
-                oracle.turbo_step(hp[i], hg[i], hs[i], sc, ts, t, tensor_id=i)
+                oracle.turbo_step_typed(pdt, pdt, hp[i], hg[i], hs[i], sc, ts, t, tensor_id=i)
                 st = states[i]
                 if hs[i].compress_m:
                     assert np.array_equal(to_host(st.m_codes).view(np.uint32), hs[i].m_codes), f"tensor {i} codes"
@@ -237,7 +248,10 @@ def test_llama_7b_turbo_sampled_tensors(pa, bits, block, group):
                     assert np.array_equal(to_host(st.scalars).view(np.uint32), hs[i].scal.view(np.uint32))
                     assert np.array_equal(to_host(st.v_index).view(np.uint32), hs[i].v_index), f"tensor {i} index"
                     assert np.array_equal(to_host(st.v_ends).view(np.uint16), hs[i].v_ends), f"tensor {i} ends"
-                assert_params(to_host(ps[i]), hp[i], what=f"tensor {i} params")
+                if dtype == "fp32":
+                    assert_params(to_host(ps[i]), hp[i], what=f"tensor {i} params")
+                else:
+                    assert np.array_equal(host(ps[i]), hp[i]), f"tensor {i} bf16 params"
             banner(f"llama-7b TurboAdam step {t}: tensors {pick} bit-exact")
     finally:
         del ps, gs, states
