@@ -331,7 +331,10 @@ size_t pa_turbo_workspace_bytes(size_t count, const pa_turbo_state* states, cons
  * pa_turbo_workspace_bytes (8-byte aligned).  The launch plan is cached per
  * distinct list (see pa_release_plans).  Written buffers may not overlap
  * each other, the gradients or the workspace (PA_ERR_ALIAS).  hyper's
- * non-finite counter, gradient scale and skip flag work as for pa_step. */
+ * non-finite counter, gradient scale and skip flag work as for pa_step.
+ * Once a list's plan exists, a call enqueues its kernels and nothing else,
+ * so it can be captured in a HIP graph (a captured call keeps its step and
+ * scalars). */
 int pa_turbo_step_list(size_t count, float* const* params, const float* const* grads, const pa_turbo_state* states,
                        const size_t* n, const pa_hyper* hyper, const pa_turbo_config* config, long long step,
                        void* workspace, size_t workspace_bytes, void* stream);

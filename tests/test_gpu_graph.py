@@ -92,3 +92,50 @@ def test_graph_replay_matches_eager(pa, mode, noalloc):
             b.mul_(1.5)
         torch.cuda.synchronize()
     banner(f"graph: 4 replays bit-identical to eager, counter {int(cnt_g.item())}")
+
+
+@pytest.mark.parametrize("general,dtype", [(False, "fp32"), (True, "fp32"), (False, "bf16")],
+                         ids=["tuned", "general", "tuned-bf16"])
+def test_turbo_graph_replay_matches_eager(pa, general, dtype):
+    """The TurboAdam list step (its step kernel, the chunk pass over the
+    residual sums and the per-tensor scale rotation) captured once its plan
+    exists and replayed: every replay is the eager call with the same step
+    number on a copy, bit for bit, state words and scales included."""
+    import torch
+    tdt = {"fp32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    sizes = [1, 300, 4096 + 77, 70001, 1 << 18]
+    g = torch.Generator(device="cuda:0").manual_seed(77)
+    ps = [(torch.randn(n, device="cuda:0", generator=g) * 0.02).to(tdt) for n in sizes]
+    gs = [(torch.randn(n, device="cuda:0", generator=g) * 1e-3).to(tdt) for n in sizes]
+    pe, ge = [p.clone() for p in ps], [x.clone() for x in gs]
+
+    def states():
+        return [pa.TurboState(n, "cuda:0", n >= 4096, n >= 4096, tensor_id=i) for i, n in enumerate(sizes)]
+    sg, se = states(), states()
+    tl_g = pa.TurboList(ps, gs, sg, general=general)
+    tl_e = pa.TurboList(pe, ge, se, general=general)
+    H = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    banner(f"turbo graph ({'general' if general else 'tuned'}, {dtype}): eager step 1 on both (plans)")
+    tl_g.step(H, 1)
+    tl_e.step(H, 1)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=side):
+        tl_g.step(H, 2, stream=side)
+    torch.cuda.synchronize()
+    for r in range(4):
+        banner(f"turbo graph: replay {r}")
+        graph.replay()
+        tl_e.step(H, 2)
+        torch.cuda.synchronize()
+        for i in range(len(sizes)):
+            assert torch.equal(ps[i].view(torch.int16 if dtype == "bf16" else torch.int32),
+                               pe[i].view(torch.int16 if dtype == "bf16" else torch.int32)), f"replay {r} params {i}"
+            for a, b in zip(sg[i].tensors(), se[i].tensors()):
+                assert torch.equal(a, b), f"replay {r} state of tensor {i}"
+        for a, b in zip(gs, ge):
+            a.mul_(1.5)
+            b.mul_(1.5)
+        torch.cuda.synchronize()
