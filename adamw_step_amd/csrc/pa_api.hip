@@ -1413,7 +1413,7 @@ int pa_debug_q1_ends(const float* in, uint32_t* out, size_t n, void* stream) {
 }
 
 int pa_debug_q1_levels(const uint32_t* ends, int bits, int exact, float* out, size_t n, void* stream) {
-  if (bits != 2 && bits != 4 && bits != 8) return PA_ERR_ARG;
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 6 && bits != 8) return PA_ERR_ARG;
   if (n == 0) return PA_OK;
   if (ends == nullptr || out == nullptr || n > ((size_t)1 << 40)) return PA_ERR_ARG;
   if (!aligned(ends, 4) || !aligned(out, 4)) return PA_ERR_ALIGN;
@@ -1426,12 +1426,13 @@ int pa_debug_q1_levels(const uint32_t* ends, int bits, int exact, float* out, si
   const dim3 grid((unsigned)grid_for(blocks, d, d.blocks_per_cu)), block(pa::kThreads);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const int ex = exact ? 1 : 0;
-  if (bits == 2)
-    hipLaunchKernelGGL(pa::q1_levels_kernel<2>, grid, block, 0, st, ends, ex, out, (long long)n);
-  else if (bits == 4)
-    hipLaunchKernelGGL(pa::q1_levels_kernel<4>, grid, block, 0, st, ends, ex, out, (long long)n);
-  else
-    hipLaunchKernelGGL(pa::q1_levels_kernel<8>, grid, block, 0, st, ends, ex, out, (long long)n);
+  switch (bits) {
+    case 2: hipLaunchKernelGGL(pa::q1_levels_kernel<2>, grid, block, 0, st, ends, ex, out, (long long)n); break;
+    case 3: hipLaunchKernelGGL(pa::q1_levels_kernel<3>, grid, block, 0, st, ends, ex, out, (long long)n); break;
+    case 4: hipLaunchKernelGGL(pa::q1_levels_kernel<4>, grid, block, 0, st, ends, ex, out, (long long)n); break;
+    case 6: hipLaunchKernelGGL(pa::q1_levels_kernel<6>, grid, block, 0, st, ends, ex, out, (long long)n); break;
+    default: hipLaunchKernelGGL(pa::q1_levels_kernel<8>, grid, block, 0, st, ends, ex, out, (long long)n); break;
+  }
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? PA_OK : hip_failed(e);
 }

@@ -1268,7 +1268,7 @@ __global__ void __launch_bounds__(kThreads) pow2_rn32_kernel(const double* x, in
 // Self-test export: the levels of endpoint word ends[w] at out[w L + k],
 // one half-wavefront per word.  exact = 0: through the step's own table
 // builders (build_tables for indices of at most 4 bits, build_levels for
-// 8); exact != 0: every level through the double-double evaluation.
+// 6 and 8); exact != 0: every level through the double-double evaluation.
 template <int BITS>
 __global__ void __launch_bounds__(kThreads) q1_levels_kernel(const uint32_t* ends, int exact, float* out, long long n) {
   constexpr int L = 1 << BITS;

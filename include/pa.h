@@ -430,7 +430,7 @@ int pa_debug_q1_ends(const float* in, uint32_t* out, size_t n, void* stream);
 
 /* 1Q level self-test export: for n device endpoint words ends[i] (low 16
  * bits the fp16 lower log2 endpoint, high 16 bits the upper one) and
- * L = 2^bits (bits 2, 4 or 8), out[i*L + k] = level k of that block as the
+ * L = 2^bits (bits 2, 3, 4, 6 or 8), out[i*L + k] = level k of that block as the
  * TurboAdam step decodes it (TurboAdam package page, 1Q): 0 for k = 0, else
  * the exact power 2^x, x = lo + (hi - lo)(k - 1)/(L - 2) in double, rounded
  * once to binary32.  exact = 0 takes the step's own table builders (the

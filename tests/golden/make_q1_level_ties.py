@@ -11,8 +11,9 @@ double exp2 rounded again.
 Input selection only: seeded random (lo, hi, bits, k) over every finite fp16
 endpoint pair in [-149, 128], screened with numpy's 64-bit-significand
 exp2 (long double) for a relative distance to the nearest midpoint below
-2^-47.  Every stored level comes from oracle.q1_levels; the tests check
-each one against a 60-digit decimal power.
+2^-47; one seeded pass over the widths 2, 4 and 8, a second over 3 and 6.
+Every stored level comes from oracle.q1_levels; the tests check each one
+against a 60-digit decimal power.
 """
 import json
 import os
@@ -27,16 +28,17 @@ import oracle  # noqa: E402
 
 OUT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "q1_level_ties.json")
 SEED = 20260
+SEED_3_6 = 20261
 ROUNDS = 32
 BATCH = 1 << 22
 LIMIT = 2.0 ** -47
 
 
-def screen(rng, pool):
+def screen(rng, pool, widths):
     a = rng.choice(pool, BATCH).view(np.float16).astype(np.float64)
     b = rng.choice(pool, BATCH).view(np.float16).astype(np.float64)
     lo, hi = np.minimum(a, b), np.maximum(a, b)
-    bits = rng.choice(np.array([2, 4, 8]), BATCH)
+    bits = rng.choice(np.array(widths), BATCH)
     L = (1 << bits).astype(np.float64)
     k = np.floor(rng.random(BATCH) * (L - 1)) + 1
     x = lo + ((hi - lo) * (k - 1)) / (L - 2)
@@ -53,16 +55,17 @@ def screen(rng, pool):
 
 
 def main():
-    rng = np.random.Generator(np.random.PCG64(SEED))
     codes = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
     vals = codes.view(np.float16).astype(np.float64)
     pool = codes[np.isfinite(vals) & (vals >= -149) & (vals <= 128)]
     found = {}
-    for _ in range(ROUNDS):
-        for log2d, lo, hi, bits, k in screen(rng, pool):
-            lo16 = int(np.array([lo]).view(np.uint16)[0])
-            hi16 = int(np.array([hi]).view(np.uint16)[0])
-            found.setdefault((lo16, hi16, bits, k), log2d)
+    for seed, widths in ((SEED, [2, 4, 8]), (SEED_3_6, [3, 6])):
+        rng = np.random.Generator(np.random.PCG64(seed))
+        for _ in range(ROUNDS):
+            for log2d, lo, hi, bits, k in screen(rng, pool, widths):
+                lo16 = int(np.array([lo]).view(np.uint16)[0])
+                hi16 = int(np.array([hi]).view(np.uint16)[0])
+                found.setdefault((lo16, hi16, bits, k), log2d)
     rows = []
     for (lo16, hi16, bits, k), log2d in sorted(found.items(), key=lambda kv: kv[1]):
         lev = oracle.q1_levels(lo16, hi16, bits)
@@ -72,7 +75,8 @@ def main():
     with open(OUT, "w") as f:
         json.dump({"source": "TurboAdam package page, 1Q (logarithmic grid levels)",
                    "recipe": " ".join(__doc__.split("\n\n")[2].split()),
-                   "seed": SEED, "samples": ROUNDS * BATCH, "rows": rows}, f, indent=1)
+                   "seed": SEED, "seed_3_6": SEED_3_6, "samples": 2 * ROUNDS * BATCH, "rows": rows}, f,
+                  indent=1)
     print(OUT, len(rows))
 
 

@@ -288,7 +288,7 @@ def _endpoint_words(r, n):
     return lo.astype(np.uint32) | (hi.astype(np.uint32) << 16)
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 6, 8])
 def test_q1_levels_match_oracle(pa, bits):
     """1Q grid levels (the exact 2^x rounded once to binary32) equal the
     oracle's bit for bit, through the step's own table builders (the device
@@ -298,7 +298,7 @@ def test_q1_levels_match_oracle(pa, bits):
     the whole endpoint range, the committed near-midpoint blocks, one-level
     blocks, and the range ends (+inf at 128, the smallest subnormal at -149)."""
     import torch
-    n = {2: 1 << 22, 4: 1 << 20, 8: 1 << 16}[bits]
+    n = {2: 1 << 22, 3: 1 << 21, 4: 1 << 20, 6: 1 << 18, 8: 1 << 16}[bits]
     words = _endpoint_words(np.random.default_rng(40 + bits), n)
     sel = [t for t in TIES if t["bits"] == bits]
     ties = [int(t["lo16"], 16) | (int(t["hi16"], 16) << 16) for t in sel]
