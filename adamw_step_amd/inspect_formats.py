@@ -6,7 +6,9 @@ The table comes from pa_format_info (host code, no device needed) and, like
 the reference's format inspection command (Packed AdamW Reference README,
 Dependency-light inspection), imports neither torch nor any kernel
 framework.  --examples additionally runs a few values through the GPU
-codecs (pa_debug_codec) and so needs a GPU and torch.
+codecs (pa_debug_codec) and one packed E4 update of a few parameters
+through pa_step, and so needs a GPU and torch (without one it says so and
+exits with status 2).
 """
 import argparse
 import ctypes
@@ -92,14 +94,91 @@ def examples():
     return "\n".join(lines)
 
 
+def _decode_words(pa, torch, words):
+    """(m, r) decoded from packed E4 words on the device."""
+    halves = words.view(torch.int16)            # little-endian: low lane first
+    lo, hi = halves[0::2].contiguous(), halves[1::2].contiguous()
+    out = []
+    for lane, codes in ((0, lo), (1, hi)):
+        back = torch.empty(codes.numel(), dtype=torch.float32, device=codes.device)
+        pa.pa_debug_codec(lane, 1, codes, back)
+        out.append(back)
+    torch.cuda.synchronize()
+    return out[0].cpu().tolist(), out[1].cpu().tolist()
+
+
+EXAMPLE_HYPER = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+EXAMPLE_STEP = 10
+
+
+def run_update_example():
+    """One packed E4 update of four parameters through the library's step
+    (pa_step): the step decodes the prior moments, reconstructs v as RMS
+    squared, updates in FP32 and packs afterwards.  Returns host lists: the
+    parameters, gradients and prior words, then the new parameters and
+    words, and the decoded (m, RMS) of the prior and new words."""
+    import torch
+    import adamw_step_amd as pa
+    dev = "cuda:0"
+    p = torch.tensor([0.5, -0.25, 1e-3, 0.0], dtype=torch.float32, device=dev)
+    g = torch.tensor([0.01, -0.003, 1e-7, 0.2], dtype=torch.float32, device=dev)
+    m0 = torch.tensor([0.004, -0.001, 0.0, 0.01], dtype=torch.float32, device=dev)
+    r0 = torch.tensor([0.02, 0.005, 1e-6, 0.05], dtype=torch.float32, device=dev)
+    halves = torch.empty(2 * p.numel(), dtype=torch.int16, device=dev)
+    for lane, x in ((0, m0), (1, r0)):
+        codes = torch.empty(p.numel(), dtype=torch.int16, device=dev)
+        pa.pa_debug_codec(lane, 0, x, codes)
+        halves[lane::2] = codes
+    w = halves.view(torch.int32)
+    out = {"param": p.cpu().tolist(), "grad": g.cpu().tolist(),
+           "word": [int(x) & 0xFFFFFFFF for x in w.cpu().tolist()]}
+    out["m"], out["rms"] = _decode_words(pa, torch, w)
+    pa.pa_step(pa.PA_PACKED_E4, p, g, w, EXAMPLE_HYPER, EXAMPLE_STEP)
+    torch.cuda.synchronize()
+    out["new_param"] = p.cpu().tolist()
+    out["new_word"] = [int(x) & 0xFFFFFFFF for x in w.cpu().tolist()]
+    out["new_m"], out["new_rms"] = _decode_words(pa, torch, w)
+    return out
+
+
+def update_example():
+    """The update inspection as text (Packed AdamW Reference README,
+    Dependency-light inspection)."""
+    r = run_update_example()
+    h = EXAMPLE_HYPER
+    lines = [f"one packed E4 update, step {EXAMPLE_STEP}, lr {h['lr']}, betas ({h['beta1']}, {h['beta2']}), "
+             f"eps {h['eps']}, weight decay {h['weight_decay']}",
+             "param, grad, prior word (m, rms) -> new param, new word (m, rms)"]
+    for i in range(len(r["param"])):
+        lines.append(f"{r['param'][i]:>10.6g} {r['grad'][i]:>10.3g}  0x{r['word'][i]:08x} "
+                     f"({r['m'][i]:.6g}, {r['rms'][i]:.6g}) -> {r['new_param'][i]:>13.9g}  "
+                     f"0x{r['new_word'][i]:08x} ({r['new_m'][i]:.6g}, {r['new_rms'][i]:.6g})")
+    return "\n".join(lines)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--markdown", action="store_true")
-    ap.add_argument("--examples", action="store_true")
+    ap.add_argument("--examples", action="store_true",
+                    help="also encode sample values and run one update on the GPU")
     a = ap.parse_args(argv)
+    have_gpu = False
+    if a.examples:
+        # torch first: the library must bind to the HIP runtime torch loads,
+        # so it is imported before the table below loads the library.
+        try:
+            import torch
+            have_gpu = torch.cuda.is_available()
+        except ImportError:
+            pass
     print(render(markdown=a.markdown))
     if a.examples:
+        if not have_gpu:
+            print("--examples runs the library's codec and step on a GPU; none is available here", file=sys.stderr)
+            return 2
         print(examples())
+        print()
+        print(update_example())
     return 0
 
 

@@ -185,6 +185,11 @@ def test_inspect_formats_runs_without_torch(pa):
     r = subprocess.run([_sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
     assert "bias 15" in r.stdout and "| 4 |" in r.stdout and "| 8 |" in r.stdout
+    if not __import__("torch").cuda.is_available():   # without a GPU the examples say so and exit 2
+        r = subprocess.run([_sys.executable, "-m", "adamw_step_amd.inspect_formats", "--examples"], cwd=ROOT,
+                           capture_output=True, text=True, timeout=300)
+        assert r.returncode == 2 and "GPU" in r.stderr and "Traceback" not in r.stderr, r.stderr
+        assert "bias 15" in r.stdout
 
 
 def test_typed_argument_rules(pa):

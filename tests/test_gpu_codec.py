@@ -172,3 +172,22 @@ def test_inspect_formats_examples(pa):
     assert "0x7c00" in line15 and "0xf800" in line15
     line2 = [l for l in text.splitlines() if l.strip().startswith("2 ")][0]
     assert "0x7fff" in line2 and "0xffff" in line2
+
+
+def test_inspect_formats_update_example(pa):
+    """The inspection command's one-update example against the oracle: the
+    prior words it builds decode to its stated moments' codes, and the new
+    parameters and words equal the oracle's packed E4 step on the same
+    inputs, bit for bit."""
+    from adamw_step_amd.inspect_formats import EXAMPLE_HYPER, EXAMPLE_STEP, run_update_example
+    banner("inspect_formats update example")
+    r = run_update_example()
+    p = np.array(r["param"], np.float32)
+    g = np.array(r["grad"], np.float32)
+    words = np.array(r["word"], np.uint32)
+    h = EXAMPLE_HYPER
+    sc = oracle.scalars(h["lr"], h["beta1"], h["beta2"], h["eps"], h["weight_decay"], EXAMPLE_STEP)
+    oracle.step_packed(1, p, g, words, sc)
+    assert np.array_equal(np.array(r["new_word"], np.uint32), words)
+    assert np.array_equal(np.array(r["new_param"], np.float32).view(np.uint32), p.view(np.uint32))
+    assert r["new_word"] != r["word"]
