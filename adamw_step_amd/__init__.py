@@ -90,7 +90,7 @@ class Format(ctypes.Structure):
 EXPORTS = ("pa_step", "pa_step_list", "pa_step_typed", "pa_step_list_typed", "pa_state_bytes",
            "pa_format_info", "pa_status_string", "pa_last_hip_error", "pa_release_plans", "pa_debug_codec",
            "pa_debug_sqrt", "pa_debug_scalars", "pa_debug_q1_ends", "pa_debug_q1_levels", "pa_debug_pow2_rn32", "pa_grad_stats_list", "pa_turbo_state_bytes", "pa_turbo_layout_bytes", "pa_turbo_workspace_bytes",
-           "pa_turbo_step_list", "pa_turbo_step_list_typed", "pa_step_list_noalloc")
+           "pa_turbo_step_list", "pa_turbo_step_list_typed", "pa_step_list_noalloc", "pa_debug_plan_count")
 
 PA_DT_F32, PA_DT_BF16, PA_DT_F16 = 0, 1, 2
 
@@ -157,6 +157,9 @@ def lib():
     L.pa_turbo_step_list.restype = ctypes.c_int
     L.pa_turbo_step_list_typed.argtypes = [ctypes.c_int, ctypes.c_int] + L.pa_turbo_step_list.argtypes
     L.pa_turbo_step_list_typed.restype = ctypes.c_int
+    ip = ctypes.POINTER(ctypes.c_int)
+    L.pa_debug_plan_count.argtypes = [ip, ip, ip]
+    L.pa_debug_plan_count.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -337,6 +340,19 @@ class StepList:
         self.count = k
         self._fn = lib().pa_step_list_typed
 
+    def set_grads(self, grads):
+        """Point the list at other gradient tensors of the same dtypes and
+        sizes (torch allocates new ones after zero_grad(set_to_none=True));
+        the library writes the new pointers into its cached table."""
+        params = self._keep[0]
+        if len(grads) != len(params):
+            raise ValueError("one gradient per parameter")
+        for i, (p, g) in enumerate(zip(params, grads)):
+            if _check_pg(p, g) != (self.pdt, self.gdt):
+                raise TypeError("the gradients must keep the list's dtype")
+            self._G[i] = _ptr(g)
+        self._keep[1] = list(grads)
+
     def step(self, hyper, step, stream=None):
         h = _hyper(hyper)
         _check(self._fn(self.mode, self.pdt, self.gdt, self.count, self._P, self._G, self._S, self._N,
@@ -377,6 +393,18 @@ class GradStats:
         self.count = k
         self._fn = lib().pa_grad_stats_list
 
+    def set_grads(self, grads):
+        """Other gradient tensors of the same dtype and sizes (see
+        StepList.set_grads)."""
+        if len(grads) != self.count:
+            raise ValueError("as many gradients as before")
+        for i, g in enumerate(grads):
+            _tensor_ok(g, "grads")
+            if _dtype_code(g) != self.gdt or g.numel() != self._N[i] or g.device != self._keep[0].device:
+                raise TypeError("the gradients must keep the list's dtype, sizes and device")
+            self._G[i] = _ptr(g)
+        self._keep = list(grads)
+
     def run(self, sumsq, nonfinite=None, clip_scale=None, max_norm=0.0, stream=None):
         s, nf, cl = _stats_outputs(sumsq, nonfinite, clip_scale)
         _check(self._fn(self.gdt, self.count, self._G, self._N, float(max_norm), s, nf, cl, _stream(stream)))
@@ -385,6 +413,14 @@ class GradStats:
 def pa_grad_stats_list(grads, sumsq, nonfinite=None, clip_scale=None, max_norm=0.0, stream=None):
     """One-shot gradient pre-pass (see GradStats and include/pa.h)."""
     GradStats(grads).run(sumsq, nonfinite, clip_scale, max_norm, stream)
+
+
+def plan_counts():
+    """(list-step plans, gradient pre-pass plans, TurboAdam plans) cached in
+    the library (pa_debug_plan_count)."""
+    a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(lib().pa_debug_plan_count(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    return a.value, b.value, c.value
 
 
 def pa_state_bytes(mode, n):
@@ -581,6 +617,19 @@ class TurboList:
         self.workspace = torch.empty(max(wsb // 8, 1), dtype=torch.float64, device=dev)
         self._wsb = wsb
         self._fn = L.pa_turbo_step_list_typed
+
+    def set_grads(self, grads):
+        """Other gradient tensors of the same dtype and sizes (see
+        StepList.set_grads)."""
+        params = self._keep[0]
+        if len(grads) != len(params):
+            raise ValueError("one gradient per parameter")
+        for i, (p, g) in enumerate(zip(params, grads)):
+            _tensor_ok(g, "grads")
+            if _dtype_code(g) != self.gdt or g.numel() != p.numel() or g.device != p.device:
+                raise TypeError("the gradients must keep the list's dtype, sizes and device")
+            self._G[i] = _ptr(g)
+        self._keep[1] = list(grads)
 
     def step(self, hyper, step, stream=None):
         h = _hyper(hyper)

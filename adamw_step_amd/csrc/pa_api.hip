@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstddef>
 #include <cstring>
 #include <list>
 #include <mutex>
@@ -504,17 +505,59 @@ hipError_t upload_table(pa::Entry* dst, const std::vector<pa::Entry>& host, hipS
   return hipSuccess;
 }
 
+// Gradient pointers written into a cached table by kernels whose arguments
+// carry them, so that a list whose gradients move between calls (torch
+// allocates fresh gradients after zero_grad(set_to_none=True)) keeps its
+// plan: no allocation, no copy from host memory, no synchronisation, and
+// the write is ordered on the stream before the step that reads it.
+constexpr int kPatchPointers = 64;
+struct PointerChunk {
+  const void* v[kPatchPointers];
+};
+
+__global__ void __launch_bounds__(64) patch_pointers(char* base, long long stride, long long offset, PointerChunk c,
+                                                     int n) {
+  const int i = threadIdx.x;
+  if (i < n) *reinterpret_cast<const void**>(base + (long long)i * stride + offset) = c.v[i];
+}
+
+// Writes vals[j] into the pointer field at `offset` of entries 0..vals.size()-1
+// of a device table whose entries are `stride` bytes apart.
+hipError_t patch_table(void* table, size_t stride, size_t offset, const std::vector<const void*>& vals,
+                       hipStream_t st) {
+  for (size_t j = 0; j < vals.size(); j += kPatchPointers) {
+    PointerChunk c;
+    std::memset(&c, 0, sizeof(c));
+    const int m = (int)std::min<size_t>(kPatchPointers, vals.size() - j);
+    for (int k = 0; k < m; ++k) c.v[k] = vals[j + k];
+    hipLaunchKernelGGL(patch_pointers, dim3(1), dim3(64), 0, st, static_cast<char*>(table) + j * stride,
+                       (long long)stride, (long long)offset, c, m);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Whether `st` is being captured into a graph (a failed query counts as no).
+bool capturing(hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(st, &cs) == hipSuccess && cs == hipStreamCaptureStatusActive;
+}
+
 // ---------------------------------------------------------------- plans
 
 struct Plan {
   int device = -1;
   int mode = -1;
   int pdt = 0, gdt = 0;
-  std::vector<uintptr_t> key;   // per tensor: p, g, s0, s1, n
+  std::vector<uintptr_t> key;   // per tensor: p, s0, s1, n (pre-pass: n and phase); not the gradients
   pa::Entry* table = nullptr;   // device memory, count+1 entries (+ partials of a pre-pass plan)
   int count = 0;                // tensors in the table (the sentinel not counted)
   long long tiles = 0;
   std::vector<Range> ranges;    // the tensors' buffers, sorted and disjoint
+  std::vector<Range> written;   // the written ones alone (sorted, disjoint)
+  std::vector<const void*> grads;   // the gradient pointer of each table entry, as last written
+  bool captured = false;        // a graph has captured a call on this plan
   double* part_sum = nullptr;   // pre-pass plans: per-workgroup partials, inside `table`'s block
   unsigned long long* part_bad = nullptr;
   int nparts = 0;
@@ -595,6 +638,9 @@ struct TurboPlan {
   long long nchunks = 0;                    // chunks of tile sums over all UState tensors
   size_t ws_bytes = 0;
   std::vector<Range> ranges;                // written buffers and gradients, merged
+  std::vector<Range> written;               // the written buffers alone, merged
+  std::vector<const void*> grads;           // the gradient pointer of each entry, as last written
+  bool captured = false;                    // a graph has captured a call on this plan
 };
 
 std::list<TurboPlan> g_turbo_plans;         // guarded by g_plan_mu, most recent first
@@ -804,6 +850,43 @@ namespace {
 
 // pa_step_list_typed (noalloc false: the table in a cached plan) and
 // pa_step_list_noalloc (noalloc true: the table in `scratch`).
+// A cached elementwise plan called with gradients other than those in its
+// table: they are checked as at the plan's creation (aligned to their
+// element, at the parameters' phase, clear of every written buffer and of
+// each other), and on success the plan's ranges and gradient list take them;
+// the caller writes them into the device table.  Nothing changes on error.
+int refresh_grads(Plan& pl, int pdt, int gdt, size_t count, void* const* params, const void* const* grads,
+                  const size_t* n, bool* changed) {
+  *changed = false;
+  std::vector<const void*> g;
+  g.reserve(pl.grads.size());
+  for (size_t i = 0; i < count; ++i)
+    if (n[i] > 0) g.push_back(grads[i]);
+  if (g == pl.grads) return PA_OK;
+  if (g.size() != pl.grads.size()) return PA_ERR_ARG;
+  const size_t ps = dtype_size(pdt), gs = dtype_size(gdt);
+  std::vector<Range> gr;
+  for (size_t i = 0; i < count; ++i) {
+    if (n[i] == 0) continue;
+    if (grads[i] == nullptr) return PA_ERR_ARG;
+    const uintptr_t ga = reinterpret_cast<uintptr_t>(grads[i]), pa_ = reinterpret_cast<uintptr_t>(params[i]);
+    if (ga % gs || ((ga / gs) & 3u) != ((pa_ / ps) & 3u)) return PA_ERR_ALIGN;
+    gr.push_back(range_of(grads[i], n[i] * gs));
+  }
+  {
+    std::vector<Range> tmp = gr;
+    if (any_overlap(tmp)) return PA_ERR_ALIAS;
+  }
+  for (const Range& r : gr)
+    if (hits_sorted(pl.written, r)) return PA_ERR_ALIAS;
+  std::vector<Range> all = pl.written;
+  all.insert(all.end(), gr.begin(), gr.end());
+  pl.ranges = merged(all);
+  pl.grads = g;
+  *changed = true;
+  return PA_OK;
+}
+
 int step_list(bool noalloc, int mode, int param_dtype, int grad_dtype, size_t count, void* const* params,
               const void* const* grads, void* const* states, const size_t* n, const pa_hyper* hyper, long long step,
               void* stream) {
@@ -876,9 +959,10 @@ int step_list(bool noalloc, int mode, int param_dtype, int grad_dtype, size_t co
   rc = device_info(&dev, &d);
   if (rc) return rc;
 
-  // Key of this list: every pointer and length, in order.
+  // Key of this list: every pointer but the gradients', and every length,
+  // in order.  The gradients are written into the table when they move.
   std::vector<uintptr_t> key;
-  key.reserve(count * 5);
+  key.reserve(count * 4);
   for (size_t i = 0; i < count; ++i) {
     uintptr_t s0 = reinterpret_cast<uintptr_t>(states[i]), s1 = 0;
     if (mode == PA_FP32 && states[i] != nullptr) {
@@ -887,7 +971,6 @@ int step_list(bool noalloc, int mode, int param_dtype, int grad_dtype, size_t co
       s1 = reinterpret_cast<uintptr_t>(fs->v);
     }
     key.push_back(reinterpret_cast<uintptr_t>(params[i]));
-    key.push_back(reinterpret_cast<uintptr_t>(grads[i]));
     key.push_back(s0);
     key.push_back(s1);
     key.push_back((uintptr_t)n[i]);
@@ -897,6 +980,7 @@ int step_list(bool noalloc, int mode, int param_dtype, int grad_dtype, size_t co
   auto it = std::find_if(g_plans.begin(), g_plans.end(), [&](const Plan& p) {
     return p.device == dev && p.mode == mode && p.pdt == param_dtype && p.gdt == grad_dtype && p.key == key;
   });
+  bool changed = false;
   if (it == g_plans.end()) {
     // Validate and build the table once for this list.
     std::vector<pa::Entry> host;
@@ -915,6 +999,18 @@ int step_list(bool noalloc, int mode, int param_dtype, int grad_dtype, size_t co
     pl.count = (int)(host.size() - 1);
     pl.tiles = tiles;
     pl.ranges = ranges;
+    for (size_t j = 0; j + 1 < host.size(); ++j) pl.grads.push_back(host[j].g);
+    {
+      std::vector<Range> w;
+      for (size_t i = 0; i < count; ++i) {
+        ElemTensor t;
+        std::vector<Range> r;
+        (void)check_elem_tensor(mode, param_dtype, grad_dtype, params[i], grads[i], states[i], n[i], &t, &r);
+        for (size_t k = 0; k < r.size(); ++k)
+          if (k != 1) w.push_back(r[k]);   // every buffer but the gradients (the second)
+      }
+      pl.written = merged(w);
+    }
     hipError_t e = hipMalloc(reinterpret_cast<void**>(&pl.table), host.size() * sizeof(pa::Entry));
     if (e != hipSuccess) {
       g_last_hip_error = (int)e;
@@ -932,12 +1028,26 @@ int step_list(bool noalloc, int mode, int param_dtype, int grad_dtype, size_t co
       g_plans.pop_back();
     }
     it = g_plans.begin();
-  } else if (it != g_plans.begin()) {
-    g_plans.splice(g_plans.begin(), g_plans, it);
-    it = g_plans.begin();
+  } else {
+    if (it != g_plans.begin()) {
+      g_plans.splice(g_plans.begin(), g_plans, it);
+      it = g_plans.begin();
+    }
+    rc = refresh_grads(*it, param_dtype, grad_dtype, count, params, grads, n, &changed);
+    if (rc) return rc;
   }
+  const bool cap = capturing(st);
   rc = hyper_clear(hyper, it->ranges);
   if (rc) return rc;
+  if (changed || it->captured || cap) {
+    // Gradients that moved are written into the table.  A replay rewrites
+    // the table with the gradients it captured, so a plan that a graph
+    // holds gets its gradients written on every call, and a captured call
+    // writes its own.
+    const hipError_t pe = patch_table(it->table, sizeof(pa::Entry), offsetof(pa::Entry, g), it->grads, st);
+    if (pe != hipSuccess) return hip_failed(pe);
+    it->captured = it->captured || cap;
+  }
   hipError_t e =
       dispatch_list(mode, param_dtype, grad_dtype, it->table, it->count, unroll, it->tiles, s, hyper->nonfinite, st);
   return e == hipSuccess ? PA_OK : hip_failed(e);
@@ -986,22 +1096,36 @@ int pa_grad_stats_list(int grad_dtype, size_t count, const void* const* grads, c
   int rc = device_info(&dev, &d);
   if (rc) return rc;
 
-  // Key: the list and the stream.  The plan holds the per-workgroup
-  // partials, so calls on different streams get plans of their own and
-  // cannot overwrite each other's partials.
+  // Key: the stream, and each gradient's length and phase (its position in
+  // elements modulo 4, which the table's tiles follow).  The plan holds the
+  // per-workgroup partials, so calls on different streams get plans of their
+  // own and cannot overwrite each other's partials.  The gradient pointers
+  // are written into the table when they move.
+  const size_t es = dtype_size(grad_dtype);
   std::vector<uintptr_t> key;
   key.reserve(count * 2 + 1);
   key.push_back(reinterpret_cast<uintptr_t>(stream));
+  std::vector<const void*> gnow;
+  std::vector<Range> gr;
   for (size_t i = 0; i < count; ++i) {
-    key.push_back(reinterpret_cast<uintptr_t>(grads[i]));
     key.push_back((uintptr_t)n[i]);
+    if (n[i] == 0) {
+      key.push_back(0);
+      continue;
+    }
+    if (grads[i] == nullptr) return PA_ERR_ARG;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(grads[i]);
+    if (a % es) return PA_ERR_ALIGN;
+    key.push_back((a / es) & 3u);
+    gnow.push_back(grads[i]);
+    gr.push_back(range_of(grads[i], n[i] * es));
   }
   std::lock_guard<std::mutex> lk(g_plan_mu);
   auto it = std::find_if(g_plans.begin(), g_plans.end(), [&](const Plan& p) {
     return p.device == dev && p.mode == kStatsPlanMode && p.gdt == grad_dtype && p.key == key;
   });
+  bool changed = false;
   if (it == g_plans.end()) {
-    const size_t es = dtype_size(grad_dtype);
     std::vector<pa::Entry> host;
     std::vector<Range> ranges;
     long long tiles = 0;
@@ -1032,6 +1156,7 @@ int pa_grad_stats_list(int grad_dtype, size_t count, const void* const* grads, c
     pl.key = key;
     pl.tiles = tiles;
     pl.ranges = merged(ranges);
+    pl.grads = gnow;
     pl.nparts = tiles > 0 ? (int)grid_for(tiles, d, d.stats_blocks_per_cu) : 0;
     // One block: the table, then the partial sums and counts (at least one
     // slot each, so the finalizer always gets valid pointers).
@@ -1056,12 +1181,28 @@ int pa_grad_stats_list(int grad_dtype, size_t count, const void* const* grads, c
       g_plans.pop_back();
     }
     it = g_plans.begin();
-  } else if (it != g_plans.begin()) {
-    g_plans.splice(g_plans.begin(), g_plans, it);
-    it = g_plans.begin();
+  } else {
+    if (it != g_plans.begin()) {
+      g_plans.splice(g_plans.begin(), g_plans, it);
+      it = g_plans.begin();
+    }
+    if (gnow != it->grads) {
+      const std::vector<Range> mr = merged(gr);
+      for (const Range& r : outs)
+        if (hits_sorted(mr, r)) return PA_ERR_ALIAS;
+      it->ranges = mr;
+      it->grads = gnow;
+      changed = true;
+    }
   }
   for (const Range& r : outs)
     if (hits_sorted(it->ranges, r)) return PA_ERR_ALIAS;
+  const bool cap = capturing(st);
+  if (changed || it->captured || cap) {   // as for the list step: moved gradients, or a plan a graph holds
+    const hipError_t pe = patch_table(it->table, sizeof(pa::Entry), offsetof(pa::Entry, g), it->grads, st);
+    if (pe != hipSuccess) return hip_failed(pe);
+    it->captured = it->captured || cap;
+  }
   hipError_t e;
   switch (grad_dtype) {
     case PA_DT_F32: e = launch_stats<pa::kF32>(*it, max_norm, sumsq, nonfinite, clip_scale, st); break;
@@ -1140,9 +1281,11 @@ int pa_turbo_step_list_typed(int param_dtype, int grad_dtype, size_t count, void
   key.push_back((uintptr_t)lay.group);
   key.push_back((uintptr_t)lay.general);
   key.push_back((uintptr_t)config->seed);
+  // The gradients are not part of the key: they are written into the table
+  // when they move.
   for (size_t i = 0; i < count; ++i) {
     const pa_turbo_state& t = states[i];
-    for (const void* ptr : {(const void*)params[i], (const void*)grads[i], (const void*)t.m_codes,
+    for (const void* ptr : {(const void*)params[i], (const void*)t.m_codes,
                             (const void*)t.m_means, (const void*)t.m_fp32, (const void*)t.v_index,
                             (const void*)t.v_ends, (const void*)t.v_fp32, (const void*)t.scalars})
       key.push_back(reinterpret_cast<uintptr_t>(ptr));
@@ -1153,6 +1296,7 @@ int pa_turbo_step_list_typed(int param_dtype, int grad_dtype, size_t count, void
   std::lock_guard<std::mutex> lk(g_plan_mu);
   auto it = std::find_if(g_turbo_plans.begin(), g_turbo_plans.end(),
                          [&](const TurboPlan& p) { return p.device == dev && p.key == key; });
+  bool changed = false;
   if (it == g_turbo_plans.end()) {
     std::vector<pa::TurboEntry> host;
     std::vector<pa::TurboReduceEntry> red;
@@ -1219,6 +1363,8 @@ int pa_turbo_step_list_typed(int param_dtype, int grad_dtype, size_t count, void
     pl.nreduce = (int)red.size();
     pl.nchunks = chunk_slots;
     pl.ws_bytes = 8 * (size_t)(ws_slots + chunk_slots);
+    pl.written = merged(written);
+    for (size_t j = 0; j + 1 < host.size(); ++j) pl.grads.push_back(host[j].g);
     written.insert(written.end(), read.begin(), read.end());
     pl.ranges = merged(written);
     const size_t tb = host.size() * sizeof(pa::TurboEntry);
@@ -1243,9 +1389,36 @@ int pa_turbo_step_list_typed(int param_dtype, int grad_dtype, size_t count, void
       g_turbo_plans.pop_back();
     }
     it = g_turbo_plans.begin();
-  } else if (it != g_turbo_plans.begin()) {
-    g_turbo_plans.splice(g_turbo_plans.begin(), g_turbo_plans, it);
-    it = g_turbo_plans.begin();
+  } else {
+    if (it != g_turbo_plans.begin()) {
+      g_turbo_plans.splice(g_turbo_plans.begin(), g_turbo_plans, it);
+      it = g_turbo_plans.begin();
+    }
+    // Gradients other than those in the table: checked as at the plan's
+    // creation (aligned, clear of every written buffer), then written.
+    std::vector<const void*> gnow;
+    std::vector<Range> gr;
+    const size_t gs = dtype_size(grad_dtype);
+    for (size_t i = 0; i < count; ++i) {
+      if (n[i] == 0) continue;
+      gnow.push_back(grads[i]);
+    }
+    if (gnow != it->grads) {
+      if (gnow.size() != it->grads.size()) return PA_ERR_ARG;
+      for (size_t i = 0; i < count; ++i) {
+        if (n[i] == 0) continue;
+        if (grads[i] == nullptr) return PA_ERR_ARG;
+        if (!aligned(grads[i], 4 * gs)) return PA_ERR_ALIGN;
+        gr.push_back(range_of(grads[i], n[i] * gs));
+      }
+      for (const Range& r : gr)
+        if (hits_sorted(it->written, r)) return PA_ERR_ALIAS;
+      std::vector<Range> all = it->written;
+      all.insert(all.end(), gr.begin(), gr.end());
+      it->ranges = merged(all);
+      it->grads = gnow;
+      changed = true;
+    }
   }
   if (workspace_bytes < it->ws_bytes || (it->ws_bytes > 0 && workspace == nullptr)) return PA_ERR_ARG;
   {
@@ -1270,6 +1443,12 @@ int pa_turbo_step_list_typed(int param_dtype, int grad_dtype, size_t count, void
   double* ws = static_cast<double*>(workspace);
   const double f = config->m_step_factor;
   unsigned long long* nf = hyper->nonfinite;
+  const bool cap = capturing(st);
+  if (changed || it->captured || cap) {   // as for the list step: moved gradients, or a plan a graph holds
+    e = patch_table(it->table, sizeof(pa::TurboEntry), offsetof(pa::TurboEntry, g), it->grads, st);
+    if (e != hipSuccess) return hip_failed(e);
+    it->captured = it->captured || cap;
+  }
   if (it->general) {
     switch (lay.bits) {
       case 2: e = launch_general<2>(*it, s, ts, ws, nf, f, st); break;
@@ -1366,6 +1545,17 @@ void pa_release_plans(void) {
   g_plans.clear();
   for (TurboPlan& p : g_turbo_plans) free_turbo_plan(p);
   g_turbo_plans.clear();
+}
+
+int pa_debug_plan_count(int* step_plans, int* stats_plans, int* turbo_plans) {
+  if (step_plans == nullptr || stats_plans == nullptr || turbo_plans == nullptr) return PA_ERR_ARG;
+  std::lock_guard<std::mutex> lk(g_plan_mu);
+  int a = 0, b = 0;
+  for (const Plan& p : g_plans) (p.mode == kStatsPlanMode ? b : a) += 1;
+  *step_plans = a;
+  *stats_plans = b;
+  *turbo_plans = (int)g_turbo_plans.size();
+  return PA_OK;
 }
 
 int pa_debug_scalars(const pa_hyper* hyper, long long step, float* out, double* inv_bc2) {

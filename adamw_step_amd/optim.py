@@ -53,6 +53,22 @@ def _add_group(opt, param_group, init):
     opt._prepared = {}
 
 
+def _cached_list(cache, gi, params, grads, build):
+    """The cached step list of group gi: built again when the parameters
+    change, pointed at the new gradients when only those moved (torch
+    allocates fresh ones after zero_grad(set_to_none=True))."""
+    pkey = tuple(p.data_ptr() for p in params)
+    gkey = tuple(g.data_ptr() for g in grads)
+    cached = cache.get(gi)
+    if cached is None or cached[0] != pkey:
+        cached = [pkey, gkey, build()]
+        cache[gi] = cached
+    elif cached[1] != gkey:
+        cached[2].set_grads(grads)
+        cached[1] = gkey
+    return cached[2]
+
+
 def _grads_of(params):
     grads = []
     for p in params:
@@ -177,9 +193,11 @@ class PackedAdamW(torch.optim.Optimizer):
             common["nonfinite"] = self._nonfinite
         if self.max_grad_norm is not None or self.skip_nonfinite:
             gkey = tuple(g.data_ptr() for g in all_grads)
-            if self._stats is None or gkey != self._stats_key:
+            if self._stats is None or len(gkey) != len(self._stats_key):
                 self._stats = GradStats(all_grads)
-                self._stats_key = gkey
+            elif gkey != self._stats_key:       # fresh gradient tensors: same list, new pointers
+                self._stats.set_grads(all_grads)
+            self._stats_key = gkey
             self._stats.run(self._sumsq, self._grad_bad,
                             self._clip if self.max_grad_norm is not None else None,
                             max_norm=self.max_grad_norm or 0.0)
@@ -192,15 +210,12 @@ class PackedAdamW(torch.optim.Optimizer):
                 self._pending = True
         for gi, group, grads in work:
             params = group["params"]
-            key = tuple(g.data_ptr() for g in grads) + tuple(p.data_ptr() for p in params)
-            cached = self._prepared.get(gi)
-            if cached is None or cached[0] != key:
-                cached = (key, StepList(self._mode, params, grads, [self._state_of(p) for p in params]))
-                self._prepared[gi] = cached
+            sl = _cached_list(self._prepared, gi, params, grads,
+                              lambda: StepList(self._mode, params, grads, [self._state_of(p) for p in params]))
             beta1, beta2 = group["betas"]
             hyper = dict(lr=group["lr"], beta1=beta1, beta2=beta2, eps=group["eps"],
                          weight_decay=group["weight_decay"], **common)
-            cached[1].step(hyper, self.step_count)
+            sl.step(hyper, self.step_count)
         return loss
 
     def state_dict(self):
@@ -328,20 +343,16 @@ class TurboAdam(torch.optim.Optimizer):
         self.step_count += 1
         for gi, group, grads in work:
             params = group["params"]
-            key = tuple(g.data_ptr() for g in grads) + tuple(p.data_ptr() for p in params)
-            cached = self._prepared.get(gi)
-            if cached is None or cached[0] != key:
-                states = [self.state[p]["turbo"] for p in params]
-                cached = (key, self._TurboList(params, grads, states, v_bits=self.v_bits,
-                                               m_step_factor=self.m_step_factor, seed=self.seed,
-                                               block_size=self.block_size, m_block_size=self.m_block_size))
-                self._prepared[gi] = cached
+            tl = _cached_list(self._prepared, gi, params, grads, lambda: self._TurboList(
+                params, grads, [self.state[p]["turbo"] for p in params], v_bits=self.v_bits,
+                m_step_factor=self.m_step_factor, seed=self.seed, block_size=self.block_size,
+                m_block_size=self.m_block_size))
             beta1, beta2 = group["betas"]
             hyper = dict(lr=group["lr"], beta1=beta1, beta2=beta2, eps=group["eps"],
                          weight_decay=group["weight_decay"])
             if self._nonfinite is not None:
                 hyper["nonfinite"] = self._nonfinite
-            cached[1].step(hyper, self.step_count)
+            tl.step(hyper, self.step_count)
         return loss
 
     def state_dict(self):

@@ -170,11 +170,18 @@ int pa_step(int mode, float* params, const float* grads, void* state, size_t n,
  * workgroup per tile (a list of more than 2^22 tiles takes one launch per
  * 2^22).  Blockwise mode: one launch per tensor.  params[i], grads[i],
  * states[i] and n[i] describe tensor i exactly as for pa_step.  The table is
- * uploaded once per distinct pointer/size list and cached (see
- * pa_release_plans).  Tensors of length 0 are skipped.  Once a list's table
- * exists, a call enqueues its kernel launch and nothing else (no allocation,
- * copy, memset or synchronisation), so it can be captured in a HIP graph;
- * a captured call keeps the step and scalars it was captured with. */
+ * uploaded once per distinct list of parameter and state pointers and sizes
+ * and cached (see pa_release_plans); the gradients are not part of it:
+ * when a call's gradients differ from those in the table (torch allocates
+ * new ones after zero_grad(set_to_none=True)), they are checked as at the
+ * table's creation and written into it by small kernels on `stream`, with
+ * no allocation or synchronisation.  Tensors of length 0 are skipped.
+ * Once a list's table exists, a call enqueues those small kernels (when
+ * needed) and its launch and nothing else (no allocation, host copy,
+ * memset or synchronisation), so it can be captured in a HIP graph; a
+ * captured call keeps the step, scalars and gradients it was captured with
+ * (a table that a graph holds gets its gradients written on every call).
+ * Calls on one list from different streams must be ordered by the caller. */
 int pa_step_list(int mode, size_t count, float* const* params, const float* const* grads,
                  void* const* states, const size_t* n, const pa_hyper* hyper, long long step,
                  void* stream);
@@ -236,9 +243,10 @@ int pa_step_list_noalloc(int mode, int param_dtype, int grad_dtype, size_t count
  * optimizer count (Packed AdamW Reference README, One-update smoke test).
  * Gradients must be aligned to their element size and must not overlap the
  * outputs.  The tensor table and per-workgroup partials are cached per
- * distinct list and stream like the step's plans (see pa_release_plans):
- * calls on different streams use separate partials; two calls on one
- * stream are ordered by it.  count == 0,
+ * distinct list of lengths and gradient phases (address in elements modulo
+ * 4) and stream, with the gradient pointers written into the table as for
+ * pa_step_list (see pa_release_plans): calls on different streams use
+ * separate partials; two calls on one stream are ordered by it.  count == 0,
  * or only empty tensors, writes 0, 0 and the coefficient of a zero norm. */
 int pa_grad_stats_list(int grad_dtype, size_t count, const void* const* grads, const size_t* n,
                        double max_norm, double* sumsq, unsigned long long* nonfinite, float* clip_scale,
@@ -329,12 +337,14 @@ size_t pa_turbo_workspace_bytes(size_t count, const pa_turbo_state* states, cons
  * completes the sum and rotates its scales.  `states` is a host array of count
  * descriptors; `workspace` a device buffer of at least
  * pa_turbo_workspace_bytes (8-byte aligned).  The launch plan is cached per
- * distinct list (see pa_release_plans).  Written buffers may not overlap
- * each other, the gradients or the workspace (PA_ERR_ALIAS).  hyper's
- * non-finite counter, gradient scale and skip flag work as for pa_step.
- * Once a list's plan exists, a call enqueues its kernels and nothing else,
- * so it can be captured in a HIP graph (a captured call keeps its step and
- * scalars). */
+ * distinct list of parameter and state pointers, sizes and configuration
+ * (see pa_release_plans), its gradient pointers written into it when they
+ * move, as for pa_step_list.  Written buffers may not overlap each other,
+ * the gradients or the workspace (PA_ERR_ALIAS).  hyper's non-finite
+ * counter, gradient scale and skip flag work as for pa_step.  Once a
+ * list's plan exists, a call enqueues its kernels and nothing else, so it
+ * can be captured in a HIP graph (a captured call keeps its step, scalars
+ * and gradients). */
 int pa_turbo_step_list(size_t count, float* const* params, const float* const* grads, const pa_turbo_state* states,
                        const size_t* n, const pa_hyper* hyper, const pa_turbo_config* config, long long step,
                        void* workspace, size_t workspace_bytes, void* stream);
@@ -392,6 +402,13 @@ int pa_last_hip_error(void);
 /* Free every cached launch-plan table (device memory).  Waits for the
  * device first.  Safe to call at any time outside a running call. */
 void pa_release_plans(void);
+
+/* Plan-cache self-test export (host only): the number of cached launch
+ * plans of list steps, of gradient pre-passes and of TurboAdam steps.  A
+ * plan is cached per list of parameters and state buffers (and lengths);
+ * gradients that move between calls reuse it.  PA_ERR_ARG for a null
+ * pointer. */
+int pa_debug_plan_count(int* step_plans, int* stats_plans, int* turbo_plans);
 
 /* Scalar self-test export (host only, no device work): the per-call
  * binary32 scalars the kernels receive, formed from `hyper` and `step`
