@@ -322,3 +322,15 @@ def test_noalloc_refuses_a_list_over_capacity_before_any_device_call(pa):
     h = pa._hyper(dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0))
     assert L.pa_step_list_noalloc(1, 0, 0, k, P, G, S, N, ctypes.byref(h), 1, None) == pa.PA_ERR_CAPACITY
     assert L.pa_step_list_noalloc(1, 0, 0, 2, P, G, S, N, ctypes.byref(h), 0, None) == pa.PA_ERR_ARG
+
+
+def test_turbo_ledger_matches_gpt2_layer_profile(pa):
+    """The library's ledger gives the page's GPT-2-layer figures for the three
+    TurboAdam configurations (the shape reading is pinned in the oracle's
+    tests by torch's own AdamW)."""
+    with open(os.path.join(ROOT, "tests", "golden", "pages_facts.json")) as f:
+        prof = json.load(f)["turboadam_gpt2_layer_profile"]
+    ns = [math.prod(s) for s in prof["shapes"]]
+    for key, (cm, cv) in (("ustate_and_oneq", (1, 1)), ("ustate_only", (1, 0)), ("oneq_only", (0, 1))):
+        total = sum(pa.pa_turbo_state_bytes(int(cm and n >= 4096), int(cv and n >= 4096), 4, n) for n in ns)
+        assert total == prof["persistent_bytes"][key], key

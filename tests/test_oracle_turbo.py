@@ -602,3 +602,28 @@ def test_typed_parameters_round_only_the_parameter(oracle_mod, pdt, gdt, bits, b
     # bfloat16 rounding itself: ties go to even, and a value just above a tie up
     x = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -8 + 2.0 ** -20], np.float32)
     assert list(_bf16_rne(x)) == [0x3F80, 0x3F82, 0x3F81]
+
+
+def test_gpt2_layer_memory_profile(oracle_mod):
+    """The page's GPT-2-layer memory table: its four persistent-byte figures
+    (AdamW, UState only, 1Q only, both) from the nine-tensor layer that the
+    fixture's reading names.  torch's own AdamW on the CPU, an independent
+    library, gives the AdamW figure from the same shapes, which pins the
+    shape reading; the oracle's ledger then gives the three TurboAdam
+    figures, the UState-only and 1Q-only ones included."""
+    import torch
+    prof = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_facts.json")))["turboadam_gpt2_layer_profile"]
+    shapes = [tuple(s) for s in prof["shapes"]]
+    want = prof["persistent_bytes"]
+    ps = [torch.nn.Parameter(torch.zeros(s)) for s in shapes]
+    opt = torch.optim.AdamW(ps, lr=1e-3)
+    for p in ps:
+        p.grad = torch.ones_like(p)
+    opt.step()
+    got = sum(t.numel() * t.element_size() for st in opt.state.values() for t in st.values() if torch.is_tensor(t))
+    assert got == want["adamw"]
+    ns = [math.prod(s) for s in shapes]
+    thr = FACTS["defaults"]["min_m_compress_elements"]
+    for key, (cm, cv) in (("ustate_and_oneq", (1, 1)), ("ustate_only", (1, 0)), ("oneq_only", (0, 1))):
+        total = sum(oracle.turbo_state_bytes(cm and n >= thr, cv and n >= thr, 4, n) for n in ns)
+        assert total == want[key], key
