@@ -60,7 +60,8 @@ PEAK_GBPS = 8000.0
 # ceiling on gfx950: the general TurboAdam kernel's counters exceed it.
 PEAK_VALU_GLANE = 256 * 128 * 2.4
 BYTES_PER_PARAM = {"e4": 20, "fp16": 20, "fp32": 28, "blockwise8": 14, "gradstats": 4, "turbo": None}
-WORKLOADS = {"single-262k": 1, "gpt-11m": 2, "gpt2-small-124m": 3, "llama-7b": 4, "blockwise-268m": 5}
+WORKLOADS = {"single-262k": 1, "gpt-11m": 2, "gpt2-small-124m": 3, "llama-7b": 4, "blockwise-268m": 5,
+             "gpt2-layer-7m": 6}
 # Device sources each kernel family is compiled from: a stored counter
 # reading stays valid while these bytes are unchanged.
 KERNEL_SOURCES = {

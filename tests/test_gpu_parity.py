@@ -207,6 +207,13 @@ def test_gpt2_small_124m_list(pa, mode):
     _list_workload(pa, 3, mode, steps=2)
 
 
+@pytest.mark.parametrize("mode", [E4, F32, F16])
+def test_gpt2_layer_7m_list(pa, mode):
+    """The GPT-2-layer list of the TurboAdam page's benchmark (as read from
+    its memory table) in each elementwise mode, three steps."""
+    _list_workload(pa, 6, mode, steps=3)
+
+
 @pytest.mark.parametrize("mode", [E4, F32])
 def test_gpt2_small_124m_list_counting_and_scaled(pa, mode):
     """The kernel variant that counts non-finite values and scales the

@@ -379,3 +379,32 @@ def test_turbo_residual_tree_past_one_chunk_level(pa, general):
     finally:
         del p, g, st, tl
         torch.cuda.empty_cache()
+
+
+def test_turbo_gpt2_layer_7m_list(pa):
+    """TurboAdam over the GPT-2-layer list of the page's own benchmark (as
+    read from its memory table; the 768-value vectors keep FP32 moments),
+    the benchmark's inputs, three steps against the oracle."""
+    import torch
+    import workloads
+    hp = workloads.host_params(6)
+    sizes = [a.size for a in hp]
+    dp = [to_dev(a) for a in hp]
+    hs = [oracle.TurboState(n, n >= 4096, n >= 4096) for n in sizes]
+    ds = [pa.TurboState(n, "cuda:0", n >= 4096, n >= 4096, tensor_id=i) for i, n in enumerate(sizes)]
+    assert sum(s.nbytes() for s in ds) == 5769288            # the page's figure for UState + 1Q
+    grads = [torch.zeros(n, dtype=torch.float32, device="cuda:0") for n in sizes]
+    tl = pa.TurboList(dp, grads, ds)
+    for t in range(1, 4):
+        hg = workloads.host_grads(6, t)
+        for gdev, g in zip(grads, hg):
+            gdev.copy_(torch.from_numpy(g))
+        banner(f"turbo gpt2-layer-7m step {t}")
+        tl.step(H, t)
+        torch.cuda.synchronize()
+        sc = oracle.scalars(H["lr"], H["beta1"], H["beta2"], H["eps"], H["weight_decay"], t)
+        ts = oracle.turbo_scalars(H["beta1"], H["beta2"], t)
+        for i in range(len(sizes)):
+            oracle.turbo_step(hp[i], hg[i], hs[i], sc, ts, t, tensor_id=i)
+            _compare_state(ds[i], hs[i], f"step {t} tensor {i}")
+            assert_params(to_host(dp[i]), hp[i], what=f"step {t} tensor {i} params")

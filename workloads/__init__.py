@@ -13,6 +13,11 @@ blockwise task's absent inputs; none of those data exist here.
     3 "gpt2-small-124m"  148-tensor GPT-2 small list (124,439,808 parameters)
     4 "llama-7b"         291-tensor Llama-7B list (6,738,415,616 parameters)
     5 "blockwise-268m"   one flat tensor of 2^28 parameters, blockwise 8-bit
+    6 "gpt2-layer-7m"    the TurboAdam page's GPT-2-layer benchmark list as read
+                         from its memory table: four 768x768 projections,
+                         768x3072 and 3072x768 MLP matrices, three 768-value
+                         vectors (7,080,192 parameters; the page prints no
+                         shapes, these reproduce its four state-byte figures)
 
 Seeds: parameters use 1000*c, gradients at step s use 1000*c + s, the
 per-tensor gradient scales use 1000*c + 999, the blockwise code maps use 5500
@@ -25,8 +30,8 @@ from __future__ import annotations
 import numpy as np
 
 NAMES = {1: "single-262k", 2: "gpt-11m", 3: "gpt2-small-124m", 4: "llama-7b",
-         5: "blockwise-268m"}
-STEPS = {1: 10, 2: 100, 3: 50, 4: 20, 5: 20}
+         5: "blockwise-268m", 6: "gpt2-layer-7m"}
+STEPS = {1: 10, 2: 100, 3: 50, 4: 20, 5: 20, 6: 100}
 WARMUP = {4: 3}
 HYPER = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
 
@@ -72,6 +77,10 @@ def shapes(cfg: int):
         return out
     if cfg == 5:
         return [("flat", (1 << 28,))]
+    if cfg == 6:
+        d, ff = 768, 3072
+        return [("q", (d, d)), ("k", (d, d)), ("v", (d, d)), ("o", (d, d)), ("fc", (d, ff)), ("proj", (ff, d)),
+                ("vec0", (d,)), ("vec1", (d,)), ("vec2", (d,))]
     raise ValueError(f"unknown workload {cfg}")
 
 
@@ -116,7 +125,7 @@ def host_params(cfg: int, limit: int | None = None):
     out = []
     for name, shp in shapes(cfg):
         n = int(np.prod(shp)) if limit is None else min(int(np.prod(shp)), limit)
-        if cfg == 3:
+        if cfg in (3, 6):
             a = r.normal(0.0, 1e-3, n)
         elif cfg == 2 and _kind(name) == "gain":
             a = np.ones(n)
@@ -194,7 +203,7 @@ def device_fill_params(cfg: int, tensors, seed_offset: int = 0):
         elif cfg == 2 and _kind(name) == "bias":
             t.zero_()
         else:
-            t.normal_(0.0, 1e-3 if cfg == 3 else 0.02, generator=gen)
+            t.normal_(0.0, 1e-3 if cfg in (3, 6) else 0.02, generator=gen)
 
 
 def device_fill_grads(cfg: int, step: int, tensors):
