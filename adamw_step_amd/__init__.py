@@ -90,7 +90,8 @@ class Format(ctypes.Structure):
 EXPORTS = ("pa_step", "pa_step_list", "pa_step_typed", "pa_step_list_typed", "pa_state_bytes",
            "pa_format_info", "pa_status_string", "pa_last_hip_error", "pa_release_plans", "pa_debug_codec",
            "pa_debug_sqrt", "pa_debug_scalars", "pa_debug_q1_ends", "pa_debug_q1_levels", "pa_debug_pow2_rn32", "pa_grad_stats_list", "pa_turbo_state_bytes", "pa_turbo_layout_bytes", "pa_turbo_workspace_bytes",
-           "pa_turbo_step_list", "pa_turbo_step_list_typed", "pa_step_list_noalloc", "pa_debug_plan_count")
+           "pa_turbo_step_list", "pa_turbo_step_list_typed", "pa_step_list_noalloc", "pa_debug_plan_count",
+           "pa_debug_blockwise_path")
 
 PA_DT_F32, PA_DT_BF16, PA_DT_F16 = 0, 1, 2
 
@@ -160,6 +161,8 @@ def lib():
     ip = ctypes.POINTER(ctypes.c_int)
     L.pa_debug_plan_count.argtypes = [ip, ip, ip]
     L.pa_debug_plan_count.restype = ctypes.c_int
+    L.pa_debug_blockwise_path.argtypes = [ctypes.c_longlong]
+    L.pa_debug_blockwise_path.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -421,6 +424,13 @@ def plan_counts():
     a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     _check(lib().pa_debug_plan_count(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
     return a.value, b.value, c.value
+
+
+def blockwise_path(blocks_per_workgroup):
+    """Which launch the blockwise step takes from now on, for tests of both
+    (pa_debug_blockwise_path): 0 by size (the default), -1 the persistent
+    launch, k >= 1 the ordered launch with k blocks per workgroup."""
+    _check(lib().pa_debug_blockwise_path(int(blocks_per_workgroup)))
 
 
 def pa_state_bytes(mode, n):

@@ -603,31 +603,84 @@ __device__ __forceinline__ void build_map(const float* lut, MapTables& t, uint32
   __syncthreads();
 }
 
-// Persistent grid over the 2048-element blocks, one 256-thread workgroup per
-// block at a time (eight values per thread), the search tables built once
-// per workgroup.  The loads of a workgroup's next block are issued before
-// the current one is reduced and encoded.  The block absmax goes through
-// one of two LDS slots, the slots alternating between consecutive blocks, so
-// one barrier per block suffices: a wavefront can only rewrite a slot after
-// every wavefront has passed the barrier of the block in between, that is
-// after every read of the slot.  Four wavefronts per SIMD are asked of the
+// The search tables of one map pair: both maps, their midpoint and bucket
+// tables, and each map's compare count and near-zero guard.  The ordered
+// launch reads them from global memory, built once per call.
+struct alignas(16) BwTables {
+  float lut_m[256], lut_v[256];
+  MapTables tab_m, tab_v;
+  int ncmp_m, ncmp_v, guard_m, guard_v;
+};
+constexpr int kBwTabVec = (int)(sizeof(BwTables) / 16);
+static_assert(sizeof(BwTables) % 16 == 0, "copied in 16-byte vectors");
+
+// One workgroup builds the tables of the map pair into `out`.
+__global__ void __launch_bounds__(kThreads) blockwise_tables(const float* qmap_m, const float* qmap_v, BwTables* out) {
+  __shared__ BwTables T;
+  __shared__ uint32_t red[2][kThreads / 64];
+  const int tid = threadIdx.x;
+  T.lut_m[tid] = qmap_m[tid];
+  T.lut_v[tid] = qmap_v[tid];
+  __syncthreads();
+  int nm, nv;
+  bool gm, gv;
+  build_map(T.lut_m, T.tab_m, red[0], nm, gm);
+  build_map(T.lut_v, T.tab_v, red[1], nv, gv);
+  if (tid == 0) {
+    T.ncmp_m = nm;
+    T.ncmp_v = nv;
+    T.guard_m = gm ? 1 : 0;
+    T.guard_v = gv ? 1 : 0;
+  }
+  __syncthreads();
+  const uint4* src = reinterpret_cast<const uint4*>(&T);
+  uint4* dst = reinterpret_cast<uint4*>(out);
+  for (int i = tid; i < kBwTabVec; i += kThreads) dst[i] = src[i];
+}
+
+// One 256-thread workgroup per 2048-element block at a time (eight values
+// per thread), in one of two launches:
+// - ORDERED: workgroup w takes blocks w*per_group .. w*per_group+per_group-1
+//   in dispatch order, so the blocks in flight form one compact window, and
+//   copies the tables that blockwise_tables built for the call into LDS;
+// - persistent: a grid of `stride` workgroups, workgroup w taking blocks w,
+//   w+stride, ..., each building the tables in LDS once.
+// The loads of a workgroup's next block are issued before the current one
+// is reduced and encoded.  The block absmax goes through one of two LDS
+// slots, the slots alternating between consecutive blocks, so one barrier
+// per block suffices: a wavefront can only rewrite a slot after every
+// wavefront has passed the barrier of the block in between, that is after
+// every read of the slot.  Four wavefronts per SIMD are asked of the
 // register allocator: with fewer the loads in flight do not cover the
-// memory latency.
-template <bool COUNT, bool SCALE>
+// memory latency.  The block step is a kernel argument in both launches: a
+// step the compiler sees as the constant 1 makes it keep per-thread
+// induction pointers, which costs registers.
+template <bool COUNT, bool SCALE, bool ORDERED>
 __global__ void __launch_bounds__(kThreads, 4)
-blockwise_kernel(BlockwiseArgs a, Scalars s, unsigned long long* nonfinite) {
-  __shared__ float lut_m[256], lut_v[256];
-  __shared__ MapTables tab_m, tab_v;
+blockwise_kernel(BlockwiseArgs a, Scalars s, unsigned long long* nonfinite, const BwTables* tabs,
+                 long long per_group, long long stride) {
+  __shared__ BwTables T;
   __shared__ uint32_t wave_max[2][2][kThreads / 64];   // [slot][moment][wavefront]
   if (!resolve_inputs(s)) return;   // uniform: before any barrier
   const int tid = threadIdx.x;
-  lut_m[tid] = a.qmap_m[tid];
-  lut_v[tid] = a.qmap_v[tid];
-  __syncthreads();
+  long long b0, bend;
   int ncmp_m, ncmp_v;
   bool guard_m, guard_v;
-  build_map(lut_m, tab_m, wave_max[0][0], ncmp_m, guard_m);
-  build_map(lut_v, tab_v, wave_max[0][1], ncmp_v, guard_v);
+  if constexpr (ORDERED) {
+    b0 = (long long)blockIdx.x * per_group;
+    bend = b0 + per_group < a.nblocks ? b0 + per_group : a.nblocks;
+    const uint4* src = reinterpret_cast<const uint4*>(tabs);
+    uint4* dst = reinterpret_cast<uint4*>(&T);
+    for (int i = tid; i < kBwTabVec; i += kThreads) dst[i] = src[i];
+  } else {
+    b0 = blockIdx.x;
+    bend = a.nblocks;
+    T.lut_m[tid] = a.qmap_m[tid];
+    T.lut_v[tid] = a.qmap_v[tid];
+    __syncthreads();
+    build_map(T.lut_m, T.tab_m, wave_max[0][0], ncmp_m, guard_m);
+    build_map(T.lut_v, T.tab_v, wave_max[0][1], ncmp_v, guard_v);
+  }
 
   // The 1e-30 lower clamp of the normaliser, as a binary32 bit pattern.
   const uint32_t floor_bits = __float_as_uint((float)1e-30);
@@ -651,9 +704,16 @@ blockwise_kernel(BlockwiseArgs a, Scalars s, unsigned long long* nonfinite) {
     in.av = a.v_absmax[blk];
   };
   BlockIn cur, nxt;
-  if (blockIdx.x < a.nblocks) load_block(blockIdx.x, cur);
+  if (b0 < bend) load_block(b0, cur);
+  if constexpr (ORDERED) {
+    __syncthreads();   // the tables copied into LDS
+    ncmp_m = T.ncmp_m;
+    ncmp_v = T.ncmp_v;
+    guard_m = T.guard_m != 0;
+    guard_v = T.guard_v != 0;
+  }
   int slot = 0;
-  for (long long b = blockIdx.x; b < a.nblocks; b += gridDim.x, slot ^= 1) {
+  for (long long b = b0; b < bend; b += stride, slot ^= 1) {
     const long long base = b * kBlock;
     float m1[8], v1[8];
 #pragma unroll
@@ -662,8 +722,8 @@ blockwise_kernel(BlockwiseArgs a, Scalars s, unsigned long long* nonfinite) {
       float po[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float m = lut_m[(cur.mc[h] >> (8 * k)) & 0xFFu] * cur.am;
-        const float v = lut_v[(cur.vc[h] >> (8 * k)) & 0xFFu] * cur.av;
+        const float m = T.lut_m[(cur.mc[h] >> (8 * k)) & 0xFFu] * cur.am;
+        const float v = T.lut_v[(cur.vc[h] >> (8 * k)) & 0xFFu] * cur.av;
         float p1;
         adamw(cur.p[h][k], scaled<SCALE>(cur.g[h][k], s), s.beta1 * m, v, s, p1, m1[h * 4 + k], v1[h * 4 + k]);
         if constexpr (COUNT) bad += nonfinite3(p1, m1[h * 4 + k], v1[h * 4 + k]);
@@ -676,7 +736,7 @@ blockwise_kernel(BlockwiseArgs a, Scalars s, unsigned long long* nonfinite) {
     }
     // The next block's loads go out before this block's reduction and
     // encoding, so their latency hides behind that work.
-    if (b + gridDim.x < a.nblocks) load_block(b + gridDim.x, nxt);
+    if (b + stride < bend) load_block(b + stride, nxt);
     // Block absmax: on non-negative floats (and NaN with the sign cleared)
     // the unsigned order of the bit patterns is the numeric order, with NaN
     // above everything, so an integer max propagates NaN as the reference's
@@ -709,10 +769,10 @@ blockwise_kernel(BlockwiseArgs a, Scalars s, unsigned long long* nonfinite) {
     const bool slow_m = guard_m || Am >= kInfBits, slow_v = guard_v || Av >= kInfBits;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const uint32_t cm = slow_m ? codes4_dispatch<true>(ncmp_m, m1 + 4 * h, dm, rdm, tab_m.mid, tab_m.base)
-                                 : codes4_dispatch<false>(ncmp_m, m1 + 4 * h, dm, rdm, tab_m.mid, tab_m.base);
-      const uint32_t cv = slow_v ? codes4_dispatch<true>(ncmp_v, v1 + 4 * h, dv, rdv, tab_v.mid, tab_v.base)
-                                 : codes4_dispatch<false>(ncmp_v, v1 + 4 * h, dv, rdv, tab_v.mid, tab_v.base);
+      const uint32_t cm = slow_m ? codes4_dispatch<true>(ncmp_m, m1 + 4 * h, dm, rdm, T.tab_m.mid, T.tab_m.base)
+                                 : codes4_dispatch<false>(ncmp_m, m1 + 4 * h, dm, rdm, T.tab_m.mid, T.tab_m.base);
+      const uint32_t cv = slow_v ? codes4_dispatch<true>(ncmp_v, v1 + 4 * h, dv, rdv, T.tab_v.mid, T.tab_v.base)
+                                 : codes4_dispatch<false>(ncmp_v, v1 + 4 * h, dv, rdv, T.tab_v.mid, T.tab_v.base);
       const long long e0 = base + h * 1024 + tid * 4;
       *reinterpret_cast<uint32_t*>(a.m_code + e0) = cm;
       *reinterpret_cast<uint32_t*>(a.v_code + e0) = cv;

@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstddef>
@@ -96,7 +97,7 @@ int device_info(int* dev_out, DeviceInfo* info) {
     if (e != hipSuccess || per < 1) per = 4;
     int bw = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &bw, reinterpret_cast<const void*>(pa::blockwise_kernel<false, false>), pa::kThreads, 0);
+        &bw, reinterpret_cast<const void*>(pa::blockwise_kernel<false, false, false>), pa::kThreads, 0);
     if (e != hipSuccess || bw < 1) bw = 2;
     d.cus = cus;
     d.blocks_per_cu = per;
@@ -402,14 +403,82 @@ int blockwise_inputs_clear(const pa::BlockwiseArgs& a, size_t n, std::vector<Ran
   return PA_OK;
 }
 
+// The blockwise tables of the ordered launch: one device buffer per (device,
+// stream), built by blockwise_tables before each launch.  Calls ordered on one
+// stream reuse its buffer in turn; calls on other streams have their own.  A
+// call under graph capture takes the persistent launch, so no graph holds a
+// buffer (which a later eviction could free).
+struct BwBuffer {
+  int dev;
+  hipStream_t st;
+  pa::BwTables* tabs;
+};
+std::mutex g_bw_mu;
+std::list<BwBuffer> g_bw_buffers;   // guarded by g_bw_mu, most recent first
+constexpr size_t kMaxBwBuffers = 16;
+std::atomic<long long> g_bw_force{0};   // pa_debug_blockwise_path
+// Blocks per workgroup of the ordered launch, and the workgroup rounds of a
+// tensor below which it keeps the persistent launch.
+constexpr long long kBwPerGroup = 12;
+constexpr long long kBwMinRounds = 4;
+
+bool capturing(hipStream_t st);
+
+// The table buffer of (dev, st), allocated on first use; nullptr when the
+// allocation fails (the caller then takes the persistent launch, which needs
+// none).
+pa::BwTables* bw_tables_for(int dev, hipStream_t st) {
+  std::lock_guard<std::mutex> lk(g_bw_mu);
+  for (auto it = g_bw_buffers.begin(); it != g_bw_buffers.end(); ++it)
+    if (it->dev == dev && it->st == st) {
+      g_bw_buffers.splice(g_bw_buffers.begin(), g_bw_buffers, it);
+      return g_bw_buffers.front().tabs;
+    }
+  pa::BwTables* t = nullptr;
+  if (hipMalloc(&t, sizeof(pa::BwTables)) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  g_bw_buffers.push_front(BwBuffer{dev, st, t});
+  while (g_bw_buffers.size() > kMaxBwBuffers) {
+    (void)hipFree(g_bw_buffers.back().tabs);   // waits for the work that reads it
+    g_bw_buffers.pop_back();
+  }
+  return t;
+}
+
+// Persistent launch (tables built per workgroup) for small tensors, for
+// pa_step_list_noalloc, under graph capture and when no table buffer can be
+// had; otherwise the
+// tables are built once into the stream's buffer and the ordered launch
+// takes kBwPerGroup blocks per workgroup.
 hipError_t launch_blockwise(const pa::BlockwiseArgs& a, const pa::Scalars& s, unsigned long long* nf,
-                            hipStream_t st, const DeviceInfo& d) {
-  const dim3 grid((unsigned)grid_for(a.nblocks, d, d.bw_blocks_per_cu)), block(pa::kThreads);
+                            hipStream_t st, int dev, const DeviceInfo& d, bool noalloc) {
   const bool sc = s.gscale != nullptr;
-  if (nf && sc) hipLaunchKernelGGL((pa::blockwise_kernel<true, true>), grid, block, 0, st, a, s, nf);
-  else if (nf) hipLaunchKernelGGL((pa::blockwise_kernel<true, false>), grid, block, 0, st, a, s, nf);
-  else if (sc) hipLaunchKernelGGL((pa::blockwise_kernel<false, true>), grid, block, 0, st, a, s, nf);
-  else hipLaunchKernelGGL((pa::blockwise_kernel<false, false>), grid, block, 0, st, a, s, nf);
+  const long long slots = (long long)d.cus * d.bw_blocks_per_cu;
+  const long long force = g_bw_force.load();
+  long long per = 0;
+  if (force > 0) per = force;
+  else if (force == 0 && a.nblocks >= kBwPerGroup * kBwMinRounds * slots) per = kBwPerGroup;
+  pa::BwTables* tabs = (per > 0 && !noalloc && !capturing(st)) ? bw_tables_for(dev, st) : nullptr;
+  const dim3 block(pa::kThreads);
+  if (tabs != nullptr) {
+    hipLaunchKernelGGL(pa::blockwise_tables, dim3(1), block, 0, st, a.qmap_m, a.qmap_v, tabs);
+    const dim3 grid((unsigned)((a.nblocks + per - 1) / per));
+    const long long one = 1;
+    if (nf && sc) hipLaunchKernelGGL((pa::blockwise_kernel<true, true, true>), grid, block, 0, st, a, s, nf, tabs, per, one);
+    else if (nf) hipLaunchKernelGGL((pa::blockwise_kernel<true, false, true>), grid, block, 0, st, a, s, nf, tabs, per, one);
+    else if (sc) hipLaunchKernelGGL((pa::blockwise_kernel<false, true, true>), grid, block, 0, st, a, s, nf, tabs, per, one);
+    else hipLaunchKernelGGL((pa::blockwise_kernel<false, false, true>), grid, block, 0, st, a, s, nf, tabs, per, one);
+    return hipGetLastError();
+  }
+  const long long g = grid_for(a.nblocks, d, d.bw_blocks_per_cu);
+  const dim3 grid((unsigned)g);
+  const pa::BwTables* none = nullptr;
+  if (nf && sc) hipLaunchKernelGGL((pa::blockwise_kernel<true, true, false>), grid, block, 0, st, a, s, nf, none, 0LL, g);
+  else if (nf) hipLaunchKernelGGL((pa::blockwise_kernel<true, false, false>), grid, block, 0, st, a, s, nf, none, 0LL, g);
+  else if (sc) hipLaunchKernelGGL((pa::blockwise_kernel<false, true, false>), grid, block, 0, st, a, s, nf, none, 0LL, g);
+  else hipLaunchKernelGGL((pa::blockwise_kernel<false, false, false>), grid, block, 0, st, a, s, nf, none, 0LL, g);
   return hipGetLastError();
 }
 
@@ -822,7 +891,7 @@ int pa_step_typed(int mode, int param_dtype, int grad_dtype, void* params, const
     if (rc) return rc;
     rc = device_info(&dev, &d);
     if (rc) return rc;
-    hipError_t e = launch_blockwise(a, s, hyper->nonfinite, st, d);
+    hipError_t e = launch_blockwise(a, s, hyper->nonfinite, st, dev, d, false);
     return e == hipSuccess ? PA_OK : hip_failed(e);
   }
   ElemTensor t;
@@ -924,7 +993,7 @@ int step_list(bool noalloc, int mode, int param_dtype, int grad_dtype, size_t co
     rc = device_info(&dev, &d);
     if (rc) return rc;
     for (const pa::BlockwiseArgs& a : args) {
-      hipError_t e = launch_blockwise(a, s, hyper->nonfinite, st, d);
+      hipError_t e = launch_blockwise(a, s, hyper->nonfinite, st, dev, d, noalloc);
       if (e != hipSuccess) return hip_failed(e);
     }
     return PA_OK;
@@ -1545,6 +1614,15 @@ void pa_release_plans(void) {
   g_plans.clear();
   for (TurboPlan& p : g_turbo_plans) free_turbo_plan(p);
   g_turbo_plans.clear();
+  std::lock_guard<std::mutex> lb(g_bw_mu);
+  for (BwBuffer& b : g_bw_buffers) (void)hipFree(b.tabs);
+  g_bw_buffers.clear();
+}
+
+int pa_debug_blockwise_path(long long blocks_per_workgroup) {
+  if (blocks_per_workgroup < -1 || blocks_per_workgroup > (1LL << 20)) return PA_ERR_ARG;
+  g_bw_force.store(blocks_per_workgroup);
+  return PA_OK;
 }
 
 int pa_debug_plan_count(int* step_plans, int* stats_plans, int* turbo_plans) {

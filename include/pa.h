@@ -168,7 +168,12 @@ int pa_step(int mode, float* params, const float* grads, void* state, size_t n,
  * the update of each element as for pa_step).  Elementwise modes: one
  * launch over a table of all of them, cut into 4096-element tiles, one
  * workgroup per tile (a list of more than 2^22 tiles takes one launch per
- * 2^22).  Blockwise mode: one launch per tensor.  params[i], grads[i],
+ * 2^22).  Blockwise mode, per tensor: from 48 blocks per workgroup slot
+ * up, two launches, one workgroup that builds the search tables of the
+ * map pair into a device buffer the library keeps per device and stream,
+ * then one workgroup per 12 consecutive blocks in dispatch order; smaller
+ * tensors, and every call under graph capture, one persistent launch
+ * whose workgroups build the tables themselves.  params[i], grads[i],
  * states[i] and n[i] describe tensor i exactly as for pa_step.  The table is
  * uploaded once per distinct list of parameter and state pointers and sizes
  * and cached (see pa_release_plans); the gradients are not part of it:
@@ -214,8 +219,9 @@ int pa_step_list_typed(int mode, int param_dtype, int grad_dtype, size_t count, 
  * beyond, before anything is enqueued).  Every call on one GPU shares the
  * array: calls that overlap on one GPU (on different streams, or from
  * different threads without ordering) race on it and may update the wrong
- * tensors; calls ordered on one stream are safe.  Blockwise mode uses no
- * table and behaves exactly as pa_step_list_typed. */
+ * tensors; calls ordered on one stream are safe.  Blockwise mode takes the
+ * persistent launch at every size (it needs no buffer) and gives the
+ * results of pa_step_list_typed. */
 #define PA_NOALLOC_MAX_TENSORS 4095
 int pa_step_list_noalloc(int mode, int param_dtype, int grad_dtype, size_t count, void* const* params,
                          const void* const* grads, void* const* states, const size_t* n,
@@ -399,8 +405,9 @@ const char* pa_status_string(int status);
  * thread (0 if none). */
 int pa_last_hip_error(void);
 
-/* Free every cached launch-plan table (device memory).  Waits for the
- * device first.  Safe to call at any time outside a running call. */
+/* Free every cached launch-plan table and blockwise table buffer (device
+ * memory).  Waits for the device first.  Safe to call at any time outside a
+ * running call. */
 void pa_release_plans(void);
 
 /* Plan-cache self-test export (host only): the number of cached launch
@@ -409,6 +416,14 @@ void pa_release_plans(void);
  * gradients that move between calls reuse it.  PA_ERR_ARG for a null
  * pointer. */
 int pa_debug_plan_count(int* step_plans, int* stats_plans, int* turbo_plans);
+
+/* Blockwise launch self-test export (host only, for the tests of both
+ * launches): 0 (the default) chooses by size as pa_step_list describes; -1
+ * takes the persistent launch at every size; k >= 1 takes the ordered launch
+ * with k blocks per workgroup at every size (the persistent launch still
+ * serves pa_step_list_noalloc and calls under graph capture).  Applies to
+ * every later call in the process.  PA_ERR_ARG below -1 or above 2^20. */
+int pa_debug_blockwise_path(long long blocks_per_workgroup);
 
 /* Scalar self-test export (host only, no device work): the per-call
  * binary32 scalars the kernels receive, formed from `hyper` and `step`

@@ -153,6 +153,16 @@ def test_debug_codec_rules(pa):
     assert L.pa_debug_pow2_rn32(FAKE + 4, 0, FAKE + 4096, 4, None) == pa.PA_ERR_ALIGN
 
 
+def test_debug_blockwise_path_rules(pa):
+    """The blockwise launch switch takes -1 (persistent), 0 (by size) and
+    1..2^20 blocks per workgroup; it only sets a flag (no device work)."""
+    L = pa.lib()
+    for bad in (-2, -(1 << 40), (1 << 20) + 1):
+        assert L.pa_debug_blockwise_path(bad) == pa.PA_ERR_ARG
+    for ok in (-1, 1, 12, 1 << 20, 0):
+        assert L.pa_debug_blockwise_path(ok) == pa.PA_OK
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     import adamw_step_amd as pa_mod
     monkeypatch.setattr(pa_mod, "LIB_PATH", str(tmp_path / "missing.so"))

@@ -188,8 +188,19 @@ def test_elementwise_hyper_grid(pa, mode):
            f"non-finite {want_bad}")
 
 
+@pytest.fixture
+def bw_path(pa, request):
+    pa.blockwise_path(request.param)
+    yield request.param
+    pa.blockwise_path(0)
+
+
+# Two blocks per combination take the persistent launch by size; the grid
+# runs again through the ordered launch (one block per workgroup, tables
+# built once per call), forced.
 @pytest.mark.timeout(600)
-def test_blockwise_hyper_grid(pa):
+@pytest.mark.parametrize("bw_path", [0, 1], indirect=True, ids=["by-size", "ordered-k1"])
+def test_blockwise_hyper_grid(pa, bw_path):
     import torch
     nb_per = 2
     n_per = nb_per * 2048
