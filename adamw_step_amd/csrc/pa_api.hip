@@ -426,9 +426,9 @@ bool capturing(hipStream_t st);
 
 // The table buffer of (dev, st), allocated on first use; nullptr when the
 // allocation fails (the caller then takes the persistent launch, which needs
-// none).
+// none).  The caller holds g_bw_mu until its launches are enqueued, so no
+// other thread frees the buffer in between.
 pa::BwTables* bw_tables_for(int dev, hipStream_t st) {
-  std::lock_guard<std::mutex> lk(g_bw_mu);
   for (auto it = g_bw_buffers.begin(); it != g_bw_buffers.end(); ++it)
     if (it->dev == dev && it->st == st) {
       g_bw_buffers.splice(g_bw_buffers.begin(), g_bw_buffers, it);
@@ -460,7 +460,12 @@ hipError_t launch_blockwise(const pa::BlockwiseArgs& a, const pa::Scalars& s, un
   long long per = 0;
   if (force > 0) per = force;
   else if (force == 0 && a.nblocks >= kBwPerGroup * kBwMinRounds * slots) per = kBwPerGroup;
-  pa::BwTables* tabs = (per > 0 && !noalloc && !capturing(st)) ? bw_tables_for(dev, st) : nullptr;
+  std::unique_lock<std::mutex> lk(g_bw_mu, std::defer_lock);
+  pa::BwTables* tabs = nullptr;
+  if (per > 0 && !noalloc && !capturing(st)) {
+    lk.lock();
+    tabs = bw_tables_for(dev, st);
+  }
   const dim3 block(pa::kThreads);
   if (tabs != nullptr) {
     hipLaunchKernelGGL(pa::blockwise_tables, dim3(1), block, 0, st, a.qmap_m, a.qmap_v, tabs);
