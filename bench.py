@@ -664,7 +664,8 @@ def main():
                    "grads": "drawn once on the device, reused every step"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": "blockwise_kernel" if mode == "blockwise8" else f"elementwise_list<{mode}>",
+                     "kernel": ("blockwise_tables + blockwise_kernel (the events span both launches of the step)"
+                                if mode == "blockwise8" else f"elementwise_list<{mode}>"),
                      "algorithmic_bytes_per_launch": algo_bytes,
                      "mean_launch_ms": round(mean_launch_ms, 4),
                      "median_launch_ms": round(sorted(launch_ms)[len(launch_ms) // 2], 4),
