@@ -716,6 +716,7 @@ blockwise_kernel(BlockwiseArgs a, Scalars s, unsigned long long* nonfinite, cons
   for (long long b = b0; b < bend; b += stride, slot ^= 1) {
     const long long base = b * kBlock;
     float m1[8], v1[8];
+    uint32_t pbad = 0;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const long long e0 = base + h * 1024 + tid * 4;
@@ -726,7 +727,7 @@ blockwise_kernel(BlockwiseArgs a, Scalars s, unsigned long long* nonfinite, cons
         const float v = T.lut_v[(cur.vc[h] >> (8 * k)) & 0xFFu] * cur.av;
         float p1;
         adamw(cur.p[h][k], scaled<SCALE>(cur.g[h][k], s), s.beta1 * m, v, s, p1, m1[h * 4 + k], v1[h * 4 + k]);
-        if constexpr (COUNT) bad += nonfinite3(p1, m1[h * 4 + k], v1[h * 4 + k]);
+        if constexpr (COUNT) pbad |= (__builtin_isfinite(p1) ? 0u : 1u) << (h * 4 + k);
         po[k] = p1;
       }
       uint2 out;
@@ -767,6 +768,17 @@ blockwise_kernel(BlockwiseArgs a, Scalars s, unsigned long long* nonfinite, cons
     // Inf or NaN in a block (absmax at or above the Inf pattern) takes the
     // slow path, which also orders NaN quotients above every midpoint.
     const bool slow_m = guard_m || Am >= kInfBits, slow_v = guard_v || Av >= kInfBits;
+    if constexpr (COUNT) {
+      // An element counts once if p', m' or v' is Inf or NaN.  p' is tested
+      // as it is formed (one bit per element); m' and v' are all finite
+      // unless the block absmax is at or above the Inf pattern, so only such
+      // blocks test them (this keeps the counting kernel free of spills).
+      if (Am >= kInfBits || Av >= kInfBits) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) pbad |= nonfinite3(1.0f, m1[k], v1[k]) << k;
+      }
+      bad += __builtin_popcount(pbad);
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint32_t cm = slow_m ? codes4_dispatch<true>(ncmp_m, m1 + 4 * h, dm, rdm, T.tab_m.mid, T.tab_m.base)
