@@ -9,7 +9,9 @@ rule the TurboAdam page sets for its compressed first moment: there the
 call is refused and leaves parameters and state as they were.
 The list mixes a tensor that keeps FP32 moments with two compressed ones
 whose tails are ragged, through the tuned kernel; a slice of the grid also
-runs through the general kernel."""
+runs through the general kernel.  The other index widths (2, 3, 6 and 8
+bits) run at four corners of the grid through both kernels, the general
+one at a 256-value 1Q block and 32-value UState groups."""
 import itertools
 
 import numpy as np
@@ -104,3 +106,48 @@ def test_turbo_hyperparameter_grid(pa, general):
     assert refused == sum(1 for pt in grid if not pt[0] * pt[0] < pt[1])
     banner(f"turbo grid: {len(grid) - refused} points bit-exact, {refused} refused, "
            f"{total_bad} non-finite values counted on both sides")
+
+
+# Other index widths, at the grid's corners: each width through the tuned
+# kernel (default blocks) and the general one (1Q block 256, UState group 32).
+CORNERS = [(0.0, 0.5, 3.0, 0.3, 0.0, 1000), (0.9, 0.999, 1e-3, 0.0, 1e-8, 2), (0.5, 0.999, 0.0, 0.3, 1e-2, 1),
+           (0.9, 0.5, 1e-3, 0.0, 1e-8, 1)]
+
+
+@pytest.mark.parametrize("bits", [2, 3, 6, 8])
+@pytest.mark.parametrize("general", [False, True], ids=["tuned", "general"])
+def test_turbo_widths_at_grid_corners(pa, bits, general):
+    import torch
+    block, group = (256, 32) if general else (128, 64)
+    r = np.random.Generator(np.random.PCG64(760 + bits + 10 * general))
+    for k, (b1, b2, lr, wd, eps, t0) in enumerate(CORNERS):
+        hp = [r.normal(0, 0.02, n).astype(np.float32) for n in SIZES]
+        dp = [to_dev(a) for a in hp]
+        hs = [oracle.TurboState(n, n >= 4096, n >= 4096, bits, block, group) for n in SIZES]
+        ds = [pa.TurboState(n, "cuda:0", n >= 4096, n >= 4096, bits, tensor_id=i, block_size=block,
+                            m_block_size=group) for i, n in enumerate(SIZES)]
+        gs = [torch.zeros(n, dtype=torch.float32, device="cuda:0") for n in SIZES]
+        tl = pa.TurboList(dp, gs, ds, v_bits=bits, block_size=block, m_block_size=group, general=general)
+        nf = torch.zeros(1, dtype=torch.int64, device="cuda:0")
+        hyper = dict(lr=lr, beta1=b1, beta2=b2, eps=eps, weight_decay=wd, nonfinite=nf)
+        if not b1 * b1 < b2:
+            with pytest.raises(pa.PAError):
+                tl.step(hyper, t0)
+            continue
+        want_bad = 0
+        for t in (t0, t0 + 1):
+            hg = [(r.normal(0, 1e-3, n) * 10.0 ** r.uniform(-3, 1)).astype(np.float32) for n in SIZES]
+            hg[1][:3] = 0.0
+            for gdev, g in zip(gs, hg):
+                gdev.copy_(torch.from_numpy(g))
+            banner(f"turbo widths: {bits} bits, {'general' if general else 'tuned'}, corner {k}, step {t}")
+            tl.step(hyper, t)
+            torch.cuda.synchronize()
+            sc = oracle.scalars(lr, b1, b2, eps, wd, t)
+            ts = oracle.turbo_scalars(b1, b2, t)
+            for i in range(len(SIZES)):
+                want_bad += oracle.turbo_step(hp[i], hg[i], hs[i], sc, ts, t, tensor_id=i)
+                what = f"{bits} bits corner {k} (b1 {b1}, b2 {b2}, lr {lr}, wd {wd}, eps {eps}, t {t}) tensor {i}"
+                _compare_state(ds[i], hs[i], what)
+                assert _bits_equal_or_both_nan(to_host(dp[i]), hp[i]), f"{what}: params"
+        assert int(nf.item()) == want_bad, (bits, k, int(nf.item()), want_bad)
