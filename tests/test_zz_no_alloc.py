@@ -2,8 +2,9 @@
 against pa_step_list on the same inputs, through the C ABI: two calls in a
 row, the second with a smaller list, in each elementwise mode; outputs
 bit-identical (the two run the same kernels; only where the tensor table
-lives differs).  Also: a list over the table's capacity is refused before
-anything is enqueued."""
+lives differs).  In blockwise mode the entry point takes the persistent
+launch (no table buffer) and matches pa_step_list's ordered one.  Also: a
+list over the table's capacity is refused before anything is enqueued."""
 import ctypes
 
 import pytest
@@ -101,3 +102,52 @@ def test_noalloc_rejects_a_list_over_capacity(pa):
     assert rc == pa.PA_ERR_CAPACITY
     torch.cuda.synchronize()
     assert int(buf.abs().sum().item()) == 0 and int(words.abs().sum().item()) == 0
+
+
+def test_noalloc_blockwise_matches_the_ordered_launch(pa):
+    """Blockwise mode: the no-allocation entry point takes the persistent
+    launch, pa_step_list the ordered one (forced here at 5 blocks per
+    workgroup); two calls in a row, the second with a smaller list, give
+    bit-identical codes, absmax values, BF16 outputs and counts."""
+    import numpy as np
+    import torch
+    import workloads
+    BW = 3
+    qm, qv = (torch.from_numpy(x).cuda() for x in workloads.code_maps())
+    zero = int(np.argmin(np.abs(workloads.code_maps()[0])))
+    hyper = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    counter_a = torch.zeros(1, dtype=torch.int64, device="cuda:0")
+    counter_b = torch.zeros(1, dtype=torch.int64, device="cuda:0")
+    pa.blockwise_path(5)
+    try:
+        for call, blocks in enumerate(([3, 40, 1], [7])):
+            g = torch.Generator(device="cuda:0").manual_seed(60 + call)
+            sets = []
+            for _ in range(2):
+                sets.append(([], [], []))
+            for nb in blocks:
+                n = nb * 2048
+                p = torch.randn(n, device="cuda:0", generator=g) * 0.02
+                gr = torch.randn(n, device="cuda:0", generator=g) * 1e-3
+                gr[n // 2] = float("inf")
+                mc = torch.full((n,), zero, dtype=torch.uint8, device="cuda:0")
+                vc = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda:0", generator=g)
+                ma = torch.rand(nb, device="cuda:0", generator=g) * 1e-3
+                va = torch.rand(nb, device="cuda:0", generator=g) * 1e-6
+                for ps, gs, ss in sets:
+                    ps.append(p.clone())
+                    gs.append(gr.clone())
+                    ss.append((mc.clone(), ma.clone(), vc.clone(), va.clone(), qm, qv,
+                               torch.zeros(n, dtype=torch.int16, device="cuda:0")))
+            (pa_, ga, sa), (pb, gb, sb) = sets
+            banner(f"no-alloc blockwise call {call + 1}: {len(blocks)} tensors")
+            pa.pa_step_list(BW, pa_, ga, sa, dict(hyper, nonfinite=counter_a), call + 1)
+            pa.pa_step_list(BW, pb, gb, sb, dict(hyper, nonfinite=counter_b), call + 1, noalloc=True)
+            torch.cuda.synchronize()
+            for i in range(len(blocks)):
+                for j in (0, 1, 2, 3, 6):
+                    x, y = sa[i][j], sb[i][j]
+                    assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), f"call {call + 1} tensor {i} field {j}"
+            assert int(counter_a.item()) == int(counter_b.item()) > 0
+    finally:
+        pa.blockwise_path(0)
