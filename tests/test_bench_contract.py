@@ -40,3 +40,21 @@ def test_stored_counter_readings_are_used_only_with_their_kernel_sources(monkeyp
     monkeypatch.setattr(bench, "kernel_sha", lambda family="elementwise": "0" * 16)
     assert bench.load_traffic("llama-7b", "e4") is None          # stale: reported as null
     assert bench.load_traffic("llama-7b", "fp32") is None        # never measured
+
+
+def test_profile_summaries_quote_commands_that_run_committed_files():
+    """Every summary under profiles/ gives the command that made it, and the
+    program each command runs is a file of this repository (bench.py at its
+    root), never one from a working folder."""
+    import glob
+    import re
+    files = sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md")))
+    assert files
+    for f in files:
+        lines = open(f).read().splitlines()
+        cmds = [l for l in lines if "rocprofv3 " in l or re.match(r"\s*(timeout .*)?python3? ", l)]
+        assert cmds, f"{os.path.basename(f)}: no command"
+        for c in cmds:
+            assert "_work" not in c, f"{os.path.basename(f)}: {c}"
+            for prog in re.findall(r"python3?\s+(?:-u\s+)?(\S+\.py)", c):
+                assert os.path.exists(os.path.join(ROOT, prog)), f"{os.path.basename(f)}: {prog} is not in the repository"
