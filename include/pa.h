@@ -172,8 +172,9 @@ int pa_step(int mode, float* params, const float* grads, void* state, size_t n,
  * up, two launches, one workgroup that builds the search tables of the
  * map pair into a device buffer the library keeps per device and stream,
  * then one workgroup per 12 consecutive blocks in dispatch order; smaller
- * tensors, and every call under graph capture, one persistent launch
- * whose workgroups build the tables themselves.  params[i], grads[i],
+ * tensors, every call under graph capture, and a stream whose buffer
+ * cannot be allocated, one persistent launch whose workgroups build the
+ * tables themselves; the results are the same.  params[i], grads[i],
  * states[i] and n[i] describe tensor i exactly as for pa_step.  The table is
  * uploaded once per distinct list of parameter and state pointers and sizes
  * and cached (see pa_release_plans); the gradients are not part of it:
