@@ -166,9 +166,9 @@ int pa_step(int mode, float* params, const float* grads, void* state, size_t n,
 /* `count` tensors sharing one hyperparameter set and one step (project
  * page, Execution contract table: one parameter group, one global step;
  * the update of each element as for pa_step).  Elementwise modes: one
- * launch over a table of all of them, cut into 4096-element tiles, one
- * workgroup per tile (a list of more than 2^22 tiles takes one launch per
- * 2^22).  Blockwise mode, per tensor: from 48 blocks per workgroup slot
+ * launch over a table of all of them, cut into 4096-element tiles (1024
+ * for lists under 32 Mi elements), one workgroup per tile (a list of more
+ * than 2^22 tiles takes one launch per 2^22).  Blockwise mode, per tensor: from 48 blocks per workgroup slot
  * up, two launches, one workgroup that builds the search tables of the
  * map pair into a device buffer the library keeps per device and stream,
  * then one workgroup per 12 consecutive blocks in dispatch order; smaller
