@@ -53,7 +53,9 @@
  *
  * Errors: every entry point returns PA_OK (0) or a negative PA_ERR_* code
  * and never aborts or throws.  A call that returns an error has enqueued
- * nothing.  There is no fallback path of any kind.
+ * nothing.  There is no fallback to code off the GPU (no CPU or eager
+ * path); the blockwise step's choice between its two GPU launches
+ * (pa_step_list) gives the same results either way.
  */
 #ifndef PA_H_
 #define PA_H_
